@@ -1,0 +1,501 @@
+/*
+ * tg_oracle.c -- plain, slow CPU oracle for the TokenGate gate-layer path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or helper with the
+ * HIP library: every function below is written from the method's definition.
+ *
+ * Sources (cited by page title and section / equation):
+ *   [DeepDive]  "TokenGate: Learnable Token Pruning for Fast, Memory-Efficient
+ *               LLM Prefill" (agientry.com paper deep dive), sections 2, 3.1,
+ *               3.2 and 3.4, equations 2-8.
+ *   [Summary]   "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
+ *               with Learned Token Pruning" (thelatestinai.com), Figure 1.
+ *
+ * Conventions:
+ *   - All floating-point arithmetic is fp64 (double).  Inputs arrive already
+ *     widened exactly from their storage type (bf16 or fp32) to double.
+ *   - Plain loops; OpenMP only over independent rows / heads.
+ *   - Compiled without fast-math and with -ffp-contract=off.
+ *
+ * Parity pins: every function is checked in tests/test_oracle_*.py against
+ * something other than itself (brute force, closed forms, NumPy/PyTorch CPU
+ * library routines, autograd, finite differences).  The readings listed as
+ * contract choices (scorer shape without biases, gate of forced tokens = 1,
+ * scalar temperature on q.k only, RoPE pairing and theta, where bf16 rounding
+ * happens) are "parity unpinned" by the pages: the pages do not fix them.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* a1. Scoring MLP and gate value                                            */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DeepDive] section 3.1, Eq. 3 (first part): a small MLP maps each token's
+ * normalised post-attention residual to one scalar score, b~_j = MLP(a~_j).
+ * Reading used here: two layers d -> d_ff -> 1, SiLU in between, no biases:
+ *     u_k = sum_i W1[k,i] h[i]            (W1 is stored out x in: [d_ff, d])
+ *     s   = sum_k w2[k] * SiLU(u_k),      SiLU(u) = u / (1 + exp(-u))
+ * Gate value: g = sigmoid(s) = 1 / (1 + exp(-s)) for prunable tokens.  For a
+ * forced (non-prunable) token, Eq. 3 sets its score to zero bias, so its gate
+ * enters attention as g = 1 (log g = 0, no bias).
+ *
+ * hidden: [T, d]; forced: [T] or NULL; scores, gates: [T] (gates may be NULL).
+ */
+void tgo_gate_score(const double *hidden, const double *w1, const double *w2,
+                    const uint8_t *forced, int64_t T, int64_t d, int64_t d_ff,
+                    double *scores, double *gates)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+        const double *h = hidden + t * d;
+        double s = 0.0;
+        for (int64_t k = 0; k < d_ff; ++k) {
+            const double *row = w1 + k * d;
+            double u = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                u += row[i] * h[i];
+            double a = u / (1.0 + exp(-u));
+            s += w2[k] * a;
+        }
+        scores[t] = s;
+        if (gates) {
+            if (forced && forced[t])
+                gates[t] = 1.0;
+            else
+                gates[t] = 1.0 / (1.0 + exp(-s));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* a2. Scaffold-aware top-K selection                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DeepDive] section 3.1, Eq. 4: S = topK over the prunable set P of the
+ * scores, united with the non-prunable set N.  Section 3.4: the budget is
+ * clamped (K' = min(K, |P|)) and a keep mask over the full sequence is built,
+ * so the kept tokens come out in their original (ascending) order.
+ *
+ * Order used to rank prunable tokens (a total order on (score, index)):
+ *   1. any non-NaN score ranks above NaN;
+ *   2. among non-NaN scores, the larger ranks higher, with -0 == +0 and
+ *      -inf < every finite value < +inf (plain IEEE comparison);
+ *   3. equal scores (and NaN vs NaN): the lower index ranks higher.
+ * Scores are compared as the fp32 values the caller holds.
+ */
+typedef struct {
+    float s;
+    int64_t idx;
+} ranked_t;
+
+/* qsort comparator: negative when a ranks before b. */
+static int rank_cmp(const void *pa, const void *pb)
+{
+    const ranked_t *a = (const ranked_t *)pa, *b = (const ranked_t *)pb;
+    int na = isnan(a->s), nb = isnan(b->s);
+    if (na != nb)
+        return na ? 1 : -1;
+    if (!na && a->s != b->s)
+        return a->s > b->s ? -1 : 1;
+    return a->idx < b->idx ? -1 : (a->idx > b->idx ? 1 : 0);
+}
+
+/*
+ * One batch row.  scores: [N]; forced: [N] or NULL (no forced token).
+ * Writes min(true M, M_alloc) ascending indices into kept[0..M_alloc) and pads
+ * the rest with -1.  Returns the true kept count M = |N| + min(K, |P|), where
+ * |N| is the number of forced tokens actually present in `forced`.
+ * Returns -1 if K < 0 or memory cannot be allocated.
+ */
+int64_t tgo_select_topk(const float *scores, const uint8_t *forced, int64_t N,
+                        int64_t K, int64_t M_alloc, int32_t *kept)
+{
+    if (K < 0)
+        return -1;
+    int64_t nF = 0;
+    for (int64_t n = 0; n < N; ++n)
+        if (forced && forced[n])
+            ++nF;
+    int64_t nP = N - nF;
+    int64_t Kc = K < nP ? K : nP;
+
+    ranked_t *cand = (ranked_t *)malloc(sizeof(ranked_t) * (size_t)(nP > 0 ? nP : 1));
+    uint8_t *keep = (uint8_t *)calloc((size_t)(N > 0 ? N : 1), 1);
+    if (!cand || !keep) {
+        free(cand);
+        free(keep);
+        return -1;
+    }
+    int64_t c = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        if (forced && forced[n]) {
+            keep[n] = 1; /* every non-prunable token survives */
+        } else {
+            cand[c].s = scores[n];
+            cand[c].idx = n;
+            ++c;
+        }
+    }
+    qsort(cand, (size_t)nP, sizeof(ranked_t), rank_cmp);
+    for (int64_t r = 0; r < Kc; ++r)
+        keep[cand[r].idx] = 1;
+
+    int64_t m = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        if (keep[n]) {
+            if (m < M_alloc)
+                kept[m] = (int32_t)n;
+            ++m;
+        }
+    }
+    for (int64_t r = m; r < M_alloc; ++r)
+        kept[r] = -1;
+    free(cand);
+    free(keep);
+    return m;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a3. Compaction                                                            */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DeepDive] section 3.4: the kept hidden states are sliced with the keep
+ * indices and the position ids are taken at the same indices (the original
+ * positions); the gate values of the kept tokens are handed to attention.
+ * A plain gather.  Rows whose index is outside [0, N) (padding, -1) give a
+ * zero hidden row, position -1 and gate 0.
+ *
+ * One batch row.  hidden: N rows of row_bytes bytes; pos: [N] or NULL
+ * (NULL means position = index); gates: [N] or NULL.
+ */
+void tgo_compact(const uint8_t *hidden, const int32_t *pos, const float *gates,
+                 const int32_t *kept, int64_t N, int64_t M, int64_t row_bytes,
+                 uint8_t *hidden_out, int32_t *pos_out, float *gates_out)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t n = kept[m];
+        int valid = (n >= 0 && n < N);
+        if (hidden_out) {
+            if (valid)
+                memcpy(hidden_out + m * row_bytes, hidden + n * row_bytes, (size_t)row_bytes);
+            else
+                memset(hidden_out + m * row_bytes, 0, (size_t)row_bytes);
+        }
+        if (pos_out)
+            pos_out[m] = valid ? (pos ? pos[n] : (int32_t)n) : -1;
+        if (gates_out)
+            gates_out[m] = valid ? (gates ? gates[n] : 1.0f) : 0.0f;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rotary position embedding at the kept tokens' original positions          */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pages say the kept positions are the original position ids
+ * ([DeepDive] section 3.4); the rotation itself is the backbone's (Qwen3 uses
+ * rotary embeddings).  Reading: rotate-half pairing (x_i, x_{i+D/2}) for
+ * i < D/2, angle phi_i = p * theta^(-2i/D), computed in fp64:
+ *     x_i'       = x_i cos(phi) - x_{i+D/2} sin(phi)
+ *     x_{i+D/2}' = x_{i+D/2} cos(phi) + x_i sin(phi)
+ */
+static void rope_rotate(double *x, int64_t D, double p, double theta, int sign)
+{
+    int64_t h = D / 2;
+    for (int64_t i = 0; i < h; ++i) {
+        double phi = p * pow(theta, -2.0 * (double)i / (double)D);
+        double cs = cos(phi), sn = sign * sin(phi);
+        double a = x[i], b = x[i + h];
+        x[i] = a * cs - b * sn;
+        x[i + h] = b * cs + a * sn;
+    }
+}
+
+/*
+ * Round a double to the nearest bf16 value (ties to even), returned as a
+ * double.  bf16 keeps 8 significant bits: clear the low 45 of the 52
+ * fraction bits of the double with round-to-nearest-even.  Values below the
+ * normal range of bf16 go through float (not reached by these workloads).
+ */
+static double round_bf16(double x)
+{
+    if (isnan(x) || isinf(x) || x == 0.0)
+        return x;
+    if (fabs(x) < 1.1754943508222875e-38) {
+        float f = (float)x;
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        u += 0x7FFFu + ((u >> 16) & 1u);
+        u &= 0xFFFF0000u;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    uint64_t u;
+    memcpy(&u, &x, 8);
+    uint64_t lsb = (u >> 45) & 1u;
+    u += ((uint64_t)1 << 44) - 1u + lsb;
+    u &= ~(((uint64_t)1 << 45) - 1u);
+    memcpy(&x, &u, 8);
+    return x;
+}
+
+/* Rotate (and optionally bf16-round) a [B, M, H, D] tensor into `out`. */
+static void rotate_all(const double *x, double *out, const int32_t *pos, double theta,
+                       int64_t B, int64_t M, int64_t H, int64_t D, int round)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t bm = 0; bm < B * M; ++bm) {
+        for (int64_t h = 0; h < H; ++h) {
+            double *y = out + (bm * H + h) * D;
+            memcpy(y, x + (bm * H + h) * D, sizeof(double) * (size_t)D);
+            if (pos) {
+                rope_rotate(y, D, (double)pos[bm], theta, +1);
+                if (round)
+                    for (int64_t e = 0; e < D; ++e)
+                        y[e] = round_bf16(y[e]);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* a4. Token-gated causal attention, forward                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DeepDive] section 2, Eq. 2 (causal attention, z = q.k / sqrt(d_head)) and
+ * section 3.2, Eq. 5 (each attention weight multiplied by its key's gate value
+ * g_j and renormalised; [Summary] Figure 1(c)), with the per-head gain of
+ * Eq. 6 and a temperature.  Form computed here, for query row i, query head h,
+ * kv head kv = floor(h / (Hq/Hkv)), keys j <= i (indices in the compacted
+ * sequence):
+ *     S_ij = q^_i . k^_j / (sqrt(D) * tau) + gamma_h * ln g_j
+ *     P_ij = exp(S_ij - lse_i),   lse_i = ln sum_{j<=i} exp(S_ij)
+ *     O_i  = sum_j P_ij v_j
+ * which equals exp(z_ij / tau) * g_j^gamma_h renormalised over j <= i.
+ * q^, k^ are q, k rotated at their positions (identity when pos == NULL) and,
+ * when round is set, rounded to bf16 (the precision the tensor cores consume).
+ * A key with g_j = 0 has ln g_j = -inf and weight 0; a row whose every logit
+ * is -inf gets O = 0 and lse = -inf.
+ *
+ * rows: optional list of nrows flattened (b * M + i) query rows to compute;
+ * NULL computes all B*M rows.  o: [B, M, Hq, D], lse: [B, Hq, M]; entries of
+ * rows not listed are left untouched.
+ */
+int tgo_attn_fwd(const double *q, const double *k, const double *v, const double *g,
+                 const double *gamma, const int32_t *pos, double theta, double tau,
+                 int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, int round,
+                 const int64_t *rows, int64_t nrows, double *o, double *lse)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0)
+        return -1;
+    int64_t grp = Hq / Hkv;
+    double c = 1.0 / (sqrt((double)D) * tau);
+    double *qr = (double *)malloc(sizeof(double) * (size_t)(B * M * Hq * D));
+    double *kr = (double *)malloc(sizeof(double) * (size_t)(B * M * Hkv * D));
+    if (!qr || !kr) {
+        free(qr);
+        free(kr);
+        return -1;
+    }
+    rotate_all(q, qr, pos, theta, B, M, Hq, D, round);
+    rotate_all(k, kr, pos, theta, B, M, Hkv, D, round);
+    int64_t R = rows ? nrows : B * M;
+
+#pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t r = 0; r < R; ++r) {
+            for (int64_t h = 0; h < Hq; ++h) {
+                int64_t bi = rows ? rows[r] : r;
+                int64_t b = bi / M, i = bi % M;
+                int64_t kv = h / grp;
+                const double *qi = qr + ((b * M + i) * Hq + h) * D;
+                double mx = -INFINITY;
+                for (int64_t j = 0; j <= i; ++j) {
+                    const double *kj = kr + ((b * M + j) * Hkv + kv) * D;
+                    double dot = 0.0;
+                    for (int64_t e = 0; e < D; ++e)
+                        dot += qi[e] * kj[e];
+                    double gj = g[b * M + j];
+                    double bias = gj > 0.0 ? gamma[h] * log(gj) : -INFINITY;
+                    logit[j] = c * dot + bias;
+                    if (logit[j] > mx)
+                        mx = logit[j];
+                }
+                double *oi = o + ((b * M + i) * Hq + h) * D;
+                for (int64_t e = 0; e < D; ++e)
+                    oi[e] = 0.0;
+                if (mx == -INFINITY) {
+                    lse[(b * Hq + h) * M + i] = -INFINITY;
+                    continue;
+                }
+                double sum = 0.0;
+                for (int64_t j = 0; j <= i; ++j)
+                    sum += exp(logit[j] - mx);
+                double l = mx + log(sum);
+                lse[(b * Hq + h) * M + i] = l;
+                for (int64_t j = 0; j <= i; ++j) {
+                    double p = exp(logit[j] - l);
+                    const double *vj = v + ((b * M + j) * Hkv + kv) * D;
+                    for (int64_t e = 0; e < D; ++e)
+                        oi[e] += p * vj[e];
+                }
+            }
+        }
+        free(logit);
+    }
+    free(qr);
+    free(kr);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a5. Token-gated causal attention, backward                                */
+/* ------------------------------------------------------------------------ */
+/*
+ * The task gradient reaches the scorer through the attention bias
+ * ([DeepDive] section 3.1 last paragraph, section 3.2, and the flowchart's
+ * "task gradient through bias" edge).  Derivatives of the forward above,
+ * given dO, for each (b, h, i) and j <= i:
+ *     dP_ij = dO_i . v_j
+ *     D_i   = sum_j P_ij dP_ij
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dq^_i += c dS_ij k^_j      dk^_j += c dS_ij q^_i      dv_j += P_ij dO_i
+ *     colsum_h(j) += dS_ij
+ * then dq = R(-phi_i) dq^, dk = R(-phi_j) dk^ (the bf16 rounding of q^, k^ is
+ * passed straight through), dk and dv summed over the query heads of the
+ * group, and for the gate terms (S depends on g_j through gamma_h ln g_j):
+ *     dg_j     = sum_h gamma_h colsum_h(j) / g_j      (0 where g_j = 0)
+ *     dgamma_h = sum_b sum_j colsum_h(j) ln g_j       (terms with g_j = 0 skipped)
+ *
+ * dq: [B,M,Hq,D]; dk, dv: [B,M,Hkv,D]; dg: [B,M]; dgamma: [Hq].
+ */
+int tgo_attn_bwd(const double *q, const double *k, const double *v, const double *g,
+                 const double *gamma, const int32_t *pos, double theta, double tau,
+                 const double *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
+                 int64_t D, int round, double *dq, double *dk, double *dv, double *dg,
+                 double *dgamma)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0)
+        return -1;
+    int64_t grp = Hq / Hkv;
+    double c = 1.0 / (sqrt((double)D) * tau);
+    double *qr = (double *)malloc(sizeof(double) * (size_t)(B * M * Hq * D));
+    double *kr = (double *)malloc(sizeof(double) * (size_t)(B * M * Hkv * D));
+    double *colsum = (double *)calloc((size_t)(B * Hq * M), sizeof(double));
+    if (!qr || !kr || !colsum) {
+        free(qr);
+        free(kr);
+        free(colsum);
+        return -1;
+    }
+    rotate_all(q, qr, pos, theta, B, M, Hq, D, round);
+    rotate_all(k, kr, pos, theta, B, M, Hkv, D, round);
+    memset(dq, 0, sizeof(double) * (size_t)(B * M * Hq * D));
+    memset(dk, 0, sizeof(double) * (size_t)(B * M * Hkv * D));
+    memset(dv, 0, sizeof(double) * (size_t)(B * M * Hkv * D));
+
+    /* One task per (b, kv head): it owns dk/dv of that kv head, so no races. */
+#pragma omp parallel
+    {
+        double *P = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+        double *dP = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t kv = 0; kv < Hkv; ++kv) {
+                for (int64_t h = kv * grp; h < (kv + 1) * grp; ++h) {
+                    for (int64_t i = 0; i < M; ++i) {
+                        const double *qi = qr + ((b * M + i) * Hq + h) * D;
+                        const double *doi = dout + ((b * M + i) * Hq + h) * D;
+                        double mx = -INFINITY;
+                        for (int64_t j = 0; j <= i; ++j) {
+                            const double *kj = kr + ((b * M + j) * Hkv + kv) * D;
+                            double dot = 0.0;
+                            for (int64_t e = 0; e < D; ++e)
+                                dot += qi[e] * kj[e];
+                            double gj = g[b * M + j];
+                            double bias = gj > 0.0 ? gamma[h] * log(gj) : -INFINITY;
+                            P[j] = c * dot + bias;
+                            if (P[j] > mx)
+                                mx = P[j];
+                        }
+                        if (mx == -INFINITY)
+                            continue; /* no visible key: zero gradient */
+                        double sum = 0.0;
+                        for (int64_t j = 0; j <= i; ++j)
+                            sum += exp(P[j] - mx);
+                        double l = mx + log(sum);
+                        double Di = 0.0;
+                        for (int64_t j = 0; j <= i; ++j) {
+                            P[j] = exp(P[j] - l);
+                            const double *vj = v + ((b * M + j) * Hkv + kv) * D;
+                            double d = 0.0;
+                            for (int64_t e = 0; e < D; ++e)
+                                d += doi[e] * vj[e];
+                            dP[j] = d;
+                            Di += P[j] * d;
+                        }
+                        double *dqi = dq + ((b * M + i) * Hq + h) * D;
+                        for (int64_t j = 0; j <= i; ++j) {
+                            double dS = P[j] * (dP[j] - Di);
+                            const double *kj = kr + ((b * M + j) * Hkv + kv) * D;
+                            double *dkj = dk + ((b * M + j) * Hkv + kv) * D;
+                            double *dvj = dv + ((b * M + j) * Hkv + kv) * D;
+                            for (int64_t e = 0; e < D; ++e) {
+                                dqi[e] += c * dS * kj[e];
+                                dkj[e] += c * dS * qi[e];
+                                dvj[e] += P[j] * doi[e];
+                            }
+                            colsum[(b * Hq + h) * M + j] += dS;
+                        }
+                    }
+                }
+            }
+        }
+        free(P);
+        free(dP);
+    }
+
+    /* Undo the rotation on the gradients of the rotated q and k. */
+    if (pos) {
+#pragma omp parallel for schedule(static)
+        for (int64_t bm = 0; bm < B * M; ++bm) {
+            for (int64_t h = 0; h < Hq; ++h)
+                rope_rotate(dq + (bm * Hq + h) * D, D, (double)pos[bm], theta, -1);
+            for (int64_t h = 0; h < Hkv; ++h)
+                rope_rotate(dk + (bm * Hkv + h) * D, D, (double)pos[bm], theta, -1);
+        }
+    }
+
+    for (int64_t bm = 0; bm < B * M; ++bm) {
+        int64_t b = bm / M, j = bm % M;
+        double gj = g[bm];
+        double acc = 0.0;
+        for (int64_t h = 0; h < Hq; ++h)
+            acc += gamma[h] * colsum[(b * Hq + h) * M + j];
+        dg[bm] = gj > 0.0 ? acc / gj : 0.0;
+    }
+    for (int64_t h = 0; h < Hq; ++h) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t j = 0; j < M; ++j) {
+                double gj = g[b * M + j];
+                if (gj > 0.0)
+                    acc += colsum[(b * Hq + h) * M + j] * log(gj);
+            }
+        dgamma[h] = acc;
+    }
+    free(qr);
+    free(kr);
+    free(colsum);
+    return 0;
+}
+
+/* Exposed for the pin tests of the bf16 rounding helper. */
+double tgo_round_bf16(double x) { return round_bf16(x); }

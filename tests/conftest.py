@@ -1,0 +1,25 @@
+"""Shared pytest setup: the `gpu` marker and import paths.
+
+Tests marked ``gpu`` need a ROCm device and the built HIP library; everything
+else runs on the CPU (oracle pins, host logic, library load/export checks).
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) device and the built libtokengate")
+
+
+@pytest.fixture(scope="session")
+def oracle_mod():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
