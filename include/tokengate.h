@@ -1,0 +1,191 @@
+/*
+ * tokengate.h -- C ABI of libtokengate, the gate-layer hot path of TokenGate
+ * (learned token pruning with gate scores) for AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the method's statement of the problem:
+ *   score every context token, keep the top K prunable tokens plus every
+ *   non-prunable (scaffold) token in original order, gather the kept hidden
+ *   states, positions and gate values, and run causal attention whose weights
+ *   are multiplied by each key's gate value; plus the backward of that
+ *   attention, through which the task gradient reaches the scores.
+ *
+ * Sources cited below (page title, then section / equation):
+ *   [DeepDive] "TokenGate: Learnable Token Pruning for Fast, Memory-Efficient
+ *              LLM Prefill" (agientry.com paper deep dive).
+ *   [Summary]  "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
+ *              with Learned Token Pruning" (thelatestinai.com).
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous
+ *     row-major, 16-byte aligned.  The library allocates no device memory and
+ *     keeps no pointer after a call returns; scratch memory comes from a
+ *     caller workspace sized by the matching *_workspace_size call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All device work
+ *     is enqueued asynchronously on it; no call synchronises with the host.
+ *     Keep buffers alive until the stream has passed the work.
+ *   - `dt` gives the storage type of hidden, w1, w2, q, k, v, o and dout
+ *     (TG_BF16 or TG_F32).  Scores, gates, lse and every gradient are fp32.
+ *   - Errors that the host can see (a NULL required pointer, a bad size, a
+ *     misaligned pointer, an unsupported shape, a small workspace) return
+ *     before anything is launched.  A failed launch returns TG_ERR_HIP; the
+ *     text is in tg_last_error() (thread-local).
+ *   - Data conditions are defined behaviour, not errors: NaN or infinite
+ *     scores, ties, K = 0, K >= the number of prunable tokens, and a forced
+ *     mask whose count differs from n_forced (see tg_select_topk).
+ *   - Calls are stateless and may be made from several threads; device
+ *     properties are cached once per device.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARG = 1, /* NULL / negative / inconsistent / misaligned argument */
+    TG_ERR_UNSUPPORTED = 2, /* valid but not implemented shape or dtype */
+    TG_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
+    TG_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int tg_version(void);
+
+/* Static description of a status code. */
+const char *tg_status_string(tg_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *tg_last_error(void);
+
+/*
+ * tg_gate_score -- the scoring MLP and the gate value of every token.
+ * [DeepDive] section 3.1, Eq. 3 (first part): a small MLP maps each token's
+ * normalised post-attention residual to one scalar; section 3.4 shows the
+ * scorer applied to the residual before selection.  Form computed:
+ *     s_t = sum_k w2[k] * SiLU( sum_i w1[k, i] * hidden[t, i] ),
+ *     gates[t] = 1 if forced_keep[t] != 0, else 1 / (1 + exp(-s_t)).
+ *   hidden      [B, N, d]  (dt)     token states at the gate layer
+ *   w1          [d_ff, d]  (dt)     first layer, stored out x in
+ *   w2          [d_ff]     (dt)     second layer
+ *   forced_keep [B, N] u8 or NULL   nonzero = non-prunable token (gate 1)
+ *   scores      [B, N] f32 out      raw scores (the ranking key)
+ *   gates       [B, N] f32 out or NULL
+ * bf16 runs on matrix cores with fp32 accumulation; SiLU, the w2 dot and the
+ * sigmoid are fp32.  Needs d % 32 == 0 for bf16 and d % 4 == 0 for f32.
+ */
+tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2,
+                        const uint8_t *forced_keep, int64_t B, int64_t N, int64_t d,
+                        int64_t d_ff, tg_dtype dt, float *scores, float *gates,
+                        void *stream);
+
+/* Kept tokens per row: n_forced + min(K, N - n_forced); -1 for invalid input. */
+int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K);
+
+/* Workspace bytes tg_select_topk needs (0 today; kept for the ABI). */
+size_t tg_select_topk_workspace_size(int64_t B, int64_t N);
+
+/*
+ * tg_select_topk -- scaffold-aware top-K, kept in original order.
+ * [DeepDive] section 3.1, Eq. 4: S = top-K of the prunable set P by score,
+ * united with the non-prunable set; section 3.4: the budget is clamped and a
+ * keep mask over the whole sequence is built.
+ *   scores      [B, N] f32           ranking key
+ *   forced_keep [B, N] u8 or NULL    nonzero = always kept (NULL: none forced)
+ *   K >= 0                           budget of prunable tokens
+ *   n_forced                         forced tokens per row the caller expects;
+ *                                    sets the row length M = tg_kept_count(N, n_forced, K)
+ *   kept_idx    [B, M] i32 out       strictly ascending token indices
+ *   kept_count  [B] i32 out or NULL  true kept count of each row
+ * Order: a non-NaN score ranks above NaN; larger ranks above smaller, with
+ * -0 == +0 and -inf < finite < +inf; equal scores rank the lower index first.
+ * A row whose forced count differs from n_forced keeps its true count
+ * M_true = F + min(K, N - F): it writes min(M_true, M) indices, pads the rest
+ * with -1 and reports M_true in kept_count.
+ */
+tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_t B,
+                         int64_t N, int64_t K, int64_t n_forced, int32_t *kept_idx,
+                         int32_t *kept_count, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * tg_compact -- gather of the kept tokens' hidden states, original positions
+ * and gate values.  [DeepDive] section 3.4: the hidden states are sliced with
+ * the keep indices and the position ids are taken at the same indices.
+ *   hidden     [B, N, d] (dt)        source rows
+ *   pos        [B, N] i32 or NULL    position ids (NULL: position = index)
+ *   gates      [B, N] f32 or NULL
+ *   kept_idx   [B, M] i32            indices from tg_select_topk
+ *   hidden_out [B, M, d] (dt) or NULL, pos_out [B, M] i32 or NULL,
+ *   gates_out  [B, M] f32 or NULL (needs gates)
+ * An index outside [0, N) (the -1 padding) yields a zero row, position -1
+ * and gate 0.  The copy is bit-exact.
+ */
+tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates,
+                     const int32_t *kept_idx, int64_t B, int64_t N, int64_t M, int64_t d,
+                     tg_dtype dt, void *hidden_out, int32_t *pos_out, float *gates_out,
+                     void *stream);
+
+/* Workspace bytes the attention calls need (bwd = 0: forward, 1: backward). */
+size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
+                                    int64_t D, int bwd);
+
+/*
+ * tg_gated_attn_fwd -- token-gated causal attention over the kept tokens.
+ * [DeepDive] section 2, Eq. 2 (causal attention); section 3.2, Eq. 5 (each
+ * weight multiplied by its key's gate value g_j, renormalised) and Eq. 6
+ * (per-head non-negative gain); section 3.4 (temperature folded into the
+ * query scale, gate passed as a per-key bias); [Summary] Figure 1(c).
+ * For batch b, query head h, kv head h / (Hq / Hkv), rows i and keys j <= i
+ * of the compacted sequence:
+ *     S_ij = (q^_i . k^_j) / (sqrt(D) * tau) + gamma[h] * ln g_j
+ *     o_i  = sum_j softmax_j(S_ij) v_j,     lse_i = ln sum_{j <= i} exp(S_ij)
+ * q^, k^ are q, k rotated by rotary embedding at pos (rotate-half pairs
+ * (x_i, x_{i+D/2}), angle pos * rope_theta^(-2i/D), computed in fp64); pos
+ * NULL means no rotation.  A key with g_j = 0 gets weight 0; a row with no
+ * visible key gets o = 0, lse = -inf.
+ *   q [B, M, Hq, D], k, v [B, M, Hkv, D], o [B, M, Hq, D] (dt)
+ *   g [B, M] f32 > = 0, gamma [Hq] f32, pos [B, M] i32 or NULL
+ *   lse [B, Hq, M] f32 out or NULL (needed by the backward)
+ * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8, 16, 32, 64, 128}; q.k and
+ * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
+ * bf16 for the P.v product.  f32: D <= 128, plain fp32 arithmetic.
+ */
+tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g,
+                            const float *gamma, const int32_t *pos, float rope_theta,
+                            float tau, int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
+                            int64_t D, tg_dtype dt, void *o, float *lse, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * tg_gated_attn_bwd -- gradients of tg_gated_attn_fwd.  The task gradient
+ * reaches the scorer through the attention bias ([DeepDive] section 3.1 last
+ * paragraph, section 3.2, and the flowchart's "task gradient through bias").
+ * Given dout = dL/do and the forward's lse:
+ *     dP_ij = dout_i . v_j,  D_i = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - D_i)
+ *     dq = R(-phi_i) c sum_j dS_ij k^_j,   dk = R(-phi_j) c sum_i dS_ij q^_i
+ *     dv_j = sum_i P_ij dout_i,            (dk, dv summed over the group)
+ *     dg_j = sum_h gamma_h colsum_h(j) / g_j      (0 where g_j = 0)
+ *     dgamma_h = sum_b sum_j colsum_h(j) ln g_j,   colsum_h(j) = sum_i dS_ij
+ * with c = 1 / (sqrt(D) tau).  D_i is formed from fp32 P and dP, not from
+ * the rounded output.  Outputs are fp32 and fully overwritten:
+ *   dq [B, M, Hq, D], dk, dv [B, M, Hkv, D], dg [B, M], dgamma [Hq].
+ * Deterministic: repeated calls give bitwise-identical results.
+ */
+tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g,
+                            const float *gamma, const int32_t *pos, float rope_theta,
+                            float tau, const float *lse, const void *dout, int64_t B,
+                            int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
+                            float *dq, float *dk, float *dv, float *dg, float *dgamma,
+                            void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

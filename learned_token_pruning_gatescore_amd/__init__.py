@@ -1,0 +1,238 @@
+"""libtokengate: the TokenGate gate-layer hot path on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/tokengate.h``.  Each ``tg_*``
+function here has the name of the C entry point it calls; it only marshals
+torch device tensors into pointers and sizes, passes the current HIP stream and
+raises on a non-OK status.  Every step of the computation runs in the HIP
+kernels of libtokengate.so; there is no fallback: if the library is not built
+the calls raise.
+
+Stages (TokenGate deep dive, "TokenGate: Learnable Token Pruning for Fast,
+Memory-Efficient LLM Prefill", sections 3.1-3.4):
+  tg_gate_score      scoring MLP -> raw scores and gate values
+  tg_select_topk     top-K prunable tokens plus every forced token, ascending
+  tg_compact         gather of kept hidden states, positions and gates
+  tg_gated_attn_fwd  causal attention with the per-key bias gamma_h * ln g_j
+  tg_gated_attn_bwd  its gradients (dq, dk, dv, dg, dgamma)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TokenGateError", "library_path", "load", "tg_version", "tg_kept_count", "tg_gate_score",
+    "tg_select_topk", "tg_compact", "tg_gated_attn_fwd", "tg_gated_attn_bwd",
+    "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libtokengate.so"
+_lib = None
+
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, TG_ERR_HIP = range(5)
+TG_F32, TG_BF16 = 0, 1
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load libtokengate.so (built in-tree by learned_token_pruning_gatescore_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m learned_token_pruning_gatescore_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i64, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    c_int = ctypes.c_int
+    lib.tg_version.restype = c_int
+    lib.tg_version.argtypes = []
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_status_string.argtypes = [c_int]
+    lib.tg_last_error.restype = ctypes.c_char_p
+    lib.tg_last_error.argtypes = []
+    lib.tg_kept_count.restype = i64
+    lib.tg_kept_count.argtypes = [i64, i64, i64]
+    lib.tg_gate_score.restype = c_int
+    lib.tg_gate_score.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P]
+    lib.tg_select_topk_workspace_size.restype = sz
+    lib.tg_select_topk_workspace_size.argtypes = [i64, i64]
+    lib.tg_select_topk.restype = c_int
+    lib.tg_select_topk.argtypes = [P, P, i64, i64, i64, i64, P, P, P, sz, P]
+    lib.tg_compact.restype = c_int
+    lib.tg_compact.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P, P]
+    lib.tg_gated_attn_workspace_size.restype = sz
+    lib.tg_gated_attn_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
+    lib.tg_gated_attn_fwd.restype = c_int
+    lib.tg_gated_attn_fwd.argtypes = [P, P, P, P, P, P, f32, f32, i64, i64, i64, i64, i64, c_int, P, P, P, sz, P]
+    lib.tg_gated_attn_bwd.restype = c_int
+    lib.tg_gated_attn_bwd.argtypes = [P, P, P, P, P, P, f32, f32, P, P, i64, i64, i64, i64, i64, c_int,
+                                      P, P, P, P, P, P, sz, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != TG_OK:
+        lib = load()
+        raise TokenGateError(status, f"{lib.tg_status_string(status).decode()}: {lib.tg_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    if t.dtype == torch.float32:
+        return TG_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def tg_version() -> int:
+    return load().tg_version()
+
+
+def tg_kept_count(N: int, n_forced: int, K: int) -> int:
+    return load().tg_kept_count(N, n_forced, K)
+
+
+def tg_select_topk_workspace_size(B: int, N: int) -> int:
+    return load().tg_select_topk_workspace_size(B, N)
+
+
+def tg_gated_attn_workspace_size(B: int, M: int, Hq: int, Hkv: int, D: int, bwd: bool) -> int:
+    return load().tg_gated_attn_workspace_size(B, M, Hq, Hkv, D, int(bool(bwd)))
+
+
+def tg_gate_score(hidden, w1, w2, forced_keep, scores, gates=None, stream=None):
+    """hidden [B, N, d], w1 [d_ff, d], w2 [d_ff] (bf16 or fp32); forced_keep u8 [B, N] or None;
+    writes scores (and gates) f32 [B, N]."""
+    _contig(hidden, w1, w2, forced_keep, scores, gates)
+    B, N, d = hidden.shape
+    d_ff = w1.shape[0]
+    _check(load().tg_gate_score(_ptr(hidden), _ptr(w1), _ptr(w2), _ptr(forced_keep), B, N, d, d_ff, _dt(hidden),
+                                _ptr(scores), _ptr(gates), _stream(stream)))
+
+
+def tg_select_topk(scores, forced_keep, K, n_forced, kept_idx, kept_count=None, ws=None, stream=None):
+    """scores f32 [B, N]; forced_keep u8 [B, N] or None; writes kept_idx i32 [B, M] (M = tg_kept_count)."""
+    _contig(scores, forced_keep, kept_idx, kept_count)
+    B, N = scores.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().tg_select_topk(_ptr(scores), _ptr(forced_keep), B, N, int(K), int(n_forced), _ptr(kept_idx),
+                                 _ptr(kept_count), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tg_compact(hidden, pos, gates, kept_idx, hidden_out=None, pos_out=None, gates_out=None, stream=None):
+    """hidden [B, N, d]; pos i32 [B, N] or None; gates f32 [B, N] or None; kept_idx i32 [B, M]."""
+    _contig(hidden, pos, gates, kept_idx, hidden_out, pos_out, gates_out)
+    B, N, d = hidden.shape
+    M = kept_idx.shape[1]
+    _check(load().tg_compact(_ptr(hidden), _ptr(pos), _ptr(gates), _ptr(kept_idx), B, N, M, d, _dt(hidden),
+                             _ptr(hidden_out), _ptr(pos_out), _ptr(gates_out), _stream(stream)))
+
+
+def attn_workspace(B, M, Hq, Hkv, D, bwd, device):
+    """A workspace tensor of the size the attention calls need (256-byte aligned by torch's allocator)."""
+    import torch
+
+    n = tg_gated_attn_workspace_size(B, M, Hq, Hkv, D, bwd)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def tg_gated_attn_fwd(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None):
+    """q [B, M, Hq, D], k, v [B, M, Hkv, D] (bf16 or fp32); g f32 [B, M]; gamma f32 [Hq];
+    pos i32 [B, M] or None; writes o [B, M, Hq, D] and lse f32 [B, Hq, M]."""
+    _contig(q, k, v, g, gamma, pos, o, lse, ws)
+    B, M, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().tg_gated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos), float(rope_theta),
+                                    float(tau), B, M, Hq, Hkv, D, _dt(q), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
+                                    _stream(stream)))
+
+
+def tg_gated_attn_bwd(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk, dv, dg, dgamma, ws,
+                      stream=None):
+    """Gradients of tg_gated_attn_fwd; dq, dk, dv, dg, dgamma are f32 outputs, fully overwritten."""
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws)
+    B, M, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(load().tg_gated_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos), float(rope_theta),
+                                    float(tau), _ptr(lse), _ptr(dout), B, M, Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(dg), _ptr(dgamma), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma, tau, rope_theta=1.0e6,
+                       pos=None, select_scores=None, bufs=None, stream=None):
+    """The four forward stages back to back on one stream (no host synchronisation).
+
+    q/k/v are the kept tokens' projections [B, M, H, D].  select_scores, when given,
+    replaces the computed scores as the ranking key (the computed scores and gates
+    are still produced).  bufs: optional dict of preallocated outputs (reused across
+    calls).  Returns the dict of outputs.
+    """
+    import torch
+
+    B, N, d = hidden.shape
+    M = tg_kept_count(N, n_forced, K)
+    dev = hidden.device
+    if bufs is None:
+        bufs = {}
+    Hq, D = q.shape[2], q.shape[3]
+
+    def buf(name, shape, dtype):
+        t = bufs.get(name)
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            bufs[name] = t
+        return t
+
+    scores = buf("scores", (B, N), torch.float32)
+    gates = buf("gates", (B, N), torch.float32)
+    kept = buf("kept_idx", (B, M), torch.int32)
+    h_out = buf("hidden_kept", (B, M, d), hidden.dtype)
+    p_out = buf("pos_kept", (B, M), torch.int32)
+    g_out = buf("g_kept", (B, M), torch.float32)
+    o = buf("o", (B, M, Hq, D), q.dtype)
+    lse = buf("lse", (B, Hq, M), torch.float32)
+    ws = bufs.get("attn_ws")
+    need = tg_gated_attn_workspace_size(B, M, Hq, k.shape[2], D, False)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        bufs["attn_ws"] = ws
+    tg_gate_score(hidden, w1, w2, forced_keep, scores, gates, stream=stream)
+    key = scores if select_scores is None else select_scores
+    tg_select_topk(key, forced_keep, K, n_forced, kept, stream=stream)
+    tg_compact(hidden, pos, gates, kept, h_out, p_out, g_out, stream=stream)
+    tg_gated_attn_fwd(q, k, v, g_out, gamma, p_out, rope_theta, tau, o, lse, ws, stream=stream)
+    return bufs

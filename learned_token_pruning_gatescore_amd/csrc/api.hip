@@ -1,0 +1,248 @@
+// api.hip -- the C ABI of libtokengate: argument validation, workspace
+// carving and kernel launches.  Every check that the host can make happens
+// before the first HIP call, so invalid calls never touch the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/tokengate.h"
+
+namespace tg {
+hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced, int64_t T,
+                             int d, int d_ff, bool bf16, float *scores, float *gates, hipStream_t s);
+hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_t B, int64_t N, int64_t K,
+                              int64_t M_alloc, int32_t *kept, int32_t *kept_count, hipStream_t s);
+hipError_t launch_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept,
+                          int64_t B, int64_t N, int64_t M, int64_t row_bytes, void *hidden_out, int32_t *pos_out,
+                          float *gates_out, hipStream_t s);
+hipError_t launch_rope_table(const int32_t *pos, int64_t rows, int D, double theta, float2 *cs, hipStream_t s);
+hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                           const float2 *cs, float tau, int B, int M, int Hq, int Hkv, int D, bool bf16, void *o,
+                           float *lse, hipStream_t s);
+hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                           const float2 *cs, float tau, const float *lse, const void *dout, int B, int M, int Hq,
+                           int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg, float *dgamma,
+                           float *ws_delta, float *ws_colsum, hipStream_t s);
+}  // namespace tg
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tg_status fail(tg_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tg_status ok() {
+  g_err[0] = '\0';
+  return TG_OK;
+}
+
+tg_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(TG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxInt = 0x7FFFFFFF;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Attention workspace: [rope cos/sin table B*M*D/2 float2] [delta B*Hq*M f32] [colsum B*Hq*M f32]
+size_t attn_ws(int64_t B, int64_t M, int64_t Hq, int64_t D, int bwd) {
+  size_t n = round_up((size_t)(B * M * (D / 2)) * sizeof(float2));
+  if (bwd) n += 2 * round_up((size_t)(B * Hq * M) * sizeof(float));
+  return n;
+}
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+tg_status check_attn(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                     float tau, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt) {
+  REQUIRE(q && k && v && g && gamma, TG_ERR_INVALID_ARG, "q, k, v, g and gamma are required");
+  REQUIRE(B >= 0 && M >= 0, TG_ERR_INVALID_ARG, "B and M must be >= 0 (B=%lld M=%lld)", (long long)B, (long long)M);
+  REQUIRE(Hq > 0 && Hkv > 0 && Hq % Hkv == 0, TG_ERR_INVALID_ARG, "Hq (%lld) must be a positive multiple of Hkv (%lld)",
+          (long long)Hq, (long long)Hkv);
+  REQUIRE(dt == TG_F32 || dt == TG_BF16, TG_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  REQUIRE(std::isfinite(tau) && tau > 0.f, TG_ERR_INVALID_ARG, "tau must be finite and > 0");
+  REQUIRE(B * M <= kMaxInt && B * M * Hq <= kMaxInt / 4, TG_ERR_UNSUPPORTED, "problem too large");
+  if (dt == TG_BF16) {
+    REQUIRE(D == 64 || D == 128, TG_ERR_UNSUPPORTED, "bf16 attention needs D in {64, 128} (got %lld)", (long long)D);
+    const int64_t G = Hq / Hkv;
+    REQUIRE(G <= 128 && (G & (G - 1)) == 0, TG_ERR_UNSUPPORTED, "bf16 attention needs Hq/Hkv a power of two <= 128");
+  } else {
+    REQUIRE(D >= 2 && D <= 128 && D % 2 == 0, TG_ERR_UNSUPPORTED, "f32 attention needs even D <= 128");
+  }
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g) && aligned16(gamma), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tg_version(void) { return 100; }
+
+const char *tg_status_string(tg_status s) {
+  switch (s) {
+    case TG_OK: return "ok";
+    case TG_ERR_INVALID_ARG: return "invalid argument";
+    case TG_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TG_ERR_WORKSPACE: return "workspace missing or too small";
+    case TG_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *tg_last_error(void) { return g_err; }
+
+int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K) {
+  if (N < 0 || K < 0 || n_forced < 0 || n_forced > N) return -1;
+  const int64_t nP = N - n_forced;
+  return n_forced + (K < nP ? K : nP);
+}
+
+tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced_keep, int64_t B,
+                        int64_t N, int64_t d, int64_t d_ff, tg_dtype dt, float *scores, float *gates,
+                        void *stream) {
+  REQUIRE(hidden && w1 && w2 && scores, TG_ERR_INVALID_ARG, "hidden, w1, w2 and scores are required");
+  REQUIRE(B >= 0 && N >= 0, TG_ERR_INVALID_ARG, "B and N must be >= 0");
+  REQUIRE(d > 0 && d_ff > 0, TG_ERR_INVALID_ARG, "d and d_ff must be > 0 (d=%lld d_ff=%lld)", (long long)d,
+          (long long)d_ff);
+  REQUIRE(dt == TG_F32 || dt == TG_BF16, TG_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  REQUIRE(d <= 65536 && d_ff <= 65536 && B * N <= kMaxInt * 16, TG_ERR_UNSUPPORTED, "problem too large");
+  if (dt == TG_BF16)
+    REQUIRE(d % 32 == 0, TG_ERR_UNSUPPORTED, "bf16 scoring needs d %% 32 == 0 (d=%lld)", (long long)d);
+  else
+    REQUIRE(d % 4 == 0 && d <= 8192, TG_ERR_UNSUPPORTED, "f32 scoring needs d %% 4 == 0 and d <= 8192");
+  REQUIRE(aligned16(hidden) && aligned16(w1) && aligned16(w2) && aligned16(scores) && aligned16(gates),
+          TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_gate_score(hidden, w1, w2, forced_keep, B * N, (int)d, (int)d_ff, dt == TG_BF16,
+                                          scores, gates, (hipStream_t)stream),
+                    "tg_gate_score launch");
+}
+
+size_t tg_select_topk_workspace_size(int64_t B, int64_t N) {
+  (void)B;
+  (void)N;
+  return 0;
+}
+
+tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t N, int64_t K,
+                         int64_t n_forced, int32_t *kept_idx, int32_t *kept_count, void *ws, size_t ws_bytes,
+                         void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  REQUIRE(B >= 0 && N >= 0, TG_ERR_INVALID_ARG, "B and N must be >= 0");
+  REQUIRE(K >= 0, TG_ERR_INVALID_ARG, "K must be >= 0 (got %lld)", (long long)K);
+  REQUIRE(n_forced >= 0 && n_forced <= N, TG_ERR_INVALID_ARG, "need 0 <= n_forced <= N (n_forced=%lld N=%lld)",
+          (long long)n_forced, (long long)N);
+  REQUIRE(forced_keep || n_forced == 0, TG_ERR_INVALID_ARG, "forced_keep is NULL but n_forced > 0");
+  REQUIRE(N <= kMaxInt && B <= 65535 * 1024, TG_ERR_UNSUPPORTED, "N must fit in int32");
+  const int64_t M = tg_kept_count(N, n_forced, K);
+  if (B * N > 0) REQUIRE(scores && kept_idx, TG_ERR_INVALID_ARG, "scores and kept_idx are required");
+  REQUIRE(aligned16(scores) && aligned16(kept_idx), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B == 0) return ok();
+  return hip_status(tg::launch_select_topk(scores, forced_keep, B, N, K, M, kept_idx, kept_count,
+                                           (hipStream_t)stream),
+                    "tg_select_topk launch");
+}
+
+tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept_idx,
+                     int64_t B, int64_t N, int64_t M, int64_t d, tg_dtype dt, void *hidden_out, int32_t *pos_out,
+                     float *gates_out, void *stream) {
+  REQUIRE(B >= 0 && N >= 0 && M >= 0, TG_ERR_INVALID_ARG, "B, N and M must be >= 0");
+  REQUIRE(dt == TG_F32 || dt == TG_BF16, TG_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  REQUIRE(B * M == 0 || kept_idx, TG_ERR_INVALID_ARG, "kept_idx is required");
+  REQUIRE(!hidden_out || (hidden && d > 0), TG_ERR_INVALID_ARG, "hidden_out needs hidden and d > 0");
+  REQUIRE(!gates_out || gates, TG_ERR_INVALID_ARG, "gates_out needs gates");
+  const int64_t esz = dt == TG_BF16 ? 2 : 4;
+  const int64_t row_bytes = hidden_out ? d * esz : 0;
+  REQUIRE(!hidden_out || row_bytes % 16 == 0, TG_ERR_UNSUPPORTED, "rows must be a multiple of 16 bytes");
+  REQUIRE(B * M <= kMaxInt * 4, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(aligned16(hidden) && aligned16(hidden_out) && aligned16(kept_idx), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  if (B * M == 0) return ok();
+  return hip_status(tg::launch_compact(hidden, pos, gates, kept_idx, B, N, M, row_bytes, hidden_out, pos_out,
+                                       gates_out, (hipStream_t)stream),
+                    "tg_compact launch");
+}
+
+size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, int bwd) {
+  (void)Hkv;
+  if (B < 0 || M < 0 || Hq <= 0 || D <= 0) return 0;
+  return attn_ws(B, M, Hq, D, bwd);
+}
+
+tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                            const int32_t *pos, float rope_theta, float tau, int64_t B, int64_t M, int64_t Hq,
+                            int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse, void *ws, size_t ws_bytes,
+                            void *stream) {
+  tg_status st = check_attn(q, k, v, g, gamma, tau, B, M, Hq, Hkv, D, dt);
+  if (st != TG_OK) return st;
+  REQUIRE(o, TG_ERR_INVALID_ARG, "o is required");
+  REQUIRE(aligned16(o) && aligned16(lse), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
+  const size_t need = pos ? attn_ws(B, M, Hq, D, 0) : 0;
+  REQUIRE(ws_bytes >= need && (need == 0 || ws), TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+          ws_bytes);
+  REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (B * M == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  float2 *cs = nullptr;
+  if (pos) {
+    cs = (float2 *)ws;
+    hipError_t e = tg::launch_rope_table(pos, B * M, (int)D, (double)rope_theta, cs, s);
+    if (e != hipSuccess) return hip_status(e, "rope table launch");
+  }
+  return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, cs, tau, (int)B, (int)M, (int)Hq, (int)Hkv, (int)D,
+                                        dt == TG_BF16, o, lse, s),
+                    "tg_gated_attn_fwd launch");
+}
+
+tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                            const int32_t *pos, float rope_theta, float tau, const float *lse, const void *dout,
+                            int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq,
+                            float *dk, float *dv, float *dg, float *dgamma, void *ws, size_t ws_bytes,
+                            void *stream) {
+  tg_status st = check_attn(q, k, v, g, gamma, tau, B, M, Hq, Hkv, D, dt);
+  if (st != TG_OK) return st;
+  REQUIRE(lse && dout && dq && dk && dv && dg && dgamma, TG_ERR_INVALID_ARG,
+          "lse, dout, dq, dk, dv, dg and dgamma are required");
+  REQUIRE(aligned16(lse) && aligned16(dout) && aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(dg) &&
+              aligned16(dgamma),
+          TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
+  const size_t need = attn_ws(B, M, Hq, D, 1);
+  REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  char *w = (char *)ws;
+  float2 *cs = pos ? (float2 *)w : nullptr;
+  w += round_up((size_t)(B * M * (D / 2)) * sizeof(float2));
+  float *delta = (float *)w;
+  w += round_up((size_t)(B * Hq * M) * sizeof(float));
+  float *colsum = (float *)w;
+  if (pos && B * M > 0) {
+    hipError_t e = tg::launch_rope_table(pos, B * M, (int)D, (double)rope_theta, cs, s);
+    if (e != hipSuccess) return hip_status(e, "rope table launch");
+  }
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, cs, tau, lse, dout, (int)B, (int)M, (int)Hq, (int)Hkv,
+                                        (int)D, dt == TG_BF16, dq, dk, dv, dg, dgamma, delta, colsum, s),
+                    "tg_gated_attn_bwd launch");
+}
+
+}  // extern "C"

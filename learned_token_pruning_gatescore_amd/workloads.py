@@ -167,9 +167,8 @@ def attn_inputs(w: Workload, M: int, with_grad: bool = False, seed_offset: int =
     q ~ N(0,1) [B, M, Hq, D]; k, v ~ N(0,1) [B, M, Hkv, D] (bf16 or fp32 per the
     workload); gamma ~ U(0.5, 1.5) [Hq]; g = 1/(1+exp(-z)), z ~ N(0,1), float32
     [B, M] (a distribution of gate values in (0, 1)); positions int32 [B, M]:
-    sorted distinct draws from [0, N) when the workload fixes M, else arange(M)
-    (replaced by the compacted positions in the full path); dout ~ N(0,1) like q
-    when with_grad.
+    sorted distinct draws from [0, max(N, M)), the shape of the original positions
+    that compaction hands to attention; dout ~ N(0,1) like q when with_grad.
     """
     rs = _streams(w.seed * 7919 + 17 + seed_offset, ["q", "k", "v", "gamma", "g", "pos", "dout"])
     q = rs["q"].standard_normal((w.B, M, w.Hq, w.D), dtype=np.float32)
@@ -178,10 +177,7 @@ def attn_inputs(w: Workload, M: int, with_grad: bool = False, seed_offset: int =
     gamma = rs["gamma"].uniform(0.5, 1.5, w.Hq).astype(np.float32)
     z = rs["g"].standard_normal((w.B, M)).astype(np.float64)
     g = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
-    if w.M_fixed:
-        pos = np.stack([np.sort(rs["pos"].choice(w.N, M, replace=False)) for _ in range(w.B)]).astype(np.int32)
-    else:
-        pos = np.broadcast_to(np.arange(M, dtype=np.int32), (w.B, M)).copy()
+    pos = np.stack([np.sort(rs["pos"].choice(max(w.N, M), M, replace=False)) for _ in range(w.B)]).astype(np.int32)
     out = dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype), gamma=gamma, g=g, pos=pos)
     if with_grad:
         out["dout"] = _store(rs["dout"].standard_normal((w.B, M, w.Hq, w.D), dtype=np.float32), w.dtype)

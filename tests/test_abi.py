@@ -1,0 +1,106 @@
+"""The C-ABI library loads and exports what include/tokengate.h declares; host-side
+argument checks return their status before any device call (CPU only, no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+
+
+def _lib():
+    import learned_token_pruning_gatescore_amd as tg
+
+    if not os.path.exists(tg.library_path()):
+        pytest.skip("libtokengate.so not built")
+    return tg.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (tg_[a-z_]+)\b", out))
+    assert set(names) <= exported
+    # nothing but the declared C entry points leaks as tg_* symbols
+    assert exported <= set(names)
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.tg_version() >= 100
+    for s in range(5):
+        assert lib.tg_status_string(s)
+    assert lib.tg_kept_count(32768, 128, 2048) == 2176
+    assert lib.tg_kept_count(100, 10, 1000) == 100
+    assert lib.tg_kept_count(100, 10, 0) == 10
+    assert lib.tg_kept_count(100, 101, 5) == -1
+    assert lib.tg_kept_count(100, 10, -1) == -1
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+MIS = ctypes.c_void_p(0x10008)    # misaligned
+
+
+def test_gate_score_validation():
+    lib = _lib()
+    st = lib.tg_gate_score(None, FAKE, FAKE, None, 1, 10, 32, 16, 1, FAKE, None, None)
+    assert st == 1 and b"required" in lib.tg_last_error()
+    assert lib.tg_gate_score(FAKE, FAKE, FAKE, None, 1, 10, 0, 16, 1, FAKE, None, None) == 1
+    assert lib.tg_gate_score(FAKE, FAKE, FAKE, None, 1, 10, 48, 16, 1, FAKE, None, None) == 2  # bf16 d % 32
+    assert lib.tg_gate_score(FAKE, FAKE, FAKE, None, 1, 10, 32, 16, 7, FAKE, None, None) == 1  # dtype
+    assert lib.tg_gate_score(MIS, FAKE, FAKE, None, 1, 10, 32, 16, 1, FAKE, None, None) == 1  # alignment
+
+
+def test_select_validation():
+    lib = _lib()
+    assert lib.tg_select_topk(FAKE, FAKE, 1, 100, -1, 0, FAKE, None, None, 0, None) == 1   # K < 0
+    assert lib.tg_select_topk(FAKE, FAKE, 1, 100, 5, 101, FAKE, None, None, 0, None) == 1  # n_forced > N
+    assert lib.tg_select_topk(FAKE, None, 1, 100, 5, 3, FAKE, None, None, 0, None) == 1    # mask missing
+    assert lib.tg_select_topk(None, None, 1, 100, 5, 0, FAKE, None, None, 0, None) == 1    # scores missing
+    assert lib.tg_select_topk(FAKE, None, 0, 100, 5, 0, FAKE, None, None, 0, None) == 0    # B = 0: nothing to do
+
+
+def test_compact_validation():
+    lib = _lib()
+    assert lib.tg_compact(FAKE, None, None, None, 1, 10, 4, 64, 1, FAKE, None, None, None) == 1     # kept_idx
+    assert lib.tg_compact(FAKE, None, None, FAKE, 1, 10, 4, 64, 1, FAKE, None, FAKE, None) == 1     # gates_out w/o gates
+    assert lib.tg_compact(FAKE, None, None, FAKE, 1, 10, 4, 4, 1, FAKE, None, None, None) == 2      # 8-byte rows
+    assert lib.tg_compact(FAKE, None, None, FAKE, 1, 10, 0, 64, 1, FAKE, None, None, None) == 0     # M = 0
+
+
+def test_attn_validation():
+    lib = _lib()
+    f = lib.tg_gated_attn_fwd
+    args = lambda **kw: [kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("pos", None), 1e6, kw.get("tau", 1.0),
+                         1, 100, kw.get("Hq", 16), kw.get("Hkv", 8), kw.get("D", 128), kw.get("dt", 1), FAKE, None,
+                         kw.get("ws", None), kw.get("wsb", 0), None]
+    assert f(*args(q=None)) == 1
+    assert f(*args(Hq=12, Hkv=8)) == 1          # Hq % Hkv
+    assert f(*args(D=96)) == 2                  # bf16 D
+    assert f(*args(Hq=24, Hkv=8)) == 2          # group of 3
+    assert f(*args(tau=0.0)) == 1
+    assert f(*args(pos=FAKE)) == 3              # RoPE table needs a workspace
+    need = lib.tg_gated_attn_workspace_size(1, 100, 16, 8, 128, 0)
+    assert need >= 100 * 64 * 8
+    assert f(*args(pos=FAKE, ws=FAKE, wsb=need - 1)) == 3
+    assert f(*args(q=MIS)) == 1
+    b = lib.tg_gated_attn_bwd
+    # missing lse
+    assert b(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, FAKE, 1, 100, 16, 8, 128, 1,
+             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    # workspace too small
+    assert b(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, FAKE, FAKE, 1, 100, 16, 8, 128, 1,
+             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3

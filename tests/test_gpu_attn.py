@@ -1,0 +1,201 @@
+"""GPU parity of token-gated attention (forward and backward) against the CPU oracle.
+
+Tolerances: max-abs 2e-2 in bf16 and 1e-4 in fp32 for o and every gradient;
+lse within the same bounds.  The oracle rounds the rotated q and k to bf16 for
+bf16 inputs, the precision the matrix cores consume.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from learned_token_pruning_gatescore_amd import workloads as wl
+from tests._gpu import assert_maxabs, dev_tensor, device, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(B, M, Hq, Hkv, D, dtype="bf16", tau=1.0, seed=21):
+    return wl.Workload("attn", seed, B=B, N=max(4 * M, 64), n_forced=0, d=0, d_ff=0, Ks=(M,), Hq=Hq, Hkv=Hkv, D=D,
+                       tau=tau, dtype=dtype, rope=True, M_fixed=M)
+
+
+def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, seed_offset=0):
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    dev = device()
+    a = wl.attn_inputs(w, M, with_grad=grad, seed_offset=seed_offset)
+    if g_override is not None:
+        a["g"] = g_override
+    q, k, v = (dev_tensor(a[n], w.dtype, dev) for n in ("q", "k", "v"))
+    g = torch.from_numpy(a["g"]).to(dev)
+    gamma = torch.from_numpy(a["gamma"]).to(dev)
+    pos = torch.from_numpy(a["pos"]).to(dev) if rope else None
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.Hq, M), float("nan"), device=dev)
+    ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, True, dev)
+    say("attn_fwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "rope" if rope else "no-rope")
+    tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, theta, w.tau, o, lse, ws)
+    torch.cuda.synchronize()
+    out = dict(a=a, q=q, k=k, v=v, g=g, gamma=gamma, pos=pos, o=o, lse=lse, ws=ws, theta=theta)
+    return out
+
+
+def _oracle_fwd(w, r, rows=None, rope=True):
+    a = r["a"]
+    f = lambda x: wl.as_float(x, w.dtype)
+    return oracle.attn_fwd(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], pos=a["pos"] if rope else None,
+                           theta=r["theta"], tau=w.tau, round_bf16=(w.dtype == "bf16"), rows=rows)
+
+
+def _tol(w):
+    return 2e-2 if w.dtype == "bf16" else 1e-4
+
+
+def test_fwd_tiny_f32():
+    w = wl.WORKLOADS["tiny_f32"]
+    r = _run_fwd(w, 96, rope=False)
+    o_ref, l_ref = _oracle_fwd(w, r, rope=False)
+    assert_maxabs(to_np(r["o"]), o_ref, 1e-4, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 1e-4, "lse")
+
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,D,rope", [
+    (1, 1, 2, 1, 128, True), (1, 63, 4, 4, 64, False), (2, 100, 4, 2, 128, True), (1, 257, 8, 2, 128, True),
+    (2, 130, 16, 4, 64, True), (1, 200, 8, 1, 128, False), (1, 333, 16, 16, 128, True)])
+def test_fwd_bf16_shapes(B, M, Hq, Hkv, D, rope):
+    w = _wl(B, M, Hq, Hkv, D, tau=1.3)
+    r = _run_fwd(w, M, rope=rope)
+    o_ref, l_ref = _oracle_fwd(w, r, rope=rope)
+    assert_maxabs(to_np(r["o"]), o_ref, 2e-2, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+def test_fwd_f32_rope_gqa():
+    w = _wl(2, 70, 6, 2, 32, dtype="f32", tau=0.9)
+    r = _run_fwd(w, 70, rope=True, theta=1e4)
+    o_ref, l_ref = _oracle_fwd(w, r)
+    assert_maxabs(to_np(r["o"]), o_ref, 1e-4, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 1e-4, "lse")
+
+
+def test_fwd_zero_gate_rows():
+    w = _wl(1, 150, 4, 2, 128)
+    g = wl.attn_inputs(w, 150)["g"].copy()
+    g[0, 0] = 0.0      # row 0 sees nothing: o = 0, lse = -inf
+    g[0, 70:80] = 0.0  # masked keys inside the sequence
+    r = _run_fwd(w, 150, g_override=g)
+    o_ref, l_ref = _oracle_fwd(w, r)
+    o = to_np(r["o"])
+    assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(to_np(r["lse"])[0, :, 0]))
+    assert_maxabs(o, o_ref, 2e-2, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+@pytest.mark.parametrize("name,K", [("qwen3_8k", 1024), ("qwen3_32k", 2048)])
+def test_fwd_full_size(name, K):
+    w = wl.WORKLOADS[name]
+    M = w.M(K)
+    r = _run_fwd(w, M)
+    o_ref, l_ref = _oracle_fwd(w, r)
+    assert_maxabs(to_np(r["o"]), o_ref, 2e-2, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+@pytest.mark.parametrize("K", [256, 1024, 4096, 16384])
+def test_fwd_sweep_128k_sampled(K):
+    w = wl.WORKLOADS["sweep_128k"]
+    M = w.M(K)
+    r = _run_fwd(w, M)
+    rng = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, M - 1], rng.choice(M, min(M, 48), replace=False)]))
+    o_ref, l_ref = _oracle_fwd(w, r, rows=rows)
+    assert_maxabs(to_np(r["o"])[0, rows], o_ref[0, rows], 2e-2, "o")
+    assert_maxabs(to_np(r["lse"])[0][:, rows], l_ref[0][:, rows], 2e-2, "lse")
+
+
+def test_fwd_deterministic():
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    w = wl.WORKLOADS["qwen3_8k"]
+    r = _run_fwd(w, 1088)
+    o1 = r["o"].clone()
+    tg.tg_gated_attn_fwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], r["theta"], w.tau, r["o"], r["lse"],
+                         r["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), r["o"].view(torch.int16))
+
+
+def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA):
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    r = _run_fwd(w, M, rope=rope, theta=theta, grad=True)
+    dev = r["q"].device
+    dout = dev_tensor(r["a"]["dout"], w.dtype, dev)
+    dq = torch.full(r["q"].shape, float("nan"), device=dev)
+    dk = torch.full(r["k"].shape, float("nan"), device=dev)
+    dv = torch.full(r["v"].shape, float("nan"), device=dev)
+    dg = torch.full(r["g"].shape, float("nan"), device=dev)
+    dgam = torch.full(r["gamma"].shape, float("nan"), device=dev)
+    say("attn_bwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D)
+    tg.tg_gated_attn_bwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], theta, w.tau, r["lse"], dout, dq, dk,
+                         dv, dg, dgam, r["ws"])
+    torch.cuda.synchronize()
+    r.update(dout=dout, dq=dq, dk=dk, dv=dv, dg=dg, dgamma=dgam)
+    return r
+
+
+def _check_bwd(w, r, rope=True):
+    a = r["a"]
+    f = lambda x: wl.as_float(x, w.dtype)
+    ref = oracle.attn_bwd(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], f(a["dout"]),
+                          pos=a["pos"] if rope else None, theta=r["theta"], tau=w.tau, round_bf16=(w.dtype == "bf16"))
+    tol = _tol(w)
+    errs = {}
+    for name, got, rf in zip(("dq", "dk", "dv", "dg", "dgamma"), (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"]), ref):
+        errs[name] = assert_maxabs(to_np(got), rf, tol, name)
+    return errs
+
+
+def test_bwd_tiny_f32():
+    w = wl.WORKLOADS["tiny_f32"]
+    r = _run_bwd(w, 96, rope=False)
+    _check_bwd(w, r, rope=False)
+
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,D,rope", [
+    (1, 1, 2, 1, 128, True), (2, 100, 4, 2, 128, True), (1, 257, 8, 2, 128, False), (1, 190, 4, 4, 64, True),
+    (1, 150, 8, 1, 128, True)])
+def test_bwd_bf16_shapes(B, M, Hq, Hkv, D, rope):
+    w = _wl(B, M, Hq, Hkv, D, tau=1.1)
+    r = _run_bwd(w, M, rope=rope)
+    _check_bwd(w, r, rope=rope)
+
+
+def test_bwd_f32_rope_gqa():
+    w = _wl(1, 80, 4, 2, 64, dtype="f32", tau=1.2)
+    r = _run_bwd(w, 80, rope=True, theta=1e4)
+    _check_bwd(w, r)
+
+
+def test_bwd_train_b4_full():
+    w = wl.WORKLOADS["train_b4"]
+    r = _run_bwd(w, 2048)
+    errs = _check_bwd(w, r)
+    say("train_b4 bwd max-abs errors", errs)
+
+
+def test_bwd_deterministic():
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    w = _wl(2, 300, 16, 8, 128)
+    r = _run_bwd(w, 300)
+    first = [t.clone() for t in (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"])]
+    tg.tg_gated_attn_bwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], r["theta"], w.tau, r["lse"],
+                         r["dout"], r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"], r["ws"])
+    torch.cuda.synchronize()
+    for a, b in zip(first, (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"])):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))

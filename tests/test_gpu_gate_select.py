@@ -1,0 +1,191 @@
+"""GPU parity of scoring, selection and compaction against the CPU oracle.
+
+Selection and compaction must be bit-exact given the same score vector;
+scores and gates within 1e-2 (bf16) / 1e-5 (fp32) of the oracle, relative to
+max(|ref|, rms(ref)).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from learned_token_pruning_gatescore_amd import workloads as wl
+from tests._gpu import assert_scores_close, dev_tensor, device, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _score(w, N=None, sample=None):
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    dev = device()
+    gi = wl.gate_inputs(w, N)
+    h = dev_tensor(gi["hidden"], w.dtype, dev)
+    w1 = dev_tensor(gi["w1"], w.dtype, dev)
+    w2 = dev_tensor(gi["w2"], w.dtype, dev)
+    f = torch.from_numpy(gi["forced"]).to(dev)
+    B, n = gi["forced"].shape
+    scores = torch.full((B, n), float("nan"), device=dev)
+    gates = torch.full((B, n), float("nan"), device=dev)
+    say("gate_score", w.name, B, n, w.d, w.d_ff)
+    tg.tg_gate_score(h, w1, w2, f, scores, gates)
+    torch.cuda.synchronize()
+    hf = wl.as_float(gi["hidden"], w.dtype).reshape(B * n, w.d)
+    idx = np.arange(B * n) if sample is None else sample
+    s_ref, g_ref = oracle.gate_score(hf[idx], wl.as_float(gi["w1"], w.dtype), wl.as_float(gi["w2"], w.dtype),
+                                     gi["forced"].reshape(-1)[idx])
+    return to_np(scores).reshape(-1)[idx], to_np(gates).reshape(-1)[idx], s_ref, g_ref
+
+
+def test_gate_score_tiny_f32():
+    s, g, sr, gr = _score(wl.WORKLOADS["tiny_f32"])
+    assert_scores_close(s, sr, 1e-5)
+    assert_scores_close(g, gr, 1e-5, "gates")
+    assert np.all(g[:32] == 1.0)
+
+
+@pytest.mark.parametrize("N,d,d_ff", [(1000, 256, 96), (77, 64, 512), (300, 128, 640), (4099, 2048, 512)])
+def test_gate_score_bf16_shapes(N, d, d_ff):
+    w = wl.Workload("shape", 11, B=2, N=N, n_forced=5, d=d, d_ff=d_ff, Ks=(1,), Hq=1, Hkv=1, D=64, tau=1.0,
+                    dtype="bf16", rope=False)
+    s, g, sr, gr = _score(w)
+    assert_scores_close(s, sr, 1e-2)
+    assert_scores_close(g, gr, 1e-2, "gates")
+
+
+def test_gate_score_qwen3_8k_full():
+    s, g, sr, gr = _score(wl.WORKLOADS["qwen3_8k"])
+    assert_scores_close(s, sr, 1e-2)
+    assert_scores_close(g, gr, 1e-2, "gates")
+
+
+def test_gate_score_qwen3_32k_sampled():
+    w = wl.WORKLOADS["qwen3_32k"]
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([np.arange(256), np.arange(w.N - 300, w.N),
+                                       rng.choice(w.N, 3000, replace=False)]))
+    s, g, sr, gr = _score(w, sample=sample)
+    assert_scores_close(s, sr, 1e-2)
+    assert_scores_close(g, gr, 1e-2, "gates")
+
+
+def _select(scores, forced, K, n_forced, M=None):
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    dev = device()
+    B, N = scores.shape
+    Mm = tg.tg_kept_count(N, n_forced, K)
+    kept = torch.full((B, max(Mm, 1)), -7, dtype=torch.int32, device=dev)[:, :Mm].contiguous()
+    cnt = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    say("select", B, N, K, n_forced)
+    tg.tg_select_topk(torch.from_numpy(np.ascontiguousarray(scores)).to(dev),
+                      None if forced is None else torch.from_numpy(forced).to(dev), K, n_forced, kept, cnt)
+    torch.cuda.synchronize()
+    ref, rc = oracle.select_topk(scores, forced, K, M=Mm)
+    return kept.cpu().numpy(), cnt.cpu().numpy(), ref, rc
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_select_random_tie_heavy(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 9000))
+    pool = np.concatenate([rng.standard_normal(6).astype(np.float32),
+                           np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-40, -1e-40], np.float32)])
+    scores = pool[rng.integers(0, len(pool), (B, N))].astype(np.float32)
+    if seed % 2:
+        scores = rng.standard_normal((B, N)).astype(np.float32)
+    nF = int(rng.integers(0, min(N, 300) + 1))
+    forced = np.zeros((B, N), np.uint8)
+    for b in range(B):
+        forced[b, rng.choice(N, nF, replace=False)] = 1
+    K = int(rng.integers(0, N + 2))
+    got, cnt, ref, rc = _select(scores, forced, K, nF)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(cnt, rc)
+
+
+def test_select_edge_cases():
+    rng = np.random.default_rng(7)
+    N = 5000
+    s = rng.standard_normal((1, N)).astype(np.float32)
+    f = np.zeros((1, N), np.uint8)
+    f[0, :64] = 1
+    for K in (0, 1, 4935, 4936, 4937, 10**6):
+        got, cnt, ref, rc = _select(s, f, K, 64)
+        np.testing.assert_array_equal(got, ref)
+    # no forced mask at all
+    got, _, ref, _ = _select(s, None, 100, 0)
+    np.testing.assert_array_equal(got, ref)
+    # all equal (zero-initialised scorer): first K documents
+    z = np.zeros((2, N), np.float32)
+    got, _, ref, _ = _select(z, np.repeat(f, 2, 0), 333, 64)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(got[0], np.arange(64 + 333))
+    # all NaN document scores
+    nan = np.full((1, N), np.nan, np.float32)
+    got, _, ref, _ = _select(nan, f, 10, 64)
+    np.testing.assert_array_equal(got, ref)
+    # forced count differs from n_forced: true count reported, row padded with -1
+    f2 = np.zeros((1, N), np.uint8)
+    f2[0, [1, 500, 4999]] = 1
+    got, cnt, ref, rc = _select(s, f2, 20, 10)
+    np.testing.assert_array_equal(got, ref)
+    assert cnt[0] == 23 and np.all(got[0, 23:] == -1)
+    # N = 1
+    got, _, ref, _ = _select(np.array([[3.0]], np.float32), None, 1, 0)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_select_clustered_32k():
+    w = wl.WORKLOADS["qwen3_32k"]
+    s = wl.clustered_scores(w)
+    f = wl.forced_mask(w)
+    got, cnt, ref, rc = _select(s, f, 2048, 128)
+    np.testing.assert_array_equal(got, ref)
+    assert got.shape == (1, 2176) and cnt[0] == 2176
+
+
+@pytest.mark.parametrize("K", [256, 1024, 4096, 16384])
+def test_select_sweep_128k(K):
+    w = wl.WORKLOADS["sweep_128k"]
+    rng = np.random.default_rng(K)
+    s = wl.bf16_to_f32(wl.bf16_bits(rng.standard_normal((1, w.N)).astype(np.float32)))  # tie-rich grid
+    f = wl.forced_mask(w)
+    got, cnt, ref, rc = _select(s, f, K, w.n_forced)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 2048), ("f32", 256), ("bf16", 8)])
+def test_compact_bit_exact(dtype, d):
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    dev = device()
+    rng = np.random.default_rng(5)
+    B, N, M = 2, 3000, 700
+    raw = rng.integers(0, 2**16, (B, N, d), dtype=np.uint16) if dtype == "bf16" else \
+        rng.standard_normal((B, N, d)).astype(np.float32)
+    pos = rng.integers(0, 10**6, (B, N)).astype(np.int32)
+    gates = rng.random((B, N)).astype(np.float32)
+    kept = np.stack([np.sort(rng.choice(N, M, replace=False)) for _ in range(B)]).astype(np.int32)
+    kept[1, -5:] = -1
+    h = dev_tensor(raw, dtype, dev)
+    ho = torch.empty((B, M, d), dtype=h.dtype, device=dev)
+    po = torch.empty((B, M), dtype=torch.int32, device=dev)
+    go = torch.empty((B, M), dtype=torch.float32, device=dev)
+    say("compact", dtype, B, N, M, d)
+    tg.tg_compact(h, torch.from_numpy(pos).to(dev), torch.from_numpy(gates).to(dev), torch.from_numpy(kept).to(dev),
+                  ho, po, go)
+    torch.cuda.synchronize()
+    rh, rp, rg = oracle.compact(raw, pos, gates, kept)
+    got_h = ho.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else ho.cpu().numpy()
+    np.testing.assert_array_equal(got_h.view(np.uint8), rh.view(np.uint8))
+    np.testing.assert_array_equal(po.cpu().numpy(), rp)
+    np.testing.assert_array_equal(go.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+    # pos = None: positions are the indices
+    tg.tg_compact(h, None, None, torch.from_numpy(kept).to(dev), None, po, None)
+    torch.cuda.synchronize()
+    _, rp2, _ = oracle.compact(raw, None, None, kept)
+    np.testing.assert_array_equal(po.cpu().numpy(), rp2)
