@@ -1,0 +1,334 @@
+"""Benchmark of the TokenGate gate-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+
+One step = the whole prefill path of one gate layer on one batch of synthetic
+input, back to back on one HIP stream with no host synchronisation:
+    tg_gate_score -> tg_select_topk -> tg_compact -> tg_gated_attn_fwd
+on the long-context workload (batch 1, N = 32768 context tokens, 128 scaffold
+tokens, K = 2048 kept documents -> M = 2176, hidden 2048, scorer 2048->512->1,
+16/8 heads, head dim 128, bf16, RoPE at the original positions).  Selection
+ranks a drawn score vector with high-score spans over ~5% of the documents.
+
+Inputs are resident in HBM before timing starts.  Three copies of every input
+rotate across steps (3 x 134 MB of hidden states > the 256 MB Infinity Cache),
+so each step reads its hidden states from HBM.  The value is whole-job
+throughput: context tokens per second.  Per-kernel durations come from HIP
+events recorded on the launch stream inside the timed region.
+
+Also measured in the same run (not part of `value`): the training-path
+attention (forward + backward at batch 4, 2048 kept tokens) and the CPU
+oracle on the same workload, timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_BF16 = 2.5e15         # MI355X dense bf16 matrix FLOP/s
+NCOPY = 3
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, M):
+    """Algorithmic FLOPs and bytes per launch of each kernel (what the method must compute / move)."""
+    B, N, d, dff, Hq, Hkv, D = w.B, w.N, w.d, w.d_ff, w.Hq, w.Hkv, w.D
+    esz = 2
+    return {
+        "gate_score": dict(flops=2.0 * B * N * d * dff + 2.0 * B * N * dff,
+                           bytes=B * N * d * esz + dff * d * esz + dff * esz + B * N * (1 + 4 + 4)),
+        "select_topk": dict(flops=0.0, bytes=B * N * (4 + 1) + B * M * 4),
+        "compact": dict(flops=0.0, bytes=2.0 * B * M * d * esz + B * M * (4 + 4 + 4 + 4 + 4)),
+        "attn_fwd": dict(flops=4.0 * B * Hq * D * M * (M + 1) / 2,
+                         bytes=B * M * (2 * Hq + 2 * Hkv) * D * esz + B * M * (4 + 4) + B * Hq * M * 4),
+    }
+
+
+def run_gpu(args):
+    import torch
+
+    import learned_token_pruning_gatescore_amd as tg
+    from learned_token_pruning_gatescore_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    tg.load()
+    w = wl.WORKLOADS["qwen3_32k"]
+    K = w.Ks[0]
+    M = w.M(K)
+    log(f"workload {w.name}: B={w.B} N={w.N} n_forced={w.n_forced} K={K} M={M}")
+    gi = wl.gate_inputs(w)
+    sel = wl.clustered_scores(w)
+    at = wl.attn_inputs(w, M)
+    T = lambda x: wl.to_torch(x, w.dtype, dev)
+    w1, w2 = T(gi["w1"]), T(gi["w2"])
+    forced = torch.from_numpy(gi["forced"]).to(dev)
+    sel_t = torch.from_numpy(sel).to(dev)
+    gamma = torch.from_numpy(at["gamma"]).to(dev)
+    h0, q0, k0, v0 = T(gi["hidden"]), T(at["q"]), T(at["k"]), T(at["v"])
+    copies = [(h0, q0, k0, v0)] + [(h0.clone(), q0.clone(), k0.clone(), v0.clone()) for _ in range(NCOPY - 1)]
+    stream = torch.cuda.current_stream()
+
+    bufs = {}
+    scores = torch.empty((w.B, w.N), device=dev)
+    gates = torch.empty((w.B, w.N), device=dev)
+    kept = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+    hk = torch.empty((w.B, M, w.d), dtype=h0.dtype, device=dev)
+    pk = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+    gk = torch.empty((w.B, M), device=dev)
+    o = torch.empty_like(q0)
+    lse = torch.empty((w.B, w.Hq, M), device=dev)
+    ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
+    names = ["gate_score", "select_topk", "compact", "attn_fwd"]
+
+    def step(i, ev=None):
+        h, q, k, v = copies[i % NCOPY]
+        if ev is not None:
+            ev[0].record(stream)
+        tg.tg_gate_score(h, w1, w2, forced, scores, gates)
+        if ev is not None:
+            ev[1].record(stream)
+        tg.tg_select_topk(sel_t, forced, K, w.n_forced, kept)
+        if ev is not None:
+            ev[2].record(stream)
+        tg.tg_compact(h, None, gates, kept, hk, pk, gk)
+        if ev is not None:
+            ev[3].record(stream)
+        tg.tg_gated_attn_fwd(q, k, v, gk, gamma, pk, wl.ROPE_THETA, w.tau, o, lse, ws)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e-3)
+    step_dev = [e[0].elapsed_time(e[4]) * 1e-3 for e in evs]
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, device path mean {np.mean(step_dev) * 1e6:.1f} us")
+
+    work = algorithmic_work(w, M)
+    kern = {}
+    for n in names:
+        t = float(np.mean(per[n]))
+        wk = work[n]
+        ent = dict(us=t * 1e6, us_min=float(np.min(per[n])) * 1e6, alg_bytes=wk["bytes"], alg_flops=wk["flops"],
+                   hbm_GBps=wk["bytes"] / t / 1e9, hbm_frac=wk["bytes"] / t / PEAK_HBM)
+        if wk["flops"]:
+            ent.update(mfma_TFLOPs=wk["flops"] / t / 1e12, mfma_frac=wk["flops"] / t / PEAK_BF16)
+        kern[n] = ent
+    gate_stage = sum(kern[n]["us"] for n in names[:3]) * 1e-6
+    gate_bytes = sum(work[n]["bytes"] for n in names[:3])
+    summary = dict(
+        gate_stage_us=gate_stage * 1e6, gate_stage_hbm_frac=gate_bytes / gate_stage / PEAK_HBM,
+        gate_stage_bound_frac=(max(work["gate_score"]["flops"] / PEAK_BF16, work["gate_score"]["bytes"] / PEAK_HBM)
+                               + (work["select_topk"]["bytes"] + work["compact"]["bytes"]) / PEAK_HBM) / gate_stage,
+        attn_fwd_mfma_frac=kern["attn_fwd"]["mfma_frac"])
+    # dominant kernel of the step
+    dom = max(names, key=lambda n: kern[n]["us"])
+    if work[dom]["flops"]:
+        roof = dict(kernel=dom, bound="mfma", achieved=kern[dom]["mfma_TFLOPs"], peak=PEAK_BF16 / 1e12,
+                    unit="TFLOP/s", frac=kern[dom]["mfma_frac"], traffic=None)
+    else:
+        roof = dict(kernel=dom, bound="hbm", achieved=kern[dom]["hbm_GBps"], peak=PEAK_HBM / 1e9, unit="GB/s",
+                    frac=kern[dom]["hbm_frac"], traffic=None)
+    traffic = load_traffic(dom)
+    if traffic is not None:
+        roof["traffic"] = traffic
+
+    elapsed = wall
+    res = dict(elapsed=elapsed, step_dev=float(np.mean(step_dev)), kernels=kern, summary=summary, roofline=roof,
+               workload=w, K=K, M=M)
+    if args.copy_calib_mb:
+        nb = args.copy_calib_mb << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nb} bytes read + {nb} bytes written")
+    if args.train_steps:
+        res["training_path"] = run_train(args, tg, wl, dev)
+    # gpu-side data needed by the CPU baseline (the same inputs)
+    res["host_inputs"] = dict(gi=gi, sel=sel, at=at)
+    return res
+
+
+def run_train(args, tg, wl, dev):
+    """Training-path attention: forward + backward at batch 4, 2048 kept tokens (not part of `value`)."""
+    import torch
+
+    w = wl.WORKLOADS["train_b4"]
+    M = w.M_fixed
+    a = wl.attn_inputs(w, M, with_grad=True)
+    T = lambda x: wl.to_torch(x, w.dtype, dev)
+    q, k, v, dout = T(a["q"]), T(a["k"]), T(a["v"]), T(a["dout"])
+    g = torch.from_numpy(a["g"]).to(dev)
+    gamma = torch.from_numpy(a["gamma"]).to(dev)
+    pos = torch.from_numpy(a["pos"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, M), device=dev)
+    dq = torch.empty(q.shape, device=dev)
+    dk = torch.empty(k.shape, device=dev)
+    dv = torch.empty(v.shape, device=dev)
+    dg = torch.empty(g.shape, device=dev)
+    dgam = torch.empty(gamma.shape, device=dev)
+    ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, True, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws)
+        if ev:
+            ev[1].record(stream)
+        tg.tg_gated_attn_bwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, dq, dk, dv, dg, dgam, ws)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.train_steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    ff = 4.0 * w.B * w.Hq * w.D * M * (M + 1) / 2
+    return dict(workload=w.name, B=w.B, M=M, fwd_us=fwd * 1e6, bwd_us=bwd * 1e6,
+                fwd_mfma_frac=ff / fwd / PEAK_BF16, bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16,
+                tokens_per_s=w.B * M / (fwd + bwd))
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (profiles/traffic.json), or None when there is none or the kernel's source has
+    changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        ent = json.load(open(path)).get(kernel)
+        if ent is None:
+            return None
+        src = os.path.join(ROOT, "learned_token_pruning_gatescore_amd", "csrc", ent["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != ent["source_sha256"]:
+            return None
+        return ent["hbm_bytes_per_launch"]
+    except (ValueError, OSError, KeyError):
+        return None
+
+
+def run_cpu_baseline(host, w, K, M):
+    """The oracle as it stands, on this host's cores, over the same workload (all tokens, all rows)."""
+    import oracle
+    from learned_token_pruning_gatescore_amd import workloads as wl
+
+    oracle.build(force=False)
+    gi, sel, at = host["gi"], host["sel"], host["at"]
+    t = {}
+    t0 = time.perf_counter()
+    hf = wl.as_float(gi["hidden"], w.dtype).reshape(w.B * w.N, w.d)
+    s, g = oracle.gate_score(hf, wl.as_float(gi["w1"], w.dtype), wl.as_float(gi["w2"], w.dtype),
+                             gi["forced"].reshape(-1))
+    t["gate_score"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    kept, _ = oracle.select_topk(sel, gi["forced"], K)
+    t["select_topk"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hk, pk, gk = oracle.compact(gi["hidden"], None, g.astype(np.float32).reshape(w.B, w.N), kept)
+    t["compact"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    f = lambda x: wl.as_float(x, w.dtype)
+    oracle.attn_fwd(f(at["q"]), f(at["k"]), f(at["v"]), gk, at["gamma"], pos=pk, theta=wl.ROPE_THETA, tau=w.tau,
+                    round_bf16=True)
+    t["attn_fwd"] = time.perf_counter() - t0
+    total = sum(t.values())
+    return dict(value=w.B * w.N / total, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"full workload once: {w.B * w.N} tokens scored, selected and compacted, attention over all "
+                       f"{M} kept rows x {w.Hq} heads; fp64 plain loops",
+                seconds=t, total_s=total)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--train-steps", type=int, default=10, help="training-path fwd+bwd steps (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
+              f"see DESIGN.md for how the path would shard.", file=sys.stderr)
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py is single-process, single-GPU", file=sys.stderr)
+        sys.exit(2)
+
+    res = run_gpu(args)
+    w, K, M = res["workload"], res["K"], res["M"]
+    ms = res["elapsed"] / args.steps * 1e3
+    value = w.B * w.N * args.steps / res["elapsed"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same workload ...")
+        cpu = run_cpu_baseline(res["host_inputs"], w, K, M)
+        log(f"oracle: {cpu['total_s']:.2f} s on {cpu['cores']} threads")
+    roof = dict(res["roofline"])
+    line = {
+        "metric": "gate-layer prefill tokens/s (N=32K->K=2K, bf16); % of HBM and MFMA peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Qwen3-1.7B-shaped gate layer; drawn clustered selection scores)",
+        "config": {"workload": "long-context gate layer: B=1, N=32768 (128 scaffold), K=2048 -> M=2176, "
+                               "d=2048, scorer 2048->512->1, 16/8 heads, D=128, RoPE theta 1e6, tau=1",
+                   "global_batch": w.B, "seq_len": w.N, "kept": M, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "device_path_us": res["step_dev"] * 1e6,
+        "kernels": res["kernels"],
+        "summary": res["summary"],
+    }
+    if "training_path" in res:
+        line["training_path"] = res["training_path"]
+    if cpu is not None:
+        line["cpu_baseline_stage_s"] = cpu["seconds"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

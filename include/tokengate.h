@@ -131,7 +131,11 @@ tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates,
                      tg_dtype dt, void *hidden_out, int32_t *pos_out, float *gates_out,
                      void *stream);
 
-/* Workspace bytes the attention calls need (bwd = 0: forward, 1: backward). */
+/* Workspace bytes the attention calls need (bwd = 0: forward, 1: backward).
+ * Both attention calls require a workspace of at least this size, 256-byte
+ * aligned: it holds the cos/sin table of the kept positions, the rotated keys,
+ * log2 of the gates and, for the backward, D_i and the per-head column sums
+ * of dS.  Its contents are scratch: nothing is carried between calls. */
 size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
                                     int64_t D, int bwd);
 
@@ -152,7 +156,7 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  *   q [B, M, Hq, D], k, v [B, M, Hkv, D], o [B, M, Hq, D] (dt)
  *   g [B, M] f32 > = 0, gamma [Hq] f32, pos [B, M] i32 or NULL
  *   lse [B, Hq, M] f32 out or NULL (needed by the backward)
- * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8, 16, 32, 64, 128}; q.k and
+ * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q.k and
  * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
  * bf16 for the P.v product.  f32: D <= 128, plain fp32 arithmetic.
  */

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "../../include/tokengate.h"
+#include "tg_attn.h"
 
 namespace tg {
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced, int64_t T,
@@ -18,14 +19,6 @@ hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_
 hipError_t launch_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept,
                           int64_t B, int64_t N, int64_t M, int64_t row_bytes, void *hidden_out, int32_t *pos_out,
                           float *gates_out, hipStream_t s);
-hipError_t launch_rope_table(const int32_t *pos, int64_t rows, int D, double theta, float2 *cs, hipStream_t s);
-hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const float2 *cs, float tau, int B, int M, int Hq, int Hkv, int D, bool bf16, void *o,
-                           float *lse, hipStream_t s);
-hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const float2 *cs, float tau, const float *lse, const void *dout, int B, int M, int Hq,
-                           int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg, float *dgamma,
-                           float *ws_delta, float *ws_colsum, hipStream_t s);
 }  // namespace tg
 
 namespace {
@@ -55,15 +48,6 @@ bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr
 constexpr int64_t kMaxInt = 0x7FFFFFFF;
 constexpr size_t kAlign = 256;
 
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// Attention workspace: [rope cos/sin table B*M*D/2 float2] [delta B*Hq*M f32] [colsum B*Hq*M f32]
-size_t attn_ws(int64_t B, int64_t M, int64_t Hq, int64_t D, int bwd) {
-  size_t n = round_up((size_t)(B * M * (D / 2)) * sizeof(float2));
-  if (bwd) n += 2 * round_up((size_t)(B * Hq * M) * sizeof(float));
-  return n;
-}
-
 #define REQUIRE(cond, st, ...) \
   do {                         \
     if (!(cond)) return fail(st, __VA_ARGS__); \
@@ -81,7 +65,7 @@ tg_status check_attn(const void *q, const void *k, const void *v, const float *g
   if (dt == TG_BF16) {
     REQUIRE(D == 64 || D == 128, TG_ERR_UNSUPPORTED, "bf16 attention needs D in {64, 128} (got %lld)", (long long)D);
     const int64_t G = Hq / Hkv;
-    REQUIRE(G <= 128 && (G & (G - 1)) == 0, TG_ERR_UNSUPPORTED, "bf16 attention needs Hq/Hkv a power of two <= 128");
+    REQUIRE(G <= 8 && (G & (G - 1)) == 0, TG_ERR_UNSUPPORTED, "bf16 attention needs Hq/Hkv in {1, 2, 4, 8}");
   } else {
     REQUIRE(D >= 2 && D <= 128 && D % 2 == 0, TG_ERR_UNSUPPORTED, "f32 attention needs even D <= 128");
   }
@@ -182,9 +166,8 @@ tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates,
 }
 
 size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, int bwd) {
-  (void)Hkv;
-  if (B < 0 || M < 0 || Hq <= 0 || D <= 0) return 0;
-  return attn_ws(B, M, Hq, D, bwd);
+  if (B < 0 || M < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+  return tg::attn_workspace_bytes(B, M, Hq, Hkv, D, bwd != 0);
 }
 
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
@@ -196,20 +179,13 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
   REQUIRE(o, TG_ERR_INVALID_ARG, "o is required");
   REQUIRE(aligned16(o) && aligned16(lse), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
-  const size_t need = pos ? attn_ws(B, M, Hq, D, 0) : 0;
-  REQUIRE(ws_bytes >= need && (need == 0 || ws), TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
-          ws_bytes);
+  const size_t need = tg::attn_workspace_bytes(B, M, Hq, Hkv, D, false);
+  REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (B * M == 0) return ok();
-  hipStream_t s = (hipStream_t)stream;
-  float2 *cs = nullptr;
-  if (pos) {
-    cs = (float2 *)ws;
-    hipError_t e = tg::launch_rope_table(pos, B * M, (int)D, (double)rope_theta, cs, s);
-    if (e != hipSuccess) return hip_status(e, "rope table launch");
-  }
-  return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, cs, tau, (int)B, (int)M, (int)Hq, (int)Hkv, (int)D,
-                                        dt == TG_BF16, o, lse, s),
+  const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
+  return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, (int)B, (int)M, (int)Hq,
+                                        (int)Hkv, (int)D, dt == TG_BF16, o, lse, w, (hipStream_t)stream),
                     "tg_gated_attn_fwd launch");
 }
 
@@ -226,22 +202,13 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
               aligned16(dgamma),
           TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
-  const size_t need = attn_ws(B, M, Hq, D, 1);
+  const size_t need = tg::attn_workspace_bytes(B, M, Hq, Hkv, D, true);
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  char *w = (char *)ws;
-  float2 *cs = pos ? (float2 *)w : nullptr;
-  w += round_up((size_t)(B * M * (D / 2)) * sizeof(float2));
-  float *delta = (float *)w;
-  w += round_up((size_t)(B * Hq * M) * sizeof(float));
-  float *colsum = (float *)w;
-  if (pos && B * M > 0) {
-    hipError_t e = tg::launch_rope_table(pos, B * M, (int)D, (double)rope_theta, cs, s);
-    if (e != hipSuccess) return hip_status(e, "rope table launch");
-  }
-  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, cs, tau, lse, dout, (int)B, (int)M, (int)Hq, (int)Hkv,
-                                        (int)D, dt == TG_BF16, dq, dk, dv, dg, dgamma, delta, colsum, s),
+  const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, lse, dout, (int)B, (int)M,
+                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, dq, dk, dv, dg, dgamma, w,
+                                        (hipStream_t)stream),
                     "tg_gated_attn_bwd launch");
 }
 

@@ -23,6 +23,7 @@
 //   3. dg (per token, fixed head order) and dgamma (one work-group per head,
 //      fixed-shape tree).
 #include "tg_common.h"
+#include "tg_attn.h"
 
 namespace tg {
 
@@ -596,9 +597,15 @@ __global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ c
 }
 
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const float2 *cs, float tau, const float *lse, const void *dout, int B, int M, int Hq,
-                           int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg, float *dgamma,
-                           float *ws_delta, float *ws_colsum, hipStream_t s) {
+                           const int32_t *pos, double theta, float tau, const float *lse, const void *dout, int B,
+                           int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg,
+                           float *dgamma, const AttnWs &w, hipStream_t s) {
+  float *ws_delta = w.delta, *ws_colsum = w.colsum;
+  const float2 *cs = pos ? w.cs : nullptr;
+  if ((int64_t)B * M > 0 && pos) {
+    hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, false, false, w, s);
+    if (e != hipSuccess) return e;
+  }
   const double cd = 1.0 / (sqrt((double)D) * (double)tau);
   const float c = (float)cd, c2 = (float)(cd * 1.4426950408889634);
   if ((int64_t)B * M > 0) {

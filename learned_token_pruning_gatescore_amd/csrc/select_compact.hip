@@ -7,15 +7,15 @@
 // (budget clamped, full-sequence keep mask, hidden states and position ids
 // sliced with the keep indices).
 //
-// Selection is a radix select over a 32-bit order key of the fp32 score:
-// four 8-bit digit passes, each a 256-bin LDS histogram fed by wavefront
-// ballots (lanes holding the same digit are counted with one ballot and one
-// atomic), find the exact key T of the K'-th best prunable token and how many
-// tokens with key == T to take (lowest index first).  A final pass emits the
-// kept indices in ascending order: per 64-token wave slice, ballots of
-// "kept, not tied" and "tied" plus mbcnt give each lane its rank, a
-// single-wave scan over the wave totals gives the slice offsets.  There is no
-// host synchronisation and no global atomics, so the output is deterministic.
+// Selection is a radix select over a 32-bit order key of the fp32 score, one
+// work-group per batch row: three digit passes (12, 10, 10 bits) over an LDS
+// histogram fed through wavefront ballots (lanes holding the first candidate's
+// digit are counted with one ballot and one atomic) find the exact key T of
+// the K'-th best prunable token and how many tokens with key == T to take
+// (lowest index first).  Each thread owns contiguous 32-token segments whose
+// keys stay in LDS; a final pass emits the kept indices in ascending
+// order from one block-wide scan of per-segment counts.  No host
+// synchronisation and no global atomics: the output is deterministic.
 #include "tg_common.h"
 
 namespace tg {
@@ -29,86 +29,176 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
-  // number of set bits of mask below this lane
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+constexpr int SEL_T = 1024;              // threads per batch row
+constexpr int SEL_I = 32;                // tokens per thread per chunk (a contiguous segment)
+constexpr int SEL_CHUNK = SEL_T * SEL_I; // 32768 tokens per chunk (keys resident in LDS)
+constexpr int SEL_W = SEL_T / 64;        // waves per work-group
+
+// Block-wide exclusive scans of two uint32 values over the SEL_W waves.
+__device__ __forceinline__ void block_exscan2(uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb, uint32_t &ta,
+                                              uint32_t &tb, uint32_t *sw, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t xa = a, xb = b;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
+    if (lane >= o) {
+      xa += ya;
+      xb += yb;
+    }
+  }
+  if (lane == 63) {
+    sw[wave] = xa;
+    sw[SEL_W + wave] = xb;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t wa = lane < SEL_W ? sw[lane] : 0u, wb = lane < SEL_W ? sw[SEL_W + lane] : 0u;
+    for (int o = 1; o < SEL_W; o <<= 1) {
+      const uint32_t ya = __shfl_up(wa, o), yb = __shfl_up(wb, o);
+      if (lane >= o) {
+        wa += ya;
+        wb += yb;
+      }
+    }
+    if (lane < SEL_W) {
+      sw[lane] = wa;
+      sw[SEL_W + lane] = wb;
+    }
+  }
+  __syncthreads();
+  ea = (wave ? sw[wave - 1] : 0u) + xa - a;
+  eb = (wave ? sw[SEL_W + wave - 1] : 0u) + xb - b;
+  ta = sw[SEL_W - 1];
+  tb = sw[2 * SEL_W - 1];
+  __syncthreads();
 }
 
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int SEL_ITEMS = 4;  // sub-slices of 1024 tokens per output round
-
-// Adds one to hist[digit] for every lane with `active`, one atomic per
-// distinct digit in the wave (up to 8 rounds, then one atomic per lane).
-__device__ __forceinline__ void ballot_hist_add(uint32_t *hist, bool active, uint32_t digit, int lane) {
-  uint64_t act = __ballot(active);
-  for (int it = 0; act != 0; ++it) {
-    if (it == 8) {
-      if (active) atomicAdd(&hist[digit], 1u);
-      break;
-    }
-    const int leader = __ffsll((unsigned long long)act) - 1;
-    const uint32_t dl = __shfl(digit, leader);
-    const uint64_t same = __ballot(active && digit == dl);
+// Adds one to hist[digit] for each lane with `cand`.  A wavefront ballot first
+// checks whether every candidate lane holds the same digit (a zero-initialised
+// scorer makes every key equal): then one atomic adds the popcount; otherwise
+// each candidate lane adds its own (distinct digits rarely collide on a bank).
+__device__ __forceinline__ void hist_add(uint32_t *hist, bool cand, uint32_t digit, int lane) {
+  const uint64_t act = __ballot(cand);
+  if (act == 0) return;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const uint32_t dl = __shfl(digit, leader);
+  const uint64_t same = __ballot(cand && digit == dl);
+  if (same == act) {
     if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
-    if (active && digit == dl) active = false;
-    act &= ~same;
+  } else if (cand) {
+    atomicAdd(&hist[digit], 1u);
   }
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_topk_kernel(
+// Finds the bin holding the need-th largest candidate.  Bins are scanned from
+// the top; thread t owns BPT consecutive bins of group (SEL_T - 1 - t).  Writes
+// the bin and the remaining need (rank inside the bin) to res[0], res[1].
+template <int BPT>
+__device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t need, uint32_t *res, uint32_t *sw, int tid) {
+  const int g = SEL_T - 1 - tid;
+  uint32_t h[BPT], loc = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    h[j] = hist[g * BPT + (BPT - 1 - j)];  // descending bins
+    loc += h[j];
+  }
+  uint32_t above, dummy, tot, tot2;
+  block_exscan2(loc, 0u, above, dummy, tot, tot2, sw, tid);
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    if (above < need && need <= above + h[j]) {
+      res[0] = (uint32_t)(g * BPT + (BPT - 1 - j));
+      res[1] = need - above;
+    }
+    above += h[j];
+  }
+  __syncthreads();
+}
+
+// One work-group per batch row.  Tokens are processed in 32768-token chunks;
+// thread t owns the contiguous segment [t*32, t*32+32) of a chunk.  The
+// chunk's keys live in LDS as skey[i][t] (conflict-free reads of item i by
+// all threads); with one chunk (N <= 32768) they are loaded once, otherwise
+// each pass reloads the chunk (L2-resident).  Forced / valid bits stay in
+// registers (one bit per item).
+__global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     const float *__restrict__ scores, const uint8_t *__restrict__ forced, int64_t N, int64_t K,
     int64_t M_alloc, int32_t *__restrict__ kept, int32_t *__restrict__ kept_count) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sSuffix[256];
-  __shared__ uint32_t sCnt[SEL_ITEMS * SEL_WAVES];   // packed (keep_nt | tie << 16) per wave slice
-  __shared__ uint32_t sOffK[SEL_ITEMS * SEL_WAVES];
-  __shared__ uint32_t sOffT[SEL_ITEMS * SEL_WAVES];
-  __shared__ int64_t sForced;
-  __shared__ uint32_t sState[4];  // prefix, mask, need, digit
-  __shared__ int64_t sRun[2];     // running kept-not-tied, running tied
+  __shared__ uint32_t skey[SEL_I * SEL_T];
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t sw[2 * SEL_W];
+  __shared__ uint32_t res[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t b = blockIdx.x;
   const float *sc = scores + b * N;
   const uint8_t *fo = forced ? forced + b * N : nullptr;
   int32_t *out = kept + b * M_alloc;
+  const int nchunks = (int)((N + SEL_CHUNK - 1) / SEL_CHUNK);
+  const bool vec_s = ((uintptr_t)sc & 15) == 0;
+  const bool vec_f = fo && ((uintptr_t)fo & 15) == 0;
 
-  if (tid < 256) hist[tid] = 0;
-  if (tid == 0) sForced = 0;
-  __syncthreads();
-
-  // Pass 0: forced count and the top-digit histogram of the prunable keys.
-  uint32_t prefix = 0, pmask = 0;
-  int64_t nF_local = 0;
-  for (int64_t base = 0; base < N; base += SEL_THREADS) {
-    const int64_t n = base + tid;
-    bool cand = false;
-    uint32_t digit = 0;
-    if (n < N) {
-      const bool f = fo && fo[n];
-      nF_local += f ? 1 : 0;
-      if (!f) {
-        cand = true;
-        digit = order_key(sc[n]) >> 24;
+  uint32_t fbits = 0, vbits = 0;  // forced / valid (n < N) bit per item of this thread's segment
+  int loaded = -1;
+  auto load = [&](int c) {  // all threads call; ends with a barrier
+    if (c == loaded) return;
+    __syncthreads();  // previous readers of skey are done
+    const int64_t n0 = (int64_t)c * SEL_CHUNK + (int64_t)tid * SEL_I;
+    const int64_t cnt64 = N - n0;
+    const int cnt = cnt64 <= 0 ? 0 : (cnt64 >= SEL_I ? SEL_I : (int)cnt64);
+    vbits = cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+    if (cnt == SEL_I && vec_s) {
+      f32x4 x[SEL_I / 4];
+#pragma unroll
+      for (int v = 0; v < SEL_I / 4; ++v) x[v] = *(const f32x4 *)(sc + n0 + 4 * v);
+#pragma unroll
+      for (int v = 0; v < SEL_I / 4; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) skey[(4 * v + e) * SEL_T + tid] = order_key(x[v][e]);
+    } else {
+      for (int i = 0; i < SEL_I; ++i) skey[i * SEL_T + tid] = i < cnt ? order_key(sc[n0 + i]) : 0u;
+    }
+    fbits = 0;
+    if (fo) {
+      if (cnt == SEL_I && vec_f) {
+        const u32x4 x0 = *(const u32x4 *)(fo + n0), x1 = *(const u32x4 *)(fo + n0 + 16);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            fbits |= (((x0[w] >> (8 * e)) & 0xFFu) ? 1u : 0u) << (4 * w + e);
+            fbits |= (((x1[w] >> (8 * e)) & 0xFFu) ? 1u : 0u) << (16 + 4 * w + e);
+          }
+      } else {
+        for (int i = 0; i < cnt; ++i) fbits |= (fo[n0 + i] ? 1u : 0u) << i;
       }
     }
-    ballot_hist_add(hist, cand, digit, lane);
+    loaded = c;
+    __syncthreads();
+  };
+
+  for (int i = tid; i < 4096; i += SEL_T) hist[i] = 0;
+  if (tid == 0) res[2] = 0;
+
+  // Pass 0: forced count and the histogram of the top 12 key bits of prunable tokens.
+  uint32_t nf = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    load(c);
+    nf += (uint32_t)__popc(fbits & vbits);
+    const uint32_t cbits = vbits & ~fbits;
+#pragma unroll 8
+    for (int i = 0; i < SEL_I; ++i) hist_add(hist, (cbits >> i) & 1u, skey[i * SEL_T + tid] >> 20, lane);
   }
-  {
-    // block sum of nF_local
-    int64_t v = nF_local;
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0 && v) atomicAdd((unsigned long long *)&sForced, (unsigned long long)v);
-  }
+  for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o);
+  if (lane == 0 && nf) atomicAdd(&res[2], nf);
   __syncthreads();
-  const int64_t nF = sForced;
+  const int64_t nF = res[2];
   const int64_t nP = N - nF;
   const int64_t Kc = K < nP ? K : nP;
   const int64_t M_true = nF + Kc;
 
-  // Threshold key and tie quota.  Kc == nP: keep all (thr 0, unlimited quota);
-  // Kc == 0: keep none (no key equals 0xFFFFFFFF).
+  // Threshold key and tie quota.  Kc == nP: keep all (thr 0 is the lowest key,
+  // unlimited quota); Kc == 0: keep none (no key equals 0xFFFFFFFF).
   uint32_t thr;
   int64_t quota;
   if (Kc >= nP) {
@@ -118,140 +208,78 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topk_kernel(
     thr = 0xFFFFFFFFu;
     quota = 0;
   } else {
-    uint32_t need = (uint32_t)Kc;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (pass > 0) {
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
-        for (int64_t base = 0; base < N; base += SEL_THREADS) {
-          const int64_t n = base + tid;
-          bool cand = false;
-          uint32_t digit = 0;
-          if (n < N && !(fo && fo[n])) {
-            const uint32_t key = order_key(sc[n]);
-            if ((key & pmask) == prefix) {
-              cand = true;
-              digit = (key >> shift) & 255u;
-            }
-          }
-          ballot_hist_add(hist, cand, digit, lane);
-        }
-        __syncthreads();
+    find_bin<4096 / SEL_T>(hist, (uint32_t)Kc, res, sw, tid);
+    const uint32_t d0 = res[0];
+    uint32_t need = res[1];
+    for (int i = tid; i < 1024; i += SEL_T) hist[i] = 0;
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      load(c);
+      const uint32_t cbits = vbits & ~fbits;
+#pragma unroll 8
+      for (int i = 0; i < SEL_I; ++i) {
+        const uint32_t k = skey[i * SEL_T + tid];
+        hist_add(hist, ((cbits >> i) & 1u) && (k >> 20) == d0, (k >> 10) & 1023u, lane);
       }
-      // suffix sums: sSuffix[d] = sum_{d' >= d} hist[d']  (wave 0, 4 bins per lane)
-      if (wave == 0) {
-        const int d0 = 252 - 4 * lane;  // lane 0 holds bins 252..255
-        uint32_t h[4], loc = 0;
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-          h[e] = hist[d0 + e];
-          loc += h[e];
-        }
-        uint32_t inc = loc;  // inclusive scan over lanes (lane 0 = top bins)
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t t = __shfl_up(inc, o);
-          if (lane >= o) inc += t;
-        }
-        uint32_t run = inc - loc;  // count above bin d0+3
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-          run += h[e];
-          sSuffix[d0 + e] = run;
-        }
-      }
-      __syncthreads();
-      // digit d* with suffix(d*+1) < need <= suffix(d*)
-      if (tid < 256) {
-        const uint32_t here = sSuffix[tid];
-        const uint32_t above = tid < 255 ? sSuffix[tid + 1] : 0u;
-        if (above < need && need <= here) {
-          sState[2] = need - above;
-          sState[3] = (uint32_t)tid;
-        }
-      }
-      __syncthreads();
-      need = sState[2];
-      prefix |= sState[3] << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
     }
-    thr = prefix;
-    quota = need;
+    __syncthreads();
+    find_bin<1024 / SEL_T>(hist, need, res, sw, tid);
+    const uint32_t p1 = (d0 << 10) | res[0];
+    need = res[1];
+    for (int i = tid; i < 1024; i += SEL_T) hist[i] = 0;
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      load(c);
+      const uint32_t cbits = vbits & ~fbits;
+#pragma unroll 8
+      for (int i = 0; i < SEL_I; ++i) {
+        const uint32_t k = skey[i * SEL_T + tid];
+        hist_add(hist, ((cbits >> i) & 1u) && (k >> 10) == p1, k & 1023u, lane);
+      }
+    }
+    __syncthreads();
+    find_bin<1024 / SEL_T>(hist, need, res, sw, tid);
+    thr = (p1 << 10) | res[0];
+    quota = res[1];
   }
 
-  // Output pass: ascending kept indices.
-  if (tid == 0) {
-    sRun[0] = 0;
-    sRun[1] = 0;
+  // Output: ascending kept indices.  Per segment, tokens kept without a tie
+  // (forced, or key > thr) and tied tokens (key == thr) are counted; one block
+  // scan gives every segment its offsets; the first `quota` ties in index order
+  // are kept.
+  int64_t runK = 0, runT = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    load(c);
+    uint32_t kn = 0, tn = 0;
+#pragma unroll 8
+    for (int i = 0; i < SEL_I; ++i) {
+      const uint32_t k = skey[i * SEL_T + tid];
+      const bool v = (vbits >> i) & 1u, f = (fbits >> i) & 1u;
+      kn += (v && (f || k > thr)) ? 1u : 0u;
+      tn += (v && !f && k == thr) ? 1u : 0u;
+    }
+    uint32_t ek, et, tk, tt;
+    block_exscan2(kn, tn, ek, et, tk, tt, sw, tid);
+    int64_t kb = runK + ek, tb = runT + et;
+    const int64_t n0 = (int64_t)c * SEL_CHUNK + (int64_t)tid * SEL_I;
+    for (int i = 0; i < SEL_I; ++i) {
+      const bool v = (vbits >> i) & 1u, f = (fbits >> i) & 1u;
+      if (!v) break;  // valid items form a prefix of the segment
+      const uint32_t k = skey[i * SEL_T + tid];
+      if (f || k > thr) {
+        const int64_t p = kb + (tb < quota ? tb : quota);
+        if (p < M_alloc) out[p] = (int32_t)(n0 + i);
+        ++kb;
+      } else if (k == thr) {
+        if (tb < quota && kb + tb < M_alloc) out[kb + tb] = (int32_t)(n0 + i);
+        ++tb;
+      }
+    }
+    runK += tk;
+    runT += tt;
   }
-  __syncthreads();
-  for (int64_t base = 0; base < N; base += (int64_t)SEL_THREADS * SEL_ITEMS) {
-    bool knt[SEL_ITEMS], tie[SEL_ITEMS];
-    uint32_t rk[SEL_ITEMS], rt[SEL_ITEMS];
-#pragma unroll
-    for (int it = 0; it < SEL_ITEMS; ++it) {
-      const int64_t n = base + (int64_t)it * SEL_THREADS + tid;
-      knt[it] = false;
-      tie[it] = false;
-      if (n < N) {
-        if (fo && fo[n]) {
-          knt[it] = true;
-        } else {
-          const uint32_t key = order_key(sc[n]);
-          knt[it] = key > thr;
-          tie[it] = key == thr;
-        }
-      }
-      const uint64_t bk = __ballot(knt[it]);
-      const uint64_t bt = __ballot(tie[it]);
-      rk[it] = lane_rank(bk);
-      rt[it] = lane_rank(bt);
-      if (lane == 0) sCnt[it * SEL_WAVES + wave] = (uint32_t)__popcll(bk) | ((uint32_t)__popcll(bt) << 16);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const uint32_t c = sCnt[lane];  // 64 = SEL_ITEMS * SEL_WAVES entries, in token order
-      uint32_t ck = c & 0xFFFFu, ct = c >> 16;
-      uint32_t ik = ck, itt = ct;
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t a = __shfl_up(ik, o), bb = __shfl_up(itt, o);
-        if (lane >= o) {
-          ik += a;
-          itt += bb;
-        }
-      }
-      sOffK[lane] = ik - ck;
-      sOffT[lane] = itt - ct;
-      if (lane == 63) {
-        sState[0] = ik;
-        sState[1] = itt;
-      }
-    }
-    __syncthreads();
-    const int64_t runK = sRun[0], runT = sRun[1];
-#pragma unroll
-    for (int it = 0; it < SEL_ITEMS; ++it) {
-      const int64_t n = base + (int64_t)it * SEL_THREADS + tid;
-      const int slot = it * SEL_WAVES + wave;
-      const int64_t kb = runK + sOffK[slot] + rk[it];  // kept-not-tied tokens before n
-      const int64_t tb = runT + sOffT[slot] + rt[it];  // tied tokens before n
-      const int64_t tk = tb < quota ? tb : quota;      // tied tokens kept before n
-      if (knt[it] || (tie[it] && tb < quota)) {
-        const int64_t p = kb + tk;
-        if (p < M_alloc) out[p] = (int32_t)n;
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      sRun[0] = runK + sState[0];
-      sRun[1] = runT + sState[1];
-    }
-    __syncthreads();
-  }
-  // pad and report
   const int64_t written = M_true < M_alloc ? M_true : M_alloc;
-  for (int64_t m = written + tid; m < M_alloc; m += SEL_THREADS) out[m] = -1;
+  for (int64_t m = written + tid; m < M_alloc; m += SEL_T) out[m] = -1;
   if (tid == 0 && kept_count) kept_count[b] = (int32_t)M_true;
 }
 
@@ -287,8 +315,8 @@ hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_
                               int64_t K, int64_t M_alloc, int32_t *kept, int32_t *kept_count,
                               hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_topk_kernel, dim3((unsigned)B), dim3(SEL_THREADS), 0, s, scores, forced, N, K,
-                     M_alloc, kept, kept_count);
+  hipLaunchKernelGGL(select_topk_kernel, dim3((unsigned)B), dim3(SEL_T), 0, s, scores, forced, N, K, M_alloc, kept,
+                     kept_count);
   return hipGetLastError();
 }
 

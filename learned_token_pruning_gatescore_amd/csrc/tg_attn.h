@@ -1,0 +1,30 @@
+// tg_attn.h -- attention workspace layout shared by the forward and backward launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+struct AttnWs {
+  float2 *cs;        // [B*M, D/2] (cos, sin) of the kept positions
+  uint16_t *khat;    // [B, M, Hkv, D] rotated keys (bf16)
+  float *bias;       // [B, Hq, M] gamma_h * log2 g_j (-inf where g_j <= 0)
+  float *delta;      // [B, Hq, M] D_i of the backward
+  float *colsum;     // [B, Hq, M] column sums of dS per head
+};
+
+size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd);
+AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
+hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
+                            int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, const AttnWs &w,
+                            hipStream_t s);
+hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                           const int32_t *pos, double theta, float tau, int B, int M, int Hq, int Hkv, int D,
+                           bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s);
+hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                           const int32_t *pos, double theta, float tau, const float *lse, const void *dout, int B,
+                           int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg,
+                           float *dgamma, const AttnWs &w, hipStream_t s);
+
+}  // namespace tg

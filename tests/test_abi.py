@@ -92,7 +92,8 @@ def test_attn_validation():
     assert f(*args(D=96)) == 2                  # bf16 D
     assert f(*args(Hq=24, Hkv=8)) == 2          # group of 3
     assert f(*args(tau=0.0)) == 1
-    assert f(*args(pos=FAKE)) == 3              # RoPE table needs a workspace
+    assert f(*args()) == 3                      # a workspace is required
+    assert f(*args(pos=FAKE)) == 3
     need = lib.tg_gated_attn_workspace_size(1, 100, 16, 8, 128, 0)
     assert need >= 100 * 64 * 8
     assert f(*args(pos=FAKE, ws=FAKE, wsb=need - 1)) == 3
