@@ -9,11 +9,11 @@
 //
 // Selection is a radix select over a 32-bit order key of the fp32 score, one
 // work-group per batch row: three digit passes (12, 10, 10 bits) over an LDS
-// histogram fed through wavefront ballots (lanes holding the first candidate's
-// digit are counted with one ballot and one atomic) find the exact key T of
+// histogram (wavefront ballots collapse a wave whose keys all share one digit
+// into a single atomic) find the exact key T of
 // the K'-th best prunable token and how many tokens with key == T to take
 // (lowest index first).  Each thread owns contiguous 32-token segments whose
-// keys stay in LDS; a final pass emits the kept indices in ascending
+// keys stay in registers; a final pass emits the kept indices in ascending
 // order from one block-wide scan of per-segment counts.  No host
 // synchronisation and no global atomics: the output is deterministic.
 #include "tg_common.h"
@@ -29,9 +29,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
+  // number of set bits of mask below this lane
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 constexpr int SEL_T = 1024;              // threads per batch row
 constexpr int SEL_I = 32;                // tokens per thread per chunk (a contiguous segment)
-constexpr int SEL_CHUNK = SEL_T * SEL_I; // 32768 tokens per chunk (keys resident in LDS)
+constexpr int SEL_CHUNK = SEL_T * SEL_I; // 32768 tokens per chunk
 constexpr int SEL_W = SEL_T / 64;        // waves per work-group
 
 // Block-wide exclusive scans of two uint32 values over the SEL_W waves.
@@ -73,18 +78,16 @@ __device__ __forceinline__ void block_exscan2(uint32_t a, uint32_t b, uint32_t &
   __syncthreads();
 }
 
-// Adds one to hist[digit] for each lane with `cand`.  A wavefront ballot first
-// checks whether every candidate lane holds the same digit (a zero-initialised
-// scorer makes every key equal): then one atomic adds the popcount; otherwise
-// each candidate lane adds its own (distinct digits rarely collide on a bank).
-__device__ __forceinline__ void hist_add(uint32_t *hist, bool cand, uint32_t digit, int lane) {
+// Adds one to hist[digit] for each lane with `cand`: one LDS atomic per lane,
+// except when every candidate lane of the wave holds the same digit (a zero-
+// initialised scorer makes every key equal), where a wavefront ballot counts
+// them and a single atomic adds the total.
+__device__ __forceinline__ void hist_add(uint32_t *hist, bool cand, uint32_t digit) {
   const uint64_t act = __ballot(cand);
-  if (act == 0) return;
-  const int leader = __ffsll((unsigned long long)act) - 1;
-  const uint32_t dl = __shfl(digit, leader);
-  const uint64_t same = __ballot(cand && digit == dl);
-  if (same == act) {
-    if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+  const uint32_t d0 = __shfl(digit, act ? __ffsll((unsigned long long)act) - 1 : 0);
+  const uint64_t same = __ballot(cand && digit == d0);
+  if (act != 0 && same == act) {
+    if (cand && lane_rank(act) == 0) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
   } else if (cand) {
     atomicAdd(&hist[digit], 1u);
   }
@@ -116,15 +119,15 @@ __device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t need, ui
 }
 
 // One work-group per batch row.  Tokens are processed in 32768-token chunks;
-// thread t owns the contiguous segment [t*32, t*32+32) of a chunk.  The
-// chunk's keys live in LDS as skey[i][t] (conflict-free reads of item i by
-// all threads); with one chunk (N <= 32768) they are loaded once, otherwise
-// each pass reloads the chunk (L2-resident).  Forced / valid bits stay in
-// registers (one bit per item).
+// thread t owns the contiguous segment [t*32, t*32+32) of a chunk.  With one
+// chunk (N <= 32768) its 32 keys stay in registers for every pass, otherwise
+// each pass reloads the chunk (L2-resident).  Forced / valid / candidate flags
+// are 32-bit masks, so the output positions of a segment come from popcounts
+// of masks rather than from a dependent counter chain.
+template <bool RES>
 __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     const float *__restrict__ scores, const uint8_t *__restrict__ forced, int64_t N, int64_t K,
     int64_t M_alloc, int32_t *__restrict__ kept, int32_t *__restrict__ kept_count) {
-  __shared__ uint32_t skey[SEL_I * SEL_T];
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t sw[2 * SEL_W];
   __shared__ uint32_t res[4];
@@ -138,25 +141,23 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
   const bool vec_s = ((uintptr_t)sc & 15) == 0;
   const bool vec_f = fo && ((uintptr_t)fo & 15) == 0;
 
+  uint32_t key[SEL_I];
   uint32_t fbits = 0, vbits = 0;  // forced / valid (n < N) bit per item of this thread's segment
-  int loaded = -1;
-  auto load = [&](int c) {  // all threads call; ends with a barrier
-    if (c == loaded) return;
-    __syncthreads();  // previous readers of skey are done
+  auto load = [&](int c) {
     const int64_t n0 = (int64_t)c * SEL_CHUNK + (int64_t)tid * SEL_I;
     const int64_t cnt64 = N - n0;
     const int cnt = cnt64 <= 0 ? 0 : (cnt64 >= SEL_I ? SEL_I : (int)cnt64);
     vbits = cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
     if (cnt == SEL_I && vec_s) {
-      f32x4 x[SEL_I / 4];
 #pragma unroll
-      for (int v = 0; v < SEL_I / 4; ++v) x[v] = *(const f32x4 *)(sc + n0 + 4 * v);
+      for (int v = 0; v < SEL_I / 4; ++v) {
+        const f32x4 x = *(const f32x4 *)(sc + n0 + 4 * v);
 #pragma unroll
-      for (int v = 0; v < SEL_I / 4; ++v)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) skey[(4 * v + e) * SEL_T + tid] = order_key(x[v][e]);
+        for (int e = 0; e < 4; ++e) key[4 * v + e] = order_key(x[e]);
+      }
     } else {
-      for (int i = 0; i < SEL_I; ++i) skey[i * SEL_T + tid] = i < cnt ? order_key(sc[n0 + i]) : 0u;
+#pragma unroll
+      for (int i = 0; i < SEL_I; ++i) key[i] = i < cnt ? order_key(sc[n0 + i]) : 0u;
     }
     fbits = 0;
     if (fo) {
@@ -173,21 +174,21 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
         for (int i = 0; i < cnt; ++i) fbits |= (fo[n0 + i] ? 1u : 0u) << i;
       }
     }
-    loaded = c;
-    __syncthreads();
   };
 
   for (int i = tid; i < 4096; i += SEL_T) hist[i] = 0;
   if (tid == 0) res[2] = 0;
+  if (RES) load(0);
+  __syncthreads();
 
   // Pass 0: forced count and the histogram of the top 12 key bits of prunable tokens.
   uint32_t nf = 0;
   for (int c = 0; c < nchunks; ++c) {
-    load(c);
+    if (!RES) load(c);
     nf += (uint32_t)__popc(fbits & vbits);
     const uint32_t cbits = vbits & ~fbits;
-#pragma unroll 8
-    for (int i = 0; i < SEL_I; ++i) hist_add(hist, (cbits >> i) & 1u, skey[i * SEL_T + tid] >> 20, lane);
+#pragma unroll
+    for (int i = 0; i < SEL_I; ++i) hist_add(hist, (cbits >> i) & 1u, key[i] >> 20);
   }
   for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o);
   if (lane == 0 && nf) atomicAdd(&res[2], nf);
@@ -213,14 +214,12 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     uint32_t need = res[1];
     for (int i = tid; i < 1024; i += SEL_T) hist[i] = 0;
     __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      load(c);
+    for (int c = 0; c < nchunks; ++c) {  // few candidates remain: plain predicated atomics
+      if (!RES) load(c);
       const uint32_t cbits = vbits & ~fbits;
-#pragma unroll 8
-      for (int i = 0; i < SEL_I; ++i) {
-        const uint32_t k = skey[i * SEL_T + tid];
-        hist_add(hist, ((cbits >> i) & 1u) && (k >> 20) == d0, (k >> 10) & 1023u, lane);
-      }
+#pragma unroll
+      for (int i = 0; i < SEL_I; ++i)
+        if (((cbits >> i) & 1u) && (key[i] >> 20) == d0) atomicAdd(&hist[(key[i] >> 10) & 1023u], 1u);
     }
     __syncthreads();
     find_bin<1024 / SEL_T>(hist, need, res, sw, tid);
@@ -229,13 +228,11 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     for (int i = tid; i < 1024; i += SEL_T) hist[i] = 0;
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
-      load(c);
+      if (!RES) load(c);
       const uint32_t cbits = vbits & ~fbits;
-#pragma unroll 8
-      for (int i = 0; i < SEL_I; ++i) {
-        const uint32_t k = skey[i * SEL_T + tid];
-        hist_add(hist, ((cbits >> i) & 1u) && (k >> 10) == p1, k & 1023u, lane);
-      }
+#pragma unroll
+      for (int i = 0; i < SEL_I; ++i)
+        if (((cbits >> i) & 1u) && (key[i] >> 10) == p1) atomicAdd(&hist[key[i] & 1023u], 1u);
     }
     __syncthreads();
     find_bin<1024 / SEL_T>(hist, need, res, sw, tid);
@@ -243,36 +240,44 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     quota = res[1];
   }
 
-  // Output: ascending kept indices.  Per segment, tokens kept without a tie
-  // (forced, or key > thr) and tied tokens (key == thr) are counted; one block
-  // scan gives every segment its offsets; the first `quota` ties in index order
-  // are kept.
+  // Output: ascending kept indices.  Per segment: mask of tokens kept without a
+  // tie (forced, or key > thr) and mask of tied tokens (key == thr); one block
+  // scan of their popcounts gives each segment its offsets, and the first
+  // `quota` ties in index order are kept.
   int64_t runK = 0, runT = 0;
   for (int c = 0; c < nchunks; ++c) {
-    load(c);
-    uint32_t kn = 0, tn = 0;
-#pragma unroll 8
+    if (!RES) load(c);
+    uint32_t km = fbits & vbits, tm = 0;
+#pragma unroll
     for (int i = 0; i < SEL_I; ++i) {
-      const uint32_t k = skey[i * SEL_T + tid];
-      const bool v = (vbits >> i) & 1u, f = (fbits >> i) & 1u;
-      kn += (v && (f || k > thr)) ? 1u : 0u;
-      tn += (v && !f && k == thr) ? 1u : 0u;
+      const uint32_t bit = 1u << i;
+      const bool cand = (vbits & ~fbits & bit) != 0;
+      km |= (cand && key[i] > thr) ? bit : 0u;
+      tm |= (cand && key[i] == thr) ? bit : 0u;
     }
     uint32_t ek, et, tk, tt;
-    block_exscan2(kn, tn, ek, et, tk, tt, sw, tid);
-    int64_t kb = runK + ek, tb = runT + et;
+    block_exscan2((uint32_t)__popc(km), (uint32_t)__popc(tm), ek, et, tk, tt, sw, tid);
+    const int64_t kb = runK + ek, tb = runT + et;
     const int64_t n0 = (int64_t)c * SEL_CHUNK + (int64_t)tid * SEL_I;
+    // a tie at item i is kept when tb + (ties before i in the segment) < quota
+    const int64_t tq = quota - tb;  // ties of this segment that can still be kept
+    uint32_t tkeep = tm;
+    if (tq <= 0) {
+      tkeep = 0u;
+    } else if (tq < 32) {
+      // keep the first tq set bits of tm
+      uint32_t m = tm;
+      for (int64_t r = 0; r < tq && m; ++r) m &= m - 1u;  // clear the lowest tq bits
+      tkeep = tm & ~m;
+    }
+    const uint32_t all = km | tkeep;
+    const int64_t base = kb + (tb < quota ? tb : quota);
+#pragma unroll
     for (int i = 0; i < SEL_I; ++i) {
-      const bool v = (vbits >> i) & 1u, f = (fbits >> i) & 1u;
-      if (!v) break;  // valid items form a prefix of the segment
-      const uint32_t k = skey[i * SEL_T + tid];
-      if (f || k > thr) {
-        const int64_t p = kb + (tb < quota ? tb : quota);
+      const uint32_t bit = 1u << i;
+      if (all & bit) {
+        const int64_t p = base + __popc(all & (bit - 1u));
         if (p < M_alloc) out[p] = (int32_t)(n0 + i);
-        ++kb;
-      } else if (k == thr) {
-        if (tb < quota && kb + tb < M_alloc) out[kb + tb] = (int32_t)(n0 + i);
-        ++tb;
       }
     }
     runK += tk;
@@ -315,8 +320,12 @@ hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_
                               int64_t K, int64_t M_alloc, int32_t *kept, int32_t *kept_count,
                               hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_topk_kernel, dim3((unsigned)B), dim3(SEL_T), 0, s, scores, forced, N, K, M_alloc, kept,
-                     kept_count);
+  if (N <= SEL_CHUNK)
+    hipLaunchKernelGGL(select_topk_kernel<true>, dim3((unsigned)B), dim3(SEL_T), 0, s, scores, forced, N, K, M_alloc,
+                       kept, kept_count);
+  else
+    hipLaunchKernelGGL(select_topk_kernel<false>, dim3((unsigned)B), dim3(SEL_T), 0, s, scores, forced, N, K,
+                       M_alloc, kept, kept_count);
   return hipGetLastError();
 }
 
