@@ -79,11 +79,39 @@ const char *tg_last_error(void);
  *   gates       [B, N] f32 out or NULL
  * bf16 runs on matrix cores with fp32 accumulation; SiLU, the w2 dot and the
  * sigmoid are fp32.  Needs d % 32 == 0 for bf16 and d % 4 == 0 for f32.
+ *   ws, ws_bytes                     bf16: device scratch of at least
+ *                                    tg_gate_score_workspace_size(d, d_ff, dt)
+ *                                    bytes, 16-byte aligned, owned by the
+ *                                    caller (W1 is rewritten there in matrix-
+ *                                    core fragment order before scoring);
+ *                                    f32: unused (may be NULL).
+ * Errors: TG_ERR_WORKSPACE when the bf16 workspace is missing or too small.
  */
 tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2,
                         const uint8_t *forced_keep, int64_t B, int64_t N, int64_t d,
                         int64_t d_ff, tg_dtype dt, float *scores, float *gates,
-                        void *stream);
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace tg_gate_score needs: the fragment-ordered copy of W1
+ * for TG_BF16 (d_ff rounded up to 512 units, d to 128 inputs, 2 bytes each);
+ * 0 for TG_F32 or invalid sizes. */
+size_t tg_gate_score_workspace_size(int64_t d, int64_t d_ff, tg_dtype dt);
+
+/*
+ * tg_gate_pack_w1 / tg_gate_score_packed -- the same scoring MLP split into
+ * a one-off weight transform and the per-call product, for callers that
+ * keep the scorer's weights resident (section 3.1: the scorer is a fixed,
+ * trained MLP at inference).  tg_gate_pack_w1 writes W1 [d_ff, d] bf16 in
+ * fragment order into w1_packed (bytes >= tg_gate_score_workspace_size);
+ * tg_gate_score_packed then computes exactly what tg_gate_score computes
+ * from that copy.  bf16 only (TG_ERR_UNSUPPORTED otherwise).
+ */
+tg_status tg_gate_pack_w1(const void *w1, int64_t d, int64_t d_ff, tg_dtype dt,
+                          void *w1_packed, size_t bytes, void *stream);
+tg_status tg_gate_score_packed(const void *hidden, const void *w1_packed, const void *w2,
+                               const uint8_t *forced_keep, int64_t B, int64_t N, int64_t d,
+                               int64_t d_ff, tg_dtype dt, float *scores, float *gates,
+                               void *stream);
 
 /* Kept tokens per row: n_forced + min(K, N - n_forced); -1 for invalid input. */
 int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K);

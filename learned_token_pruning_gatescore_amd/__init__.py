@@ -10,6 +10,8 @@ the calls raise.
 Stages (TokenGate deep dive, "TokenGate: Learnable Token Pruning for Fast,
 Memory-Efficient LLM Prefill", sections 3.1-3.4):
   tg_gate_score      scoring MLP -> raw scores and gate values
+                     (tg_gate_pack_w1 + tg_gate_score_packed: the same with W1
+                     rewritten once in matrix-core fragment order)
   tg_select_topk     top-K prunable tokens plus every forced token, ascending
   tg_compact         gather of kept hidden states, positions and gates
   tg_gated_attn_fwd  causal attention with the per-key bias gamma_h * ln g_j
@@ -22,6 +24,7 @@ import os
 
 __all__ = [
     "TokenGateError", "library_path", "load", "tg_version", "tg_kept_count", "tg_gate_score",
+    "tg_gate_score_workspace_size", "tg_gate_pack_w1", "tg_gate_score_packed", "gate_workspace",
     "tg_select_topk", "tg_compact", "tg_gated_attn_fwd", "tg_gated_attn_bwd",
     "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
 ]
@@ -64,7 +67,13 @@ def load():
     lib.tg_kept_count.restype = i64
     lib.tg_kept_count.argtypes = [i64, i64, i64]
     lib.tg_gate_score.restype = c_int
-    lib.tg_gate_score.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P]
+    lib.tg_gate_score.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P, sz, P]
+    lib.tg_gate_score_workspace_size.restype = sz
+    lib.tg_gate_score_workspace_size.argtypes = [i64, i64, c_int]
+    lib.tg_gate_pack_w1.restype = c_int
+    lib.tg_gate_pack_w1.argtypes = [P, i64, i64, c_int, P, sz, P]
+    lib.tg_gate_score_packed.restype = c_int
+    lib.tg_gate_score_packed.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P]
     lib.tg_select_topk_workspace_size.restype = sz
     lib.tg_select_topk_workspace_size.argtypes = [i64, i64]
     lib.tg_select_topk.restype = c_int
@@ -132,14 +141,45 @@ def tg_gated_attn_workspace_size(B: int, M: int, Hq: int, Hkv: int, D: int, bwd:
     return load().tg_gated_attn_workspace_size(B, M, Hq, Hkv, D, int(bool(bwd)))
 
 
-def tg_gate_score(hidden, w1, w2, forced_keep, scores, gates=None, stream=None):
+def tg_gate_score_workspace_size(d: int, d_ff: int, bf16: bool) -> int:
+    return load().tg_gate_score_workspace_size(d, d_ff, TG_BF16 if bf16 else TG_F32)
+
+
+def gate_workspace(d, d_ff, dtype, device):
+    """A workspace tensor of the size tg_gate_score needs (also the packed-W1 buffer)."""
+    import torch
+
+    n = tg_gate_score_workspace_size(d, d_ff, dtype == torch.bfloat16)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def tg_gate_score(hidden, w1, w2, forced_keep, scores, gates=None, ws=None, stream=None):
     """hidden [B, N, d], w1 [d_ff, d], w2 [d_ff] (bf16 or fp32); forced_keep u8 [B, N] or None;
-    writes scores (and gates) f32 [B, N]."""
-    _contig(hidden, w1, w2, forced_keep, scores, gates)
+    writes scores (and gates) f32 [B, N].  ws: workspace (allocated here when None)."""
+    _contig(hidden, w1, w2, forced_keep, scores, gates, ws)
     B, N, d = hidden.shape
     d_ff = w1.shape[0]
+    if ws is None:
+        ws = gate_workspace(d, d_ff, hidden.dtype, hidden.device)
+    ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_gate_score(_ptr(hidden), _ptr(w1), _ptr(w2), _ptr(forced_keep), B, N, d, d_ff, _dt(hidden),
-                                _ptr(scores), _ptr(gates), _stream(stream)))
+                                _ptr(scores), _ptr(gates), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tg_gate_pack_w1(w1, w1_packed, stream=None):
+    """w1 [d_ff, d] bf16 -> w1_packed (uint8 tensor of tg_gate_score_workspace_size bytes)."""
+    _contig(w1, w1_packed)
+    d_ff, d = w1.shape
+    nbytes = w1_packed.numel() * w1_packed.element_size()
+    _check(load().tg_gate_pack_w1(_ptr(w1), d, d_ff, _dt(w1), _ptr(w1_packed), nbytes, _stream(stream)))
+
+
+def tg_gate_score_packed(hidden, w1_packed, d_ff, w2, forced_keep, scores, gates=None, stream=None):
+    """tg_gate_score from a W1 copy made by tg_gate_pack_w1 (bf16 only)."""
+    _contig(hidden, w1_packed, w2, forced_keep, scores, gates)
+    B, N, d = hidden.shape
+    _check(load().tg_gate_score_packed(_ptr(hidden), _ptr(w1_packed), _ptr(w2), _ptr(forced_keep), B, N, d,
+                                       int(d_ff), _dt(hidden), _ptr(scores), _ptr(gates), _stream(stream)))
 
 
 def tg_select_topk(scores, forced_keep, K, n_forced, kept_idx, kept_count=None, ws=None, stream=None):
@@ -230,7 +270,12 @@ def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma,
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         bufs["attn_ws"] = ws
-    tg_gate_score(hidden, w1, w2, forced_keep, scores, gates, stream=stream)
+    gws = bufs.get("gate_ws")
+    gneed = tg_gate_score_workspace_size(d, w1.shape[0], hidden.dtype == torch.bfloat16)
+    if gws is None or gws.numel() < gneed:
+        gws = torch.empty(max(gneed, 1), dtype=torch.uint8, device=dev)
+        bufs["gate_ws"] = gws
+    tg_gate_score(hidden, w1, w2, forced_keep, scores, gates, ws=gws, stream=stream)
     key = scores if select_scores is None else select_scores
     tg_select_topk(key, forced_keep, K, n_forced, kept, stream=stream)
     tg_compact(hidden, pos, gates, kept, h_out, p_out, g_out, stream=stream)

@@ -12,6 +12,8 @@
 #include "tg_attn.h"
 
 namespace tg {
+size_t gate_packed_bytes(int d, int d_ff);
+hipError_t launch_gate_pack_w1(const void *w1, int d, int d_ff, void *packed, hipStream_t s);
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced, int64_t T,
                              int d, int d_ff, bool bf16, float *scores, float *gates, hipStream_t s);
 hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_t B, int64_t N, int64_t K,
@@ -99,9 +101,12 @@ int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K) {
   return n_forced + (K < nP ? K : nP);
 }
 
-tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced_keep, int64_t B,
-                        int64_t N, int64_t d, int64_t d_ff, tg_dtype dt, float *scores, float *gates,
-                        void *stream) {
+}  // extern "C"
+
+namespace {
+
+tg_status check_gate(const void *hidden, const void *w1, const void *w2, int64_t B, int64_t N, int64_t d,
+                     int64_t d_ff, tg_dtype dt, const float *scores, const float *gates) {
   REQUIRE(hidden && w1 && w2 && scores, TG_ERR_INVALID_ARG, "hidden, w1, w2 and scores are required");
   REQUIRE(B >= 0 && N >= 0, TG_ERR_INVALID_ARG, "B and N must be >= 0");
   REQUIRE(d > 0 && d_ff > 0, TG_ERR_INVALID_ARG, "d and d_ff must be > 0 (d=%lld d_ff=%lld)", (long long)d,
@@ -114,8 +119,62 @@ tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2, cons
     REQUIRE(d % 4 == 0 && d <= 8192, TG_ERR_UNSUPPORTED, "f32 scoring needs d %% 4 == 0 and d <= 8192");
   REQUIRE(aligned16(hidden) && aligned16(w1) && aligned16(w2) && aligned16(scores) && aligned16(gates),
           TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  return hip_status(tg::launch_gate_score(hidden, w1, w2, forced_keep, B * N, (int)d, (int)d_ff, dt == TG_BF16,
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tg_gate_score_workspace_size(int64_t d, int64_t d_ff, tg_dtype dt) {
+  if (dt != TG_BF16 || d <= 0 || d_ff <= 0 || d > 65536 || d_ff > 65536) return 0;
+  return tg::gate_packed_bytes((int)d, (int)d_ff);
+}
+
+tg_status tg_gate_pack_w1(const void *w1, int64_t d, int64_t d_ff, tg_dtype dt, void *w1_packed, size_t bytes,
+                          void *stream) {
+  REQUIRE(w1 && w1_packed, TG_ERR_INVALID_ARG, "w1 and w1_packed are required");
+  REQUIRE(dt == TG_BF16, TG_ERR_UNSUPPORTED, "only bf16 weights are packed");
+  REQUIRE(d > 0 && d_ff > 0 && d <= 65536 && d_ff <= 65536, TG_ERR_INVALID_ARG, "bad d / d_ff");
+  REQUIRE(d % 32 == 0, TG_ERR_UNSUPPORTED, "bf16 scoring needs d %% 32 == 0 (d=%lld)", (long long)d);
+  REQUIRE(aligned16(w1) && aligned16(w1_packed), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t need = tg::gate_packed_bytes((int)d, (int)d_ff);
+  REQUIRE(bytes >= need, TG_ERR_WORKSPACE, "w1_packed holds %zu bytes, needs %zu", bytes, need);
+  return hip_status(tg::launch_gate_pack_w1(w1, (int)d, (int)d_ff, w1_packed, (hipStream_t)stream),
+                    "tg_gate_pack_w1 launch");
+}
+
+tg_status tg_gate_score_packed(const void *hidden, const void *w1_packed, const void *w2,
+                               const uint8_t *forced_keep, int64_t B, int64_t N, int64_t d, int64_t d_ff,
+                               tg_dtype dt, float *scores, float *gates, void *stream) {
+  REQUIRE(dt == TG_BF16, TG_ERR_UNSUPPORTED, "packed weights exist for bf16 only");
+  const tg_status st = check_gate(hidden, w1_packed, w2, B, N, d, d_ff, dt, scores, gates);
+  if (st != TG_OK) return st;
+  return hip_status(tg::launch_gate_score(hidden, w1_packed, w2, forced_keep, B * N, (int)d, (int)d_ff, true,
                                           scores, gates, (hipStream_t)stream),
+                    "tg_gate_score_packed launch");
+}
+
+tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced_keep, int64_t B,
+                        int64_t N, int64_t d, int64_t d_ff, tg_dtype dt, float *scores, float *gates, void *ws,
+                        size_t ws_bytes, void *stream) {
+  const tg_status st = check_gate(hidden, w1, w2, B, N, d, d_ff, dt, scores, gates);
+  if (st != TG_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == TG_BF16) {
+    const size_t need = tg::gate_packed_bytes((int)d, (int)d_ff);
+    REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "bf16 scoring needs a %zu-byte workspace (got %zu)", need,
+            ws ? ws_bytes : (size_t)0);
+    REQUIRE(aligned16(ws), TG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (B * N == 0) return ok();
+    const tg_status pst = hip_status(tg::launch_gate_pack_w1(w1, (int)d, (int)d_ff, ws, s), "tg_gate_score pack");
+    if (pst != TG_OK) return pst;
+    return hip_status(tg::launch_gate_score(hidden, ws, w2, forced_keep, B * N, (int)d, (int)d_ff, true, scores,
+                                            gates, s),
+                      "tg_gate_score launch");
+  }
+  return hip_status(tg::launch_gate_score(hidden, w1, w2, forced_keep, B * N, (int)d, (int)d_ff, false, scores,
+                                          gates, s),
                     "tg_gate_score launch");
 }
 

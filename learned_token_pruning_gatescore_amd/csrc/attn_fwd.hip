@@ -89,12 +89,6 @@ __device__ __forceinline__ void rope_chunk(u32x4 &x, u32x4 &y, const float2 *__r
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Direct buffer -> LDS load (raw buffer, `size` bytes per lane): lane l's data
-// lands at lds + l * size.
-__device__ void buffer_load_lds(i32x4 rsrc, lds_u32 *lds, int size, int voffset, int soffset, int offset,
-                                int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 // LDS layout of a bf16 tile (row = key): rows of D elements, unpadded, with
 // 16-byte chunks XOR-swizzled per row.  gfx950 LDS serves 64 banks (256 bytes)
@@ -116,12 +110,6 @@ struct Tile {
   __device__ static int vswz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
-// Buffer resource over `bytes` bytes at `base` (raw buffer, stride 0): loads
-// whose offset falls outside return zero, so the tail tile needs no clamping.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
-}
 
 // Work-group: 8 waves = two teams of 4.  The 4 waves of a team own the 128
 // columns; each 128-key super-tile is split between the teams (team t takes
@@ -192,19 +180,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const int soff = t * TK * (int)rsb;
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-      buffer_load_lds(rK, (lds_u32 *)(sKV + (t & 1) * TILE + (wave * NIW + i) * 512), 16, (int)kofs(i), soff, 0, 0);
+      dma_b128(rK, lds_addr(sKV) + 2u * (uint32_t)((t & 1) * TILE + (wave * NIW + i) * 512), kofs(i), (uint32_t)soff);
   };
   auto issue_v = [&](int t) {
     const int j0 = t * TK;
     const int soff = j0 * (int)rsb;
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-      buffer_load_lds(rV, (lds_u32 *)(sKV + (2 + (t & 1)) * TILE + (wave * NIW + i) * 512), 16, (int)vofs(i), soff,
-                      0, 0);
+      dma_b128(rV, lds_addr(sKV) + 2u * (uint32_t)((2 + (t & 1)) * TILE + (wave * NIW + i) * 512), vofs(i),
+               (uint32_t)soff);
     // bias rows: G x 128 floats, 64 floats per 4-byte direct-load instruction
     for (int ii = wave; ii < 2 * G; ii += 8)
-      buffer_load_lds(rB, (lds_u32 *)&sB[t & 1][ii >> 1][(ii & 1) * 64], 4,
-                      (((ii >> 1) * M + (ii & 1) * 64 + lane) * 4), j0 * 4, 0, 0);
+      dma_b32(rB, lds_addr(&sB[t & 1][ii >> 1][(ii & 1) * 64]), (uint32_t)(((ii >> 1) * M + (ii & 1) * 64 + lane) * 4),
+              (uint32_t)(j0 * 4));
   };
   issue_k(0);
   issue_v(0);
@@ -325,14 +313,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   };
 
   f32x16 sA[2], sB2[2];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  sync_vm<0>();
   qk(0, sA);
   // Two iterations per trip so the current / next S accumulators swap roles without copies.
   for (int t = 0; t < nst; t += 2) {
     // iteration t: S(t) in sA, computes S(t+1) into sB2
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // K(t+1), V(t) landed; every wave is done with iteration t-1
+    sync_vm<0>();  // K(t+1), V(t) landed; every wave is done with iteration t-1
     if (t + 2 < nst) issue_k(t + 2);
     if (t + 1 < nst) issue_v(t + 1);
     // ping-pong: team 0 multiplies the next tile first, team 1 softmaxes first,
@@ -346,8 +332,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     }
     if (t + 1 >= nst) break;
     // iteration t+1: S(t+1) in sB2, computes S(t+2) into sA
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    sync_vm<0>();
     if (t + 3 < nst) issue_k(t + 3);
     if (t + 2 < nst) issue_v(t + 2);
     if (team == 0) {
@@ -360,8 +345,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   }
 
   // Merge team 1 into team 0 through LDS (the tile buffers are free now).
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  sync_vm<0>();
   constexpr int NR = NDB * 16 + 2;
   static_assert(4 * NR * 64 * 4 <= 4 * TILE * 2, "team exchange must fit in the tile buffers");
   float *xch = reinterpret_cast<float *>(sKV) + wt * NR * 64;

@@ -7,154 +7,206 @@
 //     g_t = 1 for a forced token, else sigmoid(s_t).
 //
 // bf16 path: a [d_ff x d] x [d x T] product on the matrix cores (32x32x16 bf16
-// MFMA, fp32 accumulation).  The W1 rows are the MFMA "A" operand and the
+// MFMA, fp32 accumulation).  W1 is the MFMA "A" operand (rows = units) and the
 // token rows the "B" operand, so each lane's accumulator holds 16 units of ONE
 // token: the SiLU * w2 reduction over units is lane-local, then one cross-half
 // shuffle and a 4-way LDS sum across the waves that split the units.  Nothing
 // of the [T, d_ff] activation ever leaves registers.
 //
-// d_ff > 512 loops over 512-unit chunks (the hidden tile is re-read from L2).
+// Data movement.  Every work-group needs all of W1 (2 MB at d = 2048,
+// d_ff = 512) for its token tile, so W1 dominates the bytes a compute unit
+// pulls from L2.  A natural-layout MFMA fragment (32 rows x 16 inputs) touches
+// 32 cache lines; a pack pass therefore first rewrites W1 in fragment order
+// (each fragment one contiguous 1 KB block), which each wave then loads
+// straight into registers, 4 to 8 16-input steps ahead.  Token rows stream
+// from HBM through a 4-stage LDS ring by direct buffer->LDS loads, one full
+// 128-byte line per row per stage.  One wave per SIMD, each holding a
+// 128-unit x 128-token accumulator tile (256 registers).
 #include "tg_common.h"
 
 namespace tg {
 
-constexpr int GS_BU = 512;   // units per work-group chunk
-constexpr int GS_BK = 32;    // d slice per pipeline stage (64-byte rows)
-constexpr int GS_THREADS = 512;
-constexpr int GS_NA = 3;     // W1 slice ring depth (L2-resident operand)
-constexpr int GS_NB = 6;     // hidden slice ring depth (HBM-streamed operand)
+constexpr int GS_U = 512;    // units per work-group chunk (4 waves x 128)
+constexpr int GS_BK = 64;    // inputs per hidden stage (one 128-byte line per token row)
+constexpr int GS_NB = 4;     // hidden ring stages
+constexpr int GS_NA = 8;     // W1 fragment register ring: one slot per 16-input step of a trip
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-__device__ void gs_buffer_load_lds(i32x4 rsrc, lds_u32 *lds, int size, int voffset, int soffset, int offset,
-                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-__device__ __forceinline__ i32x4 gs_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+// Packed W1 geometry: unit groups of 32 (padded to whole 512-unit chunks) x
+// 16-input steps (d padded to whole pairs of 64-input stages).
+__host__ __device__ inline int gate_nkk(int d) { return (d + 2 * GS_BK - 1) / (2 * GS_BK) * (2 * GS_BK / 16); }
+__host__ __device__ inline int gate_ngp(int d_ff) { return (d_ff + GS_U - 1) / GS_U * (GS_U / 32); }
+size_t gate_packed_bytes(int d, int d_ff) { return (size_t)gate_ngp(d_ff) * gate_nkk(d) * 64 * 16; }
+
+// Fragment order: block (ug, kk) is 64 lanes x 8 bf16, lane L holding
+// w1[32 ug + L % 32][16 kk + 8 (L / 32) .. +8] (zero past d_ff or d) -- the
+// A operand of one 32x32x16 MFMA, as one contiguous 1 KB block.  A work-group
+// packs 32 rows x 128 inputs: coalesced row reads into LDS, then eight
+// contiguous 1 KB blocks out.
+__global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__restrict__ w1, int d, int d_ff, int nkk,
+                                                           uint16_t *__restrict__ out) {
+  __shared__ u32x4 t[32][17];  // 32 rows x 16 chunks of 8 inputs (+1 chunk of padding)
+  const int tid = threadIdx.x, kc = blockIdx.x, ug = blockIdx.y;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = tid + 256 * j, row = idx >> 4, c = idx & 15;
+    const int u = 32 * ug + row, k0 = 128 * kc + 8 * c;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (u < d_ff && k0 < d) v = *(const u32x4 *)(w1 + (int64_t)u * d + k0);  // d % 8 == 0: all 8 in range
+    t[row][c] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = tid + 256 * j, b = idx >> 6, L = idx & 63;
+    const int kk = 8 * kc + b;
+    if (kk < nkk) *(u32x4 *)(out + (((int64_t)ug * nkk + kk) * 64 + L) * 8) = t[L & 31][2 * b + (L >> 5)];
+  }
 }
 
-// Work-group tile: 128 tokens x 512 units, 8 waves (2 along tokens x 4 along
-// units), each wave 64 tokens x 128 units (8 accumulators of 32x32).  Slices
-// of 32 d arrive by direct buffer->LDS loads into two rings (W1: 3 stages,
-// hidden: 6 stages, so the HBM stream is prefetched 5 slices ahead).  LDS rows
-// are 64 bytes with the 16-byte chunk XOR-swizzled by (row / 4) % 4, which
-// keeps the 16-row MFMA fragment reads free of bank conflicts.  Out-of-range
-// rows (the ragged token tail, units past d_ff) read as zero.
-template <int TB>  // 32-token blocks per wave: 2 -> 128-token tiles, 1 -> 64-token tiles
-__global__ __launch_bounds__(GS_THREADS) void gate_score_bf16_kernel(
-    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w1, const uint16_t *__restrict__ w2,
-    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, float *__restrict__ scores,
+// Work-group: 4 waves x (128 units x TT tokens), TT = 32 NTB.  Hidden stage st
+// (inputs 64 st .. 64 st + 63 of the tile's TT rows) lives in ring buffer
+// st % 4, rows of 128 bytes with the 16-byte chunk XOR-swizzled by
+// (row / 2) % 8, which keeps the 16-row MFMA fragment reads free of bank
+// conflicts.  Out-of-range rows and inputs read as zero.
+template <int NTB>
+__global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
+    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w1p, const uint16_t *__restrict__ w2,
+    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float *__restrict__ scores,
     float *__restrict__ gates) {
-  constexpr int BT = 64 * TB;               // tokens per work-group
-  constexpr int A_ST = GS_BU * GS_BK;       // u16 per W1 stage (32 KB)
-  constexpr int B_ST = BT * GS_BK;          // u16 per hidden stage
-  constexpr int NBI = BT / 16;               // hidden load instructions per slice (16 rows each): 8 or 4
-  __shared__ __attribute__((aligned(1024))) uint16_t sA[GS_NA * A_ST];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB[GS_NB * B_ST];
-  __shared__ __attribute__((aligned(1024))) uint16_t sDummy[512];  // target of the zero-fill loads of idle waves
-  __shared__ float sRed[4][BT];
+  constexpr int TT = 32 * NTB;         // tokens per work-group
+  constexpr int ST = TT * GS_BK;       // u16 per hidden stage
+  constexpr int NI = TT / 32;          // direct-load instructions (8 rows each) per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t sH[GS_NB * ST];
+  __shared__ float sRed[4][TT];
+  __shared__ float sW2[GS_U];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave & 3;   // unit quarter
-  const int wm = wave >> 2;  // token half
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
-  const int64_t t0 = (int64_t)blockIdx.x * BT;
-  const int nk = d / GS_BK;
-  const uint32_t rowb = (uint32_t)d * 2u;  // bytes per row of hidden / W1
-  // lane part of every direct load: row lane/4 of a 16-row instruction, chunk swizzled by (row / 4) % 4
-  const uint32_t lsw = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  const int64_t trows = T - t0 < BT ? T - t0 : BT;
-  const i32x4 rH = gs_rsrc(hidden + t0 * d, (uint32_t)(trows * rowb));
-  // fragment reads: row r of a stage, logical chunk c -> physical c ^ ((r / 4) % 4); the row's low bits are l32
-  const int fsw = (l32 >> 2) & 3;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int64_t trows = T - t0 < TT ? T - t0 : TT;
+  const uint32_t rowb = 2u * (uint32_t)d;
+  const i32x4 rH = buffer_rsrc(hidden + t0 * d, (uint32_t)(trows * rowb));
+  const int nst = nkk / 4;
 
-  float run = 0.f;  // running score of token t0 + tid (tid < BT), across unit chunks
-
-  for (int u0 = 0; u0 < d_ff; u0 += GS_BU) {
-    const int urows = d_ff - u0 < GS_BU ? d_ff - u0 : GS_BU;
-    const i32x4 rW = gs_rsrc(w1 + (int64_t)u0 * d, (uint32_t)urows * rowb);
-    // W1 slice kt -> ring stage kt % NA: wave w fills rows 64w .. 64w+63 (4 instructions)
-    auto issue_a = [&](int kt) {
-      const bool live = kt < nk;
-      const int stage = kt % GS_NA;
+  // direct loads: instruction i of this wave covers rows 8 (NI wave + i) .. +7;
+  // lane -> row + lane / 8, physical chunk lane % 8, logical chunk (lane % 8) ^ ((row / 2) % 8)
+  uint32_t dvo[NI];
+  int dlc[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 64 * wave + 16 * i;
-        const uint32_t vo = live ? (uint32_t)(r0 + (lane >> 2)) * rowb + lsw : 0xFFFFFFF0u;  // dead: zero fill
-        gs_buffer_load_lds(rW, (lds_u32 *)(sA + stage * A_ST + r0 * GS_BK), 16, (int)vo, live ? kt * GS_BK * 2 : 0, 0, 0);
-      }
-    };
-    // hidden slice kt -> ring stage kt % NB: wave w fills rows 16w .. 16w+15.  Every
-    // wave issues exactly one load per slice (waves past the tile's rows load zeros
-    // into sDummy), so each wave's count of loads in flight is the same.
-    auto issue_b = [&](int kt) {
-      const bool live = kt < nk && wave < NBI;
-      const int r0 = 16 * wave;
-      const uint32_t vo = live ? (uint32_t)(r0 + (lane >> 2)) * rowb + lsw : 0xFFFFFFF0u;
-      uint16_t *dst = wave < NBI ? sB + (kt % GS_NB) * B_ST + r0 * GS_BK : sDummy;
-      gs_buffer_load_lds(rH, (lds_u32 *)dst, 16, (int)vo, live ? kt * GS_BK * 2 : 0, 0, 0);
+  for (int i = 0; i < NI; ++i) {
+    const int row = 8 * (NI * wave + i) + (lane >> 3);
+    dlc[i] = (lane & 7) ^ ((row >> 1) & 7);
+    dvo[i] = (uint32_t)row * rowb + 16u * (uint32_t)dlc[i];
+  }
+  // hidden stage st -> ring buffer st % 4 (past the end: zero fill)
+  auto issue_h = [&](int st) {
+    const uint32_t lbase = lds_addr(sH) + 2u * (uint32_t)((st % GS_NB) * ST);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool ok = st < nst && GS_BK * st + 8 * dlc[i] < d;
+      dma_b128(rH, lbase + 2u * (uint32_t)(8 * (NI * wave + i) * GS_BK), ok ? dvo[i] + 128u * (uint32_t)st : 0x80000000u,
+               0u);
+    }
+  };
+  // B fragment offsets (u16) within a stage: token row 32 tb + l32, logical chunk 2 s + hl
+  int brow[NTB], bsw[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int row = 32 * tb + l32;
+    brow[tb] = row * GS_BK;
+    bsw[tb] = (row >> 1) & 7;
+  }
+
+  float run = 0.f;  // running score of token t0 + tid (tid < TT), across unit chunks
+
+  for (int c = 0; c < d_ff; c += GS_U) {
+    for (int i = tid; i < GS_U; i += 256) sW2[i] = c + i < d_ff ? __uint_as_float((uint32_t)w2[c + i] << 16) : 0.f;
+    // this wave's unit groups: c / 32 + 4 wave + ub, ub = 0..3
+    const uint16_t *ap = w1p + ((int64_t)(c / 32 + 4 * wave) * nkk) * 512 + lane * 8;
+    auto load_a1 = [&](int kk, int ub) {
+      const int kc = kk < nkk ? kk : nkk - 1;  // past the end: any valid block, never used
+      return *(const u32x4 *)(ap + ((int64_t)ub * nkk + kc) * 512);
     };
 
-    f32x16 acc[4][TB];
+    f32x16 acc[4][NTB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < NTB; ++j) acc[i][j] = f32x16{};
 
-    // Prologue: hidden slices 0..2, then the batches of "iterations" -2 and -1.
-    // Every iteration issues one batch {W1(kt+2), hidden(kt+5)} (dead slices load
-    // zeros), so the number of loads issued after W1(kt) is constant.
-    issue_b(0);
-    issue_b(1);
-    issue_b(2);
-    issue_a(0);
-    issue_b(3);
-    issue_a(1);
-    issue_b(4);
-    for (int kt = 0; kt < nk; ++kt) {
-      // outstanding after W1(kt): hidden(kt+3) and the 5 loads of iteration kt-1
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-      __syncthreads();  // slice kt landed for every wave; every wave is done with slice kt-1
-      issue_a(kt + 2);
-      issue_b(kt + 5);
-      const uint16_t *A = sA + (kt % GS_NA) * A_ST;
-      const uint16_t *Bt = sB + (kt % GS_NB) * B_ST;
+    // The K loop runs in trips of 8 16-input steps (two hidden stages), with
+    // the W1 fragments of trip step j in register slot j.  Right after step
+    // j's products have used slot j, the slot is reloaded with the next trip's
+    // step j: four loads per step, each eight steps ahead of its use.  The
+    // compiler cannot follow loads across the loop edge; it would wait for
+    // every load in flight at the first use of a slot in a new trip (stalling
+    // on loads issued a step earlier).  So at the end of a trip slots 0..3
+    // (loaded four or more steps earlier) are marked used -- the wait for
+    // them happens there, exactly -- and the first use of slots 4..7 comes
+    // only after sixteen newer loads, so that wait too covers old loads only.
+    // One barrier per trip: the trip's two hidden stages landed for every
+    // wave and every wave is done with the previous trip; then the direct
+    // loads of the next trip's stages go out.
+    u32x4 a[GS_NA][4];
+    auto touch03 = [&]() {
+      asm volatile("" ::"v"(a[0][0]), "v"(a[0][1]), "v"(a[0][2]), "v"(a[0][3]), "v"(a[1][0]), "v"(a[1][1]),
+                   "v"(a[1][2]), "v"(a[1][3]));
+      asm volatile("" ::"v"(a[2][0]), "v"(a[2][1]), "v"(a[2][2]), "v"(a[2][3]), "v"(a[3][0]), "v"(a[3][1]),
+                   "v"(a[3][2]), "v"(a[3][3]));
+    };
+    issue_h(0);
+    issue_h(1);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int pc = ((2 * ks + hl) ^ fsw) << 3;
-        u32x4 a[4], b[TB];
+    for (int j = 0; j < GS_NA; ++j)
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) a[ub] = *(const u32x4 *)(A + (wn * 128 + ub * 32 + l32) * GS_BK + pc);
+      for (int ub = 0; ub < 4; ++ub) a[j][ub] = load_a1(j, ub);
+    touch03();
+    for (int st = 0; st < nst; st += 2) {  // nst is even
+      const int k0 = 4 * st;               // first 16-input step of the trip
+      // at most the 16 loads of steps 4..7 of the previous trip (or of the
+      // prologue) may be in flight: the direct loads of this trip's stages,
+      // issued before them, are done
+      sync_vm<16>();
+      issue_h(st + 2);
+      issue_h(st + 3);
+      u32x4 b[2][NTB];
+      auto read_b = [&](int j, u32x4(&dst)[NTB]) {  // B fragments of trip step j
+        const uint16_t *H = sH + ((st + (j >> 2)) % GS_NB) * ST;
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) b[tb] = *(const u32x4 *)(Bt + (wm * 32 * TB + tb * 32 + l32) * GS_BK + pc);
+        for (int tb = 0; tb < NTB; ++tb)
+          dst[tb] = *(const u32x4 *)(H + brow[tb] + (((2 * (j & 3) + hl) ^ bsw[tb]) << 3));
+      };
+      read_b(0, b[0]);
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub)
+      for (int j = 0; j < GS_NA; ++j) {
+        if (j < GS_NA - 1) read_b(j + 1, b[(j + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int tb = 0; tb < TB; ++tb) acc[ub][tb] = mfma32(a[ub], b[tb], acc[ub][tb]);
+        for (int ub = 0; ub < 4; ++ub) {
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) acc[ub][tb] = mfma32(a[j][ub], b[j & 1][tb], acc[ub][tb]);
+          __builtin_amdgcn_sched_barrier(0);
+          a[j][ub] = load_a1(k0 + GS_NA + j, ub);  // slot j, ub: used up; next trip's step j
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      touch03();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the dead tail loads
+    // drain the tail loads before the ring is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: SiLU, times w2, summed over this lane's units.
-    float part[TB];
+    float part[NTB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) part[tb] = 0.f;
+    for (int tb = 0; tb < NTB; ++tb) part[tb] = 0.f;
 #pragma unroll
     for (int ub = 0; ub < 4; ++ub) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ubase = u0 + wn * 128 + ub * 32 + 8 * g4 + 4 * hl;  // 4 consecutive units
-        float wv[4];
+        // registers 4 g4 .. 4 g4 + 3 hold units 32 ub + 8 g4 + 4 hl + e
+        const f32x4 wv = *(const f32x4 *)&sW2[wave * 128 + ub * 32 + 8 * g4 + 4 * hl];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int u = ubase + e;
-          wv[e] = (u < d_ff) ? __uint_as_float((uint32_t)w2[u] << 16) : 0.f;
-        }
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
+        for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = acc[ub][tb][g4 * 4 + e];
@@ -165,16 +217,16 @@ __global__ __launch_bounds__(GS_THREADS) void gate_score_bf16_kernel(
       }
     }
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
+    for (int tb = 0; tb < NTB; ++tb) {
       part[tb] += __shfl_xor(part[tb], 32);
-      if (hl == 0) sRed[wn][wm * 32 * TB + tb * 32 + l32] = part[tb];
+      if (hl == 0) sRed[wave][32 * tb + l32] = part[tb];
     }
     __syncthreads();
-    if (tid < BT) run += (sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]);
+    if (tid < TT) run += (sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]);
     __syncthreads();
   }
 
-  if (tid < BT) {
+  if (tid < TT) {
     const int64_t t = t0 + tid;
     if (t < T) {
       scores[t] = run;
@@ -216,20 +268,29 @@ __global__ __launch_bounds__(256) void gate_score_f32_kernel(
   }
 }
 
+hipError_t launch_gate_pack_w1(const void *w1, int d, int d_ff, void *packed, hipStream_t s) {
+  const int nkk = gate_nkk(d);
+  hipLaunchKernelGGL(gate_pack_w1_kernel, dim3((unsigned)((nkk + 7) / 8), (unsigned)gate_ngp(d_ff)), dim3(256), 0, s,
+                     (const uint16_t *)w1, d, d_ff, nkk, (uint16_t *)packed);
+  return hipGetLastError();
+}
+
+// bf16: w1 is the packed copy (gate_pack_w1_kernel); f32: natural layout.
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2,
                              const uint8_t *forced, int64_t T, int d, int d_ff, bool bf16,
                              float *scores, float *gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16) {
-    const int64_t tiles128 = (T + 127) / 128;
-    if (tiles128 >= 256) {
-      hipLaunchKernelGGL(gate_score_bf16_kernel<2>, dim3((unsigned)tiles128), dim3(GS_THREADS), 0, s,
-                         (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced,
-                         T, d, d_ff, scores, gates);
+    const int nkk = gate_nkk(d);
+    // 128-token tiles when they still fill the 256 compute units, else 64
+    if ((T + 127) / 128 >= 256) {
+      hipLaunchKernelGGL(gate_score_bf16_kernel<4>, dim3((unsigned)((T + 127) / 128)), dim3(256), 0, s,
+                         (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff,
+                         nkk, scores, gates);
     } else {
-      hipLaunchKernelGGL(gate_score_bf16_kernel<1>, dim3((unsigned)((T + 63) / 64)), dim3(GS_THREADS), 0,
-                         s, (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced,
-                         T, d, d_ff, scores, gates);
+      hipLaunchKernelGGL(gate_score_bf16_kernel<2>, dim3((unsigned)((T + 63) / 64)), dim3(256), 0, s,
+                         (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff,
+                         nkk, scores, gates);
     }
   } else {
     hipLaunchKernelGGL(gate_score_f32_kernel, dim3((unsigned)T), dim3(256), (size_t)d * sizeof(float), s,

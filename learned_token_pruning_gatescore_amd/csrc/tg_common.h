@@ -58,6 +58,55 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Direct buffer -> LDS loads.  Lane l's bytes land at lds + l * size; offsets
+// past the resource's num_records read as zero.  They are issued through
+// inline assembly so that the compiler does not track them: it would
+// otherwise wait for every load in flight before each LDS read of ANY buffer
+// (it cannot tell the ring stages apart), which drains the prefetch pipeline.
+// Callers order them with sync_vm<N>(): wait until at most N vector-memory
+// loads of this wave are in flight, then a work-group barrier.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// A wave-uniform value in scalar registers (the resource, the LDS address and
+// soffset must be the same for every lane of the wave).
+__device__ __forceinline__ i32x4 uniform(const i32x4 &r) {
+  return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+
+// lds is an LDS byte address (see lds_addr).
+__device__ __forceinline__ void dma_b128(const i32x4 &rsrc, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(uniform(rsrc)),
+                  "s"(__builtin_amdgcn_readfirstlane(soffset))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const i32x4 &rsrc, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(uniform(rsrc)),
+                  "s"(__builtin_amdgcn_readfirstlane(soffset))
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding and
+// every LDS access of this wave has completed, then a work-group barrier.
+// Also a compiler barrier for memory operations.
+template <int N>
+__device__ __forceinline__ void sync_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }

@@ -56,12 +56,28 @@ MIS = ctypes.c_void_p(0x10008)    # misaligned
 
 def test_gate_score_validation():
     lib = _lib()
-    st = lib.tg_gate_score(None, FAKE, FAKE, None, 1, 10, 32, 16, 1, FAKE, None, None)
+    g = lambda *a, ws=None, wsb=0: lib.tg_gate_score(*a, ws, wsb, None)
+    st = g(None, FAKE, FAKE, None, 1, 10, 32, 16, 1, FAKE, None)
     assert st == 1 and b"required" in lib.tg_last_error()
-    assert lib.tg_gate_score(FAKE, FAKE, FAKE, None, 1, 10, 0, 16, 1, FAKE, None, None) == 1
-    assert lib.tg_gate_score(FAKE, FAKE, FAKE, None, 1, 10, 48, 16, 1, FAKE, None, None) == 2  # bf16 d % 32
-    assert lib.tg_gate_score(FAKE, FAKE, FAKE, None, 1, 10, 32, 16, 7, FAKE, None, None) == 1  # dtype
-    assert lib.tg_gate_score(MIS, FAKE, FAKE, None, 1, 10, 32, 16, 1, FAKE, None, None) == 1  # alignment
+    assert g(FAKE, FAKE, FAKE, None, 1, 10, 0, 16, 1, FAKE, None) == 1
+    assert g(FAKE, FAKE, FAKE, None, 1, 10, 48, 16, 1, FAKE, None) == 2  # bf16 d % 32
+    assert g(FAKE, FAKE, FAKE, None, 1, 10, 32, 16, 7, FAKE, None) == 1  # dtype
+    assert g(MIS, FAKE, FAKE, None, 1, 10, 32, 16, 1, FAKE, None) == 1  # alignment
+    # bf16 needs the fragment-order workspace: d_ff rounded up to 512 units, d to 128 inputs
+    need = lib.tg_gate_score_workspace_size(2048, 512, 1)
+    assert need == 512 * 2048 * 2
+    assert lib.tg_gate_score_workspace_size(32, 16, 1) == 512 * 128 * 2
+    assert lib.tg_gate_score_workspace_size(2048, 512, 0) == 0
+    assert lib.tg_gate_score_workspace_size(0, 512, 1) == 0
+    assert g(FAKE, FAKE, FAKE, None, 1, 10, 2048, 512, 1, FAKE, None) == 3
+    assert g(FAKE, FAKE, FAKE, None, 1, 10, 2048, 512, 1, FAKE, None, ws=FAKE, wsb=need - 1) == 3
+    assert g(FAKE, FAKE, FAKE, None, 0, 10, 2048, 512, 1, FAKE, None, ws=FAKE, wsb=need) == 0  # B = 0
+    # packed pair
+    assert lib.tg_gate_pack_w1(FAKE, 2048, 512, 0, FAKE, need, None) == 2            # f32 not packed
+    assert lib.tg_gate_pack_w1(FAKE, 2048, 512, 1, FAKE, need - 16, None) == 3       # too small
+    assert lib.tg_gate_pack_w1(None, 2048, 512, 1, FAKE, need, None) == 1
+    assert lib.tg_gate_score_packed(FAKE, FAKE, FAKE, None, 1, 10, 2048, 512, 0, FAKE, None, None) == 2
+    assert lib.tg_gate_score_packed(FAKE, FAKE, FAKE, None, 1, 10, 48, 512, 1, FAKE, None, None) == 2
 
 
 def test_select_validation():

@@ -44,13 +44,58 @@ def test_gate_score_tiny_f32():
     assert np.all(g[:32] == 1.0)
 
 
-@pytest.mark.parametrize("N,d,d_ff", [(1000, 256, 96), (77, 64, 512), (300, 128, 640), (4099, 2048, 512)])
-def test_gate_score_bf16_shapes(N, d, d_ff):
-    w = wl.Workload("shape", 11, B=2, N=N, n_forced=5, d=d, d_ff=d_ff, Ks=(1,), Hq=1, Hkv=1, D=64, tau=1.0,
+# d % 64 == 32 leaves half of the last 64-input stage past d; d_ff not a
+# multiple of 32 leaves padded units; N = 33001 (B = 1) takes the 128-token
+# tiles (>= 256 of them) with a ragged last tile; the others the 64-token tiles.
+@pytest.mark.parametrize("B,N,d,d_ff", [(2, 1000, 256, 96), (2, 77, 64, 512), (2, 300, 128, 640), (2, 4099, 2048, 512),
+                                        (2, 513, 96, 100), (3, 129, 160, 33), (1, 1, 32, 1), (1, 33001, 128, 200)])
+def test_gate_score_bf16_shapes(B, N, d, d_ff):
+    w = wl.Workload("shape", 11, B=B, N=N, n_forced=min(5, N), d=d, d_ff=d_ff, Ks=(1,), Hq=1, Hkv=1, D=64, tau=1.0,
                     dtype="bf16", rope=False)
     s, g, sr, gr = _score(w)
     assert_scores_close(s, sr, 1e-2)
     assert_scores_close(g, gr, 1e-2, "gates")
+
+
+def test_gate_pack_layout_and_packed_path():
+    """The packed copy follows the documented fragment order bit for bit, and
+    scoring from it is bit-identical to tg_gate_score."""
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    dev = device()
+    w = wl.Workload("pack", 12, B=2, N=700, n_forced=9, d=96, d_ff=70, Ks=(1,), Hq=1, Hkv=1, D=64, tau=1.0,
+                    dtype="bf16", rope=False)
+    gi = wl.gate_inputs(w)
+    h = dev_tensor(gi["hidden"], w.dtype, dev)
+    w1 = dev_tensor(gi["w1"], w.dtype, dev)
+    w2 = dev_tensor(gi["w2"], w.dtype, dev)
+    f = torch.from_numpy(gi["forced"]).to(dev)
+    nb = tg.tg_gate_score_workspace_size(w.d, w.d_ff, True)
+    packed = torch.full((nb,), 0xAB, dtype=torch.uint8, device=dev)
+    say("gate_pack", w.d, w.d_ff, nb)
+    tg.tg_gate_pack_w1(w1, packed)
+    torch.cuda.synchronize()
+    # expected layout from the header's definition: block (ug, kk), lane L holds
+    # w1[32 ug + L % 32][16 kk + 8 (L // 32) .. +8], zero outside [d_ff, d]
+    ngp = -(-w.d_ff // 512) * 16
+    nkk = -(-w.d // 128) * 8
+    assert nb == ngp * nkk * 64 * 16
+    wb = np.zeros((ngp * 32, nkk * 16), np.uint16)
+    wb[:w.d_ff, :w.d] = gi["w1"]
+    exp = wb.reshape(ngp, 32, nkk, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    got = to_np(packed).view(np.uint16)
+    assert np.array_equal(got, exp)
+    B, n = gi["forced"].shape
+    s1 = torch.empty((B, n), device=dev)
+    g1 = torch.empty((B, n), device=dev)
+    s2 = torch.empty((B, n), device=dev)
+    g2 = torch.empty((B, n), device=dev)
+    tg.tg_gate_score(h, w1, w2, f, s1, g1)
+    tg.tg_gate_score_packed(h, packed, w.d_ff, w2, f, s2, g2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(s1).view(np.uint32), to_np(s2).view(np.uint32))
+    assert np.array_equal(to_np(g1).view(np.uint32), to_np(g2).view(np.uint32))
 
 
 def test_gate_score_qwen3_8k_full():
