@@ -45,9 +45,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
                                                         const float *__restrict__ gamma,
                                                         const int32_t *__restrict__ pos, InvFreq inv, int64_t rows,
                                                         int M, int Hq, int Hkv, int D, float2 *__restrict__ cs,
-                                                        uint16_t *__restrict__ khat, float *__restrict__ bias) {
+                                                        uint16_t *__restrict__ khat, float *__restrict__ bias,
+                                                        int *__restrict__ cnt, int ncnt) {
   const int half = D / 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, rotary pair)
+  if (idx < ncnt) cnt[idx] = 0;  // the split-row arrival counters of the forward kernel
   if (idx >= rows * half) return;
   const int64_t r = idx / half;  // b * M + j
   const int i = (int)(idx % half);
@@ -111,109 +113,174 @@ struct Tile {
 };
 
 
-// Work-group: 8 waves = two teams of 4.  The 4 waves of a team own the 128
-// columns; each 128-key super-tile is split between the teams (team t takes
-// keys 64t..64t+63), so a query block's key chain is walked in half the steps
-// and each SIMD holds one wave of each team.  The teams merge (max, sum, O)
-// through LDS at the end.  Tiles arrive by direct buffer->LDS loads issued one
-// super-tile ahead; every per-lane address is computed once before the loop.
+// ---------------------------------------------------------------------------
+// bf16 forward.  Work-group = 4 waves (one per SIMD) = 256 columns, a column
+// being a (query, head) pair of the GQA group: BQ = 256 / G queries x G
+// heads.  Wave w owns columns 64w .. 64w+63 as two 32-column blocks (cb); a
+// block lies in one head.  Keys come in 32-key tiles.
+//
+// Per tile a wave runs 16 products for S^T = K Q^T (each K fragment read
+// from LDS feeds both column blocks) and 16 for O^T += V^T P^T, and the
+// softmax of 32 logits per lane.  The loop is pipelined two deep: iteration
+// t issues the products of S(t+1) and of P(t-1) V(t-1) and, in the same
+// basic block, the softmax of S(t), so the matrix cores and the vector ALU of
+// one wave overlap.  P(t) is computed with the running maximum before tile t;
+// only when a logit exceeds it by more than 8 (log2 units) is the maximum
+// raised, O and the sum rescaled and P(t) recomputed (rare branch).
+//
+// Long causal rows are split along the keys into pieces (at most C tiles
+// each, the diagonal in the last piece) so that the work spreads over every
+// compute unit.  Each piece of a split query block writes its unnormalised
+// (O, max, sum) to the workspace and bumps a per-block counter; the last to
+// arrive merges all pieces in piece order (deterministic) and writes o, lse.
+// ---------------------------------------------------------------------------
+constexpr int AF_TK = 32;  // keys per tile
+
 template <int D>
-__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
+struct FwdCfg {
+  static constexpr int NDB = D / 32;           // 32-row blocks of O^T
+  static constexpr int NKS = D / 16;           // 16-wide steps over the head dim
+  static constexpr int TILE = AF_TK * D;       // u16 per K or V tile
+  static constexpr int NIW = AF_TK / Tile<D>::RPI / 4;  // direct loads per wave per K (or V) tile
+  static constexpr int NVM = 2 * NIW + 1;      // direct loads per wave per iteration (K, V, bias)
+  static constexpr int NR = 2 * NDB * 16 + 4;  // floats per lane in a partial record
+};
+
+// Tiles of query block qb (keys 0 .. min((qb+1) BQ, M) - 1) and its pieces.
+__host__ __device__ inline int fwd_ntiles(int qb, int BQ, int M) {
+  const int qe = (qb + 1) * BQ < M ? (qb + 1) * BQ : M;
+  return (qe + AF_TK - 1) / AF_TK;
+}
+__host__ __device__ inline int fwd_npieces(int n, int C) { return (n + C - 1) / C; }
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, const float2 *__restrict__ cs, float c2, int B, int M, int Hq, int Hkv, int G,
-    int BQ, int nqb, uint16_t *__restrict__ o, float *__restrict__ lse) {
+    int BQ, int nqb, int C, float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o,
+    float *__restrict__ lse) {
   using T = Tile<D>;
-  constexpr int NKS = D / 16;        // 16-wide k steps over the head dim
-  constexpr int NDB = D / 32;        // 32-row blocks of O^T
-  constexpr int HALF = D / 2;
-  constexpr int TK = 128;            // keys per super-tile
-  constexpr int GMAX = 8;            // query heads per kv head handled here
-  constexpr int TILE = TK * D;       // u16 elements per K (or V) super-tile
-  constexpr int NIW = TK / T::RPI / 8;  // direct-load instructions per wave per K (or V) super-tile
-  // K tiles (2 buffers) then V tiles (2 buffers); reused for the team merge
-  __shared__ __attribute__((aligned(1024))) uint16_t sKV[4 * TILE];
-  __shared__ __attribute__((aligned(16))) float sB[2][GMAX][TK];
+  using F = FwdCfg<D>;
+  constexpr int NDB = F::NDB, NKS = F::NKS, HALF = D / 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * F::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * F::TILE];
+  __shared__ __attribute__((aligned(1024))) float sBias[3][8][AF_TK];
+  __shared__ __attribute__((aligned(1024))) float sDummy[256];  // target of the other waves' bias loads
+  __shared__ int sLast;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int team = wave >> 2, wt = wave & 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int l32 = lane & 31, hl = lane >> 5;
   const int nbh = B * Hkv;
-  const int idx = blockIdx.x;
-  const int qb = nqb - 1 - idx / nbh;  // longest causal rows first
-  const int bh = idx % nbh;
+  // consecutive work-groups take consecutive (batch, kv head): with the
+  // round-robin placement over the 8 XCDs one head's keys stay in one L2
+  const int bh = blockIdx.x % nbh;
   const int b = bh / Hkv, kvh = bh % Hkv;
+
+  // Piece -> (query block, piece index).  Pieces are listed by descending query
+  // block (longest rows first); each wave scans 64 blocks at a time.
+  int qb = 0, p = 0, np = 1, pfirst = 0;
+  {
+    int rem = blockIdx.x / nbh, base = 0;
+    for (int c0 = 0; c0 < nqb; c0 += 64) {
+      const int qq = nqb - 1 - (c0 + lane);
+      const int mine = qq >= 0 ? fwd_npieces(fwd_ntiles(qq, BQ, M), C) : 0;
+      int incl = mine;
+      for (int o2 = 1; o2 < 64; o2 <<= 1) {
+        const int y = __shfl_up(incl, o2);
+        if (lane >= o2) incl += y;
+      }
+      const int tot = __shfl(incl, 63);
+      if (rem < tot) {
+        const int src = __ffsll((unsigned long long)__ballot(incl > rem)) - 1;
+        const int excl = __shfl(incl - mine, src);
+        qb = nqb - 1 - (c0 + src);
+        np = __shfl(mine, src);
+        p = rem - excl;
+        pfirst = base + excl;
+        break;
+      }
+      rem -= tot;
+      base += tot;
+    }
+  }
+  const int ntq = fwd_ntiles(qb, BQ, M);
+  const int kt0 = p * ntq / np, nt = (p + 1) * ntq / np - kt0;  // this piece: tiles kt0 .. kt0+nt-1
   const int q0 = qb * BQ;
-  const int col = wt * 32 + l32;
-  const int hloc = col / BQ;
-  const int hq = kvh * G + hloc;
-  const int qi = q0 + col % BQ;
-  const bool vq = qi < M;
-  const int qmax = min(q0 + BQ, M) - 1;
-  const int nst = qmax / TK + 1;
+  // tiles from here on hold keys past some query of the block: causal mask
+  const int tdiag = (q0 / AF_TK - kt0) > 0 ? q0 / AF_TK - kt0 : 0;
+
+  int hloc[2], qi[2];
+  bool vq[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int c0 = 64 * wave + 32 * cb;
+    hloc[cb] = c0 / BQ;
+    qi[cb] = q0 + c0 % BQ + l32;
+    vq[cb] = qi[cb] < M;
+  }
   const int64_t bM = (int64_t)b * M;
   const uint32_t rsb = (uint32_t)(Hkv * D * 2);  // bytes between consecutive keys
   const uint32_t kv_bytes = (uint32_t)(M - 1) * rsb + D * 2;
   const i32x4 rK = buffer_rsrc(khat + (bM * Hkv + kvh) * D, kv_bytes);
   const i32x4 rV = buffer_rsrc(v + (bM * Hkv + kvh) * D, kv_bytes);
-  const i32x4 rB = buffer_rsrc(bias + ((int64_t)b * Hq + (int64_t)kvh * G) * M, (uint32_t)(G * M * 4));
-  // per-lane byte offset of this wave's direct-load instruction i: row * rsb +
-  // swizzled chunk; row = (wave * NIW + i) * RPI + lane / C
-  const uint32_t lrow = (uint32_t)(wave * NIW * T::RPI + lane / T::C) * rsb;
-  const int lpc = lane % T::C;
-  auto kofs = [&](int i) {
-    const int row = (wave * NIW + i) * T::RPI + lane / T::C;
-    return lrow + (uint32_t)(i * T::RPI) * rsb + ((lpc ^ T::kswz(row)) << 4);
-  };
-  auto vofs = [&](int i) {
-    const int row = (wave * NIW + i) * T::RPI + lane / T::C;
-    return lrow + (uint32_t)(i * T::RPI) * rsb + ((lpc ^ T::vswz(row)) << 4);
-  };
-  // highest query among this wave's columns (the causal limit of its keys)
-  int wq = vq ? qi : -1;
-  for (int o2 = 32; o2 > 0; o2 >>= 1) wq = max(wq, __shfl_xor(wq, o2));
+  const i32x4 rB = buffer_rsrc(bias + (int64_t)b * Hq * M, (uint32_t)(Hq * M * 4));
 
-  // Buffers: K super-tile t lives in K buffer t % 2, V super-tile t (with its
-  // bias rows) in V buffer t % 2.  The K stream runs one super-tile ahead of V:
-  // iteration t computes S(t+1) from K(t+1) while it turns S(t) into P(t) and
-  // multiplies P(t) by V(t).
-  auto issue_k = [&](int t) {
-    const int soff = t * TK * (int)rsb;
+  // Direct loads.  Tile t of the piece (key tile kt0 + t) lives in ring slot
+  // t % 3.  Iteration i issues K(i+3), V(i+1) and bias(i+2) (slots freed by
+  // iteration i-1); slots of tiles outside the piece are zero-filled.
+  // per-lane byte offsets within a tile (row of instruction i, swizzled chunk)
+  uint32_t kvo[F::NIW], vvo[F::NIW];
 #pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      dma_b128(rK, lds_addr(sKV) + 2u * (uint32_t)((t & 1) * TILE + (wave * NIW + i) * 512), kofs(i), (uint32_t)soff);
+  for (int i = 0; i < F::NIW; ++i) {
+    const int row = (wave * F::NIW + i) * T::RPI + lane / T::C;
+    kvo[i] = (uint32_t)row * rsb + ((uint32_t)((lane % T::C) ^ T::kswz(row)) << 4);
+    vvo[i] = (uint32_t)row * rsb + ((uint32_t)((lane % T::C) ^ T::vswz(row)) << 4);
+  }
+  // bias: wave 0 loads the G rows (8 lanes x 16 bytes per head); the other
+  // waves issue one load too (zeros, into sDummy) so every wave's count is fixed
+  const bool breal = wave == 0 && (lane >> 3) < G;
+  const uint32_t bvo = (uint32_t)((((lane >> 3) * M) + 4 * (lane & 7)) * 4);
+  auto slot = [](int t) __attribute__((always_inline)) { return ((t % 3) + 3) % 3; };
+  auto issue_kv = [&](int t, bool is_v) __attribute__((always_inline)) {
+    const bool live = t >= 0 && t < nt;
+    const uint32_t toff = (uint32_t)((kt0 + t) * AF_TK) * rsb;  // uniform
+    const uint32_t lb = lds_addr(is_v ? sV : sK) + 2u * (uint32_t)(slot(t) * F::TILE);
+#pragma unroll
+    for (int i = 0; i < F::NIW; ++i)
+      dma_b128(is_v ? rV : rK, lb + 2u * (uint32_t)((wave * F::NIW + i) * T::RPI * D),
+               live ? (is_v ? vvo[i] : kvo[i]) + toff : 0x80000000u, 0u);
   };
-  auto issue_v = [&](int t) {
-    const int j0 = t * TK;
-    const int soff = j0 * (int)rsb;
-#pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      dma_b128(rV, lds_addr(sKV) + 2u * (uint32_t)((2 + (t & 1)) * TILE + (wave * NIW + i) * 512), vofs(i),
-               (uint32_t)soff);
-    // bias rows: G x 128 floats, 64 floats per 4-byte direct-load instruction
-    for (int ii = wave; ii < 2 * G; ii += 8)
-      dma_b32(rB, lds_addr(&sB[t & 1][ii >> 1][(ii & 1) * 64]), (uint32_t)(((ii >> 1) * M + (ii & 1) * 64 + lane) * 4),
-              (uint32_t)(j0 * 4));
+  auto issue_bias = [&](int t) __attribute__((always_inline)) {
+    const bool live = t >= 0 && t < nt;
+    const uint32_t toff = (uint32_t)((kvh * G * M + (kt0 + t) * AF_TK) * 4);  // uniform
+    dma_b128(rB, wave == 0 ? lds_addr(&sBias[slot(t)][0][0]) : lds_addr(sDummy),
+             live && breal ? bvo + toff : 0x80000000u, 0u);
   };
-  issue_k(0);
-  issue_v(0);
-  if (nst > 1) issue_k(1);
-
-  // Q fragments (MFMA B operand): lane holds q^[qi, hq, 16ks + 8hl .. +8].
-  u32x4 qf[NKS];
-  const uint16_t *qrow = q + ((bM + qi) * Hq + hq) * D;
+  auto issue_group = [&](int i) __attribute__((always_inline)) {
+    issue_kv(i + 3, false);
+    issue_kv(i + 1, true);
+    issue_bias(i + 2);
+  };
+  // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8] of each column block
+  u32x4 qf[2][NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = vq ? *(const u32x4 *)(qrow + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
-  if (cs && vq) {
+  for (int cb = 0; cb < 2; ++cb) {
+    const uint16_t *qrow = q + ((bM + qi[cb]) * Hq + kvh * G + hloc[cb]) * D;
 #pragma unroll
-    for (int ks = 0; ks < NKS / 2; ++ks) rope_chunk(qf[ks], qf[ks + NKS / 2], cs + (bM + qi) * HALF + 16 * ks + 8 * hl);
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[cb][ks] = vq[cb] ? *(const u32x4 *)(qrow + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+    if (cs && vq[cb]) {
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks)
+        rope_chunk(qf[cb][ks], qf[cb][ks + NKS / 2], cs + (bM + qi[cb]) * HALF + 16 * ks + 8 * hl);
+    }
   }
 
-  // LDS element offsets of this lane's fragment reads (within a team's 64-row half tile)
-  // K: row kb*32 + l32 (swizzle depends on l32 only), logical chunk 2ks + hl.
+  // fragment-read offsets: K row l32, logical chunk 2ks + hl; V transposing
+  // reads as in the tile layout notes above
   const int krow = l32 * D;
   const int kx = T::kswz(l32);
-  // V (transposing read): source lane li = 4kq + cc of 16-lane group gi reads key
-  // kb*32 + 16hf + 8rr + 4hl + kq, d = 32db + 16(gi%2) + 4cc; swizzle depends on kq only.
   const int gi = lane >> 4, li = lane & 15, kq = li >> 2, cc = li & 3;
   int vlo[NDB];
 #pragma unroll
@@ -222,165 +289,251 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     vlo[db] = (4 * hl + kq) * D + (((dd >> 3) ^ T::vswz(kq)) << 3) + (dd & 7);
   }
 
-  // S^T = K Q^T for this team's 64 keys of super-tile t (raw dot products).
-  auto qk = [&](int t, f32x16(&s)[2]) {
-    const uint16_t *K = sKV + (t & 1) * TILE + 64 * team * D;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  f32x16 acc[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
+  // m2: reference maximum of each column (the probabilities are 2^(x - m2))
+  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  auto mref = [&](int cb) __attribute__((always_inline)) { return m2[cb] == -INFINITY ? 0.f : m2[cb]; };
+
+  auto qk = [&](int t, f32x16(&s)[2]) __attribute__((always_inline)) {  // raw dot products S(t)^T
+    const uint16_t *K = sK + slot(t) * F::TILE;
+    s[0] = s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      const u32x4 a = *(const u32x4 *)(K + krow + (((2 * ks + hl) ^ kx) << 3));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 a = *(const u32x4 *)(K + kb * 32 * D + krow + (((2 * ks + hl) ^ kx) << 3));
-        s[kb] = mfma32(a, qf[ks], s[kb]);
-      }
+      for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32(a, qf[cb][ks], s[cb]);
     }
   };
-
-  float m2 = -INFINITY, lsum = 0.f;
-  f32x16 acc[NDB];
+  // O^T += V(t)^T P(t)^T.  P slot 8hl + e of step hf is key 16hf + 8(e/4) + 4hl + e%4,
+  // which is register 8hf + e of the S accumulator.
+  auto pv = [&](int t, const u32x4(&pp)[2][2]) __attribute__((always_inline)) {
+    const uint16_t *V = sV + slot(t) * F::TILE;
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-
-  // softmax of S(t) in `s` and O^T += V(t)^T P(t)^T
-  auto attend = [&](int t, f32x16(&s)[2]) {
-    const int j0 = t * TK + 64 * team;  // this team's first key
-    if (j0 > wq) return;                // every key after every query of this wave
-    const uint16_t *V = sKV + (2 + (t & 1)) * TILE + 64 * team * D;
-    const float *bi = &sB[t & 1][hloc][64 * team];
-    // logits: x = s * c2 + bias (bias is -inf for g = 0); causal mask on the diagonal
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int db = 0; db < NDB; ++db) {
+        u32x2 pr[2];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 bv = *(const f32x4 *)(bi + kb * 32 + 8 * g4 + 4 * hl);
+        for (int rr = 0; rr < 2; ++rr)
+          pr[rr] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + (16 * hf + 8 * rr) * D + vlo[db])));
+        const u32x4 a = {pr[0][0], pr[0][1], pr[1][0], pr[1][1]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[kb][4 * g4 + e] = __builtin_fmaf(s[kb][4 * g4 + e], c2, bv[e]);
+        for (int cb = 0; cb < 2; ++cb) acc[db][cb] = mfma32(a, pp[cb][hf], acc[db][cb]);
       }
-    }
-    if (j0 + 63 > q0) {  // diagonal tile: keys after the query get -inf
-      const int lim = qi - j0;
+  };
+  // One iteration: wait for group t-2, issue group t, then, interleaved by hand
+  // in 16 slots (sched_barrier keeps the order): the products of S(t+1) and of
+  // P(t-1) V(t-1), one of each per slot, and the softmax of S(t), one logit
+  // pair per slot, against the fixed reference maximum m2 (no rescaling).
+  auto body = [&](int t, f32x16(&sc)[2], f32x16(&sn)[2], u32x4(&pc)[2][2], const u32x4(&pp)[2][2],
+                  bool masked) __attribute__((always_inline)) {
+    sync_vm<F::NVM>();
+    issue_group(t);
+    const uint16_t *K = sK + slot(t + 1) * F::TILE;
+    const uint16_t *V = sV + slot(t - 1) * F::TILE;
+    const float(*bi)[AF_TK] = sBias[slot(t)];
+    auto kread = [&](int ks) __attribute__((always_inline)) { return *(const u32x4 *)(K + krow + (((2 * ks + hl) ^ kx) << 3)); };
+    auto vread = [&](int j) __attribute__((always_inline)) {  // A fragment of P.V step j = (hf, db)
+      const int hf = j / NDB, db = j % NDB;
+      u32x2 pr[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int rr = 0; rr < 2; ++rr)
+        pr[rr] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + (16 * hf + 8 * rr) * D + vlo[db])));
+      return u32x4{pr[0][0], pr[0][1], pr[1][0], pr[1][1]};
+    };
+    sn[0] = sn[1] = f32x16{};
+    u32x4 kf[NKS], vf[2 * NDB];
+    kf[0] = kread(0);
+    kf[1] = kread(1);
+    vf[0] = vread(0);
+    vf[1] = vread(1);
+    // bias pair of slot i: keys 8(r0/4) + 4hl + r0%4 (+1) of column block i / 8, r0 = 2 (i % 8);
+    // read two slots ahead into a ring of 3
+    auto bread = [&](int i) __attribute__((always_inline)) {
+      const int r0 = 2 * (i & 7);
+      return *(const float2 *)(bi[hloc[i >> 3]] + 8 * (r0 >> 2) + 4 * hl + (r0 & 3));
+    };
+    float2 bq[3];
+    bq[0] = bread(0);
+    bq[1] = bread(1);
+    float ps[2] = {0.f, 0.f};
+    const float mu[2] = {mref(0), mref(1)};
+    const int lim[2] = {qi[0] - (kt0 + t) * AF_TK, qi[1] - (kt0 + t) * AF_TK};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = (kb * 32 + acc_row(r, hl) > lim) ? -INFINITY : s[kb][r];
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kb][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Lazy rescaling: keep the running max unless a logit exceeds it by more
-    // than 8 (log2 units), so probabilities stay <= 256 and O is rescaled rarely.
-    if (__any(mloc > m2 + 8.f)) {
-      const float mnew = fmaxf(m2, mloc);
-      const float alpha = fast_exp2(m2 - ((mnew == -INFINITY) ? 0.f : mnew));
-      m2 = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-    }
-    const float muse = (m2 == -INFINITY) ? 0.f : m2;
-    float psum = 0.f;
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 = fast_exp2(s[kb][8 * hf + 2 * w] - muse);
-          const float p1 = fast_exp2(s[kb][8 * hf + 2 * w + 1] - muse);
-          psum += p0 + p1;
-          pf[kb][hf][w] = pack_bf16x2(p0, p1);
+    for (int i = 0; i < 16; ++i) {
+      if ((i & 1) == 0 && i / 2 + 2 < NKS) kf[i / 2 + 2] = kread(i / 2 + 2);
+      if ((i & 1) == 0 && i / 2 + 2 < 2 * NDB) vf[i / 2 + 2] = vread(i / 2 + 2);
+      if (i + 2 < 16) bq[(i + 2) % 3] = bread(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i / 2 < NKS) sn[i & 1] = mfma32(kf[i / 2], qf[i & 1][i / 2], sn[i & 1]);
+      if (i / 2 < 2 * NDB) {
+        const int j = i / 2;
+        acc[j % NDB][i & 1] = mfma32(vf[j], pp[i & 1][j / NDB], acc[j % NDB][i & 1]);
+      }
+      {
+        const int cb = i >> 3, r0 = 2 * (i & 7);
+        const int key = 8 * (r0 >> 2) + 4 * hl + (r0 & 3);  // keys key, key + 1
+        const float2 bv = bq[i % 3];
+        float x0 = __builtin_fmaf(sc[cb][r0], c2, bv.x);
+        float x1 = __builtin_fmaf(sc[cb][r0 + 1], c2, bv.y);
+        if (masked) {
+          x0 = key > lim[cb] ? -INFINITY : x0;
+          x1 = key + 1 > lim[cb] ? -INFINITY : x1;
         }
-    lsum += psum;
-    // O^T += V^T P^T.  Key slot 8hl + e of step (kb, hf) is key kb*32 + 16hf + 8(e/4) + 4hl + e%4.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          u32x2 part[2];
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-            part[rr] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                    (lds_i16x4 *)(V + (kb * 32 + 16 * hf + 8 * rr) * D + vlo[db])));
-          acc[db] = mfma32(u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}, pf[kb][hf], acc[db]);
-        }
+        const float p0 = fast_exp2(x0 - mu[cb]), p1 = fast_exp2(x1 - mu[cb]);
+        pc[cb][r0 >> 3][(r0 & 7) >> 1] = pack_bf16x2(p0, p1);
+        ps[cb] += p0 + p1;  // fp32 sums: the row statistics (lse) stay exact to fp32
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum[0] += ps[0];
+    lsum[1] += ps[1];
   };
 
-  f32x16 sA[2], sB2[2];
-  sync_vm<0>();
-  qk(0, sA);
-  // Two iterations per trip so the current / next S accumulators swap roles without copies.
-  for (int t = 0; t < nst; t += 2) {
-    // iteration t: S(t) in sA, computes S(t+1) into sB2
-    sync_vm<0>();  // K(t+1), V(t) landed; every wave is done with iteration t-1
-    if (t + 2 < nst) issue_k(t + 2);
-    if (t + 1 < nst) issue_v(t + 1);
-    // ping-pong: team 0 multiplies the next tile first, team 1 softmaxes first,
-    // so each SIMD overlaps one wave's matrix work with the other's vector work
-    if (team == 0) {
-      if (t + 1 < nst) qk(t + 1, sB2);
-      attend(t, sA);
-    } else {
-      attend(t, sA);
-      if (t + 1 < nst) qk(t + 1, sB2);
+  f32x16 sA[2], sB[2];
+  u32x4 pA[2][2], pB[2][2];
+  // One pass over the piece.  The probabilities use a fixed reference maximum
+  // per column: the maximum of the first tile on the first pass.  Later logits
+  // may exceed it: while the row sum stays below 2^64, O and the sums are far
+  // from fp32 overflow and the result is exact up to rounding.  A piece whose
+  // sum does not (or is not finite) is run again with the reference raised by
+  // log2 of that sum (which bounds every probability by 1 on the next pass).
+  auto run = [&](bool first) __attribute__((always_inline)) {
+    issue_group(-3);
+    issue_group(-2);
+    issue_group(-1);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) pB[cb][hf] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
+    lsum[0] = lsum[1] = 0.f;
+    sync_vm<F::NVM>();  // K(0) and bias(0) landed
+    qk(0, sA);
+    if (first) {  // reference = maximum logit of tile 0
+      const float(*bi)[AF_TK] = sBias[slot(0)];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int lim = qi[cb] - kt0 * AF_TK;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
+          const float x = __builtin_fmaf(sA[cb][r], c2, bi[hloc[cb]][key]);
+          mx = fmaxf(mx, (tdiag == 0 && key > lim) ? -INFINITY : x);
+        }
+        m2[cb] = fmaxf(mx, __shfl_xor(mx, 32));
+      }
     }
-    if (t + 1 >= nst) break;
-    // iteration t+1: S(t+1) in sB2, computes S(t+2) into sA
-    sync_vm<0>();
-    if (t + 3 < nst) issue_k(t + 3);
-    if (t + 2 < nst) issue_v(t + 2);
-    if (team == 0) {
-      if (t + 2 < nst) qk(t + 2, sA);
-      attend(t + 1, sB2);
-    } else {
-      attend(t + 1, sB2);
-      if (t + 2 < nst) qk(t + 2, sA);
+    for (int t = 0; t < nt; t += 2) {
+      if (t >= tdiag) body(t, sA, sB, pA, pB, true);
+      else body(t, sA, sB, pA, pB, false);
+      if (t + 1 >= nt) break;
+      if (t + 1 >= tdiag) body(t + 1, sB, sA, pB, pA, true);
+      else body(t + 1, sB, sA, pB, pA, false);
     }
+    sync_vm<F::NVM>();  // V(nt-1) landed
+    if (nt & 1) pv(nt - 1, pA);
+    else pv(nt - 1, pB);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero-fill loads
+  };
+  for (int pass = 0; pass < 4; ++pass) {
+    run(pass == 0);
+    float lt[2];
+    bool bad = false;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      lt[cb] = lsum[cb] + __shfl_xor(lsum[cb], 32);
+      bad = bad || !(lt[cb] < 0x1p64f);
+    }
+    if (!__syncthreads_or(bad) || pass == 3) break;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      if (!(lt[cb] < 0x1p64f)) m2[cb] = mref(cb) + (lt[cb] < INFINITY ? __log2f(lt[cb]) : 120.f);
   }
 
-  // Merge team 1 into team 0 through LDS (the tile buffers are free now).
-  sync_vm<0>();
-  constexpr int NR = NDB * 16 + 2;
-  static_assert(4 * NR * 64 * 4 <= 4 * TILE * 2, "team exchange must fit in the tile buffers");
-  float *xch = reinterpret_cast<float *>(sKV) + wt * NR * 64;
-  if (team == 1) {
+  // Split block: publish this piece, the last one to finish merges.  Records
+  // are written and read with device-scope relaxed atomic accesses (coherent
+  // across the XCDs' L2s without flushing them); the counter bump follows the
+  // completed stores, the merger's loads follow the counter.
+  auto st_dev = [](float *a, float x) __attribute__((always_inline)) {
+    __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto ld_dev = [](const float *a) __attribute__((always_inline)) {
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int npm = 1;
+  if (np > 1) {
+    float *rec = part + ((int64_t)(pfirst + p) * nbh + bh) * (4 * F::NR * 64) + wave * F::NR * 64 + lane;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = acc[db][r];
-    xch[(NR - 2) * 64 + lane] = m2;
-    xch[(NR - 1) * 64 + lane] = lsum;
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st_dev(rec + ((db * 2 + cb) * 16 + r) * 64, acc[db][cb][r]);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      st_dev(rec + (F::NR - 4 + cb) * 64, mref(cb));  // the reference O and the sum are relative to
+      st_dev(rec + (F::NR - 2 + cb) * 64, lsum[cb]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      sLast = __hip_atomic_fetch_add(&cnt[bh * nqb + qb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+    __syncthreads();
+    if (!sLast) return;
+    npm = np;
   }
-  __syncthreads();
-  if (team == 1) return;
-  const float m1 = xch[(NR - 2) * 64 + lane], l1 = xch[(NR - 1) * 64 + lane];
-  const float mm = fmaxf(m2, m1);
-  const float mu = (mm == -INFINITY) ? 0.f : mm;
-  const float a0 = fast_exp2(m2 - mu), a1 = fast_exp2(m1 - mu);
-  const float lpart = lsum * a0 + l1 * a1;
-  const float ltot = lpart + __shfl_xor(lpart, 32);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (vq) {
-    uint16_t *orow = o + ((bM + qi) * Hq + hq) * D;
+  // merge pieces 0 .. npm-1 in order, all from their records (this one's too)
+  float mm[2], lt[2];
+  if (npm == 1) {
+    mm[0] = mref(0), mm[1] = mref(1);
+    lt[0] = lsum[0], lt[1] = lsum[1];
+  } else {
+    const float *rec0 = part + ((int64_t)pfirst * nbh + bh) * (4 * F::NR * 64) + wave * F::NR * 64 + lane;
+    const int64_t pstride = (int64_t)nbh * (4 * F::NR * 64);
+    mm[0] = mm[1] = -INFINITY;
+    for (int pp2 = 0; pp2 < npm; ++pp2)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int cb = 0; cb < 2; ++cb) mm[cb] = fmaxf(mm[cb], ld_dev(rec0 + pp2 * pstride + (F::NR - 4 + cb) * 64));
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float ov[4];
+    for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
+    lt[0] = lt[1] = 0.f;
+    for (int pp2 = 0; pp2 < npm; ++pp2) {
+      const float *rec = rec0 + pp2 * pstride;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          ov[e] = (acc[db][4 * g4 + e] * a0 + xch[(db * 16 + 4 * g4 + e) * 64 + lane] * a1) * inv;
-        const int d = db * 32 + 8 * g4 + 4 * hl;
-        *(u32x2 *)(orow + d) = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+      for (int cb = 0; cb < 2; ++cb) {
+        const float sc = mm[cb] == -INFINITY ? 0.f : fast_exp2(ld_dev(rec + (F::NR - 4 + cb) * 64) - mm[cb]);
+        lt[cb] += ld_dev(rec + (F::NR - 2 + cb) * 64) * sc;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][cb][r] += ld_dev(rec + ((db * 2 + cb) * 16 + r) * 64) * sc;
       }
     }
-    if (lse && hl == 0) lse[((int64_t)b * Hq + hq) * M + qi] = ltot > 0.f ? (mm + __log2f(ltot)) * kLn2 : -INFINITY;
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float ltot = lt[cb] + __shfl_xor(lt[cb], 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (!vq[cb]) continue;
+    const int hq = kvh * G + hloc[cb];
+    uint16_t *orow = o + ((bM + qi[cb]) * Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hl;
+        *(u32x2 *)(orow + d) = u32x2{pack_bf16x2(acc[db][cb][4 * g4] * inv, acc[db][cb][4 * g4 + 1] * inv),
+                                     pack_bf16x2(acc[db][cb][4 * g4 + 2] * inv, acc[db][cb][4 * g4 + 3] * inv)};
+      }
+    if (lse && hl == 0)
+      lse[((int64_t)b * Hq + hq) * M + qi[cb]] = ltot > 0.f ? (mm[cb] + __log2f(ltot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -454,13 +607,68 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
   if (lse && lane == 0) lse[((bM / M) * Hq + h) * M + i] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+// Split schedule of the bf16 forward: query blocks of BQ = 256 / G queries,
+// pieces of at most C 32-key tiles, one work-group per piece and (batch, kv
+// head), one work-group per compute unit at a time (256 of them).  When the
+// unsplit blocks already fill the compute units, C is the average work per
+// unit (blocks longer than that are split).  Otherwise C is the smallest piece
+// length (at least 8 tiles) that keeps every piece in a single wave of 256
+// work-groups.  Pieces of split blocks get a partial record each; split
+// blocks form a prefix of the piece list.
+FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
+  FwdSched f{};
+  const int64_t G = Hkv > 0 ? Hq / Hkv : 0;
+  if (M <= 0 || G < 1 || G > 8 || (G & (G - 1)) != 0) return f;
+  f.BQ = (int)(256 / G);
+  f.nqb = (int)((M + f.BQ - 1) / f.BQ);
+  const int64_t nbh = B * Hkv;
+  int64_t tiles = 0;
+  int nmax = 0;
+  for (int qb = 0; qb < f.nqb; ++qb) {
+    const int n = fwd_ntiles(qb, f.BQ, (int)M);
+    tiles += n;
+    nmax = n > nmax ? n : nmax;
+  }
+  auto pieces = [&](int C) {
+    int64_t np = 0;
+    for (int qb = 0; qb < f.nqb; ++qb) np += fwd_npieces(fwd_ntiles(qb, f.BQ, (int)M), C);
+    return np;
+  };
+  if (nbh * f.nqb >= 256) {
+    const int64_t avg = (nbh * tiles + 255) / 256;
+    f.C = (int)(avg > 8 ? avg : 8);
+  } else {
+    f.C = 8;
+    while (f.C < nmax && nbh * pieces(f.C) > 256) ++f.C;
+  }
+  for (int qb = 0; qb < f.nqb; ++qb) {
+    const int np = fwd_npieces(fwd_ntiles(qb, f.BQ, (int)M), f.C);
+    f.npieces += np;
+    if (np > 1) f.nmulti += np;
+  }
+  return f;
+}
+
 // Workspace of the attention calls (256-byte aligned regions):
-//   cs [B*M*D/2] float2 | khat [B*M*Hkv*D] bf16 | lg2 [B*M] f32 | delta [B*Hq*M] f32 | colsum [B*Hq*M] f32
+//   cs [B*M*D/2] float2 | khat [B*M*Hkv*D] bf16 | bias [B*Hq*M] f32 |
+//   part [nmulti*B*Hkv * 4 waves * NR * 64] f32 | cnt [B*Hkv*nqb] i32 |
+//   (backward) delta [B*Hq*M] f32 | colsum [B*Hq*M] f32
 static size_t rup(size_t x) { return (x + 255) / 256 * 256; }
+
+static size_t part_floats(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
+  const FwdSched f = fwd_sched(B, M, Hq, Hkv);
+  const int64_t nr = 2 * (D / 32) * 16 + 4;
+  return (size_t)(f.nmulti * B * Hkv * 4 * nr * 64);
+}
+
+static size_t cnt_ints(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
+  return (size_t)(B * Hkv * fwd_sched(B, M, Hq, Hkv).nqb);
+}
 
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
   size_t n = rup((size_t)(B * M * (D / 2)) * sizeof(float2)) + rup((size_t)(B * M * Hkv * D) * 2) +
-             rup((size_t)(B * Hq * M) * sizeof(float));
+             rup((size_t)(B * Hq * M) * sizeof(float)) + rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float)) +
+             rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int));
   if (bwd) n += 2 * rup((size_t)(B * Hq * M) * sizeof(float));
   return n;
 }
@@ -474,6 +682,11 @@ AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, in
   p += rup((size_t)(B * M * Hkv * D) * 2);
   w.bias = (float *)p;
   p += rup((size_t)(B * Hq * M) * sizeof(float));
+  w.part = (float *)p;
+  p += rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float));
+  w.cnt = (int *)p;
+  w.ncnt = (int)cnt_ints(B, M, Hq, Hkv);
+  p += rup((size_t)w.ncnt * sizeof(int));
   w.delta = (float *)p;
   p += rup((size_t)(B * Hq * M) * sizeof(float));
   w.colsum = (float *)p;
@@ -489,7 +702,7 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
   const int64_t rows = (int64_t)B * M;
   hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)((rows * (D / 2) + 255) / 256)), dim3(256), 0, s,
                      (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
-                     (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr);
+                     (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, w.cnt, with_bias ? w.ncnt : 0);
   return hipGetLastError();
 }
 
@@ -502,18 +715,18 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
   const float2 *cs = pos ? w.cs : nullptr;
   const double c = 1.0 / (sqrt((double)D) * (double)tau);
   if (bf16) {
-    const int G = Hq / Hkv;
-    const int BQ = 128 / G;
-    const int nqb = (M + BQ - 1) / BQ;
-    const dim3 grid((unsigned)(nqb * B * Hkv));
+    const FwdSched f = fwd_sched(B, M, Hq, Hkv);
+    const dim3 grid((unsigned)(f.npieces * B * Hkv));
     const float c2 = (float)(c * 1.4426950408889634);
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
     if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(512), 0, s, (const uint16_t *)q, kh,
-                         (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, G, BQ, nqb, (uint16_t *)o, lse);
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(256), 0, s, (const uint16_t *)q, kh,
+                         (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part,
+                         w.cnt, (uint16_t *)o, lse);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(512), 0, s, (const uint16_t *)q, kh,
-                         (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, G, BQ, nqb, (uint16_t *)o, lse);
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(256), 0, s, (const uint16_t *)q, kh,
+                         (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part,
+                         w.cnt, (uint16_t *)o, lse);
   } else {
     const int64_t rows = (int64_t)B * M * Hq;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const float *)q,

@@ -10,9 +10,19 @@ struct AttnWs {
   float2 *cs;        // [B*M, D/2] (cos, sin) of the kept positions
   uint16_t *khat;    // [B, M, Hkv, D] rotated keys (bf16)
   float *bias;       // [B, Hq, M] gamma_h * log2 g_j (-inf where g_j <= 0)
+  float *part;       // partial (O, max, sum) records of the forward's split query blocks
+  int *cnt;          // [B*Hkv, nqb] arrival counters of the split query blocks
+  int ncnt;
   float *delta;      // [B, Hq, M] D_i of the backward
   float *colsum;     // [B, Hq, M] column sums of dS per head
 };
+
+// Split schedule of the bf16 forward (query block size, blocks, tiles per
+// piece, pieces, pieces of split blocks).
+struct FwdSched {
+  int BQ, nqb, C, npieces, nmulti;
+};
+FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv);
 
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd);
 AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
