@@ -77,16 +77,6 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
   }
 }
 
-__device__ __forceinline__ void rope_chunk(u32x4 &x, u32x4 &y, const float2 *__restrict__ t) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float2 c0 = t[2 * w], c1 = t[2 * w + 1];
-    const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
-    const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
-    x[w] = pack_bf16x2(x0 * c0.x - y0 * c0.y, x1 * c1.x - y1 * c1.y);
-    y[w] = pack_bf16x2(y0 * c0.x + x0 * c0.y, y1 * c1.x + x1 * c1.y);
-  }
-}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -262,19 +252,42 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     issue_kv(i + 1, true);
     issue_bias(i + 2);
   };
+  // The first pass's direct loads go out first; the Q and rotation loads
+  // below (all issued before any use) overlap with them.
+  issue_group(-3);
+  issue_group(-2);
+  issue_group(-1);
+
   // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8] of each column block
   u32x4 qf[2][NKS];
+  f32x4 csv[2][NKS / 2][4];  // (cos, sin) of the 8 rotary pairs of (ks, hl), two pairs per vector
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const uint16_t *qrow = q + ((bM + qi[cb]) * Hq + kvh * G + hloc[cb]) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qf[cb][ks] = vq[cb] ? *(const u32x4 *)(qrow + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
-    if (cs && vq[cb]) {
+    const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq[cb] ? qi[cb] : 0)) * HALF);
 #pragma unroll
-      for (int ks = 0; ks < NKS / 2; ++ks)
-        rope_chunk(qf[cb][ks], qf[cb][ks + NKS / 2], cs + (bM + qi[cb]) * HALF + 16 * ks + 8 * hl);
-    }
+    for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) csv[cb][ks][w] = cs ? crow[(16 * ks + 8 * hl) / 2 + w] : f32x4{1.f, 0.f, 1.f, 0.f};
+  }
+  if (cs) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks) {
+        u32x4 &x = qf[cb][ks], &y = qf[cb][ks + NKS / 2];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x4 c = csv[cb][ks][w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
+          const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+          const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
+          x[w] = pack_bf16x2(x0 * c[0] - y0 * c[1], x1 * c[2] - y1 * c[3]);
+          y[w] = pack_bf16x2(y0 * c[0] + x0 * c[1], y1 * c[2] + x1 * c[3]);
+        }
+      }
   }
 
   // fragment-read offsets: K row l32, logical chunk 2ks + hl; V transposing
@@ -292,13 +305,29 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   f32x16 acc[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
-  // m2: reference maximum of each column (the probabilities are 2^(x - m2))
-  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  auto mref = [&](int cb) __attribute__((always_inline)) { return m2[cb] == -INFINITY ? 0.f : m2[cb]; };
+  // m2: reference maximum of each column (the probabilities are 2^(x - m2)).
+  // The S^T products subtract it themselves: one more 16-wide product step
+  // with a constant A fragment (1, 1 in k = 0, 1) and a per-column B fragment
+  // (-m2 / c2 as a bf16 pair hi + lo) adds -m2 / c2 to every raw dot product.
+  float m2[2] = {0.f, 0.f}, lsum[2] = {0.f, 0.f};
+  auto mref = [&](int cb) __attribute__((always_inline)) { return m2[cb]; };
+  const u32x4 kaug = hl == 0 ? u32x4{0x3F803F80u, 0u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+  u32x4 qaug[2];
+  const float inv_c2 = 1.f / c2;
+  auto set_ref = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float r = -m2[cb] * inv_c2;
+      const uint32_t hi = f32_to_bf16_bits(r);
+      const uint32_t lo = f32_to_bf16_bits(r - bf16_lo(hi));
+      qaug[cb] = hl == 0 ? u32x4{hi | (lo << 16), 0u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
-  auto qk = [&](int t, f32x16(&s)[2]) __attribute__((always_inline)) {  // raw dot products S(t)^T
+  auto qk = [&](int t, f32x16(&s)[2]) __attribute__((always_inline)) {  // S(t)^T - m2 / c2
     const uint16_t *K = sK + slot(t) * F::TILE;
-    s[0] = s[1] = f32x16{};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32(kaug, qaug[cb], f32x16{});
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const u32x4 a = *(const u32x4 *)(K + krow + (((2 * ks + hl) ^ kx) << 3));
@@ -345,7 +374,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
             u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + (16 * hf + 8 * rr) * D + vlo[db])));
       return u32x4{pr[0][0], pr[0][1], pr[1][0], pr[1][1]};
     };
-    sn[0] = sn[1] = f32x16{};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) sn[cb] = mfma32(kaug, qaug[cb], f32x16{});
     u32x4 kf[NKS], vf[2 * NDB];
     kf[0] = kread(0);
     kf[1] = kread(1);
@@ -361,7 +391,6 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     bq[0] = bread(0);
     bq[1] = bread(1);
     float ps[2] = {0.f, 0.f};
-    const float mu[2] = {mref(0), mref(1)};
     const int lim[2] = {qi[0] - (kt0 + t) * AF_TK, qi[1] - (kt0 + t) * AF_TK};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -384,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
           x0 = key > lim[cb] ? -INFINITY : x0;
           x1 = key + 1 > lim[cb] ? -INFINITY : x1;
         }
-        const float p0 = fast_exp2(x0 - mu[cb]), p1 = fast_exp2(x1 - mu[cb]);
+        const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
         pc[cb][r0 >> 3][(r0 & 7) >> 1] = pack_bf16x2(p0, p1);
         ps[cb] += p0 + p1;  // fp32 sums: the row statistics (lse) stay exact to fp32
       }
@@ -403,9 +432,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   // sum does not (or is not finite) is run again with the reference raised by
   // log2 of that sum (which bounds every probability by 1 on the next pass).
   auto run = [&](bool first) __attribute__((always_inline)) {
-    issue_group(-3);
-    issue_group(-2);
-    issue_group(-1);
+    if (!first) {  // a repeated pass refills the ring (the first pass's loads went out above)
+      issue_group(-3);
+      issue_group(-2);
+      issue_group(-1);
+    }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -415,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     lsum[0] = lsum[1] = 0.f;
     sync_vm<F::NVM>();  // K(0) and bias(0) landed
     qk(0, sA);
-    if (first) {  // reference = maximum logit of tile 0
+    if (first) {  // reference = maximum logit of tile 0 (S(0) was computed with reference 0)
       const float(*bi)[AF_TK] = sBias[slot(0)];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
@@ -427,8 +458,13 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
           const float x = __builtin_fmaf(sA[cb][r], c2, bi[hloc[cb]][key]);
           mx = fmaxf(mx, (tdiag == 0 && key > lim) ? -INFINITY : x);
         }
-        m2[cb] = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m2[cb] = mx == -INFINITY ? 0.f : mx;
+        const float sh = m2[cb] * inv_c2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sA[cb][r] -= sh;
       }
+      set_ref();
     }
     for (int t = 0; t < nt; t += 2) {
       if (t >= tdiag) body(t, sA, sB, pA, pB, true);
@@ -442,6 +478,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     else pv(nt - 1, pB);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero-fill loads
   };
+  set_ref();
   for (int pass = 0; pass < 4; ++pass) {
     run(pass == 0);
     float lt[2];
@@ -455,6 +492,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
       if (!(lt[cb] < 0x1p64f)) m2[cb] = mref(cb) + (lt[cb] < INFINITY ? __log2f(lt[cb]) : 120.f);
+    set_ref();
   }
 
   // Split block: publish this piece, the last one to finish merges.  Records
