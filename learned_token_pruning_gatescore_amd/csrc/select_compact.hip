@@ -9,8 +9,8 @@
 //
 // Selection is a radix select over a 32-bit order key of the fp32 score, one
 // work-group per batch row: three digit passes (12, 10, 10 bits) over an LDS
-// histogram (wavefront ballots collapse a wave whose keys all share one digit
-// into a single atomic) find the exact key T of
+// histogram (a wavefront vote collapses a wave whose keys are all equal into a
+// single atomic) find the exact key T of
 // the K'-th best prunable token and how many tokens with key == T to take
 // (lowest index first).  Each thread owns contiguous 32-token segments whose
 // keys stay in registers; a final pass emits the kept indices in ascending
@@ -29,10 +29,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
-  // number of set bits of mask below this lane
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 constexpr int SEL_T = 1024;              // threads per batch row
 constexpr int SEL_I = 32;                // tokens per thread per chunk (a contiguous segment)
@@ -76,21 +72,6 @@ __device__ __forceinline__ void block_exscan2(uint32_t a, uint32_t b, uint32_t &
   ta = sw[SEL_W - 1];
   tb = sw[2 * SEL_W - 1];
   __syncthreads();
-}
-
-// Adds one to hist[digit] for each lane with `cand`: one LDS atomic per lane,
-// except when every candidate lane of the wave holds the same digit (a zero-
-// initialised scorer makes every key equal), where a wavefront ballot counts
-// them and a single atomic adds the total.
-__device__ __forceinline__ void hist_add(uint32_t *hist, bool cand, uint32_t digit) {
-  const uint64_t act = __ballot(cand);
-  const uint32_t d0 = __shfl(digit, act ? __ffsll((unsigned long long)act) - 1 : 0);
-  const uint64_t same = __ballot(cand && digit == d0);
-  if (act != 0 && same == act) {
-    if (cand && lane_rank(act) == 0) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
-  } else if (cand) {
-    atomicAdd(&hist[digit], 1u);
-  }
 }
 
 // Finds the bin holding the need-th largest candidate.  Bins are scanned from
@@ -187,8 +168,20 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     if (!RES) load(c);
     nf += (uint32_t)__popc(fbits & vbits);
     const uint32_t cbits = vbits & ~fbits;
+    // One LDS atomic per candidate.  A wave whose 2048 candidates all share one
+    // key (a constant score vector) adds its count with a single atomic instead
+    // of 2048 serialised ones.
+    bool same = cbits == 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < SEL_I; ++i) hist_add(hist, (cbits >> i) & 1u, key[i] >> 20);
+    for (int i = 1; i < SEL_I; ++i) same = same && key[i] == key[0];
+    const uint32_t k0 = __shfl(key[0], 0);
+    if (__all(same && key[0] == k0)) {
+      if (lane == 0) atomicAdd(&hist[k0 >> 20], 64u * SEL_I);
+    } else {
+#pragma unroll
+      for (int i = 0; i < SEL_I; ++i)
+        if ((cbits >> i) & 1u) atomicAdd(&hist[key[i] >> 20], 1u);
+    }
   }
   for (int o = 32; o > 0; o >>= 1) nf += __shfl_xor(nf, o);
   if (lane == 0 && nf) atomicAdd(&res[2], nf);
@@ -270,15 +263,13 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
       for (int64_t r = 0; r < tq && m; ++r) m &= m - 1u;  // clear the lowest tq bits
       tkeep = tm & ~m;
     }
-    const uint32_t all = km | tkeep;
-    const int64_t base = kb + (tb < quota ? tb : quota);
-#pragma unroll
-    for (int i = 0; i < SEL_I; ++i) {
-      const uint32_t bit = 1u << i;
-      if (all & bit) {
-        const int64_t p = base + __popc(all & (bit - 1u));
-        if (p < M_alloc) out[p] = (int32_t)(n0 + i);
-      }
+    uint32_t all = km | tkeep;
+    int64_t p = kb + (tb < quota ? tb : quota);
+    while (all) {  // this segment's kept tokens in ascending order
+      const int i = __builtin_ctz(all);
+      if (p < M_alloc) out[p] = (int32_t)(n0 + i);
+      ++p;
+      all &= all - 1u;
     }
     runK += tk;
     runT += tt;
