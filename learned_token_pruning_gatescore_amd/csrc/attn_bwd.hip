@@ -11,402 +11,623 @@
 //                                   dgamma_h = sum_{b,j} colsum_h(j) ln g_j
 // then dq, dk rotated back by -phi.
 //
-// bf16 path, three launches, no atomics (bitwise deterministic):
-//   1. q-outer (same work-group shape as the forward: 4 waves x 32 (query,
-//      head) columns sharing one kv head's tiles): pass A forms D_i from fp32
-//      P and fp32 dP (not from the rounded output), pass B forms dS and
-//      accumulates dQ^T = K^T dS^T on the matrix cores; writes dq and D.
-//   2. kv-outer: each wave owns 32 keys (MFMA columns = keys, so the column
-//      sum of dS over queries is lane-local); loops over the group's heads and
-//      the query tiles at or after its keys; accumulates dV^T = dO^T P and
-//      dK^T = Q^T dS; writes dk, dv and colsum per head.
+// bf16 path: prep (rotated keys, log2-gate bias), then two matrix-core
+// kernels and two small reductions, no atomics (bitwise deterministic):
+//   1. query-outer: per (query, head) column, pass A forms D_i from fp32 P and
+//      fp32 dP (not from the rounded output), pass B forms dS and accumulates
+//      dQ^T = K^T dS^T; writes dq, D_i and the rotated queries;
+//   2. key-outer: per key, dV^T = dO^T P and dK^T = Q^T dS over every head of
+//      the group and every query at or after the key; writes dk, dv and the
+//      column sums of dS per head;
 //   3. dg (per token, fixed head order) and dgamma (one work-group per head,
 //      fixed-shape tree).
+//
+// Both matrix-core kernels run 8 waves per work-group, two per SIMD, so that
+// one wave's products overlap the other's vector work.  32-row tiles of the
+// streamed operand (keys for kernel 1, queries for kernel 2) are shared by
+// all 8 waves: direct global->LDS loads, two tiles ahead, one barrier per
+// tile.  The per-row terms of the exponent and of dS (-lse / c and -D_i)
+// enter the products as one extra 16-deep step whose operand holds the value
+// split into three bf16 parts, so the vector work per logit is one fma, one
+// exp2 and the product with dP.
 #include "tg_common.h"
 #include "tg_attn.h"
 
 namespace tg {
 
-__device__ __forceinline__ void rope_chunk2(u32x4 &x, u32x4 &y, const float2 *__restrict__ t) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float2 c0 = t[2 * w], c1 = t[2 * w + 1];
-    const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
-    const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
-    x[w] = pack_bf16x2(x0 * c0.x - y0 * c0.y, x1 * c1.x - y1 * c1.y);
-    y[w] = pack_bf16x2(y0 * c0.x + x0 * c0.y, y1 * c1.x + x1 * c1.y);
-  }
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Writes 4 rows (consecutive tokens) x 8 columns (chunk of d) of bf16 both as
-// rows of sRow[token][d] (pitch RP) and transposed into sT[d][token] (pitch TP).
-template <int RP, int TP>
-__device__ __forceinline__ void store_rows_and_transpose(uint16_t *sRow, uint16_t *sT, int tok0, int d0,
-                                                         const u32x4 (&w)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *(u32x4 *)(&sRow[(tok0 + i) * RP + d0]) = w[i];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int sh = (e & 1) * 16;
-    const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xFFFFu, a1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
-    const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xFFFFu, a3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
-    *(u32x2 *)(&sT[(d0 + e) * TP + tok0]) = u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
-  }
-}
+constexpr int AB_T = 32;   // rows per streamed tile
+constexpr int AB_NW = 8;   // waves per work-group
 
-// Stage a 64-token tile of a [*, H, D] bf16 tensor (row stride H*D, head offset
-// applied by the caller) into sRow (and, if TRANS, transposed into sT), rotating
-// by the rotary table when cs != nullptr.  All 256 threads call it.
-template <int D, bool TRANS>
-__device__ __forceinline__ void stage_tile(const uint16_t *__restrict__ base, int64_t rstride, int t0, int M,
-                                           const float2 *__restrict__ cs_b, uint16_t *sRow, uint16_t *sT, int tid) {
-  constexpr int RP = D + 8, TP = 64 + 4, HALF = D / 2, NC = D / 16;
-  // thread -> (4-token group tg4 in 0..15, chunk pair c in 0..NC-1); 16*NC <= 128 threads busy
-  for (int p = tid; p < 16 * NC; p += 256) {
-    const int tg4 = p & 15, c = p >> 4;
-    u32x4 x[4], y[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * tg4 + i;
-      if (t < M) {
-        const uint16_t *r = base + (int64_t)t * rstride;
-        x[i] = *(const u32x4 *)(r + 8 * c);
-        y[i] = *(const u32x4 *)(r + HALF + 8 * c);
-        if (cs_b) rope_chunk2(x[i], y[i], cs_b + (int64_t)t * HALF + 8 * c);
-      } else {
-        x[i] = u32x4{0, 0, 0, 0};
-        y[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (TRANS) {
-      store_rows_and_transpose<RP, TP>(sRow, sT, 4 * tg4, 8 * c, x);
-      store_rows_and_transpose<RP, TP>(sRow, sT, 4 * tg4, HALF + 8 * c, y);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *(u32x4 *)(&sRow[(4 * tg4 + i) * RP + 8 * c]) = x[i];
-        *(u32x4 *)(&sRow[(4 * tg4 + i) * RP + HALF + 8 * c]) = y[i];
-      }
-    }
+// LDS layout of a 32-row bf16 tile: chunk-major.  Chunk c (16 bytes = 8
+// elements of every row) is a 512-byte block of 32 rows; row r sits in slot
+// r ^ 4 (c % 4) of it.  One 1 KB direct load fills two chunks of all 32 rows.
+// Both fragment reads are conflict-free and every fragment address is a
+// per-lane base plus a compile-time offset:
+//   row reads (ds_read_b128, k = column): 16 lanes read 16 rows of one chunk,
+//     16 distinct slots of the 256-byte bank window;
+//   transposing reads (ds_read_b64_tr_b16, k = row): 32 lanes read 4
+//     consecutive rows of 4 chunks c with distinct c % 4; the XOR moves the
+//     four chunks' rows to distinct slots.
+template <int D>
+struct BTile {
+  static constexpr int C = D / 8;        // 16-byte chunks per row
+  static constexpr int NI = C / 2;       // 1 KB direct loads per tile
+  static constexpr int TILE = AB_T * D;  // u16 per tile
+  static constexpr int NKS = D / 16, NDB = D / 32;
+  // byte offset in global memory of the 16 bytes that lane fills in direct
+  // load i of a tile (row stride rs bytes)
+  __device__ static uint32_t goff(int i, int lane, uint32_t rs) {
+    const int c = 2 * i + (lane >> 5), row = (lane & 31) ^ (4 * (c & 3));
+    return (uint32_t)row * rs + (uint32_t)c * 16u;
   }
+};
+
+// Per-lane fragment bases into a tile (MFMA 32x32x16 operand layouts).
+template <int D>
+struct BFrag {
+  using T = BTile<D>;
+  int rb[2];  // row read, even / odd k-step
+  int tb[2];  // transposing read rr
+  __device__ void init(int lane) {
+    const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) rb[par] = hl * 256 + ((l32 ^ (8 * par + 4 * hl)) * 8);
+    const int gi = lane >> 4, li = lane & 15, kq = li >> 2, cc = li & 3;
+    const int cl = 2 * (gi & 1) + (cc >> 1);  // chunk % 4
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) tb[rr] = cl * 256 + (4 * ((hl + 2 * rr) ^ cl) + kq) * 8 + 4 * (cc & 1);
+  }
+  // A (or B) operand, k = column: lane holds row l32, columns 16 ks + 8 hl .. +8
+  __device__ __forceinline__ u32x4 rows(const uint16_t *t, int ks) const {
+    return *(const u32x4 *)(t + rb[ks & 1] + 512 * ks);
+  }
+  // A operand, k = row: lane holds column 32 db + l32 of rows 16 hf + 8 (e / 4) + 4 hl + e % 4
+  // (slot e), matching register 8 hf + e of a 32x32 accumulator whose rows are the tile rows
+  __device__ __forceinline__ u32x4 tr(const uint16_t *t, int hf, int db) const {
+    const u32x2 lo = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + tb[0] + 1024 * db + 128 * hf)));
+    const u32x2 hi = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + tb[1] + 1024 * db + 128 * hf)));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+// 16-deep operand that adds x (split into three bf16 parts, k = 0, 1, 2) to
+// every product of its row (A side) or column (B side), against kOnes.
+__device__ __forceinline__ u32x4 aug3(float x, int hl) {
+  const uint32_t h = f32_to_bf16_bits(x);
+  const float r1 = x - bf16_lo(h);
+  const uint32_t m = f32_to_bf16_bits(r1);
+  const uint32_t l = f32_to_bf16_bits(r1 - bf16_lo(m));
+  return hl == 0 ? u32x4{h | (m << 16), l, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+}
+__device__ __forceinline__ u32x4 ones3(int hl) {
+  return hl == 0 ? u32x4{0x3F803F80u, 0x00003F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
 }
 
 // ---------------------------------------------------------------------------
-// 1. q-outer: D_i and dq.
+// 1. query-outer: D_i, dq and the rotated queries.
+//
+// Work-group = 8 waves = 256 columns, a column being a (query, head) pair of
+// the GQA group (BQ = 256 / G queries x G heads); wave w owns columns
+// 32w .. 32w+31 (one head).  It computes S^T = K Q^T and dP^T = V dO^T (keys
+// on the MFMA rows: 16 keys of one column per lane), P and dS in registers,
+// and dQ^T += K^T dS^T with K^T read through the transposing LDS read.  Each
+// work-group takes query block nqb-1-p and then block p, so every work-group
+// sees about the same number of key tiles.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs,
-    const float *__restrict__ lse, const uint16_t *__restrict__ dout, float c, float c2, int B, int M, int Hq,
-    int Hkv, int G, int BQ, int nqb, float *__restrict__ dq, float *__restrict__ delta_out) {
-  constexpr int NKS = D / 16, NDB = D / 32, KP = D + 8, VP = 64 + 4, HALF = D / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * VP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[64 * KP];
-  __shared__ float sLg[64];
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v,
+    const float *__restrict__ bias, const float2 *__restrict__ cs, const float *__restrict__ lse,
+    const uint16_t *__restrict__ dout, float c, float c2, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb,
+    float *__restrict__ dq, uint16_t *__restrict__ qhat, float2 *__restrict__ rowstat) {
+  using T = BTile<D>;
+  constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
+  constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
+  constexpr int NVM = NIW + 1;            // + the bias load
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) float sBias[3][8][AB_T];
+  __shared__ __attribute__((aligned(1024))) float sDummy[256];  // target of the other waves' bias loads
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
   const int nbh = B * Hkv;
-  const int idx = blockIdx.x;
-  const int qb = nqb - 1 - idx / nbh;
-  const int bh = idx % nbh;
+  const int bh = blockIdx.x % nbh, pr = blockIdx.x / nbh;
   const int b = bh / Hkv, kvh = bh % Hkv;
-  const int q0 = qb * BQ;
-  const int col = wave * 32 + l32;
-  const int hq = kvh * G + col / BQ;
-  const int qi = q0 + col % BQ;
-  const bool vq = qi < M;
-  const int qmax = min(q0 + BQ, M) - 1;
-  const int nt = qmax / 64 + 1;
   const int64_t bM = (int64_t)b * M;
-  const float2 *cs_b = cs ? cs + bM * HALF : nullptr;
+  const uint32_t rsb = (uint32_t)(Hkv * D * 2);  // bytes between consecutive keys
+  const uint32_t kv_bytes = (uint32_t)(M - 1) * rsb + D * 2;
+  const i32x4 rK = buffer_rsrc(kh + (bM * Hkv + kvh) * D, kv_bytes);
+  const i32x4 rV = buffer_rsrc(v + (bM * Hkv + kvh) * D, kv_bytes);
+  const i32x4 rB = buffer_rsrc(bias + ((int64_t)b * Hq + (int64_t)kvh * G) * M, (uint32_t)(G * M * 4));
 
-  u32x4 qf[NKS], df[NKS];
-  const int64_t roff = ((bM + qi) * Hq + hq) * D;
+  BFrag<D> fr;
+  fr.init(lane);
+  // direct load j = wave + 8 n of the tile's 2 NI (K first, then V)
+  uint32_t dgo[NIW], dlo[NIW];
+  bool isv[NIW];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    qf[ks] = vq ? *(const u32x4 *)(q + roff + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
-    df[ks] = vq ? *(const u32x4 *)(dout + roff + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+  for (int n = 0; n < NIW; ++n) {
+    const int j = wave + AB_NW * n;
+    isv[n] = j >= T::NI;
+    dgo[n] = T::goff(j % T::NI, lane, rsb);
+    dlo[n] = 1024u * (uint32_t)(j % T::NI);
   }
-  if (cs && vq) {
-#pragma unroll
-    for (int ks = 0; ks < NKS / 2; ++ks) rope_chunk2(qf[ks], qf[ks + NKS / 2], cs + (bM + qi) * HALF + 16 * ks + 8 * hl);
-  }
-  const float gam = gamma[hq];
-  const float lrow = vq ? lse[((int64_t)b * Hq + hq) * M + qi] : -INFINITY;
-  const bool live = lrow != -INFINITY;
-  const float l2 = live ? lrow * kLog2e : 0.f;
-  const uint16_t *kb_ = k + (int64_t)kvh * D;
-  const uint16_t *vb_ = v + (int64_t)kvh * D;
-  const int64_t kstride = (int64_t)Hkv * D;
+  // bias: wave 0 loads the G rows of the tile (8 lanes x 16 bytes per head)
+  const bool breal = wave == 0 && (lane >> 3) < G;
+  const uint32_t bvo = (uint32_t)((((lane >> 3) * M) + 4 * (lane & 7)) * 4);
+  const u32x4 kones = ones3(hl);
 
-  // logits -> P (fp32) for one 64-key tile held as S^T in s[2]
-  auto probs = [&](f32x16(&s)[2], int j0) {
-    const bool diag = j0 + 63 > q0;
+  auto slot = [](int t) __attribute__((always_inline)) { return t % 3; };
+  auto issue = [&](int t, int nt) __attribute__((always_inline)) {
+    const bool live = t < nt;
+    const uint32_t toff = (uint32_t)(t * AB_T) * rsb;
+    const uint32_t so = 2u * (uint32_t)(slot(t) * T::TILE);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + acc_row(r, hl);
-        const float lg = sLg[key];
-        float p = (lg == -INFINITY || !live) ? 0.f : fast_exp2(s[kb][r] * c2 + gam * lg - l2);
-        if (diag && j0 + key > qi) p = 0.f;
-        s[kb][r] = p;
-      }
-    }
+    for (int n = 0; n < NIW; ++n)
+      dma_b128(isv[n] ? rV : rK, (isv[n] ? lds_addr(sV) : lds_addr(sK)) + so + dlo[n],
+               live ? dgo[n] + toff : 0x80000000u, 0u);
+    dma_b128(rB, wave == 0 ? lds_addr(&sBias[slot(t)][0][0]) : lds_addr(sDummy),
+             live && breal ? bvo + (uint32_t)(t * AB_T * 4) : 0x80000000u, 0u);
   };
 
-  // pass A: D_i = sum_j P_ij dP_ij
-  float dsum = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
-    f32x16 acc[NDB];
+  for (int rep = 0; rep < 2; ++rep) {
+    const int qb = rep == 0 ? nqb - 1 - pr : pr;
+    if (rep == 1 && qb >= nqb - 1 - pr) break;  // the middle block of an odd count runs once
+    const int q0 = qb * BQ;
+    const int qe = q0 + BQ < M ? q0 + BQ : M;
+    const int nt = (qe + AB_T - 1) / AB_T;
+    const int tdiag = q0 / AB_T;  // tiles from here on hold keys past some query of the block
+    const int hloc = (AB_T * wave) / BQ;
+    const int h = kvh * G + hloc;
+    const int qi = q0 + (AB_T * wave) % BQ + l32;
+    const bool vq = qi < M;
+
+    issue(0, nt);
+    issue(1, nt);
+
+    // Q and dO fragments (MFMA B operands): lane holds [qi, h, 16 ks + 8 hl .. +8]
+    u32x4 qf[NKS], of[NKS];
+    const int64_t roff = ((bM + (vq ? qi : 0)) * Hq + h) * D;
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-    float dlt = 0.f;
-    if (pass == 1) dlt = dsum;
-    for (int t = 0; t < nt; ++t) {
-      const int j0 = t * 64;
-      __syncthreads();
-      const int64_t kbase_off = bM * kstride;
-      stage_tile<D, true>(kb_ + kbase_off, kstride, j0, M, cs_b, sK, sKt, tid);
-      stage_tile<D, false>(vb_ + kbase_off, kstride, j0, M, nullptr, sV, nullptr, (tid + 128) & 255);
-      if (tid < 64) {
-        const int j = j0 + tid;
-        const float gv = (j < M) ? g[bM + j] : 0.f;
-        sLg[tid] = gv > 0.f ? fast_log2(gv) : -INFINITY;
-      }
-      __syncthreads();
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = vq ? *(const u32x4 *)(q + roff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+      of[ks] = vq ? *(const u32x4 *)(dout + roff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float lrow = vq ? lse[((int64_t)b * Hq + h) * M + qi] : -INFINITY;
+    if (cs) {
+      const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq ? qi : 0)) * HALF);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < NKS / 2; ++ks) {
+        u32x4 &x = qf[ks], &y = qf[ks + NKS / 2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = *(const u32x4 *)(&sK[(kb * 32 + l32) * KP + 16 * ks + 8 * hl]);
-          s[kb] = mfma32(a, qf[ks], s[kb]);
-          const u32x4 av = *(const u32x4 *)(&sV[(kb * 32 + l32) * KP + 16 * ks + 8 * hl]);
-          dp[kb] = mfma32(av, df[ks], dp[kb]);
+        for (int w = 0; w < 4; ++w) {
+          const f32x4 t = crow[(16 * ks + 8 * hl) / 2 + w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
+          const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+          const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
+          x[w] = pack_bf16x2(x0 * t[0] - y0 * t[1], x1 * t[2] - y1 * t[3]);
+          y[w] = pack_bf16x2(y0 * t[0] + x0 * t[1], y1 * t[2] + x1 * t[3]);
         }
       }
-      probs(s, j0);
-      if (pass == 0) {
+      if (vq) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dsum += s[kb][r] * dp[kb][r];
-      } else {
-        u32x4 dsf[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const int r0 = 8 * hf + 2 * w;
-              dsf[kb][hf][w] = pack_bf16x2(s[kb][r0] * (dp[kb][r0] - dlt), s[kb][r0 + 1] * (dp[kb][r0 + 1] - dlt));
-            }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const uint16_t *kr = &sKt[(db * 32 + l32) * VP + kb * 32 + 16 * hf + 4 * hl];
-              const u32x2 lo = *(const u32x2 *)kr, hi = *(const u32x2 *)(kr + 8);
-              acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsf[kb][hf], acc[db]);
-            }
+        for (int ks = 0; ks < NKS; ++ks) *(u32x4 *)(qhat + roff + 16 * ks + 8 * hl) = qf[ks];
       }
     }
-    if (pass == 0) {
-      dsum += __shfl_xor(dsum, 32);
-      if (vq && hl == 0) delta_out[((int64_t)b * Hq + hq) * M + qi] = dsum;
-    } else if (vq) {
-      // dq = c * R(-phi) dq^ ; lane holds rows d = db*32 + acc_row(r, hl)
-      float *drow = dq + ((bM + qi) * Hq + hq) * D;
+    // exponent of P in log2 units: (S + la) c2 + bias with la = -lse / c
+    // (dead rows and columns past M: -1e30, P = 0)
+    const float la = lrow == -INFINITY ? -1e30f : -lrow / c;
+    const u32x4 laug = aug3(la, hl);
+
+    // S^T and dP^T products over the head dim, fragments read two steps ahead
+    // (sched_barrier keeps the reads from being hoisted all at once)
+    auto sdp = [&](const uint16_t *K, const uint16_t *V, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
+      u32x4 ka[NKS], va[NKS];
+      ka[0] = fr.rows(K, 0);
+      va[0] = fr.rows(V, 0);
+      ka[1] = fr.rows(K, 1);
+      va[1] = fr.rows(V, 1);
 #pragma unroll
-      for (int db = 0; db < NDB / 2; ++db) {
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 2 < NKS) {
+          ka[ks + 2] = fr.rows(K, ks + 2);
+          va[ks + 2] = fr.rows(V, ks + 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma32(ka[ks], qf[ks], s);
+        dp = mfma32(va[ks], of[ks], dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // acc[db] += (tile^T)[db] . x over the tile rows, transposing reads two steps ahead
+    auto trprod = [&](const uint16_t *X, const u32x4(&x)[2], f32x16(&a)[NDB]) __attribute__((always_inline)) {
+      u32x4 f[2 * NDB];
+      f[0] = fr.tr(X, 0, 0);
+      f[1] = fr.tr(X, 0, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) {
+        if (i + 2 < 2 * NDB) f[i + 2] = fr.tr(X, (i + 2) / NDB, (i + 2) % NDB);
+        __builtin_amdgcn_sched_barrier(0);
+        a[i % NDB] = mfma32(f[i], x[i / NDB], a[i % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // pass A: D_i = sum_j P_ij dP_ij
+    float dsa[4] = {0.f, 0.f, 0.f, 0.f};
+    auto body_a = [&](int t, bool masked) __attribute__((always_inline)) {
+      sync_vm<NVM>();
+      issue(t + 2, nt);
+      const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
+      f32x16 s = mfma32(kones, laug, f32x16{}), dp = f32x16{};
+      sdp(K, V, s, dp);
+      const float *bi = &sBias[slot(t)][hloc][4 * hl];
+      const int lim = qi - t * AB_T;  // keys (within the tile) past the query are masked
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 bv = *(const f32x4 *)(bi + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = __builtin_fmaf(s[4 * j + e], c2, bv[e]);
+          if (masked && 8 * j + 4 * hl + e > lim) x = -INFINITY;
+          dsa[e] = __builtin_fmaf(fast_exp2(x), dp[4 * j + e], dsa[e]);
+        }
+      }
+    };
+    const int tu = tdiag < nt ? tdiag : nt;  // unmasked tiles first, then the masked ones
+    for (int t = 0; t < tu; ++t) body_a(t, false);
+    for (int t = tu; t < nt; ++t) body_a(t, true);
+    sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
+    float dsum = (dsa[0] + dsa[1]) + (dsa[2] + dsa[3]);
+    dsum += __shfl_xor(dsum, 32);
+    if (vq && hl == 0) rowstat[((int64_t)b * Hq + h) * M + qi] = make_float2(la, dsum);
+    const u32x4 daug = aug3(-dsum, hl);
+
+    // pass B: dS and dQ^T
+    issue(0, nt);
+    issue(1, nt);
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    auto body_b = [&](int t, bool masked) __attribute__((always_inline)) {
+      sync_vm<NVM>();
+      issue(t + 2, nt);
+      const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
+      f32x16 s = mfma32(kones, laug, f32x16{}), dp = mfma32(kones, daug, f32x16{});
+      sdp(K, V, s, dp);
+      const float *bi = &sBias[slot(t)][hloc][4 * hl];
+      const int lim = qi - t * AB_T;
+      float ds[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 bv = *(const float2 *)(bi + 8 * (j >> 1) + 2 * (j & 1));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * j + e;
+          float x = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+          if (masked && acc_row(r, hl) > lim) x = -INFINITY;
+          ds[r] = fast_exp2(x) * dp[r];
+        }
+      }
+      // B operand of step hf: slot e is register 8 hf + e
+      u32x4 dsf[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dsf[hf][w] = pack_bf16x2(ds[8 * hf + 2 * w], ds[8 * hf + 2 * w + 1]);
+      trprod(K, dsf, acc);
+    };
+    for (int t = 0; t < tu; ++t) body_b(t, false);
+    for (int t = tu; t < nt; ++t) body_b(t, true);
+    sync_vm<0>();
+
+    // dq = c R(-phi) dq^ ; lane holds rows d = 32 db + acc_row(r, hl) of its column
+    if (vq) {
+      float *drow = dq + ((bM + qi) * Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hl;
           float xo[4], yo[4];
+          f32x4 t0 = {1.f, 0.f, 1.f, 0.f}, t1 = {1.f, 0.f, 1.f, 0.f};
+          if (cs) {
+            const f32x4 *cp = (const f32x4 *)(cs + (bM + qi) * HALF + d);
+            t0 = cp[0];
+            t1 = cp[1];
+          }
+          const float cv[4] = {t0[0], t0[2], t1[0], t1[2]}, sv[4] = {t0[1], t0[3], t1[1], t1[3]};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = acc[db][4 * g4 + e] * c, y = acc[db + NDB / 2][4 * g4 + e] * c;
-            if (cs) {
-              const float2 t = cs[(bM + qi) * HALF + d + e];
-              xo[e] = x * t.x + y * t.y;
-              yo[e] = y * t.x - x * t.y;
-            } else {
-              xo[e] = x;
-              yo[e] = y;
-            }
+            xo[e] = x * cv[e] + y * sv[e];
+            yo[e] = y * cv[e] - x * sv[e];
           }
           *(f32x4 *)(drow + d) = f32x4{xo[0], xo[1], xo[2], xo[3]};
           *(f32x4 *)(drow + HALF + d) = f32x4{yo[0], yo[1], yo[2], yo[3]};
         }
-      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2. kv-outer: dk, dv, colsum.
+// 2. key-outer: dk, dv and the column sums of dS.
+//
+// Work-group = 8 waves over a block of 128 keys (32 per wave) and every
+// (head of the group, 32-query tile at or after the block) item, the items
+// streamed through LDS in order.  The waves split the work by role, so that
+// each fits in the registers of two waves per SIMD:
+//   role 0 (waves 0-3, K^ of its keys in registers): S = Q K^T (queries on
+//     the MFMA rows, keys on the columns: one key per lane), P, dV^T += dO^T P;
+//     hands P (fp32) to its partner through LDS;
+//   role 1 (waves 4-7, V of the same keys): one item behind, dP = dO V^T,
+//     dS = P (dP - D), the column sums, dK^T += Q^T dS.
+// Each work-group takes key block p and then block nkb-1-p.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs,
-    const float *__restrict__ lse, const uint16_t *__restrict__ dout, const float *__restrict__ delta, float c,
-    float c2, int B, int M, int Hq, int Hkv, int G, int nkb, float *__restrict__ dk, float *__restrict__ dv,
-    float *__restrict__ colsum) {
-  constexpr int NKS = D / 16, NDB = D / 32, KP = D + 8, VP = 64 + 4, HALF = D / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * VP];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sOt[D * VP];
-  __shared__ float sL2[64], sDl[64];
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
+    const uint16_t *__restrict__ qh, const uint16_t *__restrict__ dout, const float2 *__restrict__ rowstat,
+    const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v, const float *__restrict__ bias,
+    const float2 *__restrict__ cs, float c, float c2, int B, int M, int Hq, int Hkv, int G, int nkb,
+    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
+  using T = BTile<D>;
+  constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
+  constexpr int NIW = 2 * T::NI / AB_NW;  // Q and dO direct loads per wave per item
+  constexpr int NVM = NIW + 1;            // + the row-statistics load
+  constexpr int KB = 4 * AB_T;            // keys per block
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[4 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sO[4 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) float2 sRS[4][AB_T];
+  __shared__ __attribute__((aligned(1024))) f32x4 sP[2][4][4][64];  // [item parity][wave][r / 4][lane]
+  __shared__ __attribute__((aligned(1024))) float sCol[8][KB];
+  __shared__ __attribute__((aligned(256))) float sDummy[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2, sub = wave & 3;
   const int l32 = lane & 31, hl = lane >> 5;
   const int nbh = B * Hkv;
-  const int idx = blockIdx.x;
-  const int kblk = idx / nbh;  // low keys (most queries) first
-  const int bh = idx % nbh;
+  const int bh = blockIdx.x % nbh, pr = blockIdx.x / nbh;
   const int b = bh / Hkv, kvh = bh % Hkv;
-  const int k0 = kblk * 128;
-  const int kw0 = k0 + wave * 32;  // this wave's first key
-  const int key = kw0 + l32;
-  const bool vk = key < M;
   const int64_t bM = (int64_t)b * M;
-  const float2 *cs_b = cs ? cs + bM * HALF : nullptr;
+  const uint32_t rsq = (uint32_t)(Hq * D * 2);  // bytes between consecutive queries of one head
+  const uint32_t q_bytes = (uint32_t)(M - 1) * rsq + D * 2;
+  const int ntq = (M + AB_T - 1) / AB_T;
 
-  // K^, V fragments of this lane's key (MFMA B operand).
-  u32x4 kf[NKS], vf[NKS];
-  const int64_t koff = ((bM + key) * Hkv + kvh) * D;
+  BFrag<D> fr;
+  fr.init(lane);
+  uint32_t dgo[NIW], dlo[NIW];
+  bool iso[NIW];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    kf[ks] = vk ? *(const u32x4 *)(k + koff + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
-    vf[ks] = vk ? *(const u32x4 *)(v + koff + 16 * ks + 8 * hl) : u32x4{0, 0, 0, 0};
+  for (int n = 0; n < NIW; ++n) {
+    const int j = wave + AB_NW * n;
+    iso[n] = j >= T::NI;
+    dgo[n] = T::goff(j % T::NI, lane, rsq);
+    dlo[n] = 1024u * (uint32_t)(j % T::NI);
   }
-  if (cs && vk) {
+  const u32x4 kones = ones3(hl);
+  // acc[db] += (tile^T)[db] . x over the tile rows, transposing reads two steps ahead
+  auto trprod = [&](const uint16_t *X, const u32x4(&x)[2], f32x16(&a)[NDB]) __attribute__((always_inline)) {
+    u32x4 f[2 * NDB];
+    f[0] = fr.tr(X, 0, 0);
+    f[1] = fr.tr(X, 0, 1);
 #pragma unroll
-    for (int ks = 0; ks < NKS / 2; ++ks) rope_chunk2(kf[ks], kf[ks + NKS / 2], cs + (bM + key) * HALF + 16 * ks + 8 * hl);
-  }
-  const float gv = vk ? g[bM + key] : 0.f;
-  const float lg = gv > 0.f ? fast_log2(gv) : -INFINITY;
+    for (int i = 0; i < 2 * NDB; ++i) {
+      if (i + 2 < 2 * NDB) f[i + 2] = fr.tr(X, (i + 2) / NDB, (i + 2) % NDB);
+      __builtin_amdgcn_sched_barrier(0);
+      a[i % NDB] = mfma32(f[i], x[i / NDB], a[i % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  f32x16 aK[NDB], aV[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    aK[i] = f32x16{};
-    aV[i] = f32x16{};
-  }
-  const int tq0 = k0 / 64;  // first query tile that can see these keys
-  const int ntq = (M + 63) / 64;
-  const int64_t qstride = (int64_t)Hq * D;
+  for (int rep = 0; rep < 2; ++rep) {
+    const int kb = rep == 0 ? pr : nkb - 1 - pr;
+    if (rep == 1 && kb <= pr) break;  // the middle block of an odd count runs once
+    const int k0 = kb * KB;
+    const int tq0 = k0 / AB_T;
+    const int ntl = ntq - tq0;  // query tiles per head
+    const int nit = G * ntl;    // items
+    const int kw0 = k0 + AB_T * sub;
+    const int key = kw0 + l32;
+    const bool vk = key < M;
 
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = kvh * G + hh;
-    const float gam = gamma[h];
-    float csum = 0.f;
-    for (int tq = tq0; tq < ntq; ++tq) {
-      const int i0 = tq * 64;
-      __syncthreads();
-      stage_tile<D, true>(q + bM * qstride + (int64_t)h * D, qstride, i0, M, cs_b, sQ, sQt, tid);
-      stage_tile<D, true>(dout + bM * qstride + (int64_t)h * D, qstride, i0, M, nullptr, sO, sOt, (tid + 128) & 255);
-      if (tid < 64) {
-        const int i = i0 + tid;
-        const float l = i < M ? lse[((int64_t)b * Hq + h) * M + i] : -INFINITY;
-        sL2[tid] = l == -INFINITY ? INFINITY : l * kLog2e;  // +inf -> P = 0
-        sDl[tid] = i < M ? delta[((int64_t)b * Hq + h) * M + i] : 0.f;
-      }
-      __syncthreads();
+    // item it: head it / ntl of the group, query tile tq0 + it % ntl; ring slot it % 4
+    auto issue = [&](int it) __attribute__((always_inline)) {
+      const bool live = it < nit;
+      const int hh = live ? it / ntl : 0;
+      const int tq = live ? tq0 + it - hh * ntl : 0;
+      const int64_t h = (int64_t)kvh * G + hh;
+      const i32x4 rQ = buffer_rsrc(qh + (bM * Hq + h) * D, q_bytes);
+      const i32x4 rO = buffer_rsrc(dout + (bM * Hq + h) * D, q_bytes);
+      const i32x4 rR = buffer_rsrc(rowstat + ((int64_t)b * Hq + h) * M, (uint32_t)M * 8u);
+      const uint32_t toff = (uint32_t)(tq * AB_T) * rsq;
+      const uint32_t so = 2u * (uint32_t)((it & 3) * T::TILE);
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {  // 32-query halves of the tile
-        const int qa = i0 + 32 * qh;
-        if (qa + 31 < kw0) continue;  // every query before every key of this wave
-        f32x16 s = f32x16{}, dp = f32x16{};
+      for (int n = 0; n < NIW; ++n)
+        dma_b128(iso[n] ? rO : rQ, (iso[n] ? lds_addr(sO) : lds_addr(sQ)) + so + dlo[n],
+                 live ? dgo[n] + toff : 0x80000000u, 0u);
+      dma_b32(rR, wave == 0 ? lds_addr(&sRS[it & 3][0]) : lds_addr(sDummy),
+              live && wave == 0 ? (uint32_t)(tq * AB_T * 8 + 4 * lane) : 0x80000000u, 0u);
+    };
+    issue(0);
+    issue(1);
+
+    const int64_t koff = ((bM + (vk ? key : 0)) * Hkv + kvh) * D;
+    // Per head the items of this wave are: tiles before its keys (nothing to
+    // do), the diagonal tile (causal mask), then unmasked tiles.
+    const int nskip = sub < ntl ? sub : ntl;
+    if (role == 0) {
+      // ---- role 0: S, P, dV ----
+      u32x4 kf[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 a = *(const u32x4 *)(&sQ[(32 * qh + l32) * KP + 16 * ks + 8 * hl]);
-          s = mfma32(a, kf[ks], s);
-          const u32x4 ao = *(const u32x4 *)(&sO[(32 * qh + l32) * KP + 16 * ks + 8 * hl]);
-          dp = mfma32(ao, vf[ks], dp);
+      for (int ks = 0; ks < NKS; ++ks)
+        kf[ks] = vk ? *(const u32x4 *)(kh + koff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+      f32x16 aV[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) aV[db] = f32x16{};
+      float blane = -INFINITY;
+      auto item = [&](int it, bool masked) __attribute__((always_inline)) {
+        const int i0 = (tq0 + it % ntl) * AB_T;
+        const uint16_t *Qt = sQ + (it & 3) * T::TILE, *Ot = sO + (it & 3) * T::TILE;
+        const float2 rs = sRS[it & 3][l32];
+        f32x16 s = mfma32(aug3(i0 + l32 < M ? rs.x : -1e30f, hl), kones, f32x16{});
+        {
+          u32x4 f[NKS];
+          f[0] = fr.rows(Qt, 0);
+          f[1] = fr.rows(Qt, 1);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            if (ks + 2 < NKS) f[ks + 2] = fr.rows(Qt, ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            s = mfma32(f[ks], kf[ks], s);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        u32x4 pf[2], dsf[2];
+        float p[16];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int r = 0; r < 16; ++r) {
+          float x = __builtin_fmaf(s[r], c2, blane);
+          if (masked && key > i0 + acc_row(r, hl)) x = -INFINITY;
+          p[r] = fast_exp2(x);
+        }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            float pp[2], dd[2];
+        for (int j = 0; j < 4; ++j) sP[it & 1][sub][j][lane] = f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+        u32x4 pf[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 8 * hf + 2 * w + e;
-              const int ql = 32 * qh + acc_row(r, hl);  // query within the tile
-              const int qg = i0 + ql;
-              float p = (lg == -INFINITY || qg < key) ? 0.f : fast_exp2(s[r] * c2 + gam * lg - sL2[ql]);
-              const float ds = p * (dp[r] - sDl[ql]);
-              csum += ds;
-              pp[e] = p;
-              dd[e] = ds;
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pf[hf][w] = pack_bf16x2(p[8 * hf + 2 * w], p[8 * hf + 2 * w + 1]);
+        trprod(Ot, pf, aV);
+      };
+      for (int hh = 0; hh < G; ++hh) {
+        const int it0 = hh * ntl;
+        blane = vk ? bias[((int64_t)b * Hq + kvh * G + hh) * M + key] : -INFINITY;
+        for (int n = 0; n < nskip; ++n) {
+          sync_vm<NVM>();
+          issue(it0 + n + 2);
+        }
+        if (nskip < ntl) {
+          sync_vm<NVM>();
+          issue(it0 + nskip + 2);
+          item(it0 + nskip, true);
+        }
+        for (int n = nskip + 1; n < ntl; ++n) {
+          sync_vm<NVM>();
+          issue(it0 + n + 2);
+          item(it0 + n, false);
+        }
+      }
+      sync_vm<NVM>();
+      issue(nit + 2);
+      sync_vm<0>();
+      if (vk) {
+        float *dvr = dv + koff;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = db * 32 + 8 * g4 + 4 * hl;
+            *(f32x4 *)(dvr + d) = f32x4{aV[db][4 * g4], aV[db][4 * g4 + 1], aV[db][4 * g4 + 2], aV[db][4 * g4 + 3]};
+          }
+      }
+    } else {
+      // ---- role 1: dP, dS, column sums, dK (one item behind role 0) ----
+      u32x4 vf[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        vf[ks] = vk ? *(const u32x4 *)(v + koff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+      f32x16 aK[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) aK[db] = f32x16{};
+      float csum = 0.f;
+      auto item = [&](int jt) __attribute__((always_inline)) {
+        const uint16_t *Qt = sQ + (jt & 3) * T::TILE, *Ot = sO + (jt & 3) * T::TILE;
+        const float2 rs = sRS[jt & 3][l32];
+        f32x16 dp = mfma32(aug3(-rs.y, hl), kones, f32x16{});
+        {
+          u32x4 f[NKS];
+          f[0] = fr.rows(Ot, 0);
+          f[1] = fr.rows(Ot, 1);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            if (ks + 2 < NKS) f[ks + 2] = fr.rows(Ot, ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            dp = mfma32(f[ks], vf[ks], dp);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        float ds[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 pv = sP[jt & 1][sub][j][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ds[4 * j + e] = pv[e] * dp[4 * j + e];
+            csum += ds[4 * j + e];
+          }
+        }
+        u32x4 dsf[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dsf[hf][w] = pack_bf16x2(ds[8 * hf + 2 * w], ds[8 * hf + 2 * w + 1]);
+        trprod(Qt, dsf, aK);
+      };
+      sync_vm<NVM>();
+      issue(2);
+      for (int hh = 0; hh < G; ++hh) {
+        const int it0 = hh * ntl;
+        for (int n = 0; n < nskip; ++n) {
+          sync_vm<NVM>();
+          issue(it0 + n + 3);
+        }
+        for (int n = nskip; n < ntl; ++n) {
+          sync_vm<NVM>();
+          issue(it0 + n + 3);
+          item(it0 + n);
+        }
+        const float tot = csum + __shfl_xor(csum, 32);
+        if (hl == 0) sCol[hh][AB_T * sub + l32] = tot;
+        csum = 0.f;
+      }
+      sync_vm<0>();
+      if (vk) {
+        float *dkr = dk + koff;
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = db * 32 + 8 * g4 + 4 * hl;
+            f32x4 t0 = {1.f, 0.f, 1.f, 0.f}, t1 = {1.f, 0.f, 1.f, 0.f};
+            if (cs) {
+              const f32x4 *cp = (const f32x4 *)(cs + (bM + key) * HALF + d);
+              t0 = cp[0];
+              t1 = cp[1];
             }
-            pf[hf][w] = pack_bf16x2(pp[0], pp[1]);
-            dsf[hf][w] = pack_bf16x2(dd[0], dd[1]);
-          }
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS ; query slot 8hl+e of step hf is row 16hf + 8(e/4) + 4hl + e%4
+            const float cv[4] = {t0[0], t0[2], t1[0], t1[2]}, sv[4] = {t0[1], t0[3], t1[1], t1[3]};
+            float xo[4], yo[4];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const uint16_t *orr = &sOt[(db * 32 + l32) * VP + 32 * qh + 16 * hf + 4 * hl];
-            const u32x2 olo = *(const u32x2 *)orr, ohi = *(const u32x2 *)(orr + 8);
-            aV[db] = mfma32(u32x4{olo[0], olo[1], ohi[0], ohi[1]}, pf[hf], aV[db]);
-            const uint16_t *qr = &sQt[(db * 32 + l32) * VP + 32 * qh + 16 * hf + 4 * hl];
-            const u32x2 qlo = *(const u32x2 *)qr, qhi = *(const u32x2 *)(qr + 8);
-            aK[db] = mfma32(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dsf[hf], aK[db]);
+            for (int e = 0; e < 4; ++e) {
+              const float x = aK[db][4 * g4 + e] * c, y = aK[db + NDB / 2][4 * g4 + e] * c;
+              xo[e] = x * cv[e] + y * sv[e];
+              yo[e] = y * cv[e] - x * sv[e];
+            }
+            *(f32x4 *)(dkr + d) = f32x4{xo[0], xo[1], xo[2], xo[3]};
+            *(f32x4 *)(dkr + HALF + d) = f32x4{yo[0], yo[1], yo[2], yo[3]};
           }
-        }
       }
     }
-    csum += __shfl_xor(csum, 32);
-    if (vk && hl == 0) colsum[((int64_t)b * Hq + h) * M + key] = csum;
-  }
-
-  if (vk) {
-    float *dkr = dk + koff;
-    float *dvr = dv + koff;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hl;
-        *(f32x4 *)(dvr + d) = f32x4{aV[db][4 * g4], aV[db][4 * g4 + 1], aV[db][4 * g4 + 2], aV[db][4 * g4 + 3]};
-      }
+    sync_vm<0>();  // sCol complete
+    for (int i = tid; i < G * KB; i += AB_NW * 64) {
+      const int hh = i / KB, kk = i % KB;
+      if (k0 + kk < M) colsum[((int64_t)b * Hq + kvh * G + hh) * M + k0 + kk] = sCol[hh][kk];
     }
-#pragma unroll
-    for (int db = 0; db < NDB / 2; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hl;
-        float xo[4], yo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = aK[db][4 * g4 + e] * c, y = aK[db + NDB / 2][4 * g4 + e] * c;
-          if (cs) {
-            const float2 t = cs[(bM + key) * HALF + d + e];
-            xo[e] = x * t.x + y * t.y;
-            yo[e] = y * t.x - x * t.y;
-          } else {
-            xo[e] = x;
-            yo[e] = y;
-          }
-        }
-        *(f32x4 *)(dkr + d) = f32x4{xo[0], xo[1], xo[2], xo[3]};
-        *(f32x4 *)(dkr + HALF + d) = f32x4{yo[0], yo[1], yo[2], yo[3]};
-      }
-    }
+    sync_vm<0>();  // sCol read before the next block writes it
   }
 }
 
@@ -600,10 +821,9 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
                            const int32_t *pos, double theta, float tau, const float *lse, const void *dout, int B,
                            int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg,
                            float *dgamma, const AttnWs &w, hipStream_t s) {
-  float *ws_delta = w.delta, *ws_colsum = w.colsum;
   const float2 *cs = pos ? w.cs : nullptr;
-  if ((int64_t)B * M > 0 && pos) {
-    hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, false, false, w, s);
+  if ((int64_t)B * M > 0 && (pos || bf16)) {
+    hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, w, s);
     if (e != hipSuccess) return e;
   }
   const double cd = 1.0 / (sqrt((double)D) * (double)tau);
@@ -611,39 +831,42 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
   if ((int64_t)B * M > 0) {
     if (bf16) {
       const int G = Hq / Hkv;
-      const int BQ = 128 / G;
+      const int BQ = 256 / G;
       const int nqb = (M + BQ - 1) / BQ;
       const int nkb = (M + 127) / 128;
-      const dim3 g1((unsigned)(nqb * B * Hkv)), g2((unsigned)(nkb * B * Hkv));
+      const dim3 g1((unsigned)((nqb + 1) / 2 * B * Hkv)), g2((unsigned)((nkb + 1) / 2 * B * Hkv));
+      const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
+      const uint16_t *qh = pos ? w.qhat : (const uint16_t *)q;
       if (D == 128) {
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, g1, dim3(256), 0, s, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, g, gamma, cs, lse, (const uint16_t *)dout, c,
-                           c2, B, M, Hq, Hkv, G, BQ, nqb, dq, ws_delta);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, g2, dim3(256), 0, s, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, g, gamma, cs, lse, (const uint16_t *)dout,
-                           ws_delta, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv, ws_colsum);
+        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, g1, dim3(512), 0, s, (const uint16_t *)q, kh,
+                           (const uint16_t *)v, w.bias, cs, lse, (const uint16_t *)dout, c, c2, B, M, Hq, Hkv, G,
+                           BQ, nqb, dq, w.qhat, w.rowstat);
+        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, g2, dim3(512), 0, s, qh, (const uint16_t *)dout,
+                           w.rowstat, kh, (const uint16_t *)v, w.bias, cs, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv,
+                           w.colsum);
       } else {
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, g1, dim3(256), 0, s, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, g, gamma, cs, lse, (const uint16_t *)dout, c,
-                           c2, B, M, Hq, Hkv, G, BQ, nqb, dq, ws_delta);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, g2, dim3(256), 0, s, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, g, gamma, cs, lse, (const uint16_t *)dout,
-                           ws_delta, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv, ws_colsum);
+        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, g1, dim3(512), 0, s, (const uint16_t *)q, kh,
+                           (const uint16_t *)v, w.bias, cs, lse, (const uint16_t *)dout, c, c2, B, M, Hq, Hkv, G,
+                           BQ, nqb, dq, w.qhat, w.rowstat);
+        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, g2, dim3(512), 0, s, qh, (const uint16_t *)dout,
+                           w.rowstat, kh, (const uint16_t *)v, w.bias, cs, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv,
+                           w.colsum);
       }
     } else {
+      float *delta = (float *)w.rowstat;
       const int64_t rq = (int64_t)B * M * Hq, rk = (int64_t)B * M * Hkv;
       hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, dim3((unsigned)((rq + 3) / 4)), dim3(256), 0, s,
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, c, B, M, Hq, Hkv, D, dq, ws_delta);
+                         (const float *)dout, c, B, M, Hq, Hkv, D, dq, delta);
       hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, dim3((unsigned)((rk + 3) / 4)), dim3(256), 0, s,
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, ws_delta, c, B, M, Hq, Hkv, D, dk, dv, ws_colsum);
+                         (const float *)dout, delta, c, B, M, Hq, Hkv, D, dk, dv, w.colsum);
     }
     const int64_t n = (int64_t)B * M;
-    hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws_colsum, g, gamma, B, M, Hq,
+    hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w.colsum, g, gamma, B, M, Hq,
                        dg);
   }
-  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, ws_colsum, g, B, M, Hq, dgamma);
+  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, w.colsum, g, B, M, Hq, dgamma);
   return hipGetLastError();
 }
 

@@ -690,7 +690,7 @@ FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
 // Workspace of the attention calls (256-byte aligned regions):
 //   cs [B*M*D/2] float2 | khat [B*M*Hkv*D] bf16 | bias [B*Hq*M] f32 |
 //   part [nmulti*B*Hkv * 4 waves * NR * 64] f32 | cnt [B*Hkv*nqb] i32 |
-//   (backward) delta [B*Hq*M] f32 | colsum [B*Hq*M] f32
+//   (backward) qhat [B*M*Hq*D] bf16 | rowstat [B*Hq*M] float2 | colsum [B*Hq*M] f32
 static size_t rup(size_t x) { return (x + 255) / 256 * 256; }
 
 static size_t part_floats(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
@@ -707,7 +707,9 @@ size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64
   size_t n = rup((size_t)(B * M * (D / 2)) * sizeof(float2)) + rup((size_t)(B * M * Hkv * D) * 2) +
              rup((size_t)(B * Hq * M) * sizeof(float)) + rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float)) +
              rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int));
-  if (bwd) n += 2 * rup((size_t)(B * Hq * M) * sizeof(float));
+  if (bwd)
+    n += rup((size_t)(B * M * Hq * D) * 2) + rup((size_t)(B * Hq * M) * sizeof(float2)) +
+         rup((size_t)(B * Hq * M) * sizeof(float));
   return n;
 }
 
@@ -725,8 +727,10 @@ AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, in
   w.cnt = (int *)p;
   w.ncnt = (int)cnt_ints(B, M, Hq, Hkv);
   p += rup((size_t)w.ncnt * sizeof(int));
-  w.delta = (float *)p;
-  p += rup((size_t)(B * Hq * M) * sizeof(float));
+  w.qhat = (uint16_t *)p;
+  p += rup((size_t)(B * M * Hq * D) * 2);
+  w.rowstat = (float2 *)p;
+  p += rup((size_t)(B * Hq * M) * sizeof(float2));
   w.colsum = (float *)p;
   return w;
 }

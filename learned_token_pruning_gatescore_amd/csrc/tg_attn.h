@@ -13,7 +13,8 @@ struct AttnWs {
   float *part;       // partial (O, max, sum) records of the forward's split query blocks
   int *cnt;          // [B*Hkv, nqb] arrival counters of the split query blocks
   int ncnt;
-  float *delta;      // [B, Hq, M] D_i of the backward
+  uint16_t *qhat;    // [B, M, Hq, D] rotated queries (bf16) of the backward
+  float2 *rowstat;   // [B, Hq, M] (-lse / c, D_i) of the backward (fp32 path: D_i alone)
   float *colsum;     // [B, Hq, M] column sums of dS per head
 };
 
