@@ -129,9 +129,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
   constexpr int NVM = NIW + 1;            // + the bias load
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * T::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * T::TILE];
-  __shared__ __attribute__((aligned(1024))) float sBias[3][8][AB_T];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[4 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[4 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) float sBias[4][8][AB_T];
   __shared__ __attribute__((aligned(1024))) float sDummy[256];  // target of the other waves' bias loads
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
   const uint32_t bvo = (uint32_t)((((lane >> 3) * M) + 4 * (lane & 7)) * 4);
   const u32x4 kones = ones3(hl);
 
-  auto slot = [](int t) __attribute__((always_inline)) { return t % 3; };
+  auto slot = [](int t) __attribute__((always_inline)) { return t & 3; };
   auto issue = [&](int t, int nt) __attribute__((always_inline)) {
     const bool live = t < nt;
     const uint32_t toff = (uint32_t)(t * AB_T) * rsb;
@@ -258,30 +258,45 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    const int tu = tdiag < nt ? tdiag : nt;  // unmasked tiles first, then the masked ones
+    auto tile = [&](int t, f32x16 &s, f32x16 &dp, const u32x4 &dinit, bool with_d) __attribute__((always_inline)) {
+      s = mfma32(kones, laug, f32x16{});
+      dp = with_d ? mfma32(kones, dinit, f32x16{}) : f32x16{};
+      sdp(sK + slot(t) * T::TILE, sV + slot(t) * T::TILE, s, dp);
+    };
+
     // pass A: D_i = sum_j P_ij dP_ij
     float dsa[4] = {0.f, 0.f, 0.f, 0.f};
-    auto body_a = [&](int t, bool masked) __attribute__((always_inline)) {
-      sync_vm<NVM>();
-      issue(t + 2, nt);
-      const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
-      f32x16 s = mfma32(kones, laug, f32x16{}), dp = f32x16{};
-      sdp(K, V, s, dp);
+    auto valu_a = [&](int t, const f32x16 &s, const f32x16 &dp, bool masked) __attribute__((always_inline)) {
       const float *bi = &sBias[slot(t)][hloc][4 * hl];
       const int lim = qi - t * AB_T;  // keys (within the tile) past the query are masked
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 bv = *(const f32x4 *)(bi + 8 * j);
+      for (int j = 0; j < 8; ++j) {
+        const float2 bv = *(const float2 *)(bi + 8 * (j >> 1) + 2 * (j & 1));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = __builtin_fmaf(s[4 * j + e], c2, bv[e]);
-          if (masked && 8 * j + 4 * hl + e > lim) x = -INFINITY;
-          dsa[e] = __builtin_fmaf(fast_exp2(x), dp[4 * j + e], dsa[e]);
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * j + e;
+          float x = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+          if (masked && acc_row(r, hl) > lim) x = -INFINITY;
+          dsa[r & 3] = __builtin_fmaf(fast_exp2(x), dp[r], dsa[r & 3]);
         }
       }
     };
-    const int tu = tdiag < nt ? tdiag : nt;  // unmasked tiles first, then the masked ones
-    for (int t = 0; t < tu; ++t) body_a(t, false);
-    for (int t = tu; t < nt; ++t) body_a(t, true);
+    {
+      f32x16 s, dp;
+      for (int t = 0; t < tu; ++t) {
+        sync_vm<NVM>();
+        issue(t + 2, nt);
+        tile(t, s, dp, kones, false);
+        valu_a(t, s, dp, false);
+      }
+      for (int t = tu; t < nt; ++t) {
+        sync_vm<NVM>();
+        issue(t + 2, nt);
+        tile(t, s, dp, kones, false);
+        valu_a(t, s, dp, true);
+      }
+    }
     sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
     float dsum = (dsa[0] + dsa[1]) + (dsa[2] + dsa[3]);
     dsum += __shfl_xor(dsum, 32);
@@ -294,12 +309,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-    auto body_b = [&](int t, bool masked) __attribute__((always_inline)) {
-      sync_vm<NVM>();
-      issue(t + 2, nt);
-      const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
-      f32x16 s = mfma32(kones, laug, f32x16{}), dp = mfma32(kones, daug, f32x16{});
-      sdp(K, V, s, dp);
+    // dS of tile t as the B operand of the dQ^T product: step hf, slot e = register 8 hf + e
+    auto valu_b = [&](int t, const f32x16 &s, const f32x16 &dp, bool masked, u32x4(&dsf)[2]) __attribute__((always_inline)) {
       const float *bi = &sBias[slot(t)][hloc][4 * hl];
       const int lim = qi - t * AB_T;
       float ds[16];
@@ -314,16 +325,29 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
           ds[r] = fast_exp2(x) * dp[r];
         }
       }
-      // B operand of step hf: slot e is register 8 hf + e
-      u32x4 dsf[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int w = 0; w < 4; ++w) dsf[hf][w] = pack_bf16x2(ds[8 * hf + 2 * w], ds[8 * hf + 2 * w + 1]);
-      trprod(K, dsf, acc);
     };
-    for (int t = 0; t < tu; ++t) body_b(t, false);
-    for (int t = tu; t < nt; ++t) body_b(t, true);
+    {
+      f32x16 s, dp;
+      u32x4 dsf[2];
+      for (int t = 0; t < tu; ++t) {
+        sync_vm<NVM>();
+        issue(t + 2, nt);
+        tile(t, s, dp, daug, true);
+        valu_b(t, s, dp, false, dsf);
+        trprod(sK + slot(t) * T::TILE, dsf, acc);
+      }
+      for (int t = tu; t < nt; ++t) {
+        sync_vm<NVM>();
+        issue(t + 2, nt);
+        tile(t, s, dp, daug, true);
+        valu_b(t, s, dp, true, dsf);
+        trprod(sK + slot(t) * T::TILE, dsf, acc);
+      }
+    }
     sync_vm<0>();
 
     // dq = c R(-phi) dq^ ; lane holds rows d = 32 db + acc_row(r, hl) of its column
@@ -366,8 +390,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
 //     the MFMA rows, keys on the columns: one key per lane), P, dV^T += dO^T P;
 //     hands P (fp32) to its partner through LDS;
 //   role 1 (waves 4-7, V of the same keys): one item behind, dP = dO V^T,
-//     dS = P (dP - D), the column sums, dK^T += Q^T dS.
-// Each work-group takes key block p and then block nkb-1-p.
+//     dS = P (dP - D) and the column sums; the product dK^T += Q^T dS of an
+//     item runs one iteration later still, first in the iteration, so that
+//     the two waves of a SIMD are not both in their products at once.
+// Items live in a ring of 5 LDS slots (two in flight, three in use).  Each
+// work-group takes key block p and then block nkb-1-p.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
@@ -380,9 +407,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
   constexpr int NIW = 2 * T::NI / AB_NW;  // Q and dO direct loads per wave per item
   constexpr int NVM = NIW + 1;            // + the row-statistics load
   constexpr int KB = 4 * AB_T;            // keys per block
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[4 * T::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sO[4 * T::TILE];
-  __shared__ __attribute__((aligned(1024))) float2 sRS[4][AB_T];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[5 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sO[5 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) float2 sRS[5][AB_T];
   __shared__ __attribute__((aligned(1024))) f32x4 sP[2][4][4][64];  // [item parity][wave][r / 4][lane]
   __shared__ __attribute__((aligned(1024))) float sCol[8][KB];
   __shared__ __attribute__((aligned(256))) float sDummy[64];
@@ -446,12 +473,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
       const i32x4 rO = buffer_rsrc(dout + (bM * Hq + h) * D, q_bytes);
       const i32x4 rR = buffer_rsrc(rowstat + ((int64_t)b * Hq + h) * M, (uint32_t)M * 8u);
       const uint32_t toff = (uint32_t)(tq * AB_T) * rsq;
-      const uint32_t so = 2u * (uint32_t)((it & 3) * T::TILE);
+      const uint32_t so = 2u * (uint32_t)((it % 5) * T::TILE);
 #pragma unroll
       for (int n = 0; n < NIW; ++n)
         dma_b128(iso[n] ? rO : rQ, (iso[n] ? lds_addr(sO) : lds_addr(sQ)) + so + dlo[n],
                  live ? dgo[n] + toff : 0x80000000u, 0u);
-      dma_b32(rR, wave == 0 ? lds_addr(&sRS[it & 3][0]) : lds_addr(sDummy),
+      dma_b32(rR, wave == 0 ? lds_addr(&sRS[it % 5][0]) : lds_addr(sDummy),
               live && wave == 0 ? (uint32_t)(tq * AB_T * 8 + 4 * lane) : 0x80000000u, 0u);
     };
     issue(0);
@@ -473,8 +500,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
       float blane = -INFINITY;
       auto item = [&](int it, bool masked) __attribute__((always_inline)) {
         const int i0 = (tq0 + it % ntl) * AB_T;
-        const uint16_t *Qt = sQ + (it & 3) * T::TILE, *Ot = sO + (it & 3) * T::TILE;
-        const float2 rs = sRS[it & 3][l32];
+        const uint16_t *Qt = sQ + (it % 5) * T::TILE, *Ot = sO + (it % 5) * T::TILE;
+        const float2 rs = sRS[it % 5][l32];
         f32x16 s = mfma32(aug3(i0 + l32 < M ? rs.x : -1e30f, hl), kones, f32x16{});
         {
           u32x4 f[NKS];
@@ -524,6 +551,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
       }
       sync_vm<NVM>();
       issue(nit + 2);
+      sync_vm<NVM>();
+      issue(nit + 3);
       sync_vm<0>();
       if (vk) {
         float *dvr = dv + koff;
@@ -536,7 +565,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
           }
       }
     } else {
-      // ---- role 1: dP, dS, column sums, dK (one item behind role 0) ----
+      // ---- role 1: dP, dS and the column sums one item behind role 0, the
+      // dK product of an item one iteration later still (before the next dP) ----
       u32x4 vf[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
@@ -545,9 +575,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
 #pragma unroll
       for (int db = 0; db < NDB; ++db) aK[db] = f32x16{};
       float csum = 0.f;
-      auto item = [&](int jt) __attribute__((always_inline)) {
-        const uint16_t *Qt = sQ + (jt & 3) * T::TILE, *Ot = sO + (jt & 3) * T::TILE;
-        const float2 rs = sRS[jt & 3][l32];
+      u32x4 dsf[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+      int pit = -1;  // item whose dS waits for its dK product
+      auto dstep = [&](int jt) __attribute__((always_inline)) {
+        const uint16_t *Ot = sO + (jt % 5) * T::TILE;
+        const float2 rs = sRS[jt % 5][l32];
         f32x16 dp = mfma32(aug3(-rs.y, hl), kones, f32x16{});
         {
           u32x4 f[NKS];
@@ -571,30 +603,32 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
             csum += ds[4 * j + e];
           }
         }
-        u32x4 dsf[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int w = 0; w < 4; ++w) dsf[hf][w] = pack_bf16x2(ds[8 * hf + 2 * w], ds[8 * hf + 2 * w + 1]);
-        trprod(Qt, dsf, aK);
       };
       sync_vm<NVM>();
       issue(2);
       for (int hh = 0; hh < G; ++hh) {
         const int it0 = hh * ntl;
-        for (int n = 0; n < nskip; ++n) {
+        for (int n = 0; n < ntl; ++n) {
           sync_vm<NVM>();
           issue(it0 + n + 3);
-        }
-        for (int n = nskip; n < ntl; ++n) {
-          sync_vm<NVM>();
-          issue(it0 + n + 3);
-          item(it0 + n);
+          if (pit >= 0) trprod(sQ + (pit % 5) * T::TILE, dsf, aK);
+          pit = -1;
+          if (n >= nskip) {
+            dstep(it0 + n);
+            pit = it0 + n;
+          }
         }
         const float tot = csum + __shfl_xor(csum, 32);
         if (hl == 0) sCol[hh][AB_T * sub + l32] = tot;
         csum = 0.f;
       }
+      sync_vm<NVM>();
+      issue(nit + 3);
+      if (pit >= 0) trprod(sQ + (pit % 5) * T::TILE, dsf, aK);
       sync_vm<0>();
       if (vk) {
         float *dkr = dk + koff;
@@ -787,27 +821,43 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
 // ---------------------------------------------------------------------------
 // 3. gate gradients
 // ---------------------------------------------------------------------------
-__global__ void dg_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
-                          const float *__restrict__ gamma, int B, int M, int Hq, float *__restrict__ dg) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)B * M) return;
-  const int64_t b = idx / M, j = idx % M;
-  float acc = 0.f;
-  for (int h = 0; h < Hq; ++h) acc += gamma[h] * colsum[(b * Hq + h) * M + j];
-  const float gv = g[idx];
-  dg[idx] = gv > 0.f ? acc / gv : 0.f;
+// dg_j = sum_h gamma_h colsum_h(j) / g_j, one thread per token in fixed head
+// order; each work-group also leaves, per head, its tokens' share of dgamma,
+// sum_j colsum_h(j) ln g_j (fixed-shape reductions), in part[b][bx][h].
+__global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
+                                                 const float *__restrict__ gamma, int B, int M, int Hq,
+                                                 float *__restrict__ dg, float *__restrict__ part) {
+  __shared__ float red[4];
+  const int j = blockIdx.x * 256 + threadIdx.x;  // grid (ceil(M / 256), min(B, 65535))
+  const bool vj = j < M;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int b = blockIdx.y; b < B; b += gridDim.y) {
+    const float *cr = colsum + (int64_t)b * Hq * M + j;
+    const float gv = vj ? g[(int64_t)b * M + j] : 0.f;
+    const float lg = gv > 0.f ? logf(gv) : 0.f;
+    float acc = 0.f;
+    for (int h = 0; h < Hq; ++h) {
+      const float v = vj ? cr[(int64_t)h * M] : 0.f;
+      acc += gamma[h] * v;
+      float t = gv > 0.f ? v * lg : 0.f;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+      if (lane == 0) red[wave] = t;
+      __syncthreads();
+      if (threadIdx.x == 0) part[((int64_t)b * gridDim.x + blockIdx.x) * Hq + h] = (red[0] + red[1]) + (red[2] + red[3]);
+      __syncthreads();
+    }
+    if (vj) dg[(int64_t)b * M + j] = gv > 0.f ? acc / gv : 0.f;
+  }
 }
 
-__global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
-                                                     int B, int M, int Hq, float *__restrict__ dgamma) {
+// dgamma_h = sum over the n = B * ceil(M / 256) shares of head h, fixed-shape tree
+__global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ part, int n, int Hq,
+                                                     float *__restrict__ dgamma) {
   __shared__ float red[256];
   const int h = blockIdx.x;
   float acc = 0.f;
-  for (int64_t idx = threadIdx.x; idx < (int64_t)B * M; idx += 256) {
-    const int64_t b = idx / M, j = idx % M;
-    const float gv = g[idx];
-    if (gv > 0.f) acc += colsum[(b * Hq + h) * M + j] * logf(gv);
-  }
+  for (int i = threadIdx.x; i < n; i += 256) acc += part[(int64_t)i * Hq + h];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -862,11 +912,12 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
                          (const float *)dout, delta, c, B, M, Hq, Hkv, D, dk, dv, w.colsum);
     }
-    const int64_t n = (int64_t)B * M;
-    hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w.colsum, g, gamma, B, M, Hq,
-                       dg);
+    // the row statistics are dead by now: their space takes the dgamma shares
+    hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)(B < 65535 ? B : 65535)), dim3(256), 0,
+                       s, w.colsum, g, gamma, B, M, Hq, dg, (float *)w.rowstat);
   }
-  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, w.colsum, g, B, M, Hq, dgamma);
+  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, (const float *)w.rowstat,
+                     (int)((int64_t)B * ((M + 255) / 256)), Hq, dgamma);
   return hipGetLastError();
 }
 
