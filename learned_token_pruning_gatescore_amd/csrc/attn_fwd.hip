@@ -26,6 +26,7 @@
 //   * online softmax in fp32, P rounded to bf16 for the MFMA.
 #include "tg_common.h"
 #include "tg_attn.h"
+#include "tg_tile.h"
 
 namespace tg {
 
@@ -78,62 +79,36 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
 }
 
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-
-// LDS layout of a bf16 tile (row = key): rows of D elements, unpadded, with
-// 16-byte chunks XOR-swizzled per row.  gfx950 LDS serves 64 banks (256 bytes)
-// per cycle: 16 lanes of a 16-byte read, 32 lanes of an 8-byte read.
-//   K tiles are read as 16-byte MFMA fragments, 16 consecutive rows at one
-//   logical chunk per 16 lanes: the 16 rows must hit 16 distinct 16-byte slots
-//   of the 256-byte bank window -> chunk ^ (row % 16) for D = 128 (one row per
-//   window), chunk ^ ((row / 2) % 8) for D = 64 (two rows per window).
-//   V tiles are read with ds_read_b64_tr_b16: per 32 lanes, 4 consecutive rows
-//   x logical chunks {4db .. 4db+3} (8 bytes per lane): the XOR must move the
-//   4 rows to distinct chunk groups -> chunk ^ 4 (row % 4) for D = 128,
-//   chunk ^ 4 ((row / 2) % 2) for D = 64.
-template <int D>
-struct Tile {
-  static constexpr int C = D / 8;               // 16-byte chunks per row
-  static constexpr int RPI = 1024 / (2 * D);    // rows per 1 KB direct-load instruction
-  static constexpr int NI = 64 / RPI;           // instructions per 64-row tile
-  __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  __device__ static int vswz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
-};
-
-
 // ---------------------------------------------------------------------------
-// bf16 forward.  Work-group = 4 waves (one per SIMD) = 256 columns, a column
+// bf16 forward.  Work-group = 8 waves (two per SIMD) = 256 columns, a column
 // being a (query, head) pair of the GQA group: BQ = 256 / G queries x G
-// heads.  Wave w owns columns 64w .. 64w+63 as two 32-column blocks (cb); a
-// block lies in one head.  Keys come in 32-key tiles.
+// heads.  Wave w owns columns 32w .. 32w+31 (one head).  Keys come in 32-key
+// tiles, shared by the 8 waves through LDS (direct loads two tiles ahead, one
+// barrier per tile).  Per tile a wave runs S^T = K Q^T (keys on the MFMA
+// rows: each lane holds 16 keys of one column, so the row statistics are
+// lane-local plus one cross-half shuffle), the softmax of its 16 logits per
+// lane, and O^T += V^T P^T with V^T from the transposing LDS read; the other
+// wave of the SIMD fills the matrix cores while one is in its vector work.
 //
-// Per tile a wave runs 16 products for S^T = K Q^T (each K fragment read
-// from LDS feeds both column blocks) and 16 for O^T += V^T P^T, and the
-// softmax of 32 logits per lane.  The loop is pipelined two deep: iteration
-// t issues the products of S(t+1) and of P(t-1) V(t-1) and, in the same
-// basic block, the softmax of S(t), so the matrix cores and the vector ALU of
-// one wave overlap.  P(t) is computed with the running maximum before tile t;
-// only when a logit exceeds it by more than 8 (log2 units) is the maximum
-// raised, O and the sum rescaled and P(t) recomputed (rare branch).
+// The probabilities use a fixed reference maximum per column (the maximum of
+// the piece's first tile), subtracted inside the S^T products by one more
+// 16-deep step; no rescaling in the loop.  While the row sum stays below 2^64,
+// O and the sums are far from fp32 overflow and the result is exact up to
+// rounding; a piece whose sum does not is run again with the reference
+// raised by log2 of that sum (which bounds every probability by 1).
 //
 // Long causal rows are split along the keys into pieces (at most C tiles
 // each, the diagonal in the last piece) so that the work spreads over every
 // compute unit.  Each piece of a split query block writes its unnormalised
-// (O, max, sum) to the workspace and bumps a per-block counter; the last to
-// arrive merges all pieces in piece order (deterministic) and writes o, lse.
+// (O, reference, sum) to the workspace and bumps a per-block counter; the last
+// to arrive merges all pieces in piece order (deterministic) and writes o, lse.
 // ---------------------------------------------------------------------------
-constexpr int AF_TK = 32;  // keys per tile
+constexpr int AF_TK = AB_T;  // keys per tile
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  static constexpr int NKS = D / 16;           // 16-wide steps over the head dim
-  static constexpr int TILE = AF_TK * D;       // u16 per K or V tile
-  static constexpr int NIW = AF_TK / Tile<D>::RPI / 4;  // direct loads per wave per K (or V) tile
-  static constexpr int NVM = 2 * NIW + 1;      // direct loads per wave per iteration (K, V, bias)
-  static constexpr int NR = 2 * NDB * 16 + 4;  // floats per lane in a partial record
+  static constexpr int NDB = D / 32;    // 32-row blocks of O^T
+  static constexpr int NR = NDB * 16 + 2;  // floats per lane in a partial record (O^T, reference, sum)
 };
 
 // Tiles of query block qb (keys 0 .. min((qb+1) BQ, M) - 1) and its pieces.
@@ -144,16 +119,18 @@ __host__ __device__ inline int fwd_ntiles(int qb, int BQ, int M) {
 __host__ __device__ inline int fwd_npieces(int n, int C) { return (n + C - 1) / C; }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, const float2 *__restrict__ cs, float c2, int B, int M, int Hq, int Hkv, int G,
     int BQ, int nqb, int C, float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o,
     float *__restrict__ lse) {
-  using T = Tile<D>;
+  using T = BTile<D>;
   using F = FwdCfg<D>;
-  constexpr int NDB = F::NDB, NKS = F::NKS, HALF = D / 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * F::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * F::TILE];
+  constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
+  constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
+  constexpr int NVM = NIW + 1;            // + the bias load
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * T::TILE];
   __shared__ __attribute__((aligned(1024))) float sBias[3][8][AF_TK];
   __shared__ __attribute__((aligned(1024))) float sDummy[256];  // target of the other waves' bias loads
   __shared__ int sLast;
@@ -199,16 +176,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   const int q0 = qb * BQ;
   // tiles from here on hold keys past some query of the block: causal mask
   const int tdiag = (q0 / AF_TK - kt0) > 0 ? q0 / AF_TK - kt0 : 0;
+  const int tu = tdiag < nt ? tdiag : nt;
 
-  int hloc[2], qi[2];
-  bool vq[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int c0 = 64 * wave + 32 * cb;
-    hloc[cb] = c0 / BQ;
-    qi[cb] = q0 + c0 % BQ + l32;
-    vq[cb] = qi[cb] < M;
-  }
+  const int hloc = (AF_TK * wave) / BQ;
+  const int qi = q0 + (AF_TK * wave) % BQ + l32;
+  const bool vq = qi < M;
   const int64_t bM = (int64_t)b * M;
   const uint32_t rsb = (uint32_t)(Hkv * D * 2);  // bytes between consecutive keys
   const uint32_t kv_bytes = (uint32_t)(M - 1) * rsb + D * 2;
@@ -216,283 +188,172 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   const i32x4 rV = buffer_rsrc(v + (bM * Hkv + kvh) * D, kv_bytes);
   const i32x4 rB = buffer_rsrc(bias + (int64_t)b * Hq * M, (uint32_t)(Hq * M * 4));
 
-  // Direct loads.  Tile t of the piece (key tile kt0 + t) lives in ring slot
-  // t % 3.  Iteration i issues K(i+3), V(i+1) and bias(i+2) (slots freed by
-  // iteration i-1); slots of tiles outside the piece are zero-filled.
-  // per-lane byte offsets within a tile (row of instruction i, swizzled chunk)
-  uint32_t kvo[F::NIW], vvo[F::NIW];
+  BFrag<D> fr;
+  fr.init(lane);
+  // direct load j = wave + 8 n of the tile's 2 NI (K first, then V)
+  uint32_t dgo[NIW], dlo[NIW];
+  bool isv[NIW];
 #pragma unroll
-  for (int i = 0; i < F::NIW; ++i) {
-    const int row = (wave * F::NIW + i) * T::RPI + lane / T::C;
-    kvo[i] = (uint32_t)row * rsb + ((uint32_t)((lane % T::C) ^ T::kswz(row)) << 4);
-    vvo[i] = (uint32_t)row * rsb + ((uint32_t)((lane % T::C) ^ T::vswz(row)) << 4);
+  for (int n = 0; n < NIW; ++n) {
+    const int j = wave + AB_NW * n;
+    isv[n] = j >= T::NI;
+    dgo[n] = T::goff(j % T::NI, lane, rsb);
+    dlo[n] = 1024u * (uint32_t)(j % T::NI);
   }
-  // bias: wave 0 loads the G rows (8 lanes x 16 bytes per head); the other
-  // waves issue one load too (zeros, into sDummy) so every wave's count is fixed
+  // bias: wave 0 loads the G rows of the tile (8 lanes x 16 bytes per head)
   const bool breal = wave == 0 && (lane >> 3) < G;
   const uint32_t bvo = (uint32_t)((((lane >> 3) * M) + 4 * (lane & 7)) * 4);
-  auto slot = [](int t) __attribute__((always_inline)) { return ((t % 3) + 3) % 3; };
-  auto issue_kv = [&](int t, bool is_v) __attribute__((always_inline)) {
-    const bool live = t >= 0 && t < nt;
+  const u32x4 kones = ones3(hl);
+
+  auto slot = [](int t) __attribute__((always_inline)) { return t % 3; };
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const bool live = t < nt;
     const uint32_t toff = (uint32_t)((kt0 + t) * AF_TK) * rsb;  // uniform
-    const uint32_t lb = lds_addr(is_v ? sV : sK) + 2u * (uint32_t)(slot(t) * F::TILE);
+    const uint32_t so = 2u * (uint32_t)(slot(t) * T::TILE);
 #pragma unroll
-    for (int i = 0; i < F::NIW; ++i)
-      dma_b128(is_v ? rV : rK, lb + 2u * (uint32_t)((wave * F::NIW + i) * T::RPI * D),
-               live ? (is_v ? vvo[i] : kvo[i]) + toff : 0x80000000u, 0u);
-  };
-  auto issue_bias = [&](int t) __attribute__((always_inline)) {
-    const bool live = t >= 0 && t < nt;
-    const uint32_t toff = (uint32_t)((kvh * G * M + (kt0 + t) * AF_TK) * 4);  // uniform
+    for (int n = 0; n < NIW; ++n)
+      dma_b128(isv[n] ? rV : rK, (isv[n] ? lds_addr(sV) : lds_addr(sK)) + so + dlo[n],
+               live ? dgo[n] + toff : 0x80000000u, 0u);
+    const uint32_t boff = (uint32_t)((kvh * G * M + (kt0 + t) * AF_TK) * 4);  // uniform
     dma_b128(rB, wave == 0 ? lds_addr(&sBias[slot(t)][0][0]) : lds_addr(sDummy),
-             live && breal ? bvo + toff : 0x80000000u, 0u);
-  };
-  auto issue_group = [&](int i) __attribute__((always_inline)) {
-    issue_kv(i + 3, false);
-    issue_kv(i + 1, true);
-    issue_bias(i + 2);
+             live && breal ? bvo + boff : 0x80000000u, 0u);
   };
   // The first pass's direct loads go out first; the Q and rotation loads
   // below (all issued before any use) overlap with them.
-  issue_group(-3);
-  issue_group(-2);
-  issue_group(-1);
+  issue(0);
+  issue(1);
 
-  // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8] of each column block
-  u32x4 qf[2][NKS];
-  f32x4 csv[2][NKS / 2][4];  // (cos, sin) of the 8 rotary pairs of (ks, hl), two pairs per vector
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const uint16_t *qrow = q + ((bM + qi[cb]) * Hq + kvh * G + hloc[cb]) * D;
+  // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8]
+  u32x4 qf[NKS];
+  {
+    const uint16_t *qrow = q + ((bM + (vq ? qi : 0)) * Hq + kvh * G + hloc) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qf[cb][ks] = vq[cb] ? *(const u32x4 *)(qrow + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
-    const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq[cb] ? qi[cb] : 0)) * HALF);
+      qf[ks] = vq ? *(const u32x4 *)(qrow + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+    if (cs) {
+      const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq ? qi : 0)) * HALF);
+      f32x4 csv[NKS / 2][4];  // (cos, sin) of the 8 rotary pairs of (ks, hl), two pairs per vector
 #pragma unroll
-    for (int ks = 0; ks < NKS / 2; ++ks)
+      for (int ks = 0; ks < NKS / 2; ++ks)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) csv[cb][ks][w] = cs ? crow[(16 * ks + 8 * hl) / 2 + w] : f32x4{1.f, 0.f, 1.f, 0.f};
-  }
-  if (cs) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+        for (int w = 0; w < 4; ++w) csv[ks][w] = crow[(16 * ks + 8 * hl) / 2 + w];
 #pragma unroll
       for (int ks = 0; ks < NKS / 2; ++ks) {
-        u32x4 &x = qf[cb][ks], &y = qf[cb][ks + NKS / 2];
+        u32x4 &x = qf[ks], &y = qf[ks + NKS / 2];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const f32x4 c = csv[cb][ks][w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
+          const f32x4 t = csv[ks][w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
           const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
           const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
-          x[w] = pack_bf16x2(x0 * c[0] - y0 * c[1], x1 * c[2] - y1 * c[3]);
-          y[w] = pack_bf16x2(y0 * c[0] + x0 * c[1], y1 * c[2] + x1 * c[3]);
+          x[w] = pack_bf16x2(x0 * t[0] - y0 * t[1], x1 * t[2] - y1 * t[3]);
+          y[w] = pack_bf16x2(y0 * t[0] + x0 * t[1], y1 * t[2] + x1 * t[3]);
         }
       }
-  }
-
-  // fragment-read offsets: K row l32, logical chunk 2ks + hl; V transposing
-  // reads as in the tile layout notes above
-  const int krow = l32 * D;
-  const int kx = T::kswz(l32);
-  const int gi = lane >> 4, li = lane & 15, kq = li >> 2, cc = li & 3;
-  int vlo[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int dd = 32 * db + 16 * (gi & 1) + 4 * cc;
-    vlo[db] = (4 * hl + kq) * D + (((dd >> 3) ^ T::vswz(kq)) << 3) + (dd & 7);
-  }
-
-  f32x16 acc[NDB][2];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
-  // m2: reference maximum of each column (the probabilities are 2^(x - m2)).
-  // The S^T products subtract it themselves: one more 16-wide product step
-  // with a constant A fragment (1, 1 in k = 0, 1) and a per-column B fragment
-  // (-m2 / c2 as a bf16 pair hi + lo) adds -m2 / c2 to every raw dot product.
-  float m2[2] = {0.f, 0.f}, lsum[2] = {0.f, 0.f};
-  auto mref = [&](int cb) __attribute__((always_inline)) { return m2[cb]; };
-  const u32x4 kaug = hl == 0 ? u32x4{0x3F803F80u, 0u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
-  u32x4 qaug[2];
-  const float inv_c2 = 1.f / c2;
-  auto set_ref = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const float r = -m2[cb] * inv_c2;
-      const uint32_t hi = f32_to_bf16_bits(r);
-      const uint32_t lo = f32_to_bf16_bits(r - bf16_lo(hi));
-      qaug[cb] = hl == 0 ? u32x4{hi | (lo << 16), 0u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
     }
-  };
+  }
 
-  auto qk = [&](int t, f32x16(&s)[2]) __attribute__((always_inline)) {  // S(t)^T - m2 / c2
-    const uint16_t *K = sK + slot(t) * F::TILE;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32(kaug, qaug[cb], f32x16{});
+  // m2: reference maximum of the column (probabilities are 2^(x - m2)); the
+  // S^T products subtract m2 / c2 themselves through the extra step qaug.
+  float m2 = 0.f, lsum = 0.f;
+  u32x4 qaug = u32x4{0u, 0u, 0u, 0u};
+  const float inv_c2 = 1.f / c2;
+  f32x16 acc[NDB];
+
+  // S^T = K Q^T over the head dim, fragments read two steps ahead
+  auto sprod = [&](const uint16_t *K, f32x16 &s) __attribute__((always_inline)) {
+    u32x4 f[NKS];
+    f[0] = fr.rows(K, 0);
+    f[1] = fr.rows(K, 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const u32x4 a = *(const u32x4 *)(K + krow + (((2 * ks + hl) ^ kx) << 3));
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) s[cb] = mfma32(a, qf[cb][ks], s[cb]);
+      if (ks + 2 < NKS) f[ks + 2] = fr.rows(K, ks + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      s = mfma32(f[ks], qf[ks], s);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // O^T += V(t)^T P(t)^T.  P slot 8hl + e of step hf is key 16hf + 8(e/4) + 4hl + e%4,
-  // which is register 8hf + e of the S accumulator.
-  auto pv = [&](int t, const u32x4(&pp)[2][2]) __attribute__((always_inline)) {
-    const uint16_t *V = sV + slot(t) * F::TILE;
+  // O^T[db] += V^T[db] P^T over the tile's keys, transposing reads two steps ahead
+  auto pvprod = [&](const uint16_t *V, const u32x4(&x)[2]) __attribute__((always_inline)) {
+    u32x4 f[2 * NDB];
+    f[0] = fr.tr(V, 0, 0);
+    f[1] = fr.tr(V, 0, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {
+      if (i + 2 < 2 * NDB) f[i + 2] = fr.tr(V, (i + 2) / NDB, (i + 2) % NDB);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[i % NDB] = mfma32(f[i], x[i / NDB], acc[i % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // One tile: wait for it, issue tile t+2, S^T, the softmax of its 16 logits per
+  // lane (ref: the first tile of the first pass, which sets the reference), P V.
+  auto tile = [&](int t, bool masked, bool ref) __attribute__((always_inline)) {
+    sync_vm<NVM>();
+    issue(t + 2);
+    const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
+    f32x16 s = mfma32(kones, qaug, f32x16{});
+    sprod(K, s);
+    const float *bi = &sBias[slot(t)][hloc][4 * hl];
+    const int lim = qi - (kt0 + t) * AF_TK;  // keys (within the tile) past the query are masked
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 bv = *(const float2 *)(bi + 8 * (j >> 1) + 2 * (j & 1));
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * j + e;
+        x[r] = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+        if (masked && acc_row(r, hl) > lim) x[r] = -INFINITY;
+      }
+    }
+    if (ref) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m2 = mx == -INFINITY ? 0.f : mx;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] -= m2;
+      qaug = aug3(-m2 * inv_c2, hl);
+    }
+    float ps = 0.f;
+    u32x4 pf[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x2 pr[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          pr[rr] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + (16 * hf + 8 * rr) * D + vlo[db])));
-        const u32x4 a = {pr[0][0], pr[0][1], pr[1][0], pr[1][1]};
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[db][cb] = mfma32(a, pp[cb][hf], acc[db][cb]);
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = fast_exp2(x[8 * hf + 2 * w]), p1 = fast_exp2(x[8 * hf + 2 * w + 1]);
+        ps += p0 + p1;  // fp32 sums: the row statistics (lse) stay exact to fp32
+        pf[hf][w] = pack_bf16x2(p0, p1);
       }
+    lsum += ps;
+    pvprod(V, pf);
   };
-  // One iteration: wait for group t-2, issue group t, then, interleaved by hand
-  // in 16 slots (sched_barrier keeps the order): the products of S(t+1) and of
-  // P(t-1) V(t-1), one of each per slot, and the softmax of S(t), one logit
-  // pair per slot, against the fixed reference maximum m2 (no rescaling).
-  auto body = [&](int t, f32x16(&sc)[2], f32x16(&sn)[2], u32x4(&pc)[2][2], const u32x4(&pp)[2][2],
-                  bool masked) __attribute__((always_inline)) {
-    sync_vm<F::NVM>();
-    issue_group(t);
-    const uint16_t *K = sK + slot(t + 1) * F::TILE;
-    const uint16_t *V = sV + slot(t - 1) * F::TILE;
-    const float(*bi)[AF_TK] = sBias[slot(t)];
-    auto kread = [&](int ks) __attribute__((always_inline)) { return *(const u32x4 *)(K + krow + (((2 * ks + hl) ^ kx) << 3)); };
-    auto vread = [&](int j) __attribute__((always_inline)) {  // A fragment of P.V step j = (hf, db)
-      const int hf = j / NDB, db = j % NDB;
-      u32x2 pr[2];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
-        pr[rr] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + (16 * hf + 8 * rr) * D + vlo[db])));
-      return u32x4{pr[0][0], pr[0][1], pr[1][0], pr[1][1]};
-    };
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) sn[cb] = mfma32(kaug, qaug[cb], f32x16{});
-    u32x4 kf[NKS], vf[2 * NDB];
-    kf[0] = kread(0);
-    kf[1] = kread(1);
-    vf[0] = vread(0);
-    vf[1] = vread(1);
-    // bias pair of slot i: keys 8(r0/4) + 4hl + r0%4 (+1) of column block i / 8, r0 = 2 (i % 8);
-    // read two slots ahead into a ring of 3
-    auto bread = [&](int i) __attribute__((always_inline)) {
-      const int r0 = 2 * (i & 7);
-      return *(const float2 *)(bi[hloc[i >> 3]] + 8 * (r0 >> 2) + 4 * hl + (r0 & 3));
-    };
-    float2 bq[3];
-    bq[0] = bread(0);
-    bq[1] = bread(1);
-    float ps[2] = {0.f, 0.f};
-    const int lim[2] = {qi[0] - (kt0 + t) * AF_TK, qi[1] - (kt0 + t) * AF_TK};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((i & 1) == 0 && i / 2 + 2 < NKS) kf[i / 2 + 2] = kread(i / 2 + 2);
-      if ((i & 1) == 0 && i / 2 + 2 < 2 * NDB) vf[i / 2 + 2] = vread(i / 2 + 2);
-      if (i + 2 < 16) bq[(i + 2) % 3] = bread(i + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i / 2 < NKS) sn[i & 1] = mfma32(kf[i / 2], qf[i & 1][i / 2], sn[i & 1]);
-      if (i / 2 < 2 * NDB) {
-        const int j = i / 2;
-        acc[j % NDB][i & 1] = mfma32(vf[j], pp[i & 1][j / NDB], acc[j % NDB][i & 1]);
-      }
-      {
-        const int cb = i >> 3, r0 = 2 * (i & 7);
-        const int key = 8 * (r0 >> 2) + 4 * hl + (r0 & 3);  // keys key, key + 1
-        const float2 bv = bq[i % 3];
-        float x0 = __builtin_fmaf(sc[cb][r0], c2, bv.x);
-        float x1 = __builtin_fmaf(sc[cb][r0 + 1], c2, bv.y);
-        if (masked) {
-          x0 = key > lim[cb] ? -INFINITY : x0;
-          x1 = key + 1 > lim[cb] ? -INFINITY : x1;
-        }
-        const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
-        pc[cb][r0 >> 3][(r0 & 7) >> 1] = pack_bf16x2(p0, p1);
-        ps[cb] += p0 + p1;  // fp32 sums: the row statistics (lse) stay exact to fp32
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lsum[0] += ps[0];
-    lsum[1] += ps[1];
-  };
-
-  f32x16 sA[2], sB[2];
-  u32x4 pA[2][2], pB[2][2];
-  // One pass over the piece.  The probabilities use a fixed reference maximum
-  // per column: the maximum of the first tile on the first pass.  Later logits
-  // may exceed it: while the row sum stays below 2^64, O and the sums are far
-  // from fp32 overflow and the result is exact up to rounding.  A piece whose
-  // sum does not (or is not finite) is run again with the reference raised by
-  // log2 of that sum (which bounds every probability by 1 on the next pass).
   auto run = [&](bool first) __attribute__((always_inline)) {
     if (!first) {  // a repeated pass refills the ring (the first pass's loads went out above)
-      issue_group(-3);
-      issue_group(-2);
-      issue_group(-1);
+      issue(0);
+      issue(1);
     }
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) pB[cb][hf] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
-    lsum[0] = lsum[1] = 0.f;
-    sync_vm<F::NVM>();  // K(0) and bias(0) landed
-    qk(0, sA);
-    if (first) {  // reference = maximum logit of tile 0 (S(0) was computed with reference 0)
-      const float(*bi)[AF_TK] = sBias[slot(0)];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int lim = qi[cb] - kt0 * AF_TK;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-          const float x = __builtin_fmaf(sA[cb][r], c2, bi[hloc[cb]][key]);
-          mx = fmaxf(mx, (tdiag == 0 && key > lim) ? -INFINITY : x);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        m2[cb] = mx == -INFINITY ? 0.f : mx;
-        const float sh = m2[cb] * inv_c2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sA[cb][r] -= sh;
-      }
-      set_ref();
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    lsum = 0.f;
+    int t = 0;
+    if (first) {  // tile 0 sets the reference
+      if (tu > 0) tile(0, false, true);
+      else tile(0, true, true);
+      t = 1;
     }
-    for (int t = 0; t < nt; t += 2) {
-      if (t >= tdiag) body(t, sA, sB, pA, pB, true);
-      else body(t, sA, sB, pA, pB, false);
-      if (t + 1 >= nt) break;
-      if (t + 1 >= tdiag) body(t + 1, sB, sA, pB, pA, true);
-      else body(t + 1, sB, sA, pB, pA, false);
-    }
-    sync_vm<F::NVM>();  // V(nt-1) landed
-    if (nt & 1) pv(nt - 1, pA);
-    else pv(nt - 1, pB);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero-fill loads
+    for (; t < tu; ++t) tile(t, false, false);
+    for (; t < nt; ++t) tile(t, true, false);
+    sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
   };
-  set_ref();
   for (int pass = 0; pass < 4; ++pass) {
     run(pass == 0);
-    float lt[2];
-    bool bad = false;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      lt[cb] = lsum[cb] + __shfl_xor(lsum[cb], 32);
-      bad = bad || !(lt[cb] < 0x1p64f);
-    }
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const bool bad = !(lt < 0x1p64f);
     if (!__syncthreads_or(bad) || pass == 3) break;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      if (!(lt[cb] < 0x1p64f)) m2[cb] = mref(cb) + (lt[cb] < INFINITY ? __log2f(lt[cb]) : 120.f);
-    set_ref();
+    if (bad) m2 += lt < INFINITY ? __log2f(lt) : 120.f;
+    qaug = aug3(-m2 * inv_c2, hl);
   }
 
   // Split block: publish this piece, the last one to finish merges.  Records
@@ -505,20 +366,16 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
   auto ld_dev = [](const float *a) __attribute__((always_inline)) {
     return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
+  constexpr int RW = AB_NW * F::NR * 64;  // floats per work-group record
   int npm = 1;
   if (np > 1) {
-    float *rec = part + ((int64_t)(pfirst + p) * nbh + bh) * (4 * F::NR * 64) + wave * F::NR * 64 + lane;
+    float *rec = part + ((int64_t)(pfirst + p) * nbh + bh) * RW + wave * F::NR * 64 + lane;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st_dev(rec + ((db * 2 + cb) * 16 + r) * 64, acc[db][cb][r]);
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      st_dev(rec + (F::NR - 4 + cb) * 64, mref(cb));  // the reference O and the sum are relative to
-      st_dev(rec + (F::NR - 2 + cb) * 64, lsum[cb]);
-    }
+      for (int r = 0; r < 16; ++r) st_dev(rec + (db * 16 + r) * 64, acc[db][r]);
+    st_dev(rec + (F::NR - 2) * 64, m2);  // the reference O and the sum are relative to
+    st_dev(rec + (F::NR - 1) * 64, lsum);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0)
@@ -528,51 +385,39 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(
     npm = np;
   }
   // merge pieces 0 .. npm-1 in order, all from their records (this one's too)
-  float mm[2], lt[2];
-  if (npm == 1) {
-    mm[0] = mref(0), mm[1] = mref(1);
-    lt[0] = lsum[0], lt[1] = lsum[1];
-  } else {
-    const float *rec0 = part + ((int64_t)pfirst * nbh + bh) * (4 * F::NR * 64) + wave * F::NR * 64 + lane;
-    const int64_t pstride = (int64_t)nbh * (4 * F::NR * 64);
-    mm[0] = mm[1] = -INFINITY;
-    for (int pp2 = 0; pp2 < npm; ++pp2)
+  float mm = m2, lt = lsum;
+  if (npm > 1) {
+    const float *rec0 = part + ((int64_t)pfirst * nbh + bh) * RW + wave * F::NR * 64 + lane;
+    const int64_t pstride = (int64_t)nbh * RW;
+    mm = -INFINITY;
+    for (int pp2 = 0; pp2 < npm; ++pp2) mm = fmaxf(mm, ld_dev(rec0 + pp2 * pstride + (F::NR - 2) * 64));
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mm[cb] = fmaxf(mm[cb], ld_dev(rec0 + pp2 * pstride + (F::NR - 4 + cb) * 64));
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x16{};
-    lt[0] = lt[1] = 0.f;
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    lt = 0.f;
     for (int pp2 = 0; pp2 < npm; ++pp2) {
       const float *rec = rec0 + pp2 * pstride;
+      const float sc = mm == -INFINITY ? 0.f : fast_exp2(ld_dev(rec + (F::NR - 2) * 64) - mm);
+      lt += ld_dev(rec + (F::NR - 1) * 64) * sc;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const float sc = mm[cb] == -INFINITY ? 0.f : fast_exp2(ld_dev(rec + (F::NR - 4 + cb) * 64) - mm[cb]);
-        lt[cb] += ld_dev(rec + (F::NR - 2 + cb) * 64) * sc;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][cb][r] += ld_dev(rec + ((db * 2 + cb) * 16 + r) * 64) * sc;
-      }
+        for (int r = 0; r < 16; ++r) acc[db][r] += ld_dev(rec + (db * 16 + r) * 64) * sc;
     }
   }
+  const float ltot = lt + __shfl_xor(lt, 32);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (!vq) return;
+  const int hq = kvh * G + hloc;
+  uint16_t *orow = o + ((bM + qi) * Hq + hq) * D;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float ltot = lt[cb] + __shfl_xor(lt[cb], 32);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (!vq[cb]) continue;
-    const int hq = kvh * G + hloc[cb];
-    uint16_t *orow = o + ((bM + qi[cb]) * Hq + hq) * D;
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hl;
-        *(u32x2 *)(orow + d) = u32x2{pack_bf16x2(acc[db][cb][4 * g4] * inv, acc[db][cb][4 * g4 + 1] * inv),
-                                     pack_bf16x2(acc[db][cb][4 * g4 + 2] * inv, acc[db][cb][4 * g4 + 3] * inv)};
-      }
-    if (lse && hl == 0)
-      lse[((int64_t)b * Hq + hq) * M + qi[cb]] = ltot > 0.f ? (mm[cb] + __log2f(ltot)) * kLn2 : -INFINITY;
-  }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hl;
+      *(u32x2 *)(orow + d) = u32x2{pack_bf16x2(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv),
+                                   pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
+    }
+  if (lse && hl == 0) lse[((int64_t)b * Hq + hq) * M + qi] = ltot > 0.f ? (mm + __log2f(ltot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -695,8 +540,8 @@ static size_t rup(size_t x) { return (x + 255) / 256 * 256; }
 
 static size_t part_floats(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
   const FwdSched f = fwd_sched(B, M, Hq, Hkv);
-  const int64_t nr = 2 * (D / 32) * 16 + 4;
-  return (size_t)(f.nmulti * B * Hkv * 4 * nr * 64);
+  const int64_t nr = (D / 32) * 16 + 2;  // floats per lane of a record, 8 waves per work-group
+  return (size_t)(f.nmulti * B * Hkv * 8 * nr * 64);
 }
 
 static size_t cnt_ints(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
@@ -762,11 +607,11 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const float c2 = (float)(c * 1.4426950408889634);
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
     if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(256), 0, s, (const uint16_t *)q, kh,
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(512), 0, s, (const uint16_t *)q, kh,
                          (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part,
                          w.cnt, (uint16_t *)o, lse);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(256), 0, s, (const uint16_t *)q, kh,
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(512), 0, s, (const uint16_t *)q, kh,
                          (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part,
                          w.cnt, (uint16_t *)o, lse);
   } else {
