@@ -162,7 +162,9 @@ tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates,
 /* Workspace bytes the attention calls need (bwd = 0: forward, 1: backward).
  * Both attention calls require a workspace of at least this size, 256-byte
  * aligned: it holds the cos/sin table of the kept positions, the rotated keys,
- * log2 of the gates and, for the backward, D_i and the per-head column sums
+ * the per-head bias gamma_h log2 g_j, the partial results and arrival
+ * counters of the forward's split rows and, for the backward, the rotated
+ * queries, the row statistics (-lse / c, D_i) and the per-head column sums
  * of dS.  Its contents are scratch: nothing is carried between calls. */
 size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
                                     int64_t D, int bwd);

@@ -11,19 +11,20 @@
 //
 // bf16 kernel layout (gfx950, 32x32x16 bf16 MFMA, fp32 accumulate):
 //   * a prep pass computes the cos/sin table of the kept positions (fp64
-//     angles), the rotated keys and log2 g once per row;
-//   * one work-group = 4 waves = one (batch, kv head) and 128 "columns",
-//     a column being a (query, head) pair of the GQA group: BQ = 128 / G query
-//     positions x G heads share every K/V tile staged in LDS;
+//     angles), the rotated keys and the per-head bias gamma_h log2 g_j;
+//   * one work-group = 8 waves (two per SIMD) = one (batch, kv head) and 256
+//     "columns", a column being a (query, head) pair of the GQA group:
+//     BQ = 256 / G query positions x G heads share every K/V tile in LDS;
 //   * each wave owns 32 columns; it computes S^T = K Q^T (keys on the MFMA
 //     rows, its columns on the MFMA columns), so every lane holds 16 keys of a
-//     single column: the softmax max / sum is lane-local plus one cross-half
+//     single column: the row statistics are lane-local plus one cross-half
 //     shuffle, and P^T feeds the P.V product straight from registers;
-//   * O^T = V^T P^T reads V row-major through the transposing LDS read
+//   * O^T = V^T P^T reads V through the transposing LDS read
 //     ds_read_b64_tr_b16; Q (rotated) lives in registers for the whole loop;
-//   * 64-key tiles are double-buffered in LDS and filled by direct
-//     global->LDS loads issued one tile ahead (one barrier per tile);
-//   * online softmax in fp32, P rounded to bf16 for the MFMA.
+//   * 32-key tiles in chunk-major LDS layout (tg_tile.h), filled by direct
+//     global->LDS loads two tiles ahead (one barrier per tile);
+//   * softmax in fp32 against a fixed per-column reference, P rounded to
+//     bf16 for the MFMA, row sums in fp32.
 #include "tg_common.h"
 #include "tg_attn.h"
 #include "tg_tile.h"
