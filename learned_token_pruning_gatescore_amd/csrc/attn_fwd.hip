@@ -53,8 +53,15 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, rotary pair)
   if (idx < ncnt) cnt[idx] = 0;  // the split-row arrival counters of the forward kernel
   if (idx >= rows * half) return;
-  const int64_t r = idx / half;  // b * M + j
-  const int i = (int)(idx % half);
+  int64_t r;  // b * M + j
+  int i;
+  if (idx < 0x100000000ll) {  // 32-bit division where it suffices (always, at realistic sizes)
+    r = (uint32_t)idx / (uint32_t)half;
+    i = (int)((uint32_t)idx - (uint32_t)r * (uint32_t)half);
+  } else {
+    r = idx / half;
+    i = (int)(idx % half);
+  }
   if (pos) {
     const double phi = (double)pos[r] * inv.v[i];
     double sn, cn;
@@ -62,19 +69,31 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
     const float c = (float)cn, s = (float)sn;
     cs[r * half + i] = make_float2(c, s);
     if (khat) {
-      for (int h = 0; h < Hkv; ++h) {
-        const int64_t o = (r * Hkv + h) * D;
-        const float x = __uint_as_float((uint32_t)k[o + i] << 16);
-        const float y = __uint_as_float((uint32_t)k[o + half + i] << 16);
-        khat[o + i] = (uint16_t)f32_to_bf16_bits(x * c - y * s);
-        khat[o + half + i] = (uint16_t)f32_to_bf16_bits(y * c + x * s);
+      // eight heads at a time: all loads in flight before the first use
+      for (int h0 = 0; h0 < Hkv; h0 += 8) {
+        uint16_t xs[8], ys[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t o = (r * Hkv + (h0 + u < Hkv ? h0 + u : h0)) * D;
+          xs[u] = k[o + i];
+          ys[u] = k[o + half + i];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (h0 + u >= Hkv) break;
+          const int64_t o = (r * Hkv + h0 + u) * D;
+          const float x = __uint_as_float((uint32_t)xs[u] << 16);
+          const float y = __uint_as_float((uint32_t)ys[u] << 16);
+          khat[o + i] = (uint16_t)f32_to_bf16_bits(x * c - y * s);
+          khat[o + half + i] = (uint16_t)f32_to_bf16_bits(y * c + x * s);
+        }
       }
     }
   }
   if (bias) {
     const float gv = g[r];
     const float lg = gv > 0.f ? log2f(gv) : -INFINITY;
-    const int64_t b = r / M, j = r % M;
+    const int b = (int)r / M, j = (int)r - b * M;  // B * M < 2^31
     for (int h = i; h < Hq; h += half) bias[(b * Hq + h) * M + j] = gv > 0.f ? gamma[h] * lg : -INFINITY;
   }
 }
@@ -129,11 +148,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   using F = FwdCfg<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
-  constexpr int NVM = NIW + 1;            // + the bias load
+  constexpr int NVM = NIW + 1;            // + the bias load (wave 0 only)
   __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * T::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * T::TILE];
   __shared__ __attribute__((aligned(1024))) float sBias[3][8][AF_TK];
-  __shared__ __attribute__((aligned(1024))) float sDummy[256];  // target of the other waves' bias loads
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -216,8 +234,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       dma_b128(isv[n] ? rV : rK, (isv[n] ? lds_addr(sV) : lds_addr(sK)) + so + dlo[n],
                live ? dgo[n] + toff : 0x80000000u, 0u);
     const uint32_t boff = (uint32_t)((kvh * G * M + (kt0 + t) * AF_TK) * 4);  // uniform
-    dma_b128(rB, wave == 0 ? lds_addr(&sBias[slot(t)][0][0]) : lds_addr(sDummy),
-             live && breal ? bvo + boff : 0x80000000u, 0u);
+    if (wave == 0) dma_b128(rB, lds_addr(&sBias[slot(t)][0][0]), live && breal ? bvo + boff : 0x80000000u, 0u);
+  };
+  // wait for this wave's loads of the oldest tile in flight, then the barrier
+  auto sync_tile = [&]() __attribute__((always_inline)) {
+    if (wave == 0) sync_vm<NVM>();
+    else sync_vm<NVM - 1>();
   };
   // The first pass's direct loads go out first; the Q and rotation loads
   // below (all issued before any use) overlap with them.
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // One tile: wait for it, issue tile t+2, S^T, the softmax of its 16 logits per
   // lane (ref: the first tile of the first pass, which sets the reference), P V.
   auto tile = [&](int t, bool masked, bool ref) __attribute__((always_inline)) {
-    sync_vm<NVM>();
+    sync_tile();
     issue(t + 2);
     const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
     f32x16 s = mfma32(kones, qaug, f32x16{});
