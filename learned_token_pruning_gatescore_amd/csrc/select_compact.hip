@@ -129,6 +129,30 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
     const int64_t cnt64 = N - n0;
     const int cnt = cnt64 <= 0 ? 0 : (cnt64 >= SEL_I ? SEL_I : (int)cnt64);
     vbits = cnt >= 32 ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+    if (cnt == SEL_I && vec_s && (!fo || vec_f)) {
+      // every load of the segment in flight before the first use
+      f32x4 x[SEL_I / 4];
+      u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int v = 0; v < SEL_I / 4; ++v) x[v] = *(const f32x4 *)(sc + n0 + 4 * v);
+      if (fo) {
+        x0 = *(const u32x4 *)(fo + n0);
+        x1 = *(const u32x4 *)(fo + n0 + 16);
+      }
+#pragma unroll
+      for (int v = 0; v < SEL_I / 4; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * v + e] = order_key(x[v][e]);
+      fbits = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          fbits |= (((x0[w] >> (8 * e)) & 0xFFu) ? 1u : 0u) << (4 * w + e);
+          fbits |= (((x1[w] >> (8 * e)) & 0xFFu) ? 1u : 0u) << (16 + 4 * w + e);
+        }
+      return;
+    }
     if (cnt == SEL_I && vec_s) {
 #pragma unroll
       for (int v = 0; v < SEL_I / 4; ++v) {
@@ -263,13 +287,17 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
       for (int64_t r = 0; r < tq && m; ++r) m &= m - 1u;  // clear the lowest tq bits
       tkeep = tm & ~m;
     }
-    uint32_t all = km | tkeep;
-    int64_t p = kb + (tb < quota ? tb : quota);
-    while (all) {  // this segment's kept tokens in ascending order
-      const int i = __builtin_ctz(all);
-      if (p < M_alloc) out[p] = (int32_t)(n0 + i);
-      ++p;
-      all &= all - 1u;
+    const uint32_t all = km | tkeep;
+    const int64_t p = kb + (tb < quota ? tb : quota);
+    // this segment's kept tokens in ascending order: item i goes to p + (kept items before i)
+    if (all) {
+      int32_t *op = out + p;
+      const int64_t room = M_alloc - p;
+#pragma unroll
+      for (int i = 0; i < SEL_I; ++i) {
+        const int r = __popc(all & ((1u << i) - 1u));
+        if (((all >> i) & 1u) && r < room) op[r] = (int32_t)(n0 + i);
+      }
     }
     runK += tk;
     runT += tt;
