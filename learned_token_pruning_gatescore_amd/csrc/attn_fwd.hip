@@ -31,7 +31,8 @@
 
 namespace tg {
 
-// Prep pass over the B*M kept rows (one thread per (row, rotary pair)):
+// Prep pass over the B*M kept rows (one thread per (row, rotary pair); the key
+// rotation by the work-group's threads in 16-byte pieces):
 //   cs[row][i]    = (cos, sin)(pos[row] * inv_freq[i]) with the angle and the
 //                   trigonometry in fp64 (inv_freq[i] = theta^(-2i/D), computed
 //                   on the host in fp64), stored as fp32;
@@ -49,48 +50,45 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
                                                         int M, int Hq, int Hkv, int D, float2 *__restrict__ cs,
                                                         uint16_t *__restrict__ khat, float *__restrict__ bias,
                                                         int *__restrict__ cnt, int ncnt) {
-  const int half = D / 2;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, rotary pair)
+  __shared__ float2 scs[256];
+  const int half = D / 2, R = 256 / half;  // R rows per work-group, one thread per (row, rotary pair)
+  const int t = threadIdx.x;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + t;
   if (idx < ncnt) cnt[idx] = 0;  // the split-row arrival counters of the forward kernel
-  if (idx >= rows * half) return;
-  int64_t r;  // b * M + j
-  int i;
-  if (idx < 0x100000000ll) {  // 32-bit division where it suffices (always, at realistic sizes)
-    r = (uint32_t)idx / (uint32_t)half;
-    i = (int)((uint32_t)idx - (uint32_t)r * (uint32_t)half);
-  } else {
-    r = idx / half;
-    i = (int)(idx % half);
-  }
-  if (pos) {
-    const double phi = (double)pos[r] * inv.v[i];
+  const int lr = t / half, i = t - lr * half;
+  const int64_t r0 = (int64_t)blockIdx.x * R, r = r0 + lr;
+  const bool vr = lr < R && r < rows;
+  if (pos && vr) {
     double sn, cn;
-    sincos(phi, &sn, &cn);
-    const float c = (float)cn, s = (float)sn;
-    cs[r * half + i] = make_float2(c, s);
-    if (khat) {
-      // eight heads at a time: all loads in flight before the first use
-      for (int h0 = 0; h0 < Hkv; h0 += 8) {
-        uint16_t xs[8], ys[8];
+    sincos((double)pos[r] * inv.v[i], &sn, &cn);
+    const float2 v = make_float2((float)cn, (float)sn);
+    cs[r * half + i] = v;
+    scs[t] = v;
+  }
+  if (pos && khat) {
+    // the work-group's R rows x Hkv heads x (half / 8) chunks: 16-byte loads and stores
+    __syncthreads();
+    const int nch = half / 8, per_row = Hkv * nch;
+    for (int it = t; it < R * per_row; it += 256) {
+      const int lr2 = it / per_row, rem = it - lr2 * per_row, h = rem / nch, ch = rem - h * nch;
+      if (r0 + lr2 >= rows) break;
+      const int64_t o = ((r0 + lr2) * Hkv + h) * D + 8 * ch;
+      const u32x4 x = *(const u32x4 *)(k + o), y = *(const u32x4 *)(k + o + half);
+      const float2 *cp = scs + lr2 * half + 8 * ch;
+      u32x4 xo, yo;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int64_t o = (r * Hkv + (h0 + u < Hkv ? h0 + u : h0)) * D;
-          xs[u] = k[o + i];
-          ys[u] = k[o + half + i];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (h0 + u >= Hkv) break;
-          const int64_t o = (r * Hkv + h0 + u) * D;
-          const float x = __uint_as_float((uint32_t)xs[u] << 16);
-          const float y = __uint_as_float((uint32_t)ys[u] << 16);
-          khat[o + i] = (uint16_t)f32_to_bf16_bits(x * c - y * s);
-          khat[o + half + i] = (uint16_t)f32_to_bf16_bits(y * c + x * s);
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float2 a0 = cp[2 * w], a1 = cp[2 * w + 1];
+        const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+        const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
+        xo[w] = pack_bf16x2(x0 * a0.x - y0 * a0.y, x1 * a1.x - y1 * a1.y);
+        yo[w] = pack_bf16x2(y0 * a0.x + x0 * a0.y, y1 * a1.x + x1 * a1.y);
       }
+      *(u32x4 *)(khat + o) = xo;
+      *(u32x4 *)(khat + o + half) = yo;
     }
   }
-  if (bias) {
+  if (bias && vr) {
     const float gv = g[r];
     const float lg = gv > 0.f ? log2f(gv) : -INFINITY;
     const int b = (int)r / M, j = (int)r - b * M;  // B * M < 2^31
@@ -610,7 +608,8 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
   InvFreq inv;
   for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
   const int64_t rows = (int64_t)B * M;
-  hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)((rows * (D / 2) + 255) / 256)), dim3(256), 0, s,
+  const int64_t R = 256 / (D / 2), nwg_rows = (rows + R - 1) / R, nwg_cnt = ((int64_t)w.ncnt + 255) / 256;
+  hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0, s,
                      (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
                      (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, w.cnt, with_bias ? w.ncnt : 0);
   return hipGetLastError();
