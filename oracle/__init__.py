@@ -61,12 +61,12 @@ def _load():
     lib.tgo_select_topk.restype = _i64
     lib.tgo_compact.argtypes = [_U8, _I32, _F, _I32, _i64, _i64, _i64, _U8, _I32, _F]
     lib.tgo_compact.restype = None
-    lib.tgo_attn_fwd.argtypes = [_D, _D, _D, _D, _D, _I32, ctypes.c_double, ctypes.c_double,
+    lib.tgo_attn_fwd.argtypes = [_D, _D, _D, _D, _D, _I32, ctypes.c_double, ctypes.c_double, _D,
                                  _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _I64, _i64, _D, _D]
     lib.tgo_attn_fwd.restype = ctypes.c_int
-    lib.tgo_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _I32, ctypes.c_double, ctypes.c_double,
+    lib.tgo_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _I32, ctypes.c_double, ctypes.c_double, _D,
                                  _D, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
-                                 _D, _D, _D, _D, _D]
+                                 _D, _D, _D, _D, _D, _D]
     lib.tgo_attn_bwd.restype = ctypes.c_int
     lib.tgo_round_bf16.argtypes = [ctypes.c_double]
     lib.tgo_round_bf16.restype = ctypes.c_double
@@ -180,9 +180,10 @@ def compact(hidden, pos, gates, kept):
     return out, pos_out, g_out
 
 
-def attn_fwd(q, k, v, g, gamma, pos=None, theta=1e6, tau=1.0, round_bf16=False, rows=None):
+def attn_fwd(q, k, v, g, gamma, pos=None, theta=1e6, tau=1.0, round_bf16=False, rows=None, sigma=None):
     """Token-gated causal attention forward (DeepDive section 2 Eq. 2, section 3.2 Eqs. 5-6;
-    Summary Figure 1(c)).
+    Summary Figure 1(c)).  With sigma [Hq] the operative rule of section 3.2 Eq. 8: the whole
+    logit scaled by tau_ih = softplus(sigma_h) ln(i+1) / ln max(2, pos_i+1) (Eq. 7).
 
     q [B, M, Hq, D]; k, v [B, M, Hkv, D]; g [B, M]; gamma [Hq]; pos int32 [B, M] or None.
     round_bf16: round the rotated q, k to bf16 before the product (as the tensor cores see them).
@@ -199,19 +200,21 @@ def attn_fwd(q, k, v, g, gamma, pos=None, theta=1e6, tau=1.0, round_bf16=False, 
     o = np.full((B, M, Hq, D), np.nan)
     lse = np.full((B, Hq, M), np.nan)
     r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    sg = None if sigma is None else _f64(sigma).reshape(Hq)
     rc = lib.tgo_attn_fwd(_ptr(Q, _D), _ptr(Kt, _D), _ptr(V, _D), _ptr(G, _D), _ptr(gm, _D), _ptr(p, _I32),
-                          float(theta), float(tau), B, M, Hq, Hkv, D, int(bool(round_bf16)),
+                          float(theta), float(tau), _ptr(sg, _D), B, M, Hq, Hkv, D, int(bool(round_bf16)),
                           _ptr(r, _I64), 0 if r is None else r.size, _ptr(o, _D), _ptr(lse, _D))
     if rc != 0:
         raise ValueError("oracle attn_fwd: bad arguments")
     return o, lse
 
 
-def attn_bwd(q, k, v, g, gamma, dout, pos=None, theta=1e6, tau=1.0, round_bf16=False):
+def attn_bwd(q, k, v, g, gamma, dout, pos=None, theta=1e6, tau=1.0, round_bf16=False, sigma=None):
     """Gradients of the token-gated attention (DeepDive section 3.1 last paragraph and section 3.2:
     the task gradient reaches the scores through the attention bias).
 
-    Returns (dq [B,M,Hq,D], dk [B,M,Hkv,D], dv [B,M,Hkv,D], dg [B,M], dgamma [Hq]), all float64.
+    Returns (dq [B,M,Hq,D], dk [B,M,Hkv,D], dv [B,M,Hkv,D], dg [B,M], dgamma [Hq]), all float64,
+    followed by dsigma [Hq] when sigma is given (the temperature of Eq. 7/8).
     """
     lib = _load()
     Q, Kt, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
@@ -225,12 +228,17 @@ def attn_bwd(q, k, v, g, gamma, dout, pos=None, theta=1e6, tau=1.0, round_bf16=F
     dv = np.empty((B, M, Hkv, D))
     dg = np.empty((B, M))
     dgamma = np.empty(Hq)
+    sg = None if sigma is None else _f64(sigma).reshape(Hq)
+    dsigma = None if sigma is None else np.empty(Hq)
     rc = lib.tgo_attn_bwd(_ptr(Q, _D), _ptr(Kt, _D), _ptr(V, _D), _ptr(G, _D), _ptr(gm, _D), _ptr(p, _I32),
-                          float(theta), float(tau), _ptr(dO, _D), B, M, Hq, Hkv, D, int(bool(round_bf16)),
-                          _ptr(dq, _D), _ptr(dk, _D), _ptr(dv, _D), _ptr(dg, _D), _ptr(dgamma, _D))
+                          float(theta), float(tau), _ptr(sg, _D), _ptr(dO, _D), B, M, Hq, Hkv, D,
+                          int(bool(round_bf16)), _ptr(dq, _D), _ptr(dk, _D), _ptr(dv, _D), _ptr(dg, _D),
+                          _ptr(dgamma, _D), _ptr(dsigma, _D))
     if rc != 0:
         raise ValueError("oracle attn_bwd: bad arguments")
-    return dq, dk, dv, dg, dgamma
+    if sigma is None:
+        return dq, dk, dv, dg, dgamma
+    return dq, dk, dv, dg, dgamma, dsigma
 
 
 def round_bf16(x: float) -> float:

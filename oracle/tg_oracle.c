@@ -263,6 +263,20 @@ static void rotate_all(const double *x, double *out, const int32_t *pos, double 
     }
 }
 
+/*
+ * Temperature of the operative attention rule ([DeepDive] section 3.2, Eq. 7):
+ *     tau_ih = softplus(sigma_h) * ln m_i / ln max(2, p_i)
+ * with m_i = i + 1 the kept keys visible to compacted row i and p_i = pos_i + 1
+ * the original positions visible to it (p_i = m_i without positions).
+ */
+static double softplus_d(double x) { return x > 30.0 ? x : log1p(exp(x)); }
+static double temp_ratio(int64_t i, const int32_t *pos, int64_t bm)
+{
+    double m = (double)(i + 1);
+    double p = pos ? (double)pos[bm] + 1.0 : m;
+    return log(m) / log(p > 2.0 ? p : 2.0);
+}
+
 /* ------------------------------------------------------------------------ */
 /* a4. Token-gated causal attention, forward                                 */
 /* ------------------------------------------------------------------------ */
@@ -282,14 +296,20 @@ static void rotate_all(const double *x, double *out, const int32_t *pos, double 
  * A key with g_j = 0 has ln g_j = -inf and weight 0; a row whose every logit
  * is -inf gets O = 0 and lse = -inf.
  *
+ * With sigma (per query head, NULL for none) the rule is the operative one of
+ * [DeepDive] section 3.2, Eq. 8: the whole logit is scaled by the temperature
+ * tau_ih of Eq. 7 (see temp_ratio above),
+ *     S_ij = tau_ih * (q^_i . k^_j / (sqrt(D) * tau) + gamma_h * ln g_j),
+ * a key with g_j = 0 still getting weight 0.
+ *
  * rows: optional list of nrows flattened (b * M + i) query rows to compute;
  * NULL computes all B*M rows.  o: [B, M, Hq, D], lse: [B, Hq, M]; entries of
  * rows not listed are left untouched.
  */
 int tgo_attn_fwd(const double *q, const double *k, const double *v, const double *g,
                  const double *gamma, const int32_t *pos, double theta, double tau,
-                 int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, int round,
-                 const int64_t *rows, int64_t nrows, double *o, double *lse)
+                 const double *sigma, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
+                 int round, const int64_t *rows, int64_t nrows, double *o, double *lse)
 {
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;
@@ -316,6 +336,7 @@ int tgo_attn_fwd(const double *q, const double *k, const double *v, const double
                 int64_t b = bi / M, i = bi % M;
                 int64_t kv = h / grp;
                 const double *qi = qr + ((b * M + i) * Hq + h) * D;
+                double t = sigma ? softplus_d(sigma[h]) * temp_ratio(i, pos, b * M + i) : 1.0;
                 double mx = -INFINITY;
                 for (int64_t j = 0; j <= i; ++j) {
                     const double *kj = kr + ((b * M + j) * Hkv + kv) * D;
@@ -323,8 +344,7 @@ int tgo_attn_fwd(const double *q, const double *k, const double *v, const double
                     for (int64_t e = 0; e < D; ++e)
                         dot += qi[e] * kj[e];
                     double gj = g[b * M + j];
-                    double bias = gj > 0.0 ? gamma[h] * log(gj) : -INFINITY;
-                    logit[j] = c * dot + bias;
+                    logit[j] = gj > 0.0 ? t * (c * dot + gamma[h] * log(gj)) : -INFINITY;
                     if (logit[j] > mx)
                         mx = logit[j];
                 }
@@ -373,14 +393,19 @@ int tgo_attn_fwd(const double *q, const double *k, const double *v, const double
  * group, and for the gate terms (S depends on g_j through gamma_h ln g_j):
  *     dg_j     = sum_h gamma_h colsum_h(j) / g_j      (0 where g_j = 0)
  *     dgamma_h = sum_b sum_j colsum_h(j) ln g_j       (terms with g_j = 0 skipped)
+ * With sigma (Eq. 8, S_ij = tau_ih Z_ij, Z_ij the bracket of the forward), the
+ * bracket's gradient is dZ_ij = tau_ih dS_ij: it replaces dS_ij in dq^, dk^ and
+ * colsum, and the temperature gets dtau_ih = sum_j dS_ij Z_ij, so
+ *     dsigma_h = sum_b sum_i dtau_ih * ln m_i / ln max(2, p_i) * sigmoid(sigma_h).
  *
- * dq: [B,M,Hq,D]; dk, dv: [B,M,Hkv,D]; dg: [B,M]; dgamma: [Hq].
+ * dq: [B,M,Hq,D]; dk, dv: [B,M,Hkv,D]; dg: [B,M]; dgamma: [Hq]; dsigma: [Hq]
+ * (written when sigma is given).
  */
 int tgo_attn_bwd(const double *q, const double *k, const double *v, const double *g,
                  const double *gamma, const int32_t *pos, double theta, double tau,
-                 const double *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
-                 int64_t D, int round, double *dq, double *dk, double *dv, double *dg,
-                 double *dgamma)
+                 const double *sigma, const double *dout, int64_t B, int64_t M, int64_t Hq,
+                 int64_t Hkv, int64_t D, int round, double *dq, double *dk, double *dv,
+                 double *dg, double *dgamma, double *dsigma)
 {
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;
@@ -389,10 +414,12 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
     double *qr = (double *)malloc(sizeof(double) * (size_t)(B * M * Hq * D));
     double *kr = (double *)malloc(sizeof(double) * (size_t)(B * M * Hkv * D));
     double *colsum = (double *)calloc((size_t)(B * Hq * M), sizeof(double));
-    if (!qr || !kr || !colsum) {
+    double *dsig = (double *)calloc((size_t)(B * Hq), sizeof(double)); /* per (b, h): no races */
+    if (!qr || !kr || !colsum || !dsig) {
         free(qr);
         free(kr);
         free(colsum);
+        free(dsig);
         return -1;
     }
     rotate_all(q, qr, pos, theta, B, M, Hq, D, round);
@@ -406,6 +433,7 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
     {
         double *P = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
         double *dP = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+        double *Z = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
 #pragma omp for schedule(dynamic, 1) collapse(2)
         for (int64_t b = 0; b < B; ++b) {
             for (int64_t kv = 0; kv < Hkv; ++kv) {
@@ -413,6 +441,8 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
                     for (int64_t i = 0; i < M; ++i) {
                         const double *qi = qr + ((b * M + i) * Hq + h) * D;
                         const double *doi = dout + ((b * M + i) * Hq + h) * D;
+                        double ratio = sigma ? temp_ratio(i, pos, b * M + i) : 1.0;
+                        double t = sigma ? softplus_d(sigma[h]) * ratio : 1.0;
                         double mx = -INFINITY;
                         for (int64_t j = 0; j <= i; ++j) {
                             const double *kj = kr + ((b * M + j) * Hkv + kv) * D;
@@ -420,8 +450,8 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
                             for (int64_t e = 0; e < D; ++e)
                                 dot += qi[e] * kj[e];
                             double gj = g[b * M + j];
-                            double bias = gj > 0.0 ? gamma[h] * log(gj) : -INFINITY;
-                            P[j] = c * dot + bias;
+                            Z[j] = gj > 0.0 ? c * dot + gamma[h] * log(gj) : -INFINITY;
+                            P[j] = gj > 0.0 ? t * Z[j] : -INFINITY;
                             if (P[j] > mx)
                                 mx = P[j];
                         }
@@ -442,24 +472,30 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
                             Di += P[j] * d;
                         }
                         double *dqi = dq + ((b * M + i) * Hq + h) * D;
+                        double dt = 0.0;
                         for (int64_t j = 0; j <= i; ++j) {
                             double dS = P[j] * (dP[j] - Di);
+                            double dZ = t * dS;
                             const double *kj = kr + ((b * M + j) * Hkv + kv) * D;
                             double *dkj = dk + ((b * M + j) * Hkv + kv) * D;
                             double *dvj = dv + ((b * M + j) * Hkv + kv) * D;
                             for (int64_t e = 0; e < D; ++e) {
-                                dqi[e] += c * dS * kj[e];
-                                dkj[e] += c * dS * qi[e];
+                                dqi[e] += c * dZ * kj[e];
+                                dkj[e] += c * dZ * qi[e];
                                 dvj[e] += P[j] * doi[e];
                             }
-                            colsum[(b * Hq + h) * M + j] += dS;
+                            colsum[(b * Hq + h) * M + j] += dZ;
+                            if (g[b * M + j] > 0.0)
+                                dt += dS * Z[j];
                         }
+                        dsig[b * Hq + h] += dt * ratio;
                     }
                 }
             }
         }
         free(P);
         free(dP);
+        free(Z);
     }
 
     /* Undo the rotation on the gradients of the rotated q and k. */
@@ -491,9 +527,18 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
             }
         dgamma[h] = acc;
     }
+    if (sigma && dsigma) {
+        for (int64_t h = 0; h < Hq; ++h) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                acc += dsig[b * Hq + h];
+            dsigma[h] = acc / (1.0 + exp(-sigma[h])); /* d softplus / d sigma = sigmoid(sigma) */
+        }
+    }
     free(qr);
     free(kr);
     free(colsum);
+    free(dsig);
     return 0;
 }
 

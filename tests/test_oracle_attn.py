@@ -240,3 +240,109 @@ def test_bwd_invariants(oracle_mod):
     d1 = np.random.default_rng(31).standard_normal((1, 9, 1, 4))
     _, _, _, dg1, dgam1 = oracle_mod.attn_bwd(q1, k1, v1, g1, gam1, d1)
     np.testing.assert_allclose(dgam1[0], (g1 * dg1 * np.log(g1)).sum() / gam1[0], rtol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# The operative rule with the pruning-ratio temperature (DeepDive section 3.2,
+# Eq. 7 and Eq. 8): S_ij = tau_ih (q^.k^ / (sqrt(D) tau) + gamma_h ln g_j),
+# tau_ih = softplus(sigma_h) ln m_i / ln max(2, p_i), m_i = i + 1, p_i = pos_i + 1.
+# ---------------------------------------------------------------------------
+def _temp(sigma, pos, B, M):
+    """tau [B, M, Hq] from Eq. 7 (torch, differentiable in sigma)."""
+    m = torch.arange(1, M + 1, dtype=torch.float64)[None, :].expand(B, M)
+    p = (pos.to(torch.float64) + 1.0) if pos is not None else m
+    r = torch.log(m) / torch.log(torch.clamp(p, min=2.0))
+    return F.softplus(sigma)[None, None, :] * r[:, :, None]
+
+
+def _sdpa_temp_ref(q, k, v, g, gamma, sigma, tau, pos=None, theta=1e6):
+    """SDPA with the temperature folded in: the query scaled by tau_ih / (sqrt(D) tau) and the
+    additive mask tau_ih gamma_h ln g_j (both per row and head)."""
+    B, M, Hq, D = q.shape
+    grp = Hq // k.shape[2]
+    t = _temp(sigma, pos, B, M)  # [B, M, Hq]
+    if pos is not None:
+        q = _rope_complex(q, pos, theta)
+        k = _rope_complex(k, pos, theta)
+    qh = (q * t[..., None] / (math.sqrt(D) * tau)).permute(0, 2, 1, 3)
+    kh = k.repeat_interleave(grp, dim=2).permute(0, 2, 1, 3)
+    vh = v.repeat_interleave(grp, dim=2).permute(0, 2, 1, 3)
+    bias = t.permute(0, 2, 1)[..., None] * gamma[None, :, None, None] * torch.log(g)[:, None, None, :]
+    causal = torch.ones(M, M, dtype=torch.bool).tril()
+    mask = torch.where(causal[None, None], bias, torch.tensor(float("-inf"), dtype=torch.float64))
+    o = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=1.0)
+    return o.permute(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_temp_fwd_matches_sdpa(oracle_mod, rope):
+    B, M, Hq, Hkv, D = 2, 14, 4, 2, 8
+    q, k, v, g, gamma, pos = _inputs(41, B, M, Hq, Hkv, D)
+    sigma = np.random.default_rng(42).normal(0.0, 1.0, Hq)
+    p = pos if rope else None
+    o, lse = oracle_mod.attn_fwd(q, k, v, g, gamma, pos=p, theta=400.0, tau=1.1, sigma=sigma)
+    ref = _sdpa_temp_ref(T(q), T(k), T(v), T(g), T(gamma), T(sigma), 1.1, torch.from_numpy(pos) if rope else None,
+                         400.0)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_temp_closed_form_and_reductions(oracle_mod):
+    B, M, Hq, Hkv, D = 1, 9, 2, 1, 4
+    q, k, v, g, gamma, pos = _inputs(43, B, M, Hq, Hkv, D)
+    sigma = np.array([0.3, -0.7])
+    # q = 0: S_ij = tau_i gamma_h ln g_j, so P_ij is proportional to g_j^(tau_i gamma_h)
+    pos = np.array([[0, 3, 4, 10, 11, 40, 41, 42, 300]], dtype=np.int32)
+    o, _ = oracle_mod.attn_fwd(np.zeros_like(q), k, v, g, gamma, pos=pos, sigma=sigma)
+    sp = np.log1p(np.exp(sigma))
+    for h in range(Hq):
+        for i in range(M):
+            t = sp[h] * math.log(i + 1) / math.log(max(2.0, pos[0, i] + 1.0))
+            w = g[0, : i + 1] ** (t * gamma[h])
+            ref = (w[:, None] * v[0, : i + 1, 0]).sum(0) / w.sum()
+            np.testing.assert_allclose(o[0, i, h], ref, rtol=1e-12, atol=1e-13)
+    # softplus(sigma) = 1 and no positions (p_i = m_i): tau = 1 on every row that sees more
+    # than one key, so the output is the temperature-free one
+    one = np.full(Hq, math.log(math.e - 1.0))
+    o1, l1 = oracle_mod.attn_fwd(q, k, v, g, gamma, sigma=one)
+    o0, l0 = oracle_mod.attn_fwd(q, k, v, g, gamma)
+    np.testing.assert_allclose(o1, o0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1[:, :, 1:], l0[:, :, 1:], rtol=1e-12, atol=1e-13)
+    assert np.all(l1[:, :, 0] == 0.0)  # row 0: tau = 0, one key, logit 0
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_temp_bwd_matches_autograd(oracle_mod, rope):
+    B, M, Hq, Hkv, D = 2, 12, 4, 2, 8
+    q, k, v, g, gamma, pos = _inputs(44, B, M, Hq, Hkv, D)
+    sigma = np.random.default_rng(45).normal(0.0, 1.0, Hq)
+    dout = np.random.default_rng(46).standard_normal((B, M, Hq, D))
+    p = pos if rope else None
+    got = oracle_mod.attn_bwd(q, k, v, g, gamma, dout, pos=p, theta=300.0, tau=0.9, sigma=sigma)
+    leaves = [T(a).requires_grad_() for a in (q, k, v, g, gamma, sigma)]
+    o = _sdpa_temp_ref(*leaves[:5], leaves[5], 0.9, torch.from_numpy(pos) if rope else None, 300.0)
+    (o * T(dout)).sum().backward()
+    assert len(got) == 6
+    for a, ref in zip(got, leaves):
+        np.testing.assert_allclose(a, ref.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_temp_bwd_finite_differences(oracle_mod):
+    B, M, Hq, Hkv, D = 1, 6, 2, 1, 4
+    q, k, v, g, gamma, pos = _inputs(47, B, M, Hq, Hkv, D)
+    sigma = np.array([0.4, -1.2])
+    dout = np.random.default_rng(48).standard_normal((B, M, Hq, D))
+    grads = oracle_mod.attn_bwd(q, k, v, g, gamma, dout, pos=pos, theta=60.0, sigma=sigma)
+
+    def loss(s):
+        o, _ = oracle_mod.attn_fwd(q, k, v, g, gamma, pos=pos, theta=60.0, sigma=s)
+        return float((o * dout).sum())
+
+    h = 1e-6
+    for j in range(Hq):
+        sp, sm = sigma.copy(), sigma.copy()
+        sp[j] += h
+        sm[j] -= h
+        fd = (loss(sp) - loss(sm)) / (2 * h)
+        assert abs(fd - grads[5][j]) < 1e-6 * max(1.0, abs(fd)), (j, fd, grads[5][j])
+    # dg under the temperature: sum_j g_j dg_j = 0 still holds (each row's softmax is shift-free)
+    np.testing.assert_allclose((g * grads[3]).sum(axis=1), 0.0, atol=1e-11)
