@@ -163,9 +163,11 @@ tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates,
  * Both attention calls require a workspace of at least this size, 256-byte
  * aligned: it holds the cos/sin table of the kept positions, the rotated keys,
  * the per-head bias gamma_h log2 g_j, the partial results and arrival
- * counters of the forward's split rows and, for the backward, the rotated
- * queries, the row statistics (-lse / c, D_i) and the per-head column sums
- * of dS.  Its contents are scratch: nothing is carried between calls. */
+ * counters of the forward's split rows, the temperature's row factors and,
+ * for the backward, the rotated queries, the row statistics (-lse / c, D_i),
+ * the per-head column sums of dL/dZ and the per-row temperatures and their
+ * gradient terms.  Its contents are scratch: nothing is carried between
+ * calls. */
 size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
                                     int64_t D, int bwd);
 
@@ -183,8 +185,17 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  * (x_i, x_{i+D/2}), angle pos * rope_theta^(-2i/D), computed in fp64); pos
  * NULL means no rotation.  A key with g_j = 0 gets weight 0; a row with no
  * visible key gets o = 0, lse = -inf.
+ * With sigma (non-NULL) the logits follow the operative rule of [DeepDive]
+ * section 3.2, Eq. 8, with the pruning-ratio temperature of Eq. 7:
+ *     S_ij = t_ih * Z_ij,  Z_ij = (q^_i . k^_j) / (sqrt(D) * tau) + gamma[h] ln g_j
+ *     t_ih = softplus(sigma[h]) * ln m_i / ln max(2, p_i)
+ * with m_i = i + 1 the keys row i sees after pruning and p_i = pos_i + 1 the
+ * positions it saw before (p_i = i + 1 when pos is NULL).  t is computed in
+ * fp32 and kept >= 1e-30 (t = 0 at row 0, whose only live key gets weight 1
+ * either way), so a sigma below about -69 behaves as that floor.
  *   q [B, M, Hq, D], k, v [B, M, Hkv, D], o [B, M, Hq, D] (dt)
  *   g [B, M] f32 > = 0, gamma [Hq] f32, pos [B, M] i32 or NULL
+ *   sigma [Hq] f32 or NULL (no temperature: t = 1)
  *   lse [B, Hq, M] f32 out or NULL (needed by the backward)
  * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q.k and
  * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
@@ -192,8 +203,8 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  */
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g,
                             const float *gamma, const int32_t *pos, float rope_theta,
-                            float tau, int64_t B, int64_t M, int64_t Hq, int64_t Hkv,
-                            int64_t D, tg_dtype dt, void *o, float *lse, void *ws,
+                            float tau, const float *sigma, int64_t B, int64_t M, int64_t Hq,
+                            int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse, void *ws,
                             size_t ws_bytes, void *stream);
 
 /*
@@ -207,16 +218,22 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
  *     dg_j = sum_h gamma_h colsum_h(j) / g_j      (0 where g_j = 0)
  *     dgamma_h = sum_b sum_j colsum_h(j) ln g_j,   colsum_h(j) = sum_i dS_ij
  * with c = 1 / (sqrt(D) tau).  D_i is formed from fp32 P and dP, not from
- * the rounded output.  Outputs are fp32 and fully overwritten:
- *   dq [B, M, Hq, D], dk, dv [B, M, Hkv, D], dg [B, M], dgamma [Hq].
+ * the rounded output.  With sigma (the temperature of Eq. 7/8, as in the
+ * forward) dS_ij is dL/dS of S = t Z, dL/dZ_ij = t_ih dS_ij takes its place in
+ * dq, dk and colsum, and
+ *     dsigma_h = sigmoid(sigma_h) sum_b sum_i (ln m_i / ln max(2, p_i)) sum_j dS_ij Z_ij
+ * (sigma and dsigma both given or both NULL).  Outputs are fp32 and fully
+ * overwritten:
+ *   dq [B, M, Hq, D], dk, dv [B, M, Hkv, D], dg [B, M], dgamma [Hq], dsigma [Hq].
  * Deterministic: repeated calls give bitwise-identical results.
  */
 tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g,
                             const float *gamma, const int32_t *pos, float rope_theta,
-                            float tau, const float *lse, const void *dout, int64_t B,
-                            int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
-                            float *dq, float *dk, float *dv, float *dg, float *dgamma,
-                            void *ws, size_t ws_bytes, void *stream);
+                            float tau, const float *sigma, const float *lse, const void *dout,
+                            int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
+                            tg_dtype dt, float *dq, float *dk, float *dv, float *dg,
+                            float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
+                            void *stream);
 
 #ifdef __cplusplus
 }

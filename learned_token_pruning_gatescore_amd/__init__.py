@@ -14,8 +14,9 @@ Memory-Efficient LLM Prefill", sections 3.1-3.4):
                      rewritten once in matrix-core fragment order)
   tg_select_topk     top-K prunable tokens plus every forced token, ascending
   tg_compact         gather of kept hidden states, positions and gates
-  tg_gated_attn_fwd  causal attention with the per-key bias gamma_h * ln g_j
-  tg_gated_attn_bwd  its gradients (dq, dk, dv, dg, dgamma)
+  tg_gated_attn_fwd  causal attention with the per-key bias gamma_h * ln g_j and,
+                     optionally, the pruning-ratio temperature (section 3.2, Eq. 7/8)
+  tg_gated_attn_bwd  its gradients (dq, dk, dv, dg, dgamma, and dsigma)
 """
 from __future__ import annotations
 
@@ -83,10 +84,11 @@ def load():
     lib.tg_gated_attn_workspace_size.restype = sz
     lib.tg_gated_attn_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     lib.tg_gated_attn_fwd.restype = c_int
-    lib.tg_gated_attn_fwd.argtypes = [P, P, P, P, P, P, f32, f32, i64, i64, i64, i64, i64, c_int, P, P, P, sz, P]
+    lib.tg_gated_attn_fwd.argtypes = [P, P, P, P, P, P, f32, f32, P, i64, i64, i64, i64, i64, c_int, P, P, P, sz,
+                                      P]
     lib.tg_gated_attn_bwd.restype = c_int
-    lib.tg_gated_attn_bwd.argtypes = [P, P, P, P, P, P, f32, f32, P, P, i64, i64, i64, i64, i64, c_int,
-                                      P, P, P, P, P, P, sz, P]
+    lib.tg_gated_attn_bwd.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, i64, i64, i64, i64, i64, c_int,
+                                      P, P, P, P, P, P, P, sz, P]
     _lib = lib
     return lib
 
@@ -208,28 +210,31 @@ def attn_workspace(B, M, Hq, Hkv, D, bwd, device):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def tg_gated_attn_fwd(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None):
+def tg_gated_attn_fwd(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None, *, sigma=None):
     """q [B, M, Hq, D], k, v [B, M, Hkv, D] (bf16 or fp32); g f32 [B, M]; gamma f32 [Hq];
-    pos i32 [B, M] or None; writes o [B, M, Hq, D] and lse f32 [B, Hq, M]."""
-    _contig(q, k, v, g, gamma, pos, o, lse, ws)
+    pos i32 [B, M] or None; sigma f32 [Hq] or None (the pruning-ratio temperature);
+    writes o [B, M, Hq, D] and lse f32 [B, Hq, M]."""
+    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma)
     B, M, Hq, D = q.shape
     Hkv = k.shape[2]
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos), float(rope_theta),
-                                    float(tau), B, M, Hq, Hkv, D, _dt(q), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
-                                    _stream(stream)))
+                                    float(tau), _ptr(sigma), B, M, Hq, Hkv, D, _dt(q), _ptr(o), _ptr(lse), _ptr(ws),
+                                    ws_bytes, _stream(stream)))
 
 
 def tg_gated_attn_bwd(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk, dv, dg, dgamma, ws,
-                      stream=None):
-    """Gradients of tg_gated_attn_fwd; dq, dk, dv, dg, dgamma are f32 outputs, fully overwritten."""
-    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws)
+                      stream=None, *, sigma=None, dsigma=None):
+    """Gradients of tg_gated_attn_fwd; dq, dk, dv, dg, dgamma (and dsigma f32 [Hq], given with
+    sigma) are f32 outputs, fully overwritten."""
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma)
     B, M, Hq, D = q.shape
     Hkv = k.shape[2]
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos), float(rope_theta),
-                                    float(tau), _ptr(lse), _ptr(dout), B, M, Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk),
-                                    _ptr(dv), _ptr(dg), _ptr(dgamma), _ptr(ws), ws_bytes, _stream(stream)))
+                                    float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), B, M, Hq, Hkv, D, _dt(q),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgamma), _ptr(dsigma), _ptr(ws),
+                                    ws_bytes, _stream(stream)))
 
 
 def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma, tau, rope_theta=1.0e6,

@@ -230,12 +230,13 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
 }
 
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                            const int32_t *pos, float rope_theta, float tau, int64_t B, int64_t M, int64_t Hq,
-                            int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse, void *ws, size_t ws_bytes,
-                            void *stream) {
+                            const int32_t *pos, float rope_theta, float tau, const float *sigma, int64_t B,
+                            int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse,
+                            void *ws, size_t ws_bytes, void *stream) {
   tg_status st = check_attn(q, k, v, g, gamma, tau, B, M, Hq, Hkv, D, dt);
   if (st != TG_OK) return st;
   REQUIRE(o, TG_ERR_INVALID_ARG, "o is required");
+  REQUIRE(!sigma || aligned16(sigma), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   REQUIRE(aligned16(o) && aligned16(lse), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
   const size_t need = tg::attn_workspace_bytes(B, M, Hq, Hkv, D, false);
@@ -243,20 +244,23 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (B * M == 0) return ok();
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
-  return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, (int)B, (int)M, (int)Hq,
-                                        (int)Hkv, (int)D, dt == TG_BF16, o, lse, w, (hipStream_t)stream),
+  return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, (int)B, (int)M,
+                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, o, lse, w, (hipStream_t)stream),
                     "tg_gated_attn_fwd launch");
 }
 
 tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                            const int32_t *pos, float rope_theta, float tau, const float *lse, const void *dout,
-                            int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq,
-                            float *dk, float *dv, float *dg, float *dgamma, void *ws, size_t ws_bytes,
-                            void *stream) {
+                            const int32_t *pos, float rope_theta, float tau, const float *sigma, const float *lse,
+                            const void *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
+                            float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
+                            size_t ws_bytes, void *stream) {
   tg_status st = check_attn(q, k, v, g, gamma, tau, B, M, Hq, Hkv, D, dt);
   if (st != TG_OK) return st;
   REQUIRE(lse && dout && dq && dk && dv && dg && dgamma, TG_ERR_INVALID_ARG,
           "lse, dout, dq, dk, dv, dg and dgamma are required");
+  REQUIRE(!sigma == !dsigma, TG_ERR_INVALID_ARG, "sigma and dsigma go together");
+  REQUIRE(!sigma || (aligned16(sigma) && aligned16(dsigma)), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(aligned16(lse) && aligned16(dout) && aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(dg) &&
               aligned16(dgamma),
           TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
@@ -265,9 +269,9 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
-  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, lse, dout, (int)B, (int)M,
-                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, dq, dk, dv, dg, dgamma, w,
-                                        (hipStream_t)stream),
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, (int)B,
+                                        (int)M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, dq, dk, dv, dg, dgamma,
+                                        dsigma, w, (hipStream_t)stream),
                     "tg_gated_attn_bwd launch");
 }
 

@@ -47,12 +47,14 @@ namespace tg {
 // work-group takes query block nqb-1-p and then block p, so every work-group
 // sees about the same number of key tiles.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, const float2 *__restrict__ cs, const float *__restrict__ lse,
-    const uint16_t *__restrict__ dout, float c, float c2, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb,
-    float *__restrict__ dq, uint16_t *__restrict__ qhat, float2 *__restrict__ rowstat) {
+    const uint16_t *__restrict__ dout, float c, float c2, const float *__restrict__ sigma,
+    const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb,
+    float *__restrict__ dq, uint16_t *__restrict__ qhat, float2 *__restrict__ rowstat, float *__restrict__ tau,
+    float *__restrict__ tstat) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
@@ -120,6 +122,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     issue(0, nt);
     issue(1, nt);
 
+    // temperature of the column (1 without it, and past M): logits t Z, with
+    // t >= 1e-30 so that a key with bias -inf stays at -inf
+    float tq = 1.f, rq = 0.f;
+    if (TEMP && vq) {
+      rq = ratio[bM + qi];
+      tq = fmaxf(softplus_f(sigma[h]) * rq, 1e-30f);
+    }
+
     // Q and dO fragments (MFMA B operands): lane holds [qi, h, 16 ks + 8 hl .. +8]
     u32x4 qf[NKS], of[NKS];
     const int64_t roff = ((bM + (vq ? qi : 0)) * Hq + h) * D;
@@ -148,9 +158,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
         for (int ks = 0; ks < NKS; ++ks) *(u32x4 *)(qhat + roff + 16 * ks + 8 * hl) = qf[ks];
       }
     }
-    // exponent of P in log2 units: (S + la) c2 + bias with la = -lse / c
+    // exponent of P in log2 units: t ((S + la) c2 + bias) with la = -lse / (c t)
     // (dead rows and columns past M: -1e30, P = 0)
-    const float la = lrow == -INFINITY ? -1e30f : -lrow / c;
+    const float la = lrow == -INFINITY ? -1e30f : -lrow / (TEMP ? c * tq : c);
     const u32x4 laug = aug3(la, hl);
 
     // S^T and dP^T products over the head dim, fragments read two steps ahead
@@ -205,6 +215,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * j + e;
           float x = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+          if (TEMP) x *= tq;
           if (masked && acc_row(r, hl) > lim) x = -INFINITY;
           dsa[r & 3] = __builtin_fmaf(fast_exp2(x), dp[r], dsa[r & 3]);
         }
@@ -237,7 +248,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-    // dS of tile t as the B operand of the dQ^T product: step hf, slot e = register 8 hf + e
+    // dS of tile t as the B operand of the dQ^T product: step hf, slot e = register 8 hf + e.
+    // With the temperature, dt = sum_j dS_ij Z_ij: Z_ij is y / log2(e) plus a
+    // per-row constant (the exponent's shift), and sum_j dS_ij = 0, so the
+    // shifted y = (S + la) c2 + bias serves (-inf clamped: there dS = 0).
+    float dty[4] = {0.f, 0.f, 0.f, 0.f};
     auto valu_b = [&](int t, const f32x16 &s, const f32x16 &dp, bool masked, u32x4(&dsf)[2]) __attribute__((always_inline)) {
       const float *bi = &sBias[slot(t)][hloc][4 * hl];
       const int lim = qi - t * AB_T;
@@ -248,9 +263,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * j + e;
-          float x = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+          const float y = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+          float x = TEMP ? y * tq : y;
           if (masked && acc_row(r, hl) > lim) x = -INFINITY;
           ds[r] = fast_exp2(x) * dp[r];
+          if (TEMP) dty[r & 3] = __builtin_fmaf(ds[r], fmaxf(y, -1e30f), dty[r & 3]);
         }
       }
 #pragma unroll
@@ -277,8 +294,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       }
     }
     sync_vm<0>();
+    if (TEMP) {  // the temperature for the key-outer kernel, and ratio_i dL/dt_ih
+      float dts = (dty[0] + dty[1]) + (dty[2] + dty[3]);
+      dts += __shfl_xor(dts, 32);
+      const int64_t Mp = (M + AB_T - 1) / AB_T * AB_T;
+      if (hl == 0 && qi < Mp) tau[((int64_t)b * Hq + h) * Mp + qi] = tq;
+      if (hl == 0 && vq) tstat[((int64_t)b * Hq + h) * M + qi] = rq * dts * kLn2;
+    }
 
-    // dq = c R(-phi) dq^ ; lane holds rows d = 32 db + acc_row(r, hl) of its column
+    // dq = c t R(-phi) dq^ ; lane holds rows d = 32 db + acc_row(r, hl) of its column
+    const float cq = TEMP ? c * tq : c;
     if (vq) {
       float *drow = dq + ((bM + qi) * Hq + h) * D;
 #pragma unroll
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
           const float cv[4] = {t0[0], t0[2], t1[0], t1[2]}, sv[4] = {t0[1], t0[3], t1[1], t1[3]};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x = acc[db][4 * g4 + e] * c, y = acc[db + NDB / 2][4 * g4 + e] * c;
+            const float x = acc[db][4 * g4 + e] * cq, y = acc[db + NDB / 2][4 * g4 + e] * cq;
             xo[e] = x * cv[e] + y * sv[e];
             yo[e] = y * cv[e] - x * sv[e];
           }
@@ -324,20 +349,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
 // Items live in a ring of 5 LDS slots (two in flight, three in use).  Each
 // work-group takes key block p and then block nkb-1-p.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
     const uint16_t *__restrict__ qh, const uint16_t *__restrict__ dout, const float2 *__restrict__ rowstat,
-    const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v, const float *__restrict__ bias,
-    const float2 *__restrict__ cs, float c, float c2, int B, int M, int Hq, int Hkv, int G, int nkb,
-    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
+    const float *__restrict__ tau, const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v,
+    const float *__restrict__ bias, const float2 *__restrict__ cs, float c, float c2, int B, int M, int Hq,
+    int Hkv, int G, int nkb, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / AB_NW;  // Q and dO direct loads per wave per item
-  constexpr int NVM = NIW + 1;            // + the row-statistics load
+  constexpr int NVM = NIW + 1 + TEMP;     // + the row-statistics load (+ the temperature load)
   constexpr int KB = 4 * AB_T;            // keys per block
   __shared__ __attribute__((aligned(1024))) uint16_t sQ[5 * T::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sO[5 * T::TILE];
   __shared__ __attribute__((aligned(1024))) float2 sRS[5][AB_T];
+  __shared__ __attribute__((aligned(256))) float sT[TEMP ? 5 : 1][64];  // [slot][row] t (rows 32..63: fill)
   __shared__ __attribute__((aligned(1024))) f32x4 sP[2][4][4][64];  // [item parity][wave][r / 4][lane]
   __shared__ __attribute__((aligned(1024))) float sCol[8][KB];
   __shared__ __attribute__((aligned(256))) float sDummy[64];
@@ -353,6 +379,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
   const uint32_t rsq = (uint32_t)(Hq * D * 2);  // bytes between consecutive queries of one head
   const uint32_t q_bytes = (uint32_t)(M - 1) * rsq + D * 2;
   const int ntq = (M + AB_T - 1) / AB_T;
+  const int64_t Mp = (int64_t)ntq * AB_T;  // row stride of the temperatures
 
   BFrag<D> fr;
   fr.init(lane);
@@ -408,6 +435,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
                  live ? dgo[n] + toff : 0x80000000u, 0u);
       dma_b32(rR, wave == 0 ? lds_addr(&sRS[it % 5][0]) : lds_addr(sDummy),
               live && wave == 0 ? (uint32_t)(tq * AB_T * 8 + 4 * lane) : 0x80000000u, 0u);
+      if (TEMP) {
+        const i32x4 rT = buffer_rsrc(tau + ((int64_t)b * Hq + h) * Mp, (uint32_t)Mp * 4u);
+        dma_b32(rT, wave == 1 ? lds_addr(&sT[it % 5][0]) : lds_addr(sDummy),
+                live && wave == 1 && lane < AB_T ? (uint32_t)(tq * AB_T * 4 + 4 * lane) : 0x80000000u, 0u);
+      }
     };
     issue(0);
     issue(1);
@@ -443,15 +475,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        // temperatures of the item's rows (lane rows acc_row(4 j .. 4 j + 3, hl))
+        f32x4 tv[4];
+        if (TEMP) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tv[j] = *(const f32x4 *)&sT[TEMP ? it % 5 : 0][8 * j + 4 * hl];
+        }
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = __builtin_fmaf(s[r], c2, blane);
+          if (TEMP) x *= tv[r >> 2][r & 3];
           if (masked && key > i0 + acc_row(r, hl)) x = -INFINITY;
           p[r] = fast_exp2(x);
         }
+        // the partner's dS takes t P (dL/dZ = t dL/dS)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sP[it & 1][sub][j][lane] = f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+        for (int j = 0; j < 4; ++j) {
+          f32x4 pj = f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+          if (TEMP) pj *= tv[j];
+          sP[it & 1][sub][j][lane] = pj;
+        }
         u32x4 pf[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -611,8 +655,9 @@ __device__ __forceinline__ float logit_bias(float gam, float gv) { return gv > 0
 __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs,
-    const float *__restrict__ lse, const float *__restrict__ dout, float c, int B, int M, int Hq, int Hkv, int D,
-    float *__restrict__ dq, float *__restrict__ delta) {
+    const float *__restrict__ lse, const float *__restrict__ dout, float c, const float *__restrict__ sigma,
+    const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D, float *__restrict__ dq,
+    float *__restrict__ delta, float *__restrict__ tstat) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (int64_t)B * M * Hq) return;
@@ -634,6 +679,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
   }
   const float gam = gamma[h];
   const float l = lse[(b * Hq + h) * M + i];
+  const float t = sigma ? fmaxf(softplus_f(sigma[h]) * ratio[bi], 1e-30f) : 1.f;  // logits t Z
   float Di = 0.f;
   if (l != -INFINITY) {
     for (int j = 0; j <= i; ++j) {
@@ -646,12 +692,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
         vx = v[kr + lane];
         vy = v[kr + half + lane];
       }
-      const float sj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, g[bM + j]);
-      const float p = sj == -INFINITY ? 0.f : expf(sj - l);
+      const float zj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, g[bM + j]);
+      const float p = zj == -INFINITY ? 0.f : expf(t * zj - l);
       Di += p * wave_sum(ox * vx + oy * vy);
     }
   }
-  float ax = 0.f, ay = 0.f;
+  float ax = 0.f, ay = 0.f, dt = 0.f;
   if (l != -INFINITY) {
     for (int j = 0; j <= i; ++j) {
       const int64_t kr = ((bM + j) * Hkv + kv) * D;
@@ -663,29 +709,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
         vx = v[kr + lane];
         vy = v[kr + half + lane];
       }
-      const float sj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, g[bM + j]);
-      const float p = sj == -INFINITY ? 0.f : expf(sj - l);
+      const float zj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, g[bM + j]);
+      if (zj == -INFINITY) continue;
+      const float p = expf(t * zj - l);
       const float ds = p * (wave_sum(ox * vx + oy * vy) - Di);
+      dt += ds * zj;
       ax += ds * kx;
       ay += ds * ky;
     }
   }
-  ax *= c;
-  ay *= c;
+  ax *= c * t;
+  ay *= c * t;
   if (act) {
     rot(ax, ay, cs, bi * half + lane, -1.f);
     dq[row * D + lane] = ax;
     dq[row * D + half + lane] = ay;
   }
   if (lane == 0) delta[(b * Hq + h) * M + i] = Di;
+  if (sigma && lane == 0) tstat[(b * Hq + h) * M + i] = ratio[bi] * dt;
 }
 
 // one wave per (b, j, kv head): dk, dv, colsum of every head of the group
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs,
-    const float *__restrict__ lse, const float *__restrict__ dout, const float *__restrict__ delta, float c, int B,
-    int M, int Hq, int Hkv, int D, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
+    const float *__restrict__ lse, const float *__restrict__ dout, const float *__restrict__ delta, float c,
+    const float *__restrict__ sigma, const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D,
+    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, j, kv)
   if (row >= (int64_t)B * M * Hkv) return;
@@ -710,6 +760,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
   for (int hh = 0; hh < G; ++hh) {
     const int h = kv * G + hh;
     const float bias = logit_bias(gamma[h], gv);
+    const float sp = sigma ? softplus_f(sigma[h]) : 1.f;
     float cs_h = 0.f;
     if (bias != -INFINITY) {
       for (int i = j; i < M; ++i) {
@@ -724,8 +775,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
           ox = dout[qr + lane];
           oy = dout[qr + half + lane];
         }
-        const float p = expf(wave_sum(qx * kx + qy * ky) * c + bias - l);
-        const float ds = p * (wave_sum(ox * vx + oy * vy) - delta[(b * Hq + h) * M + i]);
+        const float t = sigma ? fmaxf(sp * ratio[bM + i], 1e-30f) : 1.f;
+        const float p = expf(t * (wave_sum(qx * kx + qy * ky) * c + bias) - l);
+        const float ds = t * p * (wave_sum(ox * vx + oy * vy) - delta[(b * Hq + h) * M + i]);  // dL/dZ
         cs_h += ds;
         akx += ds * qx;
         aky += ds * qy;
@@ -795,13 +847,33 @@ __global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ p
   if (threadIdx.x == 0) dgamma[h] = red[0];
 }
 
+// dsigma_h = sigmoid(sigma_h) sum_{b,i} ratio_i dL/dt_ih (softplus' = sigmoid),
+// one work-group per head, fixed-shape tree
+__global__ __launch_bounds__(256) void dsigma_kernel(const float *__restrict__ tstat, const float *__restrict__ sigma,
+                                                     int B, int M, int Hq, float *__restrict__ dsigma) {
+  __shared__ float red[256];
+  const int h = blockIdx.x;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float *row = tstat + ((int64_t)b * Hq + h) * M;
+    for (int i = threadIdx.x; i < M; i += 256) acc += row[i];
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsigma[h] = red[0] / (1.f + expf(-sigma[h]));
+}
+
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const int32_t *pos, double theta, float tau, const float *lse, const void *dout, int B,
-                           int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg,
-                           float *dgamma, const AttnWs &w, hipStream_t s) {
+                           const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
+                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk,
+                           float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w, hipStream_t s) {
   const float2 *cs = pos ? w.cs : nullptr;
-  if ((int64_t)B * M > 0 && (pos || bf16)) {
-    hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, w, s);
+  if ((int64_t)B * M > 0 && (pos || bf16 || sigma)) {
+    hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, w, s);
     if (e != hipSuccess) return e;
   }
   const double cd = 1.0 / (sqrt((double)D) * (double)tau);
@@ -815,30 +887,25 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
       const dim3 g1((unsigned)((nqb + 1) / 2 * B * Hkv)), g2((unsigned)((nkb + 1) / 2 * B * Hkv));
       const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
       const uint16_t *qh = pos ? w.qhat : (const uint16_t *)q;
-      if (D == 128) {
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, g1, dim3(512), 0, s, (const uint16_t *)q, kh,
-                           (const uint16_t *)v, w.bias, cs, lse, (const uint16_t *)dout, c, c2, B, M, Hq, Hkv, G,
-                           BQ, nqb, dq, w.qhat, w.rowstat);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, g2, dim3(512), 0, s, qh, (const uint16_t *)dout,
-                           w.rowstat, kh, (const uint16_t *)v, w.bias, cs, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv,
-                           w.colsum);
-      } else {
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, g1, dim3(512), 0, s, (const uint16_t *)q, kh,
-                           (const uint16_t *)v, w.bias, cs, lse, (const uint16_t *)dout, c, c2, B, M, Hq, Hkv, G,
-                           BQ, nqb, dq, w.qhat, w.rowstat);
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, g2, dim3(512), 0, s, qh, (const uint16_t *)dout,
-                           w.rowstat, kh, (const uint16_t *)v, w.bias, cs, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv,
-                           w.colsum);
-      }
+      const bool t = sigma != nullptr;
+      auto k1 = D == 128 ? (t ? attn_bwd_dq_bf16_kernel<128, true> : attn_bwd_dq_bf16_kernel<128, false>)
+                         : (t ? attn_bwd_dq_bf16_kernel<64, true> : attn_bwd_dq_bf16_kernel<64, false>);
+      auto k2 = D == 128 ? (t ? attn_bwd_dkdv_bf16_kernel<128, true> : attn_bwd_dkdv_bf16_kernel<128, false>)
+                         : (t ? attn_bwd_dkdv_bf16_kernel<64, true> : attn_bwd_dkdv_bf16_kernel<64, false>);
+      hipLaunchKernelGGL(k1, g1, dim3(512), 0, s, (const uint16_t *)q, kh, (const uint16_t *)v, w.bias, cs, lse,
+                         (const uint16_t *)dout, c, c2, sigma, w.ratio, B, M, Hq, Hkv, G, BQ, nqb, dq, w.qhat,
+                         w.rowstat, w.tau, w.tstat);
+      hipLaunchKernelGGL(k2, g2, dim3(512), 0, s, qh, (const uint16_t *)dout, w.rowstat, (const float *)w.tau, kh,
+                         (const uint16_t *)v, w.bias, cs, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv, w.colsum);
     } else {
       float *delta = (float *)w.rowstat;
       const int64_t rq = (int64_t)B * M * Hq, rk = (int64_t)B * M * Hkv;
       hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, dim3((unsigned)((rq + 3) / 4)), dim3(256), 0, s,
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, c, B, M, Hq, Hkv, D, dq, delta);
+                         (const float *)dout, c, sigma, w.ratio, B, M, Hq, Hkv, D, dq, delta, w.tstat);
       hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, dim3((unsigned)((rk + 3) / 4)), dim3(256), 0, s,
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, delta, c, B, M, Hq, Hkv, D, dk, dv, w.colsum);
+                         (const float *)dout, delta, c, sigma, w.ratio, B, M, Hq, Hkv, D, dk, dv, w.colsum);
     }
     // the row statistics are dead by now: their space takes the dgamma shares
     hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)(B < 65535 ? B : 65535)), dim3(256), 0,
@@ -846,6 +913,9 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
   }
   hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, (const float *)w.rowstat,
                      (int)((int64_t)B * ((M + 255) / 256)), Hq, dgamma);
+  if (sigma)
+    hipLaunchKernelGGL(dsigma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, (const float *)w.tstat, sigma, B, M, Hq,
+                       dsigma);
   return hipGetLastError();
 }
 

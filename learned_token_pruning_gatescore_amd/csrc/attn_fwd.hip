@@ -38,7 +38,10 @@ namespace tg {
 //                   on the host in fp64), stored as fp32;
 //   khat[row]     = k[row] rotated (bf16, every kv head), when khat != nullptr;
 //   bias[b][h][j] = gamma_h * log2 g_j (-inf where g_j <= 0), the per-key,
-//                   per-head logit bias in log2 units, when bias != nullptr.
+//                   per-head logit bias in log2 units, when bias != nullptr;
+//   ratio[row]    = ln m_i / ln max(2, p_i), the row factor of the attention
+//                   temperature (m_i = i + 1, p_i = pos + 1, or i + 1 without
+//                   positions), when ratio != nullptr.
 // Rotating K once here replaces a rotation per query block in the main loop.
 struct InvFreq {
   double v[64];
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
                                                         const int32_t *__restrict__ pos, InvFreq inv, int64_t rows,
                                                         int M, int Hq, int Hkv, int D, float2 *__restrict__ cs,
                                                         uint16_t *__restrict__ khat, float *__restrict__ bias,
-                                                        int *__restrict__ cnt, int ncnt) {
+                                                        float *__restrict__ ratio, int *__restrict__ cnt, int ncnt) {
   __shared__ float2 scs[256];
   const int half = D / 2, R = 256 / half;  // R rows per work-group, one thread per (row, rotary pair)
   const int t = threadIdx.x;
@@ -94,6 +97,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
     const int b = (int)r / M, j = (int)r - b * M;  // B * M < 2^31
     for (int h = i; h < Hq; h += half) bias[(b * Hq + h) * M + j] = gv > 0.f ? gamma[h] * lg : -INFINITY;
   }
+  if (ratio && vr && i == 0) {  // the temperature's row factor ln m_i / ln max(2, p_i) (fp64 logs)
+    const int b = (int)r / M, j = (int)r - b * M;
+    const double m = (double)j + 1.0, pp = pos ? (double)pos[r] + 1.0 : m;
+    ratio[r] = (float)(log(m) / log(pp > 2.0 ? pp : 2.0));
+  }
 }
 
 
@@ -136,12 +144,12 @@ __host__ __device__ inline int fwd_ntiles(int qb, int BQ, int M) {
 }
 __host__ __device__ inline int fwd_npieces(int n, int C) { return (n + C - 1) / C; }
 
-template <int D>
+template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
-    const float *__restrict__ bias, const float2 *__restrict__ cs, float c2, int B, int M, int Hq, int Hkv, int G,
-    int BQ, int nqb, int C, float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o,
-    float *__restrict__ lse) {
+    const float *__restrict__ bias, const float2 *__restrict__ cs, float c2, const float *__restrict__ sigma,
+    const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb, int C,
+    float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o, float *__restrict__ lse) {
   using T = BTile<D>;
   using F = FwdCfg<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
@@ -273,11 +281,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     }
   }
 
+  // Temperature of the column's row (1 without it): x = t (c2 s + bias).  t is
+  // kept >= 1e-30 so that a key with bias -inf stays at -inf (t = 0 at the
+  // first row, where every live logit is 0 either way).
+  float tq = 1.f;
+  if (TEMP && vq) tq = fmaxf(softplus_f(sigma[kvh * G + hloc]) * ratio[bM + qi], 1e-30f);
   // m2: reference maximum of the column (probabilities are 2^(x - m2)); the
-  // S^T products subtract m2 / c2 themselves through the extra step qaug.
+  // S^T products subtract m2 / (t c2) themselves through the extra step qaug.
   float m2 = 0.f, lsum = 0.f;
   u32x4 qaug = u32x4{0u, 0u, 0u, 0u};
-  const float inv_c2 = 1.f / c2;
+  const float inv_c2 = TEMP ? 1.f / (c2 * tq) : 1.f / c2;
   f32x16 acc[NDB];
 
   // S^T = K Q^T over the head dim, fragments read two steps ahead
@@ -324,6 +337,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * j + e;
         x[r] = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
+        if (TEMP) x[r] *= tq;
         if (masked && acc_row(r, hl) > lim) x[r] = -INFINITY;
       }
     }
@@ -452,7 +466,8 @@ __device__ __forceinline__ float bias_of(float gam, float gv) {
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs, float c,
-    int B, int M, int Hq, int Hkv, int D, float *__restrict__ o, float *__restrict__ lse) {
+    const float *__restrict__ sigma, const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D,
+    float *__restrict__ o, float *__restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, i, h) flattened
   if (row >= (int64_t)B * M * Hq) return;
@@ -462,6 +477,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
   const int64_t bM = bi - i;
   const int kv = h / (Hq / Hkv);
   const int half = D / 2;
+  const float t = sigma ? fmaxf(softplus_f(sigma[h]) * ratio[bi], 1e-30f) : 1.f;
   const bool act = lane < half;
   float qx = 0.f, qy = 0.f;
   if (act) {
@@ -489,7 +505,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
         ky = y;
       }
     }
-    const float sj = wave_sum(qx * kx + qy * ky) * c + bias_of(gam, g[bM + j]);
+    const float sj = t * (wave_sum(qx * kx + qy * ky) * c + bias_of(gam, g[bM + j]));
     if (sj == -INFINITY) continue;
     const float mn = fmaxf(m, sj);
     const float al = expf(m - mn), p = expf(sj - mn);
@@ -556,7 +572,9 @@ FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
 // Workspace of the attention calls (256-byte aligned regions):
 //   cs [B*M*D/2] float2 | khat [B*M*Hkv*D] bf16 | bias [B*Hq*M] f32 |
 //   part [nmulti*B*Hkv * 4 waves * NR * 64] f32 | cnt [B*Hkv*nqb] i32 |
-//   (backward) qhat [B*M*Hq*D] bf16 | rowstat [B*Hq*M] float2 | colsum [B*Hq*M] f32
+//   ratio [B*M] f32 |
+//   (backward) qhat [B*M*Hq*D] bf16 | rowstat [B*Hq*M] float2 | colsum [B*Hq*M] f32 |
+//   tau [B*Hq*Mp] f32 (Mp = M rounded up to 32) | tstat [B*Hq*M] f32
 static size_t rup(size_t x) { return (x + 255) / 256 * 256; }
 
 static size_t part_floats(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
@@ -572,10 +590,10 @@ static size_t cnt_ints(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
   size_t n = rup((size_t)(B * M * (D / 2)) * sizeof(float2)) + rup((size_t)(B * M * Hkv * D) * 2) +
              rup((size_t)(B * Hq * M) * sizeof(float)) + rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float)) +
-             rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int));
+             rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int)) + rup((size_t)(B * M) * sizeof(float));
   if (bwd)
     n += rup((size_t)(B * M * Hq * D) * 2) + rup((size_t)(B * Hq * M) * sizeof(float2)) +
-         rup((size_t)(B * Hq * M) * sizeof(float));
+         2 * rup((size_t)(B * Hq * M) * sizeof(float)) + rup((size_t)(B * Hq * ((M + 31) / 32 * 32)) * sizeof(float));
   return n;
 }
 
@@ -593,17 +611,23 @@ AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, in
   w.cnt = (int *)p;
   w.ncnt = (int)cnt_ints(B, M, Hq, Hkv);
   p += rup((size_t)w.ncnt * sizeof(int));
+  w.ratio = (float *)p;
+  p += rup((size_t)(B * M) * sizeof(float));
   w.qhat = (uint16_t *)p;
   p += rup((size_t)(B * M * Hq * D) * 2);
   w.rowstat = (float2 *)p;
   p += rup((size_t)(B * Hq * M) * sizeof(float2));
   w.colsum = (float *)p;
+  p += rup((size_t)(B * Hq * M) * sizeof(float));
+  w.tau = (float *)p;
+  p += rup((size_t)(B * Hq * ((M + 31) / 32 * 32)) * sizeof(float));
+  w.tstat = (float *)p;
   return w;
 }
 
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
-                            int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, const AttnWs &w,
-                            hipStream_t s) {
+                            int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
+                            const AttnWs &w, hipStream_t s) {
   if ((int64_t)B * M == 0) return hipSuccess;
   InvFreq inv;
   for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
@@ -611,15 +635,16 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
   const int64_t R = 256 / (D / 2), nwg_rows = (rows + R - 1) / R, nwg_cnt = ((int64_t)w.ncnt + 255) / 256;
   hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0, s,
                      (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
-                     (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, w.cnt, with_bias ? w.ncnt : 0);
+                     (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, with_ratio ? w.ratio : nullptr,
+                     w.cnt, with_bias ? w.ncnt : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const int32_t *pos, double theta, float tau, int B, int M, int Hq, int Hkv, int D,
-                           bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s) {
+                           const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
+                           int Hkv, int D, bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s) {
   if ((int64_t)B * M == 0) return hipSuccess;
-  hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, w, s);
+  hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, w, s);
   if (e != hipSuccess) return e;
   const float2 *cs = pos ? w.cs : nullptr;
   const double c = 1.0 / (sqrt((double)D) * (double)tau);
@@ -628,19 +653,15 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const dim3 grid((unsigned)(f.npieces * B * Hkv));
     const float c2 = (float)(c * 1.4426950408889634);
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
-    if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(512), 0, s, (const uint16_t *)q, kh,
-                         (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part,
-                         w.cnt, (uint16_t *)o, lse);
-    else
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(512), 0, s, (const uint16_t *)q, kh,
-                         (const uint16_t *)v, w.bias, cs, c2, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part,
-                         w.cnt, (uint16_t *)o, lse);
+    auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>)
+                         : (sigma ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(512), 0, s, (const uint16_t *)q, kh, (const uint16_t *)v, w.bias, cs, c2,
+                       sigma, w.ratio, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part, w.cnt, (uint16_t *)o, lse);
   } else {
     const int64_t rows = (int64_t)B * M * Hq;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const float *)q,
-                       (const float *)k, (const float *)v, g, gamma, cs, (float)c, B, M, Hq, Hkv, D, (float *)o,
-                       lse);
+                       (const float *)k, (const float *)v, g, gamma, cs, (float)c, sigma, w.ratio, B, M, Hq, Hkv,
+                       D, (float *)o, lse);
   }
   return hipGetLastError();
 }

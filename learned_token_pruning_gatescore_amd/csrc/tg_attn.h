@@ -13,9 +13,13 @@ struct AttnWs {
   float *part;       // partial (O, max, sum) records of the forward's split query blocks
   int *cnt;          // [B*Hkv, nqb] arrival counters of the split query blocks
   int ncnt;
+  float *ratio;      // [B, M] ln m_i / ln max(2, p_i), the temperature's row factor
   uint16_t *qhat;    // [B, M, Hq, D] rotated queries (bf16) of the backward
   float2 *rowstat;   // [B, Hq, M] (-lse / c, D_i) of the backward (fp32 path: D_i alone)
   float *colsum;     // [B, Hq, M] column sums of dS per head
+  float *tau;        // [B, Hq, Mp] temperature of each (row, head) of the backward, Mp = M rounded up
+                     // to 32 (1 past M)
+  float *tstat;      // [B, Hq, M] ratio_i * dL/dtau_ih, reduced into dsigma
 };
 
 // Split schedule of the bf16 forward (query block size, blocks, tiles per
@@ -28,14 +32,17 @@ FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv);
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd);
 AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
-                            int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, const AttnWs &w,
-                            hipStream_t s);
+                            int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
+                            const AttnWs &w, hipStream_t s);
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const int32_t *pos, double theta, float tau, int B, int M, int Hq, int Hkv, int D,
-                           bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s);
+                           const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
+                           int Hkv, int D, bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s);
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
-                           const int32_t *pos, double theta, float tau, const float *lse, const void *dout, int B,
-                           int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk, float *dv, float *dg,
-                           float *dgamma, const AttnWs &w, hipStream_t s);
+                           const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
+                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk,
+                           float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w, hipStream_t s);
+
+// softplus in fp32 (the temperature's positive scale)
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(__expf(x)); }
 
 }  // namespace tg

@@ -168,9 +168,11 @@ def attn_inputs(w: Workload, M: int, with_grad: bool = False, seed_offset: int =
     workload); gamma ~ U(0.5, 1.5) [Hq]; g = 1/(1+exp(-z)), z ~ N(0,1), float32
     [B, M] (a distribution of gate values in (0, 1)); positions int32 [B, M]:
     sorted distinct draws from [0, max(N, M)), the shape of the original positions
-    that compaction hands to attention; dout ~ N(0,1) like q when with_grad.
+    that compaction hands to attention; dout ~ N(0,1) like q when with_grad;
+    sigma [Hq] float32 ~ N(ln(e - 1), 0.5^2), the raw temperature parameter
+    (softplus(ln(e - 1)) = 1, the identity scale, plus a spread across heads).
     """
-    rs = _streams(w.seed * 7919 + 17 + seed_offset, ["q", "k", "v", "gamma", "g", "pos", "dout"])
+    rs = _streams(w.seed * 7919 + 17 + seed_offset, ["q", "k", "v", "gamma", "g", "pos", "dout", "sigma"])
     q = rs["q"].standard_normal((w.B, M, w.Hq, w.D), dtype=np.float32)
     k = rs["k"].standard_normal((w.B, M, w.Hkv, w.D), dtype=np.float32)
     v = rs["v"].standard_normal((w.B, M, w.Hkv, w.D), dtype=np.float32)
@@ -178,7 +180,9 @@ def attn_inputs(w: Workload, M: int, with_grad: bool = False, seed_offset: int =
     z = rs["g"].standard_normal((w.B, M)).astype(np.float64)
     g = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
     pos = np.stack([np.sort(rs["pos"].choice(max(w.N, M), M, replace=False)) for _ in range(w.B)]).astype(np.int32)
-    out = dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype), gamma=gamma, g=g, pos=pos)
+    sigma = (np.log(np.e - 1.0) + 0.5 * rs["sigma"].standard_normal(w.Hq)).astype(np.float32)
+    out = dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype), gamma=gamma, g=g, pos=pos,
+               sigma=sigma)
     if with_grad:
         out["dout"] = _store(rs["dout"].standard_normal((w.B, M, w.Hq, w.D), dtype=np.float32), w.dtype)
     return out

@@ -101,8 +101,8 @@ def test_attn_validation():
     lib = _lib()
     f = lib.tg_gated_attn_fwd
     args = lambda **kw: [kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("pos", None), 1e6, kw.get("tau", 1.0),
-                         1, 100, kw.get("Hq", 16), kw.get("Hkv", 8), kw.get("D", 128), kw.get("dt", 1), FAKE, None,
-                         kw.get("ws", None), kw.get("wsb", 0), None]
+                         kw.get("sigma", None), 1, 100, kw.get("Hq", 16), kw.get("Hkv", 8), kw.get("D", 128),
+                         kw.get("dt", 1), FAKE, None, kw.get("ws", None), kw.get("wsb", 0), None]
     assert f(*args(q=None)) == 1
     assert f(*args(Hq=12, Hkv=8)) == 1          # Hq % Hkv
     assert f(*args(D=96)) == 2                  # bf16 D
@@ -114,10 +114,13 @@ def test_attn_validation():
     assert need >= 100 * 64 * 8
     assert f(*args(pos=FAKE, ws=FAKE, wsb=need - 1)) == 3
     assert f(*args(q=MIS)) == 1
+    assert f(*args(sigma=MIS)) == 1             # misaligned sigma
     b = lib.tg_gated_attn_bwd
-    # missing lse
-    assert b(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, FAKE, 1, 100, 16, 8, 128, 1,
-             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
-    # workspace too small
-    assert b(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, FAKE, FAKE, 1, 100, 16, 8, 128, 1,
-             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    bargs = lambda **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, kw.get("sigma", None), kw.get("lse", FAKE),
+                          FAKE, 1, 100, 16, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("dsigma", None),
+                          FAKE, kw.get("wsb", 1 << 20), None]
+    assert b(*bargs(lse=None)) == 1              # missing lse
+    assert b(*bargs(wsb=16)) == 3                # workspace too small
+    assert b(*bargs(sigma=FAKE)) == 1            # sigma without dsigma
+    assert b(*bargs(dsigma=FAKE)) == 1           # dsigma without sigma
+    assert b(*bargs(sigma=FAKE, dsigma=MIS)) == 1

@@ -19,7 +19,7 @@ def _wl(B, M, Hq, Hkv, D, dtype="bf16", tau=1.0, seed=21):
                        tau=tau, dtype=dtype, rope=True, M_fixed=M)
 
 
-def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, seed_offset=0):
+def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, seed_offset=0, temp=False):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
@@ -31,21 +31,23 @@ def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, 
     g = torch.from_numpy(a["g"]).to(dev)
     gamma = torch.from_numpy(a["gamma"]).to(dev)
     pos = torch.from_numpy(a["pos"]).to(dev) if rope else None
+    sigma = torch.from_numpy(a["sigma"]).to(dev) if temp else None
     o = torch.full_like(q, float("nan"))
     lse = torch.full((w.B, w.Hq, M), float("nan"), device=dev)
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, True, dev)
-    say("attn_fwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "rope" if rope else "no-rope")
-    tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, theta, w.tau, o, lse, ws)
+    say("attn_fwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "rope" if rope else "no-rope", "temp" if temp else "")
+    tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, theta, w.tau, o, lse, ws, sigma=sigma)
     torch.cuda.synchronize()
-    out = dict(a=a, q=q, k=k, v=v, g=g, gamma=gamma, pos=pos, o=o, lse=lse, ws=ws, theta=theta)
+    out = dict(a=a, q=q, k=k, v=v, g=g, gamma=gamma, pos=pos, sigma=sigma, o=o, lse=lse, ws=ws, theta=theta)
     return out
 
 
 def _oracle_fwd(w, r, rows=None, rope=True):
     a = r["a"]
     f = lambda x: wl.as_float(x, w.dtype)
+    sig = None if r["sigma"] is None else a["sigma"]
     return oracle.attn_fwd(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], pos=a["pos"] if rope else None,
-                           theta=r["theta"], tau=w.tau, round_bf16=(w.dtype == "bf16"), rows=rows)
+                           theta=r["theta"], tau=w.tau, round_bf16=(w.dtype == "bf16"), rows=rows, sigma=sig)
 
 
 def _tol(w):
@@ -127,11 +129,11 @@ def test_fwd_deterministic():
     assert torch.equal(o1.view(torch.int16), r["o"].view(torch.int16))
 
 
-def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA):
+def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA, temp=False, g_override=None):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
-    r = _run_fwd(w, M, rope=rope, theta=theta, grad=True)
+    r = _run_fwd(w, M, rope=rope, theta=theta, grad=True, temp=temp, g_override=g_override)
     dev = r["q"].device
     dout = dev_tensor(r["a"]["dout"], w.dtype, dev)
     dq = torch.full(r["q"].shape, float("nan"), device=dev)
@@ -139,23 +141,27 @@ def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA):
     dv = torch.full(r["v"].shape, float("nan"), device=dev)
     dg = torch.full(r["g"].shape, float("nan"), device=dev)
     dgam = torch.full(r["gamma"].shape, float("nan"), device=dev)
-    say("attn_bwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D)
+    dsig = torch.full(r["gamma"].shape, float("nan"), device=dev) if temp else None
+    say("attn_bwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "temp" if temp else "")
     tg.tg_gated_attn_bwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], theta, w.tau, r["lse"], dout, dq, dk,
-                         dv, dg, dgam, r["ws"])
+                         dv, dg, dgam, r["ws"], sigma=r["sigma"], dsigma=dsig)
     torch.cuda.synchronize()
-    r.update(dout=dout, dq=dq, dk=dk, dv=dv, dg=dg, dgamma=dgam)
+    r.update(dout=dout, dq=dq, dk=dk, dv=dv, dg=dg, dgamma=dgam, dsigma=dsig)
     return r
 
 
 def _check_bwd(w, r, rope=True):
     a = r["a"]
     f = lambda x: wl.as_float(x, w.dtype)
+    temp = r["sigma"] is not None
     ref = oracle.attn_bwd(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], f(a["dout"]),
-                          pos=a["pos"] if rope else None, theta=r["theta"], tau=w.tau, round_bf16=(w.dtype == "bf16"))
+                          pos=a["pos"] if rope else None, theta=r["theta"], tau=w.tau, round_bf16=(w.dtype == "bf16"),
+                          sigma=a["sigma"] if temp else None)
     tol = _tol(w)
+    names = ("dq", "dk", "dv", "dg", "dgamma") + (("dsigma",) if temp else ())
     errs = {}
-    for name, got, rf in zip(("dq", "dk", "dv", "dg", "dgamma"), (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"]), ref):
-        errs[name] = assert_maxabs(to_np(got), rf, tol, name)
+    for name, rf in zip(names, ref):
+        errs[name] = assert_maxabs(to_np(r[name]), rf, tol, name)
     return errs
 
 
@@ -199,3 +205,106 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(first, (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"])):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# --- pruning-ratio temperature (deep dive section 3.2, Eq. 7/8): sigma per head ---
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,D,rope", [
+    (1, 1, 2, 1, 128, True), (1, 63, 4, 4, 64, False), (2, 100, 4, 2, 128, True), (1, 257, 8, 2, 128, True),
+    (2, 130, 16, 4, 64, True), (1, 333, 16, 16, 128, False)])
+def test_temp_fwd_bf16_shapes(B, M, Hq, Hkv, D, rope):
+    w = _wl(B, M, Hq, Hkv, D, tau=1.3)
+    r = _run_fwd(w, M, rope=rope, temp=True)
+    o_ref, l_ref = _oracle_fwd(w, r, rope=rope)
+    assert_maxabs(to_np(r["o"]), o_ref, 2e-2, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+@pytest.mark.parametrize("rope", [True, False])
+def test_temp_fwd_f32(rope):
+    w = _wl(2, 70, 6, 2, 32, dtype="f32", tau=0.9)
+    r = _run_fwd(w, 70, rope=rope, theta=1e4, temp=True)
+    o_ref, l_ref = _oracle_fwd(w, r, rope=rope)
+    assert_maxabs(to_np(r["o"]), o_ref, 1e-4, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 1e-4, "lse")
+
+
+def test_temp_fwd_zero_gate_rows():
+    w = _wl(1, 150, 4, 2, 128)
+    g = wl.attn_inputs(w, 150)["g"].copy()
+    g[0, 0] = 0.0
+    g[0, 70:80] = 0.0
+    r = _run_fwd(w, 150, g_override=g, temp=True)
+    o_ref, l_ref = _oracle_fwd(w, r)
+    o = to_np(r["o"])
+    assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(to_np(r["lse"])[0, :, 0]))
+    assert_maxabs(o, o_ref, 2e-2, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+def test_temp_fwd_full_size():
+    w = wl.WORKLOADS["qwen3_32k"]
+    M = w.M(2048)
+    r = _run_fwd(w, M, temp=True)
+    o_ref, l_ref = _oracle_fwd(w, r)
+    assert_maxabs(to_np(r["o"]), o_ref, 2e-2, "o")
+    assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+def test_temp_fwd_sweep_128k_sampled():
+    w = wl.WORKLOADS["sweep_128k"]
+    M = w.M(16384)
+    r = _run_fwd(w, M, temp=True)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, M - 1], rng.choice(M, 48, replace=False)]))
+    o_ref, l_ref = _oracle_fwd(w, r, rows=rows)
+    assert_maxabs(to_np(r["o"])[0, rows], o_ref[0, rows], 2e-2, "o")
+    assert_maxabs(to_np(r["lse"])[0][:, rows], l_ref[0][:, rows], 2e-2, "lse")
+
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,D,rope", [
+    (1, 1, 2, 1, 128, True), (2, 100, 4, 2, 128, True), (1, 257, 8, 2, 128, False), (1, 190, 4, 4, 64, True),
+    (1, 150, 8, 1, 128, True)])
+def test_temp_bwd_bf16_shapes(B, M, Hq, Hkv, D, rope):
+    w = _wl(B, M, Hq, Hkv, D, tau=1.1)
+    r = _run_bwd(w, M, rope=rope, temp=True)
+    _check_bwd(w, r, rope=rope)
+
+
+@pytest.mark.parametrize("rope", [True, False])
+def test_temp_bwd_f32(rope):
+    w = _wl(1, 80, 4, 2, 64, dtype="f32", tau=1.2)
+    r = _run_bwd(w, 80, rope=rope, theta=1e4, temp=True)
+    _check_bwd(w, r, rope=rope)
+
+
+def test_temp_bwd_zero_gate_rows():
+    w = _wl(1, 150, 4, 2, 128)
+    g = wl.attn_inputs(w, 150)["g"].copy()
+    g[0, 0] = 0.0
+    g[0, 70:80] = 0.0
+    r = _run_bwd(w, 150, temp=True, g_override=g)
+    _check_bwd(w, r)
+
+
+def test_temp_bwd_train_b4_full():
+    w = wl.WORKLOADS["train_b4"]
+    r = _run_bwd(w, 2048, temp=True)
+    errs = _check_bwd(w, r)
+    say("train_b4 temperature bwd max-abs errors", errs)
+
+
+def test_temp_bwd_deterministic():
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    w = _wl(2, 300, 16, 8, 128)
+    r = _run_bwd(w, 300, temp=True)
+    names = ("dq", "dk", "dv", "dg", "dgamma", "dsigma")
+    first = [r[n].clone() for n in names]
+    tg.tg_gated_attn_bwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], r["theta"], w.tau, r["lse"],
+                         r["dout"], r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"], r["ws"], sigma=r["sigma"],
+                         dsigma=r["dsigma"])
+    torch.cuda.synchronize()
+    for a, n in zip(first, names):
+        assert torch.equal(a.view(torch.int32), r[n].view(torch.int32)), n
