@@ -17,9 +17,11 @@ so each step reads its hidden states from HBM.  The value is whole-job
 throughput: context tokens per second.  Per-kernel durations come from HIP
 events recorded on the launch stream inside the timed region.
 
-Also measured in the same run (not part of `value`): the training-path
-attention (forward + backward at batch 4, 2048 kept tokens) and the CPU
-oracle on the same workload, timed on this host's cores.
+Also measured in the same run (not part of `value`): the attention with the
+pruning-ratio temperature (the deep dive's operative rule, section 3.2 Eq. 7/8)
+on the same inputs, the training-path attention (forward + backward at batch
+4, 2048 kept tokens) with and without that temperature, and the CPU oracle on
+the same workload, timed on this host's cores.
 """
 from __future__ import annotations
 
@@ -136,6 +138,15 @@ def run_gpu(args):
     step_dev = [e[0].elapsed_time(e[NEV - 1]) * 1e-3 for e in evs]
     log(f"timed {args.steps} steps: wall {wall * 1e3:.3f} ms, device path mean {np.mean(step_dev) * 1e6:.1f} us")
 
+    # the operative rule (per-row, per-head temperature) on the same inputs
+    sigma = torch.from_numpy(at["sigma"]).to(dev)
+
+    def attn_temp(i):
+        h, q, k, v = copies[i % NCOPY]
+        tg.tg_gated_attn_fwd(q, k, v, gk, gamma, pk, wl.ROPE_THETA, w.tau, o, lse, ws, sigma=sigma)
+
+    temp_us = time_loop(attn_temp, args.steps, stream) * 1e6
+
     work = algorithmic_work(w, M)
     kern = {}
     for n in names:
@@ -153,7 +164,9 @@ def run_gpu(args):
         gate_stage_bound_frac=(max(work["gate_score"]["flops"] / PEAK_BF16, work["gate_score"]["bytes"] / PEAK_HBM)
                                + (work["gate_pack_w1"]["bytes"] + work["select_topk"]["bytes"]
                                   + work["compact"]["bytes"]) / PEAK_HBM) / gate_stage,
-        attn_fwd_mfma_frac=kern["attn_fwd"]["mfma_frac"])
+        attn_fwd_mfma_frac=kern["attn_fwd"]["mfma_frac"],
+        attn_fwd_temperature_us=temp_us,
+        attn_fwd_temperature_mfma_frac=work["attn_fwd"]["flops"] / (temp_us * 1e-6) / PEAK_BF16)
     # dominant kernel of the step
     dom = max(names, key=lambda n: kern[n]["us"])
     if work[dom]["flops"]:
@@ -184,6 +197,22 @@ def run_gpu(args):
     return res
 
 
+def time_loop(fn, n, stream):
+    """Mean device time of fn(i) over n calls, from HIP events on `stream` (after 3 warm-up calls)."""
+    import torch
+
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+
 def run_train(args, tg, wl, dev):
     """Training-path attention: forward + backward at batch 4, 2048 kept tokens (not part of `value`)."""
     import torch
@@ -203,32 +232,43 @@ def run_train(args, tg, wl, dev):
     dv = torch.empty(v.shape, device=dev)
     dg = torch.empty(g.shape, device=dev)
     dgam = torch.empty(gamma.shape, device=dev)
+    sigma = torch.from_numpy(a["sigma"]).to(dev)
+    dsig = torch.empty(gamma.shape, device=dev)
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, True, dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, temp=False):
+        sg = dict(sigma=sigma) if temp else {}
         if ev:
             ev[0].record(stream)
-        tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws)
+        tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws, **sg)
         if ev:
             ev[1].record(stream)
-        tg.tg_gated_attn_bwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, dq, dk, dv, dg, dgam, ws)
+        if temp:
+            sg["dsigma"] = dsig
+        tg.tg_gated_attn_bwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, dq, dk, dv, dg, dgam, ws, **sg)
         if ev:
             ev[2].record(stream)
 
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.train_steps)]
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
     ff = 4.0 * w.B * w.Hq * w.D * M * (M + 1) / 2
-    return dict(workload=w.name, B=w.B, M=M, fwd_us=fwd * 1e6, bwd_us=bwd * 1e6,
-                fwd_mfma_frac=ff / fwd / PEAK_BF16, bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16,
-                tokens_per_s=w.B * M / (fwd + bwd))
+    out = dict(workload=w.name, B=w.B, M=M)
+    for temp in (False, True):
+        for _ in range(3):
+            step(temp=temp)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.train_steps)]
+        for e in evs:
+            step(e, temp=temp)
+        torch.cuda.synchronize()
+        fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+        bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+        r = dict(fwd_us=fwd * 1e6, bwd_us=bwd * 1e6, fwd_mfma_frac=ff / fwd / PEAK_BF16,
+                 bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16, tokens_per_s=w.B * M / (fwd + bwd))
+        if temp:
+            out["temperature"] = r
+        else:
+            out.update(r)
+    return out
 
 
 def load_traffic(kernel):
