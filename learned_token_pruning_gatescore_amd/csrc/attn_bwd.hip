@@ -802,69 +802,90 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
 // 3. gate gradients
 // ---------------------------------------------------------------------------
 // dg_j = sum_h gamma_h colsum_h(j) / g_j, one thread per token in fixed head
-// order; each work-group also leaves, per head, its tokens' share of dgamma,
-// sum_j colsum_h(j) ln g_j (fixed-shape reductions), in part[b][bx][h].
+// order.  Each work-group also leaves, per head, its tokens' share of dgamma,
+// sum_j colsum_h(j) ln g_j, and (with the temperature) of the dsigma sum,
+// sum_j tstat_h(j), in part[b][bx][h] and part[n + (b][bx][h)] (n = the
+// number of shares): butterfly sums within each wave, then the four waves in
+// order, so the shares are fixed-shape (bitwise deterministic).  Heads go in
+// chunks of 64 per barrier.
 __global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
-                                                 const float *__restrict__ gamma, int B, int M, int Hq,
-                                                 float *__restrict__ dg, float *__restrict__ part) {
-  __shared__ float red[4];
+                                                 const float *__restrict__ gamma, const float *__restrict__ tstat,
+                                                 int B, int M, int Hq, float *__restrict__ dg,
+                                                 float *__restrict__ part) {
+  __shared__ float red[2][64][4];
   const int j = blockIdx.x * 256 + threadIdx.x;  // grid (ceil(M / 256), min(B, 65535))
   const bool vj = j < M;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nshare = (int64_t)B * gridDim.x * Hq;
   for (int b = blockIdx.y; b < B; b += gridDim.y) {
     const float *cr = colsum + (int64_t)b * Hq * M + j;
+    const float *tr = tstat ? tstat + (int64_t)b * Hq * M + j : nullptr;
     const float gv = vj ? g[(int64_t)b * M + j] : 0.f;
     const float lg = gv > 0.f ? logf(gv) : 0.f;
     float acc = 0.f;
-    for (int h = 0; h < Hq; ++h) {
-      const float v = vj ? cr[(int64_t)h * M] : 0.f;
-      acc += gamma[h] * v;
-      float t = gv > 0.f ? v * lg : 0.f;
+    for (int h0 = 0; h0 < Hq; h0 += 64) {
+      const int nh = Hq - h0 < 64 ? Hq - h0 : 64;
+      for (int hh = 0; hh < nh; hh += 8) {
+        float v[8], ts[8];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-      if (lane == 0) red[wave] = t;
+        for (int e = 0; e < 8; ++e) {  // eight independent loads in flight
+          const bool ok = vj && hh + e < nh;
+          v[e] = ok ? cr[(int64_t)(h0 + hh + e) * M] : 0.f;
+          ts[e] = ok && tr ? tr[(int64_t)(h0 + hh + e) * M] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (hh + e >= nh) break;
+          acc += gamma[h0 + hh + e] * v[e];
+          float t = gv > 0.f ? v[e] * lg : 0.f;
+          float u = ts[e];
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) {
+            t += __shfl_xor(t, o);
+            u += __shfl_xor(u, o);
+          }
+          if (lane == 0) {
+            red[0][hh + e][wave] = t;
+            red[1][hh + e][wave] = u;
+          }
+        }
+      }
       __syncthreads();
-      if (threadIdx.x == 0) part[((int64_t)b * gridDim.x + blockIdx.x) * Hq + h] = (red[0] + red[1]) + (red[2] + red[3]);
+      if ((int)threadIdx.x < nh) {
+        const int h = h0 + threadIdx.x;
+        const int64_t o = ((int64_t)b * gridDim.x + blockIdx.x) * Hq + h;
+        const float(*r0)[4] = red[0], (*r1)[4] = red[1];
+        part[o] = (r0[threadIdx.x][0] + r0[threadIdx.x][1]) + (r0[threadIdx.x][2] + r0[threadIdx.x][3]);
+        if (tstat) part[nshare + o] = (r1[threadIdx.x][0] + r1[threadIdx.x][1]) + (r1[threadIdx.x][2] + r1[threadIdx.x][3]);
+      }
       __syncthreads();
     }
     if (vj) dg[(int64_t)b * M + j] = gv > 0.f ? acc / gv : 0.f;
   }
 }
 
-// dgamma_h = sum over the n = B * ceil(M / 256) shares of head h, fixed-shape tree
+// Block h < Hq: dgamma_h = sum over the n = B * ceil(M / 256) shares of head h;
+// block Hq + h (with the temperature): dsigma_h = sigmoid(sigma_h) times the
+// sum of head h's dsigma shares (softplus' = sigmoid).  Fixed-shape tree.
 __global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ part, int n, int Hq,
-                                                     float *__restrict__ dgamma) {
+                                                     const float *__restrict__ sigma, float *__restrict__ dgamma,
+                                                     float *__restrict__ dsigma) {
   __shared__ float red[256];
-  const int h = blockIdx.x;
+  const bool sig = (int)blockIdx.x >= Hq;
+  const int h = sig ? blockIdx.x - Hq : blockIdx.x;
+  const float *p = part + (sig ? (int64_t)n * Hq : 0);
   float acc = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) acc += part[(int64_t)i * Hq + h];
+  for (int i = threadIdx.x; i < n; i += 256) acc += p[(int64_t)i * Hq + h];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dgamma[h] = red[0];
-}
-
-// dsigma_h = sigmoid(sigma_h) sum_{b,i} ratio_i dL/dt_ih (softplus' = sigmoid),
-// one work-group per head, fixed-shape tree
-__global__ __launch_bounds__(256) void dsigma_kernel(const float *__restrict__ tstat, const float *__restrict__ sigma,
-                                                     int B, int M, int Hq, float *__restrict__ dsigma) {
-  __shared__ float red[256];
-  const int h = blockIdx.x;
-  float acc = 0.f;
-  for (int b = 0; b < B; ++b) {
-    const float *row = tstat + ((int64_t)b * Hq + h) * M;
-    for (int i = threadIdx.x; i < M; i += 256) acc += row[i];
+  if (threadIdx.x == 0) {
+    if (sig) dsigma[h] = red[0] / (1.f + expf(-sigma[h]));
+    else dgamma[h] = red[0];
   }
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) dsigma[h] = red[0] / (1.f + expf(-sigma[h]));
 }
 
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
@@ -907,15 +928,14 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
                          (const float *)dout, delta, c, sigma, w.ratio, B, M, Hq, Hkv, D, dk, dv, w.colsum);
     }
-    // the row statistics are dead by now: their space takes the dgamma shares
+    // the row statistics are dead by now: their space (2 B Hq M floats) takes the
+    // dgamma and dsigma shares (2 B ceil(M / 256) Hq floats)
     hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)(B < 65535 ? B : 65535)), dim3(256), 0,
-                       s, w.colsum, g, gamma, B, M, Hq, dg, (float *)w.rowstat);
+                       s, w.colsum, g, gamma, sigma ? (const float *)w.tstat : nullptr, B, M, Hq, dg,
+                       (float *)w.rowstat);
   }
-  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, (const float *)w.rowstat,
-                     (int)((int64_t)B * ((M + 255) / 256)), Hq, dgamma);
-  if (sigma)
-    hipLaunchKernelGGL(dsigma_kernel, dim3((unsigned)Hq), dim3(256), 0, s, (const float *)w.tstat, sigma, B, M, Hq,
-                       dsigma);
+  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)(sigma ? 2 * Hq : Hq)), dim3(256), 0, s, (const float *)w.rowstat,
+                     (int)((int64_t)B * ((M + 255) / 256)), Hq, sigma, dgamma, dsigma);
   return hipGetLastError();
 }
 

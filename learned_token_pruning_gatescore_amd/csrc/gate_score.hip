@@ -20,13 +20,18 @@
 // (each fragment one contiguous 1 KB block), which each wave then loads
 // straight into registers, 4 to 8 16-input steps ahead.  Token rows stream
 // from HBM through a 4-stage LDS ring by direct buffer->LDS loads, one full
-// 128-byte line per row per stage.  One wave per SIMD, each holding a
-// 128-unit x 128-token accumulator tile (256 registers).
+// 128-byte line per row per stage.  Two waves per SIMD, each holding a
+// 64-unit x 128-token accumulator tile (128 registers): a wave alone on its
+// SIMD stalls on its own load and direct-load instructions (measured: about a
+// third of the product time with one 128-unit wave per SIMD), and the second
+// wave's products fill those gaps.
 #include "tg_common.h"
 
 namespace tg {
 
-constexpr int GS_U = 512;    // units per work-group chunk (4 waves x 128)
+constexpr int GS_W = 8;      // waves per work-group (two per SIMD)
+constexpr int GS_UB = 2;     // 32-unit blocks per wave
+constexpr int GS_U = GS_W * GS_UB * 32;  // units per work-group chunk (8 waves x 64)
 constexpr int GS_BK = 64;    // inputs per hidden stage (one 128-byte line per token row)
 constexpr int GS_NB = 4;     // hidden ring stages
 constexpr int GS_NA = 8;     // W1 fragment register ring: one slot per 16-input step of a trip
@@ -63,21 +68,22 @@ __global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__res
   }
 }
 
-// Work-group: 4 waves x (128 units x TT tokens), TT = 32 NTB.  Hidden stage st
+// Work-group: 8 waves x (64 units x TT tokens), TT = 32 NTB.  Hidden stage st
 // (inputs 64 st .. 64 st + 63 of the tile's TT rows) lives in ring buffer
 // st % 4, rows of 128 bytes with the 16-byte chunk XOR-swizzled by
 // (row / 2) % 8, which keeps the 16-row MFMA fragment reads free of bank
 // conflicts.  Out-of-range rows and inputs read as zero.
 template <int NTB>
-__global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
+__global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w1p, const uint16_t *__restrict__ w2,
     const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float *__restrict__ scores,
     float *__restrict__ gates) {
   constexpr int TT = 32 * NTB;         // tokens per work-group
   constexpr int ST = TT * GS_BK;       // u16 per hidden stage
-  constexpr int NI = TT / 32;          // direct-load instructions (8 rows each) per wave per stage
+  constexpr int NI = TT / (8 * GS_W);  // direct-load instructions (8 rows each) per wave per stage
+  static_assert(NI >= 1 && TT % (8 * GS_W) == 0, "tile rows must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint16_t sH[GS_NB * ST];
-  __shared__ float sRed[4][TT];
+  __shared__ float sRed[GS_W][TT];
   __shared__ float sW2[GS_U];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,17 +126,17 @@ __global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
   float run = 0.f;  // running score of token t0 + tid (tid < TT), across unit chunks
 
   for (int c = 0; c < d_ff; c += GS_U) {
-    for (int i = tid; i < GS_U; i += 256) sW2[i] = c + i < d_ff ? __uint_as_float((uint32_t)w2[c + i] << 16) : 0.f;
-    // this wave's unit groups: c / 32 + 4 wave + ub, ub = 0..3
-    const uint16_t *ap = w1p + ((int64_t)(c / 32 + 4 * wave) * nkk) * 512 + lane * 8;
+    for (int i = tid; i < GS_U; i += 64 * GS_W) sW2[i] = c + i < d_ff ? __uint_as_float((uint32_t)w2[c + i] << 16) : 0.f;
+    // this wave's unit groups: c / 32 + GS_UB wave + ub, ub < GS_UB
+    const uint16_t *ap = w1p + ((int64_t)(c / 32 + GS_UB * wave) * nkk) * 512 + lane * 8;
     auto load_a1 = [&](int kk, int ub) {
       const int kc = kk < nkk ? kk : nkk - 1;  // past the end: any valid block, never used
       return *(const u32x4 *)(ap + ((int64_t)ub * nkk + kc) * 512);
     };
 
-    f32x16 acc[4][NTB];
+    f32x16 acc[GS_UB][NTB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < GS_UB; ++i)
 #pragma unroll
       for (int j = 0; j < NTB; ++j) acc[i][j] = f32x16{};
 
@@ -143,30 +149,29 @@ __global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
     // on loads issued a step earlier).  So at the end of a trip slots 0..3
     // (loaded four or more steps earlier) are marked used -- the wait for
     // them happens there, exactly -- and the first use of slots 4..7 comes
-    // only after sixteen newer loads, so that wait too covers old loads only.
+    // only after 4 GS_UB newer loads, so that wait too covers old loads only.
     // One barrier per trip: the trip's two hidden stages landed for every
     // wave and every wave is done with the previous trip; then the direct
     // loads of the next trip's stages go out.
-    u32x4 a[GS_NA][4];
+    u32x4 a[GS_NA][GS_UB];
+    static_assert(GS_UB == 2, "touch03 lists two unit blocks per slot");
     auto touch03 = [&]() {
-      asm volatile("" ::"v"(a[0][0]), "v"(a[0][1]), "v"(a[0][2]), "v"(a[0][3]), "v"(a[1][0]), "v"(a[1][1]),
-                   "v"(a[1][2]), "v"(a[1][3]));
-      asm volatile("" ::"v"(a[2][0]), "v"(a[2][1]), "v"(a[2][2]), "v"(a[2][3]), "v"(a[3][0]), "v"(a[3][1]),
-                   "v"(a[3][2]), "v"(a[3][3]));
+      asm volatile("" ::"v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]), "v"(a[2][0]), "v"(a[2][1]),
+                   "v"(a[3][0]), "v"(a[3][1]));
     };
     issue_h(0);
     issue_h(1);
 #pragma unroll
     for (int j = 0; j < GS_NA; ++j)
 #pragma unroll
-      for (int ub = 0; ub < 4; ++ub) a[j][ub] = load_a1(j, ub);
+      for (int ub = 0; ub < GS_UB; ++ub) a[j][ub] = load_a1(j, ub);
     touch03();
     for (int st = 0; st < nst; st += 2) {  // nst is even
       const int k0 = 4 * st;               // first 16-input step of the trip
-      // at most the 16 loads of steps 4..7 of the previous trip (or of the
-      // prologue) may be in flight: the direct loads of this trip's stages,
-      // issued before them, are done
-      sync_vm<16>();
+      // at most the 4 GS_UB loads of steps 4..7 of the previous trip (or of
+      // the prologue) may be in flight: the direct loads of this trip's
+      // stages, issued before them, are done
+      sync_vm<4 * GS_UB>();
       issue_h(st + 2);
       issue_h(st + 3);
       u32x4 b[2][NTB];
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
         if (j < GS_NA - 1) read_b(j + 1, b[(j + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
+        for (int ub = 0; ub < GS_UB; ++ub) {
 #pragma unroll
           for (int tb = 0; tb < NTB; ++tb) acc[ub][tb] = mfma32(a[j][ub], b[j & 1][tb], acc[ub][tb]);
           __builtin_amdgcn_sched_barrier(0);
@@ -200,11 +205,11 @@ __global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) part[tb] = 0.f;
 #pragma unroll
-    for (int ub = 0; ub < 4; ++ub) {
+    for (int ub = 0; ub < GS_UB; ++ub) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         // registers 4 g4 .. 4 g4 + 3 hold units 32 ub + 8 g4 + 4 hl + e
-        const f32x4 wv = *(const f32x4 *)&sW2[wave * 128 + ub * 32 + 8 * g4 + 4 * hl];
+        const f32x4 wv = *(const f32x4 *)&sW2[wave * 32 * GS_UB + ub * 32 + 8 * g4 + 4 * hl];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
@@ -222,7 +227,9 @@ __global__ __launch_bounds__(256, 1) void gate_score_bf16_kernel(
       if (hl == 0) sRed[wave][32 * tb + l32] = part[tb];
     }
     __syncthreads();
-    if (tid < TT) run += (sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid]);
+    if (tid < TT)  // fixed-order tree over the waves
+      run += ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid])) +
+             ((sRed[4][tid] + sRed[5][tid]) + (sRed[6][tid] + sRed[7][tid]));
     __syncthreads();
   }
 
@@ -284,11 +291,11 @@ hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2,
     const int nkk = gate_nkk(d);
     // 128-token tiles when they still fill the 256 compute units, else 64
     if ((T + 127) / 128 >= 256) {
-      hipLaunchKernelGGL(gate_score_bf16_kernel<4>, dim3((unsigned)((T + 127) / 128)), dim3(256), 0, s,
+      hipLaunchKernelGGL(gate_score_bf16_kernel<4>, dim3((unsigned)((T + 127) / 128)), dim3(64 * GS_W), 0, s,
                          (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff,
                          nkk, scores, gates);
     } else {
-      hipLaunchKernelGGL(gate_score_bf16_kernel<2>, dim3((unsigned)((T + 63) / 64)), dim3(256), 0, s,
+      hipLaunchKernelGGL(gate_score_bf16_kernel<2>, dim3((unsigned)((T + 63) / 64)), dim3(64 * GS_W), 0, s,
                          (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff,
                          nkk, scores, gates);
     }
