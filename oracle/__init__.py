@@ -69,6 +69,10 @@ def _load():
                                  _D, _D, _D, _D, _D, _D]
     lib.tgo_attn_bwd.restype = ctypes.c_int
     lib.tgo_round_bf16.argtypes = [ctypes.c_double]
+    lib.tgo_gate_score_ln.argtypes = [_D, _D, ctypes.c_double, _D, _D, _U8, _i64, _i64, _i64, _D, _D]
+    lib.tgo_score_normalize.argtypes = [_D, _U8, _i64, _i64, ctypes.c_double, _D]
+    lib.tgo_gate_softmax.argtypes = [_D, _I32, _i64, _i64, _D]
+    lib.tgo_gate_softmax_bwd.argtypes = [_D, _D, _i64, _i64, _D]
     lib.tgo_round_bf16.restype = ctypes.c_double
     _lib = lib
     return lib
@@ -112,6 +116,72 @@ def gate_score(hidden, w1, w2, forced=None):
     lib.tgo_gate_score(_ptr(h, _D), _ptr(W1, _D), _ptr(W2, _D), _ptr(f, _U8), T, d, d_ff,
                        _ptr(s, _D), _ptr(g, _D))
     return s, g
+
+
+def gate_score_ln(hidden, ln_w, eps, w1, w2, forced=None):
+    """Scores and gates of the LN2-normalised residual (DeepDive section 2 Eq. 1, section 3.1 Eq. 3).
+
+    hidden [T, d] raw residual; ln_w [d] RMSNorm weight or None (= 1); eps >= 0.
+    Returns (scores float64 [T], gates float64 [T]) as gate_score on the normalised rows.
+    """
+    lib = _load()
+    h = _f64(hidden)
+    W1 = _f64(w1)
+    W2 = _f64(w2).reshape(-1)
+    T, d = h.shape
+    d_ff = W1.shape[0]
+    lw = None if ln_w is None else _f64(ln_w).reshape(d)
+    f = None if forced is None else np.ascontiguousarray(np.asarray(forced, dtype=np.uint8).reshape(T))
+    s = np.empty(T, np.float64)
+    g = np.empty(T, np.float64)
+    lib.tgo_gate_score_ln(_ptr(h, _D), _ptr(lw, _D), float(eps), _ptr(W1, _D), _ptr(W2, _D), _ptr(f, _U8), T, d,
+                          d_ff, _ptr(s, _D), _ptr(g, _D))
+    return s, g
+
+
+def score_normalize(scores, forced, eps):
+    """Sequence RMS normalisation over the prunable positions, 0 on forced ones (DeepDive section 3.1 Eq. 3).
+
+    scores [B, N] or [N]; forced of the same shape (nonzero = non-prunable) or None.  Returns float64, same shape.
+    """
+    lib = _load()
+    s = _f64(scores)
+    shp = s.shape
+    s2 = s.reshape(-1, shp[-1])
+    B, N = s2.shape
+    f = None if forced is None else np.ascontiguousarray(np.asarray(forced, dtype=np.uint8).reshape(B, N))
+    out = np.empty((B, N), np.float64)
+    lib.tgo_score_normalize(_ptr(np.ascontiguousarray(s2), _D), _ptr(f, _U8), B, N, float(eps), _ptr(out, _D))
+    return out.reshape(shp)
+
+
+def gate_softmax(bsc, kept=None):
+    """Gate values as the softmax of the normalised scores over the kept set (DeepDive section 3.2 Eq. 5).
+
+    bsc [B, M] or [M]; kept int32 of the same shape or None (negative index = padding, g = 0).
+    """
+    lib = _load()
+    x = _f64(bsc)
+    shp = x.shape
+    x2 = np.ascontiguousarray(x.reshape(-1, shp[-1]))
+    B, M = x2.shape
+    k = None if kept is None else np.ascontiguousarray(np.asarray(kept, dtype=np.int32).reshape(B, M))
+    g = np.empty((B, M), np.float64)
+    lib.tgo_gate_softmax(_ptr(x2, _D), _ptr(k, _I32), B, M, _ptr(g, _D))
+    return g.reshape(shp)
+
+
+def gate_softmax_bwd(g, dg):
+    """db = g (dg - sum g dg) per row: the backward of gate_softmax."""
+    lib = _load()
+    G = _f64(g)
+    shp = G.shape
+    G2 = np.ascontiguousarray(G.reshape(-1, shp[-1]))
+    dG = np.ascontiguousarray(_f64(dg).reshape(G2.shape))
+    B, M = G2.shape
+    out = np.empty((B, M), np.float64)
+    lib.tgo_gate_softmax_bwd(_ptr(G2, _D), _ptr(dG, _D), B, M, _ptr(out, _D))
+    return out.reshape(shp)
 
 
 def select_topk(scores, forced, K, M=None):

@@ -542,5 +542,107 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* The rest of the scoring definition: LN2 before the scorer, the sequence  */
+/* RMS normalisation of the scores, and the softmax-over-S gate             */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DeepDive] section 2, Eq. 1: the gate reads the post-attention residual
+ * after the layer's second normalisation, a~_j = LN2(a_j), and section 3.1,
+ * Eq. 3 feeds a~_j to the scorer.  Reading used here (the pages name the
+ * normaliser, not its kind): RMSNorm with a per-channel weight w,
+ *     a~_j[i] = a_j[i] / sqrt((1/d) sum_i a_j[i]^2 + eps) * w[i],
+ * the normaliser of the Qwen3 models the pages evaluate; ln_w NULL means
+ * w = 1.  Then the scorer of section a1 above on a~.
+ */
+void tgo_gate_score_ln(const double *hidden, const double *ln_w, double eps, const double *w1,
+                       const double *w2, const uint8_t *forced, int64_t T, int64_t d, int64_t d_ff,
+                       double *scores, double *gates)
+{
+    double *norm = (double *)malloc((size_t)(T * d) * sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double *h = hidden + t * d;
+        double ss = 0.0;
+        for (int64_t i = 0; i < d; ++i)
+            ss += h[i] * h[i];
+        double r = 1.0 / sqrt(ss / (double)d + eps);
+        for (int64_t i = 0; i < d; ++i)
+            norm[t * d + i] = h[i] * r * (ln_w ? ln_w[i] : 1.0);
+    }
+    tgo_gate_score(norm, w1, w2, forced, T, d, d_ff, scores, gates);
+    free(norm);
+}
+
+/*
+ * [DeepDive] section 3.1, Eq. 3 (second part): the raw scores of one request
+ * are divided by their root mean square over the prunable positions P, and
+ * the non-prunable positions N get 0:
+ *     b_j = b~_j / sqrt((1/|P|) sum_{j' in P} b~_{j'}^2 + eps)   (j in P)
+ *     b_j = 0                                                   (j in N)
+ * A row with no prunable position is all zeros.  scores, out: [B, N];
+ * forced: [B, N] (nonzero = in N) or NULL (every position prunable).
+ */
+void tgo_score_normalize(const double *scores, const uint8_t *forced, int64_t B, int64_t N, double eps,
+                         double *out)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        const double *s = scores + b * N;
+        const uint8_t *f = forced ? forced + b * N : NULL;
+        double ss = 0.0;
+        int64_t np = 0;
+        for (int64_t j = 0; j < N; ++j)
+            if (!(f && f[j])) {
+                ss += s[j] * s[j];
+                ++np;
+            }
+        double r = np > 0 ? sqrt(ss / (double)np + eps) : 1.0;
+        for (int64_t j = 0; j < N; ++j)
+            out[b * N + j] = (f && f[j]) ? 0.0 : s[j] / r;
+    }
+}
+
+/*
+ * [DeepDive] section 3.2, Eq. 5: the gate of a kept token is the softmax of
+ * the normalised scores over the kept set S,
+ *     g_j = exp(b_j) / sum_{j' in S} exp(b_j').
+ * b: [B, M] normalised scores of the kept tokens; kept: [B, M] kept indices
+ * or NULL: an entry whose index is negative (padding) is not in S and gets
+ * g = 0.  Eq. 6 scales b by a per-head gain c before the softmax; since
+ * softmax_S(c b)_j = softmax_S(b)_j^c / Z_c, the attention bias c ln g_j of
+ * this gate equals Eq. 6's ln g_j^h up to a per-head constant, which the
+ * attention softmax over keys removes.
+ */
+void tgo_gate_softmax(const double *bsc, const int32_t *kept, int64_t B, int64_t M, double *g)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        const double *x = bsc + b * M;
+        const int32_t *k = kept ? kept + b * M : NULL;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < M; ++j)
+            if (!(k && k[j] < 0) && x[j] > mx)
+                mx = x[j];
+        double z = 0.0;
+        for (int64_t j = 0; j < M; ++j)
+            if (!(k && k[j] < 0))
+                z += exp(x[j] - mx);
+        for (int64_t j = 0; j < M; ++j)
+            g[b * M + j] = (k && k[j] < 0) ? 0.0 : exp(x[j] - mx) / z;
+    }
+}
+
+/* Backward of tgo_gate_softmax: db_j = g_j (dg_j - sum_{k in S} g_k dg_k)
+ * (padding has g = 0, so db = 0 there). */
+void tgo_gate_softmax_bwd(const double *g, const double *dg, int64_t B, int64_t M, double *db)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        double dot = 0.0;
+        for (int64_t j = 0; j < M; ++j)
+            dot += g[b * M + j] * dg[b * M + j];
+        for (int64_t j = 0; j < M; ++j)
+            db[b * M + j] = g[b * M + j] * (dg[b * M + j] - dot);
+    }
+}
+
 /* Exposed for the pin tests of the bf16 rounding helper. */
 double tgo_round_bf16(double x) { return round_bf16(x); }
