@@ -113,6 +113,65 @@ tg_status tg_gate_score_packed(const void *hidden, const void *w1_packed, const 
                                int64_t d_ff, tg_dtype dt, float *scores, float *gates,
                                void *stream);
 
+/*
+ * tg_gate_score_ln -- tg_gate_score on the raw post-attention residual, with
+ * the layer's second normalisation in front.  [DeepDive] section 2, Eq. 1 (the
+ * gate reads a~ = LN2(a)) and section 3.1, Eq. 3 (the scorer maps a~_j).  The
+ * normaliser is RMSNorm with a per-channel weight (the Qwen3 models' LN2):
+ *     a~[t,i] = a[t,i] / sqrt(mean_i a[t,i]^2 + ln_eps) * ln_w[i]
+ * followed by exactly the scorer of tg_gate_score.
+ *   hidden [B, N, d] (dt) raw residual; ln_w [d] (dt) or NULL (= 1);
+ *   ln_eps finite >= 0 (an all-zero row with ln_eps = 0 gives NaN).
+ * Other arguments, outputs, workspace (the same size) and errors as
+ * tg_gate_score.  bf16: ln_w is folded into the packed W1 (one bf16 rounding
+ * of w1 * ln_w) and each token's 1 / sqrt(mean square + eps), formed in fp32
+ * from the bf16 inputs, scales its pre-activations before SiLU.
+ */
+tg_status tg_gate_score_ln(const void *hidden, const void *ln_w, float ln_eps, const void *w1,
+                           const void *w2, const uint8_t *forced_keep, int64_t B, int64_t N,
+                           int64_t d, int64_t d_ff, tg_dtype dt, float *scores, float *gates,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * tg_score_normalize -- sequence RMS normalisation of one request's scores.
+ * [DeepDive] section 3.1, Eq. 3 (second part): per row b,
+ *     out_j = s_j / sqrt((1/|P|) sum_{j' in P} s_{j'}^2 + eps)   (j prunable)
+ *     out_j = 0                                                 (j forced)
+ * with P the positions whose forced_keep is 0.  A row with no prunable
+ * position is all zeros.  Ranking out instead of s keeps the order of the
+ * prunable scores (a positive scale); out feeds tg_select_topk and, gathered
+ * by tg_compact, tg_gate_softmax.
+ *   scores [B, N] f32; forced_keep [B, N] u8 or NULL (every position prunable);
+ *   out [B, N] f32 (may equal scores: in place); eps finite >= 0; N <= 2^24.
+ * fp32 arithmetic, fixed-order reductions (deterministic).
+ */
+tg_status tg_score_normalize(const float *scores, const uint8_t *forced_keep, int64_t B,
+                             int64_t N, float eps, float *out, void *stream);
+
+/*
+ * tg_gate_softmax -- gate values as the softmax of the normalised scores over
+ * the kept set.  [DeepDive] section 3.2, Eq. 5:
+ *     g_j = exp(b_j) / sum_{j' in S} exp(b_j')
+ * per row, over the kept tokens (b gathered by tg_compact).  Entries whose
+ * kept_idx is negative (padding) are not in S and get g = 0.  Eq. 6's per-head
+ * gain: tg_gated_attn_fwd with these g and gamma_h = the gain (the softplus of
+ * the raw parameter) gives softmax_j(z_ij + gamma_h b_j), i.e. Eq. 6's gate
+ * with the per-head normaliser removed by the attention softmax.
+ *   b [B, M] f32; kept_idx [B, M] i32 or NULL; g [B, M] f32 out.
+ * fp32 arithmetic (expf), fixed-order reductions (deterministic).
+ */
+tg_status tg_gate_softmax(const float *b, const int32_t *kept_idx, int64_t B, int64_t M,
+                          float *g, void *stream);
+
+/*
+ * tg_gate_softmax_bwd -- backward of tg_gate_softmax: per row
+ *     db_j = g_j (dg_j - sum_k g_k dg_k)
+ * with g the forward's output and dg = dL/dg (e.g. from tg_gated_attn_bwd).
+ *   g, dg, db [B, M] f32 (db fully overwritten; 0 where g = 0).
+ */
+tg_status tg_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db,
+                              void *stream);
+
 /* Kept tokens per row: n_forced + min(K, N - n_forced); -1 for invalid input. */
 int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K);
 

@@ -17,6 +17,11 @@ Memory-Efficient LLM Prefill", sections 3.1-3.4):
   tg_gated_attn_fwd  causal attention with the per-key bias gamma_h * ln g_j and,
                      optionally, the pruning-ratio temperature (section 3.2, Eq. 7/8)
   tg_gated_attn_bwd  its gradients (dq, dk, dv, dg, dgamma, and dsigma)
+The rest of the scoring definition (section 2 Eq. 1, section 3.1 Eq. 3, section 3.2 Eq. 5):
+  tg_gate_score_ln     the scorer on the raw residual with the RMSNorm (LN2) in front
+  tg_score_normalize   sequence RMS normalisation over the prunable positions, 0 on forced ones
+  tg_gate_softmax      gate values as the softmax of the normalised scores over the kept set
+  tg_gate_softmax_bwd  its backward
 """
 from __future__ import annotations
 
@@ -28,6 +33,7 @@ __all__ = [
     "tg_gate_score_workspace_size", "tg_gate_pack_w1", "tg_gate_score_packed", "gate_workspace",
     "tg_select_topk", "tg_compact", "tg_gated_attn_fwd", "tg_gated_attn_bwd",
     "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
+    "tg_gate_score_ln", "tg_score_normalize", "tg_gate_softmax", "tg_gate_softmax_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +87,14 @@ def load():
     lib.tg_select_topk.argtypes = [P, P, i64, i64, i64, i64, P, P, P, sz, P]
     lib.tg_compact.restype = c_int
     lib.tg_compact.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P, P]
+    lib.tg_gate_score_ln.restype = c_int
+    lib.tg_gate_score_ln.argtypes = [P, P, f32, P, P, P, i64, i64, i64, i64, c_int, P, P, P, sz, P]
+    lib.tg_score_normalize.restype = c_int
+    lib.tg_score_normalize.argtypes = [P, P, i64, i64, f32, P, P]
+    lib.tg_gate_softmax.restype = c_int
+    lib.tg_gate_softmax.argtypes = [P, P, i64, i64, P, P]
+    lib.tg_gate_softmax_bwd.restype = c_int
+    lib.tg_gate_softmax_bwd.argtypes = [P, P, i64, i64, P, P]
     lib.tg_gated_attn_workspace_size.restype = sz
     lib.tg_gated_attn_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     lib.tg_gated_attn_fwd.restype = c_int
@@ -182,6 +196,38 @@ def tg_gate_score_packed(hidden, w1_packed, d_ff, w2, forced_keep, scores, gates
     B, N, d = hidden.shape
     _check(load().tg_gate_score_packed(_ptr(hidden), _ptr(w1_packed), _ptr(w2), _ptr(forced_keep), B, N, d,
                                        int(d_ff), _dt(hidden), _ptr(scores), _ptr(gates), _stream(stream)))
+
+
+def tg_gate_score_ln(hidden, ln_w, ln_eps, w1, w2, forced_keep, scores, gates=None, ws=None, stream=None):
+    """tg_gate_score on the raw residual [B, N, d] with the RMSNorm (weight ln_w [d] or None, eps) in front."""
+    _contig(hidden, ln_w, w1, w2, forced_keep, scores, gates, ws)
+    B, N, d = hidden.shape
+    d_ff = w1.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().tg_gate_score_ln(_ptr(hidden), _ptr(ln_w), float(ln_eps), _ptr(w1), _ptr(w2), _ptr(forced_keep),
+                                   B, N, d, d_ff, _dt(hidden), _ptr(scores), _ptr(gates), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
+
+
+def tg_score_normalize(scores, forced_keep, eps, out, stream=None):
+    """out [B, N] = scores / their RMS over the prunable positions (+eps), 0 on forced ones (out may be scores)."""
+    _contig(scores, forced_keep, out)
+    B, N = scores.shape
+    _check(load().tg_score_normalize(_ptr(scores), _ptr(forced_keep), B, N, float(eps), _ptr(out), _stream(stream)))
+
+
+def tg_gate_softmax(b, kept_idx, g, stream=None):
+    """g [B, M] = softmax of b [B, M] over each row's kept entries (kept_idx < 0: padding, g = 0)."""
+    _contig(b, kept_idx, g)
+    B, M = b.shape
+    _check(load().tg_gate_softmax(_ptr(b), _ptr(kept_idx), B, M, _ptr(g), _stream(stream)))
+
+
+def tg_gate_softmax_bwd(g, dg, db, stream=None):
+    """db = g (dg - sum g dg) per row."""
+    _contig(g, dg, db)
+    B, M = g.shape
+    _check(load().tg_gate_softmax_bwd(_ptr(g), _ptr(dg), B, M, _ptr(db), _stream(stream)))
 
 
 def tg_select_topk(scores, forced_keep, K, n_forced, kept_idx, kept_count=None, ws=None, stream=None):

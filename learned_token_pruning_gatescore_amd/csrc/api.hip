@@ -13,9 +13,14 @@
 
 namespace tg {
 size_t gate_packed_bytes(int d, int d_ff);
-hipError_t launch_gate_pack_w1(const void *w1, int d, int d_ff, void *packed, hipStream_t s);
+hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s);
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced, int64_t T,
-                             int d, int d_ff, bool bf16, float *scores, float *gates, hipStream_t s);
+                             int d, int d_ff, bool bf16, bool ln, const void *ln_w, float ln_eps, float *scores,
+                             float *gates, hipStream_t s);
+hipError_t launch_score_normalize(const float *s, const uint8_t *forced, int64_t B, int64_t N, float eps, float *out,
+                                  hipStream_t st);
+hipError_t launch_gate_softmax(const float *x, const int32_t *kept, int64_t B, int64_t M, float *g, hipStream_t st);
+hipError_t launch_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db, hipStream_t st);
 hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_t B, int64_t N, int64_t K,
                               int64_t M_alloc, int32_t *kept, int32_t *kept_count, hipStream_t s);
 hipError_t launch_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept,
@@ -140,7 +145,7 @@ tg_status tg_gate_pack_w1(const void *w1, int64_t d, int64_t d_ff, tg_dtype dt, 
   REQUIRE(aligned16(w1) && aligned16(w1_packed), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   const size_t need = tg::gate_packed_bytes((int)d, (int)d_ff);
   REQUIRE(bytes >= need, TG_ERR_WORKSPACE, "w1_packed holds %zu bytes, needs %zu", bytes, need);
-  return hip_status(tg::launch_gate_pack_w1(w1, (int)d, (int)d_ff, w1_packed, (hipStream_t)stream),
+  return hip_status(tg::launch_gate_pack_w1(w1, nullptr, (int)d, (int)d_ff, w1_packed, (hipStream_t)stream),
                     "tg_gate_pack_w1 launch");
 }
 
@@ -150,8 +155,8 @@ tg_status tg_gate_score_packed(const void *hidden, const void *w1_packed, const 
   REQUIRE(dt == TG_BF16, TG_ERR_UNSUPPORTED, "packed weights exist for bf16 only");
   const tg_status st = check_gate(hidden, w1_packed, w2, B, N, d, d_ff, dt, scores, gates);
   if (st != TG_OK) return st;
-  return hip_status(tg::launch_gate_score(hidden, w1_packed, w2, forced_keep, B * N, (int)d, (int)d_ff, true,
-                                          scores, gates, (hipStream_t)stream),
+  return hip_status(tg::launch_gate_score(hidden, w1_packed, w2, forced_keep, B * N, (int)d, (int)d_ff, true, false,
+                                          nullptr, 0.f, scores, gates, (hipStream_t)stream),
                     "tg_gate_score_packed launch");
 }
 
@@ -167,15 +172,72 @@ tg_status tg_gate_score(const void *hidden, const void *w1, const void *w2, cons
             ws ? ws_bytes : (size_t)0);
     REQUIRE(aligned16(ws), TG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     if (B * N == 0) return ok();
-    const tg_status pst = hip_status(tg::launch_gate_pack_w1(w1, (int)d, (int)d_ff, ws, s), "tg_gate_score pack");
+    const tg_status pst =
+        hip_status(tg::launch_gate_pack_w1(w1, nullptr, (int)d, (int)d_ff, ws, s), "tg_gate_score pack");
     if (pst != TG_OK) return pst;
-    return hip_status(tg::launch_gate_score(hidden, ws, w2, forced_keep, B * N, (int)d, (int)d_ff, true, scores,
-                                            gates, s),
+    return hip_status(tg::launch_gate_score(hidden, ws, w2, forced_keep, B * N, (int)d, (int)d_ff, true, false,
+                                            nullptr, 0.f, scores, gates, s),
                       "tg_gate_score launch");
   }
-  return hip_status(tg::launch_gate_score(hidden, w1, w2, forced_keep, B * N, (int)d, (int)d_ff, false, scores,
-                                          gates, s),
+  return hip_status(tg::launch_gate_score(hidden, w1, w2, forced_keep, B * N, (int)d, (int)d_ff, false, false,
+                                          nullptr, 0.f, scores, gates, s),
                     "tg_gate_score launch");
+}
+
+tg_status tg_gate_score_ln(const void *hidden, const void *ln_w, float ln_eps, const void *w1, const void *w2,
+                           const uint8_t *forced_keep, int64_t B, int64_t N, int64_t d, int64_t d_ff, tg_dtype dt,
+                           float *scores, float *gates, void *ws, size_t ws_bytes, void *stream) {
+  const tg_status st = check_gate(hidden, w1, w2, B, N, d, d_ff, dt, scores, gates);
+  if (st != TG_OK) return st;
+  REQUIRE(std::isfinite(ln_eps) && ln_eps >= 0.f, TG_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
+  REQUIRE(aligned16(ln_w), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == TG_BF16) {
+    const size_t need = tg::gate_packed_bytes((int)d, (int)d_ff);
+    REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "bf16 scoring needs a %zu-byte workspace (got %zu)", need,
+            ws ? ws_bytes : (size_t)0);
+    REQUIRE(aligned16(ws), TG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (B * N == 0) return ok();
+    const tg_status pst =
+        hip_status(tg::launch_gate_pack_w1(w1, ln_w, (int)d, (int)d_ff, ws, s), "tg_gate_score_ln pack");
+    if (pst != TG_OK) return pst;
+    return hip_status(tg::launch_gate_score(hidden, ws, w2, forced_keep, B * N, (int)d, (int)d_ff, true, true,
+                                            nullptr, ln_eps, scores, gates, s),
+                      "tg_gate_score_ln launch");
+  }
+  return hip_status(tg::launch_gate_score(hidden, w1, w2, forced_keep, B * N, (int)d, (int)d_ff, false, true, ln_w,
+                                          ln_eps, scores, gates, s),
+                    "tg_gate_score_ln launch");
+}
+
+tg_status tg_score_normalize(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t N, float eps,
+                             float *out, void *stream) {
+  REQUIRE(scores && out, TG_ERR_INVALID_ARG, "scores and out are required");
+  REQUIRE(B >= 0 && N >= 0, TG_ERR_INVALID_ARG, "B and N must be >= 0");
+  REQUIRE(B <= 0x7FFFFFFF && N <= (int64_t)1 << 24, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(std::isfinite(eps) && eps >= 0.f, TG_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  REQUIRE(aligned16(scores) && aligned16(out), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_score_normalize(scores, forced_keep, B, N, eps, out, (hipStream_t)stream),
+                    "tg_score_normalize launch");
+}
+
+tg_status tg_gate_softmax(const float *b, const int32_t *kept_idx, int64_t B, int64_t M, float *g, void *stream) {
+  REQUIRE(b && g, TG_ERR_INVALID_ARG, "b and g are required");
+  REQUIRE(B >= 0 && M >= 0, TG_ERR_INVALID_ARG, "B and M must be >= 0");
+  REQUIRE(B <= 0x7FFFFFFF, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(aligned16(b) && aligned16(kept_idx) && aligned16(g), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_gate_softmax(b, kept_idx, B, M, g, (hipStream_t)stream), "tg_gate_softmax launch");
+}
+
+tg_status tg_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db, void *stream) {
+  REQUIRE(g && dg && db, TG_ERR_INVALID_ARG, "g, dg and db are required");
+  REQUIRE(B >= 0 && M >= 0, TG_ERR_INVALID_ARG, "B and M must be >= 0");
+  REQUIRE(B <= 0x7FFFFFFF, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(aligned16(g) && aligned16(dg) && aligned16(db), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_gate_softmax_bwd(g, dg, B, M, db, (hipStream_t)stream),
+                    "tg_gate_softmax_bwd launch");
 }
 
 size_t tg_select_topk_workspace_size(int64_t B, int64_t N) {

@@ -5,6 +5,12 @@
 // maps each token's normalised residual to one scalar score; here
 //     s_t = sum_k w2[k] * SiLU(sum_i w1[k,i] h[t,i]),
 //     g_t = 1 for a forced token, else sigmoid(s_t).
+// With the layer's second normalisation in front (section 2, Eq. 1; RMSNorm
+// with weight w, the Qwen3 normaliser): h is the raw residual a and
+//     sum_i w1[k,i] a~[t,i] = r_t sum_i (w1[k,i] w[i]) a[t,i],
+//     r_t = 1 / sqrt(mean_i a[t,i]^2 + eps),
+// so w is folded into the packed W1 (one bf16 rounding of the product) and
+// r_t scales each token's pre-activations before SiLU.
 //
 // bf16 path: a [d_ff x d] x [d x T] product on the matrix cores (32x32x16 bf16
 // MFMA, fp32 accumulation).  W1 is the MFMA "A" operand (rows = units) and the
@@ -47,8 +53,9 @@ size_t gate_packed_bytes(int d, int d_ff) { return (size_t)gate_ngp(d_ff) * gate
 // A operand of one 32x32x16 MFMA, as one contiguous 1 KB block.  A work-group
 // packs 32 rows x 128 inputs: coalesced row reads into LDS, then eight
 // contiguous 1 KB blocks out.
-__global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__restrict__ w1, int d, int d_ff, int nkk,
-                                                           uint16_t *__restrict__ out) {
+__global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__restrict__ w1,
+                                                           const uint16_t *__restrict__ ln_w, int d, int d_ff,
+                                                           int nkk, uint16_t *__restrict__ out) {
   __shared__ u32x4 t[32][17];  // 32 rows x 16 chunks of 8 inputs (+1 chunk of padding)
   const int tid = threadIdx.x, kc = blockIdx.x, ug = blockIdx.y;
 #pragma unroll
@@ -56,7 +63,15 @@ __global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__res
     const int idx = tid + 256 * j, row = idx >> 4, c = idx & 15;
     const int u = 32 * ug + row, k0 = 128 * kc + 8 * c;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (u < d_ff && k0 < d) v = *(const u32x4 *)(w1 + (int64_t)u * d + k0);  // d % 8 == 0: all 8 in range
+    if (u < d_ff && k0 < d) {
+      v = *(const u32x4 *)(w1 + (int64_t)u * d + k0);  // d % 8 == 0: all 8 in range
+      if (ln_w) {  // w1[u, i] * w[i]: exact in fp32 (bf16 x bf16), rounded once to bf16
+        const u32x4 lw = *(const u32x4 *)(ln_w + k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = pack_bf16x2(bf16_lo(v[e]) * bf16_lo(lw[e]), bf16_hi(v[e]) * bf16_hi(lw[e]));
+      }
+    }
     t[row][c] = v;
   }
   __syncthreads();
@@ -73,11 +88,15 @@ __global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__res
 // st % 4, rows of 128 bytes with the 16-byte chunk XOR-swizzled by
 // (row / 2) % 8, which keeps the 16-row MFMA fragment reads free of bank
 // conflicts.  Out-of-range rows and inputs read as zero.
-template <int NTB>
+// LN: the rows are raw residuals; each token's sum of squares is gathered from
+// the B fragments the waves read anyway (fragment tb, step j of a trip is
+// squared by the one wave with wave % NTB == tb and wave / NTB == j % (8 / NTB)),
+// then r_t scales the pre-activations.
+template <int NTB, bool LN>
 __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w1p, const uint16_t *__restrict__ w2,
-    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float *__restrict__ scores,
-    float *__restrict__ gates) {
+    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float ln_eps,
+    float *__restrict__ scores, float *__restrict__ gates) {
   constexpr int TT = 32 * NTB;         // tokens per work-group
   constexpr int ST = TT * GS_BK;       // u16 per hidden stage
   constexpr int NI = TT / (8 * GS_W);  // direct-load instructions (8 rows each) per wave per stage
@@ -85,6 +104,10 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sH[GS_NB * ST];
   __shared__ float sRed[GS_W][TT];
   __shared__ float sW2[GS_U];
+  __shared__ float sSq[LN ? GS_W : 1][64];
+  __shared__ float sR[LN ? TT : 1];
+  constexpr int SQP = GS_W / NTB;  // waves sharing one fragment's squares (by step parity)
+  static_assert(GS_NA % SQP == 0, "a trip's steps split evenly over those waves");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -134,6 +157,8 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
       return *(const u32x4 *)(ap + ((int64_t)ub * nkk + kc) * 512);
     };
 
+    const int sq_tb = __builtin_amdgcn_readfirstlane(wave % NTB), sq_ph = __builtin_amdgcn_readfirstlane(wave / NTB);
+    float sq = 0.f;  // LN: this lane's share of token 32 sq_tb + l32's sum of squares
     f32x16 acc[GS_UB][NTB];
 #pragma unroll
     for (int i = 0; i < GS_UB; ++i)
@@ -194,12 +219,41 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
           a[j][ub] = load_a1(k0 + GS_NA + j, ub);  // slot j, ub: used up; next trip's step j
           __builtin_amdgcn_sched_barrier(0);
         }
+        if (LN && j % SQP == sq_ph) {  // wave-uniform
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb)
+            if (tb == sq_tb) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float lo = bf16_lo(b[j & 1][tb][e]), hi = bf16_hi(b[j & 1][tb][e]);
+                sq = __builtin_fmaf(lo, lo, sq);
+                sq = __builtin_fmaf(hi, hi, sq);
+              }
+            }
+        }
       }
       touch03();
     }
     // drain the tail loads before the ring is reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // LN: r_t of every token of the tile (fixed-order sum of its 2 SQP shares)
+    float rt[NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) rt[tb] = 1.f;
+    if (LN) {
+      sSq[wave][lane] = sq;
+      __syncthreads();
+      if (tid < TT) {
+        const int tb = tid / 32, l = tid % 32;
+        float ss = 0.f;
+        for (int ph = 0; ph < SQP; ++ph) ss += sSq[ph * NTB + tb][l] + sSq[ph * NTB + tb][l + 32];
+        sR[tid] = 1.f / sqrtf(ss / (float)d + ln_eps);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) rt[tb] = sR[32 * tb + l32];
+    }
     // Epilogue: SiLU, times w2, summed over this lane's units.
     float part[NTB];
 #pragma unroll
@@ -214,7 +268,7 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
         for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x = acc[ub][tb][g4 * 4 + e];
+            const float x = LN ? acc[ub][tb][g4 * 4 + e] * rt[tb] : acc[ub][tb][g4 * 4 + e];
             const float silu = x * fast_rcp(1.f + fast_exp2(-x * kLog2e));
             part[tb] += silu * wv[e];
           }
@@ -247,15 +301,30 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
 
 // fp32 path: one work-group (4 waves) per token; waves take units round-robin,
 // lanes split d; fixed-order reductions (deterministic).
+// ln_w (with ln_eps): the row is RMS-normalised first (fixed-order sum of squares).
 __global__ __launch_bounds__(256) void gate_score_f32_kernel(
     const float *__restrict__ hidden, const float *__restrict__ w1, const float *__restrict__ w2,
-    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, float *__restrict__ scores,
-    float *__restrict__ gates) {
+    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, const float *__restrict__ ln_w, float ln_eps,
+    bool ln, float *__restrict__ scores, float *__restrict__ gates) {
   extern __shared__ float sh[];  // d floats
   __shared__ float sPart[4];
+  __shared__ float sR;
   const int64_t t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < d; i += 256) sh[i] = hidden[t * d + i];
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    sh[i] = hidden[t * d + i];
+    ss += sh[i] * sh[i];
+  }
+  if (ln) {
+    ss = wave_sum(ss);
+    if (lane == 0) sPart[wave] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) sR = 1.f / sqrtf(((sPart[0] + sPart[1]) + (sPart[2] + sPart[3])) / (float)d + ln_eps);
+    __syncthreads();
+    const float r = sR;
+    for (int i = threadIdx.x; i < d; i += 256) sh[i] = sh[i] * r * (ln_w ? ln_w[i] : 1.f);
+  }
   __syncthreads();
   float part = 0.f;
   for (int k = wave; k < d_ff; k += 4) {
@@ -275,34 +344,32 @@ __global__ __launch_bounds__(256) void gate_score_f32_kernel(
   }
 }
 
-hipError_t launch_gate_pack_w1(const void *w1, int d, int d_ff, void *packed, hipStream_t s) {
+hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s) {
   const int nkk = gate_nkk(d);
   hipLaunchKernelGGL(gate_pack_w1_kernel, dim3((unsigned)((nkk + 7) / 8), (unsigned)gate_ngp(d_ff)), dim3(256), 0, s,
-                     (const uint16_t *)w1, d, d_ff, nkk, (uint16_t *)packed);
+                     (const uint16_t *)w1, (const uint16_t *)ln_w, d, d_ff, nkk, (uint16_t *)packed);
   return hipGetLastError();
 }
 
-// bf16: w1 is the packed copy (gate_pack_w1_kernel); f32: natural layout.
+// bf16: w1 is the packed copy (gate_pack_w1_kernel, with the RMSNorm weight
+// folded in when ln); f32: natural layout, ln_w applied in the kernel.
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2,
-                             const uint8_t *forced, int64_t T, int d, int d_ff, bool bf16,
-                             float *scores, float *gates, hipStream_t s) {
+                             const uint8_t *forced, int64_t T, int d, int d_ff, bool bf16, bool ln,
+                             const void *ln_w, float ln_eps, float *scores, float *gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16) {
     const int nkk = gate_nkk(d);
     // 128-token tiles when they still fill the 256 compute units, else 64
-    if ((T + 127) / 128 >= 256) {
-      hipLaunchKernelGGL(gate_score_bf16_kernel<4>, dim3((unsigned)((T + 127) / 128)), dim3(64 * GS_W), 0, s,
-                         (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff,
-                         nkk, scores, gates);
-    } else {
-      hipLaunchKernelGGL(gate_score_bf16_kernel<2>, dim3((unsigned)((T + 63) / 64)), dim3(64 * GS_W), 0, s,
-                         (const uint16_t *)hidden, (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff,
-                         nkk, scores, gates);
-    }
+    const bool big = (T + 127) / 128 >= 256;
+    auto k = big ? (ln ? gate_score_bf16_kernel<4, true> : gate_score_bf16_kernel<4, false>)
+                 : (ln ? gate_score_bf16_kernel<2, true> : gate_score_bf16_kernel<2, false>);
+    const int tt = big ? 128 : 64;
+    hipLaunchKernelGGL(k, dim3((unsigned)((T + tt - 1) / tt)), dim3(64 * GS_W), 0, s, (const uint16_t *)hidden,
+                       (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff, nkk, ln_eps, scores, gates);
   } else {
     hipLaunchKernelGGL(gate_score_f32_kernel, dim3((unsigned)T), dim3(256), (size_t)d * sizeof(float), s,
                        (const float *)hidden, (const float *)w1, (const float *)w2, forced, T, d, d_ff,
-                       scores, gates);
+                       (const float *)ln_w, ln_eps, ln, scores, gates);
   }
   return hipGetLastError();
 }

@@ -128,6 +128,21 @@ def gate_inputs(w: Workload, N: int | None = None):
     return dict(hidden=_store(h, w.dtype), w1=_store(w1, w.dtype), w2=_store(w2, w.dtype), forced=f)
 
 
+def residual_inputs(w: Workload, N: int | None = None):
+    """Raw post-attention residual rows and an RMSNorm weight, for the scorer with LN2 in front.
+
+    hidden [B, N, d]: N(0,1) rows, each scaled by exp(U(ln 1/4, ln 4)) (token norms spread over
+    a factor of 16, the spread the normalisation removes), stored bf16 (or fp32); ln_w [d] ~
+    U(0.5, 1.5) in the same storage type.  The scorer weights are gate_inputs' (same seed).
+    """
+    N = w.N if N is None else N
+    rs = _streams(w.seed + 2000, ["hidden", "scale", "ln_w"])
+    h = rs["hidden"].standard_normal((w.B, N, w.d), dtype=np.float32)
+    h *= np.exp(rs["scale"].uniform(np.log(0.25), np.log(4.0), (w.B, N, 1))).astype(np.float32)
+    lw = rs["ln_w"].uniform(0.5, 1.5, w.d).astype(np.float32)
+    return dict(hidden=_store(h, w.dtype), ln_w=_store(lw, w.dtype))
+
+
 def clustered_scores(w: Workload, N: int | None = None, frac: float = 0.05) -> np.ndarray:
     """float32 [B, N] selection scores with relevant spans.
 

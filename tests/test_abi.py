@@ -124,3 +124,39 @@ def test_attn_validation():
     assert b(*bargs(sigma=FAKE)) == 1            # sigma without dsigma
     assert b(*bargs(dsigma=FAKE)) == 1           # dsigma without sigma
     assert b(*bargs(sigma=FAKE, dsigma=MIS)) == 1
+
+
+def test_norm_gate_validation():
+    lib = _lib()
+    # tg_gate_score_ln: (hidden, ln_w, ln_eps, w1, w2, forced, B, N, d, d_ff, dt, scores, gates, ws, ws_bytes, stream)
+    f = lib.tg_gate_score_ln
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(FAKE, None, -1.0, FAKE, FAKE, None, 1, 10, 64, 16, 1, FAKE, None, FAKE, 1 << 30, None) == 1  # eps < 0
+    assert f(FAKE, None, float("nan"), FAKE, FAKE, None, 1, 10, 64, 16, 1, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert f(FAKE, MIS, 1e-6, FAKE, FAKE, None, 1, 10, 64, 16, 1, FAKE, None, FAKE, 1 << 30, None) == 1  # ln_w
+    assert f(FAKE, None, 1e-6, FAKE, FAKE, None, 1, 10, 64, 16, 1, FAKE, None, FAKE, 16, None) == 3  # workspace
+    assert f(FAKE, None, 1e-6, FAKE, FAKE, None, 1, 10, 48, 16, 1, FAKE, None, FAKE, 1 << 30, None) == 2  # d % 32
+    n = lib.tg_score_normalize
+    n.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert n(None, None, 1, 10, 1e-6, FAKE, None) == 1
+    assert n(FAKE, None, 1, 10, -1.0, FAKE, None) == 1
+    assert n(FAKE, None, -1, 10, 1e-6, FAKE, None) == 1
+    assert n(FAKE, None, 1, (1 << 24) + 1, 1e-6, FAKE, None) == 2
+    assert n(FAKE, None, 1, 10, 1e-6, MIS, None) == 1
+    assert n(FAKE, None, 0, 10, 1e-6, FAKE, None) == 0  # empty: nothing launched
+    s = lib.tg_gate_softmax
+    s.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert s(None, None, 1, 10, FAKE, None) == 1
+    assert s(FAKE, MIS, 1, 10, FAKE, None) == 1
+    assert s(FAKE, None, 1, -2, FAKE, None) == 1
+    assert s(FAKE, None, 1, 0, FAKE, None) == 0
+    sb = lib.tg_gate_softmax_bwd
+    sb.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    assert sb(FAKE, None, 1, 10, FAKE, None) == 1
+    assert sb(FAKE, FAKE, 1, 10, MIS, None) == 1
+    assert sb(FAKE, FAKE, 0, 10, FAKE, None) == 0
