@@ -19,8 +19,12 @@ events recorded on the launch stream inside the timed region.
 
 Also measured in the same run (not part of `value`): the attention with the
 pruning-ratio temperature (the deep dive's operative rule, section 3.2 Eq. 7/8)
-on the same inputs, the training-path attention (forward + backward at batch
-4, 2048 kept tokens) with and without that temperature, and the CPU oracle on
+on the same inputs; the operative scoring path on the same workload (section 2
+Eq. 1 and sections 3.1-3.2 Eqs. 3-8: the scorer on the raw residual with the
+RMSNorm in front, the sequence RMS normalisation, selection, compaction, the
+softmax-over-S gate and the attention with the per-head gain and the
+temperature); the training-path attention (forward + backward at batch 4,
+2048 kept tokens) with and without that temperature, and the CPU oracle on
 the same workload, timed on this host's cores.
 """
 from __future__ import annotations
@@ -146,6 +150,7 @@ def run_gpu(args):
         tg.tg_gated_attn_fwd(q, k, v, gk, gamma, pk, wl.ROPE_THETA, w.tau, o, lse, ws, sigma=sigma)
 
     temp_us = time_loop(attn_temp, args.steps, stream) * 1e6
+    operative = run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M)
 
     work = algorithmic_work(w, M)
     kern = {}
@@ -181,7 +186,7 @@ def run_gpu(args):
 
     elapsed = wall
     res = dict(elapsed=elapsed, step_dev=float(np.mean(step_dev)), kernels=kern, summary=summary, roofline=roof,
-               workload=w, K=K, M=M)
+               workload=w, K=K, M=M, operative=operative)
     if args.copy_calib_mb:
         nb = args.copy_calib_mb << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
@@ -211,6 +216,69 @@ def time_loop(fn, n, stream):
         b.record(stream)
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+
+def run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M):
+    """The operative scoring path on the long-context workload, one HIP stream, per-stage events.
+
+    Raw residual rows (three rotating copies, as in the main loop) -> tg_gate_score_ln (RMSNorm
+    weight folded into W1 by its pack pass, then the scorer) -> tg_score_normalize -> tg_select_topk
+    -> tg_compact (of the normalised scores) -> tg_gate_softmax -> tg_gated_attn_fwd with the
+    per-head gain and the Eq. 7/8 temperature.  Selection ranks the drawn clustered score vector
+    after the same normalisation (as the main path ranks the drawn vector).
+    """
+    import torch
+
+    ri = wl.residual_inputs(w)
+    T = lambda x: wl.to_torch(x, w.dtype, dev)
+    hs = [T(ri["hidden"])]
+    hs += [hs[0].clone() for _ in range(NCOPY - 1)]
+    lw, w1, w2 = T(ri["ln_w"]), T(gi["w1"]), T(gi["w2"])
+    forced = torch.from_numpy(gi["forced"]).to(dev)
+    sel_t = torch.from_numpy(sel).to(dev)
+    q, k, v = T(at["q"]), T(at["k"]), T(at["v"])
+    gain = torch.from_numpy(np.log1p(np.exp(at["gamma"])).astype(np.float32)).to(dev)
+    sigma = torch.from_numpy(at["sigma"]).to(dev)
+    raw = torch.empty((w.B, w.N), device=dev)
+    bsel = torch.empty((w.B, w.N), device=dev)
+    kept = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+    hk = torch.empty((w.B, M, w.d), dtype=hs[0].dtype, device=dev)
+    pk = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+    bk = torch.empty((w.B, M), device=dev)
+    g = torch.empty((w.B, M), device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, M), device=dev)
+    ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
+    gws = tg.gate_workspace(w.d, w.d_ff, hs[0].dtype, dev)
+    names = ["gate_score_ln", "score_normalize", "select_topk", "compact", "gate_softmax", "attn_fwd_temperature"]
+
+    def step(i, ev=None):
+        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        rec(0)
+        tg.tg_gate_score_ln(hs[i % NCOPY], lw, 1e-6, w1, w2, forced, raw, None, gws)
+        rec(1)
+        tg.tg_score_normalize(sel_t, forced, 1e-6, bsel)
+        rec(2)
+        tg.tg_select_topk(bsel, forced, K, w.n_forced, kept)
+        rec(3)
+        tg.tg_compact(hs[i % NCOPY], None, bsel, kept, hk, pk, bk)
+        rec(4)
+        tg.tg_gate_softmax(bk, kept, g)
+        rec(5)
+        tg.tg_gated_attn_fwd(q, k, v, g, gain, pk, wl.ROPE_THETA, w.tau, o, lse, ws, sigma=sigma)
+        rec(6)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    for i, e in enumerate(evs):
+        step(i, e)
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j, n in enumerate(names)}
+    tot = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])) * 1e-3
+    return dict(stages_us=per, device_path_us=tot * 1e6, tokens_per_s=w.B * w.N / tot,
+                note="gate_score_ln includes its W1 pack pass (RMSNorm weight folded in)")
 
 
 def run_train(args, tg, wl, dev):
@@ -372,6 +440,7 @@ def main():
         "device_path_us": res["step_dev"] * 1e6,
         "kernels": res["kernels"],
         "summary": res["summary"],
+        "operative_path": res["operative"],
     }
     if "training_path" in res:
         line["training_path"] = res["training_path"]

@@ -143,7 +143,8 @@ tg_status tg_gate_score_ln(const void *hidden, const void *ln_w, float ln_eps, c
  * by tg_compact, tg_gate_softmax.
  *   scores [B, N] f32; forced_keep [B, N] u8 or NULL (every position prunable);
  *   out [B, N] f32 (may equal scores: in place); eps finite >= 0; N <= 2^24.
- * fp32 arithmetic, fixed-order reductions (deterministic).
+ * fp32 arithmetic (out_j = s_j times the fp32 reciprocal of the root, within
+ * an ulp of the quotient), fixed-order reductions (deterministic).
  */
 tg_status tg_score_normalize(const float *scores, const uint8_t *forced_keep, int64_t B,
                              int64_t N, float eps, float *out, void *stream);

@@ -14,11 +14,10 @@
 //     so the attention bias gamma_h ln g_j with gamma_h = c_h gives Eq. 6 up to a
 //     per-head constant that the attention softmax removes.)
 //
-// Each is one work-group of 1024 threads per row (a row is a few thousand to a
-// few hundred thousand values, streamed twice: once for the reduction, once
-// for the output), with fixed-shape reductions (bitwise deterministic).  These
-// are latency-bound passes; they keep the whole scoring definition on the
-// device without a host round trip.  The normalisation may run in place.
+// Each is one work-group of 1024 threads per row with fixed-shape reductions
+// (bitwise deterministic).  These are latency-bound passes; they keep the
+// whole scoring definition on the device without a host round trip.  The
+// normalisation may run in place.
 #include "tg_common.h"
 
 namespace tg {
@@ -43,76 +42,210 @@ __device__ __forceinline__ float block_reduce(float v, float *red) {
   return r;
 }
 
+// Rows are read in chunks of SN_R values per thread (SN_T SN_R per chunk): all of
+// a chunk's loads are issued before any is used, so a pass costs one memory
+// latency per chunk rather than one per value.  A row of at most one chunk
+// (32 K values) stays in registers between the passes.
+constexpr int SN_R = 32;
+constexpr int64_t SN_CHUNK = (int64_t)SN_T * SN_R;
+
+// Element u of a thread's chunk is row index idx(u) = base + V (SN_T (u / V) + tid) + u % V:
+// with V = 4 (rows whose length is a multiple of 4, so 16-byte aligned) a thread
+// loads 4 consecutive values per instruction, with V = 1 one.  Group u / V is
+// live for some thread iff base + V SN_T (u / V) < n, a work-group-uniform test,
+// so empty groups cost a scalar branch.
+template <int V>
+__device__ __forceinline__ int64_t elem(int64_t base, int u) {
+  return base + (int64_t)V * ((int64_t)SN_T * (u / V) + threadIdx.x) + u % V;
+}
+template <int V>
+__device__ __forceinline__ bool slot_live(int64_t base, int u, int64_t n) {
+  return base + (int64_t)V * SN_T * (u / V) < n;
+}
+
+template <int V, typename T>
+__device__ __forceinline__ void load_chunk(const T *row, int64_t base, int64_t n, T fill, T (&x)[SN_R]) {
+#pragma unroll
+  for (int u = 0; u < SN_R; u += V) {
+    const int64_t j = elem<V>(base, u);
+#pragma unroll
+    for (int e = 0; e < V; ++e) x[u + e] = fill;
+    if (slot_live<V>(base, u, n) && j < n) {
+      if constexpr (V == 4) {  // n % 4 == 0: the whole group is in range
+        if constexpr (sizeof(T) == 4) {
+          const uint4 w = *(const uint4 *)(row + j);
+          x[u] = __builtin_bit_cast(T, w.x);
+          x[u + 1] = __builtin_bit_cast(T, w.y);
+          x[u + 2] = __builtin_bit_cast(T, w.z);
+          x[u + 3] = __builtin_bit_cast(T, w.w);
+        } else {
+          const uint32_t w = *(const uint32_t *)(row + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[u + e] = (T)((w >> (8 * e)) & 0xFFu);
+        }
+      } else {
+        x[u] = row[j];
+      }
+    }
+  }
+}
+
+template <int V>
 __global__ __launch_bounds__(SN_T) void score_normalize_kernel(const float *s, const uint8_t *__restrict__ forced,
                                                               int64_t N, float eps, float *out) {
   __shared__ float red[SN_T / 64];
   const int64_t b = blockIdx.x;
   const float *row = s + b * N;
   const uint8_t *f = forced ? forced + b * N : nullptr;
-  float ss = 0.f, np = 0.f;  // np counts exactly in fp32 up to 2^24 positions per thread
-  for (int64_t j = threadIdx.x; j < N; j += SN_T) {
-    const bool p = !(f && f[j]);
-    const float x = row[j];
-    if (p) {
-      ss = __builtin_fmaf(x, x, ss);
-      np += 1.f;
+  float x[SN_R];
+  uint8_t fx[SN_R];
+  float ss = 0.f, np = 0.f;  // np: exact in fp32 (at most 2^24 positions per row)
+  for (int64_t base = 0; base < N; base += SN_CHUNK) {
+    load_chunk<V>(row, base, N, 0.f, x);
+    if (f) load_chunk<V>(f, base, N, (uint8_t)1, fx);
+#pragma unroll
+    for (int u = 0; u < SN_R; ++u) {
+      if (!slot_live<V>(base, u, N)) break;
+      const bool p = f ? fx[u] == 0 : elem<V>(base, u) < N;
+      if (p) {
+        ss = __builtin_fmaf(x[u], x[u], ss);
+        np += 1.f;
+      }
     }
   }
   const float tot = block_reduce<false>(ss, red);
   const float cnt = block_reduce<false>(np, red);
   const float r = cnt > 0.f ? sqrtf(tot / cnt + eps) : 1.f;
-  for (int64_t j = threadIdx.x; j < N; j += SN_T) {
-    const bool p = !(f && f[j]);
-    out[b * N + j] = p ? row[j] / r : 0.f;
+  const float rinv = 1.f / r;  // x * (1 / r): within an ulp of x / r
+  for (int64_t base = 0; base < N; base += SN_CHUNK) {
+    if (N > SN_CHUNK) {  // the row did not stay in registers
+      load_chunk<V>(row, base, N, 0.f, x);
+      if (f) load_chunk<V>(f, base, N, (uint8_t)1, fx);
+    }
+#pragma unroll
+    for (int u = 0; u < SN_R; u += V) {
+      if (!slot_live<V>(base, u, N)) break;
+      const int64_t j = elem<V>(base, u);
+      if (j >= N) continue;
+      float y[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) y[e] = (f && fx[u + e]) ? 0.f : x[u + e] * rinv;
+      if constexpr (V == 4)
+        *(float4 *)(out + b * N + j) = make_float4(y[0], y[1], y[2], y[3]);
+      else
+        out[b * N + j] = y[0];
+    }
   }
 }
 
-__global__ __launch_bounds__(SN_T) void gate_softmax_kernel(const float *__restrict__ x, const int32_t *__restrict__ kept,
-                                                           int64_t M, float *__restrict__ g) {
+template <int V>
+__global__ __launch_bounds__(SN_T) void gate_softmax_kernel(const float *__restrict__ xin,
+                                                           const int32_t *__restrict__ kept, int64_t M,
+                                                           float *__restrict__ g) {
   __shared__ float red[SN_T / 64];
   const int64_t b = blockIdx.x;
-  const float *row = x + b * M;
+  const float *row = xin + b * M;
   const int32_t *k = kept ? kept + b * M : nullptr;
+  float x[SN_R];
+  int32_t kx[SN_R];
+  auto load = [&](int64_t base) __attribute__((always_inline)) {
+    load_chunk<V>(row, base, M, -INFINITY, x);
+    if (k) {
+      load_chunk<V>(k, base, M, (int32_t)-1, kx);
+#pragma unroll
+      for (int u = 0; u < SN_R; ++u)
+        if (kx[u] < 0) x[u] = -INFINITY;  // padding: not in S
+    }
+  };
   float mx = -INFINITY;
-  for (int64_t j = threadIdx.x; j < M; j += SN_T)
-    if (!(k && k[j] < 0)) mx = fmaxf(mx, row[j]);
+  for (int64_t base = 0; base < M; base += SN_CHUNK) {
+    load(base);
+#pragma unroll
+    for (int u = 0; u < SN_R; ++u) {
+      if (!slot_live<V>(base, u, M)) break;
+      mx = fmaxf(mx, x[u]);
+    }
+  }
   mx = block_reduce<true>(mx, red);
   float z = 0.f;
-  for (int64_t j = threadIdx.x; j < M; j += SN_T)
-    if (!(k && k[j] < 0)) z += expf(row[j] - mx);
+  for (int64_t base = 0; base < M; base += SN_CHUNK) {
+    if (M > SN_CHUNK) load(base);
+#pragma unroll
+    for (int u = 0; u < SN_R; ++u) {
+      if (!slot_live<V>(base, u, M)) break;
+      z += x[u] == -INFINITY ? 0.f : expf(x[u] - mx);
+    }
+  }
   z = block_reduce<false>(z, red);
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  for (int64_t j = threadIdx.x; j < M; j += SN_T)
-    g[b * M + j] = (k && k[j] < 0) ? 0.f : expf(row[j] - mx) * inv;
+  for (int64_t base = 0; base < M; base += SN_CHUNK) {
+    if (M > SN_CHUNK) load(base);
+#pragma unroll
+    for (int u = 0; u < SN_R; ++u) {
+      if (!slot_live<V>(base, u, M)) break;
+      const int64_t j = elem<V>(base, u);
+      if (j < M) g[b * M + j] = x[u] == -INFINITY ? 0.f : expf(x[u] - mx) * inv;
+    }
+  }
 }
 
 // db_j = g_j (dg_j - sum_k g_k dg_k)
+template <int V>
 __global__ __launch_bounds__(SN_T) void gate_softmax_bwd_kernel(const float *__restrict__ g, const float *__restrict__ dg,
                                                                int64_t M, float *__restrict__ db) {
   __shared__ float red[SN_T / 64];
   const int64_t b = blockIdx.x;
+  float gx[SN_R], dx[SN_R];
   float dot = 0.f;
-  for (int64_t j = threadIdx.x; j < M; j += SN_T) dot = __builtin_fmaf(g[b * M + j], dg[b * M + j], dot);
+  for (int64_t base = 0; base < M; base += SN_CHUNK) {
+    load_chunk<V>(g + b * M, base, M, 0.f, gx);
+    load_chunk<V>(dg + b * M, base, M, 0.f, dx);
+#pragma unroll
+    for (int u = 0; u < SN_R; ++u) {
+      if (!slot_live<V>(base, u, M)) break;
+      dot = __builtin_fmaf(gx[u], dx[u], dot);
+    }
+  }
   dot = block_reduce<false>(dot, red);
-  for (int64_t j = threadIdx.x; j < M; j += SN_T) db[b * M + j] = g[b * M + j] * (dg[b * M + j] - dot);
+  for (int64_t base = 0; base < M; base += SN_CHUNK) {
+    if (M > SN_CHUNK) {
+      load_chunk<V>(g + b * M, base, M, 0.f, gx);
+      load_chunk<V>(dg + b * M, base, M, 0.f, dx);
+    }
+#pragma unroll
+    for (int u = 0; u < SN_R; ++u) {
+      if (!slot_live<V>(base, u, M)) break;
+      const int64_t j = elem<V>(base, u);
+      if (j < M) db[b * M + j] = gx[u] * (dx[u] - dot);
+    }
+  }
 }
 
 hipError_t launch_score_normalize(const float *s, const uint8_t *forced, int64_t B, int64_t N, float eps, float *out,
                                   hipStream_t st) {
   if (B * N == 0) return hipSuccess;
-  hipLaunchKernelGGL(score_normalize_kernel, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, out);
+  if (N % 4 == 0)
+    hipLaunchKernelGGL(score_normalize_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, out);
+  else
+    hipLaunchKernelGGL(score_normalize_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, out);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_softmax(const float *x, const int32_t *kept, int64_t B, int64_t M, float *g, hipStream_t st) {
   if (B * M == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_softmax_kernel, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, g);
+  if (M % 4 == 0)
+    hipLaunchKernelGGL(gate_softmax_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, g);
+  else
+    hipLaunchKernelGGL(gate_softmax_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db, hipStream_t st) {
   if (B * M == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_softmax_bwd_kernel, dim3((unsigned)B), dim3(SN_T), 0, st, g, dg, M, db);
+  if (M % 4 == 0)
+    hipLaunchKernelGGL(gate_softmax_bwd_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, g, dg, M, db);
+  else
+    hipLaunchKernelGGL(gate_softmax_bwd_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, g, dg, M, db);
   return hipGetLastError();
 }
 
