@@ -311,6 +311,67 @@ def attn_bwd(q, k, v, g, gamma, dout, pos=None, theta=1e6, tau=1.0, round_bf16=F
     return dq, dk, dv, dg, dgamma, dsigma
 
 
+def _runs(cu_seqlens):
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    assert cu[0] == 0 and np.all(np.diff(cu) >= 0)
+    return cu
+
+
+def attn_fwd_varlen(q, k, v, g, gamma, cu_seqlens, pos=None, theta=1e6, tau=1.0, round_bf16=False, sigma=None):
+    """Token-gated attention over packed sequences (the training path packs both budgets in one call:
+    DeepDive section 3.3): sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends
+    causally within itself only, exactly as attn_fwd on that sequence alone (row index i and the
+    temperature's m_i = i + 1 count from the sequence start).
+
+    q [T, Hq, D]; k, v [T, Hkv, D]; g [T]; pos int32 [T] or None.  Returns (o [T, Hq, D], lse [Hq * T]),
+    lse holding sequence s's [Hq, M_s] block at offset Hq * cu_seqlens[s].
+    """
+    cu = _runs(cu_seqlens)
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    T, Hq, D = Q.shape
+    o = np.full((T, Hq, D), np.nan)
+    lse = np.full(Hq * T, np.nan)
+    G = _f64(g).reshape(T)
+    P = None if pos is None else np.asarray(pos, dtype=np.int32).reshape(T)
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        os_, ls = attn_fwd(Q[None, a:e], K[None, a:e], V[None, a:e], G[None, a:e], gamma,
+                           pos=None if P is None else P[None, a:e], theta=theta, tau=tau, round_bf16=round_bf16,
+                           sigma=sigma)
+        o[a:e] = os_[0]
+        lse[Hq * a:Hq * e] = ls.reshape(-1)
+    return o, lse
+
+
+def attn_bwd_varlen(q, k, v, g, gamma, dout, cu_seqlens, pos=None, theta=1e6, tau=1.0, round_bf16=False,
+                    sigma=None):
+    """Gradients of attn_fwd_varlen: dq, dk, dv, dg per token; dgamma (and dsigma) summed over sequences."""
+    cu = _runs(cu_seqlens)
+    Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
+    T, Hq, D = Q.shape
+    Hkv = K.shape[1]
+    G = _f64(g).reshape(T)
+    P = None if pos is None else np.asarray(pos, dtype=np.int32).reshape(T)
+    dq, dk, dv, dg = np.zeros((T, Hq, D)), np.zeros((T, Hkv, D)), np.zeros((T, Hkv, D)), np.zeros(T)
+    dgamma, dsigma = np.zeros(Hq), np.zeros(Hq)
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        r = attn_bwd(Q[None, a:e], K[None, a:e], V[None, a:e], G[None, a:e], gamma, dO[None, a:e],
+                     pos=None if P is None else P[None, a:e], theta=theta, tau=tau, round_bf16=round_bf16,
+                     sigma=sigma)
+        dq[a:e], dk[a:e], dv[a:e], dg[a:e] = r[0][0], r[1][0], r[2][0], r[3][0]
+        dgamma += r[4]
+        if sigma is not None:
+            dsigma += r[5]
+    if sigma is None:
+        return dq, dk, dv, dg, dgamma
+    return dq, dk, dv, dg, dgamma, dsigma
+
+
 def round_bf16(x: float) -> float:
     """The oracle's fp64 -> bf16 round-to-nearest-even (exposed for its pin tests)."""
     return _load().tgo_round_bf16(float(x))

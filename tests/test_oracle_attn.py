@@ -346,3 +346,84 @@ def test_temp_bwd_finite_differences(oracle_mod):
         assert abs(fd - grads[5][j]) < 1e-6 * max(1.0, abs(fd)), (j, fd, grads[5][j])
     # dg under the temperature: sum_j g_j dg_j = 0 still holds (each row's softmax is shift-free)
     np.testing.assert_allclose((g * grads[3]).sum(axis=1), 0.0, atol=1e-11)
+
+
+# --- packed variable-length sequences (the training path packs both budgets in one call) ---
+
+def _sdpa_varlen_ref(q, k, v, g, gamma, cu, tau, pos=None, theta=1e6, sigma=None):
+    """fp64 SDPA over all packed tokens as one sequence, with a mask that is causal inside each
+    sequence and -inf across sequences; the temperature's m_i counts from the sequence start."""
+    T_, Hq, D = q.shape
+    grp = Hq // k.shape[1]
+    seg = torch.from_numpy(np.repeat(np.arange(len(cu) - 1), np.diff(cu)))
+    idx = torch.arange(T_) - torch.from_numpy(np.asarray(cu[:-1]))[seg]
+    if pos is not None:
+        q = _rope_complex(q[None], pos[None], theta)[0]
+        k = _rope_complex(k[None], pos[None], theta)[0]
+    t = torch.ones(T_, Hq, dtype=torch.float64)
+    if sigma is not None:
+        p = (pos.to(torch.float64) if pos is not None else idx.to(torch.float64)) + 1.0
+        ratio = torch.log(idx.to(torch.float64) + 1.0) / torch.log(torch.clamp(p, min=2.0))
+        t = torch.nn.functional.softplus(sigma)[None, :] * ratio[:, None]
+    qh = (q * t[..., None] / (math.sqrt(D) * tau)).permute(1, 0, 2)[None]
+    kh = k.repeat_interleave(grp, dim=1).permute(1, 0, 2)[None]
+    vh = v.repeat_interleave(grp, dim=1).permute(1, 0, 2)[None]
+    allowed = (seg[:, None] == seg[None, :]) & (torch.arange(T_)[None, :] <= torch.arange(T_)[:, None])
+    bias = t.permute(1, 0)[:, :, None] * gamma[:, None, None] * torch.log(g)[None, None, :]
+    mask = torch.where(allowed[None], bias, torch.tensor(float("-inf"), dtype=torch.float64))[None]
+    o = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=1.0)
+    return o[0].permute(1, 0, 2)
+
+
+def _varlen_inputs(seed, lens, Hq=4, Hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    T_ = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = rng.standard_normal((T_, Hq, D))
+    k = rng.standard_normal((T_, Hkv, D))
+    v = rng.standard_normal((T_, Hkv, D))
+    g = 1.0 / (1.0 + np.exp(-rng.standard_normal(T_)))
+    gamma = rng.uniform(0.5, 1.5, Hq)
+    pos = np.concatenate([np.sort(rng.choice(200, n, replace=False)) for n in lens]).astype(np.int32)
+    sigma = rng.normal(0.0, 1.0, Hq)
+    return q, k, v, g, gamma, cu, pos, sigma
+
+
+@pytest.mark.parametrize("rope", [False, True])
+@pytest.mark.parametrize("temp", [False, True])
+def test_varlen_matches_blockdiag_sdpa(oracle_mod, rope, temp):
+    lens = [5, 0, 9, 1, 7]
+    q, k, v, g, gamma, cu, pos, sigma = _varlen_inputs(51, lens)
+    p = pos if rope else None
+    o, lse = oracle_mod.attn_fwd_varlen(q, k, v, g, gamma, cu, pos=p, theta=300.0, tau=1.2,
+                                        sigma=sigma if temp else None)
+    ref = _sdpa_varlen_ref(T(q), T(k), T(v), T(g), T(gamma), cu, 1.2, torch.from_numpy(pos) if rope else None,
+                           300.0, T(sigma) if temp else None)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=1e-11, atol=1e-12)
+    assert lse.shape == (4 * sum(lens),) and np.all(np.isfinite(lse))
+
+
+def test_varlen_equal_lengths_is_the_batch(oracle_mod):
+    q, k, v, g, gamma, pos = _inputs(52, 3, 11, 4, 2, 8)
+    cu = np.arange(4) * 11
+    o, lse = oracle_mod.attn_fwd_varlen(q.reshape(33, 4, 8), k.reshape(33, 2, 8), v.reshape(33, 2, 8), g.reshape(-1),
+                                        gamma, cu, pos=pos.reshape(-1), theta=400.0)
+    ob, lb = oracle_mod.attn_fwd(q, k, v, g, gamma, pos=pos, theta=400.0)
+    np.testing.assert_allclose(o.reshape(3, 11, 4, 8), ob, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse.reshape(3, 4, 11), lb, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("temp", [False, True])
+def test_varlen_bwd_matches_autograd(oracle_mod, temp):
+    lens = [6, 0, 4, 9]
+    q, k, v, g, gamma, cu, pos, sigma = _varlen_inputs(53, lens)
+    dout = np.random.default_rng(54).standard_normal(q.shape)
+    got = oracle_mod.attn_bwd_varlen(q, k, v, g, gamma, dout, cu, pos=pos, theta=250.0, tau=0.8,
+                                     sigma=sigma if temp else None)
+    leaves = [T(a).requires_grad_() for a in (q, k, v, g, gamma, sigma)]
+    o = _sdpa_varlen_ref(*leaves[:5], cu, 0.8, torch.from_numpy(pos), 250.0, leaves[5] if temp else None)
+    (o * T(dout)).sum().backward()
+    n = 6 if temp else 5
+    assert len(got) == n
+    for a, ref in zip(got, leaves[:n]):
+        np.testing.assert_allclose(a, ref.grad.numpy(), rtol=1e-10, atol=1e-11)
