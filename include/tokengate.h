@@ -295,6 +295,44 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
                             float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
                             void *stream);
 
+/*
+ * Packed variable-length attention: the training path evaluates both budgets'
+ * targets in one call ([DeepDive] section 3.3), i.e. several sequences of
+ * different lengths packed back to back.  Sequence s holds tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends causally within itself only,
+ * exactly as tg_gated_attn_fwd / _bwd on that sequence alone (row index, and
+ * the temperature's m_i, counted from the sequence start; positions, if given,
+ * are the caller's per token).
+ *   cu_seqlens: HOST array of nseq + 1 int64 offsets, cu_seqlens[0] = 0,
+ *     non-decreasing (empty sequences allowed); T = cu_seqlens[nseq] tokens.
+ *   q [T, Hq, D], k, v [T, Hkv, D], o [T, Hq, D] (dt); g [T] f32; pos [T] i32
+ *     or NULL; sigma [Hq] or NULL (as in tg_gated_attn_fwd);
+ *   lse: Hq * T f32, sequence s's [Hq, M_s] block at offset Hq * cu_seqlens[s];
+ *   backward: dq [T, Hq, D], dk, dv [T, Hkv, D], dg [T] f32 per token; dgamma
+ *     (and dsigma) [Hq] summed over all sequences.
+ * Each maximal run of adjacent equal-length sequences (empty ones skipped) is
+ * one batched launch, so packing equal lengths next to each other (e.g. all
+ * rows of one budget, then all rows of the other) costs one launch per
+ * budget; the workspace (tg_gated_attn_varlen_workspace_size, 256-byte
+ * aligned) is reused by the runs in stream order.  Validation, dtypes and
+ * errors as the batched calls; dgamma / dsigma are summed in run order
+ * (deterministic).
+ */
+size_t tg_gated_attn_varlen_workspace_size(const int64_t *cu_seqlens, int64_t nseq, int64_t Hq,
+                                           int64_t Hkv, int64_t D, int bwd);
+tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, const float *g,
+                                   const float *gamma, const int32_t *pos, float rope_theta,
+                                   float tau, const float *sigma, const int64_t *cu_seqlens,
+                                   int64_t nseq, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
+                                   void *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, const float *g,
+                                   const float *gamma, const int32_t *pos, float rope_theta,
+                                   float tau, const float *sigma, const float *lse,
+                                   const void *dout, const int64_t *cu_seqlens, int64_t nseq,
+                                   int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq,
+                                   float *dk, float *dv, float *dg, float *dgamma, float *dsigma,
+                                   void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

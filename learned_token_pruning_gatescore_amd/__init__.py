@@ -22,6 +22,8 @@ The rest of the scoring definition (section 2 Eq. 1, section 3.1 Eq. 3, section 
   tg_score_normalize   sequence RMS normalisation over the prunable positions, 0 on forced ones
   tg_gate_softmax      gate values as the softmax of the normalised scores over the kept set
   tg_gate_softmax_bwd  its backward
+Packed variable-length sequences (section 3.3: both budgets in one call):
+  tg_gated_attn_fwd_varlen / tg_gated_attn_bwd_varlen
 """
 from __future__ import annotations
 
@@ -34,6 +36,8 @@ __all__ = [
     "tg_select_topk", "tg_compact", "tg_gated_attn_fwd", "tg_gated_attn_bwd",
     "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
     "tg_gate_score_ln", "tg_score_normalize", "tg_gate_softmax", "tg_gate_softmax_bwd",
+    "tg_gated_attn_varlen_workspace_size", "tg_gated_attn_fwd_varlen", "tg_gated_attn_bwd_varlen",
+    "attn_varlen_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +99,14 @@ def load():
     lib.tg_gate_softmax.argtypes = [P, P, i64, i64, P, P]
     lib.tg_gate_softmax_bwd.restype = c_int
     lib.tg_gate_softmax_bwd.argtypes = [P, P, i64, i64, P, P]
+    lib.tg_gated_attn_varlen_workspace_size.restype = sz
+    lib.tg_gated_attn_varlen_workspace_size.argtypes = [P, i64, i64, i64, i64, c_int]
+    lib.tg_gated_attn_fwd_varlen.restype = c_int
+    lib.tg_gated_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, f32, f32, P, P, i64, i64, i64, i64, c_int, P, P, P,
+                                             sz, P]
+    lib.tg_gated_attn_bwd_varlen.restype = c_int
+    lib.tg_gated_attn_bwd_varlen.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, P, i64, i64, i64, i64, c_int,
+                                             P, P, P, P, P, P, P, sz, P]
     lib.tg_gated_attn_workspace_size.restype = sz
     lib.tg_gated_attn_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     lib.tg_gated_attn_fwd.restype = c_int
@@ -281,6 +293,58 @@ def tg_gated_attn_bwd(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk
                                     float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), B, M, Hq, Hkv, D, _dt(q),
                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgamma), _ptr(dsigma), _ptr(ws),
                                     ws_bytes, _stream(stream)))
+
+
+def _cu_host(cu_seqlens):
+    """cu_seqlens as a host int64 array (list, NumPy or CPU tensor) and the pointer to pass."""
+    import numpy as np
+
+    if hasattr(cu_seqlens, "detach"):
+        if cu_seqlens.device.type != "cpu":
+            raise TokenGateError(1, "cu_seqlens must be a host (CPU) array")
+        cu_seqlens = cu_seqlens.detach().numpy()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).reshape(-1))
+    return cu, cu.ctypes.data_as(ctypes.c_void_p)
+
+
+def tg_gated_attn_varlen_workspace_size(cu_seqlens, Hq, Hkv, D, bwd) -> int:
+    cu, p = _cu_host(cu_seqlens)
+    return load().tg_gated_attn_varlen_workspace_size(p, cu.size - 1, Hq, Hkv, D, int(bool(bwd)))
+
+
+def attn_varlen_workspace(cu_seqlens, Hq, Hkv, D, bwd, device):
+    import torch
+
+    n = tg_gated_attn_varlen_workspace_size(cu_seqlens, Hq, Hkv, D, bwd)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, rope_theta, tau, cu_seqlens, o, lse=None, ws=None,
+                             stream=None, *, sigma=None):
+    """Packed sequences: q [T, Hq, D], k, v [T, Hkv, D]; g [T]; pos [T] or None; cu_seqlens host [nseq + 1].
+    Writes o [T, Hq, D] and lse (Hq * T, sequence s's [Hq, M_s] block at Hq * cu_seqlens[s])."""
+    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    cu, cp = _cu_host(cu_seqlens)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().tg_gated_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
+                                           float(rope_theta), float(tau), _ptr(sigma), cp, cu.size - 1, Hq, Hkv, D,
+                                           _dt(q), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tg_gated_attn_bwd_varlen(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, cu_seqlens, dq, dk, dv, dg, dgamma,
+                             ws, stream=None, *, sigma=None, dsigma=None):
+    """Gradients of tg_gated_attn_fwd_varlen (per token; dgamma, dsigma summed over the sequences)."""
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    cu, cp = _cu_host(cu_seqlens)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(load().tg_gated_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
+                                           float(rope_theta), float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), cp,
+                                           cu.size - 1, Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                           _ptr(dgamma), _ptr(dsigma), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma, tau, rope_theta=1.0e6,

@@ -888,6 +888,29 @@ __global__ __launch_bounds__(256) void dgamma_kernel(const float *__restrict__ p
   }
 }
 
+// Packed variable-length calls run one backward per run of equal-length
+// sequences, each leaving its dgamma (and dsigma) in part[r][0 .. Hq) (and
+// part[r][Hq .. 2 Hq)); this sums them in run order (deterministic).  With no
+// run at all it writes zeros.
+__global__ __launch_bounds__(256) void sum_runs_kernel(const float *__restrict__ part, int nruns, int Hq,
+                                                       float *__restrict__ dgamma, float *__restrict__ dsigma) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= Hq) return;
+  float a = 0.f, b = 0.f;
+  for (int r = 0; r < nruns; ++r) {
+    a += part[(int64_t)r * 2 * Hq + h];
+    b += part[(int64_t)r * 2 * Hq + Hq + h];
+  }
+  dgamma[h] = a;
+  if (dsigma) dsigma[h] = b;
+}
+
+hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, float *dsigma, hipStream_t s) {
+  hipLaunchKernelGGL(sum_runs_kernel, dim3((unsigned)((Hq + 255) / 256)), dim3(256), 0, s, part, nruns, Hq, dgamma,
+                     dsigma);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
                            const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk,

@@ -42,6 +42,8 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
                            const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk,
                            float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w, hipStream_t s);
 
+hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, float *dsigma, hipStream_t s);
+
 // softplus in fp32 (the temperature's positive scale)
 __device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(__expf(x)); }
 

@@ -160,3 +160,41 @@ def test_norm_gate_validation():
     assert sb(FAKE, None, 1, 10, FAKE, None) == 1
     assert sb(FAKE, FAKE, 1, 10, MIS, None) == 1
     assert sb(FAKE, FAKE, 0, 10, FAKE, None) == 0
+
+
+def test_varlen_validation():
+    lib = _lib()
+    i64 = ctypes.c_int64
+    ws = lib.tg_gated_attn_varlen_workspace_size
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, ctypes.c_int]
+    cu_t = ctypes.c_int64 * 5
+    good = cu_t(0, 100, 100, 200, 250)  # runs: (2 x 100), (1 x 50)
+    bad0 = cu_t(1, 100, 100, 200, 250)
+    desc = cu_t(0, 100, 90, 200, 250)
+    assert ws(good, 4, 16, 8, 128, 0) > 0
+    assert ws(good, 4, 16, 8, 128, 1) > ws(good, 4, 16, 8, 128, 0)
+    assert ws(bad0, 4, 16, 8, 128, 0) == 0 and ws(desc, 4, 16, 8, 128, 0) == 0 and ws(None, 4, 16, 8, 128, 0) == 0
+    # the workspace of the largest run: (2 sequences x 100 tokens) here
+    assert ws(good, 4, 16, 8, 128, 0) >= lib.tg_gated_attn_workspace_size(2, 100, 16, 8, 128, 0)
+    f = lib.tg_gated_attn_fwd_varlen
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, i64, i64,
+                                          i64, i64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
+    args = lambda cu, **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, cu, 4, kw.get("Hq", 16), 8,
+                             kw.get("D", 128), 1, FAKE, None, kw.get("ws", FAKE), kw.get("wsb", 16), None]
+    assert f(*args(None)) == 1                 # cu_seqlens required
+    assert f(*args(bad0)) == 1                 # cu_seqlens[0] != 0
+    assert f(*args(desc)) == 1                 # decreasing
+    assert f(*args(good, Hq=12)) == 1          # Hq % Hkv
+    assert f(*args(good, D=96)) == 2           # bf16 D
+    assert f(*args(good)) == 3                 # workspace too small
+    b = lib.tg_gated_attn_bwd_varlen
+    b.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 4 + [
+        i64, i64, i64, i64, ctypes.c_int] + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
+    bargs = lambda **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, kw.get("sigma", None), kw.get("lse", FAKE),
+                          FAKE, good, 4, 16, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("dsigma", None), FAKE,
+                          kw.get("wsb", 16), None]
+    assert b(*bargs(lse=None)) == 1
+    assert b(*bargs(sigma=FAKE)) == 1          # sigma without dsigma
+    assert b(*bargs()) == 3                    # workspace too small

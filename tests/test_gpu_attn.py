@@ -308,3 +308,82 @@ def test_temp_bwd_deterministic():
     torch.cuda.synchronize()
     for a, n in zip(first, names):
         assert torch.equal(a.view(torch.int32), r[n].view(torch.int32)), n
+
+
+# --- packed variable-length sequences (both training budgets in one call) ---
+
+def _varlen_case(lens, Hq, Hkv, D, dtype="bf16", seed=61, rope=True, temp=False, grad=False):
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    rng = np.random.default_rng(seed)
+    T_ = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    store = (lambda x: wl.bf16_bits(x)) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    a = dict(q=store(rng.standard_normal((T_, Hq, D), dtype=np.float32)),
+             k=store(rng.standard_normal((T_, Hkv, D), dtype=np.float32)),
+             v=store(rng.standard_normal((T_, Hkv, D), dtype=np.float32)),
+             dout=store(rng.standard_normal((T_, Hq, D), dtype=np.float32)),
+             g=(1.0 / (1.0 + np.exp(-rng.standard_normal(T_)))).astype(np.float32),
+             gamma=rng.uniform(0.5, 1.5, Hq).astype(np.float32),
+             pos=np.concatenate([np.sort(rng.choice(max(4 * n, 64), n, replace=False)) for n in lens]).astype(np.int32),
+             sigma=(0.54 + 0.5 * rng.standard_normal(Hq)).astype(np.float32))
+    dev = device()
+    q, k, v, dout = (dev_tensor(a[n], dtype, dev) for n in ("q", "k", "v", "dout"))
+    g, gamma = torch.from_numpy(a["g"]).to(dev), torch.from_numpy(a["gamma"]).to(dev)
+    pos = torch.from_numpy(a["pos"]).to(dev) if rope else None
+    sigma = torch.from_numpy(a["sigma"]).to(dev) if temp else None
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((Hq * T_,), float("nan"), device=dev)
+    ws = tg.attn_varlen_workspace(cu, Hq, Hkv, D, True, dev)
+    say("attn_fwd_varlen", dtype, lens, Hq, Hkv, D, "rope" if rope else "", "temp" if temp else "")
+    tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, 1.1, cu, o, lse, ws, sigma=sigma)
+    torch.cuda.synchronize()
+    f = lambda x: wl.as_float(x, dtype)
+    o_ref, l_ref = oracle.attn_fwd_varlen(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], cu,
+                                          pos=a["pos"] if rope else None, theta=wl.ROPE_THETA, tau=1.1,
+                                          round_bf16=(dtype == "bf16"), sigma=a["sigma"] if temp else None)
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    assert_maxabs(to_np(o), o_ref, tol, "o")
+    assert_maxabs(to_np(lse), l_ref, tol, "lse")
+    if not grad:
+        return
+    dq = torch.full(q.shape, float("nan"), device=dev)
+    dk = torch.full(k.shape, float("nan"), device=dev)
+    dv = torch.full(v.shape, float("nan"), device=dev)
+    dg = torch.full(g.shape, float("nan"), device=dev)
+    dgam = torch.full(gamma.shape, float("nan"), device=dev)
+    dsig = torch.full(gamma.shape, float("nan"), device=dev) if temp else None
+    say("attn_bwd_varlen", dtype, lens)
+    tg.tg_gated_attn_bwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, 1.1, lse, dout, cu, dq, dk, dv, dg, dgam, ws,
+                                sigma=sigma, dsigma=dsig)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd_varlen(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], f(a["dout"]), cu,
+                                 pos=a["pos"] if rope else None, theta=wl.ROPE_THETA, tau=1.1,
+                                 round_bf16=(dtype == "bf16"), sigma=a["sigma"] if temp else None)
+    got = (dq, dk, dv, dg, dgam) + ((dsig,) if temp else ())
+    for name, gt, rf in zip(("dq", "dk", "dv", "dg", "dgamma", "dsigma"), got, ref):
+        assert_maxabs(to_np(gt), rf, tol, name)
+
+
+# two budgets packed by budget (two runs), interleaved lengths (one run per sequence),
+# empty and one-token sequences, a single sequence
+@pytest.mark.parametrize("lens,Hq,Hkv,D", [([300, 300, 150, 150], 8, 4, 128), ([130, 70, 130, 70], 4, 2, 128),
+                                           ([0, 1, 257, 0, 257, 33], 8, 2, 64), ([517], 16, 8, 128)])
+def test_varlen_bf16(lens, Hq, Hkv, D):
+    _varlen_case(lens, Hq, Hkv, D, grad=True)
+
+
+@pytest.mark.parametrize("temp,rope", [(True, True), (True, False), (False, False)])
+def test_varlen_bf16_temperature_and_rope(temp, rope):
+    _varlen_case([200, 200, 96], 8, 4, 128, temp=temp, rope=rope, grad=True, seed=62)
+
+
+def test_varlen_f32():
+    _varlen_case([40, 40, 17, 0, 9], 6, 2, 32, dtype="f32", temp=True, grad=True, seed=63)
+
+
+def test_varlen_two_budgets_train_shape():
+    """Batch 4 at two budgets packed by budget: 4 x 2048 then 4 x 1024 kept tokens (sampled checks are
+    the full oracle here: 12288 tokens, 16 / 8 heads, D = 128)."""
+    _varlen_case([2048] * 4 + [1024] * 4, 16, 8, 128, temp=True, grad=True, seed=64)
