@@ -320,6 +320,7 @@ def run_train(args, tg, wl, dev):
 
     ff = 4.0 * w.B * w.Hq * w.D * M * (M + 1) / 2
     out = dict(workload=w.name, B=w.B, M=M)
+    out["two_budgets_packed"] = run_train_varlen(args, tg, wl, dev, w)
     for temp in (False, True):
         for _ in range(3):
             step(temp=temp)
@@ -337,6 +338,60 @@ def run_train(args, tg, wl, dev):
         else:
             out.update(r)
     return out
+
+
+def run_train_varlen(args, tg, wl, dev, w):
+    """Both training budgets in one packed call (DeepDive section 3.3): each of the B rows at its
+    full budget (M = 2048 kept) and at half of it (1024), packed by budget, forward + backward with
+    the Eq. 7/8 temperature (not part of `value`)."""
+    import torch
+
+    lens = [w.M_fixed] * w.B + [w.M_fixed // 2] * w.B
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T_ = int(cu[-1])
+    rs = np.random.default_rng(w.seed + 3000)
+    T = lambda x: wl.to_torch(x, w.dtype, dev)
+    q = T(wl.bf16_bits(rs.standard_normal((T_, w.Hq, w.D), dtype=np.float32)))
+    k = T(wl.bf16_bits(rs.standard_normal((T_, w.Hkv, w.D), dtype=np.float32)))
+    v = T(wl.bf16_bits(rs.standard_normal((T_, w.Hkv, w.D), dtype=np.float32)))
+    dout = T(wl.bf16_bits(rs.standard_normal((T_, w.Hq, w.D), dtype=np.float32)))
+    g = torch.from_numpy((1.0 / (1.0 + np.exp(-rs.standard_normal(T_)))).astype(np.float32)).to(dev)
+    gamma = torch.from_numpy(rs.uniform(0.5, 1.5, w.Hq).astype(np.float32)).to(dev)
+    pos = torch.from_numpy(np.concatenate([np.sort(rs.choice(w.N, n, replace=False)) for n in lens])
+                           .astype(np.int32)).to(dev)
+    sigma = torch.from_numpy((0.54 + 0.5 * rs.standard_normal(w.Hq)).astype(np.float32)).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.Hq * T_, device=dev)
+    dq, dk, dv = (torch.empty(x.shape, device=dev) for x in (q, k, v))
+    dg = torch.empty(T_, device=dev)
+    dgam, dsig = torch.empty(w.Hq, device=dev), torch.empty(w.Hq, device=dev)
+    ws = tg.attn_varlen_workspace(cu, w.Hq, w.Hkv, w.D, True, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, cu, o, lse, ws, sigma=sigma)
+        if ev:
+            ev[1].record(stream)
+        tg.tg_gated_attn_bwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, cu, dq, dk, dv, dg, dgam,
+                                    ws, sigma=sigma, dsigma=dsig)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.train_steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    ff = sum(4.0 * w.Hq * w.D * n * (n + 1) / 2 for n in lens)
+    return dict(lens=f"{w.B} x {w.M_fixed} + {w.B} x {w.M_fixed // 2}", tokens=T_, fwd_us=fwd * 1e6,
+                bwd_us=bwd * 1e6, fwd_mfma_frac=ff / fwd / PEAK_BF16, bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16,
+                tokens_per_s=T_ / (fwd + bwd))
 
 
 def load_traffic(kernel):
