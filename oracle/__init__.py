@@ -62,13 +62,14 @@ def _load():
     lib.tgo_compact.argtypes = [_U8, _I32, _F, _I32, _i64, _i64, _i64, _U8, _I32, _F]
     lib.tgo_compact.restype = None
     lib.tgo_attn_fwd.argtypes = [_D, _D, _D, _D, _D, _I32, ctypes.c_double, ctypes.c_double, _D,
-                                 _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _I64, _i64, _D, _D]
+                                 _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _I64, _i64, ctypes.c_int, _D, _D]
     lib.tgo_attn_fwd.restype = ctypes.c_int
     lib.tgo_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _I32, ctypes.c_double, ctypes.c_double, _D,
-                                 _D, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                 _D, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                  _D, _D, _D, _D, _D, _D]
     lib.tgo_attn_bwd.restype = ctypes.c_int
     lib.tgo_round_bf16.argtypes = [ctypes.c_double]
+    lib.tgo_gate_score_heads.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, _D]
     lib.tgo_gate_score_ln.argtypes = [_D, _D, ctypes.c_double, _D, _D, _U8, _i64, _i64, _i64, _D, _D]
     lib.tgo_score_normalize.argtypes = [_D, _U8, _i64, _i64, ctypes.c_double, _D]
     lib.tgo_gate_softmax.argtypes = [_D, _I32, _i64, _i64, _D]
@@ -137,6 +138,30 @@ def gate_score_ln(hidden, ln_w, eps, w1, w2, forced=None):
     lib.tgo_gate_score_ln(_ptr(h, _D), _ptr(lw, _D), float(eps), _ptr(W1, _D), _ptr(W2, _D), _ptr(f, _U8), T, d,
                           d_ff, _ptr(s, _D), _ptr(g, _D))
     return s, g
+
+
+def gate_score_heads(hidden, w1, w2):
+    """Per-head scores (DeepDive section 3.4: per-head bias, uniform head aggregation for selection).
+
+    hidden [T, d] (already normalised); w1 [d_ff, d]; w2 [H, d_ff].  Returns float64 [H, T].
+    """
+    lib = _load()
+    h = _f64(hidden)
+    W1 = _f64(w1)
+    W2 = np.ascontiguousarray(_f64(w2).reshape(-1, W1.shape[0]))
+    T, d = h.shape
+    d_ff = W1.shape[0]
+    H = W2.shape[0]
+    out = np.empty((H, T), np.float64)
+    lib.tgo_gate_score_heads(_ptr(h, _D), _ptr(W1, _D), _ptr(W2, _D), T, d, d_ff, H, _ptr(out, _D))
+    return out
+
+
+def aggregate_heads(b):
+    """Uniform aggregation over heads for selection (DeepDive section 3.4): the mean over axis -2 of
+    [..., H, N] normalised per-head scores."""
+    x = _f64(b)
+    return x.sum(axis=-2) / x.shape[-2]
 
 
 def score_normalize(scores, forced, eps):
@@ -255,7 +280,8 @@ def attn_fwd(q, k, v, g, gamma, pos=None, theta=1e6, tau=1.0, round_bf16=False, 
     Summary Figure 1(c)).  With sigma [Hq] the operative rule of section 3.2 Eq. 8: the whole
     logit scaled by tau_ih = softplus(sigma_h) ln(i+1) / ln max(2, pos_i+1) (Eq. 7).
 
-    q [B, M, Hq, D]; k, v [B, M, Hkv, D]; g [B, M]; gamma [Hq]; pos int32 [B, M] or None.
+    q [B, M, Hq, D]; k, v [B, M, Hkv, D]; g [B, M] (one gate per key) or [B, Hq, M] (per-head gates,
+    the per-head bias of section 3.4's released-code walkthrough); gamma [Hq]; pos int32 [B, M] or None.
     round_bf16: round the rotated q, k to bf16 before the product (as the tensor cores see them).
     rows: optional flattened query rows (b*M + i) to compute; the others come back NaN.
     Returns (o float64 [B, M, Hq, D], lse float64 [B, Hq, M]).
@@ -264,7 +290,9 @@ def attn_fwd(q, k, v, g, gamma, pos=None, theta=1e6, tau=1.0, round_bf16=False, 
     Q, Kt, V = _f64(q), _f64(k), _f64(v)
     B, M, Hq, D = Q.shape
     Hkv = Kt.shape[2]
-    G = _f64(g).reshape(B, M)
+    G = _f64(g)
+    per_head = G.ndim == 3
+    G = np.ascontiguousarray(G.reshape((B, Hq, M) if per_head else (B, M)))
     gm = _f64(gamma).reshape(Hq)
     p = None if pos is None else np.ascontiguousarray(np.asarray(pos, dtype=np.int32).reshape(B, M))
     o = np.full((B, M, Hq, D), np.nan)
@@ -273,7 +301,7 @@ def attn_fwd(q, k, v, g, gamma, pos=None, theta=1e6, tau=1.0, round_bf16=False, 
     sg = None if sigma is None else _f64(sigma).reshape(Hq)
     rc = lib.tgo_attn_fwd(_ptr(Q, _D), _ptr(Kt, _D), _ptr(V, _D), _ptr(G, _D), _ptr(gm, _D), _ptr(p, _I32),
                           float(theta), float(tau), _ptr(sg, _D), B, M, Hq, Hkv, D, int(bool(round_bf16)),
-                          _ptr(r, _I64), 0 if r is None else r.size, _ptr(o, _D), _ptr(lse, _D))
+                          _ptr(r, _I64), 0 if r is None else r.size, int(per_head), _ptr(o, _D), _ptr(lse, _D))
     if rc != 0:
         raise ValueError("oracle attn_fwd: bad arguments")
     return o, lse
@@ -283,26 +311,29 @@ def attn_bwd(q, k, v, g, gamma, dout, pos=None, theta=1e6, tau=1.0, round_bf16=F
     """Gradients of the token-gated attention (DeepDive section 3.1 last paragraph and section 3.2:
     the task gradient reaches the scores through the attention bias).
 
-    Returns (dq [B,M,Hq,D], dk [B,M,Hkv,D], dv [B,M,Hkv,D], dg [B,M], dgamma [Hq]), all float64,
-    followed by dsigma [Hq] when sigma is given (the temperature of Eq. 7/8).
+    Returns (dq [B,M,Hq,D], dk [B,M,Hkv,D], dv [B,M,Hkv,D], dg (the shape of g: [B,M] or per-head
+    [B,Hq,M]), dgamma [Hq]), all float64, followed by dsigma [Hq] when sigma is given (Eq. 7/8).
     """
     lib = _load()
     Q, Kt, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, M, Hq, D = Q.shape
     Hkv = Kt.shape[2]
-    G = _f64(g).reshape(B, M)
+    G = _f64(g)
+    per_head = G.ndim == 3
+    G = np.ascontiguousarray(G.reshape((B, Hq, M) if per_head else (B, M)))
     gm = _f64(gamma).reshape(Hq)
     p = None if pos is None else np.ascontiguousarray(np.asarray(pos, dtype=np.int32).reshape(B, M))
     dq = np.empty((B, M, Hq, D))
     dk = np.empty((B, M, Hkv, D))
     dv = np.empty((B, M, Hkv, D))
-    dg = np.empty((B, M))
+    dg = np.empty(G.shape)
     dgamma = np.empty(Hq)
     sg = None if sigma is None else _f64(sigma).reshape(Hq)
     dsigma = None if sigma is None else np.empty(Hq)
     rc = lib.tgo_attn_bwd(_ptr(Q, _D), _ptr(Kt, _D), _ptr(V, _D), _ptr(G, _D), _ptr(gm, _D), _ptr(p, _I32),
                           float(theta), float(tau), _ptr(sg, _D), _ptr(dO, _D), B, M, Hq, Hkv, D,
-                          int(bool(round_bf16)), _ptr(dq, _D), _ptr(dk, _D), _ptr(dv, _D), _ptr(dg, _D),
+                          int(bool(round_bf16)), int(per_head), _ptr(dq, _D), _ptr(dk, _D), _ptr(dv, _D),
+                          _ptr(dg, _D),
                           _ptr(dgamma, _D), _ptr(dsigma, _D))
     if rc != 0:
         raise ValueError("oracle attn_bwd: bad arguments")

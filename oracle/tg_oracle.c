@@ -309,7 +309,7 @@ static double temp_ratio(int64_t i, const int32_t *pos, int64_t bm)
 int tgo_attn_fwd(const double *q, const double *k, const double *v, const double *g,
                  const double *gamma, const int32_t *pos, double theta, double tau,
                  const double *sigma, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
-                 int round, const int64_t *rows, int64_t nrows, double *o, double *lse)
+                 int round, const int64_t *rows, int64_t nrows, int g_per_head, double *o, double *lse)
 {
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;
@@ -343,7 +343,7 @@ int tgo_attn_fwd(const double *q, const double *k, const double *v, const double
                     double dot = 0.0;
                     for (int64_t e = 0; e < D; ++e)
                         dot += qi[e] * kj[e];
-                    double gj = g[b * M + j];
+                    double gj = g[g_per_head ? (b * Hq + h) * M + j : b * M + j];
                     logit[j] = gj > 0.0 ? t * (c * dot + gamma[h] * log(gj)) : -INFINITY;
                     if (logit[j] > mx)
                         mx = logit[j];
@@ -404,8 +404,8 @@ int tgo_attn_fwd(const double *q, const double *k, const double *v, const double
 int tgo_attn_bwd(const double *q, const double *k, const double *v, const double *g,
                  const double *gamma, const int32_t *pos, double theta, double tau,
                  const double *sigma, const double *dout, int64_t B, int64_t M, int64_t Hq,
-                 int64_t Hkv, int64_t D, int round, double *dq, double *dk, double *dv,
-                 double *dg, double *dgamma, double *dsigma)
+                 int64_t Hkv, int64_t D, int round, int g_per_head, double *dq, double *dk,
+                 double *dv, double *dg, double *dgamma, double *dsigma)
 {
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;
@@ -449,7 +449,7 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
                             double dot = 0.0;
                             for (int64_t e = 0; e < D; ++e)
                                 dot += qi[e] * kj[e];
-                            double gj = g[b * M + j];
+                            double gj = g[g_per_head ? (b * Hq + h) * M + j : b * M + j];
                             Z[j] = gj > 0.0 ? c * dot + gamma[h] * log(gj) : -INFINITY;
                             P[j] = gj > 0.0 ? t * Z[j] : -INFINITY;
                             if (P[j] > mx)
@@ -485,7 +485,7 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
                                 dvj[e] += P[j] * doi[e];
                             }
                             colsum[(b * Hq + h) * M + j] += dZ;
-                            if (g[b * M + j] > 0.0)
+                            if (g[g_per_head ? (b * Hq + h) * M + j : b * M + j] > 0.0)
                                 dt += dS * Z[j];
                         }
                         dsig[b * Hq + h] += dt * ratio;
@@ -509,19 +509,29 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
         }
     }
 
-    for (int64_t bm = 0; bm < B * M; ++bm) {
-        int64_t b = bm / M, j = bm % M;
-        double gj = g[bm];
-        double acc = 0.0;
-        for (int64_t h = 0; h < Hq; ++h)
-            acc += gamma[h] * colsum[(b * Hq + h) * M + j];
-        dg[bm] = gj > 0.0 ? acc / gj : 0.0;
+    /* dg: per key (summed over heads) for a shared gate, per (head, key) for per-head gates
+     * (dL/dg_hj = gamma_h colsum_h(j) / g_hj). */
+    if (g_per_head) {
+        for (int64_t bh = 0; bh < B * Hq; ++bh)
+            for (int64_t j = 0; j < M; ++j) {
+                double gj = g[bh * M + j];
+                dg[bh * M + j] = gj > 0.0 ? gamma[bh % Hq] * colsum[bh * M + j] / gj : 0.0;
+            }
+    } else {
+        for (int64_t bm = 0; bm < B * M; ++bm) {
+            int64_t b = bm / M, j = bm % M;
+            double gj = g[bm];
+            double acc = 0.0;
+            for (int64_t h = 0; h < Hq; ++h)
+                acc += gamma[h] * colsum[(b * Hq + h) * M + j];
+            dg[bm] = gj > 0.0 ? acc / gj : 0.0;
+        }
     }
     for (int64_t h = 0; h < Hq; ++h) {
         double acc = 0.0;
         for (int64_t b = 0; b < B; ++b)
             for (int64_t j = 0; j < M; ++j) {
-                double gj = g[b * M + j];
+                double gj = g[g_per_head ? (b * Hq + h) * M + j : b * M + j];
                 if (gj > 0.0)
                     acc += colsum[(b * Hq + h) * M + j] * log(gj);
             }
@@ -641,6 +651,40 @@ void tgo_gate_softmax_bwd(const double *g, const double *dg, int64_t B, int64_t 
             dot += g[b * M + j] * dg[b * M + j];
         for (int64_t j = 0; j < M; ++j)
             db[b * M + j] = g[b * M + j] * (dg[b * M + j] - dot);
+    }
+}
+
+/*
+ * [DeepDive] section 3.4 (the released code's invariants): per-head scores and
+ * a uniform aggregation over heads for selection.  Reading used here: the
+ * scorer's second layer has H outputs, one per attention head,
+ *     b~_j^h = sum_k w2[h, k] SiLU(sum_i W1[k, i] a~_j[i]),
+ * i.e. the a1 scorer with H rows in w2.  scores: [H, T] (head-major).
+ */
+void tgo_gate_score_heads(const double *hidden, const double *w1, const double *w2, int64_t T,
+                          int64_t d, int64_t d_ff, int64_t H, double *scores)
+{
+#pragma omp parallel
+    {
+        double *act = (double *)malloc((size_t)(d_ff > 0 ? d_ff : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < T; ++t) {
+            const double *h = hidden + t * d;
+            for (int64_t k = 0; k < d_ff; ++k) {
+                const double *row = w1 + k * d;
+                double u = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    u += row[i] * h[i];
+                act[k] = u / (1.0 + exp(-u));
+            }
+            for (int64_t hh = 0; hh < H; ++hh) {
+                double s = 0.0;
+                for (int64_t k = 0; k < d_ff; ++k)
+                    s += w2[hh * d_ff + k] * act[k];
+                scores[hh * T + t] = s;
+            }
+        }
+        free(act);
     }
 }
 

@@ -9,6 +9,10 @@ DeepDive = "TokenGate: Learnable Token Pruning for Fast, Memory-Efficient LLM Pr
   * Softmax-over-S gate (section 3.2, Eq. 5) and its backward: SciPy's softmax, padding,
     shift invariance, autograd, central finite differences; Eq. 6's per-head gain reproduced by
     the attention bias through this gate.
+  * Per-head scores and uniform head aggregation (section 3.4): each head equals the single-head
+    scorer with that row of w2; identical heads aggregate to themselves.  Per-head gates in the
+    attention: equal heads reduce to the shared gate; otherwise fp64 SDPA with the per-head
+    additive bias, and autograd for the per-head dg.
 """
 import math
 
@@ -141,3 +145,47 @@ def test_eq6_gain_through_the_attention_bias(o):
     bias = torch.from_numpy(c)[None, :, None, None] * torch.from_numpy(b)[:, None, None, :] + mask
     ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=bias).permute(0, 2, 1, 3)
     np.testing.assert_allclose(o1, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+# --- per-head scores, uniform head aggregation, per-head gates (DeepDive section 3.4) ---
+
+def test_score_heads_reduce_to_the_single_head_scorer(o):
+    h, w1, _, _ = _mlp(7, 29, 40, 24)
+    w2 = np.random.default_rng(8).normal(0.0, 0.2, (5, 24))
+    sh = o.gate_score_heads(h, w1, w2)
+    assert sh.shape == (5, 29)
+    for k in range(5):
+        s, _ = o.gate_score(h, w1, w2[k])
+        np.testing.assert_allclose(sh[k], s, rtol=1e-13, atol=1e-15)
+    # the uniform aggregation of identical heads is that head
+    same = np.repeat(sh[:1], 4, axis=0)
+    np.testing.assert_allclose(o.aggregate_heads(same), sh[0], rtol=1e-15)
+    np.testing.assert_allclose(o.aggregate_heads(sh), sh.mean(axis=0), rtol=1e-14)
+
+
+def test_per_head_gates_attention(o):
+    """Per-head gates: equal heads reduce to the shared gate; otherwise fp64 SDPA with the per-head
+    additive bias gamma_h ln g_hj, and autograd for the per-head dg."""
+    rng = np.random.default_rng(10)
+    B, M, Hq, Hkv, D = 2, 9, 4, 2, 8
+    q, k, v = (rng.normal(0.0, 1.0, (B, M, H, D)) for H in (Hq, Hkv, Hkv))
+    gamma = rng.uniform(0.5, 1.5, Hq)
+    g1 = 1.0 / (1.0 + np.exp(-rng.normal(0.0, 1.0, (B, M))))
+    o_sh, l_sh = o.attn_fwd(q, k, v, g1, gamma)
+    o_ph, l_ph = o.attn_fwd(q, k, v, np.repeat(g1[:, None, :], Hq, axis=1), gamma)
+    np.testing.assert_allclose(o_ph, o_sh, rtol=1e-14, atol=1e-15)
+    gh = 1.0 / (1.0 + np.exp(-rng.normal(0.0, 1.0, (B, Hq, M))))
+    dout = rng.normal(0.0, 1.0, (B, M, Hq, D))
+    leaves = [torch.from_numpy(a).requires_grad_() for a in (q, k, v, gh, gamma)]
+    qt, kt, vt = (x.permute(0, 2, 1, 3) for x in leaves[:3])
+    kt, vt = kt.repeat_interleave(Hq // Hkv, 1), vt.repeat_interleave(Hq // Hkv, 1)
+    causal = torch.full((M, M), float("-inf"), dtype=torch.float64).triu(1)
+    bias = leaves[4][None, :, None, None] * torch.log(leaves[3])[:, :, None, :] + causal
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=bias).permute(0, 2, 1, 3)
+    out, _ = o.attn_fwd(q, k, v, gh, gamma)
+    np.testing.assert_allclose(out, ref.detach().numpy(), rtol=1e-11, atol=1e-12)
+    (ref * torch.from_numpy(dout)).sum().backward()
+    got = o.attn_bwd(q, k, v, gh, gamma, dout)
+    assert got[3].shape == (B, Hq, M)
+    for a, leaf in zip(got, leaves):
+        np.testing.assert_allclose(a, leaf.grad.numpy(), rtol=1e-10, atol=1e-11)
