@@ -296,6 +296,61 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
                             void *stream);
 
 /*
+ * Per-head scores with a uniform head aggregation for selection, and per-head
+ * gates ([DeepDive] section 3.4: the released code keeps a per-layer, per-head
+ * bias and aggregates the heads uniformly for selection).  Reading: the
+ * scorer's second layer has H outputs (w2 [H, d_ff]); each head's scores are
+ * normalised as in tg_score_normalize; selection ranks their mean over heads;
+ * each head's gate is the softmax over the kept set of its own scores; and
+ * query head h attends with bias gamma_h ln g_hj.
+ *
+ * tg_gate_score_heads: b~[b][h][n] = sum_k w2[h,k] SiLU(sum_i w1[k,i] a~[b,n,i])
+ *   with a~ = RMSNorm(hidden) (weight ln_w or NULL = 1, ln_eps) when ln != 0,
+ *   else a~ = hidden.  hidden [B, N, d] (dt), w1 [d_ff, d], w2 [H, d_ff] (dt),
+ *   1 <= H <= 16; scores [B, H, N] f32 out; workspace and errors as
+ *   tg_gate_score (bf16: the packed W1).
+ * tg_score_normalize_heads: tg_score_normalize on each (b, h) row of
+ *   scores [B, H, N], with b's forced mask [B, N] (or NULL); out may be scores.
+ * tg_aggregate_heads: out[b][n] = (sum_h b[b][h][n]) / H (heads in order),
+ *   b [B, H, N], out [B, N] f32: the vector tg_select_topk ranks.
+ * tg_gather_heads: out[b][h][m] = b[b][h][kept_idx[b][m]] (0 where the index is
+ *   negative): b [B, H, N], kept_idx [B, M], out [B, H, M].
+ * tg_gate_softmax_heads: tg_gate_softmax on each (b, h) row of b [B, H, M]
+ *   with b's kept_idx [B, M] (or NULL); g [B, H, M].  (tg_gate_softmax_bwd
+ *   applies to [B * H, M] as it is.)
+ * tg_gated_attn_fwd_headgates / _bwd_headgates: tg_gated_attn_fwd / _bwd with
+ *   one gate per (query head, key): g [B, Hq, M] f32 (> = 0), bias
+ *   gamma_h ln g_hj; the backward's dg is [B, Hq, M],
+ *   dg_hj = gamma_h colsum_h(j) / g_hj (0 where g_hj = 0), and dgamma uses
+ *   ln g_hj.  Everything else (sigma, workspace, dtypes, errors) as the
+ *   shared-gate calls.
+ */
+tg_status tg_gate_score_heads(const void *hidden, int ln, const void *ln_w, float ln_eps,
+                              const void *w1, const void *w2, int64_t B, int64_t N, int64_t d,
+                              int64_t d_ff, int64_t H, tg_dtype dt, float *scores, void *ws,
+                              size_t ws_bytes, void *stream);
+tg_status tg_score_normalize_heads(const float *scores, const uint8_t *forced_keep, int64_t B,
+                                   int64_t H, int64_t N, float eps, float *out, void *stream);
+tg_status tg_aggregate_heads(const float *b, int64_t B, int64_t H, int64_t N, float *out,
+                             void *stream);
+tg_status tg_gather_heads(const float *b, const int32_t *kept_idx, int64_t B, int64_t H,
+                          int64_t N, int64_t M, float *out, void *stream);
+tg_status tg_gate_softmax_heads(const float *b, const int32_t *kept_idx, int64_t B, int64_t H,
+                                int64_t M, float *g, void *stream);
+tg_status tg_gated_attn_fwd_headgates(const void *q, const void *k, const void *v, const float *g,
+                                      const float *gamma, const int32_t *pos, float rope_theta,
+                                      float tau, const float *sigma, int64_t B, int64_t M,
+                                      int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o,
+                                      float *lse, void *ws, size_t ws_bytes, void *stream);
+tg_status tg_gated_attn_bwd_headgates(const void *q, const void *k, const void *v, const float *g,
+                                      const float *gamma, const int32_t *pos, float rope_theta,
+                                      float tau, const float *sigma, const float *lse,
+                                      const void *dout, int64_t B, int64_t M, int64_t Hq,
+                                      int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk,
+                                      float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
+                                      size_t ws_bytes, void *stream);
+
+/*
  * Packed variable-length attention: the training path evaluates both budgets'
  * targets in one call ([DeepDive] section 3.3), i.e. several sequences of
  * different lengths packed back to back.  Sequence s holds tokens

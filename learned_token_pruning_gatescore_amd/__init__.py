@@ -22,6 +22,9 @@ The rest of the scoring definition (section 2 Eq. 1, section 3.1 Eq. 3, section 
   tg_score_normalize   sequence RMS normalisation over the prunable positions, 0 on forced ones
   tg_gate_softmax      gate values as the softmax of the normalised scores over the kept set
   tg_gate_softmax_bwd  its backward
+Per-head scores, uniform head aggregation, per-head gates (section 3.4):
+  tg_gate_score_heads, tg_score_normalize_heads, tg_aggregate_heads, tg_gather_heads,
+  tg_gate_softmax_heads, tg_gated_attn_fwd_headgates / tg_gated_attn_bwd_headgates
 Packed variable-length sequences (section 3.3: both budgets in one call):
   tg_gated_attn_fwd_varlen / tg_gated_attn_bwd_varlen
 """
@@ -37,7 +40,8 @@ __all__ = [
     "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
     "tg_gate_score_ln", "tg_score_normalize", "tg_gate_softmax", "tg_gate_softmax_bwd",
     "tg_gated_attn_varlen_workspace_size", "tg_gated_attn_fwd_varlen", "tg_gated_attn_bwd_varlen",
-    "attn_varlen_workspace",
+    "attn_varlen_workspace", "tg_gate_score_heads", "tg_score_normalize_heads", "tg_aggregate_heads",
+    "tg_gather_heads", "tg_gate_softmax_heads", "tg_gated_attn_fwd_headgates", "tg_gated_attn_bwd_headgates",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,6 +103,16 @@ def load():
     lib.tg_gate_softmax.argtypes = [P, P, i64, i64, P, P]
     lib.tg_gate_softmax_bwd.restype = c_int
     lib.tg_gate_softmax_bwd.argtypes = [P, P, i64, i64, P, P]
+    lib.tg_gate_score_heads.restype = c_int
+    lib.tg_gate_score_heads.argtypes = [P, c_int, P, f32, P, P, i64, i64, i64, i64, i64, c_int, P, P, sz, P]
+    lib.tg_score_normalize_heads.restype = c_int
+    lib.tg_score_normalize_heads.argtypes = [P, P, i64, i64, i64, f32, P, P]
+    lib.tg_aggregate_heads.restype = c_int
+    lib.tg_aggregate_heads.argtypes = [P, i64, i64, i64, P, P]
+    lib.tg_gather_heads.restype = c_int
+    lib.tg_gather_heads.argtypes = [P, P, i64, i64, i64, i64, P, P]
+    lib.tg_gate_softmax_heads.restype = c_int
+    lib.tg_gate_softmax_heads.argtypes = [P, P, i64, i64, i64, P, P]
     lib.tg_gated_attn_varlen_workspace_size.restype = sz
     lib.tg_gated_attn_varlen_workspace_size.argtypes = [P, i64, i64, i64, i64, c_int]
     lib.tg_gated_attn_fwd_varlen.restype = c_int
@@ -115,6 +129,10 @@ def load():
     lib.tg_gated_attn_bwd.restype = c_int
     lib.tg_gated_attn_bwd.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, i64, i64, i64, i64, i64, c_int,
                                       P, P, P, P, P, P, P, sz, P]
+    lib.tg_gated_attn_fwd_headgates.restype = c_int
+    lib.tg_gated_attn_fwd_headgates.argtypes = lib.tg_gated_attn_fwd.argtypes
+    lib.tg_gated_attn_bwd_headgates.restype = c_int
+    lib.tg_gated_attn_bwd_headgates.argtypes = lib.tg_gated_attn_bwd.argtypes
     _lib = lib
     return lib
 
@@ -293,6 +311,70 @@ def tg_gated_attn_bwd(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk
                                     float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), B, M, Hq, Hkv, D, _dt(q),
                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgamma), _ptr(dsigma), _ptr(ws),
                                     ws_bytes, _stream(stream)))
+
+
+def tg_gate_score_heads(hidden, w1, w2, scores, ws=None, ln_w=None, ln_eps=None, stream=None):
+    """Per-head scores [B, H, N] of hidden [B, N, d] (RMSNorm in front when ln_eps is given); w2 [H, d_ff]."""
+    _contig(hidden, w1, w2, scores, ws, ln_w)
+    B, N, d = hidden.shape
+    d_ff = w1.shape[0]
+    H = w2.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ln = ln_eps is not None
+    _check(load().tg_gate_score_heads(_ptr(hidden), int(ln), _ptr(ln_w), float(ln_eps if ln else 0.0), _ptr(w1),
+                                      _ptr(w2), B, N, d, d_ff, H, _dt(hidden), _ptr(scores), _ptr(ws), ws_bytes,
+                                      _stream(stream)))
+
+
+def tg_score_normalize_heads(scores, forced_keep, eps, out, stream=None):
+    _contig(scores, forced_keep, out)
+    B, H, N = scores.shape
+    _check(load().tg_score_normalize_heads(_ptr(scores), _ptr(forced_keep), B, H, N, float(eps), _ptr(out),
+                                           _stream(stream)))
+
+
+def tg_aggregate_heads(b, out, stream=None):
+    _contig(b, out)
+    B, H, N = b.shape
+    _check(load().tg_aggregate_heads(_ptr(b), B, H, N, _ptr(out), _stream(stream)))
+
+
+def tg_gather_heads(b, kept_idx, out, stream=None):
+    _contig(b, kept_idx, out)
+    B, H, N = b.shape
+    M = kept_idx.shape[1]
+    _check(load().tg_gather_heads(_ptr(b), _ptr(kept_idx), B, H, N, M, _ptr(out), _stream(stream)))
+
+
+def tg_gate_softmax_heads(b, kept_idx, g, stream=None):
+    _contig(b, kept_idx, g)
+    B, H, M = b.shape
+    _check(load().tg_gate_softmax_heads(_ptr(b), _ptr(kept_idx), B, H, M, _ptr(g), _stream(stream)))
+
+
+def tg_gated_attn_fwd_headgates(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None, *,
+                                sigma=None):
+    """tg_gated_attn_fwd with per-head gates g [B, Hq, M]."""
+    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma)
+    B, M, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().tg_gated_attn_fwd_headgates(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
+                                              float(rope_theta), float(tau), _ptr(sigma), B, M, Hq, Hkv, D, _dt(q),
+                                              _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tg_gated_attn_bwd_headgates(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk, dv, dg, dgamma, ws,
+                                stream=None, *, sigma=None, dsigma=None):
+    """tg_gated_attn_bwd with per-head gates g [B, Hq, M]; dg [B, Hq, M]."""
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma)
+    B, M, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(load().tg_gated_attn_bwd_headgates(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
+                                              float(rope_theta), float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), B, M,
+                                              Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                              _ptr(dgamma), _ptr(dsigma), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def _cu_host(cu_seqlens):

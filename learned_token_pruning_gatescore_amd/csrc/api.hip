@@ -17,10 +17,14 @@ size_t gate_packed_bytes(int d, int d_ff);
 hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s);
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced, int64_t T,
                              int d, int d_ff, bool bf16, bool ln, const void *ln_w, float ln_eps, float *scores,
-                             float *gates, hipStream_t s);
+                             float *gates, hipStream_t s, int H = 0, int64_t Nrow = 0);
 hipError_t launch_score_normalize(const float *s, const uint8_t *forced, int64_t B, int64_t N, float eps, float *out,
-                                  hipStream_t st);
-hipError_t launch_gate_softmax(const float *x, const int32_t *kept, int64_t B, int64_t M, float *g, hipStream_t st);
+                                  hipStream_t st, int heads = 1);
+hipError_t launch_gate_softmax(const float *x, const int32_t *kept, int64_t B, int64_t M, float *g, hipStream_t st,
+                               int heads = 1);
+hipError_t launch_aggregate_heads(const float *s, int64_t B, int H, int64_t N, float *out, hipStream_t st);
+hipError_t launch_gather_heads(const float *s, const int32_t *kept, int64_t B, int H, int64_t N, int64_t M, float *out,
+                               hipStream_t st);
 hipError_t launch_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db, hipStream_t st);
 hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_t B, int64_t N, int64_t K,
                               int64_t M_alloc, int32_t *kept, int32_t *kept_count, hipStream_t s);
@@ -248,6 +252,36 @@ tg_status tg_gate_score_ln(const void *hidden, const void *ln_w, float ln_eps, c
                     "tg_gate_score_ln launch");
 }
 
+tg_status tg_gate_score_heads(const void *hidden, int ln, const void *ln_w, float ln_eps, const void *w1,
+                              const void *w2, int64_t B, int64_t N, int64_t d, int64_t d_ff, int64_t H, tg_dtype dt,
+                              float *scores, void *ws, size_t ws_bytes, void *stream) {
+  const tg_status st = check_gate(hidden, w1, w2, B, N, d, d_ff, dt, scores, nullptr);
+  if (st != TG_OK) return st;
+  REQUIRE(H >= 1 && H <= 16, TG_ERR_UNSUPPORTED, "1 <= H <= 16 heads (got %lld)", (long long)H);
+  if (ln) {
+    REQUIRE(std::isfinite(ln_eps) && ln_eps >= 0.f, TG_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
+    REQUIRE(aligned16(ln_w), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == TG_BF16) {
+    const size_t need = tg::gate_packed_bytes((int)d, (int)d_ff);
+    REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "bf16 scoring needs a %zu-byte workspace (got %zu)", need,
+            ws ? ws_bytes : (size_t)0);
+    REQUIRE(aligned16(ws), TG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (B * N == 0) return ok();
+    const tg_status pst = hip_status(
+        tg::launch_gate_pack_w1(w1, ln ? ln_w : nullptr, (int)d, (int)d_ff, ws, s), "tg_gate_score_heads pack");
+    if (pst != TG_OK) return pst;
+    return hip_status(tg::launch_gate_score(hidden, ws, w2, nullptr, B * N, (int)d, (int)d_ff, true, ln != 0, nullptr,
+                                            ln_eps, scores, nullptr, s, (int)H, N),
+                      "tg_gate_score_heads launch");
+  }
+  if (B * N == 0) return ok();
+  return hip_status(tg::launch_gate_score(hidden, w1, w2, nullptr, B * N, (int)d, (int)d_ff, false, ln != 0, ln_w,
+                                          ln_eps, scores, nullptr, s, (int)H, N),
+                    "tg_gate_score_heads launch");
+}
+
 tg_status tg_score_normalize(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t N, float eps,
                              float *out, void *stream) {
   REQUIRE(scores && out, TG_ERR_INVALID_ARG, "scores and out are required");
@@ -266,6 +300,48 @@ tg_status tg_gate_softmax(const float *b, const int32_t *kept_idx, int64_t B, in
   REQUIRE(aligned16(b) && aligned16(kept_idx) && aligned16(g), TG_ERR_INVALID_ARG,
           "tensor pointers must be 16-byte aligned");
   return hip_status(tg::launch_gate_softmax(b, kept_idx, B, M, g, (hipStream_t)stream), "tg_gate_softmax launch");
+}
+
+tg_status tg_score_normalize_heads(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t H, int64_t N,
+                                   float eps, float *out, void *stream) {
+  REQUIRE(scores && out, TG_ERR_INVALID_ARG, "scores and out are required");
+  REQUIRE(B >= 0 && N >= 0 && H >= 1, TG_ERR_INVALID_ARG, "B, N >= 0 and H >= 1");
+  REQUIRE(B * H <= 0x7FFFFFFF && H <= 0x7FFFFFFF && N <= (int64_t)1 << 24, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(std::isfinite(eps) && eps >= 0.f, TG_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  REQUIRE(aligned16(scores) && aligned16(out), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_score_normalize(scores, forced_keep, B * H, N, eps, out, (hipStream_t)stream, (int)H),
+                    "tg_score_normalize_heads launch");
+}
+
+tg_status tg_aggregate_heads(const float *b, int64_t B, int64_t H, int64_t N, float *out, void *stream) {
+  REQUIRE(b && out, TG_ERR_INVALID_ARG, "b and out are required");
+  REQUIRE(B >= 0 && N >= 0 && H >= 1, TG_ERR_INVALID_ARG, "B, N >= 0 and H >= 1");
+  REQUIRE(B * N <= kMaxInt * 16 && H <= 0x7FFFFFFF, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(aligned16(b) && aligned16(out), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_aggregate_heads(b, B, (int)H, N, out, (hipStream_t)stream),
+                    "tg_aggregate_heads launch");
+}
+
+tg_status tg_gather_heads(const float *b, const int32_t *kept_idx, int64_t B, int64_t H, int64_t N, int64_t M,
+                          float *out, void *stream) {
+  REQUIRE(b && kept_idx && out, TG_ERR_INVALID_ARG, "b, kept_idx and out are required");
+  REQUIRE(B >= 0 && N >= 0 && M >= 0 && H >= 1, TG_ERR_INVALID_ARG, "B, N, M >= 0 and H >= 1");
+  REQUIRE(B * H * M <= kMaxInt * 16 && H <= 0x7FFFFFFF && N <= kMaxInt, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(aligned16(b) && aligned16(kept_idx) && aligned16(out), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_gather_heads(b, kept_idx, B, (int)H, N, M, out, (hipStream_t)stream),
+                    "tg_gather_heads launch");
+}
+
+tg_status tg_gate_softmax_heads(const float *b, const int32_t *kept_idx, int64_t B, int64_t H, int64_t M, float *g,
+                                void *stream) {
+  REQUIRE(b && g, TG_ERR_INVALID_ARG, "b and g are required");
+  REQUIRE(B >= 0 && M >= 0 && H >= 1, TG_ERR_INVALID_ARG, "B, M >= 0 and H >= 1");
+  REQUIRE(B * H <= 0x7FFFFFFF, TG_ERR_UNSUPPORTED, "problem too large");
+  REQUIRE(aligned16(b) && aligned16(kept_idx) && aligned16(g), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  return hip_status(tg::launch_gate_softmax(b, kept_idx, B * H, M, g, (hipStream_t)stream, (int)H),
+                    "tg_gate_softmax_heads launch");
 }
 
 tg_status tg_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db, void *stream) {
@@ -329,7 +405,9 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
   return tg::attn_workspace_bytes(B, M, Hq, Hkv, D, bwd != 0);
 }
 
-tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+}  // extern "C"
+
+static tg_status attn_fwd_impl(bool gph, const void *q, const void *k, const void *v, const float *g, const float *gamma,
                             const int32_t *pos, float rope_theta, float tau, const float *sigma, int64_t B,
                             int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse,
                             void *ws, size_t ws_bytes, void *stream) {
@@ -345,11 +423,11 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
   if (B * M == 0) return ok();
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
   return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, (int)B, (int)M,
-                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, o, lse, w, (hipStream_t)stream),
+                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, o, lse, w, (hipStream_t)stream),
                     "tg_gated_attn_fwd launch");
 }
 
-tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+static tg_status attn_bwd_impl(bool gph, const void *q, const void *k, const void *v, const float *g, const float *gamma,
                             const int32_t *pos, float rope_theta, float tau, const float *sigma, const float *lse,
                             const void *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
                             float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
@@ -370,9 +448,46 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
   return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, (int)B,
-                                        (int)M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, dq, dk, dv, dg, dgamma,
+                                        (int)M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, dq, dk, dv, dg, dgamma,
                                         dsigma, w, (hipStream_t)stream),
                     "tg_gated_attn_bwd launch");
+}
+
+extern "C" {
+
+tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                            const int32_t *pos, float rope_theta, float tau, const float *sigma, int64_t B,
+                            int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse,
+                            void *ws, size_t ws_bytes, void *stream) {
+  return attn_fwd_impl(false, q, k, v, g, gamma, pos, rope_theta, tau, sigma, B, M, Hq, Hkv, D, dt, o, lse, ws,
+                       ws_bytes, stream);
+}
+
+tg_status tg_gated_attn_fwd_headgates(const void *q, const void *k, const void *v, const float *g,
+                                      const float *gamma, const int32_t *pos, float rope_theta, float tau,
+                                      const float *sigma, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
+                                      tg_dtype dt, void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  return attn_fwd_impl(true, q, k, v, g, gamma, pos, rope_theta, tau, sigma, B, M, Hq, Hkv, D, dt, o, lse, ws,
+                       ws_bytes, stream);
+}
+
+tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                            const int32_t *pos, float rope_theta, float tau, const float *sigma, const float *lse,
+                            const void *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
+                            float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
+                            size_t ws_bytes, void *stream) {
+  return attn_bwd_impl(false, q, k, v, g, gamma, pos, rope_theta, tau, sigma, lse, dout, B, M, Hq, Hkv, D, dt, dq,
+                       dk, dv, dg, dgamma, dsigma, ws, ws_bytes, stream);
+}
+
+tg_status tg_gated_attn_bwd_headgates(const void *q, const void *k, const void *v, const float *g,
+                                      const float *gamma, const int32_t *pos, float rope_theta, float tau,
+                                      const float *sigma, const float *lse, const void *dout, int64_t B, int64_t M,
+                                      int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk,
+                                      float *dv, float *dg, float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
+                                      void *stream) {
+  return attn_bwd_impl(true, q, k, v, g, gamma, pos, rope_theta, tau, sigma, lse, dout, B, M, Hq, Hkv, D, dt, dq,
+                       dk, dv, dg, dgamma, dsigma, ws, ws_bytes, stream);
 }
 
 size_t tg_gated_attn_varlen_workspace_size(const int64_t *cu_seqlens, int64_t nseq, int64_t Hq, int64_t Hkv,
@@ -405,7 +520,7 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
     const hipError_t e = tg::launch_attn_fwd(
         (const char *)q + r.off * Hq * D * esz, (const char *)k + r.off * Hkv * D * esz,
         (const char *)v + r.off * Hkv * D * esz, g + r.off, gamma, pos ? pos + r.off : nullptr, (double)rope_theta,
-        tau, sigma, (int)r.n, (int)r.M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, (char *)o + r.off * Hq * D * esz,
+        tau, sigma, (int)r.n, (int)r.M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, false, (char *)o + r.off * Hq * D * esz,
         lse ? lse + Hq * r.off : nullptr, w, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "tg_gated_attn_fwd_varlen launch");
   }
@@ -445,7 +560,7 @@ tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, 
         (const char *)q + r.off * Hq * D * esz, (const char *)k + r.off * Hkv * D * esz,
         (const char *)v + r.off * Hkv * D * esz, g + r.off, gamma, pos ? pos + r.off : nullptr, (double)rope_theta,
         tau, sigma, lse + Hq * r.off, (const char *)dout + r.off * Hq * D * esz, (int)r.n, (int)r.M, (int)Hq,
-        (int)Hkv, (int)D, dt == TG_BF16, dq + r.off * Hq * D, dk + r.off * Hkv * D, dv + r.off * Hkv * D,
+        (int)Hkv, (int)D, dt == TG_BF16, false, dq + r.off * Hq * D, dk + r.off * Hkv * D, dv + r.off * Hkv * D,
         dg + r.off, part + i * 2 * Hq, sigma ? part + i * 2 * Hq + Hq : nullptr, w, s);
     if (e != hipSuccess) return hip_status(e, "tg_gated_attn_bwd_varlen launch");
   }

@@ -656,7 +656,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs,
     const float *__restrict__ lse, const float *__restrict__ dout, float c, const float *__restrict__ sigma,
-    const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D, float *__restrict__ dq,
+    const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D, int gph, float *__restrict__ dq,
     float *__restrict__ delta, float *__restrict__ tstat) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -678,6 +678,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
     oy = dout[row * D + half + lane];
   }
   const float gam = gamma[h];
+  const float *gh = gph ? g + (b * Hq + h) * M : g + bM;  // this head's gates of the row
   const float l = lse[(b * Hq + h) * M + i];
   const float t = sigma ? fmaxf(softplus_f(sigma[h]) * ratio[bi], 1e-30f) : 1.f;  // logits t Z
   float Di = 0.f;
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
         vx = v[kr + lane];
         vy = v[kr + half + lane];
       }
-      const float zj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, g[bM + j]);
+      const float zj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, gh[j]);
       const float p = zj == -INFINITY ? 0.f : expf(t * zj - l);
       Di += p * wave_sum(ox * vx + oy * vy);
     }
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(
         vx = v[kr + lane];
         vy = v[kr + half + lane];
       }
-      const float zj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, g[bM + j]);
+      const float zj = wave_sum(qx * kx + qy * ky) * c + logit_bias(gam, gh[j]);
       if (zj == -INFINITY) continue;
       const float p = expf(t * zj - l);
       const float ds = p * (wave_sum(ox * vx + oy * vy) - Di);
@@ -734,7 +735,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs,
     const float *__restrict__ lse, const float *__restrict__ dout, const float *__restrict__ delta, float c,
-    const float *__restrict__ sigma, const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D,
+    const float *__restrict__ sigma, const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D, int gph,
     float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, j, kv)
@@ -755,11 +756,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
     vx = v[row * D + lane];
     vy = v[row * D + half + lane];
   }
-  const float gv = g[bj];
   float akx = 0.f, aky = 0.f, avx = 0.f, avy = 0.f;
   for (int hh = 0; hh < G; ++hh) {
     const int h = kv * G + hh;
-    const float bias = logit_bias(gamma[h], gv);
+    const float bias = logit_bias(gamma[h], g[gph ? (b * Hq + h) * M + j : bj]);
     const float sp = sigma ? softplus_f(sigma[h]) : 1.f;
     float cs_h = 0.f;
     if (bias != -INFINITY) {
@@ -808,9 +808,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
 // number of shares): butterfly sums within each wave, then the four waves in
 // order, so the shares are fixed-shape (bitwise deterministic).  Heads go in
 // chunks of 64 per barrier.
+// With per-head gates (gph) g and dg are [B, Hq, M]: dg_hj = gamma_h colsum_h(j) / g_hj and the
+// dgamma share uses ln g_hj.
 __global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
                                                  const float *__restrict__ gamma, const float *__restrict__ tstat,
-                                                 int B, int M, int Hq, float *__restrict__ dg,
+                                                 int B, int M, int Hq, int gph, float *__restrict__ dg,
                                                  float *__restrict__ part) {
   __shared__ float red[2][64][4];
   const int j = blockIdx.x * 256 + threadIdx.x;  // grid (ceil(M / 256), min(B, 65535))
@@ -820,7 +822,7 @@ __global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsu
   for (int b = blockIdx.y; b < B; b += gridDim.y) {
     const float *cr = colsum + (int64_t)b * Hq * M + j;
     const float *tr = tstat ? tstat + (int64_t)b * Hq * M + j : nullptr;
-    const float gv = vj ? g[(int64_t)b * M + j] : 0.f;
+    const float gv = vj && !gph ? g[(int64_t)b * M + j] : 0.f;
     const float lg = gv > 0.f ? logf(gv) : 0.f;
     float acc = 0.f;
     for (int h0 = 0; h0 < Hq; h0 += 64) {
@@ -838,6 +840,12 @@ __global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsu
           if (hh + e >= nh) break;
           acc += gamma[h0 + hh + e] * v[e];
           float t = gv > 0.f ? v[e] * lg : 0.f;
+          if (gph) {  // this head's own gate
+            const int64_t o = ((int64_t)b * Hq + h0 + hh + e) * M + j;
+            const float gh = vj ? g[o] : 0.f;
+            t = gh > 0.f ? v[e] * logf(gh) : 0.f;
+            if (vj) dg[o] = gh > 0.f ? gamma[h0 + hh + e] * v[e] / gh : 0.f;
+          }
           float u = ts[e];
 #pragma unroll
           for (int o = 32; o > 0; o >>= 1) {
@@ -860,7 +868,7 @@ __global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsu
       }
       __syncthreads();
     }
-    if (vj) dg[(int64_t)b * M + j] = gv > 0.f ? acc / gv : 0.f;
+    if (vj && !gph) dg[(int64_t)b * M + j] = gv > 0.f ? acc / gv : 0.f;
   }
 }
 
@@ -913,11 +921,14 @@ hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, 
 
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
-                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk,
-                           float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w, hipStream_t s) {
+                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, bool g_per_head,
+                           float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w,
+                           hipStream_t s) {
   const float2 *cs = pos ? w.cs : nullptr;
+  const int gph = (int)g_per_head;
   if ((int64_t)B * M > 0 && (pos || bf16 || sigma)) {
-    hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, w, s);
+    hipError_t e =
+        launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, g_per_head, w, s);
     if (e != hipSuccess) return e;
   }
   const double cd = 1.0 / (sqrt((double)D) * (double)tau);
@@ -946,15 +957,15 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
       const int64_t rq = (int64_t)B * M * Hq, rk = (int64_t)B * M * Hkv;
       hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, dim3((unsigned)((rq + 3) / 4)), dim3(256), 0, s,
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, c, sigma, w.ratio, B, M, Hq, Hkv, D, dq, delta, w.tstat);
+                         (const float *)dout, c, sigma, w.ratio, B, M, Hq, Hkv, D, gph, dq, delta, w.tstat);
       hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, dim3((unsigned)((rk + 3) / 4)), dim3(256), 0, s,
                          (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, delta, c, sigma, w.ratio, B, M, Hq, Hkv, D, dk, dv, w.colsum);
+                         (const float *)dout, delta, c, sigma, w.ratio, B, M, Hq, Hkv, D, gph, dk, dv, w.colsum);
     }
     // the row statistics are dead by now: their space (2 B Hq M floats) takes the
     // dgamma and dsigma shares (2 B ceil(M / 256) Hq floats)
     hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)(B < 65535 ? B : 65535)), dim3(256), 0,
-                       s, w.colsum, g, gamma, sigma ? (const float *)w.tstat : nullptr, B, M, Hq, dg,
+                       s, w.colsum, g, gamma, sigma ? (const float *)w.tstat : nullptr, B, M, Hq, gph, dg,
                        (float *)w.rowstat);
   }
   hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)(sigma ? 2 * Hq : Hq)), dim3(256), 0, s, (const float *)w.rowstat,

@@ -38,7 +38,8 @@ namespace tg {
 //                   on the host in fp64), stored as fp32;
 //   khat[row]     = k[row] rotated (bf16, every kv head), when khat != nullptr;
 //   bias[b][h][j] = gamma_h * log2 g_j (-inf where g_j <= 0), the per-key,
-//                   per-head logit bias in log2 units, when bias != nullptr;
+//                   per-head logit bias in log2 units, when bias != nullptr
+//                   (g_hj with per-head gates);
 //   ratio[row]    = ln m_i / ln max(2, p_i), the row factor of the attention
 //                   temperature (m_i = i + 1, p_i = pos + 1, or i + 1 without
 //                   positions), when ratio != nullptr.
@@ -52,7 +53,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
                                                         const int32_t *__restrict__ pos, InvFreq inv, int64_t rows,
                                                         int M, int Hq, int Hkv, int D, float2 *__restrict__ cs,
                                                         uint16_t *__restrict__ khat, float *__restrict__ bias,
-                                                        float *__restrict__ ratio, int *__restrict__ cnt, int ncnt) {
+                                                        float *__restrict__ ratio, int *__restrict__ cnt, int ncnt,
+                                                        int gph) {
   __shared__ float2 scs[256];
   const int half = D / 2, R = 256 / half;  // R rows per work-group, one thread per (row, rotary pair)
   const int t = threadIdx.x;
@@ -91,11 +93,12 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
       *(u32x4 *)(khat + o + half) = yo;
     }
   }
-  if (bias && vr) {
-    const float gv = g[r];
-    const float lg = gv > 0.f ? log2f(gv) : -INFINITY;
+  if (bias && vr) {  // gph: one gate per (head, key), g [B, Hq, M]; else one per key, g [B, M]
     const int b = (int)r / M, j = (int)r - b * M;  // B * M < 2^31
-    for (int h = i; h < Hq; h += half) bias[(b * Hq + h) * M + j] = gv > 0.f ? gamma[h] * lg : -INFINITY;
+    for (int h = i; h < Hq; h += half) {
+      const float gv = g[gph ? ((int64_t)b * Hq + h) * M + j : r];
+      bias[(b * Hq + h) * M + j] = gv > 0.f ? gamma[h] * log2f(gv) : -INFINITY;
+    }
   }
   if (ratio && vr && i == 0) {  // the temperature's row factor ln m_i / ln max(2, p_i) (fp64 logs)
     const int b = (int)r / M, j = (int)r - b * M;
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ gamma, const float2 *__restrict__ cs, float c,
     const float *__restrict__ sigma, const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int D,
-    float *__restrict__ o, float *__restrict__ lse) {
+    int gph, float *__restrict__ o, float *__restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, i, h) flattened
   if (row >= (int64_t)B * M * Hq) return;
@@ -491,6 +494,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     }
   }
   const float gam = gamma[h];
+  const float *gh = gph ? g + ((bM / M) * Hq + h) * M : g + bM;  // this head's gates of the row
   float m = -INFINITY, l = 0.f, ax = 0.f, ay = 0.f;
   for (int j = 0; j <= i; ++j) {
     const int64_t kr = ((bM + j) * Hkv + kv) * D;
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
         ky = y;
       }
     }
-    const float sj = t * (wave_sum(qx * kx + qy * ky) * c + bias_of(gam, g[bM + j]));
+    const float sj = t * (wave_sum(qx * kx + qy * ky) * c + bias_of(gam, gh[j]));
     if (sj == -INFINITY) continue;
     const float mn = fmaxf(m, sj);
     const float al = expf(m - mn), p = expf(sj - mn);
@@ -627,7 +631,7 @@ AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, in
 
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
                             int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
-                            const AttnWs &w, hipStream_t s) {
+                            bool g_per_head, const AttnWs &w, hipStream_t s) {
   if ((int64_t)B * M == 0) return hipSuccess;
   InvFreq inv;
   for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
@@ -636,15 +640,17 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
   hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0, s,
                      (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
                      (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, with_ratio ? w.ratio : nullptr,
-                     w.cnt, with_bias ? w.ncnt : 0);
+                     w.cnt, with_bias ? w.ncnt : 0, (int)g_per_head);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
-                           int Hkv, int D, bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s) {
+                           int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, const AttnWs &w,
+                           hipStream_t s) {
   if ((int64_t)B * M == 0) return hipSuccess;
-  hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, w, s);
+  hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, g_per_head,
+                                  w, s);
   if (e != hipSuccess) return e;
   const float2 *cs = pos ? w.cs : nullptr;
   const double c = 1.0 / (sqrt((double)D) * (double)tau);
@@ -661,7 +667,7 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const int64_t rows = (int64_t)B * M * Hq;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const float *)q,
                        (const float *)k, (const float *)v, g, gamma, cs, (float)c, sigma, w.ratio, B, M, Hq, Hkv,
-                       D, (float *)o, lse);
+                       D, (int)g_per_head, (float *)o, lse);
   }
   return hipGetLastError();
 }

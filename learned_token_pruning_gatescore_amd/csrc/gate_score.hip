@@ -38,6 +38,7 @@ namespace tg {
 constexpr int GS_W = 8;      // waves per work-group (two per SIMD)
 constexpr int GS_UB = 2;     // 32-unit blocks per wave
 constexpr int GS_U = GS_W * GS_UB * 32;  // units per work-group chunk (8 waves x 64)
+constexpr int GS_HMAX = 16;  // most output heads of the per-head scorer
 constexpr int GS_BK = 64;    // inputs per hidden stage (one 128-byte line per token row)
 constexpr int GS_NB = 4;     // hidden ring stages
 constexpr int GS_NA = 8;     // W1 fragment register ring: one slot per 16-input step of a trip
@@ -92,10 +93,12 @@ __global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__res
 // the B fragments the waves read anyway (fragment tb, step j of a trip is
 // squared by the one wave with wave % NTB == tb and wave / NTB == j % (8 / NTB)),
 // then r_t scales the pre-activations.
-template <int NTB, bool LN>
+// MH: H output heads (w2 [H, d_ff]); scores [B, H, Nrow] head-major, no gates
+// (the per-head gates come from the per-head softmax over the kept set).
+template <int NTB, bool LN, bool MH>
 __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w1p, const uint16_t *__restrict__ w2,
-    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float ln_eps,
+    const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float ln_eps, int H, int64_t Nrow,
     float *__restrict__ scores, float *__restrict__ gates) {
   constexpr int TT = 32 * NTB;         // tokens per work-group
   constexpr int ST = TT * GS_BK;       // u16 per hidden stage
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
   static_assert(NI >= 1 && TT % (8 * GS_W) == 0, "tile rows must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint16_t sH[GS_NB * ST];
   __shared__ float sRed[GS_W][TT];
-  __shared__ float sW2[GS_U];
+  __shared__ float sW2[MH ? GS_HMAX * GS_U : GS_U];
   __shared__ float sSq[LN ? GS_W : 1][64];
   __shared__ float sR[LN ? TT : 1];
   constexpr int SQP = GS_W / NTB;  // waves sharing one fragment's squares (by step parity)
@@ -147,9 +150,19 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
   }
 
   float run = 0.f;  // running score of token t0 + tid (tid < TT), across unit chunks
+  float runh[MH ? GS_HMAX : 1];  // MH: one per head
+#pragma unroll
+  for (int h = 0; h < (MH ? GS_HMAX : 1); ++h) runh[h] = 0.f;
 
   for (int c = 0; c < d_ff; c += GS_U) {
-    for (int i = tid; i < GS_U; i += 64 * GS_W) sW2[i] = c + i < d_ff ? __uint_as_float((uint32_t)w2[c + i] << 16) : 0.f;
+    if (MH) {
+      for (int i = tid; i < H * GS_U; i += 64 * GS_W) {
+        const int h = i / GS_U, u = i - h * GS_U;
+        sW2[i] = c + u < d_ff ? __uint_as_float((uint32_t)w2[(int64_t)h * d_ff + c + u] << 16) : 0.f;
+      }
+    } else {
+      for (int i = tid; i < GS_U; i += 64 * GS_W) sW2[i] = c + i < d_ff ? __uint_as_float((uint32_t)w2[c + i] << 16) : 0.f;
+    }
     // this wave's unit groups: c / 32 + GS_UB wave + ub, ub < GS_UB
     const uint16_t *ap = w1p + ((int64_t)(c / 32 + GS_UB * wave) * nkk) * 512 + lane * 8;
     auto load_a1 = [&](int kk, int ub) {
@@ -254,6 +267,49 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) rt[tb] = sR[32 * tb + l32];
     }
+    if (MH) {
+      // SiLU in place, then per head: times that head's w2 row, summed over this
+      // lane's units, the two halves and the waves (fixed order)
+#pragma unroll
+      for (int ub = 0; ub < GS_UB; ++ub)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = LN ? acc[ub][tb][r] * rt[tb] : acc[ub][tb][r];
+            acc[ub][tb][r] = x * fast_rcp(1.f + fast_exp2(-x * kLog2e));
+          }
+      for (int h = 0; h < H; ++h) {
+        float ph[NTB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) ph[tb] = 0.f;
+#pragma unroll
+        for (int ub = 0; ub < GS_UB; ++ub)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 wv = *(const f32x4 *)&sW2[h * GS_U + wave * 32 * GS_UB + ub * 32 + 8 * g4 + 4 * hl];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ph[tb] = __builtin_fmaf(acc[ub][tb][g4 * 4 + e], wv[e], ph[tb]);
+          }
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          ph[tb] += __shfl_xor(ph[tb], 32);
+          if (hl == 0) sRed[wave][32 * tb + l32] = ph[tb];
+        }
+        __syncthreads();
+        if (tid < TT) {
+          const float v = ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid])) +
+                          ((sRed[4][tid] + sRed[5][tid]) + (sRed[6][tid] + sRed[7][tid]));
+#pragma unroll
+          for (int hh = 0; hh < GS_HMAX; ++hh)
+            if (hh == h) runh[hh] += v;
+        }
+        __syncthreads();
+      }
+      continue;
+    }
     // Epilogue: SiLU, times w2, summed over this lane's units.
     float part[NTB];
 #pragma unroll
@@ -287,6 +343,16 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
     __syncthreads();
   }
 
+  if (MH) {
+    const int64_t t = t0 + tid;
+    if (tid < TT && t < T) {
+      const int64_t b = t / Nrow, n = t - b * Nrow;
+#pragma unroll
+      for (int h = 0; h < GS_HMAX; ++h)
+        if (h < H) scores[(b * H + h) * Nrow + n] = runh[h];
+    }
+    return;
+  }
   if (tid < TT) {
     const int64_t t = t0 + tid;
     if (t < T) {
@@ -305,8 +371,8 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
 __global__ __launch_bounds__(256) void gate_score_f32_kernel(
     const float *__restrict__ hidden, const float *__restrict__ w1, const float *__restrict__ w2,
     const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, const float *__restrict__ ln_w, float ln_eps,
-    bool ln, float *__restrict__ scores, float *__restrict__ gates) {
-  extern __shared__ float sh[];  // d floats
+    bool ln, int H, int64_t Nrow, float *__restrict__ scores, float *__restrict__ gates) {
+  extern __shared__ float sh[];  // d floats (+ d_ff activations with H > 0)
   __shared__ float sPart[4];
   __shared__ float sR;
   const int64_t t = blockIdx.x;
@@ -326,6 +392,25 @@ __global__ __launch_bounds__(256) void gate_score_f32_kernel(
     for (int i = threadIdx.x; i < d; i += 256) sh[i] = sh[i] * r * (ln_w ? ln_w[i] : 1.f);
   }
   __syncthreads();
+  if (H > 0) {  // per-head scores: the activations first, then one dot product per head
+    float *act = sh + d;
+    for (int k = wave; k < d_ff; k += 4) {
+      const float *row = w1 + (int64_t)k * d;
+      float u = 0.f;
+      for (int i = lane; i < d; i += 64) u += row[i] * sh[i];
+      u = wave_sum(u);
+      if (lane == 0) act[k] = u / (1.f + expf(-u));
+    }
+    __syncthreads();
+    const int64_t b = t / Nrow, n = t - b * Nrow;
+    for (int h = wave; h < H; h += 4) {
+      float sv = 0.f;
+      for (int k = lane; k < d_ff; k += 64) sv += w2[(int64_t)h * d_ff + k] * act[k];
+      sv = wave_sum(sv);
+      if (lane == 0) scores[(b * H + h) * Nrow + n] = sv;
+    }
+    return;
+  }
   float part = 0.f;
   for (int k = wave; k < d_ff; k += 4) {
     const float *row = w1 + (int64_t)k * d;
@@ -353,23 +438,29 @@ hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff
 
 // bf16: w1 is the packed copy (gate_pack_w1_kernel, with the RMSNorm weight
 // folded in when ln); f32: natural layout, ln_w applied in the kernel.
+// H > 0: the per-head scorer (w2 [H, d_ff], scores [B, H, Nrow], no gates).
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2,
                              const uint8_t *forced, int64_t T, int d, int d_ff, bool bf16, bool ln,
-                             const void *ln_w, float ln_eps, float *scores, float *gates, hipStream_t s) {
+                             const void *ln_w, float ln_eps, float *scores, float *gates, hipStream_t s, int H,
+                             int64_t Nrow) {
   if (T == 0) return hipSuccess;
+  const bool mh = H > 0;
   if (bf16) {
     const int nkk = gate_nkk(d);
     // 128-token tiles when they still fill the 256 compute units, else 64
     const bool big = (T + 127) / 128 >= 256;
-    auto k = big ? (ln ? gate_score_bf16_kernel<4, true> : gate_score_bf16_kernel<4, false>)
-                 : (ln ? gate_score_bf16_kernel<2, true> : gate_score_bf16_kernel<2, false>);
+    auto k = big ? (mh ? (ln ? gate_score_bf16_kernel<4, true, true> : gate_score_bf16_kernel<4, false, true>)
+                       : (ln ? gate_score_bf16_kernel<4, true, false> : gate_score_bf16_kernel<4, false, false>))
+                 : (mh ? (ln ? gate_score_bf16_kernel<2, true, true> : gate_score_bf16_kernel<2, false, true>)
+                       : (ln ? gate_score_bf16_kernel<2, true, false> : gate_score_bf16_kernel<2, false, false>));
     const int tt = big ? 128 : 64;
     hipLaunchKernelGGL(k, dim3((unsigned)((T + tt - 1) / tt)), dim3(64 * GS_W), 0, s, (const uint16_t *)hidden,
-                       (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff, nkk, ln_eps, scores, gates);
+                       (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff, nkk, ln_eps, H, Nrow, scores,
+                       gates);
   } else {
-    hipLaunchKernelGGL(gate_score_f32_kernel, dim3((unsigned)T), dim3(256), (size_t)d * sizeof(float), s,
+    hipLaunchKernelGGL(gate_score_f32_kernel, dim3((unsigned)T), dim3(256), (size_t)(d + d_ff) * sizeof(float), s,
                        (const float *)hidden, (const float *)w1, (const float *)w2, forced, T, d, d_ff,
-                       (const float *)ln_w, ln_eps, ln, scores, gates);
+                       (const float *)ln_w, ln_eps, ln, H, Nrow, scores, gates);
   }
   return hipGetLastError();
 }

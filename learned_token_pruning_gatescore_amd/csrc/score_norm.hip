@@ -90,13 +90,15 @@ __device__ __forceinline__ void load_chunk(const T *row, int64_t base, int64_t n
   }
 }
 
+// Row blockIdx.x of [rows, N]; with per-head scores [B, H, N] the rows are
+// (b, h) and the forced mask is b's: row / heads.
 template <int V>
 __global__ __launch_bounds__(SN_T) void score_normalize_kernel(const float *s, const uint8_t *__restrict__ forced,
-                                                              int64_t N, float eps, float *out) {
+                                                              int64_t N, float eps, int heads, float *out) {
   __shared__ float red[SN_T / 64];
   const int64_t b = blockIdx.x;
   const float *row = s + b * N;
-  const uint8_t *f = forced ? forced + b * N : nullptr;
+  const uint8_t *f = forced ? forced + (b / heads) * N : nullptr;
   float x[SN_R];
   uint8_t fx[SN_R];
   float ss = 0.f, np = 0.f;  // np: exact in fp32 (at most 2^24 positions per row)
@@ -140,12 +142,12 @@ __global__ __launch_bounds__(SN_T) void score_normalize_kernel(const float *s, c
 
 template <int V>
 __global__ __launch_bounds__(SN_T) void gate_softmax_kernel(const float *__restrict__ xin,
-                                                           const int32_t *__restrict__ kept, int64_t M,
+                                                           const int32_t *__restrict__ kept, int64_t M, int heads,
                                                            float *__restrict__ g) {
   __shared__ float red[SN_T / 64];
-  const int64_t b = blockIdx.x;
+  const int64_t b = blockIdx.x;  // row (b, h) with per-head scores: kept row b / heads
   const float *row = xin + b * M;
-  const int32_t *k = kept ? kept + b * M : nullptr;
+  const int32_t *k = kept ? kept + (b / heads) * M : nullptr;
   float x[SN_R];
   int32_t kx[SN_R];
   auto load = [&](int64_t base) __attribute__((always_inline)) {
@@ -221,22 +223,60 @@ __global__ __launch_bounds__(SN_T) void gate_softmax_bwd_kernel(const float *__r
   }
 }
 
+// Uniform aggregation over heads for selection: out[b][n] = (sum_h s[b][h][n]) / H,
+// heads summed in order.
+__global__ __launch_bounds__(256) void aggregate_heads_kernel(const float *__restrict__ s, int64_t B, int H, int64_t N,
+                                                             float *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * N) return;
+  const int64_t b = i / N, n = i - b * N;
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) acc += s[(b * H + h) * N + n];
+  out[i] = acc / (float)H;
+}
+
+// out[b][h][m] = s[b][h][kept[b][m]] (0 for padding, kept < 0)
+__global__ __launch_bounds__(256) void gather_heads_kernel(const float *__restrict__ s, const int32_t *__restrict__ kept,
+                                                          int64_t B, int H, int64_t N, int64_t M,
+                                                          float *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * H * M) return;
+  const int64_t bh = i / M, m = i - bh * M, b = bh / H;
+  const int32_t j = kept[b * M + m];
+  out[i] = (j >= 0 && j < N) ? s[bh * N + j] : 0.f;
+}
+
 hipError_t launch_score_normalize(const float *s, const uint8_t *forced, int64_t B, int64_t N, float eps, float *out,
-                                  hipStream_t st) {
+                                  hipStream_t st, int heads) {
   if (B * N == 0) return hipSuccess;
   if (N % 4 == 0)
-    hipLaunchKernelGGL(score_normalize_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, out);
+    hipLaunchKernelGGL(score_normalize_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, heads, out);
   else
-    hipLaunchKernelGGL(score_normalize_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, out);
+    hipLaunchKernelGGL(score_normalize_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, s, forced, N, eps, heads, out);
   return hipGetLastError();
 }
 
-hipError_t launch_gate_softmax(const float *x, const int32_t *kept, int64_t B, int64_t M, float *g, hipStream_t st) {
+hipError_t launch_gate_softmax(const float *x, const int32_t *kept, int64_t B, int64_t M, float *g, hipStream_t st,
+                               int heads) {
   if (B * M == 0) return hipSuccess;
   if (M % 4 == 0)
-    hipLaunchKernelGGL(gate_softmax_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, g);
+    hipLaunchKernelGGL(gate_softmax_kernel<4>, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, heads, g);
   else
-    hipLaunchKernelGGL(gate_softmax_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, g);
+    hipLaunchKernelGGL(gate_softmax_kernel<1>, dim3((unsigned)B), dim3(SN_T), 0, st, x, kept, M, heads, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_aggregate_heads(const float *s, int64_t B, int H, int64_t N, float *out, hipStream_t st) {
+  if (B * N == 0) return hipSuccess;
+  hipLaunchKernelGGL(aggregate_heads_kernel, dim3((unsigned)((B * N + 255) / 256)), dim3(256), 0, st, s, B, H, N, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_heads(const float *s, const int32_t *kept, int64_t B, int H, int64_t N, int64_t M, float *out,
+                               hipStream_t st) {
+  if (B * H * M == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_heads_kernel, dim3((unsigned)((B * H * M + 255) / 256)), dim3(256), 0, st, s, kept, B, H,
+                     N, M, out);
   return hipGetLastError();
 }
 

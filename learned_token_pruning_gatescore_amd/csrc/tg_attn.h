@@ -33,14 +33,16 @@ size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64
 AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
                             int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
-                            const AttnWs &w, hipStream_t s);
+                            bool g_per_head, const AttnWs &w, hipStream_t s);
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
-                           int Hkv, int D, bool bf16, void *o, float *lse, const AttnWs &w, hipStream_t s);
+                           int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, const AttnWs &w,
+                           hipStream_t s);
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
-                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, float *dq, float *dk,
-                           float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w, hipStream_t s);
+                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, bool g_per_head,
+                           float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w,
+                           hipStream_t s);
 
 hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, float *dsigma, hipStream_t s);
 

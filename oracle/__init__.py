@@ -70,6 +70,7 @@ def _load():
     lib.tgo_attn_bwd.restype = ctypes.c_int
     lib.tgo_round_bf16.argtypes = [ctypes.c_double]
     lib.tgo_gate_score_heads.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, _D]
+    lib.tgo_rms_norm.argtypes = [_D, _D, ctypes.c_double, _i64, _i64, _D]
     lib.tgo_gate_score_ln.argtypes = [_D, _D, ctypes.c_double, _D, _D, _U8, _i64, _i64, _i64, _D, _D]
     lib.tgo_score_normalize.argtypes = [_D, _U8, _i64, _i64, ctypes.c_double, _D]
     lib.tgo_gate_softmax.argtypes = [_D, _I32, _i64, _i64, _D]
@@ -138,6 +139,17 @@ def gate_score_ln(hidden, ln_w, eps, w1, w2, forced=None):
     lib.tgo_gate_score_ln(_ptr(h, _D), _ptr(lw, _D), float(eps), _ptr(W1, _D), _ptr(W2, _D), _ptr(f, _U8), T, d,
                           d_ff, _ptr(s, _D), _ptr(g, _D))
     return s, g
+
+
+def rms_norm(hidden, ln_w, eps):
+    """LN2 as RMSNorm (DeepDive section 2 Eq. 1): rows divided by their root mean square (+eps), times w."""
+    lib = _load()
+    h = _f64(hidden)
+    T, d = h.shape
+    lw = None if ln_w is None else _f64(ln_w).reshape(d)
+    out = np.empty((T, d), np.float64)
+    lib.tgo_rms_norm(_ptr(h, _D), _ptr(lw, _D), float(eps), T, d, _ptr(out, _D))
+    return out
 
 
 def gate_score_heads(hidden, w1, w2):

@@ -565,11 +565,8 @@ int tgo_attn_bwd(const double *q, const double *k, const double *v, const double
  * the normaliser of the Qwen3 models the pages evaluate; ln_w NULL means
  * w = 1.  Then the scorer of section a1 above on a~.
  */
-void tgo_gate_score_ln(const double *hidden, const double *ln_w, double eps, const double *w1,
-                       const double *w2, const uint8_t *forced, int64_t T, int64_t d, int64_t d_ff,
-                       double *scores, double *gates)
+void tgo_rms_norm(const double *hidden, const double *ln_w, double eps, int64_t T, int64_t d, double *out)
 {
-    double *norm = (double *)malloc((size_t)(T * d) * sizeof(double));
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         const double *h = hidden + t * d;
@@ -578,8 +575,16 @@ void tgo_gate_score_ln(const double *hidden, const double *ln_w, double eps, con
             ss += h[i] * h[i];
         double r = 1.0 / sqrt(ss / (double)d + eps);
         for (int64_t i = 0; i < d; ++i)
-            norm[t * d + i] = h[i] * r * (ln_w ? ln_w[i] : 1.0);
+            out[t * d + i] = h[i] * r * (ln_w ? ln_w[i] : 1.0);
     }
+}
+
+void tgo_gate_score_ln(const double *hidden, const double *ln_w, double eps, const double *w1,
+                       const double *w2, const uint8_t *forced, int64_t T, int64_t d, int64_t d_ff,
+                       double *scores, double *gates)
+{
+    double *norm = (double *)malloc((size_t)(T * d) * sizeof(double));
+    tgo_rms_norm(hidden, ln_w, eps, T, d, norm);
     tgo_gate_score(norm, w1, w2, forced, T, d, d_ff, scores, gates);
     free(norm);
 }

@@ -198,3 +198,38 @@ def test_varlen_validation():
     assert b(*bargs(lse=None)) == 1
     assert b(*bargs(sigma=FAKE)) == 1          # sigma without dsigma
     assert b(*bargs()) == 3                    # workspace too small
+
+
+def test_heads_validation():
+    lib = _lib()
+    i64 = ctypes.c_int64
+    f = lib.tg_gate_score_heads
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                  i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    assert f(FAKE, 0, None, 0.0, FAKE, FAKE, 1, 10, 64, 16, 17, 1, FAKE, FAKE, 1 << 30, None) == 2  # H > 16
+    assert f(FAKE, 0, None, 0.0, FAKE, FAKE, 1, 10, 64, 16, 0, 1, FAKE, FAKE, 1 << 30, None) == 2   # H < 1
+    assert f(FAKE, 1, None, -1.0, FAKE, FAKE, 1, 10, 64, 16, 4, 1, FAKE, FAKE, 1 << 30, None) == 1  # eps
+    assert f(FAKE, 0, None, 0.0, FAKE, FAKE, 1, 10, 64, 16, 4, 1, FAKE, FAKE, 16, None) == 3        # workspace
+    n = lib.tg_score_normalize_heads
+    n.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, i64, i64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    assert n(FAKE, None, 1, 0, 10, 1e-6, FAKE, None) == 1
+    assert n(None, None, 1, 2, 10, 1e-6, FAKE, None) == 1
+    a = lib.tg_aggregate_heads
+    a.argtypes = [ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, ctypes.c_void_p]
+    assert a(FAKE, 1, 0, 10, FAKE, None) == 1
+    assert a(FAKE, 1, 2, 10, MIS, None) == 1
+    g = lib.tg_gather_heads
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, i64, i64, i64, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(FAKE, None, 1, 2, 10, 5, FAKE, None) == 1
+    s = lib.tg_gate_softmax_heads
+    s.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64, i64, i64, ctypes.c_void_p, ctypes.c_void_p]
+    assert s(FAKE, None, 1, 0, 10, FAKE, None) == 1
+    hf = lib.tg_gated_attn_fwd_headgates
+    hf.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, i64, i64, i64, i64, i64,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
+    assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 12, 8, 128, 1, FAKE, None, None, 0,
+              None) == 1  # Hq % Hkv
+    assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 16, 8, 128, 1, FAKE, None, None, 0,
+              None) == 3  # workspace

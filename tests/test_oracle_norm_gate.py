@@ -50,6 +50,12 @@ def test_ln_scorer_matches_torch_rms_norm(o):
     np.testing.assert_allclose(g, g_ref, rtol=1e-13, atol=1e-14)
 
 
+def test_rms_norm_matches_torch(o):
+    h, _, _, lw = _mlp(11, 19, 48, 8)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(h), (48,), torch.from_numpy(lw), 1e-5).numpy()
+    np.testing.assert_allclose(o.rms_norm(h, lw, 1e-5), ref, rtol=1e-13, atol=1e-15)
+
+
 def test_ln_scorer_scale_invariance_and_unit_weight(o):
     h, w1, w2, _ = _mlp(2, 25, 32, 16)
     s1, _ = o.gate_score_ln(h, None, 0.0, w1, w2)
