@@ -151,6 +151,7 @@ def run_gpu(args):
 
     temp_us = time_loop(attn_temp, args.steps, stream) * 1e6
     operative = run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M)
+    operative["per_head"] = run_operative_heads(args, tg, wl, w, dev, stream, gi, at, K, M)
 
     work = algorithmic_work(w, M)
     kern = {}
@@ -279,6 +280,72 @@ def run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M):
     tot = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])) * 1e-3
     return dict(stages_us=per, device_path_us=tot * 1e6, tokens_per_s=w.B * w.N / tot,
                 note="gate_score_ln includes its W1 pack pass (RMSNorm weight folded in)")
+
+
+def run_operative_heads(args, tg, wl, w, dev, stream, gi, at, K, M):
+    """The per-head variant (DeepDive section 3.4): the scorer with one output per query head (RMSNorm in
+    front), per-head normalisation, uniform head aggregation, selection on the aggregate, compaction,
+    per-head gather and softmax gate, attention with per-head gates, gain and temperature."""
+    import torch
+
+    H = w.Hq
+    ri = wl.residual_inputs(w)
+    T = lambda x: wl.to_torch(x, w.dtype, dev)
+    hs = [T(ri["hidden"])]
+    hs += [hs[0].clone() for _ in range(NCOPY - 1)]
+    lw, w1 = T(ri["ln_w"]), T(gi["w1"])
+    rs = np.random.default_rng(w.seed + 4000)
+    w2h = T(wl.bf16_bits((rs.standard_normal((H, w.d_ff)) / np.sqrt(w.d_ff)).astype(np.float32)))
+    forced = torch.from_numpy(gi["forced"]).to(dev)
+    q, k, v = T(at["q"]), T(at["k"]), T(at["v"])
+    gain = torch.from_numpy(np.log1p(np.exp(at["gamma"])).astype(np.float32)).to(dev)
+    sigma = torch.from_numpy(at["sigma"]).to(dev)
+    raw = torch.empty((w.B, H, w.N), device=dev)
+    b = torch.empty((w.B, H, w.N), device=dev)
+    agg = torch.empty((w.B, w.N), device=dev)
+    kept = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+    hk = torch.empty((w.B, M, w.d), dtype=hs[0].dtype, device=dev)
+    pk = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+    bk = torch.empty((w.B, H, M), device=dev)
+    g = torch.empty((w.B, H, M), device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, M), device=dev)
+    ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
+    gws = tg.gate_workspace(w.d, w.d_ff, hs[0].dtype, dev)
+    names = ["gate_score_heads", "score_normalize_heads", "aggregate_heads", "select_topk", "compact",
+             "gather_heads", "gate_softmax_heads", "attn_fwd_headgates"]
+
+    def step(i, ev=None):
+        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        rec(0)
+        tg.tg_gate_score_heads(hs[i % NCOPY], w1, w2h, raw, gws, ln_w=lw, ln_eps=1e-6)
+        rec(1)
+        tg.tg_score_normalize_heads(raw, forced, 1e-6, b)
+        rec(2)
+        tg.tg_aggregate_heads(b, agg)
+        rec(3)
+        tg.tg_select_topk(agg, forced, K, w.n_forced, kept)
+        rec(4)
+        tg.tg_compact(hs[i % NCOPY], None, None, kept, hk, pk, None)
+        rec(5)
+        tg.tg_gather_heads(b, kept, bk)
+        rec(6)
+        tg.tg_gate_softmax_heads(bk, kept, g)
+        rec(7)
+        tg.tg_gated_attn_fwd_headgates(q, k, v, g, gain, pk, wl.ROPE_THETA, w.tau, o, lse, ws, sigma=sigma)
+        rec(8)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    for i, e in enumerate(evs):
+        step(i, e)
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3 for j, n in enumerate(names)}
+    tot = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])) * 1e-3
+    return dict(heads=H, stages_us=per, device_path_us=tot * 1e6, tokens_per_s=w.B * w.N / tot,
+                note="gate_score_heads includes its W1 pack pass (RMSNorm weight folded in)")
 
 
 def run_train(args, tg, wl, dev):
