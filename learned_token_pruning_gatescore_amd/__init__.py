@@ -148,8 +148,9 @@ def _ptr(t):
 
 
 def _stream(stream):
+    """The HIP stream handle: a torch Stream, a raw handle, or None for torch's current stream."""
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
 
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
