@@ -22,7 +22,11 @@
 //   * O^T = V^T P^T reads V through the transposing LDS read
 //     ds_read_b64_tr_b16; Q (rotated) lives in registers for the whole loop;
 //   * 32-key tiles in chunk-major LDS layout (tg_tile.h), filled by direct
-//     global->LDS loads two tiles ahead (one barrier per tile);
+//     global->LDS loads AF_NS - 1 tiles ahead into a ring of AF_NS slots (one barrier
+//     per tile), issued by one wave per SIMD;
+//   * software pipeline per wave: S^T of tile t+1 on the matrix cores while the
+//     softmax of tile t runs on the vector units; the per-key bias enters the
+//     S^T products through their extra 16-deep step;
 //   * softmax in fp32 against a fixed per-column reference, P rounded to
 //     bf16 for the MFMA, row sums in fp32.
 #include "tg_common.h"
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
 // to arrive merges all pieces in piece order (deterministic) and writes o, lse.
 // ---------------------------------------------------------------------------
 constexpr int AF_TK = AB_T;  // keys per tile
+constexpr int AF_NS = 4;     // slots of the LDS tile ring (loads go out AF_NS - 1 tiles ahead)
 
 template <int D>
 struct FwdCfg {
@@ -147,6 +152,29 @@ __host__ __device__ inline int fwd_ntiles(int qb, int BQ, int M) {
 }
 __host__ __device__ inline int fwd_npieces(int n, int C) { return (n + C - 1) / C; }
 
+// x as three bf16 parts (hi, mid, lo; their sum is x to about 2^-24 relative).
+__device__ __forceinline__ void split3(float x, uint32_t &h, uint32_t &m, uint32_t &l) {
+  h = pack_bf16x2(x, 0.f) & 0xFFFFu;
+  const float r1 = x - bf16_lo(h);
+  m = pack_bf16x2(r1, 0.f) & 0xFFFFu;
+  l = pack_bf16x2(r1 - bf16_lo(m), 0.f) & 0xFFFFu;
+}
+// Operands of the extra 16-deep step of an S^T = K Q^T product (32x32x16
+// layout: element k of row i in lane i + 32 (k / 8)).  Key side (A, one row
+// per key): ones at k = 0..2, the key's x in three parts at k = 3..5.  Query
+// side (B, one column per query): the column's x in three parts at k = 0..2,
+// ones at k = 3..5.  The step adds key value + query value to every product.
+__device__ __forceinline__ u32x4 aug_key(float x, int hl) {
+  uint32_t h, m, l;
+  split3(x, h, m, l);
+  return hl == 0 ? u32x4{0x3F803F80u, 0x3F80u | (h << 16), m | (l << 16), 0u} : u32x4{0u, 0u, 0u, 0u};
+}
+__device__ __forceinline__ u32x4 aug_query(float x, int hl) {
+  uint32_t h, m, l;
+  split3(x, h, m, l);
+  return hl == 0 ? u32x4{h | (m << 16), l | (0x3F80u << 16), 0x3F803F80u, 0u} : u32x4{0u, 0u, 0u, 0u};
+}
+
 template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
@@ -156,11 +184,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   using T = BTile<D>;
   using F = FwdCfg<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
-  constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
+  // The tiles' direct loads are issued by the first wave of each SIMD only
+  // (waves 0..3): issuing them takes the vector-memory path a few hundred
+  // clocks per tile, and those waves reach the barrier first.
+  constexpr int NLW = 4;                  // loader waves
+  constexpr int NIW = 2 * T::NI / NLW;    // K and V direct loads per loader wave per tile
   constexpr int NVM = NIW + 1;            // + the bias load (wave 0 only)
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[3 * T::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[3 * T::TILE];
-  __shared__ __attribute__((aligned(1024))) float sBias[3][8][AF_TK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[AF_NS * T::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[AF_NS * T::TILE];
+  __shared__ __attribute__((aligned(1024))) float sBias[AF_NS][8][AF_TK];
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -218,42 +250,45 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
 
   BFrag<D> fr;
   fr.init(lane);
-  // direct load j = wave + 8 n of the tile's 2 NI (K first, then V)
+  // loader wave w issues direct load j = w + 4 n of the tile's 2 NI (K for
+  // n < NIW / 2, then V)
+  const bool loader = wave < NLW;
   uint32_t dgo[NIW], dlo[NIW];
-  bool isv[NIW];
 #pragma unroll
   for (int n = 0; n < NIW; ++n) {
-    const int j = wave + AB_NW * n;
-    isv[n] = j >= T::NI;
-    dgo[n] = T::goff(j % T::NI, lane, rsb);
-    dlo[n] = 1024u * (uint32_t)(j % T::NI);
+    const int j = (wave % NLW + NLW * n) % T::NI;
+    dgo[n] = T::goff(j, lane, rsb);
+    dlo[n] = 1024u * (uint32_t)j;
   }
   // bias: wave 0 loads the G rows of the tile (8 lanes x 16 bytes per head)
   const bool breal = wave == 0 && (lane >> 3) < G;
   const uint32_t bvo = (uint32_t)((((lane >> 3) * M) + 4 * (lane & 7)) * 4);
-  const u32x4 kones = ones3(hl);
-
-  auto slot = [](int t) __attribute__((always_inline)) { return t % 3; };
+  auto slot = [](int t) __attribute__((always_inline)) { return t & (AF_NS - 1); };
   auto issue = [&](int t) __attribute__((always_inline)) {
+    if (!loader) return;
     const bool live = t < nt;
     const uint32_t toff = (uint32_t)((kt0 + t) * AF_TK) * rsb;  // uniform
     const uint32_t so = 2u * (uint32_t)(slot(t) * T::TILE);
 #pragma unroll
     for (int n = 0; n < NIW; ++n)
-      dma_b128(isv[n] ? rV : rK, (isv[n] ? lds_addr(sV) : lds_addr(sK)) + so + dlo[n],
+      dma_b128(n >= NIW / 2 ? rV : rK, (n >= NIW / 2 ? lds_addr(sV) : lds_addr(sK)) + so + dlo[n],
                live ? dgo[n] + toff : 0x80000000u, 0u);
     const uint32_t boff = (uint32_t)((kvh * G * M + (kt0 + t) * AF_TK) * 4);  // uniform
     if (wave == 0) dma_b128(rB, lds_addr(&sBias[slot(t)][0][0]), live && breal ? bvo + boff : 0x80000000u, 0u);
   };
   // wait for this wave's loads of the oldest tile in flight, then the barrier
   auto sync_tile = [&]() __attribute__((always_inline)) {
-    if (wave == 0) sync_vm<NVM>();
-    else sync_vm<NVM - 1>();
+    if (wave == 0) sync_vm<(AF_NS - 3) * NVM>();
+    else if (loader) sync_vm<(AF_NS - 3) * (NVM - 1)>();
+    else sync_vm<0>();
+  };
+  auto issue_first = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < AF_NS - 1; ++t) issue(t);
   };
   // The first pass's direct loads go out first; the Q and rotation loads
   // below (all issued before any use) overlap with them.
-  issue(0);
-  issue(1);
+  issue_first();
 
   // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8]
   u32x4 qf[NKS];
@@ -285,104 +320,143 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   }
 
   // Temperature of the column's row (1 without it): x = t (c2 s + bias).  t is
-  // kept >= 1e-30 so that a key with bias -inf stays at -inf (t = 0 at the
-  // first row, where every live logit is 0 either way).
+  // kept >= 1e-30 (t = 0 at the first row, where every live logit is 0 either
+  // way).
   float tq = 1.f;
   if (TEMP && vq) tq = fmaxf(softplus_f(sigma[kvh * G + hloc]) * ratio[bM + qi], 1e-30f);
-  // m2: reference maximum of the column (probabilities are 2^(x - m2)); the
-  // S^T products subtract m2 / (t c2) themselves through the extra step qaug.
+  const float tc2 = c2 * tq;           // logit = tc2 * (S^T entry)
+  const float inv_c2 = 1.f / tc2;      // reference -> S units
+  const float inv_c2k = 1.f / c2;      // bias -> S units
+  // m2: reference maximum of the column (probabilities are 2^(x - m2)).  The
+  // extra 16-deep step of every S^T product adds bias_j / c2 (key side) and
+  // -m2 / (t c2) (query side), each as three bf16 parts against ones, so the
+  // logit is one multiply.  A key with bias -inf enters as -2^127 / c2 ...
+  // -2^127: its logit is at most -2^127 t c2 <= -1e7 below the reference, and
+  // its probability 0.
   float m2 = 0.f, lsum = 0.f;
-  u32x4 qaug = u32x4{0u, 0u, 0u, 0u};
-  const float inv_c2 = TEMP ? 1.f / (c2 * tq) : 1.f / c2;
+  u32x4 qaug = aug_query(0.f, hl);
   f32x16 acc[NDB];
 
-  // S^T = K Q^T over the head dim, fragments read two steps ahead
-  auto sprod = [&](const uint16_t *K, f32x16 &s) __attribute__((always_inline)) {
-    u32x4 f[NKS];
-    f[0] = fr.rows(K, 0);
-    f[1] = fr.rows(K, 1);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (ks + 2 < NKS) f[ks + 2] = fr.rows(K, ks + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      s = mfma32(f[ks], qf[ks], s);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  // S^T = K Q^T + extra step for tile t (K fragments read three steps ahead)
+  auto key_aug = [&](float bv) __attribute__((always_inline)) {
+    return aug_key(fmaxf(bv * inv_c2k, -0x1p127f), hl);
   };
-  // O^T[db] += V^T[db] P^T over the tile's keys, transposing reads two steps ahead
-  auto pvprod = [&](const uint16_t *V, const u32x4(&x)[2]) __attribute__((always_inline)) {
-    u32x4 f[2 * NDB];
-    f[0] = fr.tr(V, 0, 0);
-    f[1] = fr.tr(V, 0, 1);
-#pragma unroll
-    for (int i = 0; i < 2 * NDB; ++i) {
-      if (i + 2 < 2 * NDB) f[i + 2] = fr.tr(V, (i + 2) / NDB, (i + 2) % NDB);
-      __builtin_amdgcn_sched_barrier(0);
-      acc[i % NDB] = mfma32(f[i], x[i / NDB], acc[i % NDB]);
-      __builtin_amdgcn_sched_barrier(0);
+  // softmax of 2 of the 16 logits per lane (registers 2c, 2c+1) of a tile
+  auto soft2 = [&](const f32x16 &s, int c, float msub, bool masked, int lim, float &ps, u32x4(&pf)[2])
+      __attribute__((always_inline)) {
+    float x0 = __builtin_fmaf(s[2 * c], tc2, -msub), x1 = __builtin_fmaf(s[2 * c + 1], tc2, -msub);
+    if (masked) {
+      if (acc_row(2 * c, hl) > lim) x0 = -INFINITY;
+      if (acc_row(2 * c + 1, hl) > lim) x1 = -INFINITY;
     }
+    const float p0 = fast_exp2(x0), p1 = fast_exp2(x1);
+    const uint32_t pk = pack_bf16x2(p0, p1);
+    ps += p0 + p1;  // fp32 sums: the row statistics (lse) stay exact to fp32
+    // an empty volatile statement on the results keeps this work where it is
+    // written (between the products it overlaps) instead of sunk to its uses
+    asm volatile("" : "+v"(ps) : "v"(pk));
+    pf[c >> 2][c & 3] = pk;
   };
-  // One tile: wait for it, issue tile t+2, S^T, the softmax of its 16 logits per
-  // lane (ref: the first tile of the first pass, which sets the reference), P V.
-  auto tile = [&](int t, bool masked, bool ref) __attribute__((always_inline)) {
+  // One step of the software pipeline: wait for tile t+1;
+  // S^T of tile t+1 on the matrix cores while the first half of the softmax
+  // of tile t (S^T in sc, msub the reference it was computed without) runs on
+  // the vector units; then O^T += V^T P^T of tile t, its first 16 keys while
+  // the second half of the softmax runs; then the loads of tile t+AF_NS-1.
+  // After the barrier every wave is done with tile t-1, whose ring slot that
+  // tile takes.
+  auto step = [&](int t, f32x16 &sc, bool masked, float msub) __attribute__((always_inline)) {
     sync_tile();
-    issue(t + 2);
-    const uint16_t *K = sK + slot(t) * T::TILE, *V = sV + slot(t) * T::TILE;
-    f32x16 s = mfma32(kones, qaug, f32x16{});
-    sprod(K, s);
-    const float *bi = &sBias[slot(t)][hloc][4 * hl];
+    const uint16_t *K = sK + slot(t + 1) * T::TILE, *V = sV + slot(t) * T::TILE;
+    const float bnext = sBias[slot(t + 1)][hloc][l32];
     const int lim = qi - (kt0 + t) * AF_TK;  // keys (within the tile) past the query are masked
-    float x[16];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float2 bv = *(const float2 *)(bi + 8 * (j >> 1) + 2 * (j & 1));
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = 2 * j + e;
-        x[r] = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
-        if (TEMP) x[r] *= tq;
-        if (masked && acc_row(r, hl) > lim) x[r] = -INFINITY;
-      }
-    }
-    if (ref) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m2 = mx == -INFINITY ? 0.f : mx;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] -= m2;
-      qaug = aug3(-m2 * inv_c2, hl);
-    }
+    f32x16 sn = f32x16{};
     float ps = 0.f;
     u32x4 pf[2];
+    {
+      u32x4 f[NKS];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+      for (int i = 0; i < 3; ++i) f[i] = fr.rows(K, i);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = fast_exp2(x[8 * hf + 2 * w]), p1 = fast_exp2(x[8 * hf + 2 * w + 1]);
-        ps += p0 + p1;  // fp32 sums: the row statistics (lse) stay exact to fp32
-        pf[hf][w] = pack_bf16x2(p0, p1);
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 3 < NKS) f[ks + 3] = fr.rows(K, ks + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        sn = mfma32(f[ks], qf[ks], sn);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)  // chunk c after the last product of its quarter of the k-steps
+          if ((c + 1) * NKS / 4 - 1 == ks) soft2(sc, c, msub, masked, lim, ps, pf);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    sn = mfma32(key_aug(bnext), qaug, sn);
+    {
+      u32x4 f[2 * NDB];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) f[i] = fr.tr(V, i / NDB, i % NDB);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) {
+        if (i + 3 < 2 * NDB) f[i + 3] = fr.tr(V, (i + 3) / NDB, (i + 3) % NDB);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i % NDB] = mfma32(f[i], pf[i / NDB], acc[i % NDB]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)  // chunks 4..7 spread over the products of the first 16 keys
+          if (i < NDB && c * NDB / 4 == i) soft2(sc, 4 + c, msub, masked, lim, ps, pf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     lsum += ps;
-    pvprod(V, pf);
+    sc = sn;
+    issue(t + AF_NS - 1);  // the loader waves, after their work: into tile t-1's slot
   };
   auto run = [&](bool first) __attribute__((always_inline)) {
-    if (!first) {  // a repeated pass refills the ring (the first pass's loads went out above)
-      issue(0);
-      issue(1);
-    }
+    if (!first) issue_first();  // a repeated pass refills the ring (the first pass's loads went out above)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
     lsum = 0.f;
-    int t = 0;
-    if (first) {  // tile 0 sets the reference
-      if (tu > 0) tile(0, false, true);
-      else tile(0, true, true);
-      t = 1;
+    // prologue: S^T of tile 0 (tiles 1 .. AF_NS - 2 may still be in flight)
+    if (wave == 0) sync_vm<(AF_NS - 2) * NVM>();
+    else if (loader) sync_vm<(AF_NS - 2) * (NVM - 1)>();
+    else sync_vm<0>();
+    f32x16 sc = f32x16{};
+    float msub = 0.f;
+    {
+      const uint16_t *K = sK + slot(0) * T::TILE;
+      const float b0 = sBias[slot(0)][hloc][l32];
+      u32x4 f[NKS];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) f[i] = fr.rows(K, i);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 3 < NKS) f[ks + 3] = fr.rows(K, ks + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        sc = mfma32(f[ks], qf[ks], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sc = mfma32(key_aug(b0), qaug, sc);
+      if (first) {  // tile 0 sets the reference: the maximum over its live keys
+        const uint64_t dead = __ballot(b0 == -INFINITY);  // bit j (j < 32): key j of the tile
+        const int lim = qi - kt0 * AF_TK;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row(r, hl);
+          const bool live = !((dead >> row) & 1u) && !(tu == 0 && row > lim);
+          if (live) mx = fmaxf(mx, sc[r] * tc2);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m2 = mx == -INFINITY ? 0.f : mx;
+        msub = m2;  // tile 0's products ran without it
+        qaug = aug_query(-m2 * inv_c2, hl);
+      }
     }
-    for (; t < tu; ++t) tile(t, false, false);
-    for (; t < nt; ++t) tile(t, true, false);
+    int t = 0;
+    for (; t < tu; ++t) {
+      step(t, sc, false, msub);
+      msub = 0.f;
+    }
+    for (; t < nt; ++t) {
+      step(t, sc, true, msub);
+      msub = 0.f;
+    }
     sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
   };
   for (int pass = 0; pass < 4; ++pass) {
@@ -391,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const bool bad = !(lt < 0x1p64f);
     if (!__syncthreads_or(bad) || pass == 3) break;
     if (bad) m2 += lt < INFINITY ? __log2f(lt) : 120.f;
-    qaug = aug3(-m2 * inv_c2, hl);
+    qaug = aug_query(-m2 * inv_c2, hl);
   }
 
   // Split block: publish this piece, the last one to finish merges.  Records
