@@ -118,7 +118,8 @@ __global__ __launch_bounds__(SEL_T) void select_topk_kernel(
   const float *sc = scores + b * N;
   const uint8_t *fo = forced ? forced + b * N : nullptr;
   int32_t *out = kept + b * M_alloc;
-  const int nchunks = (int)((N + SEL_CHUNK - 1) / SEL_CHUNK);
+  // one chunk (N <= 32768): a compile-time single trip, so the keys die after their last use
+  const int nchunks = RES ? 1 : (int)((N + SEL_CHUNK - 1) / SEL_CHUNK);
   const bool vec_s = ((uintptr_t)sc & 15) == 0;
   const bool vec_f = fo && ((uintptr_t)fo & 15) == 0;
 

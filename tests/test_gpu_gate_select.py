@@ -192,6 +192,22 @@ def test_select_clustered_32k():
     assert got.shape == (1, 2176) and cnt[0] == 2176
 
 
+@pytest.mark.parametrize("B,N,K,nF", [(2, 32771, 2048, 128), (3, 40001, 5000, 7), (1, 32768, 32640, 128),
+                                       (2, 4099, 1, 0)])
+def test_select_ragged_rows_and_chunks(B, N, K, nF):
+    # rows that start off 16-byte alignment (N % 4 != 0), a second partial chunk, a budget that keeps all but one
+    # forced-free token, and a single kept token
+    rng = np.random.default_rng(N + K)
+    s = rng.standard_normal((B, N)).astype(np.float32)
+    s[:, rng.choice(N, N // 10, replace=False)] = 0.5  # a large tie class
+    f = np.zeros((B, N), np.uint8)
+    for b in range(B):
+        f[b, rng.choice(N, nF, replace=False)] = 1
+    got, cnt, ref, rc = _select(s, f, K, nF)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(cnt, rc)
+
+
 @pytest.mark.parametrize("K", [256, 1024, 4096, 16384])
 def test_select_sweep_128k(K):
     w = wl.WORKLOADS["sweep_128k"]
