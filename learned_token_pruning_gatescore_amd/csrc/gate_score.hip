@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
   static_assert(NI >= 1 && TT % (8 * GS_W) == 0, "tile rows must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint16_t sH[GS_NB * ST];
   __shared__ float sRed[GS_W][TT];
-  __shared__ float sW2[MH ? GS_HMAX * GS_U : GS_U];
+  __shared__ float sW2[GS_U];
   __shared__ float sSq[LN ? GS_W : 1][64];
   __shared__ float sR[LN ? TT : 1];
   constexpr int SQP = GS_W / NTB;  // waves sharing one fragment's squares (by step parity)
@@ -150,19 +150,15 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
   }
 
   float run = 0.f;  // running score of token t0 + tid (tid < TT), across unit chunks
-  float runh[MH ? GS_HMAX : 1];  // MH: one per head
+  // MH: running scores of the (head, token) pairs (tid / TT + k NPS, t0 + tid % TT), k < NPH
+  constexpr int NPS = 64 * GS_W / TT, NPH = GS_HMAX / NPS;
+  float runh[MH ? NPH : 1];
 #pragma unroll
-  for (int h = 0; h < (MH ? GS_HMAX : 1); ++h) runh[h] = 0.f;
+  for (int k = 0; k < (MH ? NPH : 1); ++k) runh[k] = 0.f;
 
   for (int c = 0; c < d_ff; c += GS_U) {
-    if (MH) {
-      for (int i = tid; i < H * GS_U; i += 64 * GS_W) {
-        const int h = i / GS_U, u = i - h * GS_U;
-        sW2[i] = c + u < d_ff ? __uint_as_float((uint32_t)w2[(int64_t)h * d_ff + c + u] << 16) : 0.f;
-      }
-    } else {
+    if (!MH)
       for (int i = tid; i < GS_U; i += 64 * GS_W) sW2[i] = c + i < d_ff ? __uint_as_float((uint32_t)w2[c + i] << 16) : 0.f;
-    }
     // this wave's unit groups: c / 32 + GS_UB wave + ub, ub < GS_UB
     const uint16_t *ap = w1p + ((int64_t)(c / 32 + GS_UB * wave) * nkk) * 512 + lane * 8;
     auto load_a1 = [&](int kk, int ub) {
@@ -268,46 +264,77 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
       for (int tb = 0; tb < NTB; ++tb) rt[tb] = sR[32 * tb + l32];
     }
     if (MH) {
-      // SiLU in place, then per head: times that head's w2 row, summed over this
-      // lane's units, the two halves and the waves (fixed order)
+      // The head sums are a second matrix product, C2[h][t] = sum_u w2[h][u] SiLU(a[u][t]),
+      // over this wave's 64 units, four 16-unit steps.  The accumulator layout already is
+      // the B operand: in step (ub, s) the lane of token j and half q holds, as element e,
+      // registers 8 s + e of acc[ub][tb], i.e. unit 32 ub + 16 s + 8 (e / 4) + 4 q + e % 4;
+      // the A operand (rows = heads, H <= 16 of 32) takes w2 in that unit order.  SiLU
+      // enters as two bf16 parts (fp32 accumulate).
+      u32x4 a2[GS_UB][2];
 #pragma unroll
       for (int ub = 0; ub < GS_UB; ++ub)
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
+        for (int sh = 0; sh < 2; ++sh) {
+          const int u0 = c + wave * 32 * GS_UB + 32 * ub + 16 * sh + 4 * hl;  // units u0 + {0..3}, u0 + 8 + {0..3}
+          const uint16_t *wr = w2 + (int64_t)l32 * d_ff;
+          uint32_t e16[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float x = LN ? acc[ub][tb][r] * rt[tb] : acc[ub][tb][r];
-            acc[ub][tb][r] = x * fast_rcp(1.f + fast_exp2(-x * kLog2e));
+          for (int e = 0; e < 8; ++e) {
+            const int u = u0 + 8 * (e >> 2) + (e & 3);
+            e16[e] = (l32 < H && u < d_ff) ? (uint32_t)wr[u] : 0u;
           }
-      for (int h = 0; h < H; ++h) {
-        float ph[NTB];
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) ph[tb] = 0.f;
+          for (int w = 0; w < 4; ++w) a2[ub][sh][w] = e16[2 * w] | (e16[2 * w + 1] << 16);
+        }
+      f32x16 c2[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        c2[tb] = f32x16{};
 #pragma unroll
         for (int ub = 0; ub < GS_UB; ++ub)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 wv = *(const f32x4 *)&sW2[h * GS_U + wave * 32 * GS_UB + ub * 32 + 8 * g4 + 4 * hl];
+          for (int sh = 0; sh < 2; ++sh) {
+            // SiLU as a bf16 pair hi + lo (|SiLU - hi - lo| <= 2^-17 |SiLU|): two products
+            u32x4 bh, bl;
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) ph[tb] = __builtin_fmaf(acc[ub][tb][g4 * 4 + e], wv[e], ph[tb]);
+            for (int w = 0; w < 4; ++w) {
+              float x0 = acc[ub][tb][8 * sh + 2 * w], x1 = acc[ub][tb][8 * sh + 2 * w + 1];
+              if (LN) {
+                x0 *= rt[tb];
+                x1 *= rt[tb];
+              }
+              const float s0 = x0 * fast_rcp(1.f + fast_exp2(-x0 * kLog2e));
+              const float s1 = x1 * fast_rcp(1.f + fast_exp2(-x1 * kLog2e));
+              bh[w] = pack_bf16x2(s0, s1);
+              bl[w] = pack_bf16x2(s0 - bf16_lo(bh[w]), s1 - bf16_hi(bh[w]));
+            }
+            c2[tb] = mfma32(a2[ub][sh], bh, c2[tb]);
+            c2[tb] = mfma32(a2[ub][sh], bl, c2[tb]);
           }
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          ph[tb] += __shfl_xor(ph[tb], 32);
-          if (hl == 0) sRed[wave][32 * tb + l32] = ph[tb];
-        }
-        __syncthreads();
-        if (tid < TT) {
-          const float v = ((sRed[0][tid] + sRed[1][tid]) + (sRed[2][tid] + sRed[3][tid])) +
-                          ((sRed[4][tid] + sRed[5][tid]) + (sRed[6][tid] + sRed[7][tid]));
-#pragma unroll
-          for (int hh = 0; hh < GS_HMAX; ++hh)
-            if (hh == h) runh[hh] += v;
-        }
-        __syncthreads();
       }
+      // Sum over the waves (fixed order) through the hidden ring, free after the loop:
+      // red[wave][h][t], registers 0..7 of c2 hold heads 8 (r / 4) + 4 q + r % 4 < 16.
+      float *red = reinterpret_cast<float *>(sH);
+      static_assert(GS_W * GS_HMAX * TT <= GS_NB * ST / 2, "the head partials fit in the hidden ring");
+      __syncthreads();  // every wave's loads landed (drained above) and its ring reads done
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int h = 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (h < H) red[(wave * GS_HMAX + h) * TT + 32 * tb + l32] = c2[tb][r];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NPH; ++k) {
+        const int h = tid / TT + k * NPS, t = tid % TT;
+        if (h < H) {
+          const float *q = red + h * TT + t;
+          constexpr int WS = GS_HMAX * TT;  // stride between the waves' partials
+          runh[k] += ((q[0] + q[WS]) + (q[2 * WS] + q[3 * WS])) + ((q[4 * WS] + q[5 * WS]) + (q[6 * WS] + q[7 * WS]));
+        }
+      }
+      __syncthreads();  // the ring is refilled by the next chunk
       continue;
     }
     // Epilogue: SiLU, times w2, summed over this lane's units.
@@ -344,12 +371,14 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
   }
 
   if (MH) {
-    const int64_t t = t0 + tid;
-    if (tid < TT && t < T) {
+    const int64_t t = t0 + tid % TT;
+    if (t < T) {
       const int64_t b = t / Nrow, n = t - b * Nrow;
 #pragma unroll
-      for (int h = 0; h < GS_HMAX; ++h)
-        if (h < H) scores[(b * H + h) * Nrow + n] = runh[h];
+      for (int k = 0; k < NPH; ++k) {
+        const int h = tid / TT + k * NPS;
+        if (h < H) scores[(b * H + h) * Nrow + n] = runh[k];
+      }
     }
     return;
   }
