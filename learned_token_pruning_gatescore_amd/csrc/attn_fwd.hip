@@ -128,7 +128,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
 // 16-deep step; no rescaling in the loop.  While the row sum stays below 2^64,
 // O and the sums are far from fp32 overflow and the result is exact up to
 // rounding; a piece whose sum does not is run again with the reference
-// raised by log2 of that sum (which bounds every probability by 1).
+// raised by log2 of that sum (which bounds every probability by 1).  The
+// causal split puts a visible key in every piece's first tile; only keys with
+// bias -inf (g = 0) can leave that tile without a live key for a column, which
+// then takes the reference 0: its later keys still count unless all their
+// logits lie below 2^-126 of it (log2 units: below -126).
 //
 // Long causal rows are split along the keys into pieces (at most C tiles
 // each, the diagonal in the last piece) so that the work spreads over every
@@ -486,7 +490,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st_dev(rec + (db * 16 + r) * 64, acc[db][r]);
-    st_dev(rec + (F::NR - 2) * 64, m2);  // the reference O and the sum are relative to
+    // the reference O and the sum are relative to; -inf for a column with no
+    // live key in this piece (every key it sees has bias -inf), which the merge
+    // then skips instead of letting its placeholder reference 0 set the scale
+    const float lcol = lsum + __shfl_xor(lsum, 32);
+    st_dev(rec + (F::NR - 2) * 64, lcol > 0.f ? m2 : -INFINITY);
     st_dev(rec + (F::NR - 1) * 64, lsum);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

@@ -19,7 +19,8 @@ def _wl(B, M, Hq, Hkv, D, dtype="bf16", tau=1.0, seed=21):
                        tau=tau, dtype=dtype, rope=True, M_fixed=M)
 
 
-def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, seed_offset=0, temp=False):
+def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, seed_offset=0, temp=False,
+             gamma_override=None):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
@@ -27,6 +28,8 @@ def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, 
     a = wl.attn_inputs(w, M, with_grad=grad, seed_offset=seed_offset)
     if g_override is not None:
         a["g"] = g_override
+    if gamma_override is not None:
+        a["gamma"] = gamma_override
     q, k, v = (dev_tensor(a[n], w.dtype, dev) for n in ("q", "k", "v"))
     g = torch.from_numpy(a["g"]).to(dev)
     gamma = torch.from_numpy(a["gamma"]).to(dev)
@@ -92,6 +95,27 @@ def test_fwd_zero_gate_rows():
     assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(to_np(r["lse"])[0, :, 0]))
     assert_maxabs(o, o_ref, 2e-2, "o")
     assert_maxabs(to_np(r["lse"]), l_ref, 2e-2, "lse")
+
+
+def test_fwd_split_row_with_a_dead_piece():
+    # M = 1024 with 8 kv heads splits the rows of 16, 24 and 32 tiles (query blocks 3, 5, 7)
+    # into 8-tile pieces; keys 0..255 (exactly their first piece) have g = 0 and every other key
+    # a bias of 2 log2 2^-120 = -240, so the live logits lie far below 0.  A piece with no live
+    # key must not set the merged reference (the softmax is shift invariant); the rows of keys
+    # < 256 only (blocks 0, 1) are empty.  Blocks 2, 4, 6 split at 6 or 7 tiles, so one of their
+    # pieces starts on a dead tile while later keys are live: below -126 the reference-0
+    # placeholder loses them (a documented limit of the fixed reference), not checked here.
+    w = _wl(1, 1024, 16, 8, 128)
+    g = np.full((1, 1024), 2.0 ** -120, np.float32)
+    g[0, :256] = 0.0
+    r = _run_fwd(w, 1024, g_override=g, gamma_override=np.full(16, 2.0, np.float32))
+    o_ref, l_ref = _oracle_fwd(w, r)
+    o, lse = to_np(r["o"]), to_np(r["lse"])
+    assert np.all(o[0, :256] == 0.0) and np.all(np.isneginf(lse[0, :, :256]))
+    rows = np.concatenate([np.arange(384, 512), np.arange(640, 768), np.arange(896, 1024)])
+    assert np.all(np.isfinite(lse[0][:, rows])) and np.all(lse[0][:, rows] < -100.0)
+    assert_maxabs(o[:, rows], o_ref[:, rows], 2e-2, "o")
+    assert_maxabs(lse[:, :, rows], l_ref[:, :, rows], 2e-2, "lse")
 
 
 @pytest.mark.parametrize("name,K", [("qwen3_8k", 1024), ("qwen3_32k", 2048)])
