@@ -260,6 +260,11 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q.k and
  * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
  * bf16 for the P.v product.  f32: D <= 128, plain fp32 arithmetic.
+ * bf16 limit: the softmax of a stretch of keys is taken against the largest
+ * logit of its first 32 keys; when g = 0 on all 32 of them, a row whose live
+ * logits all lie more than 126 / log2(e) (about 87) below zero loses them
+ * (o = 0).  g = 0 on whole leading stretches does not arise from the scorer's
+ * gates (only trailing padding of a kept list has g = 0).
  */
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g,
                             const float *gamma, const int32_t *pos, float rope_theta,
