@@ -534,6 +534,70 @@ def run_cpu_baseline(host, w, K, M):
                 seconds=t, total_s=total)
 
 
+def run_sweep(args):
+    """The same path (pack, score, select, compact, attention forward) at the other workload sizes:
+    8K context (K = 1024) and 128K context (K = 256, 1024, 4096, 16384); one JSON line each (not `value`)."""
+    import torch
+
+    import learned_token_pruning_gatescore_amd as tg
+    from learned_token_pruning_gatescore_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    tg.load()
+    for name in ("qwen3_8k", "sweep_128k"):
+        w = wl.WORKLOADS[name]
+        gi = wl.gate_inputs(w)
+        sel = torch.from_numpy(wl.clustered_scores(w)).to(dev)
+        T = lambda x: wl.to_torch(x, w.dtype, dev)
+        h, w1, w2 = T(gi["hidden"]), T(gi["w1"]), T(gi["w2"])
+        forced = torch.from_numpy(gi["forced"]).to(dev)
+        scores = torch.empty((w.B, w.N), device=dev)
+        gates = torch.empty_like(scores)
+        gws = tg.gate_workspace(w.d, w.d_ff, h.dtype, dev)
+        for K in w.Ks:
+            M = w.M(K)
+            at = wl.attn_inputs(w, M)
+            q, k, v = T(at["q"]), T(at["k"]), T(at["v"])
+            gamma = torch.from_numpy(at["gamma"]).to(dev)
+            kept = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+            hk = torch.empty((w.B, M, w.d), dtype=h.dtype, device=dev)
+            pk = torch.empty((w.B, M), dtype=torch.int32, device=dev)
+            gk = torch.empty((w.B, M), device=dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((w.B, w.Hq, M), device=dev)
+            ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
+            launches = [("gate_pack_w1", lambda: tg.tg_gate_pack_w1(w1, gws)),
+                        ("gate_score", lambda: tg.tg_gate_score_packed(h, gws, w.d_ff, w2, forced, scores, gates)),
+                        ("select_topk", lambda: tg.tg_select_topk(sel, forced, K, w.n_forced, kept)),
+                        ("compact", lambda: tg.tg_compact(h, None, gates, kept, hk, pk, gk)),
+                        ("attn_fwd", lambda: tg.tg_gated_attn_fwd(q, k, v, gk, gamma, pk, wl.ROPE_THETA, w.tau, o,
+                                                                  lse, ws))]
+            step = lambda: [f() for _, f in launches]
+            for _ in range(args.warmup):
+                step()
+            n = max(args.steps // 5, 4)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(n)]
+            for e in evs:
+                for j, (_, f) in enumerate(launches):
+                    e[j].record()
+                    f()
+                e[-1].record()
+            torch.cuda.synchronize()
+            per = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
+                   for j, (nm, _) in enumerate(launches)}
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                step()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / n
+            attn_flops = 4.0 * w.B * w.Hq * w.D * M * (M + 1) / 2
+            print(json.dumps(dict(sweep=name, N=w.N, K=K, M=M, step_us=wall * 1e6, tokens_per_s=w.B * w.N / wall,
+                                  kernels_us_with_events=per,
+                                  gate_score_TFLOPs=2.0 * w.B * w.N * w.d * w.d_ff / (per["gate_score"] * 1e-6) / 1e12,
+                                  attn_fwd_TFLOPs=attn_flops / (per["attn_fwd"] * 1e-6) / 1e12)), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,6 +605,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--train-steps", type=int, default=10, help="training-path fwd+bwd steps (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: the same path at 8K and 128K context, one JSON line per (workload, K)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -552,6 +618,9 @@ def main():
         print("bench.py is single-process, single-GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.sweep:
+        run_sweep(args)
+        return
     res = run_gpu(args)
     w, K, M = res["workload"], res["K"], res["M"]
     ms = res["elapsed"] / args.steps * 1e3
