@@ -116,12 +116,14 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
 // bf16 forward.  Work-group = 8 waves (two per SIMD) = 256 columns, a column
 // being a (query, head) pair of the GQA group: BQ = 256 / G queries x G
 // heads.  Wave w owns columns 32w .. 32w+31 (one head).  Keys come in 32-key
-// tiles, shared by the 8 waves through LDS (direct loads two tiles ahead, one
-// barrier per tile).  Per tile a wave runs S^T = K Q^T (keys on the MFMA
-// rows: each lane holds 16 keys of one column, so the row statistics are
-// lane-local plus one cross-half shuffle), the softmax of its 16 logits per
-// lane, and O^T += V^T P^T with V^T from the transposing LDS read; the other
-// wave of the SIMD fills the matrix cores while one is in its vector work.
+// tiles, shared by the 8 waves through LDS (direct loads AF_NS - 1 tiles
+// ahead, issued by one wave per SIMD; one barrier per tile).  Per tile a wave
+// runs S^T = K Q^T (keys on the MFMA rows: each lane holds 16 keys of one
+// column, so the row statistics are lane-local plus one cross-half shuffle),
+// the softmax of its 16 logits per lane, and O^T += V^T P^T with V^T from the
+// transposing LDS read.  Software pipeline: the S^T products of tile t+1 run
+// while the softmax of tile t is on the vector units; the other wave of the
+// SIMD fills remaining gaps.
 //
 // The probabilities use a fixed reference maximum per column (the maximum of
 // the piece's first tile), subtracted inside the S^T products by one more
@@ -334,9 +336,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // m2: reference maximum of the column (probabilities are 2^(x - m2)).  The
   // extra 16-deep step of every S^T product adds bias_j / c2 (key side) and
   // -m2 / (t c2) (query side), each as three bf16 parts against ones, so the
-  // logit is one multiply.  A key with bias -inf enters as -2^127 / c2 ...
-  // -2^127: its logit is at most -2^127 t c2 <= -1e7 below the reference, and
-  // its probability 0.
+  // logit is one multiply.  A key with bias -inf enters with bias / c2
+  // clamped to -2^127: its logit is then about -2^127 t c2 (below -1e7 for any
+  // t >= 1e-30) and its probability 0.
   float m2 = 0.f, lsum = 0.f;
   u32x4 qaug = aug_query(0.f, hl);
   f32x16 acc[NDB];
