@@ -30,9 +30,9 @@ def _score(w, N=None, sample=None):
     say("gate_score", w.name, B, n, w.d, w.d_ff)
     tg.tg_gate_score(h, w1, w2, f, scores, gates)
     torch.cuda.synchronize()
-    hf = wl.as_float(gi["hidden"], w.dtype).reshape(B * n, w.d)
     idx = np.arange(B * n) if sample is None else sample
-    s_ref, g_ref = oracle.gate_score(hf[idx], wl.as_float(gi["w1"], w.dtype), wl.as_float(gi["w2"], w.dtype),
+    hf = wl.as_float(gi["hidden"].reshape(B * n, w.d)[idx], w.dtype)  # only the rows the oracle scores
+    s_ref, g_ref = oracle.gate_score(hf, wl.as_float(gi["w1"], w.dtype), wl.as_float(gi["w2"], w.dtype),
                                      gi["forced"].reshape(-1)[idx])
     return to_np(scores).reshape(-1)[idx], to_np(gates).reshape(-1)[idx], s_ref, g_ref
 
@@ -109,6 +109,17 @@ def test_gate_score_qwen3_32k_sampled():
     rng = np.random.default_rng(0)
     sample = np.unique(np.concatenate([np.arange(256), np.arange(w.N - 300, w.N),
                                        rng.choice(w.N, 3000, replace=False)]))
+    s, g, sr, gr = _score(w, sample=sample)
+    assert_scores_close(s, sr, 1e-2)
+    assert_scores_close(g, gr, 1e-2, "gates")
+
+
+def test_gate_score_sweep_128k_sampled():
+    # the 128K-context workload: 1024 work-groups of 128 tokens, sampled rows against the oracle
+    w = wl.WORKLOADS["sweep_128k"]
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([np.arange(256), np.arange(w.N - 300, w.N),
+                                       rng.choice(w.N, 2000, replace=False)]))
     s, g, sr, gr = _score(w, sample=sample)
     assert_scores_close(s, sr, 1e-2)
     assert_scores_close(g, gr, 1e-2, "gates")
