@@ -611,8 +611,9 @@ def main():
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no multi-GPU path; "
-              f"see DESIGN.md for how the path would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library has no multi-GPU path "
+              f"(it would shard batch rows, or one row's tokens for scoring and its kv heads for attention, "
+              f"one process per GPU).", file=sys.stderr)
         sys.exit(2)
     if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
         print("bench.py is single-process, single-GPU", file=sys.stderr)
