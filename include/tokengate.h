@@ -313,7 +313,9 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
  *   with a~ = RMSNorm(hidden) (weight ln_w or NULL = 1, ln_eps) when ln != 0,
  *   else a~ = hidden.  hidden [B, N, d] (dt), w1 [d_ff, d], w2 [H, d_ff] (dt),
  *   1 <= H <= 16; scores [B, H, N] f32 out; workspace and errors as
- *   tg_gate_score (bf16: the packed W1).
+ *   tg_gate_score (bf16: the packed W1).  bf16: both products on the matrix
+ *   cores with fp32 accumulation; the second takes SiLU as two bf16 parts
+ *   (hi + lo, within 2^-17 of the fp32 value) and w2 as stored.
  * tg_score_normalize_heads: tg_score_normalize on each (b, h) row of
  *   scores [B, H, N], with b's forced mask [B, N] (or NULL); out may be scores.
  * tg_aggregate_heads: out[b][n] = (sum_h b[b][h][n]) / H (heads in order),
