@@ -102,6 +102,7 @@ def run_gpu(args):
     lse = torch.empty((w.B, w.Hq, M), device=dev)
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
     gws = tg.gate_workspace(w.d, w.d_ff, h0.dtype, dev)
+    sws = tg.select_workspace(w.B, w.N, dev)
     # tg_gate_score = tg_gate_pack_w1 + tg_gate_score_packed; the two halves are
     # called (and timed) separately here, the work is the same
     names = ["gate_pack_w1", "gate_score", "select_topk", "compact", "attn_fwd"]
@@ -110,7 +111,7 @@ def run_gpu(args):
     launches = [
         ("gate_pack_w1", lambda h, q, k, v: tg.tg_gate_pack_w1(w1, gws)),
         ("gate_score", lambda h, q, k, v: tg.tg_gate_score_packed(h, gws, w.d_ff, w2, forced, scores, gates)),
-        ("select_topk", lambda h, q, k, v: tg.tg_select_topk(sel_t, forced, K, w.n_forced, kept)),
+        ("select_topk", lambda h, q, k, v: tg.tg_select_topk(sel_t, forced, K, w.n_forced, kept, ws=sws)),
         ("compact", lambda h, q, k, v: tg.tg_compact(h, None, gates, kept, hk, pk, gk)),
         ("attn_fwd", lambda h, q, k, v: tg.tg_gated_attn_fwd(q, k, v, gk, gamma, pk, wl.ROPE_THETA, w.tau, o, lse,
                                                                ws)),
@@ -272,6 +273,7 @@ def run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M):
     lse = torch.empty((w.B, w.Hq, M), device=dev)
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
     gws = tg.gate_workspace(w.d, w.d_ff, hs[0].dtype, dev)
+    sws = tg.select_workspace(w.B, w.N, dev)
     names = ["gate_score_ln", "score_normalize", "select_topk", "compact", "gate_softmax", "attn_fwd_temperature"]
 
     def step(i, ev=None):
@@ -281,7 +283,7 @@ def run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M):
         rec(1)
         tg.tg_score_normalize(sel_t, forced, 1e-6, bsel)
         rec(2)
-        tg.tg_select_topk(bsel, forced, K, w.n_forced, kept)
+        tg.tg_select_topk(bsel, forced, K, w.n_forced, kept, ws=sws)
         rec(3)
         tg.tg_compact(hs[i % NCOPY], None, bsel, kept, hk, pk, bk)
         rec(4)
@@ -333,6 +335,7 @@ def run_operative_heads(args, tg, wl, w, dev, stream, gi, at, K, M):
     lse = torch.empty((w.B, w.Hq, M), device=dev)
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
     gws = tg.gate_workspace(w.d, w.d_ff, hs[0].dtype, dev)
+    sws = tg.select_workspace(w.B, w.N, dev)
     names = ["gate_score_heads", "score_normalize_heads", "aggregate_heads", "select_topk", "compact",
              "gather_heads", "gate_softmax_heads", "attn_fwd_headgates"]
 
@@ -345,7 +348,7 @@ def run_operative_heads(args, tg, wl, w, dev, stream, gi, at, K, M):
         rec(2)
         tg.tg_aggregate_heads(b, agg)
         rec(3)
-        tg.tg_select_topk(agg, forced, K, w.n_forced, kept)
+        tg.tg_select_topk(agg, forced, K, w.n_forced, kept, ws=sws)
         rec(4)
         tg.tg_compact(hs[i % NCOPY], None, None, kept, hk, pk, None)
         rec(5)
@@ -503,6 +506,20 @@ def load_traffic(kernel):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), with the logical CPUs this process may use."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({len(os.sched_getaffinity(0))} logical CPUs available)"
+
+
 def run_cpu_baseline(host, w, K, M):
     """The oracle as it stands, on this host's cores, over the same workload (all tokens, all rows)."""
     import oracle
@@ -528,7 +545,7 @@ def run_cpu_baseline(host, w, K, M):
                     round_bf16=True)
     t["attn_fwd"] = time.perf_counter() - t0
     total = sum(t.values())
-    return dict(value=w.B * w.N / total, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    return dict(value=w.B * w.N / total, unit="tokens/s", cores=oracle.num_threads(), cpu=cpu_model(), kind="oracle",
                 sample=f"full workload once: {w.B * w.N} tokens scored, selected and compacted, attention over all "
                        f"{M} kept rows x {w.Hq} heads; fp64 plain loops",
                 seconds=t, total_s=total)
@@ -554,6 +571,7 @@ def run_sweep(args):
         scores = torch.empty((w.B, w.N), device=dev)
         gates = torch.empty_like(scores)
         gws = tg.gate_workspace(w.d, w.d_ff, h.dtype, dev)
+        sws = tg.select_workspace(w.B, w.N, dev)
         for K in w.Ks:
             M = w.M(K)
             at = wl.attn_inputs(w, M)
@@ -568,7 +586,7 @@ def run_sweep(args):
             ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, False, dev)
             launches = [("gate_pack_w1", lambda: tg.tg_gate_pack_w1(w1, gws)),
                         ("gate_score", lambda: tg.tg_gate_score_packed(h, gws, w.d_ff, w2, forced, scores, gates)),
-                        ("select_topk", lambda: tg.tg_select_topk(sel, forced, K, w.n_forced, kept)),
+                        ("select_topk", lambda: tg.tg_select_topk(sel, forced, K, w.n_forced, kept, ws=sws)),
                         ("compact", lambda: tg.tg_compact(h, None, gates, kept, hk, pk, gk)),
                         ("attn_fwd", lambda: tg.tg_gated_attn_fwd(q, k, v, gk, gamma, pk, wl.ROPE_THETA, w.tau, o,
                                                                   lse, ws))]
@@ -649,7 +667,8 @@ def main():
                                "d=2048, scorer 2048->512->1, 16/8 heads, D=128, RoPE theta 1e6, tau=1",
                    "global_batch": w.B, "seq_len": w.N, "kept": M, "parallelism": "single GPU"},
         "roofline": roof,
-        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "cpu", "kind",
+                                                                       "sample")},
         "device_path_us_instrumented": res["step_dev"] * 1e6,
         "kernels": res["kernels"],
         "summary": res["summary"],

@@ -176,7 +176,9 @@ tg_status tg_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_
 /* Kept tokens per row: n_forced + min(K, N - n_forced); -1 for invalid input. */
 int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K);
 
-/* Workspace bytes tg_select_topk needs (0 today; kept for the ABI). */
+/* Workspace bytes tg_select_topk needs: per row, per-work-group histograms
+ * (4352 words per 4096 tokens) and 8 bytes per token for the threshold bin's
+ * candidates; 0 for invalid sizes or N > 2^22. */
 size_t tg_select_topk_workspace_size(int64_t B, int64_t N);
 
 /*
@@ -196,6 +198,16 @@ size_t tg_select_topk_workspace_size(int64_t B, int64_t N);
  * A row whose forced count differs from n_forced keeps its true count
  * M_true = F + min(K, N - F): it writes min(M_true, M) indices, pads the rest
  * with -1 and reports M_true in kept_count.
+ *   ws, ws_bytes                     device scratch of at least
+ *                                    tg_select_topk_workspace_size(B, N) bytes,
+ *                                    256-byte aligned, owned by the caller; its
+ *                                    contents need no initial value and carry
+ *                                    nothing between calls
+ * Exact radix select over a monotone 32-bit key of the score in three
+ * launches of 4096-token work-groups (histogram of the top 12 key bits,
+ * threshold bin and exact threshold, output); deterministic.  N <= 2^22,
+ * B <= 65535 (TG_ERR_UNSUPPORTED otherwise); TG_ERR_WORKSPACE when the
+ * workspace is missing or too small.
  */
 tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_t B,
                          int64_t N, int64_t K, int64_t n_forced, int32_t *kept_idx,
@@ -260,11 +272,11 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q.k and
  * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
  * bf16 for the P.v product.  f32: D <= 128, plain fp32 arithmetic.
- * bf16 limit: the softmax of a stretch of keys is taken against the largest
- * logit of its first 32 keys; when g = 0 on all 32 of them, a row whose live
- * logits all lie more than 126 / log2(e) (about 87) below zero loses them
- * (o = 0).  g = 0 on whole leading stretches does not arise from the scorer's
- * gates (only trailing padding of a kept list has g = 0).
+ * The bf16 softmax of a stretch of keys is taken against a fixed reference:
+ * the largest live logit of its first 32 keys, or, when g = 0 on every key of
+ * those 32 that a row sees, the logit of the stretch's first key with g > 0;
+ * a stretch whose sum would overflow is recomputed with the reference raised.
+ * Live logits count at any scale.
  */
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g,
                             const float *gamma, const int32_t *pos, float rope_theta,

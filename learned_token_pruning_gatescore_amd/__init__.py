@@ -38,6 +38,7 @@ __all__ = [
     "tg_gate_score_workspace_size", "tg_gate_pack_w1", "tg_gate_score_packed", "gate_workspace",
     "tg_select_topk", "tg_compact", "tg_gated_attn_fwd", "tg_gated_attn_bwd",
     "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
+    "select_workspace",
     "tg_gate_score_ln", "tg_score_normalize", "tg_gate_softmax", "tg_gate_softmax_bwd",
     "tg_gated_attn_varlen_workspace_size", "tg_gated_attn_fwd_varlen", "tg_gated_attn_bwd_varlen",
     "attn_varlen_workspace", "tg_gate_score_heads", "tg_score_normalize_heads", "tg_aggregate_heads",
@@ -261,11 +262,21 @@ def tg_gate_softmax_bwd(g, dg, db, stream=None):
     _check(load().tg_gate_softmax_bwd(_ptr(g), _ptr(dg), B, M, _ptr(db), _stream(stream)))
 
 
+def select_workspace(B, N, device):
+    """A workspace tensor of the size tg_select_topk needs (256-byte aligned by the allocator)."""
+    import torch
+
+    return torch.empty(max(tg_select_topk_workspace_size(B, N), 1), dtype=torch.uint8, device=device)
+
+
 def tg_select_topk(scores, forced_keep, K, n_forced, kept_idx, kept_count=None, ws=None, stream=None):
-    """scores f32 [B, N]; forced_keep u8 [B, N] or None; writes kept_idx i32 [B, M] (M = tg_kept_count)."""
-    _contig(scores, forced_keep, kept_idx, kept_count)
+    """scores f32 [B, N]; forced_keep u8 [B, N] or None; writes kept_idx i32 [B, M] (M = tg_kept_count).
+    ws: the workspace (select_workspace); allocated here when None."""
+    _contig(scores, forced_keep, kept_idx, kept_count, ws)
     B, N = scores.shape
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = select_workspace(B, N, scores.device)
+    ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_select_topk(_ptr(scores), _ptr(forced_keep), B, N, int(K), int(n_forced), _ptr(kept_idx),
                                  _ptr(kept_count), _ptr(ws), ws_bytes, _stream(stream)))
 
@@ -437,7 +448,9 @@ def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma,
     q/k/v are the kept tokens' projections [B, M, H, D].  select_scores, when given,
     replaces the computed scores as the ranking key (the computed scores and gates
     are still produced).  bufs: optional dict of preallocated outputs (reused across
-    calls).  Returns the dict of outputs.
+    calls).  Returns the dict of outputs; "kept_count" [B] holds each row's true kept
+    count, which differs from M when a row's forced count differs from n_forced (its
+    kept_idx row is then truncated to M, or padded with -1).
     """
     import torch
 
@@ -458,6 +471,7 @@ def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma,
     scores = buf("scores", (B, N), torch.float32)
     gates = buf("gates", (B, N), torch.float32)
     kept = buf("kept_idx", (B, M), torch.int32)
+    kept_count = buf("kept_count", (B,), torch.int32)
     h_out = buf("hidden_kept", (B, M, d), hidden.dtype)
     p_out = buf("pos_kept", (B, M), torch.int32)
     g_out = buf("g_kept", (B, M), torch.float32)
@@ -475,7 +489,12 @@ def gate_layer_forward(hidden, w1, w2, forced_keep, n_forced, K, q, k, v, gamma,
         bufs["gate_ws"] = gws
     tg_gate_score(hidden, w1, w2, forced_keep, scores, gates, ws=gws, stream=stream)
     key = scores if select_scores is None else select_scores
-    tg_select_topk(key, forced_keep, K, n_forced, kept, stream=stream)
+    sws = bufs.get("select_ws")
+    sneed = tg_select_topk_workspace_size(B, N)
+    if sws is None or sws.numel() < sneed:
+        sws = select_workspace(B, N, dev)
+        bufs["select_ws"] = sws
+    tg_select_topk(key, forced_keep, K, n_forced, kept, kept_count, ws=sws, stream=stream)
     tg_compact(hidden, pos, gates, kept, h_out, p_out, g_out, stream=stream)
     tg_gated_attn_fwd(q, k, v, g_out, gamma, p_out, rope_theta, tau, o, lse, ws, stream=stream)
     return bufs

@@ -27,7 +27,8 @@ hipError_t launch_gather_heads(const float *s, const int32_t *kept, int64_t B, i
                                hipStream_t st);
 hipError_t launch_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_t M, float *db, hipStream_t st);
 hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_t B, int64_t N, int64_t K,
-                              int64_t M_alloc, int32_t *kept, int32_t *kept_count, hipStream_t s);
+                              int64_t M_alloc, int32_t *kept, int32_t *kept_count, void *ws, hipStream_t s);
+size_t select_ws_bytes(int64_t B, int64_t N);
 hipError_t launch_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept,
                           int64_t B, int64_t N, int64_t M, int64_t row_bytes, void *hidden_out, int32_t *pos_out,
                           float *gates_out, hipStream_t s);
@@ -58,6 +59,7 @@ tg_status hip_status(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxInt = 0x7FFFFFFF;
+constexpr int64_t kSelMaxN = (int64_t)1 << 22;  // selection: 1024 work-groups of 4096 tokens per row
 constexpr size_t kAlign = 256;
 
 #define REQUIRE(cond, st, ...) \
@@ -78,6 +80,11 @@ tg_status check_attn(const void *q, const void *k, const void *v, const float *g
     REQUIRE(D == 64 || D == 128, TG_ERR_UNSUPPORTED, "bf16 attention needs D in {64, 128} (got %lld)", (long long)D);
     const int64_t G = Hq / Hkv;
     REQUIRE(G <= 8 && (G & (G - 1)) == 0, TG_ERR_UNSUPPORTED, "bf16 attention needs Hq/Hkv in {1, 2, 4, 8}");
+    // the bf16 kernels address one row's q, k, v (and the per-head bias and
+    // row statistics, which are smaller) through buffer resources with 32-bit
+    // byte ranges, and park dead loads at offset 2^31: every range stays below it
+    REQUIRE(M * (Hq > Hkv ? Hq : Hkv) * D * 2 < ((int64_t)1 << 31), TG_ERR_UNSUPPORTED,
+            "bf16 attention needs M * max(Hq, Hkv) * D * 2 < 2^31 bytes (M=%lld)", (long long)M);
   } else {
     REQUIRE(D >= 2 && D <= 128 && D % 2 == 0, TG_ERR_UNSUPPORTED, "f32 attention needs even D <= 128");
   }
@@ -355,27 +362,28 @@ tg_status tg_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_
 }
 
 size_t tg_select_topk_workspace_size(int64_t B, int64_t N) {
-  (void)B;
-  (void)N;
-  return 0;
+  if (B < 0 || N < 0 || N > kSelMaxN) return 0;
+  return tg::select_ws_bytes(B, N);
 }
 
 tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t N, int64_t K,
                          int64_t n_forced, int32_t *kept_idx, int32_t *kept_count, void *ws, size_t ws_bytes,
                          void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   REQUIRE(B >= 0 && N >= 0, TG_ERR_INVALID_ARG, "B and N must be >= 0");
   REQUIRE(K >= 0, TG_ERR_INVALID_ARG, "K must be >= 0 (got %lld)", (long long)K);
   REQUIRE(n_forced >= 0 && n_forced <= N, TG_ERR_INVALID_ARG, "need 0 <= n_forced <= N (n_forced=%lld N=%lld)",
           (long long)n_forced, (long long)N);
   REQUIRE(forced_keep || n_forced == 0, TG_ERR_INVALID_ARG, "forced_keep is NULL but n_forced > 0");
-  REQUIRE(N <= kMaxInt && B <= 65535 * 1024, TG_ERR_UNSUPPORTED, "N must fit in int32");
+  REQUIRE(N <= kSelMaxN && B <= 65535, TG_ERR_UNSUPPORTED, "selection needs N <= 2^22 and B <= 65535");
   const int64_t M = tg_kept_count(N, n_forced, K);
   if (B * N > 0) REQUIRE(scores && kept_idx, TG_ERR_INVALID_ARG, "scores and kept_idx are required");
   REQUIRE(aligned16(scores) && aligned16(kept_idx), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (B == 0) return ok();
-  return hip_status(tg::launch_select_topk(scores, forced_keep, B, N, K, M, kept_idx, kept_count,
+  const size_t need = tg::select_ws_bytes(B, N);
+  REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "selection needs a %zu-byte workspace (got %zu)", need,
+          ws ? ws_bytes : (size_t)0);
+  REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return hip_status(tg::launch_select_topk(scores, forced_keep, B, N, K, M, kept_idx, kept_count, ws,
                                            (hipStream_t)stream),
                     "tg_select_topk launch");
 }

@@ -132,9 +132,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
 // rounding; a piece whose sum does not is run again with the reference
 // raised by log2 of that sum (which bounds every probability by 1).  The
 // causal split puts a visible key in every piece's first tile; only keys with
-// bias -inf (g = 0) can leave that tile without a live key for a column, which
-// then takes the reference 0: its later keys still count unless all their
-// logits lie below 2^-126 of it (log2 units: below -126).
+// bias -inf (g = 0) can leave that tile without a live key for a column.  Such
+// a column takes instead the logit of the first key of the piece whose bias
+// is finite (if it sees one): any live logit is a valid reference, since
+// every probability of the column is then 2^(x - m2) with m2 <= max x, and
+// the guard above bounds the sum.
 //
 // Long causal rows are split along the keys into pieces (at most C tiles
 // each, the diagonal in the last piece) so that the work spreads over every
@@ -347,6 +349,28 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   auto key_aug = [&](float bv) __attribute__((always_inline)) {
     return aug_key(fmaxf(bv * inv_c2k, -0x1p127f), hl);
   };
+  // Logit x = t (c2 q^.k^_j0 + bias_j0) of the first key j0 of tiles 1 .. nt-1
+  // of the piece whose bias (this wave's head) is finite, for each column that
+  // sees it; -inf for the others, or when there is no such key.  Wave-uniform
+  // search over the bias row in global memory, then q^.k^_j0 for the wave's 32
+  // columns as one S^T product whose 32 key rows all hold k^_j0.
+  auto first_live_logit = [&]() __attribute__((always_inline)) -> float {
+    const float *brow = bias + ((int64_t)b * Hq + kvh * G + hloc) * M;
+    const int jend = (kt0 + nt) * AF_TK < M ? (kt0 + nt) * AF_TK : M;
+    int j0 = jend;
+    for (int j = (kt0 + 1) * AF_TK; j < jend; j += 64) {
+      const uint64_t live = __ballot(j + lane < jend && brow[j + lane] != -INFINITY);
+      if (live) {
+        j0 = j + __ffsll((unsigned long long)live) - 1;
+        break;
+      }
+    }
+    if (j0 >= jend) return -INFINITY;
+    const uint16_t *krow = khat + ((bM + j0) * Hkv + kvh) * D + 8 * hl;
+    f32x16 s0 = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks) s0 = mfma32(*(const u32x4 *)(krow + 16 * ks), qf[ks], s0);
+    return qi >= j0 ? tc2 * (s0[0] + brow[j0] * inv_c2k) : -INFINITY;
+  };
   // softmax of 2 of the 16 logits per lane (registers 2c, 2c+1) of a tile
   auto soft2 = [&](const f32x16 &s, int c, float msub, bool masked, int lim, float &ps, u32x4(&pf)[2])
       __attribute__((always_inline)) {
@@ -449,6 +473,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
           if (live) mx = fmaxf(mx, sc[r] * tc2);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // a column that sees no live key in tile 0 (g = 0 on all of them) but
+        // one later in the piece: the logit of the piece's first live key
+        if (nt > 1 && __ballot(vq && mx == -INFINITY)) mx = fmaxf(mx, first_live_logit());
         m2 = mx == -INFINITY ? 0.f : mx;
         msub = m2;  // tile 0's products ran without it
         qaug = aug_query(-m2 * inv_c2, hl);

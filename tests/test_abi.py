@@ -86,6 +86,14 @@ def test_select_validation():
     assert lib.tg_select_topk(FAKE, FAKE, 1, 100, 5, 101, FAKE, None, None, 0, None) == 1  # n_forced > N
     assert lib.tg_select_topk(FAKE, None, 1, 100, 5, 3, FAKE, None, None, 0, None) == 1    # mask missing
     assert lib.tg_select_topk(None, None, 1, 100, 5, 0, FAKE, None, None, 0, None) == 1    # scores missing
+    # a workspace of tg_select_topk_workspace_size bytes (256-byte aligned) is required
+    need = lib.tg_select_topk_workspace_size(2, 40000)
+    assert need >= 2 * 40000 * 8 and lib.tg_select_topk_workspace_size(1, 1) > 0
+    assert lib.tg_select_topk_workspace_size(1, (1 << 22) + 1) == 0
+    assert lib.tg_select_topk(FAKE, None, 2, 40000, 5, 0, FAKE, None, None, 0, None) == 3
+    assert lib.tg_select_topk(FAKE, None, 2, 40000, 5, 0, FAKE, None, FAKE, need - 1, None) == 3
+    assert lib.tg_select_topk(FAKE, None, 2, 40000, 5, 0, FAKE, None, ctypes.c_void_p(0x10010), need, None) == 1
+    assert lib.tg_select_topk(FAKE, None, 1, (1 << 22) + 1, 5, 0, FAKE, None, FAKE, 1 << 40, None) == 2
     assert lib.tg_select_topk(FAKE, None, 0, 100, 5, 0, FAKE, None, None, 0, None) == 0    # B = 0: nothing to do
 
 
@@ -115,6 +123,15 @@ def test_attn_validation():
     assert f(*args(pos=FAKE, ws=FAKE, wsb=need - 1)) == 3
     assert f(*args(q=MIS)) == 1
     assert f(*args(sigma=MIS)) == 1             # misaligned sigma
+    # the bf16 kernels' 32-bit buffer ranges: M * max(Hq, Hkv) * D * 2 must stay below 2^31
+    big = lambda M: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, M, 16, 8, 128, 1, FAKE, None, FAKE,
+                     1 << 40, None]
+    assert f(*big(1 << 20)) == 2
+    assert f(*big((1 << 19) + 1)) == 2
+    assert b"2^31" in lib.tg_last_error()
+    bbig = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, FAKE, FAKE, 1, 1 << 20, 16, 8, 128, 1, FAKE, FAKE,
+            FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None]
+    assert lib.tg_gated_attn_bwd(*bbig) == 2
     b = lib.tg_gated_attn_bwd
     bargs = lambda **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, kw.get("sigma", None), kw.get("lse", FAKE),
                           FAKE, 1, 100, 16, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("dsigma", None),
@@ -189,6 +206,8 @@ def test_varlen_validation():
     assert f(*args(good, Hq=12)) == 1          # Hq % Hkv
     assert f(*args(good, D=96)) == 2           # bf16 D
     assert f(*args(good)) == 3                 # workspace too small
+    huge = cu_t(0, 1 << 19, 1 << 20, (1 << 20) + 5, (1 << 20) + 5)
+    assert f(*args(huge, wsb=1 << 40)) == 2    # the packed tokens exceed the kernels' 32-bit ranges
     b = lib.tg_gated_attn_bwd_varlen
     b.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 4 + [
         i64, i64, i64, i64, ctypes.c_int] + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]

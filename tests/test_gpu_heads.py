@@ -130,7 +130,7 @@ def test_normalize_aggregate_gather_softmax_heads():
                             f"g head {h}")
 
 
-def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=81, zero_heads=False):
+def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=81, zero_heads=False, far=False):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
@@ -142,6 +142,14 @@ def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=8
     if zero_heads:
         gh[0, 1, : M // 3] = 0.0  # one head sees no early keys
         gh[0, 0, 0] = 0.0
+    if far:
+        # gates in [0.5, 0.52] with a gain of 150: biases between -150 and -141.5 (log2 units), so
+        # every live logit lies far below zero; head h has g = 0 on its first 32 (h % 3 + 1) keys, so
+        # each head's first live key sits in a different tile
+        gh = rng.uniform(0.5, 0.52, (B, Hq, M)).astype(np.float32)
+        for h in range(Hq):
+            gh[:, h, : 32 * (h % 3 + 1)] = 0.0
+        a["gamma"] = np.full(Hq, 150.0, np.float32)
     dev = device()
     q, k, v, dout = (dev_tensor(a[n], dtype, dev) for n in ("q", "k", "v", "dout"))
     g = torch.from_numpy(gh).to(dev)
@@ -170,7 +178,11 @@ def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=8
     ref = oracle.attn_bwd(f(a["q"]), f(a["k"]), f(a["v"]), gh, a["gamma"], f(a["dout"]), **kw)
     got = (dq, dk, dv, dg, dgam) + ((dsig,) if temp else ())
     for name, gt, rf in zip(("dq", "dk", "dv", "dg", "dgamma", "dsigma"), got, ref):
-        assert_maxabs(to_np(gt), rf, tol, name)
+        gt = to_np(gt)
+        if far and name == "dg":  # dg_hj = gain_h colsum_h(j) / g_hj: compare the column sums
+            sc = gh / a["gamma"][None, :, None]
+            gt, rf = gt * sc, rf * sc
+        assert_maxabs(gt, rf, tol, name)
 
 
 @pytest.mark.parametrize("B,M,Hq,Hkv,D,rope,temp", [(2, 100, 4, 2, 128, True, False), (1, 257, 8, 2, 128, True, True),
@@ -181,6 +193,11 @@ def test_headgates_bf16(B, M, Hq, Hkv, D, rope, temp):
 
 def test_headgates_zero_gates():
     _headgate_case(1, 150, 4, 2, 128, zero_heads=True)
+
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,temp", [(1, 200, 4, 2, False), (2, 700, 16, 8, True)])
+def test_headgates_dead_leading_tiles_far_logits(B, M, Hq, Hkv, temp):
+    _headgate_case(B, M, Hq, Hkv, 128, rope=False, temp=temp, far=True)
 
 
 def test_headgates_f32():
