@@ -176,9 +176,10 @@ tg_status tg_gate_softmax_bwd(const float *g, const float *dg, int64_t B, int64_
 /* Kept tokens per row: n_forced + min(K, N - n_forced); -1 for invalid input. */
 int64_t tg_kept_count(int64_t N, int64_t n_forced, int64_t K);
 
-/* Workspace bytes tg_select_topk needs: per row, per-work-group histograms
- * (4352 words per 4096 tokens) and 8 bytes per token for the threshold bin's
- * candidates; 0 for invalid sizes or N > 2^22. */
+/* Workspace bytes tg_select_topk needs: 256 when N <= 32768 (one work-group
+ * per row, nothing kept in it); otherwise, per row, per-work-group histograms
+ * (4356 words per 4096 tokens) and 8 bytes per token for the threshold bin's
+ * candidates.  0 for invalid sizes or N > 2^22. */
 size_t tg_select_topk_workspace_size(int64_t B, int64_t N);
 
 /*
@@ -203,11 +204,12 @@ size_t tg_select_topk_workspace_size(int64_t B, int64_t N);
  *                                    256-byte aligned, owned by the caller; its
  *                                    contents need no initial value and carry
  *                                    nothing between calls
- * Exact radix select over a monotone 32-bit key of the score in three
- * launches of 4096-token work-groups (histogram of the top 12 key bits,
- * threshold bin and exact threshold, output); deterministic.  N <= 2^22,
- * B <= 65535 (TG_ERR_UNSUPPORTED otherwise); TG_ERR_WORKSPACE when the
- * workspace is missing or too small.
+ * Exact radix select over a monotone 32-bit key of the score (digits of 12,
+ * 10 and 10 bits), deterministic: rows of up to 32768 tokens in one
+ * work-group each with the keys in registers; longer rows in three launches
+ * of 4096-token work-groups (histograms of the top 12 key bits, threshold bin
+ * and exact threshold, output).  N <= 2^22, B <= 65535 (TG_ERR_UNSUPPORTED
+ * otherwise); TG_ERR_WORKSPACE when the workspace is missing or too small.
  */
 tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_t B,
                          int64_t N, int64_t K, int64_t n_forced, int32_t *kept_idx,

@@ -29,28 +29,52 @@
 //     S^T products through their extra 16-deep step;
 //   * softmax in fp32 against a fixed per-column reference, P rounded to
 //     bf16 for the MFMA, row sums in fp32.
+#include <type_traits>
+
 #include "tg_common.h"
 #include "tg_attn.h"
 #include "tg_tile.h"
 
 namespace tg {
 
-// Prep pass over the B*M kept rows (one thread per (row, rotary pair); the key
-// rotation by the work-group's threads in 16-byte pieces):
+// Prep pass over the B*M kept rows (R = 256 / (D/2) rows per work-group, one
+// thread per (row, rotary pair); the rotations by the work-group's threads in
+// 16-byte pieces):
 //   cs[row][i]    = (cos, sin)(pos[row] * inv_freq[i]) with the angle and the
 //                   trigonometry in fp64 (inv_freq[i] = theta^(-2i/D), computed
 //                   on the host in fp64), stored as fp32;
 //   khat[row]     = k[row] rotated (bf16, every kv head), when khat != nullptr;
+//   qfr           = q (rotated when positions are given), bf16, in the order
+//                   of the forward's MFMA B fragments, when qfr != nullptr:
+//                   block (b, head, 32-row block, 16-element step) is 64
+//                   lanes x 16 bytes, lane l32 + 32 hl holding elements
+//                   16 step + 8 hl .. +8 of row 32 block + l32, so the forward
+//                   loads each of its fragments as one contiguous 1 KB block
+//                   (consecutive threads here write consecutive rows' slots);
 //   bias[b][h][j] = gamma_h * log2 g_j (-inf where g_j <= 0), the per-key,
 //                   per-head logit bias in log2 units, when bias != nullptr
 //                   (g_hj with per-head gates);
 //   ratio[row]    = ln m_i / ln max(2, p_i), the row factor of the attention
 //                   temperature (m_i = i + 1, p_i = pos + 1, or i + 1 without
 //                   positions), when ratio != nullptr.
-// Rotating K once here replaces a rotation per query block in the main loop.
+// Rotating K and Q once here replaces a rotation per query block in the main
+// loop.
 struct InvFreq {
   double v[64];
 };
+
+// rotate-half of one 16-byte piece x (elements i..i+7) with its partner y
+// (elements i + D/2 ..), angles of pairs i..i+7 in cp
+__device__ __forceinline__ void rot8(u32x4 &x, u32x4 &y, const float2 *cp) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2 a0 = cp[2 * w], a1 = cp[2 * w + 1];
+    const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+    const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
+    x[w] = pack_bf16x2(x0 * a0.x - y0 * a0.y, x1 * a1.x - y1 * a1.y);
+    y[w] = pack_bf16x2(y0 * a0.x + x0 * a0.y, y1 * a1.x + x1 * a1.y);
+  }
+}
 
 __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restrict__ k, const float *__restrict__ g,
                                                         const float *__restrict__ gamma,
@@ -58,7 +82,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
                                                         int M, int Hq, int Hkv, int D, float2 *__restrict__ cs,
                                                         uint16_t *__restrict__ khat, float *__restrict__ bias,
                                                         float *__restrict__ ratio, int *__restrict__ cnt, int ncnt,
-                                                        int gph) {
+                                                        int gph, const uint16_t *__restrict__ q,
+                                                        uint16_t *__restrict__ qfr, int nq32) {
   __shared__ float2 scs[256];
   const int half = D / 2, R = 256 / half;  // R rows per work-group, one thread per (row, rotary pair)
   const int t = threadIdx.x;
@@ -74,38 +99,49 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
     cs[r * half + i] = v;
     scs[t] = v;
   }
+  if (pos && (khat || qfr)) __syncthreads();
   if (pos && khat) {
-    // the work-group's R rows x Hkv heads x (half / 8) chunks: 16-byte loads and stores
-    __syncthreads();
+    // the work-group's R rows x Hkv heads x (half / 8) piece pairs: 16-byte loads and stores
     const int nch = half / 8, per_row = Hkv * nch;
     for (int it = t; it < R * per_row; it += 256) {
       const int lr2 = it / per_row, rem = it - lr2 * per_row, h = rem / nch, ch = rem - h * nch;
       if (r0 + lr2 >= rows) break;
       const int64_t o = ((r0 + lr2) * Hkv + h) * D + 8 * ch;
-      const u32x4 x = *(const u32x4 *)(k + o), y = *(const u32x4 *)(k + o + half);
-      const float2 *cp = scs + lr2 * half + 8 * ch;
-      u32x4 xo, yo;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float2 a0 = cp[2 * w], a1 = cp[2 * w + 1];
-        const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
-        const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
-        xo[w] = pack_bf16x2(x0 * a0.x - y0 * a0.y, x1 * a1.x - y1 * a1.y);
-        yo[w] = pack_bf16x2(y0 * a0.x + x0 * a0.y, y1 * a1.x + x1 * a1.y);
-      }
-      *(u32x4 *)(khat + o) = xo;
-      *(u32x4 *)(khat + o + half) = yo;
+      u32x4 x = *(const u32x4 *)(k + o), y = *(const u32x4 *)(k + o + half);
+      rot8(x, y, scs + lr2 * half + 8 * ch);
+      *(u32x4 *)(khat + o) = x;
+      *(u32x4 *)(khat + o + half) = y;
+    }
+  }
+  if (qfr) {
+    // items (head, step pair kp, half hl, row lr2), the row fastest: row j's piece of elements
+    // e = 16 kp + 8 hl goes to slot (j % 32) + 32 hl of block (b, head, j / 32, kp), its rotary
+    // partner e + D/2 to the same slot of step kp + D/32
+    const int nks = D / 16, npair = nks / 2;
+    for (int it = t; it < R * 2 * Hq * npair; it += 256) {
+      const int lr2 = it % R, rest = it / R, hl = rest & 1, rest2 = rest >> 1, kp = rest2 % npair,
+                h = rest2 / npair;
+      const int64_t row = r0 + lr2;
+      if (row >= rows) continue;
+      const int e = 16 * kp + 8 * hl;
+      const int64_t o = (row * Hq + h) * D + e;
+      u32x4 x = *(const u32x4 *)(q + o), y = *(const u32x4 *)(q + o + half);
+      if (pos) rot8(x, y, scs + lr2 * half + e);
+      const int bb = (int)(row / M), j = (int)(row - (int64_t)bb * M);
+      uint16_t *blk = qfr + ((((int64_t)bb * Hq + h) * nq32 + j / 32) * nks) * 512 + ((j & 31) + 32 * hl) * 8;
+      *(u32x4 *)(blk + kp * 512) = x;
+      *(u32x4 *)(blk + (kp + npair) * 512) = y;
     }
   }
   if (bias && vr) {  // gph: one gate per (head, key), g [B, Hq, M]; else one per key, g [B, M]
-    const int b = (int)r / M, j = (int)r - b * M;  // B * M < 2^31
+    const int64_t bb = r / M, j = r - bb * M;
     for (int h = i; h < Hq; h += half) {
-      const float gv = g[gph ? ((int64_t)b * Hq + h) * M + j : r];
-      bias[(b * Hq + h) * M + j] = gv > 0.f ? gamma[h] * log2f(gv) : -INFINITY;
+      const float gv = g[gph ? (bb * Hq + h) * M + j : r];
+      bias[(bb * Hq + h) * M + j] = gv > 0.f ? gamma[h] * log2f(gv) : -INFINITY;
     }
   }
   if (ratio && vr && i == 0) {  // the temperature's row factor ln m_i / ln max(2, p_i) (fp64 logs)
-    const int b = (int)r / M, j = (int)r - b * M;
+    const int64_t bb = r / M, j = r - bb * M;
     const double m = (double)j + 1.0, pp = pos ? (double)pos[r] + 1.0 : m;
     ratio[r] = (float)(log(m) / log(pp > 2.0 ? pp : 2.0));
   }
@@ -185,13 +221,13 @@ __device__ __forceinline__ u32x4 aug_query(float x, int hl) {
 
 template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
-    const float *__restrict__ bias, const float2 *__restrict__ cs, float c2, const float *__restrict__ sigma,
+    const uint16_t *__restrict__ qfr, int nq32, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
+    const float *__restrict__ bias, float c2, const float *__restrict__ sigma,
     const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb, int C,
     float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o, float *__restrict__ lse) {
   using T = BTile<D>;
   using F = FwdCfg<D>;
-  constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
+  constexpr int NKS = T::NKS, NDB = T::NDB;
   // The tiles' direct loads are issued by the first wave of each SIMD only
   // (waves 0..3): issuing them takes the vector-memory path a few hundred
   // clocks per tile, and those waves reach the barrier first.
@@ -298,32 +334,17 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // below (all issued before any use) overlap with them.
   issue_first();
 
-  // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8]
+  // Q fragments (MFMA B operand): lane holds q^[qi, h, 16 ks + 8 hl .. +8],
+  // from the prep pass's fragment-ordered copy (one contiguous 1 KB block
+  // per wave and 16-element step)
   u32x4 qf[NKS];
   {
-    const uint16_t *qrow = q + ((bM + (vq ? qi : 0)) * Hq + kvh * G + hloc) * D;
+    const int qb32 = (q0 + (AF_TK * wave) % BQ) / AF_TK;
+    const u32x4 *src = (const u32x4 *)(qfr + (((int64_t)b * Hq + kvh * G + hloc) * nq32 + qb32) * NKS * 512) + lane;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = vq ? *(const u32x4 *)(qrow + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
-    if (cs) {
-      const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq ? qi : 0)) * HALF);
-      f32x4 csv[NKS / 2][4];  // (cos, sin) of the 8 rotary pairs of (ks, hl), two pairs per vector
-#pragma unroll
-      for (int ks = 0; ks < NKS / 2; ++ks)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) csv[ks][w] = crow[(16 * ks + 8 * hl) / 2 + w];
-#pragma unroll
-      for (int ks = 0; ks < NKS / 2; ++ks) {
-        u32x4 &x = qf[ks], &y = qf[ks + NKS / 2];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f32x4 t = csv[ks][w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
-          const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
-          const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
-          x[w] = pack_bf16x2(x0 * t[0] - y0 * t[1], x1 * t[2] - y1 * t[3]);
-          y[w] = pack_bf16x2(y0 * t[0] + x0 * t[1], y1 * t[2] + x1 * t[3]);
-        }
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const u32x4 x = src[64 * ks];
+      qf[ks] = vq ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -394,7 +415,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // the second half of the softmax runs; then the loads of tile t+AF_NS-1.
   // After the barrier every wave is done with tile t-1, whose ring slot that
   // tile takes.
-  auto step = [&](int t, f32x16 &sc, bool masked, float msub) __attribute__((always_inline)) {
+  // (masked_c: std::true_type on the tiles that reach the diagonal, std::false_type before:
+  // two instantiations, so the tiles before the diagonal carry no mask work)
+  auto step = [&](int t, f32x16 &sc, auto masked_c, float msub) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(masked_c)::value;
     sync_tile();
     const uint16_t *K = sK + slot(t + 1) * T::TILE, *V = sV + slot(t) * T::TILE;
     const float bnext = sBias[slot(t + 1)][hloc][l32];
@@ -483,11 +507,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     }
     int t = 0;
     for (; t < tu; ++t) {
-      step(t, sc, false, msub);
+      step(t, sc, std::false_type{}, msub);
       msub = 0.f;
     }
     for (; t < nt; ++t) {
-      step(t, sc, true, msub);
+      step(t, sc, std::true_type{}, msub);
       msub = 0.f;
     }
     sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
@@ -533,40 +557,71 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     if (!sLast) return;
     npm = np;
   }
-  // merge pieces 0 .. npm-1 in order, all from their records (this one's too)
+  // merge pieces 0 .. npm-1 in piece order: the other pieces from their
+  // records, this one from its registers (the same values its record holds,
+  // so the sums do not depend on which piece arrives last)
   float mm = m2, lt = lsum;
   if (npm > 1) {
     const float *rec0 = part + ((int64_t)pfirst * nbh + bh) * RW + wave * F::NR * 64 + lane;
     const int64_t pstride = (int64_t)nbh * RW;
+    const float ref_own = lsum + __shfl_xor(lsum, 32) > 0.f ? m2 : -INFINITY, l_own = lsum;
+    f32x16 own[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) own[db] = acc[db];
     mm = -INFINITY;
-    for (int pp2 = 0; pp2 < npm; ++pp2) mm = fmaxf(mm, ld_dev(rec0 + pp2 * pstride + (F::NR - 2) * 64));
+    for (int pp2 = 0; pp2 < npm; ++pp2)
+      mm = fmaxf(mm, pp2 == p ? ref_own : ld_dev(rec0 + pp2 * pstride + (F::NR - 2) * 64));
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
     lt = 0.f;
     for (int pp2 = 0; pp2 < npm; ++pp2) {
       const float *rec = rec0 + pp2 * pstride;
-      const float sc = mm == -INFINITY ? 0.f : fast_exp2(ld_dev(rec + (F::NR - 2) * 64) - mm);
-      lt += ld_dev(rec + (F::NR - 1) * 64) * sc;
+      const bool mine = pp2 == p;  // work-group uniform
+      const float rf = mine ? ref_own : ld_dev(rec + (F::NR - 2) * 64);
+      const float sc = mm == -INFINITY ? 0.f : fast_exp2(rf - mm);
+      lt += (mine ? l_own : ld_dev(rec + (F::NR - 1) * 64)) * sc;
+      if (mine) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] += ld_dev(rec + (db * 16 + r) * 64) * sc;
+          for (int r = 0; r < 16; ++r) acc[db][r] += own[db][r] * sc;
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] += ld_dev(rec + (db * 16 + r) * 64) * sc;
+      }
     }
   }
   const float ltot = lt + __shfl_xor(lt, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (!vq) return;
   const int hq = kvh * G + hloc;
-  uint16_t *orow = o + ((bM + qi) * Hq + hq) * D;
+  if (lse && hl == 0 && vq)
+    lse[((int64_t)b * Hq + hq) * M + qi] = ltot > 0.f ? (mm + __log2f(ltot)) * kLn2 : -INFINITY;
+  // The normalised O^T tile goes out through LDS (the K/V ring, idle now):
+  // wave w stages its 32 columns x D as rows of D bf16 (16-byte pieces
+  // XOR-swizzled by the column), then writes each column's row of o as D/8
+  // contiguous 16-byte pieces.
+  constexpr int CPR = D / 8;  // 16-byte pieces per row
+  __syncthreads();            // every wave is done with the ring
+  uint8_t *stg = (uint8_t *)(wave < 4 ? sK : sV) + (wave & 3) * (AF_TK * D * 2);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hl;
-      *(u32x2 *)(orow + d) = u32x2{pack_bf16x2(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv),
-                                   pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
+      const int pc = (4 * db + g4) ^ (l32 & (CPR - 1));  // piece of elements 32 db + 8 g4 ..
+      *(u32x2 *)(stg + l32 * (2 * D) + pc * 16 + 8 * hl) =
+          u32x2{pack_bf16x2(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv),
+                pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
     }
-  if (lse && hl == 0) lse[((int64_t)b * Hq + hq) * M + qi] = ltot > 0.f ? (mm + __log2f(ltot)) * kLn2 : -INFINITY;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back only what it wrote
+  const int qcol0 = q0 + (AF_TK * wave) % BQ;           // query of column 0 of this wave
+#pragma unroll
+  for (int it = 0; it < AF_TK * CPR / 64; ++it) {
+    const int c = lane + 64 * it, col = c / CPR, ch = c % CPR;
+    const u32x4 x = *(const u32x4 *)(stg + col * (2 * D) + ((ch ^ (col & (CPR - 1))) * 16));
+    if (qcol0 + col < M) *(u32x4 *)(o + ((bM + qcol0 + col) * Hq + hq) * D + 8 * ch) = x;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -702,13 +757,20 @@ static size_t cnt_ints(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
   return (size_t)(B * Hkv * fwd_sched(B, M, Hq, Hkv).nqb);
 }
 
+// rotated queries: the backward's [B, M, Hq, D] or the forward's fragment
+// order over 32-query blocks [B, Hq, ceil(M / 32) * 32, D] (the larger)
+static size_t qhat_bytes(int64_t B, int64_t M, int64_t Hq, int64_t D) {
+  return (size_t)(B * Hq * ((M + 31) / 32 * 32) * D) * 2;
+}
+
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
   size_t n = rup((size_t)(B * M * (D / 2)) * sizeof(float2)) + rup((size_t)(B * M * Hkv * D) * 2) +
              rup((size_t)(B * Hq * M) * sizeof(float)) + rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float)) +
-             rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int)) + rup((size_t)(B * M) * sizeof(float));
+             rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int)) + rup((size_t)(B * M) * sizeof(float)) +
+             rup(qhat_bytes(B, M, Hq, D));
   if (bwd)
-    n += rup((size_t)(B * M * Hq * D) * 2) + rup((size_t)(B * Hq * M) * sizeof(float2)) +
-         2 * rup((size_t)(B * Hq * M) * sizeof(float)) + rup((size_t)(B * Hq * ((M + 31) / 32 * 32)) * sizeof(float));
+    n += rup((size_t)(B * Hq * M) * sizeof(float2)) + 2 * rup((size_t)(B * Hq * M) * sizeof(float)) +
+         rup((size_t)(B * Hq * ((M + 31) / 32 * 32)) * sizeof(float));
   return n;
 }
 
@@ -729,7 +791,7 @@ AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, in
   w.ratio = (float *)p;
   p += rup((size_t)(B * M) * sizeof(float));
   w.qhat = (uint16_t *)p;
-  p += rup((size_t)(B * M * Hq * D) * 2);
+  p += rup(qhat_bytes(B, M, Hq, D));
   w.rowstat = (float2 *)p;
   p += rup((size_t)(B * Hq * M) * sizeof(float2));
   w.colsum = (float *)p;
@@ -742,7 +804,7 @@ AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, in
 
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
                             int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
-                            bool g_per_head, const AttnWs &w, hipStream_t s) {
+                            bool g_per_head, const AttnWs &w, hipStream_t s, const void *q) {
   if ((int64_t)B * M == 0) return hipSuccess;
   InvFreq inv;
   for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
@@ -751,7 +813,8 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
   hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0, s,
                      (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
                      (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, with_ratio ? w.ratio : nullptr,
-                     w.cnt, with_bias ? w.ncnt : 0, (int)g_per_head);
+                     w.cnt, with_bias ? w.ncnt : 0, (int)g_per_head, (const uint16_t *)q, q ? w.qhat : nullptr,
+                     (M + 31) / 32);
   return hipGetLastError();
 }
 
@@ -761,7 +824,7 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
                            hipStream_t s) {
   if ((int64_t)B * M == 0) return hipSuccess;
   hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, g_per_head,
-                                  w, s);
+                                  w, s, bf16 ? q : nullptr);
   if (e != hipSuccess) return e;
   const float2 *cs = pos ? w.cs : nullptr;
   const double c = 1.0 / (sqrt((double)D) * (double)tau);
@@ -772,8 +835,9 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
     auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>)
                          : (sigma ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>);
-    hipLaunchKernelGGL(kern, grid, dim3(512), 0, s, (const uint16_t *)q, kh, (const uint16_t *)v, w.bias, cs, c2,
-                       sigma, w.ratio, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part, w.cnt, (uint16_t *)o, lse);
+    hipLaunchKernelGGL(kern, grid, dim3(512), 0, s, (const uint16_t *)w.qhat, (M + 31) / 32, kh, (const uint16_t *)v,
+                       w.bias, c2, sigma, w.ratio, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part, w.cnt,
+                       (uint16_t *)o, lse);
   } else {
     const int64_t rows = (int64_t)B * M * Hq;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const float *)q,

@@ -14,7 +14,8 @@ struct AttnWs {
   int *cnt;          // [B*Hkv, nqb] arrival counters of the split query blocks
   int ncnt;
   float *ratio;      // [B, M] ln m_i / ln max(2, p_i), the temperature's row factor
-  uint16_t *qhat;    // [B, M, Hq, D] rotated queries (bf16) of the backward
+  uint16_t *qhat;    // rotated queries (bf16): the backward's [B, M, Hq, D], or the forward's
+                     // MFMA-fragment order [B, Hq, ceil(M / 32), D / 16, 64 lanes, 8]
   float2 *rowstat;   // [B, Hq, M] (-lse / c, D_i) of the backward (fp32 path: D_i alone)
   float *colsum;     // [B, Hq, M] column sums of dS per head
   float *tau;        // [B, Hq, Mp] temperature of each (row, head) of the backward, Mp = M rounded up
@@ -33,7 +34,7 @@ size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64
 AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
                             int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
-                            bool g_per_head, const AttnWs &w, hipStream_t s);
+                            bool g_per_head, const AttnWs &w, hipStream_t s, const void *q = nullptr);
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
                            int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, const AttnWs &w,
