@@ -216,6 +216,22 @@ tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_
                          int32_t *kept_count, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * tg_select_topk_noalloc -- tg_select_topk with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments, results
+ * and errors as tg_select_topk.  Its scratch is a 16 MiB device array inside
+ * the library, one per GPU, held until the process ends: a call needing more
+ * than that (tg_select_topk_workspace_size(B, N) > 16 MiB: rows of up to
+ * 32768 tokens need none; a single row fits up to about 1.3 M tokens) returns
+ * TG_ERR_UNSUPPORTED before any launch.  It allocates nothing.  Calls on one GPU share that array: calls that overlap
+ * on one GPU (several streams or threads at once) race and must be ordered by
+ * the caller; no state carries over from one call to the next.
+ */
+tg_status tg_select_topk_noalloc(const float *scores, const uint8_t *forced_keep, int64_t B,
+                                 int64_t N, int64_t K, int64_t n_forced, int32_t *kept_idx,
+                                 int32_t *kept_count, void *stream);
+
+/*
  * tg_compact -- gather of the kept tokens' hidden states, original positions
  * and gate values.  [DeepDive] section 3.4: the hidden states are sliced with
  * the keep indices and the position ids are taken at the same indices.

@@ -38,7 +38,7 @@ __all__ = [
     "tg_gate_score_workspace_size", "tg_gate_pack_w1", "tg_gate_score_packed", "gate_workspace",
     "tg_select_topk", "tg_compact", "tg_gated_attn_fwd", "tg_gated_attn_bwd",
     "tg_select_topk_workspace_size", "tg_gated_attn_workspace_size", "gate_layer_forward", "attn_workspace",
-    "select_workspace",
+    "select_workspace", "tg_select_topk_noalloc",
     "tg_gate_score_ln", "tg_score_normalize", "tg_gate_softmax", "tg_gate_softmax_bwd",
     "tg_gated_attn_varlen_workspace_size", "tg_gated_attn_fwd_varlen", "tg_gated_attn_bwd_varlen",
     "attn_varlen_workspace", "tg_gate_score_heads", "tg_score_normalize_heads", "tg_aggregate_heads",
@@ -94,6 +94,8 @@ def load():
     lib.tg_select_topk_workspace_size.argtypes = [i64, i64]
     lib.tg_select_topk.restype = c_int
     lib.tg_select_topk.argtypes = [P, P, i64, i64, i64, i64, P, P, P, sz, P]
+    lib.tg_select_topk_noalloc.restype = c_int
+    lib.tg_select_topk_noalloc.argtypes = [P, P, i64, i64, i64, i64, P, P, P]
     lib.tg_compact.restype = c_int
     lib.tg_compact.argtypes = [P, P, P, P, i64, i64, i64, i64, c_int, P, P, P, P]
     lib.tg_gate_score_ln.restype = c_int
@@ -279,6 +281,14 @@ def tg_select_topk(scores, forced_keep, K, n_forced, kept_idx, kept_count=None, 
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_select_topk(_ptr(scores), _ptr(forced_keep), B, N, int(K), int(n_forced), _ptr(kept_idx),
                                  _ptr(kept_count), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tg_select_topk_noalloc(scores, forced_keep, K, n_forced, kept_idx, kept_count=None, stream=None):
+    """tg_select_topk with the library's own device scratch (no workspace, nothing allocated)."""
+    _contig(scores, forced_keep, kept_idx, kept_count)
+    B, N = scores.shape
+    _check(load().tg_select_topk_noalloc(_ptr(scores), _ptr(forced_keep), B, N, int(K), int(n_forced),
+                                         _ptr(kept_idx), _ptr(kept_count), _stream(stream)))
 
 
 def tg_compact(hidden, pos, gates, kept_idx, hidden_out=None, pos_out=None, gates_out=None, stream=None):

@@ -29,6 +29,8 @@ hipError_t launch_gate_softmax_bwd(const float *g, const float *dg, int64_t B, i
 hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_t B, int64_t N, int64_t K,
                               int64_t M_alloc, int32_t *kept, int32_t *kept_count, void *ws, hipStream_t s);
 size_t select_ws_bytes(int64_t B, int64_t N);
+size_t select_scratch_bytes();
+void *select_scratch(hipError_t *err);
 hipError_t launch_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept,
                           int64_t B, int64_t N, int64_t M, int64_t row_bytes, void *hidden_out, int32_t *pos_out,
                           float *gates_out, hipStream_t s);
@@ -386,6 +388,30 @@ tg_status tg_select_topk(const float *scores, const uint8_t *forced_keep, int64_
   return hip_status(tg::launch_select_topk(scores, forced_keep, B, N, K, M, kept_idx, kept_count, ws,
                                            (hipStream_t)stream),
                     "tg_select_topk launch");
+}
+
+tg_status tg_select_topk_noalloc(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t N, int64_t K,
+                                 int64_t n_forced, int32_t *kept_idx, int32_t *kept_count, void *stream) {
+  REQUIRE(B >= 0 && N >= 0, TG_ERR_INVALID_ARG, "B and N must be >= 0");
+  REQUIRE(K >= 0, TG_ERR_INVALID_ARG, "K must be >= 0 (got %lld)", (long long)K);
+  REQUIRE(n_forced >= 0 && n_forced <= N, TG_ERR_INVALID_ARG, "need 0 <= n_forced <= N (n_forced=%lld N=%lld)",
+          (long long)n_forced, (long long)N);
+  REQUIRE(forced_keep || n_forced == 0, TG_ERR_INVALID_ARG, "forced_keep is NULL but n_forced > 0");
+  REQUIRE(N <= kSelMaxN && B <= 65535, TG_ERR_UNSUPPORTED, "selection needs N <= 2^22 and B <= 65535");
+  const size_t need = tg::select_ws_bytes(B, N), cap = tg::select_scratch_bytes();
+  REQUIRE(need <= cap, TG_ERR_UNSUPPORTED,
+          "tg_select_topk_noalloc: B=%lld, N=%lld needs %zu bytes of scratch, more than its %zu (use tg_select_topk "
+          "with a workspace)", (long long)B, (long long)N, need, cap);
+  const int64_t M = tg_kept_count(N, n_forced, K);
+  if (B * N > 0) REQUIRE(scores && kept_idx, TG_ERR_INVALID_ARG, "scores and kept_idx are required");
+  REQUIRE(aligned16(scores) && aligned16(kept_idx), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (B == 0) return ok();
+  hipError_t e = hipSuccess;
+  void *ws = tg::select_scratch(&e);
+  if (!ws) return hip_status(e, "tg_select_topk_noalloc scratch address");
+  return hip_status(tg::launch_select_topk(scores, forced_keep, B, N, K, M, kept_idx, kept_count, ws,
+                                           (hipStream_t)stream),
+                    "tg_select_topk_noalloc launch");
 }
 
 tg_status tg_compact(const void *hidden, const int32_t *pos, const float *gates, const int32_t *kept_idx,

@@ -27,6 +27,8 @@
 // Every count is an integer and every position comes from a prefix sum, so
 // the output is deterministic; the workspace needs no initial contents (each
 // launch writes what the next one reads).
+#include <mutex>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -791,6 +793,44 @@ hipError_t launch_select_topk(const float *scores, const uint8_t *forced, int64_
   hipLaunchKernelGGL(select_refine_kernel, grid, dim3(SEL_TPB), 0, s, scores, forced, N, K, G, w, kept_count);
   hipLaunchKernelGGL(select_emit_kernel, grid, dim3(SEL_TPB), 0, s, scores, forced, N, M_alloc, G, w, kept);
   return hipGetLastError();
+}
+
+// Allocation-free selection: the workspace lives in a device array of this
+// library, one per GPU (each GPU holds its own copy at its own address, taken
+// once per device with hipGetSymbolAddress; host code uses only that address,
+// never the array's name).  Calls on one GPU share it, so calls that overlap
+// on that GPU race; every launch of a call writes what the next one reads, so
+// nothing needs clearing between calls.
+constexpr size_t kSelScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kSelScratchBytes];
+
+size_t select_scratch_bytes() { return kSelScratchBytes; }
+
+// The device address of this GPU's scratch array (nullptr on failure, with
+// the HIP error in *err).  The first call on a device, with that device
+// current, takes the address; later calls reuse it.
+void *select_scratch(hipError_t *err) {
+  static std::mutex mu;
+  static void *ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= 64)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      *err = e;
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptr[dev];
 }
 
 hipError_t launch_compact(const void *hidden, const int32_t *pos, const float *gates,
