@@ -70,6 +70,7 @@ def _load():
     lib.tgo_attn_bwd.restype = ctypes.c_int
     lib.tgo_round_bf16.argtypes = [ctypes.c_double]
     lib.tgo_gate_score_heads.argtypes = [_D, _D, _D, _i64, _i64, _i64, _i64, _D]
+    lib.tgo_gate_score_clone.argtypes = [_D, _D, _D, _D, _D, _i64, _i64, _i64, _i64, _D]
     lib.tgo_rms_norm.argtypes = [_D, _D, ctypes.c_double, _i64, _i64, _D]
     lib.tgo_gate_score_ln.argtypes = [_D, _D, ctypes.c_double, _D, _D, _U8, _i64, _i64, _i64, _D, _D]
     lib.tgo_score_normalize.argtypes = [_D, _U8, _i64, _i64, ctypes.c_double, _D]
@@ -166,6 +167,29 @@ def gate_score_heads(hidden, w1, w2):
     H = W2.shape[0]
     out = np.empty((H, T), np.float64)
     lib.tgo_gate_score_heads(_ptr(h, _D), _ptr(W1, _D), _ptr(W2, _D), T, d, d_ff, H, _ptr(out, _D))
+    return out
+
+
+def gate_score_clone(hidden, w_gate, w_up, w_down, w_head):
+    """Raw scores of the scoring branch cloned from the gate layer's MLP (DeepDive section 3.4 and the
+    section 3 pipeline figure), read as the gated (SwiGLU) MLP followed by a head projection:
+    b~^h = w_head[h] . (w_down (SiLU(w_gate a~) * (w_up a~))).
+
+    hidden [T, d] (already normalised); w_gate, w_up [d_i, d]; w_down [d, d_i]; w_head [H, d] (or [d]
+    for one head).  Returns float64 [H, T].
+    """
+    lib = _load()
+    h = _f64(hidden)
+    Wg, Wu, Wd = _f64(w_gate), _f64(w_up), _f64(w_down)
+    T, d = h.shape
+    d_i = Wg.shape[0]
+    if Wg.shape != (d_i, d) or Wu.shape != (d_i, d) or Wd.shape != (d, d_i):
+        raise ValueError("w_gate, w_up must be [d_i, d] and w_down [d, d_i]")
+    P = np.ascontiguousarray(_f64(w_head).reshape(-1, d))
+    H = P.shape[0]
+    out = np.empty((H, T), np.float64)
+    lib.tgo_gate_score_clone(_ptr(h, _D), _ptr(Wg, _D), _ptr(Wu, _D), _ptr(Wd, _D), _ptr(P, _D), T, d, d_i, H,
+                             _ptr(out, _D))
     return out
 
 

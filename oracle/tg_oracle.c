@@ -24,7 +24,8 @@
  * library routines, autograd, finite differences).  The readings listed as
  * contract choices (scorer shape without biases, gate of forced tokens = 1,
  * scalar temperature on q.k only, RoPE pairing and theta, where bf16 rounding
- * happens) are "parity unpinned" by the pages: the pages do not fix them.
+ * happens, the clone scorer's SwiGLU form and head projection) are "parity
+ * unpinned" by the pages: the pages do not fix them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -695,3 +696,55 @@ void tgo_gate_score_heads(const double *hidden, const double *w1, const double *
 
 /* Exposed for the pin tests of the bf16 rounding helper. */
 double tgo_round_bf16(double x) { return round_bf16(x); }
+
+/*
+ * [DeepDive] section 3.4 (the released code keeps a scoring branch cloned from
+ * the gate layer's MLP) and the pipeline figure of section 3 ("MLP clone of
+ * gate-layer MLP", whose outputs become the raw scores of Eq. 3).  The pages
+ * give neither the MLP's form nor how a scalar (or one value per head) is read
+ * off it.  Reading used here: the gate layer's MLP is the gated (SwiGLU) MLP of
+ * the Qwen3 models the pages evaluate, cloned with its shapes, followed by a
+ * head projection P with H rows (zero at initialisation, which gives the
+ * "score MLP starts at zero" of section 3.1):
+ *     gt_k = sum_i Wg[k, i] a~[i],   up_k = sum_i Wu[k, i] a~[i]   (k < d_i)
+ *     m_k  = SiLU(gt_k) * up_k
+ *     y_o  = sum_k Wd[o, k] m_k                                    (o < d)
+ *     b~^h = sum_o P[h, o] y_o                                     (h < H)
+ * Wg, Wu: [d_i, d]; Wd: [d, d_i]; P: [H, d] (all out x in).  hidden: [T, d]
+ * (already normalised); scores: [H, T] (head-major).
+ */
+void tgo_gate_score_clone(const double *hidden, const double *wg, const double *wu, const double *wd,
+                          const double *wh, int64_t T, int64_t d, int64_t d_i, int64_t H, double *scores)
+{
+#pragma omp parallel
+    {
+        double *m = (double *)malloc((size_t)(d_i > 0 ? d_i : 1) * sizeof(double));
+        double *y = (double *)malloc((size_t)(d > 0 ? d : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < T; ++t) {
+            const double *h = hidden + t * d;
+            for (int64_t k = 0; k < d_i; ++k) {
+                double gt = 0.0, up = 0.0;
+                for (int64_t i = 0; i < d; ++i) {
+                    gt += wg[k * d + i] * h[i];
+                    up += wu[k * d + i] * h[i];
+                }
+                m[k] = gt / (1.0 + exp(-gt)) * up;
+            }
+            for (int64_t o = 0; o < d; ++o) {
+                double s = 0.0;
+                for (int64_t k = 0; k < d_i; ++k)
+                    s += wd[o * d_i + k] * m[k];
+                y[o] = s;
+            }
+            for (int64_t hh = 0; hh < H; ++hh) {
+                double s = 0.0;
+                for (int64_t o = 0; o < d; ++o)
+                    s += wh[hh * d + o] * y[o];
+                scores[hh * T + t] = s;
+            }
+        }
+        free(m);
+        free(y);
+    }
+}
