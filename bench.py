@@ -172,6 +172,7 @@ def run_gpu(args):
     temp_us = time_loop(attn_temp, args.steps, stream) * 1e6
     operative = run_operative(args, tg, wl, w, dev, stream, gi, sel, at, K, M)
     operative["per_head"] = run_operative_heads(args, tg, wl, w, dev, stream, gi, at, K, M)
+    operative["clone_scorer"] = run_clone(args, tg, wl, w, dev, gi)
 
     work = algorithmic_work(w, M)
     kern = {}
@@ -370,6 +371,39 @@ def run_operative_heads(args, tg, wl, w, dev, stream, gi, at, K, M):
     tot = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs])) * 1e-3
     return dict(heads=H, stages_us=per, device_path_us=tot * 1e6, tokens_per_s=w.B * w.N / tot,
                 note="gate_score_heads includes its W1 pack pass (RMSNorm weight folded in)")
+
+
+def run_clone(args, tg, wl, w, dev, gi):
+    """The scorer cloned from the gate layer's MLP (SwiGLU at the Qwen3-1.7B width + a 16-row head
+    projection) over the same hidden states: time per call, including its weight packing and the
+    down/head fold (not part of `value`)."""
+    import torch
+
+    d_i, H = wl.QWEN3_1P7B_MLP, 16
+    ci = wl.clone_inputs(w, d_i, H)
+    T = lambda x: wl.to_torch(x, w.dtype, dev)
+    h = T(gi["hidden"])
+    wg, wu, wd, wh = (T(ci[k]) for k in ("w_gate", "w_up", "w_down", "w_head"))
+    scores = torch.empty((w.B, H, w.N), device=dev)
+    ws = torch.empty(tg.tg_gate_score_clone_workspace_size(w.d, d_i, H), dtype=torch.uint8, device=dev)
+    call = lambda: tg.tg_gate_score_clone(h, wg, wu, wd, wh, scores, ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    n = max(3, min(args.steps, 10))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])) * 1e-3
+    tok = w.B * w.N
+    flops = 2.0 * tok * w.d * 2 * d_i + 2.0 * tok * d_i * H
+    return dict(d_i=d_i, heads=H, us=t * 1e6, alg_flops=flops, mfma_TFLOPs=flops / t / 1e12,
+                mfma_frac=flops / t / PEAK_BF16, tokens_per_s=tok / t,
+                note="one tg_gate_score_clone call: gate/up packing, the down x head fold, the gated "
+                     "products and the head sums")
 
 
 def run_train(args, tg, wl, dev):

@@ -388,6 +388,42 @@ tg_status tg_gated_attn_bwd_headgates(const void *q, const void *k, const void *
                                       size_t ws_bytes, void *stream);
 
 /*
+ * tg_gate_score_clone -- raw scores from a scoring branch cloned from the gate
+ * layer's MLP ([DeepDive] section 3.4, and the section 3 pipeline figure's
+ * "MLP clone of gate-layer MLP" feeding the sequence-normalised scores of
+ * Eq. 3).  The pages give the branch no shape.  Reading: the gated (SwiGLU)
+ * MLP of the Qwen3 models the pages evaluate, with its shapes, followed by a
+ * head projection P of H rows (zero at initialisation, so the scores start
+ * at zero as section 3.1 states):
+ *   m_k    = SiLU(sum_i w_gate[k,i] a~[b,n,i]) * (sum_i w_up[k,i] a~[b,n,i])
+ *   b~[b][h][n] = sum_o w_head[h,o] sum_k w_down[o,k] m_k
+ * with a~ = RMSNorm(hidden) (weight ln_w or NULL = 1, ln_eps) when ln != 0,
+ * else a~ = hidden.  The outputs feed tg_score_normalize_heads (or, with
+ * H = 1, tg_score_normalize) exactly as the per-head scorer's do.
+ *   hidden [B, N, d] (dt); w_gate, w_up [d_i, d]; w_down [d, d_i];
+ *   w_head [H, d] (dt), 1 <= H <= 16, d_i <= 32768; scores [B, H, N] f32 out.
+ *   The call computes U = w_head w_down ([H, d_i], fp32) into the workspace and
+ *   then b~ = U m, the same sum taken in the other order.  bf16: d % 32 == 0;
+ *   ln_w is folded into the packed gate and up weights (one bf16 rounding of
+ *   each product, as tg_gate_score_ln); the gate and up products on the matrix
+ *   cores (fp32 accumulation), SiLU and
+ *   m in fp32, and U m as a matrix-core product of bf16 pairs (U and m each as
+ *   hi + lo, within 2^-16 of the fp32 product).  f32: d % 4 == 0,
+ *   d + d_i <= 16000, plain fp32.
+ *   ws: tg_gate_score_clone_workspace_size(d, d_i, H, dt) bytes, 16-byte
+ *   aligned (bf16: the gate/up weights packed in fragment order; then U and
+ *   the partial sums that form it), owned by the caller, overwritten.
+ *   Errors as tg_gate_score; TG_ERR_UNSUPPORTED for H or d_i out of range.
+ *   Deterministic: fixed-order sums throughout.
+ */
+size_t tg_gate_score_clone_workspace_size(int64_t d, int64_t d_i, int64_t H, tg_dtype dt);
+tg_status tg_gate_score_clone(const void *hidden, int ln, const void *ln_w, float ln_eps,
+                              const void *w_gate, const void *w_up, const void *w_down,
+                              const void *w_head, int64_t B, int64_t N, int64_t d, int64_t d_i,
+                              int64_t H, tg_dtype dt, float *scores, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
  * Packed variable-length attention: the training path evaluates both budgets'
  * targets in one call ([DeepDive] section 3.3), i.e. several sequences of
  * different lengths packed back to back.  Sequence s holds tokens

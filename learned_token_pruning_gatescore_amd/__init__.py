@@ -25,6 +25,8 @@ The rest of the scoring definition (section 2 Eq. 1, section 3.1 Eq. 3, section 
 Per-head scores, uniform head aggregation, per-head gates (section 3.4):
   tg_gate_score_heads, tg_score_normalize_heads, tg_aggregate_heads, tg_gather_heads,
   tg_gate_softmax_heads, tg_gated_attn_fwd_headgates / tg_gated_attn_bwd_headgates
+The scoring branch cloned from the gate layer's MLP (section 3.4):
+  tg_gate_score_clone
 Packed variable-length sequences (section 3.3: both budgets in one call):
   tg_gated_attn_fwd_varlen / tg_gated_attn_bwd_varlen
 """
@@ -43,6 +45,7 @@ __all__ = [
     "tg_gated_attn_varlen_workspace_size", "tg_gated_attn_fwd_varlen", "tg_gated_attn_bwd_varlen",
     "attn_varlen_workspace", "tg_gate_score_heads", "tg_score_normalize_heads", "tg_aggregate_heads",
     "tg_gather_heads", "tg_gate_softmax_heads", "tg_gated_attn_fwd_headgates", "tg_gated_attn_bwd_headgates",
+    "tg_gate_score_clone", "tg_gate_score_clone_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +111,10 @@ def load():
     lib.tg_gate_softmax_bwd.argtypes = [P, P, i64, i64, P, P]
     lib.tg_gate_score_heads.restype = c_int
     lib.tg_gate_score_heads.argtypes = [P, c_int, P, f32, P, P, i64, i64, i64, i64, i64, c_int, P, P, sz, P]
+    lib.tg_gate_score_clone_workspace_size.restype = sz
+    lib.tg_gate_score_clone_workspace_size.argtypes = [i64, i64, i64, c_int]
+    lib.tg_gate_score_clone.restype = c_int
+    lib.tg_gate_score_clone.argtypes = [P, c_int, P, f32, P, P, P, P, i64, i64, i64, i64, i64, c_int, P, P, sz, P]
     lib.tg_score_normalize_heads.restype = c_int
     lib.tg_score_normalize_heads.argtypes = [P, P, i64, i64, i64, f32, P, P]
     lib.tg_aggregate_heads.restype = c_int
@@ -346,6 +353,30 @@ def tg_gate_score_heads(hidden, w1, w2, scores, ws=None, ln_w=None, ln_eps=None,
     _check(load().tg_gate_score_heads(_ptr(hidden), int(ln), _ptr(ln_w), float(ln_eps if ln else 0.0), _ptr(w1),
                                       _ptr(w2), B, N, d, d_ff, H, _dt(hidden), _ptr(scores), _ptr(ws), ws_bytes,
                                       _stream(stream)))
+
+
+def tg_gate_score_clone_workspace_size(d, d_i, H, bf16=True):
+    return load().tg_gate_score_clone_workspace_size(d, d_i, H, TG_BF16 if bf16 else TG_F32)
+
+
+def tg_gate_score_clone(hidden, w_gate, w_up, w_down, w_head, scores, ws=None, ln_w=None, ln_eps=None, stream=None):
+    """Scores [B, H, N] of the branch cloned from the gate layer's MLP: hidden [B, N, d]; w_gate, w_up
+    [d_i, d]; w_down [d, d_i]; w_head [H, d] (RMSNorm in front when ln_eps is given).  ws: workspace
+    (allocated here when None)."""
+    import torch
+
+    _contig(hidden, w_gate, w_up, w_down, w_head, scores, ws, ln_w)
+    B, N, d = hidden.shape
+    d_i = w_gate.shape[0]
+    H = w_head.shape[0] if w_head.dim() == 2 else 1
+    if ws is None:
+        n = tg_gate_score_clone_workspace_size(d, d_i, H, hidden.dtype == torch.bfloat16)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=hidden.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    ln = ln_eps is not None
+    _check(load().tg_gate_score_clone(_ptr(hidden), int(ln), _ptr(ln_w), float(ln_eps if ln else 0.0), _ptr(w_gate),
+                                      _ptr(w_up), _ptr(w_down), _ptr(w_head), B, N, d, d_i, H, _dt(hidden),
+                                      _ptr(scores), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tg_score_normalize_heads(scores, forced_keep, eps, out, stream=None):

@@ -14,7 +14,12 @@
 
 namespace tg {
 size_t gate_packed_bytes(int d, int d_ff);
-hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s);
+hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s,
+                               const void *w_up = nullptr);
+size_t gate_clone_ws_bytes(int d, int d_i, int H, bool bf16);
+hipError_t launch_gate_clone(const void *hidden, const void *w_gate, const void *w_up, const void *w_down,
+                             const void *w_head, int64_t T, int d, int d_i, int H, bool bf16, bool ln,
+                             const void *ln_w, float ln_eps, float *scores, int64_t Nrow, void *ws, hipStream_t s);
 hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2, const uint8_t *forced, int64_t T,
                              int d, int d_ff, bool bf16, bool ln, const void *ln_w, float ln_eps, float *scores,
                              float *gates, hipStream_t s, int H = 0, int64_t Nrow = 0);
@@ -289,6 +294,37 @@ tg_status tg_gate_score_heads(const void *hidden, int ln, const void *ln_w, floa
   return hip_status(tg::launch_gate_score(hidden, w1, w2, nullptr, B * N, (int)d, (int)d_ff, false, ln != 0, ln_w,
                                           ln_eps, scores, nullptr, s, (int)H, N),
                     "tg_gate_score_heads launch");
+}
+
+size_t tg_gate_score_clone_workspace_size(int64_t d, int64_t d_i, int64_t H, tg_dtype dt) {
+  if ((dt != TG_BF16 && dt != TG_F32) || d <= 0 || d_i <= 0 || H < 1 || H > 16 || d > 65536 || d_i > 32768) return 0;
+  return tg::gate_clone_ws_bytes((int)d, (int)d_i, (int)H, dt == TG_BF16);
+}
+
+tg_status tg_gate_score_clone(const void *hidden, int ln, const void *ln_w, float ln_eps, const void *w_gate,
+                              const void *w_up, const void *w_down, const void *w_head, int64_t B, int64_t N,
+                              int64_t d, int64_t d_i, int64_t H, tg_dtype dt, float *scores, void *ws,
+                              size_t ws_bytes, void *stream) {
+  const tg_status st = check_gate(hidden, w_gate, w_up, B, N, d, d_i, dt, scores, nullptr);
+  if (st != TG_OK) return st;
+  REQUIRE(w_down && w_head, TG_ERR_INVALID_ARG, "w_down and w_head are required");
+  REQUIRE(aligned16(w_down) && aligned16(w_head), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(H >= 1 && H <= 16, TG_ERR_UNSUPPORTED, "1 <= H <= 16 heads (got %lld)", (long long)H);
+  REQUIRE(d_i <= 32768, TG_ERR_UNSUPPORTED, "d_i <= 32768 (got %lld)", (long long)d_i);
+  if (dt == TG_F32)
+    REQUIRE(d + d_i <= 16000, TG_ERR_UNSUPPORTED, "f32 clone scoring needs d + d_i <= 16000 (one row in LDS)");
+  if (ln) {
+    REQUIRE(std::isfinite(ln_eps) && ln_eps >= 0.f, TG_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
+    REQUIRE(aligned16(ln_w), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  }
+  const size_t need = tg::gate_clone_ws_bytes((int)d, (int)d_i, (int)H, dt == TG_BF16);
+  REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "clone scoring needs a %zu-byte workspace (got %zu)", need,
+          ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned16(ws), TG_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (B * N == 0) return ok();
+  return hip_status(tg::launch_gate_clone(hidden, w_gate, w_up, w_down, w_head, B * N, (int)d, (int)d_i, (int)H,
+                                          dt == TG_BF16, ln != 0, ln_w, ln_eps, scores, N, ws, (hipStream_t)stream),
+                    "tg_gate_score_clone launch");
 }
 
 tg_status tg_score_normalize(const float *scores, const uint8_t *forced_keep, int64_t B, int64_t N, float eps,

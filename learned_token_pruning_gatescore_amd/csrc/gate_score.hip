@@ -54,18 +54,25 @@ size_t gate_packed_bytes(int d, int d_ff) { return (size_t)gate_ngp(d_ff) * gate
 // A operand of one 32x32x16 MFMA, as one contiguous 1 KB block.  A work-group
 // packs 32 rows x 128 inputs: coalesced row reads into LDS, then eight
 // contiguous 1 KB blocks out.
+// With w_up (the gated MLP of the clone scorer, d_ff = units per matrix):
+// group ug holds rows 32 (ug / 2) .. + 31 of w1 (the gate product) for even ug
+// and of w_up for odd ug, so one wave's two 32-row blocks are the gate and up
+// rows of the same 32 units.
 __global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__restrict__ w1,
+                                                           const uint16_t *__restrict__ w_up,
                                                            const uint16_t *__restrict__ ln_w, int d, int d_ff,
                                                            int nkk, uint16_t *__restrict__ out) {
   __shared__ u32x4 t[32][17];  // 32 rows x 16 chunks of 8 inputs (+1 chunk of padding)
   const int tid = threadIdx.x, kc = blockIdx.x, ug = blockIdx.y;
+  const uint16_t *src = w_up && (ug & 1) ? w_up : w1;
+  const int ubase = w_up ? 32 * (ug >> 1) : 32 * ug;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int idx = tid + 256 * j, row = idx >> 4, c = idx & 15;
-    const int u = 32 * ug + row, k0 = 128 * kc + 8 * c;
+    const int u = ubase + row, k0 = 128 * kc + 8 * c;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (u < d_ff && k0 < d) {
-      v = *(const u32x4 *)(w1 + (int64_t)u * d + k0);  // d % 8 == 0: all 8 in range
+      v = *(const u32x4 *)(src + (int64_t)u * d + k0);  // d % 8 == 0: all 8 in range
       if (ln_w) {  // w1[u, i] * w[i]: exact in fp32 (bf16 x bf16), rounded once to bf16
         const u32x4 lw = *(const u32x4 *)(ln_w + k0);
 #pragma unroll
@@ -95,11 +102,17 @@ __global__ __launch_bounds__(256) void gate_pack_w1_kernel(const uint16_t *__res
 // then r_t scales the pre-activations.
 // MH: H output heads (w2 [H, d_ff]); scores [B, H, Nrow] head-major, no gates
 // (the per-head gates come from the per-head softmax over the kept set).
-template <int NTB, bool LN, bool MH>
+// GLU (with MH): the clone scorer.  w1p is the interleaved gate/up packing
+// (d_ff = 2 d_i rows), so wave w's blocks in chunk c are the gate (ub = 0) and
+// up (ub = 1) rows of units 32 (c / 64 + w) .. + 31; m = SiLU(gate) * up, and
+// the head sums take ufold [H, d_i] (the head projection times the down
+// projection, fp32) in place of w2.
+template <int NTB, bool LN, bool MH, bool GLU = false>
 __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
     const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ w1p, const uint16_t *__restrict__ w2,
     const uint8_t *__restrict__ forced, int64_t T, int d, int d_ff, int nkk, float ln_eps, int H, int64_t Nrow,
-    float *__restrict__ scores, float *__restrict__ gates) {
+    float *__restrict__ scores, float *__restrict__ gates, const float *__restrict__ ufold) {
+  static_assert(!GLU || MH, "the clone scorer writes per-head scores");
   constexpr int TT = 32 * NTB;         // tokens per work-group
   constexpr int ST = TT * GS_BK;       // u16 per hidden stage
   constexpr int NI = TT / (8 * GS_W);  // direct-load instructions (8 rows each) per wave per stage
@@ -264,53 +277,102 @@ __global__ __launch_bounds__(64 * GS_W, 1) void gate_score_bf16_kernel(
       for (int tb = 0; tb < NTB; ++tb) rt[tb] = sR[32 * tb + l32];
     }
     if (MH) {
-      // The head sums are a second matrix product, C2[h][t] = sum_u w2[h][u] SiLU(a[u][t]),
-      // over this wave's 64 units, four 16-unit steps.  The accumulator layout already is
-      // the B operand: in step (ub, s) the lane of token j and half q holds, as element e,
-      // registers 8 s + e of acc[ub][tb], i.e. unit 32 ub + 16 s + 8 (e / 4) + 4 q + e % 4;
-      // the A operand (rows = heads, H <= 16 of 32) takes w2 in that unit order.  SiLU
-      // enters as two bf16 parts (fp32 accumulate).
-      u32x4 a2[GS_UB][2];
-#pragma unroll
-      for (int ub = 0; ub < GS_UB; ++ub)
+      f32x16 c2[NTB];
+      if (GLU) {
+        // The head sums C2[h][t] = sum_u U[h][u] m[u][t] over this wave's 32 units, two
+        // 16-unit steps, with the B operand laid out as in the MH branch below (step sh, element
+        // e: register 8 sh + e, unit 16 sh + 8 (e / 4) + 4 q + e % 4 of the block).  U and m
+        // enter as bf16 pairs hi + lo; three products (hi hi, hi lo, lo hi) leave out lo lo.
+        const int dI = d_ff / 2, ub0 = 32 * (c / 64 + wave);
+        u32x4 uh[2], ul[2];
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh) {
-          const int u0 = c + wave * 32 * GS_UB + 32 * ub + 16 * sh + 4 * hl;  // units u0 + {0..3}, u0 + 8 + {0..3}
-          const uint16_t *wr = w2 + (int64_t)l32 * d_ff;
-          uint32_t e16[8];
+          float uv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int u = u0 + 8 * (e >> 2) + (e & 3);
-            e16[e] = (l32 < H && u < d_ff) ? (uint32_t)wr[u] : 0u;
+            const int u = ub0 + 16 * sh + 8 * (e >> 2) + 4 * hl + (e & 3);
+            uv[e] = (l32 < H && u < dI) ? ufold[(int64_t)l32 * dI + u] : 0.f;
           }
 #pragma unroll
-          for (int w = 0; w < 4; ++w) a2[ub][sh][w] = e16[2 * w] | (e16[2 * w + 1] << 16);
+          for (int w = 0; w < 4; ++w) {
+            uh[sh][w] = pack_bf16x2(uv[2 * w], uv[2 * w + 1]);
+            ul[sh][w] = pack_bf16x2(uv[2 * w] - bf16_lo(uh[sh][w]), uv[2 * w + 1] - bf16_hi(uh[sh][w]));
+          }
         }
-      f32x16 c2[NTB];
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        c2[tb] = f32x16{};
+        for (int tb = 0; tb < NTB; ++tb) {
+          c2[tb] = f32x16{};
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            u32x4 bh, bl;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              float m[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                float xg = acc[0][tb][8 * sh + 2 * w + e], xu = acc[1][tb][8 * sh + 2 * w + e];
+                if (LN) {
+                  xg *= rt[tb];
+                  xu *= rt[tb];
+                }
+                m[e] = xg * fast_rcp(1.f + fast_exp2(-xg * kLog2e)) * xu;
+              }
+              bh[w] = pack_bf16x2(m[0], m[1]);
+              bl[w] = pack_bf16x2(m[0] - bf16_lo(bh[w]), m[1] - bf16_hi(bh[w]));
+            }
+            c2[tb] = mfma32(uh[sh], bh, c2[tb]);
+            c2[tb] = mfma32(uh[sh], bl, c2[tb]);
+            c2[tb] = mfma32(ul[sh], bh, c2[tb]);
+          }
+        }
+      } else {
+        // The head sums are a second matrix product, C2[h][t] = sum_u w2[h][u] SiLU(a[u][t]),
+        // over this wave's 64 units, four 16-unit steps.  The accumulator layout already is
+        // the B operand: in step (ub, s) the lane of token j and half q holds, as element e,
+        // registers 8 s + e of acc[ub][tb], i.e. unit 32 ub + 16 s + 8 (e / 4) + 4 q + e % 4;
+        // the A operand (rows = heads, H <= 16 of 32) takes w2 in that unit order.  SiLU
+        // enters as two bf16 parts (fp32 accumulate).
+        u32x4 a2[GS_UB][2];
 #pragma unroll
         for (int ub = 0; ub < GS_UB; ++ub)
 #pragma unroll
           for (int sh = 0; sh < 2; ++sh) {
-            // SiLU as a bf16 pair hi + lo (|SiLU - hi - lo| <= 2^-17 |SiLU|): two products
-            u32x4 bh, bl;
+            const int u0 = c + wave * 32 * GS_UB + 32 * ub + 16 * sh + 4 * hl;  // units u0 + {0..3}, u0 + 8 + {0..3}
+            const uint16_t *wr = w2 + (int64_t)l32 * d_ff;
+            uint32_t e16[8];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              float x0 = acc[ub][tb][8 * sh + 2 * w], x1 = acc[ub][tb][8 * sh + 2 * w + 1];
-              if (LN) {
-                x0 *= rt[tb];
-                x1 *= rt[tb];
-              }
-              const float s0 = x0 * fast_rcp(1.f + fast_exp2(-x0 * kLog2e));
-              const float s1 = x1 * fast_rcp(1.f + fast_exp2(-x1 * kLog2e));
-              bh[w] = pack_bf16x2(s0, s1);
-              bl[w] = pack_bf16x2(s0 - bf16_lo(bh[w]), s1 - bf16_hi(bh[w]));
+            for (int e = 0; e < 8; ++e) {
+              const int u = u0 + 8 * (e >> 2) + (e & 3);
+              e16[e] = (l32 < H && u < d_ff) ? (uint32_t)wr[u] : 0u;
             }
-            c2[tb] = mfma32(a2[ub][sh], bh, c2[tb]);
-            c2[tb] = mfma32(a2[ub][sh], bl, c2[tb]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) a2[ub][sh][w] = e16[2 * w] | (e16[2 * w + 1] << 16);
           }
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          c2[tb] = f32x16{};
+#pragma unroll
+          for (int ub = 0; ub < GS_UB; ++ub)
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) {
+              // SiLU as a bf16 pair hi + lo (|SiLU - hi - lo| <= 2^-17 |SiLU|): two products
+              u32x4 bh, bl;
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                float x0 = acc[ub][tb][8 * sh + 2 * w], x1 = acc[ub][tb][8 * sh + 2 * w + 1];
+                if (LN) {
+                  x0 *= rt[tb];
+                  x1 *= rt[tb];
+                }
+                const float s0 = x0 * fast_rcp(1.f + fast_exp2(-x0 * kLog2e));
+                const float s1 = x1 * fast_rcp(1.f + fast_exp2(-x1 * kLog2e));
+                bh[w] = pack_bf16x2(s0, s1);
+                bl[w] = pack_bf16x2(s0 - bf16_lo(bh[w]), s1 - bf16_hi(bh[w]));
+              }
+              c2[tb] = mfma32(a2[ub][sh], bh, c2[tb]);
+              c2[tb] = mfma32(a2[ub][sh], bl, c2[tb]);
+            }
+        }
       }
       // Sum over the waves (fixed order) through the hidden ring, free after the loop:
       // red[wave][h][t], registers 0..7 of c2 hold heads 8 (r / 4) + 4 q + r % 4 < 16.
@@ -458,10 +520,118 @@ __global__ __launch_bounds__(256) void gate_score_f32_kernel(
   }
 }
 
-hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s) {
+// The clone scorer's down and head projections folded into one matrix,
+// U[h][k] = sum_o P[h][o] Wd[o][k] (fp32), so that b~^h = sum_k U[h][k] m_k:
+// the same value as P (Wd m) with the two sums taken in the other order.
+// Pass 1, work-group (64 units k, 256 outputs o): P's 256 columns staged in LDS
+// as fp32, each lane one unit, the 4 waves every 4th output, the waves' sums
+// added in a fixed order into part[o block][h][k].  Pass 2: U = the o blocks'
+// partial sums in block order.
+constexpr int GF_O = 256;  // outputs o per fold work-group
+__device__ __forceinline__ float wf(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float wf(float x) { return x; }
+
+template <typename TW>
+__global__ __launch_bounds__(256) void gate_fold_part_kernel(const TW *__restrict__ wd, const TW *__restrict__ wh,
+                                                             int d, int d_i, int H, float *__restrict__ part) {
+  __shared__ float sP[GF_O][GS_HMAX];       // P[h][o0 + j] at [j][h]
+  __shared__ float sAcc[4][GS_HMAX][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = blockIdx.x * 64 + lane, o0 = blockIdx.y * GF_O;
+  const int no = d - o0 < GF_O ? d - o0 : GF_O;
+  for (int i = tid; i < GF_O * GS_HMAX; i += 256) {
+    const int h = i / GF_O, j = i % GF_O;
+    sP[j][h] = (h < H && j < no) ? wf(wh[(int64_t)h * d + o0 + j]) : 0.f;
+  }
+  __syncthreads();
+  float acc[GS_HMAX];
+#pragma unroll
+  for (int h = 0; h < GS_HMAX; ++h) acc[h] = 0.f;
+  if (k < d_i) {
+    const TW *col = wd + (int64_t)o0 * d_i + k;
+#pragma unroll 4
+    for (int j = wave; j < no; j += 4) {
+      const float x = wf(col[(int64_t)j * d_i]);
+#pragma unroll
+      for (int h = 0; h < GS_HMAX; ++h) acc[h] = __builtin_fmaf(sP[j][h], x, acc[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GS_HMAX; ++h) sAcc[wave][h][lane] = acc[h];
+  __syncthreads();
+  if (wave == 0 && k < d_i)
+    for (int h = 0; h < H; ++h)
+      part[((int64_t)blockIdx.y * H + h) * d_i + k] =
+          (sAcc[0][h][lane] + sAcc[1][h][lane]) + (sAcc[2][h][lane] + sAcc[3][h][lane]);
+}
+
+__global__ __launch_bounds__(256) void gate_fold_sum_kernel(const float *__restrict__ part, int nob, int64_t n,
+                                                            float *__restrict__ U) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int ob = 0; ob < nob; ++ob) s += part[ob * n + i];
+  U[i] = s;
+}
+
+// fp32 clone scorer: one work-group per token.  The (normalised) row goes to
+// LDS, then m_k = SiLU(gate_k) up_k for every unit (waves round-robin, lanes
+// split d), then one dot product with U per head.  Fixed-order reductions.
+__global__ __launch_bounds__(256) void gate_clone_f32_kernel(const float *__restrict__ hidden,
+                                                             const float *__restrict__ wg,
+                                                             const float *__restrict__ wu,
+                                                             const float *__restrict__ U, int64_t T, int d, int d_i,
+                                                             const float *__restrict__ ln_w, float ln_eps, bool ln,
+                                                             int H, int64_t Nrow, float *__restrict__ scores) {
+  extern __shared__ float sh[];  // d inputs, then d_i activations
+  __shared__ float sPart[4];
+  __shared__ float sR;
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    sh[i] = hidden[t * d + i];
+    ss += sh[i] * sh[i];
+  }
+  if (ln) {
+    ss = wave_sum(ss);
+    if (lane == 0) sPart[wave] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) sR = 1.f / sqrtf(((sPart[0] + sPart[1]) + (sPart[2] + sPart[3])) / (float)d + ln_eps);
+    __syncthreads();
+    const float r = sR;
+    for (int i = threadIdx.x; i < d; i += 256) sh[i] = sh[i] * r * (ln_w ? ln_w[i] : 1.f);
+  }
+  __syncthreads();
+  float *m = sh + d;
+  for (int k = wave; k < d_i; k += 4) {
+    const float *rg = wg + (int64_t)k * d, *ru = wu + (int64_t)k * d;
+    float g = 0.f, u = 0.f;
+    for (int i = lane; i < d; i += 64) {
+      g += rg[i] * sh[i];
+      u += ru[i] * sh[i];
+    }
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == 0) m[k] = g / (1.f + expf(-g)) * u;
+  }
+  __syncthreads();
+  const int64_t b = t / Nrow, n = t - b * Nrow;
+  for (int h = wave; h < H; h += 4) {
+    float sv = 0.f;
+    for (int k = lane; k < d_i; k += 64) sv += U[(int64_t)h * d_i + k] * m[k];
+    sv = wave_sum(sv);
+    if (lane == 0) scores[(b * H + h) * Nrow + n] = sv;
+  }
+}
+
+hipError_t launch_gate_pack_w1(const void *w1, const void *ln_w, int d, int d_ff, void *packed, hipStream_t s,
+                               const void *w_up) {
   const int nkk = gate_nkk(d);
-  hipLaunchKernelGGL(gate_pack_w1_kernel, dim3((unsigned)((nkk + 7) / 8), (unsigned)gate_ngp(d_ff)), dim3(256), 0, s,
-                     (const uint16_t *)w1, (const uint16_t *)ln_w, d, d_ff, nkk, (uint16_t *)packed);
+  const int ngp = gate_ngp(w_up ? 2 * d_ff : d_ff);
+  hipLaunchKernelGGL(gate_pack_w1_kernel, dim3((unsigned)((nkk + 7) / 8), (unsigned)ngp), dim3(256), 0, s,
+                     (const uint16_t *)w1, (const uint16_t *)w_up, (const uint16_t *)ln_w, d, d_ff, nkk,
+                     (uint16_t *)packed);
   return hipGetLastError();
 }
 
@@ -485,11 +655,61 @@ hipError_t launch_gate_score(const void *hidden, const void *w1, const void *w2,
     const int tt = big ? 128 : 64;
     hipLaunchKernelGGL(k, dim3((unsigned)((T + tt - 1) / tt)), dim3(64 * GS_W), 0, s, (const uint16_t *)hidden,
                        (const uint16_t *)w1, (const uint16_t *)w2, forced, T, d, d_ff, nkk, ln_eps, H, Nrow, scores,
-                       gates);
+                       gates, (const float *)nullptr);
   } else {
     hipLaunchKernelGGL(gate_score_f32_kernel, dim3((unsigned)T), dim3(256), (size_t)(d + d_ff) * sizeof(float), s,
                        (const float *)hidden, (const float *)w1, (const float *)w2, forced, T, d, d_ff,
                        (const float *)ln_w, ln_eps, ln, H, Nrow, scores, gates);
+  }
+  return hipGetLastError();
+}
+
+// The clone scorer (gate/up of d_i units each, down, head projection P [H, d]):
+// bf16: w_gate / w_up packed interleaved into ws, U = P Wd (fp32) after them,
+// then the fold's partial sums; f32: U and the partial sums.  scores [B, H, Nrow].
+// ws: [packed gate/up (bf16 only)] [U: H d_i fp32] [fold partials: ceil(d / 256) H d_i fp32]
+static size_t clone_pack_bytes(int d, int d_i, bool bf16) {
+  return bf16 ? (gate_packed_bytes(d, 2 * d_i) + 255) / 256 * 256 : 0;
+}
+static size_t clone_u_bytes(int d_i, int H) { return ((size_t)H * d_i * sizeof(float) + 255) / 256 * 256; }
+
+size_t gate_clone_ws_bytes(int d, int d_i, int H, bool bf16) {
+  const size_t nob = (size_t)(d + GF_O - 1) / GF_O;
+  return clone_pack_bytes(d, d_i, bf16) + clone_u_bytes(d_i, H) + nob * H * d_i * sizeof(float);
+}
+
+hipError_t launch_gate_clone(const void *hidden, const void *w_gate, const void *w_up, const void *w_down,
+                             const void *w_head, int64_t T, int d, int d_i, int H, bool bf16, bool ln,
+                             const void *ln_w, float ln_eps, float *scores, int64_t Nrow, void *ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  float *U = (float *)((char *)ws + clone_pack_bytes(d, d_i, bf16));
+  float *part = (float *)((char *)U + clone_u_bytes(d_i, H));
+  const int nob = (d + GF_O - 1) / GF_O;
+  const dim3 gf((unsigned)((d_i + 63) / 64), (unsigned)nob);
+  const int64_t nu = (int64_t)H * d_i;
+  if (bf16) {
+    hipError_t e = launch_gate_pack_w1(w_gate, ln ? ln_w : nullptr, d, d_i, ws, s, w_up);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_fold_part_kernel<uint16_t>, gf, dim3(256), 0, s, (const uint16_t *)w_down,
+                       (const uint16_t *)w_head, d, d_i, H, part);
+    hipLaunchKernelGGL(gate_fold_sum_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, s,
+                       (const float *)part, nob, nu, U);
+    const int nkk = gate_nkk(d);
+    const bool big = (T + 127) / 128 >= 256;
+    auto k = big ? (ln ? gate_score_bf16_kernel<4, true, true, true> : gate_score_bf16_kernel<4, false, true, true>)
+                 : (ln ? gate_score_bf16_kernel<2, true, true, true> : gate_score_bf16_kernel<2, false, true, true>);
+    const int tt = big ? 128 : 64;
+    hipLaunchKernelGGL(k, dim3((unsigned)((T + tt - 1) / tt)), dim3(64 * GS_W), 0, s, (const uint16_t *)hidden,
+                       (const uint16_t *)ws, (const uint16_t *)nullptr, (const uint8_t *)nullptr, T, d, 2 * d_i, nkk,
+                       ln_eps, H, Nrow, scores, (float *)nullptr, (const float *)U);
+  } else {
+    hipLaunchKernelGGL(gate_fold_part_kernel<float>, gf, dim3(256), 0, s, (const float *)w_down,
+                       (const float *)w_head, d, d_i, H, part);
+    hipLaunchKernelGGL(gate_fold_sum_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, s,
+                       (const float *)part, nob, nu, U);
+    hipLaunchKernelGGL(gate_clone_f32_kernel, dim3((unsigned)T), dim3(256), (size_t)(d + d_i) * sizeof(float), s,
+                       (const float *)hidden, (const float *)w_gate, (const float *)w_up, (const float *)U, T, d, d_i,
+                       (const float *)ln_w, ln_eps, ln, H, Nrow, scores);
   }
   return hipGetLastError();
 }

@@ -143,6 +143,25 @@ def residual_inputs(w: Workload, N: int | None = None):
     return dict(hidden=_store(h, w.dtype), ln_w=_store(lw, w.dtype))
 
 
+QWEN3_1P7B_MLP = 6144  # the Qwen3-1.7B MLP width (public model config; the pages give no width)
+
+
+def clone_inputs(w: Workload, d_i: int, H: int, N: int | None = None, seed_offset: int = 0):
+    """Weights of the scorer cloned from the gate layer's MLP, for w's hidden states.
+
+    w_gate, w_up ~ N(0, 1/d) [d_i, d]; w_down ~ N(0, 1/d_i) [d, d_i]; w_head ~ N(0, 1/d) [H, d]
+    (all out x in, in w's storage type).  Hidden rows and the RMSNorm weight are gate_inputs' and
+    residual_inputs' (same seed).  Returns dict(w_gate, w_up, w_down, w_head).
+    """
+    rs = _streams(w.seed + 3000 + seed_offset, ["w_gate", "w_up", "w_down", "w_head"])
+    sd, si = np.float32(1.0 / np.sqrt(w.d)), np.float32(1.0 / np.sqrt(d_i))
+    wg = rs["w_gate"].standard_normal((d_i, w.d), dtype=np.float32) * sd
+    wu = rs["w_up"].standard_normal((d_i, w.d), dtype=np.float32) * sd
+    wd = rs["w_down"].standard_normal((w.d, d_i), dtype=np.float32) * si
+    wh = rs["w_head"].standard_normal((H, w.d), dtype=np.float32) * sd
+    return {k: _store(v, w.dtype) for k, v in dict(w_gate=wg, w_up=wu, w_down=wd, w_head=wh).items()}
+
+
 def clustered_scores(w: Workload, N: int | None = None, frac: float = 0.05) -> np.ndarray:
     """float32 [B, N] selection scores with relevant spans.
 

@@ -252,3 +252,33 @@ def test_heads_validation():
               None) == 1  # Hq % Hkv
     assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 16, 8, 128, 1, FAKE, None, None, 0,
               None) == 3  # workspace
+
+
+def test_clone_validation():
+    lib = _lib()
+    i64 = ctypes.c_int64
+    P = ctypes.c_void_p
+    f = lib.tg_gate_score_clone
+    f.argtypes = [P, ctypes.c_int, P, ctypes.c_float, P, P, P, P, i64, i64, i64, i64, i64, ctypes.c_int, P, P,
+                  ctypes.c_size_t, P]
+    ws = lib.tg_gate_score_clone_workspace_size
+    ws.argtypes = [i64, i64, i64, ctypes.c_int]
+    ws.restype = ctypes.c_size_t
+    # workspace: packed gate/up (bf16), then U = [H, d_i] fp32 and the fold's partial sums
+    assert ws(2048, 6144, 16, 1) >= 2 * 6144 * 2048 * 2 + 2 * 16 * 6144 * 4
+    assert 2 * 3 * 100 * 4 <= ws(256, 100, 3, 0) < ws(256, 100, 3, 1)
+    assert ws(256, 100, 17, 1) == 0 and ws(256, 40000, 1, 1) == 0 and ws(0, 64, 1, 1) == 0
+    big = 1 << 34
+    c = lambda *a, **kw: f(kw.get("h", FAKE), kw.get("ln", 0), None, kw.get("eps", 0.0), FAKE, FAKE,
+                           kw.get("wd", FAKE), kw.get("wh", FAKE), *a, kw.get("dt", 1), FAKE, kw.get("ws", FAKE),
+                           kw.get("wsb", big), None)
+    assert c(1, 10, 64, 32, 17) == 2                       # H > 16
+    assert c(1, 10, 64, 32, 0) == 2                        # H < 1
+    assert c(1, 10, 64, 40000, 4) == 2                     # d_i > 32768
+    assert c(1, 10, 48, 32, 4) == 2                        # bf16 needs d % 32 == 0
+    assert c(1, 10, 64, 16000, 4, dt=0) == 2               # f32: d + d_i too large for one row in LDS
+    assert c(1, 10, 64, 32, 4, wd=None) == 1               # w_down missing
+    assert c(1, 10, 64, 32, 4, wh=MIS) == 1                # misaligned
+    assert c(1, 10, 64, 32, 4, ln=1, eps=-1.0) == 1        # ln_eps
+    assert c(1, 10, 64, 32, 4, wsb=16) == 3                # workspace too small
+    assert c(1, 10, 64, 32, 4, ws=None) == 3               # workspace missing
