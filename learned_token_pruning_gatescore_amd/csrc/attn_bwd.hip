@@ -139,6 +139,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       of[ks] = vq ? *(const u32x4 *)(dout + roff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
     }
     const float lrow = vq ? lse[((int64_t)b * Hq + h) * M + qi] : -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      settle(qf[ks]);
+      settle(of[ks]);
+    }
+    settle(lrow);
+    settle(tq);
+    settle(rq);
     if (cs) {
       const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq ? qi : 0)) * HALF);
 #pragma unroll
@@ -303,21 +311,30 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     }
 
     // dq = c t R(-phi) dq^ ; lane holds rows d = 32 db + acc_row(r, hl) of its column
+    // (the angles of all its rows loaded at once, then the products)
     const float cq = TEMP ? c * tq : c;
     if (vq) {
       float *drow = dq + ((bM + qi) * Hq + h) * D;
+      f32x4 ca[NDB / 2][4][2];
+#pragma unroll
+      for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          ca[db][g4][0] = ca[db][g4][1] = f32x4{1.f, 0.f, 1.f, 0.f};
+          if (cs) {
+            const f32x4 *cp = (const f32x4 *)(cs + (bM + qi) * HALF + db * 32 + 8 * g4 + 4 * hl);
+            ca[db][g4][0] = cp[0];
+            ca[db][g4][1] = cp[1];
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hl;
           float xo[4], yo[4];
-          f32x4 t0 = {1.f, 0.f, 1.f, 0.f}, t1 = {1.f, 0.f, 1.f, 0.f};
-          if (cs) {
-            const f32x4 *cp = (const f32x4 *)(cs + (bM + qi) * HALF + d);
-            t0 = cp[0];
-            t1 = cp[1];
-          }
+          const f32x4 t0 = ca[db][g4][0], t1 = ca[db][g4][1];
           const float cv[4] = {t0[0], t0[2], t1[0], t1[2]}, sv[4] = {t0[1], t0[3], t1[1], t1[3]};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -357,8 +374,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
     int Hkv, int G, int nkb, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
-  constexpr int NIW = 2 * T::NI / AB_NW;  // Q and dO direct loads per wave per item
-  constexpr int NVM = NIW + 1 + TEMP;     // + the row-statistics load (+ the temperature load)
+  constexpr int NIW = 2 * T::NI / 4;  // Q and dO direct loads per role-0 wave per item
   constexpr int KB = 4 * AB_T;            // keys per block
   __shared__ __attribute__((aligned(1024))) uint16_t sQ[5 * T::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sO[5 * T::TILE];
@@ -366,7 +382,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(256))) float sT[TEMP ? 5 : 1][64];  // [slot][row] t (rows 32..63: fill)
   __shared__ __attribute__((aligned(1024))) f32x4 sP[2][4][4][64];  // [item parity][wave][r / 4][lane]
   __shared__ __attribute__((aligned(1024))) float sCol[8][KB];
-  __shared__ __attribute__((aligned(256))) float sDummy[64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -387,7 +402,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
   bool iso[NIW];
 #pragma unroll
   for (int n = 0; n < NIW; ++n) {
-    const int j = wave + AB_NW * n;
+    const int j = sub + 4 * n;
     iso[n] = j >= T::NI;
     dgo[n] = T::goff(j % T::NI, lane, rsq);
     dlo[n] = 1024u * (uint32_t)(j % T::NI);
@@ -418,7 +433,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
     const int key = kw0 + l32;
     const bool vk = key < M;
 
-    // item it: head it / ntl of the group, query tile tq0 + it % ntl; ring slot it % 4
+    // item it: head it / ntl of the group, query tile tq0 + it % ntl; ring slot it % 5.
+    // Only the role-0 waves load (role 1, on the critical path, never queues behind
+    // the direct loads): the Q and dO tiles split over the four of them, the row
+    // statistics from wave 0, the temperatures from wave 1.  A load past the end
+    // (an item >= nit) reads zeros, so every item has the same loads per wave.
     auto issue = [&](int it) __attribute__((always_inline)) {
       const bool live = it < nit;
       const int hh = live ? it / ntl : 0;
@@ -433,16 +452,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
       for (int n = 0; n < NIW; ++n)
         dma_b128(iso[n] ? rO : rQ, (iso[n] ? lds_addr(sO) : lds_addr(sQ)) + so + dlo[n],
                  live ? dgo[n] + toff : 0x80000000u, 0u);
-      dma_b32(rR, wave == 0 ? lds_addr(&sRS[it % 5][0]) : lds_addr(sDummy),
-              live && wave == 0 ? (uint32_t)(tq * AB_T * 8 + 4 * lane) : 0x80000000u, 0u);
-      if (TEMP) {
+      if (wave == 0) dma_b32(rR, lds_addr(&sRS[it % 5][0]), live ? (uint32_t)(tq * AB_T * 8 + 4 * lane) : 0x80000000u, 0u);
+      if (TEMP && wave == 1) {
         const i32x4 rT = buffer_rsrc(tau + ((int64_t)b * Hq + h) * Mp, (uint32_t)Mp * 4u);
-        dma_b32(rT, wave == 1 ? lds_addr(&sT[it % 5][0]) : lds_addr(sDummy),
-                live && wave == 1 && lane < AB_T ? (uint32_t)(tq * AB_T * 4 + 4 * lane) : 0x80000000u, 0u);
+        dma_b32(rT, lds_addr(&sT[it % 5][0]), live && lane < AB_T ? (uint32_t)(tq * AB_T * 4 + 4 * lane) : 0x80000000u,
+                0u);
       }
     };
-    issue(0);
-    issue(1);
+    // Barrier of an item: the loads of item it landed (this wave's loads of item
+    // it + 1 may still be in flight).  Role 1 has none of its own.
+    auto sync_item = [&]() __attribute__((always_inline)) {
+      if (role == 1) sync_vm<0>();
+      else if (wave == 0 || (TEMP && wave == 1)) sync_vm<NIW + 1>();
+      else sync_vm<NIW>();
+    };
+    if (role == 0) {
+      issue(0);
+      issue(1);
+    }
 
     const int64_t koff = ((bM + (vk ? key : 0)) * Hkv + kvh) * D;
     // Per head the items of this wave are: tiles before its keys (nothing to
@@ -454,6 +481,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         kf[ks] = vk ? *(const u32x4 *)(kh + koff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) settle(kf[ks]);
       f32x16 aV[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) aV[db] = f32x16{};
@@ -506,25 +535,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
       for (int hh = 0; hh < G; ++hh) {
         const int it0 = hh * ntl;
         blane = vk ? bias[((int64_t)b * Hq + kvh * G + hh) * M + key] : -INFINITY;
+        settle(blane);
         for (int n = 0; n < nskip; ++n) {
-          sync_vm<NVM>();
+          sync_item();
           issue(it0 + n + 2);
         }
         if (nskip < ntl) {
-          sync_vm<NVM>();
+          sync_item();
           issue(it0 + nskip + 2);
           item(it0 + nskip, true);
         }
         for (int n = nskip + 1; n < ntl; ++n) {
-          sync_vm<NVM>();
+          sync_item();
           issue(it0 + n + 2);
           item(it0 + n, false);
         }
       }
-      sync_vm<NVM>();
-      issue(nit + 2);
-      sync_vm<NVM>();
-      issue(nit + 3);
+      // the barriers of role 1's last two iterations
+      sync_vm<0>();
+      sync_vm<0>();
       sync_vm<0>();
       if (vk) {
         float *dvr = dv + koff;
@@ -543,6 +572,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         vf[ks] = vk ? *(const u32x4 *)(v + koff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) settle(vf[ks]);
       f32x16 aK[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) aK[db] = f32x16{};
@@ -580,13 +611,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
 #pragma unroll
           for (int w = 0; w < 4; ++w) dsf[hf][w] = pack_bf16x2(ds[8 * hf + 2 * w], ds[8 * hf + 2 * w + 1]);
       };
-      sync_vm<NVM>();
-      issue(2);
+      sync_item();
       for (int hh = 0; hh < G; ++hh) {
         const int it0 = hh * ntl;
         for (int n = 0; n < ntl; ++n) {
-          sync_vm<NVM>();
-          issue(it0 + n + 3);
+          sync_item();
           if (pit >= 0) trprod(sQ + (pit % 5) * T::TILE, dsf, aK);
           pit = -1;
           if (n >= nskip) {
@@ -598,23 +627,30 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
         if (hl == 0) sCol[hh][AB_T * sub + l32] = tot;
         csum = 0.f;
       }
-      sync_vm<NVM>();
-      issue(nit + 3);
+      sync_item();
       if (pit >= 0) trprod(sQ + (pit % 5) * T::TILE, dsf, aK);
       sync_vm<0>();
       if (vk) {
         float *dkr = dk + koff;
+        f32x4 ca[NDB / 2][4][2];  // the key's angles, all loaded before the products
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            ca[db][g4][0] = ca[db][g4][1] = f32x4{1.f, 0.f, 1.f, 0.f};
+            if (cs) {
+              const f32x4 *cp = (const f32x4 *)(cs + (bM + key) * HALF + db * 32 + 8 * g4 + 4 * hl);
+              ca[db][g4][0] = cp[0];
+              ca[db][g4][1] = cp[1];
+            }
+          }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int d = db * 32 + 8 * g4 + 4 * hl;
-            f32x4 t0 = {1.f, 0.f, 1.f, 0.f}, t1 = {1.f, 0.f, 1.f, 0.f};
-            if (cs) {
-              const f32x4 *cp = (const f32x4 *)(cs + (bM + key) * HALF + d);
-              t0 = cp[0];
-              t1 = cp[1];
-            }
+            const f32x4 t0 = ca[db][g4][0], t1 = ca[db][g4][1];
             const float cv[4] = {t0[0], t0[2], t1[0], t1[2]}, sv[4] = {t0[1], t0[3], t1[1], t1[3]};
             float xo[4], yo[4];
 #pragma unroll

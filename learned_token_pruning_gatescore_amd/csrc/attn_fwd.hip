@@ -346,6 +346,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       const u32x4 x = src[64 * ks];
       qf[ks] = vq ? x : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) settle(qf[ks]);
   }
 
   // Temperature of the column's row (1 without it): x = t (c2 s + bias).  t is
@@ -353,6 +355,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // way).
   float tq = 1.f;
   if (TEMP && vq) tq = fmaxf(softplus_f(sigma[kvh * G + hloc]) * ratio[bM + qi], 1e-30f);
+  settle(tq);
   const float tc2 = c2 * tq;           // logit = tc2 * (S^T entry)
   const float inv_c2 = 1.f / tc2;      // reference -> S units
   const float inv_c2k = 1.f / c2;      // bias -> S units

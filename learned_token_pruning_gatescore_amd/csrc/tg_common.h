@@ -107,6 +107,16 @@ __device__ __forceinline__ void sync_vm() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
+// Consume a loaded value here, so that the compiler waits for its load at
+// this point.  The direct buffer->LDS loads above are inline asm the compiler
+// does not track; a load of its own that it still counts as in flight at a
+// loop header makes it put a full `s_waitcnt vmcnt(0)` inside the loop, which
+// at run time also waits for every direct load in flight (the tile
+// prefetches), once per iteration.  Settling the prologue's loads before the
+// loop keeps that wait out of it.
+__device__ __forceinline__ void settle(const u32x4 &x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
