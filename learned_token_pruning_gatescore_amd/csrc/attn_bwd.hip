@@ -57,12 +57,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     float *__restrict__ tstat) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
-  constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile
-  constexpr int NVM = NIW + 1;            // + the bias load
+  constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile (+ wave 0's bias load)
   __shared__ __attribute__((aligned(1024))) uint16_t sK[4 * T::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[4 * T::TILE];
   __shared__ __attribute__((aligned(1024))) float sBias[4][8][AB_T];
-  __shared__ __attribute__((aligned(1024))) float sDummy[256];  // target of the other waves' bias loads
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,8 +101,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     for (int n = 0; n < NIW; ++n)
       dma_b128(isv[n] ? rV : rK, (isv[n] ? lds_addr(sV) : lds_addr(sK)) + so + dlo[n],
                live ? dgo[n] + toff : 0x80000000u, 0u);
-    dma_b128(rB, wave == 0 ? lds_addr(&sBias[slot(t)][0][0]) : lds_addr(sDummy),
-             live && breal ? bvo + (uint32_t)(t * AB_T * 4) : 0x80000000u, 0u);
+    if (wave == 0)
+      dma_b128(rB, lds_addr(&sBias[slot(t)][0][0]), live && breal ? bvo + (uint32_t)(t * AB_T * 4) : 0x80000000u,
+               0u);
+  };
+  // barrier of tile t: its loads landed (this wave's loads of tile t + 1 may still be in flight)
+  auto sync_tile = [&]() __attribute__((always_inline)) {
+    if (wave == 0) sync_vm<NIW + 1>();
+    else sync_vm<NIW>();
   };
 
   for (int rep = 0; rep < 2; ++rep) {
@@ -232,13 +236,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     {
       f32x16 s, dp;
       for (int t = 0; t < tu; ++t) {
-        sync_vm<NVM>();
+        sync_tile();
         issue(t + 2, nt);
         tile(t, s, dp, kones, false);
         valu_a(t, s, dp, false);
       }
       for (int t = tu; t < nt; ++t) {
-        sync_vm<NVM>();
+        sync_tile();
         issue(t + 2, nt);
         tile(t, s, dp, kones, false);
         valu_a(t, s, dp, true);
@@ -287,14 +291,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       f32x16 s, dp;
       u32x4 dsf[2];
       for (int t = 0; t < tu; ++t) {
-        sync_vm<NVM>();
+        sync_tile();
         issue(t + 2, nt);
         tile(t, s, dp, daug, true);
         valu_b(t, s, dp, false, dsf);
         trprod(sK + slot(t) * T::TILE, dsf, acc);
       }
       for (int t = tu; t < nt; ++t) {
-        sync_vm<NVM>();
+        sync_tile();
         issue(t + 2, nt);
         tile(t, s, dp, daug, true);
         valu_b(t, s, dp, true, dsf);
