@@ -438,13 +438,15 @@ tg_status tg_gate_score_clone(const void *hidden, int ln, const void *ln_w, floa
  *   lse: Hq * T f32, sequence s's [Hq, M_s] block at offset Hq * cu_seqlens[s];
  *   backward: dq [T, Hq, D], dk, dv [T, Hkv, D], dg [T] f32 per token; dgamma
  *     (and dsigma) [Hq] summed over all sequences.
- * Each maximal run of adjacent equal-length sequences (empty ones skipped) is
- * one batched launch, so packing equal lengths next to each other (e.g. all
- * rows of one budget, then all rows of the other) costs one launch per
- * budget; the workspace (tg_gated_attn_varlen_workspace_size, 256-byte
- * aligned) is reused by the runs in stream order.  Validation, dtypes and
- * errors as the batched calls; dgamma / dsigma are summed in run order
- * (deterministic).
+ * Maximal runs of adjacent equal-length sequences (empty ones skipped) are
+ * the unit of work.  The backward's matrix-core kernels take every run in
+ * one launch each: each work-group holds one block of one sequence of one
+ * run, with the blocks of all runs ordered longest first, so sequences of
+ * different lengths share the compute units.  The forward runs one batched
+ * launch per run.  The workspace (tg_gated_attn_varlen_workspace_size,
+ * 256-byte aligned) holds every run's arrays side by side.  Validation,
+ * dtypes and errors as the batched calls; dgamma / dsigma are summed in run
+ * order (deterministic).
  */
 size_t tg_gated_attn_varlen_workspace_size(const int64_t *cu_seqlens, int64_t nseq, int64_t Hq,
                                            int64_t Hkv, int64_t D, int bwd);

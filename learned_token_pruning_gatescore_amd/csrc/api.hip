@@ -148,12 +148,10 @@ tg_status check_gate(const void *hidden, const void *w1, const void *w2, int64_t
 
 // Packed variable-length attention: maximal runs of adjacent sequences of
 // equal length (empty sequences skipped, which keeps a run's tokens
-// contiguous) go to the batched kernels as one call each.
-struct Run {
-  int64_t n, M, off;  // n sequences of M tokens starting at token off
-};
-
-tg_status varlen_runs(const int64_t *cu, int64_t nseq, std::vector<Run> &runs) {
+// contiguous).  The workspace holds every run's arrays side by side, and the
+// per-dgamma-run partial sums after them (backward).
+tg_status varlen_runs(const int64_t *cu, int64_t nseq, int64_t Hq, int64_t Hkv, int64_t D,
+                      std::vector<tg::RunRow> &runs) {
   REQUIRE(cu, TG_ERR_INVALID_ARG, "cu_seqlens (host array of nseq + 1 offsets) is required");
   REQUIRE(nseq >= 0, TG_ERR_INVALID_ARG, "nseq must be >= 0");
   REQUIRE(cu[0] == 0, TG_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
@@ -161,26 +159,26 @@ tg_status varlen_runs(const int64_t *cu, int64_t nseq, std::vector<Run> &runs) {
     REQUIRE(cu[s + 1] >= cu[s], TG_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (at %lld)", (long long)s);
   REQUIRE(cu[nseq] <= kMaxInt, TG_ERR_UNSUPPORTED, "problem too large");
   runs.clear();
+  int64_t padded = 0;
   for (int64_t s = 0; s < nseq; ++s) {
     const int64_t M = cu[s + 1] - cu[s];
     if (M == 0) continue;
+    padded += (M + 31) / 32 * 32;
     if (!runs.empty() && runs.back().M == M) ++runs.back().n;
-    else runs.push_back(Run{1, M, cu[s]});
+    else runs.push_back(tg::RunRow{(int)cu[s], 0, 1, (int)M, 0, 0});
   }
+  REQUIRE(padded <= kMaxInt, TG_ERR_UNSUPPORTED, "problem too large");
+  tg::plan_runs(runs.data(), (int)runs.size(), Hq, Hkv, D);
   return TG_OK;
 }
 
 size_t rup256(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-size_t varlen_ws_bytes(const std::vector<Run> &runs, int64_t Hq, int64_t Hkv, int64_t D, bool bwd, size_t *part_off) {
-  size_t mx = 0;
-  for (const Run &r : runs) {
-    const size_t b = tg::attn_workspace_bytes(r.n, r.M, Hq, Hkv, D, bwd);
-    mx = b > mx ? b : mx;
-  }
-  mx = rup256(mx);
-  if (part_off) *part_off = mx;
-  return mx + (bwd ? rup256(runs.size() * 2 * (size_t)Hq * sizeof(float)) : 0);
+size_t varlen_ws_bytes(const std::vector<tg::RunRow> &runs, int64_t Hq, int64_t Hkv, int64_t D, bool bwd,
+                       size_t *part_off) {
+  const size_t n = rup256(tg::attn_workspace_bytes_runs(runs.data(), (int)runs.size(), Hq, Hkv, D, bwd));
+  if (part_off) *part_off = n;
+  return n + (bwd ? rup256(runs.size() * 2 * (size_t)Hq * sizeof(float)) : 0);
 }
 
 }  // namespace
@@ -517,9 +515,10 @@ static tg_status attn_bwd_impl(bool gph, const void *q, const void *k, const voi
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
-  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, (int)B,
-                                        (int)M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, dq, dk, dv, dg, dgamma,
-                                        dsigma, w, (hipStream_t)stream),
+  const tg::RunRow run{0, 0, (int)B, (int)M, 0, 0};
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, &run, 1,
+                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, dq, dk, dv, dg, dgamma, dsigma,
+                                        nullptr, w, (hipStream_t)stream),
                     "tg_gated_attn_bwd launch");
 }
 
@@ -562,8 +561,8 @@ tg_status tg_gated_attn_bwd_headgates(const void *q, const void *k, const void *
 
 size_t tg_gated_attn_varlen_workspace_size(const int64_t *cu_seqlens, int64_t nseq, int64_t Hq, int64_t Hkv,
                                            int64_t D, int bwd) {
-  std::vector<Run> runs;
-  if (Hq <= 0 || Hkv <= 0 || D <= 0 || varlen_runs(cu_seqlens, nseq, runs) != TG_OK) return 0;
+  std::vector<tg::RunRow> runs;
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || varlen_runs(cu_seqlens, nseq, Hq, Hkv, D, runs) != TG_OK) return 0;
   return varlen_ws_bytes(runs, Hq, Hkv, D, bwd != 0, nullptr);
 }
 
@@ -571,8 +570,9 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
                                    const int32_t *pos, float rope_theta, float tau, const float *sigma,
                                    const int64_t *cu_seqlens, int64_t nseq, int64_t Hq, int64_t Hkv, int64_t D,
                                    tg_dtype dt, void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
-  std::vector<Run> runs;
-  tg_status st = varlen_runs(cu_seqlens, nseq, runs);
+  REQUIRE(Hq > 0 && Hkv > 0 && D > 0, TG_ERR_INVALID_ARG, "Hq, Hkv and D must be > 0");
+  std::vector<tg::RunRow> runs;
+  tg_status st = varlen_runs(cu_seqlens, nseq, Hq, Hkv, D, runs);
   if (st != TG_OK) return st;
   const int64_t T = cu_seqlens[nseq];
   st = check_attn(q, k, v, g, gamma, tau, 1, T, Hq, Hkv, D, dt);
@@ -585,13 +585,15 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const size_t esz = dt == TG_BF16 ? 2 : 4;
-  for (const Run &r : runs) {
-    const tg::AttnWs w = tg::carve_attn_ws(ws, r.n, r.M, Hq, Hkv, D);
+  const tg::AttnWs wall = tg::carve_attn_ws_runs(ws, runs.data(), (int)runs.size(), Hq, Hkv, D);
+  for (const tg::RunRow &r : runs) {
+    const tg::AttnWs w = tg::run_view(wall, r, Hq, Hkv, D);
+    const int64_t off = r.off;
     const hipError_t e = tg::launch_attn_fwd(
-        (const char *)q + r.off * Hq * D * esz, (const char *)k + r.off * Hkv * D * esz,
-        (const char *)v + r.off * Hkv * D * esz, g + r.off, gamma, pos ? pos + r.off : nullptr, (double)rope_theta,
-        tau, sigma, (int)r.n, (int)r.M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, false, (char *)o + r.off * Hq * D * esz,
-        lse ? lse + Hq * r.off : nullptr, w, (hipStream_t)stream);
+        (const char *)q + off * Hq * D * esz, (const char *)k + off * Hkv * D * esz,
+        (const char *)v + off * Hkv * D * esz, g + off, gamma, pos ? pos + off : nullptr, (double)rope_theta, tau,
+        sigma, r.n, r.M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, false, (char *)o + off * Hq * D * esz,
+        lse ? lse + Hq * off : nullptr, w, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "tg_gated_attn_fwd_varlen launch");
   }
   return ok();
@@ -603,8 +605,9 @@ tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, 
                                    int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk, float *dv,
                                    float *dg, float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
                                    void *stream) {
-  std::vector<Run> runs;
-  tg_status st = varlen_runs(cu_seqlens, nseq, runs);
+  REQUIRE(Hq > 0 && Hkv > 0 && D > 0, TG_ERR_INVALID_ARG, "Hq, Hkv and D must be > 0");
+  std::vector<tg::RunRow> runs;
+  tg_status st = varlen_runs(cu_seqlens, nseq, Hq, Hkv, D, runs);
   if (st != TG_OK) return st;
   const int64_t T = cu_seqlens[nseq];
   st = check_attn(q, k, v, g, gamma, tau, 1, T, Hq, Hkv, D, dt);
@@ -620,21 +623,11 @@ tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, 
   const size_t need = varlen_ws_bytes(runs, Hq, Hkv, D, true, &part_off);
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t esz = dt == TG_BF16 ? 2 : 4;
-  float *part = (float *)((char *)ws + part_off);
-  hipStream_t s = (hipStream_t)stream;
-  for (size_t i = 0; i < runs.size(); ++i) {
-    const Run &r = runs[i];
-    const tg::AttnWs w = tg::carve_attn_ws(ws, r.n, r.M, Hq, Hkv, D);
-    const hipError_t e = tg::launch_attn_bwd(
-        (const char *)q + r.off * Hq * D * esz, (const char *)k + r.off * Hkv * D * esz,
-        (const char *)v + r.off * Hkv * D * esz, g + r.off, gamma, pos ? pos + r.off : nullptr, (double)rope_theta,
-        tau, sigma, lse + Hq * r.off, (const char *)dout + r.off * Hq * D * esz, (int)r.n, (int)r.M, (int)Hq,
-        (int)Hkv, (int)D, dt == TG_BF16, false, dq + r.off * Hq * D, dk + r.off * Hkv * D, dv + r.off * Hkv * D,
-        dg + r.off, part + i * 2 * Hq, sigma ? part + i * 2 * Hq + Hq : nullptr, w, s);
-    if (e != hipSuccess) return hip_status(e, "tg_gated_attn_bwd_varlen launch");
-  }
-  return hip_status(tg::launch_sum_runs(part, (int)runs.size(), (int)Hq, dgamma, dsigma, s),
+  const tg::AttnWs w = tg::carve_attn_ws_runs(ws, runs.data(), (int)runs.size(), Hq, Hkv, D);
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout,
+                                        runs.data(), (int)runs.size(), (int)Hq, (int)Hkv, (int)D, dt == TG_BF16,
+                                        false, dq, dk, dv, dg, dgamma, dsigma, (float *)((char *)ws + part_off), w,
+                                        (hipStream_t)stream),
                     "tg_gated_attn_bwd_varlen launch");
 }
 

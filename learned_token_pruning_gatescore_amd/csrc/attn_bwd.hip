@@ -43,18 +43,18 @@ namespace tg {
 // the GQA group (BQ = 256 / G queries x G heads); wave w owns columns
 // 32w .. 32w+31 (one head).  It computes S^T = K Q^T and dP^T = V dO^T (keys
 // on the MFMA rows: 16 keys of one column per lane), P and dS in registers,
-// and dQ^T += K^T dS^T with K^T read through the transposing LDS read.  Each
-// work-group takes query block nqb-1-p and then block p, so every work-group
-// sees about the same number of key tiles.
+// and dQ^T += K^T dS^T with K^T read through the transposing LDS read.  A
+// work-group takes one query block of one run (RunTable): the blocks go out
+// longest first, so the dispatcher balances them over the compute units.
 // ---------------------------------------------------------------------------
 template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, const float2 *__restrict__ cs, const float *__restrict__ lse,
     const uint16_t *__restrict__ dout, float c, float c2, const float *__restrict__ sigma,
-    const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb,
-    float *__restrict__ dq, uint16_t *__restrict__ qhat, float2 *__restrict__ rowstat, float *__restrict__ tau,
-    float *__restrict__ tstat) {
+    const float *__restrict__ ratio, int Hq, int Hkv, int G, int BQ, float *__restrict__ dq,
+    uint16_t *__restrict__ qhat, float2 *__restrict__ rowstat, float *__restrict__ tau, float *__restrict__ tstat,
+    const RunTable rt) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile (+ wave 0's bias load)
@@ -65,8 +65,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int nbh = B * Hkv;
-  const int bh = blockIdx.x % nbh, pr = blockIdx.x / nbh;
+  const Unit u = unit_of(rt, blockIdx.x, Hkv);
+  const int M = rt.run[u.run].M;
+  {  // the run's tensors and workspace
+    const int64_t t0 = rt.run[u.run].off, p0 = rt.run[u.run].poff;
+    q += t0 * Hq * D;
+    kh += t0 * Hkv * D;
+    v += t0 * Hkv * D;
+    bias += t0 * Hq;
+    if (cs) cs += t0 * HALF;
+    lse += t0 * Hq;
+    dout += t0 * Hq * D;
+    if (TEMP) ratio += t0;
+    dq += t0 * Hq * D;
+    qhat += p0 * Hq * D;
+    rowstat += t0 * Hq;
+    tau += p0 * Hq;
+    tstat += t0 * Hq;
+  }
+  const int bh = u.bh;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int64_t bM = (int64_t)b * M;
   const uint32_t rsb = (uint32_t)(Hkv * D * 2);  // bytes between consecutive keys
@@ -111,9 +128,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     else sync_vm<NIW>();
   };
 
-  for (int rep = 0; rep < 2; ++rep) {
-    const int qb = rep == 0 ? nqb - 1 - pr : pr;
-    if (rep == 1 && qb >= nqb - 1 - pr) break;  // the middle block of an odd count runs once
+  {
+    const int qb = u.blk;
     const int q0 = qb * BQ;
     const int qe = q0 + BQ < M ? q0 + BQ : M;
     const int nt = (qe + AB_T - 1) / AB_T;
@@ -367,15 +383,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
 //     dS = P (dP - D) and the column sums; the product dK^T += Q^T dS of an
 //     item runs one iteration later still, first in the iteration, so that
 //     the two waves of a SIMD are not both in their products at once.
-// Items live in a ring of 5 LDS slots (two in flight, three in use).  Each
-// work-group takes key block p and then block nkb-1-p.
+// Items live in a ring of 5 LDS slots (two in flight, three in use).  A
+// work-group takes one key block of one run (RunTable), longest first.
 // ---------------------------------------------------------------------------
 template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
     const uint16_t *__restrict__ qh, const uint16_t *__restrict__ dout, const float2 *__restrict__ rowstat,
     const float *__restrict__ tau, const uint16_t *__restrict__ kh, const uint16_t *__restrict__ v,
-    const float *__restrict__ bias, const float2 *__restrict__ cs, float c, float c2, int B, int M, int Hq,
-    int Hkv, int G, int nkb, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum) {
+    const float *__restrict__ bias, const float2 *__restrict__ cs, float c, float c2, int Hq, int Hkv, int G,
+    int qh_padded, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ colsum, const RunTable rt) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / 4;  // Q and dO direct loads per role-0 wave per item
@@ -391,8 +407,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int role = wave >> 2, sub = wave & 3;
   const int l32 = lane & 31, hl = lane >> 5;
-  const int nbh = B * Hkv;
-  const int bh = blockIdx.x % nbh, pr = blockIdx.x / nbh;
+  const Unit u = unit_of(rt, blockIdx.x, Hkv);
+  const int M = rt.run[u.run].M;
+  {  // the run's tensors and workspace (qh: the rotated queries of the workspace,
+     // placed by padded tokens, or the caller's q)
+    const int64_t t0 = rt.run[u.run].off, p0 = rt.run[u.run].poff;
+    qh += (qh_padded ? p0 : t0) * Hq * D;
+    dout += t0 * Hq * D;
+    rowstat += t0 * Hq;
+    tau += p0 * Hq;
+    kh += t0 * Hkv * D;
+    v += t0 * Hkv * D;
+    bias += t0 * Hq;
+    if (cs) cs += t0 * HALF;
+    dk += t0 * Hkv * D;
+    dv += t0 * Hkv * D;
+    colsum += t0 * Hq;
+  }
+  const int bh = u.bh;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int64_t bM = (int64_t)b * M;
   const uint32_t rsq = (uint32_t)(Hq * D * 2);  // bytes between consecutive queries of one head
@@ -426,9 +458,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_bf16_kernel(
     }
   };
 
-  for (int rep = 0; rep < 2; ++rep) {
-    const int kb = rep == 0 ? pr : nkb - 1 - pr;
-    if (rep == 1 && kb <= pr) break;  // the middle block of an odd count runs once
+  {
+    const int kb = u.blk;
     const int k0 = kb * KB;
     const int tq0 = k0 / AB_T;
     const int ntl = ntq - tq0;  // query tiles per head
@@ -961,55 +992,104 @@ hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, 
 
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
-                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, bool g_per_head,
-                           float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w,
-                           hipStream_t s) {
-  const float2 *cs = pos ? w.cs : nullptr;
+                           const void *dout, const RunRow *runs, int nruns, int Hq, int Hkv, int D, bool bf16,
+                           bool g_per_head, float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma,
+                           float *part, const AttnWs &w, hipStream_t s) {
   const int gph = (int)g_per_head;
-  if ((int64_t)B * M > 0 && (pos || bf16 || sigma)) {
-    hipError_t e =
-        launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, g_per_head, w, s);
+  const int64_t esz = bf16 ? 2 : 4;
+  auto live = [](const RunRow &r) { return (int64_t)r.n * r.M > 0; };
+  // rotated keys, biases, temperature ratios of every run
+  for (int i = 0; i < nruns; ++i) {
+    const RunRow &r = runs[i];
+    if (!live(r) || !(pos || bf16 || sigma)) continue;
+    const int64_t t0 = r.off;
+    const hipError_t e = launch_attn_prep((const char *)k + t0 * Hkv * D * esz, g + (gph ? t0 * Hq : t0), gamma,
+                                          pos ? pos + t0 : nullptr, theta, r.n, r.M, Hq, Hkv, D, bf16, bf16,
+                                          sigma != nullptr, g_per_head, run_view(w, r, Hq, Hkv, D), s);
     if (e != hipSuccess) return e;
   }
   const double cd = 1.0 / (sqrt((double)D) * (double)tau);
   const float c = (float)cd, c2 = (float)(cd * 1.4426950408889634);
-  if ((int64_t)B * M > 0) {
-    if (bf16) {
-      const int G = Hq / Hkv;
-      const int BQ = 256 / G;
-      const int nqb = (M + BQ - 1) / BQ;
-      const int nkb = (M + 127) / 128;
-      const dim3 g1((unsigned)((nqb + 1) / 2 * B * Hkv)), g2((unsigned)((nkb + 1) / 2 * B * Hkv));
-      const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
-      const uint16_t *qh = pos ? w.qhat : (const uint16_t *)q;
-      const bool t = sigma != nullptr;
-      auto k1 = D == 128 ? (t ? attn_bwd_dq_bf16_kernel<128, true> : attn_bwd_dq_bf16_kernel<128, false>)
-                         : (t ? attn_bwd_dq_bf16_kernel<64, true> : attn_bwd_dq_bf16_kernel<64, false>);
-      auto k2 = D == 128 ? (t ? attn_bwd_dkdv_bf16_kernel<128, true> : attn_bwd_dkdv_bf16_kernel<128, false>)
-                         : (t ? attn_bwd_dkdv_bf16_kernel<64, true> : attn_bwd_dkdv_bf16_kernel<64, false>);
-      hipLaunchKernelGGL(k1, g1, dim3(512), 0, s, (const uint16_t *)q, kh, (const uint16_t *)v, w.bias, cs, lse,
-                         (const uint16_t *)dout, c, c2, sigma, w.ratio, B, M, Hq, Hkv, G, BQ, nqb, dq, w.qhat,
-                         w.rowstat, w.tau, w.tstat);
-      hipLaunchKernelGGL(k2, g2, dim3(512), 0, s, qh, (const uint16_t *)dout, w.rowstat, (const float *)w.tau, kh,
-                         (const uint16_t *)v, w.bias, cs, c, c2, B, M, Hq, Hkv, G, nkb, dk, dv, w.colsum);
-    } else {
-      float *delta = (float *)w.rowstat;
-      const int64_t rq = (int64_t)B * M * Hq, rk = (int64_t)B * M * Hkv;
-      hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, dim3((unsigned)((rq + 3) / 4)), dim3(256), 0, s,
-                         (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, c, sigma, w.ratio, B, M, Hq, Hkv, D, gph, dq, delta, w.tstat);
-      hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, dim3((unsigned)((rk + 3) / 4)), dim3(256), 0, s,
-                         (const float *)q, (const float *)k, (const float *)v, g, gamma, cs, lse,
-                         (const float *)dout, delta, c, sigma, w.ratio, B, M, Hq, Hkv, D, gph, dk, dv, w.colsum);
+  if (bf16) {
+    // one launch per kernel over all runs (kMaxRuns at a time): query
+    // blocks cost their key tiles plus about six tiles of fixed work, key
+    // blocks their items plus about two
+    const int G = Hq / Hkv;
+    const int BQ = 256 / G;
+    const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
+    const uint16_t *qh = pos ? w.qhat : (const uint16_t *)q;
+    const bool t = sigma != nullptr;
+    auto k1 = D == 128 ? (t ? attn_bwd_dq_bf16_kernel<128, true> : attn_bwd_dq_bf16_kernel<128, false>)
+                       : (t ? attn_bwd_dq_bf16_kernel<64, true> : attn_bwd_dq_bf16_kernel<64, false>);
+    auto k2 = D == 128 ? (t ? attn_bwd_dkdv_bf16_kernel<128, true> : attn_bwd_dkdv_bf16_kernel<128, false>)
+                       : (t ? attn_bwd_dkdv_bf16_kernel<64, true> : attn_bwd_dkdv_bf16_kernel<64, false>);
+    std::vector<Level> l1, l2;
+    std::vector<RunTable> t1, t2;
+    std::vector<unsigned> g1, g2;
+    for (int r0 = 0; r0 < nruns; r0 += kMaxRuns) {
+      const int nr = nruns - r0 < kMaxRuns ? nruns - r0 : kMaxRuns;
+      const RunRow *rr = runs + r0;
+      l1.clear();
+      l2.clear();
+      for (int i = 0; i < nr; ++i) {
+        if (!live(rr[i])) continue;
+        const int M = rr[i].M, nqb = (M + BQ - 1) / BQ, nkb = (M + 127) / 128, ntq = (M + AB_T - 1) / AB_T;
+        for (int qb = 0; qb < nqb; ++qb) {
+          const int qe = (qb + 1) * BQ < M ? (qb + 1) * BQ : M;
+          l1.push_back(Level{i, qb, (int64_t)((qe + AB_T - 1) / AB_T) + 6});
+        }
+        for (int kb = 0; kb < nkb; ++kb) l2.push_back(Level{i, kb, (int64_t)G * (ntq - 4 * kb) + 2});
+      }
+      if (l1.empty()) continue;
+      make_tables(l1, rr, nr, Hkv, t1, g1);
+      make_tables(l2, rr, nr, Hkv, t2, g2);
+      for (size_t j = 0; j < t1.size(); ++j)
+        hipLaunchKernelGGL(k1, dim3(g1[j]), dim3(512), 0, s, (const uint16_t *)q, kh, (const uint16_t *)v, w.bias,
+                           pos ? w.cs : nullptr, lse, (const uint16_t *)dout, c, c2, sigma, w.ratio, Hq, Hkv, G, BQ,
+                           dq, w.qhat, w.rowstat, w.tau, w.tstat, t1[j]);
+      for (size_t j = 0; j < t2.size(); ++j)
+        hipLaunchKernelGGL(k2, dim3(g2[j]), dim3(512), 0, s, qh, (const uint16_t *)dout, w.rowstat,
+                           (const float *)w.tau, kh, (const uint16_t *)v, w.bias, pos ? w.cs : nullptr, c, c2, Hq,
+                           Hkv, G, pos ? 1 : 0, dk, dv, w.colsum, t2[j]);
     }
-    // the row statistics are dead by now: their space (2 B Hq M floats) takes the
-    // dgamma and dsigma shares (2 B ceil(M / 256) Hq floats)
-    hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((M + 255) / 256), (unsigned)(B < 65535 ? B : 65535)), dim3(256), 0,
-                       s, w.colsum, g, gamma, sigma ? (const float *)w.tstat : nullptr, B, M, Hq, gph, dg,
-                       (float *)w.rowstat);
+  } else {
+    for (int i = 0; i < nruns; ++i) {
+      const RunRow &r = runs[i];
+      if (!live(r)) continue;
+      const AttnWs wv = run_view(w, r, Hq, Hkv, D);
+      const int64_t t0 = r.off;
+      const float *qr = (const float *)q + t0 * Hq * D, *kr = (const float *)k + t0 * Hkv * D,
+                  *vr = (const float *)v + t0 * Hkv * D, *gr = g + (gph ? t0 * Hq : t0), *lr = lse + t0 * Hq,
+                  *dr = (const float *)dout + t0 * Hq * D;
+      float *delta = (float *)wv.rowstat;
+      const float2 *cs = pos ? wv.cs : nullptr;
+      const int64_t rq = (int64_t)r.n * r.M * Hq, rk = (int64_t)r.n * r.M * Hkv;
+      hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, dim3((unsigned)((rq + 3) / 4)), dim3(256), 0, s, qr, kr, vr, gr,
+                         gamma, cs, lr, dr, c, sigma, wv.ratio, r.n, r.M, Hq, Hkv, D, gph, dq + t0 * Hq * D, delta,
+                         wv.tstat);
+      hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, dim3((unsigned)((rk + 3) / 4)), dim3(256), 0, s, qr, kr, vr, gr,
+                         gamma, cs, lr, dr, delta, c, sigma, wv.ratio, r.n, r.M, Hq, Hkv, D, gph, dk + t0 * Hkv * D,
+                         dv + t0 * Hkv * D, wv.colsum);
+    }
   }
-  hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)(sigma ? 2 * Hq : Hq)), dim3(256), 0, s, (const float *)w.rowstat,
-                     (int)((int64_t)B * ((M + 255) / 256)), Hq, sigma, dgamma, dsigma);
+  // dg per token, and per run the dgamma (dsigma) sums; a run's row
+  // statistics are dead by now: their space (2 n Hq M floats) takes its
+  // shares (2 n ceil(M / 256) Hq floats)
+  for (int i = 0; i < nruns; ++i) {
+    const RunRow &r = runs[i];
+    const AttnWs wv = run_view(w, r, Hq, Hkv, D);
+    const int64_t t0 = r.off;
+    if (live(r))
+      hipLaunchKernelGGL(dg_kernel, dim3((unsigned)((r.M + 255) / 256), (unsigned)(r.n < 65535 ? r.n : 65535)),
+                         dim3(256), 0, s, wv.colsum, g + (gph ? t0 * Hq : t0), gamma,
+                         sigma ? (const float *)wv.tstat : nullptr, r.n, r.M, Hq, gph, dg + (gph ? t0 * Hq : t0),
+                         (float *)wv.rowstat);
+    float *dgo = part ? part + (int64_t)i * 2 * Hq : dgamma;
+    float *dso = part ? (sigma ? part + (int64_t)i * 2 * Hq + Hq : nullptr) : dsigma;
+    hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)(sigma ? 2 * Hq : Hq)), dim3(256), 0, s,
+                       (const float *)wv.rowstat, live(r) ? r.n * ((r.M + 255) / 256) : 0, Hq, sigma, dgo, dso);
+  }
+  if (part) return launch_sum_runs(part, nruns, Hq, dgamma, dsigma, s);
   return hipGetLastError();
 }
 

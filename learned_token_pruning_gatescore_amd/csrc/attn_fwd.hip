@@ -29,6 +29,8 @@
 //     S^T products through their extra 16-deep step;
 //   * softmax in fp32 against a fixed per-column reference, P rounded to
 //     bf16 for the MFMA, row sums in fp32.
+#include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "tg_common.h"
@@ -766,43 +768,155 @@ static size_t qhat_bytes(int64_t B, int64_t M, int64_t Hq, int64_t D) {
   return (size_t)(B * Hq * ((M + 31) / 32 * 32) * D) * 2;
 }
 
-size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
-  size_t n = rup((size_t)(B * M * (D / 2)) * sizeof(float2)) + rup((size_t)(B * M * Hkv * D) * 2) +
-             rup((size_t)(B * Hq * M) * sizeof(float)) + rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float)) +
-             rup(cnt_ints(B, M, Hq, Hkv) * sizeof(int)) + rup((size_t)(B * M) * sizeof(float)) +
-             rup(qhat_bytes(B, M, Hq, D));
+// floats of one partial record (8 waves x 64 lanes x NR)
+static int64_t rec_floats(int64_t D) { return 8 * ((D / 32) * 16 + 2) * 64; }
+
+void plan_runs(RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D) {
+  (void)D;
+  int64_t poff = 0, rec = 0, cnt = 0;
+  for (int i = 0; i < nruns; ++i) {
+    RunRow &r = runs[i];
+    r.poff = (int)poff;
+    r.rec0 = (int)rec;
+    r.cnt0 = (int)cnt;
+    const FwdSched f = fwd_sched(r.n, r.M, Hq, Hkv);
+    poff += (int64_t)r.n * ((r.M + 31) / 32 * 32);
+    rec += (int64_t)f.nmulti * r.n * Hkv;
+    cnt += (int64_t)r.n * Hkv * f.nqb;
+  }
+}
+
+namespace {
+struct RunTotals {
+  int64_t T = 0, PT = 0, recs = 0, cnts = 0;
+};
+RunTotals run_totals(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv) {
+  RunTotals t;
+  for (int i = 0; i < nruns; ++i) {
+    const RunRow &r = runs[i];
+    const FwdSched f = fwd_sched(r.n, r.M, Hq, Hkv);
+    t.T += (int64_t)r.n * r.M;
+    t.PT += (int64_t)r.n * ((r.M + 31) / 32 * 32);
+    t.recs += (int64_t)f.nmulti * r.n * Hkv;
+    t.cnts += (int64_t)r.n * Hkv * f.nqb;
+  }
+  return t;
+}
+}  // namespace
+
+size_t attn_workspace_bytes_runs(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
+  const RunTotals t = run_totals(runs, nruns, Hq, Hkv);
+  size_t n = rup((size_t)(t.T * (D / 2)) * sizeof(float2)) + rup((size_t)(t.T * Hkv * D) * 2) +
+             rup((size_t)(Hq * t.T) * sizeof(float)) + rup((size_t)(t.recs * rec_floats(D)) * sizeof(float)) +
+             rup((size_t)t.cnts * sizeof(int)) + rup((size_t)t.T * sizeof(float)) +
+             rup((size_t)(t.PT * Hq * D) * 2);
   if (bwd)
-    n += rup((size_t)(B * Hq * M) * sizeof(float2)) + 2 * rup((size_t)(B * Hq * M) * sizeof(float)) +
-         rup((size_t)(B * Hq * ((M + 31) / 32 * 32)) * sizeof(float));
+    n += rup((size_t)(Hq * t.T) * sizeof(float2)) + 2 * rup((size_t)(Hq * t.T) * sizeof(float)) +
+         rup((size_t)(t.PT * Hq) * sizeof(float));
   return n;
 }
 
-AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
+AttnWs carve_attn_ws_runs(void *ws, const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D) {
+  const RunTotals t = run_totals(runs, nruns, Hq, Hkv);
   AttnWs w;
   char *p = (char *)ws;
   w.cs = (float2 *)p;
-  p += rup((size_t)(B * M * (D / 2)) * sizeof(float2));
+  p += rup((size_t)(t.T * (D / 2)) * sizeof(float2));
   w.khat = (uint16_t *)p;
-  p += rup((size_t)(B * M * Hkv * D) * 2);
+  p += rup((size_t)(t.T * Hkv * D) * 2);
   w.bias = (float *)p;
-  p += rup((size_t)(B * Hq * M) * sizeof(float));
+  p += rup((size_t)(Hq * t.T) * sizeof(float));
   w.part = (float *)p;
-  p += rup(part_floats(B, M, Hq, Hkv, D) * sizeof(float));
+  p += rup((size_t)(t.recs * rec_floats(D)) * sizeof(float));
   w.cnt = (int *)p;
-  w.ncnt = (int)cnt_ints(B, M, Hq, Hkv);
-  p += rup((size_t)w.ncnt * sizeof(int));
+  w.ncnt = (int)t.cnts;
+  p += rup((size_t)t.cnts * sizeof(int));
   w.ratio = (float *)p;
-  p += rup((size_t)(B * M) * sizeof(float));
+  p += rup((size_t)t.T * sizeof(float));
   w.qhat = (uint16_t *)p;
-  p += rup(qhat_bytes(B, M, Hq, D));
+  p += rup((size_t)(t.PT * Hq * D) * 2);
   w.rowstat = (float2 *)p;
-  p += rup((size_t)(B * Hq * M) * sizeof(float2));
+  p += rup((size_t)(Hq * t.T) * sizeof(float2));
   w.colsum = (float *)p;
-  p += rup((size_t)(B * Hq * M) * sizeof(float));
+  p += rup((size_t)(Hq * t.T) * sizeof(float));
   w.tau = (float *)p;
-  p += rup((size_t)(B * Hq * ((M + 31) / 32 * 32)) * sizeof(float));
+  p += rup((size_t)(t.PT * Hq) * sizeof(float));
   w.tstat = (float *)p;
   return w;
+}
+
+AttnWs run_view(const AttnWs &w, const RunRow &r, int64_t Hq, int64_t Hkv, int64_t D) {
+  AttnWs v = w;
+  const int64_t off = r.off, poff = r.poff;
+  v.cs = w.cs + off * (D / 2);
+  v.khat = w.khat + off * Hkv * D;
+  v.bias = w.bias + off * Hq;
+  v.part = w.part + (int64_t)r.rec0 * rec_floats(D);
+  v.cnt = w.cnt + r.cnt0;
+  v.ncnt = (int)cnt_ints(r.n, r.M, Hq, Hkv);
+  v.ratio = w.ratio + off;
+  v.qhat = w.qhat + poff * Hq * D;
+  v.rowstat = w.rowstat + off * Hq;
+  v.colsum = w.colsum + off * Hq;
+  v.tau = w.tau + poff * Hq;
+  v.tstat = w.tstat + off * Hq;
+  return v;
+}
+
+size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
+  const RunRow r{0, 0, (int)B, (int)M, 0, 0};
+  return attn_workspace_bytes_runs(&r, 1, Hq, Hkv, D, bwd);
+}
+
+AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
+  const RunRow r{0, 0, (int)B, (int)M, 0, 0};
+  return carve_attn_ws_runs(ws, &r, 1, Hq, Hkv, D);
+}
+
+void make_tables(std::vector<Level> &lv, const RunRow *runs, int nruns, int Hkv, std::vector<RunTable> &tabs,
+                 std::vector<unsigned> &grids) {
+  std::stable_sort(lv.begin(), lv.end(), [](const Level &a, const Level &b) {
+    return a.cost != b.cost ? a.cost > b.cost : a.run < b.run;
+  });
+  tabs.clear();
+  grids.clear();
+  RunTable t;
+  int ne = 0, cur_run = -1, blk0 = 0, last = 0, len = 0;
+  bool desc = false;
+  unsigned wg = 0;
+  auto flush = [&]() {
+    for (int i = ne; i < kMaxEnt; ++i) {
+      t.start[i] = INT_MAX;
+      t.code[i] = 0;
+    }
+    for (int i = 0; i < kMaxRuns; ++i) t.run[i] = i < nruns ? runs[i] : RunRow{0, 0, 0, 0, 0, 0};
+    tabs.push_back(t);
+    grids.push_back(wg);
+    ne = 0;
+    wg = 0;
+    cur_run = -1;
+  };
+  for (const Level &L : lv) {
+    const unsigned nbh = (unsigned)(runs[L.run].n * Hkv);
+    bool merge = ne > 0 && L.run == cur_run;
+    if (merge) {
+      if (len == 1 && (L.blk == last + 1 || L.blk == last - 1)) desc = L.blk < last;
+      else merge = len > 1 && L.blk == last + (desc ? -1 : 1);
+    }
+    if (!merge) {
+      if (ne == kMaxEnt) flush();
+      t.start[ne++] = (int)wg;
+      cur_run = L.run;
+      blk0 = L.blk;
+      len = 0;
+      desc = false;
+    }
+    last = L.blk;
+    ++len;
+    t.code[ne - 1] = L.run | blk0 << 8 | (desc ? 1 : 0) << 30;
+    wg += nbh;
+  }
+  if (ne) flush();
 }
 
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace tg {
 
 struct AttnWs {
@@ -23,6 +25,68 @@ struct AttnWs {
   float *tstat;      // [B, Hq, M] ratio_i * dL/dtau_ih, reduced into dsigma
 };
 
+// Packed batches.  A run is n sequences of M tokens each, stored one after
+// another from token off of the packed tensors; poff counts the padded tokens
+// before it (each sequence's length rounded up to 32), which place the
+// padded workspace arrays.  rec0 and cnt0 are the run's first partial record
+// and first arrival counter of the forward's split query blocks.
+struct RunRow {
+  int off, poff, n, M, rec0, cnt0;
+};
+constexpr int kMaxRuns = 16;  // runs per launch
+constexpr int kMaxEnt = 64;   // work-group ranges per launch
+
+// Work-group table of one launch over runs.  The launch's work-groups are
+// cut into ranges; range e starts at work-group start[e] (start[0] = 0,
+// INT_MAX past the last range) and holds whole blocks of one run, each block
+// as n Hkv consecutive work-groups (batch row, kv head), the blocks numbered
+// from blk0 upwards or downwards.  code[e] = run | blk0 << 8 | descending << 30.
+struct RunTable {
+  int start[kMaxEnt];
+  int code[kMaxEnt];
+  RunRow run[kMaxRuns];
+};
+
+struct Unit {
+  int run, blk, bh;
+};
+// The run, block and (batch row * Hkv + kv head) of work-group w.
+__host__ __device__ __forceinline__ Unit unit_of(const RunTable &rt, int w, int Hkv) {
+  int e = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxEnt; ++i) e += w >= rt.start[i] ? 1 : 0;
+  const int code = rt.code[e];
+  Unit u;
+  u.run = code & 0xFF;
+  const int nbh = rt.run[u.run].n * Hkv, loc = w - rt.start[e], blk0 = (code >> 8) & 0x3FFFFF;
+  u.bh = loc % nbh;
+  u.blk = (code >> 30) & 1 ? blk0 - loc / nbh : blk0 + loc / nbh;
+  return u;
+}
+
+// One (run, block) group of n Hkv work-groups of equal cost.
+struct Level {
+  int run, blk;
+  int64_t cost;
+};
+// Tables and grids of the launches over runs[0 .. nruns) (nruns <= kMaxRuns):
+// the levels longest first (the dispatcher places work-groups in order on the
+// first free compute unit, so this is a longest-processing-time schedule
+// across the runs), consecutive blocks of one run merged into one range, at
+// most kMaxEnt ranges per launch.
+void make_tables(std::vector<Level> &lv, const RunRow *runs, int nruns, int Hkv, std::vector<RunTable> &tabs,
+                 std::vector<unsigned> &grids);
+
+// Runs of a packed batch and the workspace that holds all of them: the
+// arrays of every run side by side (the layout of one run's workspace with
+// B M tokens replaced by the runs' total, and the padded arrays by the
+// padded total).  run_view gives one run's part of it as a workspace of its
+// own.
+void plan_runs(RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D);
+size_t attn_workspace_bytes_runs(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D, bool bwd);
+AttnWs carve_attn_ws_runs(void *ws, const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D);
+AttnWs run_view(const AttnWs &w, const RunRow &r, int64_t Hq, int64_t Hkv, int64_t D);
+
 // Split schedule of the bf16 forward (query block size, blocks, tiles per
 // piece, pieces, pieces of split blocks).
 struct FwdSched {
@@ -39,11 +103,16 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
                            int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, const AttnWs &w,
                            hipStream_t s);
+// Backward over the runs of a packed batch (one run: an ordinary batch).
+// The tensors are the packed ones; w is the workspace of all runs.  With
+// one run dgamma / dsigma receive the sums; with several, part holds 2 Hq
+// floats per run (its dgamma, then its dsigma shares) and one fixed-order
+// pass sums them into dgamma / dsigma.
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
-                           const void *dout, int B, int M, int Hq, int Hkv, int D, bool bf16, bool g_per_head,
-                           float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, const AttnWs &w,
-                           hipStream_t s);
+                           const void *dout, const RunRow *runs, int nruns, int Hq, int Hkv, int D, bool bf16,
+                           bool g_per_head, float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma,
+                           float *part, const AttnWs &w, hipStream_t s);
 
 hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, float *dsigma, hipStream_t s);
 
