@@ -419,6 +419,7 @@ def run_train(args, tg, wl, dev):
     gamma = torch.from_numpy(a["gamma"]).to(dev)
     pos = torch.from_numpy(a["pos"]).to(dev)
     o = torch.empty_like(q)
+    o_lo = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, M), device=dev)
     dq = torch.empty(q.shape, device=dev)
     dk = torch.empty(k.shape, device=dev)
@@ -430,45 +431,53 @@ def run_train(args, tg, wl, dev):
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, True, dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None, temp=False):
+    def step(ev=None, temp=False, use_o=False):
         sg = dict(sigma=sigma) if temp else {}
         if ev:
             ev[0].record(stream)
-        tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws, **sg)
+        tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws, o_lo=o_lo if use_o else None,
+                             **sg)
         if ev:
             ev[1].record(stream)
         if temp:
             sg["dsigma"] = dsig
+        if use_o:
+            sg.update(o=o, o_lo=o_lo)
         tg.tg_gated_attn_bwd(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, dq, dk, dv, dg, dgam, ws, **sg)
         if ev:
             ev[2].record(stream)
 
     ff = 4.0 * w.B * w.Hq * w.D * M * (M + 1) / 2
     out = dict(workload=w.name, B=w.B, M=M)
-    out["two_budgets_packed"] = run_train_varlen(args, tg, wl, dev, w)
-    for temp in (False, True):
-        for _ in range(3):
-            step(temp=temp)
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.train_steps)]
-        for e in evs:
-            step(e, temp=temp)
-        torch.cuda.synchronize()
-        fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-        bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
-        r = dict(fwd_us=fwd * 1e6, bwd_us=bwd * 1e6, fwd_mfma_frac=ff / fwd / PEAK_BF16,
-                 bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16, tokens_per_s=w.B * M / (fwd + bwd))
-        if temp:
-            out["temperature"] = r
-        else:
-            out.update(r)
+    out["two_budgets_packed"] = run_train_varlen(args, tg, wl, dev, w, False)
+    out["two_budgets_packed_d_from_o"] = run_train_varlen(args, tg, wl, dev, w, True)
+    # without o: the backward forms D_i by its own pass over the keys; with o: the forward also
+    # writes o_lo and the backward takes D_i = dO . (o + o_lo)
+    for use_o in (False, True):
+        for temp in (False, True):
+            for _ in range(3):
+                step(temp=temp, use_o=use_o)
+            torch.cuda.synchronize()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.train_steps)]
+            for e in evs:
+                step(e, temp=temp, use_o=use_o)
+            torch.cuda.synchronize()
+            fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+            bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+            r = dict(fwd_us=fwd * 1e6, bwd_us=bwd * 1e6, fwd_mfma_frac=ff / fwd / PEAK_BF16,
+                     bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16, tokens_per_s=w.B * M / (fwd + bwd))
+            key = ("d_from_o" if use_o else "") + ("_temperature" if use_o and temp else "temperature" if temp else "")
+            if key:
+                out[key] = r
+            else:
+                out.update(r)
     return out
 
 
-def run_train_varlen(args, tg, wl, dev, w):
+def run_train_varlen(args, tg, wl, dev, w, use_o):
     """Both training budgets in one packed call (DeepDive section 3.3): each of the B rows at its
     full budget (M = 2048 kept) and at half of it (1024), packed by budget, forward + backward with
-    the Eq. 7/8 temperature (not part of `value`)."""
+    the Eq. 7/8 temperature (not part of `value`); use_o: the backward's row terms from o + o_lo."""
     import torch
 
     lens = [w.M_fixed] * w.B + [w.M_fixed // 2] * w.B
@@ -486,6 +495,7 @@ def run_train_varlen(args, tg, wl, dev, w):
                            .astype(np.int32)).to(dev)
     sigma = torch.from_numpy((0.54 + 0.5 * rs.standard_normal(w.Hq)).astype(np.float32)).to(dev)
     o = torch.empty_like(q)
+    o_lo = torch.empty_like(q) if use_o else None
     lse = torch.empty(w.Hq * T_, device=dev)
     dq, dk, dv = (torch.empty(x.shape, device=dev) for x in (q, k, v))
     dg = torch.empty(T_, device=dev)
@@ -496,11 +506,12 @@ def run_train_varlen(args, tg, wl, dev, w):
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, cu, o, lse, ws, sigma=sigma)
+        tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, cu, o, lse, ws, sigma=sigma,
+                                    o_lo=o_lo)
         if ev:
             ev[1].record(stream)
         tg.tg_gated_attn_bwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, cu, dq, dk, dv, dg, dgam,
-                                    ws, sigma=sigma, dsigma=dsig)
+                                    ws, sigma=sigma, dsigma=dsig, o=o if use_o else None, o_lo=o_lo)
         if ev:
             ev[2].record(stream)
 

@@ -287,6 +287,9 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  *   g [B, M] f32 > = 0, gamma [Hq] f32, pos [B, M] i32 or NULL
  *   sigma [Hq] f32 or NULL (no temperature: t = 1)
  *   lse [B, Hq, M] f32 out or NULL (needed by the backward)
+ *   o_lo [B, M, Hq, D] bf16 out or NULL (bf16 only): the residual of o's
+ *     rounding, o_lo = bf16(o32 - o) for the fp32 output o32, so that
+ *     o + o_lo is o32 to about 2^-18 relative (for the backward's D_i)
  * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q.k and
  * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
  * bf16 for the P.v product.  f32: D <= 128, plain fp32 arithmetic.
@@ -299,8 +302,8 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g,
                             const float *gamma, const int32_t *pos, float rope_theta,
                             float tau, const float *sigma, int64_t B, int64_t M, int64_t Hq,
-                            int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse, void *ws,
-                            size_t ws_bytes, void *stream);
+                            int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse, void *o_lo,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /*
  * tg_gated_attn_bwd -- gradients of tg_gated_attn_fwd.  The task gradient
@@ -312,8 +315,11 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
  *     dv_j = sum_i P_ij dout_i,            (dk, dv summed over the group)
  *     dg_j = sum_h gamma_h colsum_h(j) / g_j      (0 where g_j = 0)
  *     dgamma_h = sum_b sum_j colsum_h(j) ln g_j,   colsum_h(j) = sum_i dS_ij
- * with c = 1 / (sqrt(D) tau).  D_i is formed from fp32 P and dP, not from
- * the rounded output.  With sigma (the temperature of Eq. 7/8, as in the
+ * with c = 1 / (sqrt(D) tau).  D_i = dout_i . o_i: with o and o_lo (bf16,
+ * both given or both NULL; the forward's o and o_lo of the same inputs) it
+ * is taken as dout_i . (o_i + o_lo_i); without them it is formed from fp32 P
+ * and dP by one more pass over the keys.  The rounded output alone would
+ * not do: its rounding moves dg by more than the bf16 tolerance.  With sigma (the temperature of Eq. 7/8, as in the
  * forward) dS_ij is dL/dS of S = t Z, dL/dZ_ij = t_ih dS_ij takes its place in
  * dq, dk and colsum, and
  *     dsigma_h = sigmoid(sigma_h) sum_b sum_i (ln m_i / ln max(2, p_i)) sum_j dS_ij Z_ij
@@ -325,7 +331,8 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
 tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g,
                             const float *gamma, const int32_t *pos, float rope_theta,
                             float tau, const float *sigma, const float *lse, const void *dout,
-                            int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
+                            const void *o, const void *o_lo, int64_t B, int64_t M, int64_t Hq,
+                            int64_t Hkv, int64_t D,
                             tg_dtype dt, float *dq, float *dk, float *dv, float *dg,
                             float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
                             void *stream);
@@ -378,11 +385,13 @@ tg_status tg_gated_attn_fwd_headgates(const void *q, const void *k, const void *
                                       const float *gamma, const int32_t *pos, float rope_theta,
                                       float tau, const float *sigma, int64_t B, int64_t M,
                                       int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o,
-                                      float *lse, void *ws, size_t ws_bytes, void *stream);
+                                      float *lse, void *o_lo, void *ws, size_t ws_bytes,
+                                      void *stream);
 tg_status tg_gated_attn_bwd_headgates(const void *q, const void *k, const void *v, const float *g,
                                       const float *gamma, const int32_t *pos, float rope_theta,
                                       float tau, const float *sigma, const float *lse,
-                                      const void *dout, int64_t B, int64_t M, int64_t Hq,
+                                      const void *dout, const void *o, const void *o_lo,
+                                      int64_t B, int64_t M, int64_t Hq,
                                       int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk,
                                       float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
                                       size_t ws_bytes, void *stream);
@@ -454,11 +463,13 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
                                    const float *gamma, const int32_t *pos, float rope_theta,
                                    float tau, const float *sigma, const int64_t *cu_seqlens,
                                    int64_t nseq, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
-                                   void *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+                                   void *o, float *lse, void *o_lo, void *ws, size_t ws_bytes,
+                                   void *stream);
 tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, const float *g,
                                    const float *gamma, const int32_t *pos, float rope_theta,
                                    float tau, const float *sigma, const float *lse,
-                                   const void *dout, const int64_t *cu_seqlens, int64_t nseq,
+                                   const void *dout, const void *o, const void *o_lo,
+                                   const int64_t *cu_seqlens, int64_t nseq,
                                    int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq,
                                    float *dk, float *dv, float *dg, float *dgamma, float *dsigma,
                                    void *ws, size_t ws_bytes, void *stream);

@@ -127,17 +127,17 @@ def load():
     lib.tg_gated_attn_varlen_workspace_size.argtypes = [P, i64, i64, i64, i64, c_int]
     lib.tg_gated_attn_fwd_varlen.restype = c_int
     lib.tg_gated_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, f32, f32, P, P, i64, i64, i64, i64, c_int, P, P, P,
-                                             sz, P]
+                                             P, sz, P]
     lib.tg_gated_attn_bwd_varlen.restype = c_int
-    lib.tg_gated_attn_bwd_varlen.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, P, i64, i64, i64, i64, c_int,
-                                             P, P, P, P, P, P, P, sz, P]
+    lib.tg_gated_attn_bwd_varlen.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, P, P, P, i64, i64, i64, i64,
+                                             c_int, P, P, P, P, P, P, P, sz, P]
     lib.tg_gated_attn_workspace_size.restype = sz
     lib.tg_gated_attn_workspace_size.argtypes = [i64, i64, i64, i64, i64, c_int]
     lib.tg_gated_attn_fwd.restype = c_int
-    lib.tg_gated_attn_fwd.argtypes = [P, P, P, P, P, P, f32, f32, P, i64, i64, i64, i64, i64, c_int, P, P, P, sz,
-                                      P]
+    lib.tg_gated_attn_fwd.argtypes = [P, P, P, P, P, P, f32, f32, P, i64, i64, i64, i64, i64, c_int, P, P, P, P,
+                                      sz, P]
     lib.tg_gated_attn_bwd.restype = c_int
-    lib.tg_gated_attn_bwd.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, i64, i64, i64, i64, i64, c_int,
+    lib.tg_gated_attn_bwd.argtypes = [P, P, P, P, P, P, f32, f32, P, P, P, P, P, i64, i64, i64, i64, i64, c_int,
                                       P, P, P, P, P, P, P, sz, P]
     lib.tg_gated_attn_fwd_headgates.restype = c_int
     lib.tg_gated_attn_fwd_headgates.argtypes = lib.tg_gated_attn_fwd.argtypes
@@ -315,31 +315,34 @@ def attn_workspace(B, M, Hq, Hkv, D, bwd, device):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def tg_gated_attn_fwd(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None, *, sigma=None):
+def tg_gated_attn_fwd(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None, *, sigma=None,
+                      o_lo=None):
     """q [B, M, Hq, D], k, v [B, M, Hkv, D] (bf16 or fp32); g f32 [B, M]; gamma f32 [Hq];
     pos i32 [B, M] or None; sigma f32 [Hq] or None (the pruning-ratio temperature);
-    writes o [B, M, Hq, D] and lse f32 [B, Hq, M]."""
-    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma)
+    writes o [B, M, Hq, D], lse f32 [B, Hq, M] and (bf16, if given) o_lo [B, M, Hq, D],
+    the residual of o's rounding."""
+    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma, o_lo)
     B, M, Hq, D = q.shape
     Hkv = k.shape[2]
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos), float(rope_theta),
-                                    float(tau), _ptr(sigma), B, M, Hq, Hkv, D, _dt(q), _ptr(o), _ptr(lse), _ptr(ws),
-                                    ws_bytes, _stream(stream)))
+                                    float(tau), _ptr(sigma), B, M, Hq, Hkv, D, _dt(q), _ptr(o), _ptr(lse),
+                                    _ptr(o_lo), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tg_gated_attn_bwd(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk, dv, dg, dgamma, ws,
-                      stream=None, *, sigma=None, dsigma=None):
+                      stream=None, *, sigma=None, dsigma=None, o=None, o_lo=None):
     """Gradients of tg_gated_attn_fwd; dq, dk, dv, dg, dgamma (and dsigma f32 [Hq], given with
-    sigma) are f32 outputs, fully overwritten."""
-    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma)
+    sigma) are f32 outputs, fully overwritten.  o and o_lo (the forward's, bf16, together)
+    give the row terms D_i without a second pass over the keys."""
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma, o, o_lo)
     B, M, Hq, D = q.shape
     Hkv = k.shape[2]
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos), float(rope_theta),
-                                    float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), B, M, Hq, Hkv, D, _dt(q),
-                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgamma), _ptr(dsigma), _ptr(ws),
-                                    ws_bytes, _stream(stream)))
+                                    float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), _ptr(o), _ptr(o_lo), B, M, Hq,
+                                    Hkv, D, _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgamma),
+                                    _ptr(dsigma), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tg_gate_score_heads(hidden, w1, w2, scores, ws=None, ln_w=None, ln_eps=None, stream=None):
@@ -406,27 +409,28 @@ def tg_gate_softmax_heads(b, kept_idx, g, stream=None):
 
 
 def tg_gated_attn_fwd_headgates(q, k, v, g, gamma, pos, rope_theta, tau, o, lse=None, ws=None, stream=None, *,
-                                sigma=None):
+                                sigma=None, o_lo=None):
     """tg_gated_attn_fwd with per-head gates g [B, Hq, M]."""
-    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma)
+    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma, o_lo)
     B, M, Hq, D = q.shape
     Hkv = k.shape[2]
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_fwd_headgates(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
                                               float(rope_theta), float(tau), _ptr(sigma), B, M, Hq, Hkv, D, _dt(q),
-                                              _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+                                              _ptr(o), _ptr(lse), _ptr(o_lo), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def tg_gated_attn_bwd_headgates(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, dq, dk, dv, dg, dgamma, ws,
-                                stream=None, *, sigma=None, dsigma=None):
+                                stream=None, *, sigma=None, dsigma=None, o=None, o_lo=None):
     """tg_gated_attn_bwd with per-head gates g [B, Hq, M]; dg [B, Hq, M]."""
-    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma)
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma, o, o_lo)
     B, M, Hq, D = q.shape
     Hkv = k.shape[2]
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_bwd_headgates(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
-                                              float(rope_theta), float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), B, M,
-                                              Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                              float(rope_theta), float(tau), _ptr(sigma), _ptr(lse), _ptr(dout),
+                                              _ptr(o), _ptr(o_lo), B, M, Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk),
+                                              _ptr(dv), _ptr(dg),
                                               _ptr(dgamma), _ptr(dsigma), _ptr(ws), ws_bytes, _stream(stream)))
 
 
@@ -455,30 +459,31 @@ def attn_varlen_workspace(cu_seqlens, Hq, Hkv, D, bwd, device):
 
 
 def tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, rope_theta, tau, cu_seqlens, o, lse=None, ws=None,
-                             stream=None, *, sigma=None):
+                             stream=None, *, sigma=None, o_lo=None):
     """Packed sequences: q [T, Hq, D], k, v [T, Hkv, D]; g [T]; pos [T] or None; cu_seqlens host [nseq + 1].
     Writes o [T, Hq, D] and lse (Hq * T, sequence s's [Hq, M_s] block at Hq * cu_seqlens[s])."""
-    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma)
+    _contig(q, k, v, g, gamma, pos, o, lse, ws, sigma, o_lo)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     cu, cp = _cu_host(cu_seqlens)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
                                            float(rope_theta), float(tau), _ptr(sigma), cp, cu.size - 1, Hq, Hkv, D,
-                                           _dt(q), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+                                           _dt(q), _ptr(o), _ptr(lse), _ptr(o_lo), _ptr(ws), ws_bytes,
+                                           _stream(stream)))
 
 
 def tg_gated_attn_bwd_varlen(q, k, v, g, gamma, pos, rope_theta, tau, lse, dout, cu_seqlens, dq, dk, dv, dg, dgamma,
-                             ws, stream=None, *, sigma=None, dsigma=None):
+                             ws, stream=None, *, sigma=None, dsigma=None, o=None, o_lo=None):
     """Gradients of tg_gated_attn_fwd_varlen (per token; dgamma, dsigma summed over the sequences)."""
-    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma)
+    _contig(q, k, v, g, gamma, pos, lse, dout, dq, dk, dv, dg, dgamma, ws, sigma, dsigma, o, o_lo)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     cu, cp = _cu_host(cu_seqlens)
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().tg_gated_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gamma), _ptr(pos),
-                                           float(rope_theta), float(tau), _ptr(sigma), _ptr(lse), _ptr(dout), cp,
-                                           cu.size - 1, Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                           float(rope_theta), float(tau), _ptr(sigma), _ptr(lse), _ptr(dout),
+                                           _ptr(o), _ptr(o_lo), cp, cu.size - 1, Hq, Hkv, D, _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
                                            _ptr(dgamma), _ptr(dsigma), _ptr(ws), ws_bytes, _stream(stream)))
 
 

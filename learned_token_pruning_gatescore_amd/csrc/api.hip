@@ -478,12 +478,14 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
 static tg_status attn_fwd_impl(bool gph, const void *q, const void *k, const void *v, const float *g, const float *gamma,
                             const int32_t *pos, float rope_theta, float tau, const float *sigma, int64_t B,
                             int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse,
-                            void *ws, size_t ws_bytes, void *stream) {
+                            void *o_lo, void *ws, size_t ws_bytes, void *stream) {
   tg_status st = check_attn(q, k, v, g, gamma, tau, B, M, Hq, Hkv, D, dt);
   if (st != TG_OK) return st;
   REQUIRE(o, TG_ERR_INVALID_ARG, "o is required");
   REQUIRE(!sigma || aligned16(sigma), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  REQUIRE(aligned16(o) && aligned16(lse), TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(aligned16(o) && aligned16(lse) && aligned16(o_lo), TG_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  REQUIRE(!o_lo || dt == TG_BF16, TG_ERR_INVALID_ARG, "o_lo exists for bf16 only");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
   const size_t need = tg::attn_workspace_bytes(B, M, Hq, Hkv, D, false);
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
@@ -491,13 +493,15 @@ static tg_status attn_fwd_impl(bool gph, const void *q, const void *k, const voi
   if (B * M == 0) return ok();
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
   return hip_status(tg::launch_attn_fwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, (int)B, (int)M,
-                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, o, lse, w, (hipStream_t)stream),
+                                        (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, o, lse, o_lo, w,
+                                        (hipStream_t)stream),
                     "tg_gated_attn_fwd launch");
 }
 
 static tg_status attn_bwd_impl(bool gph, const void *q, const void *k, const void *v, const float *g, const float *gamma,
                             const int32_t *pos, float rope_theta, float tau, const float *sigma, const float *lse,
-                            const void *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
+                            const void *dout, const void *o, const void *o_lo, int64_t B, int64_t M, int64_t Hq,
+                            int64_t Hkv, int64_t D, tg_dtype dt,
                             float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
                             size_t ws_bytes, void *stream) {
   tg_status st = check_attn(q, k, v, g, gamma, tau, B, M, Hq, Hkv, D, dt);
@@ -508,15 +512,18 @@ static tg_status attn_bwd_impl(bool gph, const void *q, const void *k, const voi
   REQUIRE(!sigma || (aligned16(sigma) && aligned16(dsigma)), TG_ERR_INVALID_ARG,
           "tensor pointers must be 16-byte aligned");
   REQUIRE(aligned16(lse) && aligned16(dout) && aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(dg) &&
-              aligned16(dgamma),
+              aligned16(dgamma) && aligned16(o) && aligned16(o_lo),
           TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(!o == !o_lo, TG_ERR_INVALID_ARG, "o and o_lo go together");
+  REQUIRE(!o || dt == TG_BF16, TG_ERR_INVALID_ARG, "o and o_lo are taken for bf16 only");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
   const size_t need = tg::attn_workspace_bytes(B, M, Hq, Hkv, D, true);
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const tg::AttnWs w = tg::carve_attn_ws(ws, B, M, Hq, Hkv, D);
   const tg::RunRow run{0, 0, (int)B, (int)M, 0, 0};
-  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, &run, 1,
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, o, o_lo,
+                                        &run, 1,
                                         (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, gph, dq, dk, dv, dg, dgamma, dsigma,
                                         nullptr, w, (hipStream_t)stream),
                     "tg_gated_attn_bwd launch");
@@ -527,36 +534,37 @@ extern "C" {
 tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                             const int32_t *pos, float rope_theta, float tau, const float *sigma, int64_t B,
                             int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, void *o, float *lse,
-                            void *ws, size_t ws_bytes, void *stream) {
-  return attn_fwd_impl(false, q, k, v, g, gamma, pos, rope_theta, tau, sigma, B, M, Hq, Hkv, D, dt, o, lse, ws,
-                       ws_bytes, stream);
+                            void *o_lo, void *ws, size_t ws_bytes, void *stream) {
+  return attn_fwd_impl(false, q, k, v, g, gamma, pos, rope_theta, tau, sigma, B, M, Hq, Hkv, D, dt, o, lse, o_lo,
+                       ws, ws_bytes, stream);
 }
 
 tg_status tg_gated_attn_fwd_headgates(const void *q, const void *k, const void *v, const float *g,
                                       const float *gamma, const int32_t *pos, float rope_theta, float tau,
                                       const float *sigma, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
-                                      tg_dtype dt, void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
-  return attn_fwd_impl(true, q, k, v, g, gamma, pos, rope_theta, tau, sigma, B, M, Hq, Hkv, D, dt, o, lse, ws,
-                       ws_bytes, stream);
+                                      tg_dtype dt, void *o, float *lse, void *o_lo, void *ws, size_t ws_bytes,
+                                      void *stream) {
+  return attn_fwd_impl(true, q, k, v, g, gamma, pos, rope_theta, tau, sigma, B, M, Hq, Hkv, D, dt, o, lse, o_lo,
+                       ws, ws_bytes, stream);
 }
 
 tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                             const int32_t *pos, float rope_theta, float tau, const float *sigma, const float *lse,
-                            const void *dout, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt,
-                            float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma, void *ws,
-                            size_t ws_bytes, void *stream) {
-  return attn_bwd_impl(false, q, k, v, g, gamma, pos, rope_theta, tau, sigma, lse, dout, B, M, Hq, Hkv, D, dt, dq,
-                       dk, dv, dg, dgamma, dsigma, ws, ws_bytes, stream);
+                            const void *dout, const void *o, const void *o_lo, int64_t B, int64_t M, int64_t Hq,
+                            int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk, float *dv, float *dg,
+                            float *dgamma, float *dsigma, void *ws, size_t ws_bytes, void *stream) {
+  return attn_bwd_impl(false, q, k, v, g, gamma, pos, rope_theta, tau, sigma, lse, dout, o, o_lo, B, M, Hq, Hkv, D,
+                       dt, dq, dk, dv, dg, dgamma, dsigma, ws, ws_bytes, stream);
 }
 
 tg_status tg_gated_attn_bwd_headgates(const void *q, const void *k, const void *v, const float *g,
                                       const float *gamma, const int32_t *pos, float rope_theta, float tau,
-                                      const float *sigma, const float *lse, const void *dout, int64_t B, int64_t M,
-                                      int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk,
-                                      float *dv, float *dg, float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
-                                      void *stream) {
-  return attn_bwd_impl(true, q, k, v, g, gamma, pos, rope_theta, tau, sigma, lse, dout, B, M, Hq, Hkv, D, dt, dq,
-                       dk, dv, dg, dgamma, dsigma, ws, ws_bytes, stream);
+                                      const float *sigma, const float *lse, const void *dout, const void *o,
+                                      const void *o_lo, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D,
+                                      tg_dtype dt, float *dq, float *dk, float *dv, float *dg, float *dgamma,
+                                      float *dsigma, void *ws, size_t ws_bytes, void *stream) {
+  return attn_bwd_impl(true, q, k, v, g, gamma, pos, rope_theta, tau, sigma, lse, dout, o, o_lo, B, M, Hq, Hkv, D,
+                       dt, dq, dk, dv, dg, dgamma, dsigma, ws, ws_bytes, stream);
 }
 
 size_t tg_gated_attn_varlen_workspace_size(const int64_t *cu_seqlens, int64_t nseq, int64_t Hq, int64_t Hkv,
@@ -569,7 +577,8 @@ size_t tg_gated_attn_varlen_workspace_size(const int64_t *cu_seqlens, int64_t ns
 tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                                    const int32_t *pos, float rope_theta, float tau, const float *sigma,
                                    const int64_t *cu_seqlens, int64_t nseq, int64_t Hq, int64_t Hkv, int64_t D,
-                                   tg_dtype dt, void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+                                   tg_dtype dt, void *o, float *lse, void *o_lo, void *ws, size_t ws_bytes,
+                                   void *stream) {
   REQUIRE(Hq > 0 && Hkv > 0 && D > 0, TG_ERR_INVALID_ARG, "Hq, Hkv and D must be > 0");
   std::vector<tg::RunRow> runs;
   tg_status st = varlen_runs(cu_seqlens, nseq, Hq, Hkv, D, runs);
@@ -578,8 +587,9 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
   st = check_attn(q, k, v, g, gamma, tau, 1, T, Hq, Hkv, D, dt);
   if (st != TG_OK) return st;
   REQUIRE(o, TG_ERR_INVALID_ARG, "o is required");
-  REQUIRE(aligned16(o) && aligned16(lse) && aligned16(sigma), TG_ERR_INVALID_ARG,
+  REQUIRE(aligned16(o) && aligned16(lse) && aligned16(sigma) && aligned16(o_lo), TG_ERR_INVALID_ARG,
           "tensor pointers must be 16-byte aligned");
+  REQUIRE(!o_lo || dt == TG_BF16, TG_ERR_INVALID_ARG, "o_lo exists for bf16 only");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
   const size_t need = varlen_ws_bytes(runs, Hq, Hkv, D, false, nullptr);
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
@@ -593,7 +603,7 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
         (const char *)q + off * Hq * D * esz, (const char *)k + off * Hkv * D * esz,
         (const char *)v + off * Hkv * D * esz, g + off, gamma, pos ? pos + off : nullptr, (double)rope_theta, tau,
         sigma, r.n, r.M, (int)Hq, (int)Hkv, (int)D, dt == TG_BF16, false, (char *)o + off * Hq * D * esz,
-        lse ? lse + Hq * off : nullptr, w, (hipStream_t)stream);
+        lse ? lse + Hq * off : nullptr, o_lo ? (char *)o_lo + off * Hq * D * esz : nullptr, w, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "tg_gated_attn_fwd_varlen launch");
   }
   return ok();
@@ -601,10 +611,10 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
 
 tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                                    const int32_t *pos, float rope_theta, float tau, const float *sigma,
-                                   const float *lse, const void *dout, const int64_t *cu_seqlens, int64_t nseq,
-                                   int64_t Hq, int64_t Hkv, int64_t D, tg_dtype dt, float *dq, float *dk, float *dv,
-                                   float *dg, float *dgamma, float *dsigma, void *ws, size_t ws_bytes,
-                                   void *stream) {
+                                   const float *lse, const void *dout, const void *o, const void *o_lo,
+                                   const int64_t *cu_seqlens, int64_t nseq, int64_t Hq, int64_t Hkv, int64_t D,
+                                   tg_dtype dt, float *dq, float *dk, float *dv, float *dg, float *dgamma,
+                                   float *dsigma, void *ws, size_t ws_bytes, void *stream) {
   REQUIRE(Hq > 0 && Hkv > 0 && D > 0, TG_ERR_INVALID_ARG, "Hq, Hkv and D must be > 0");
   std::vector<tg::RunRow> runs;
   tg_status st = varlen_runs(cu_seqlens, nseq, Hq, Hkv, D, runs);
@@ -616,15 +626,17 @@ tg_status tg_gated_attn_bwd_varlen(const void *q, const void *k, const void *v, 
           "lse, dout, dq, dk, dv, dg and dgamma are required");
   REQUIRE(!sigma == !dsigma, TG_ERR_INVALID_ARG, "sigma and dsigma go together");
   REQUIRE(aligned16(lse) && aligned16(dout) && aligned16(dq) && aligned16(dk) && aligned16(dv) && aligned16(dg) &&
-              aligned16(dgamma) && aligned16(sigma) && aligned16(dsigma),
+              aligned16(dgamma) && aligned16(sigma) && aligned16(dsigma) && aligned16(o) && aligned16(o_lo),
           TG_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(!o == !o_lo, TG_ERR_INVALID_ARG, "o and o_lo go together");
+  REQUIRE(!o || dt == TG_BF16, TG_ERR_INVALID_ARG, "o and o_lo are taken for bf16 only");
   if (pos) REQUIRE(std::isfinite(rope_theta) && rope_theta > 1.f, TG_ERR_INVALID_ARG, "rope_theta must be > 1");
   size_t part_off = 0;
   const size_t need = varlen_ws_bytes(runs, Hq, Hkv, D, true, &part_off);
   REQUIRE(ws && ws_bytes >= need, TG_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const tg::AttnWs w = tg::carve_attn_ws_runs(ws, runs.data(), (int)runs.size(), Hq, Hkv, D);
-  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout,
+  return hip_status(tg::launch_attn_bwd(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, lse, dout, o, o_lo,
                                         runs.data(), (int)runs.size(), (int)Hq, (int)Hkv, (int)D, dt == TG_BF16,
                                         false, dq, dk, dv, dg, dgamma, dsigma, (float *)((char *)ws + part_off), w,
                                         (hipStream_t)stream),

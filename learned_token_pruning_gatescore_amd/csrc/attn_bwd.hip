@@ -54,7 +54,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     const uint16_t *__restrict__ dout, float c, float c2, const float *__restrict__ sigma,
     const float *__restrict__ ratio, int Hq, int Hkv, int G, int BQ, float *__restrict__ dq,
     uint16_t *__restrict__ qhat, float2 *__restrict__ rowstat, float *__restrict__ tau, float *__restrict__ tstat,
-    const RunTable rt) {
+    const uint16_t *__restrict__ o, const uint16_t *__restrict__ o_lo, const RunTable rt) {
   using T = BTile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, HALF = D / 2;
   constexpr int NIW = 2 * T::NI / AB_NW;  // K and V direct loads per wave per tile (+ wave 0's bias load)
@@ -76,6 +76,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     if (cs) cs += t0 * HALF;
     lse += t0 * Hq;
     dout += t0 * Hq * D;
+    if (o) {
+      o += t0 * Hq * D;
+      o_lo += t0 * Hq * D;
+    }
     if (TEMP) ratio += t0;
     dq += t0 * Hq * D;
     qhat += p0 * Hq * D;
@@ -159,6 +163,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       of[ks] = vq ? *(const u32x4 *)(dout + roff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
     }
     const float lrow = vq ? lse[((int64_t)b * Hq + h) * M + qi] : -INFINITY;
+    // With the forward's output o and its rounding residual o_lo: D_i = dO_i . O_i
+    // (O_i = sum_j P_ij V_j, so this is sum_j P_ij dP_ij without the pass over the keys)
+    float dso = 0.f;
+    if (o) {
+      if (vq) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const u32x4 hi = *(const u32x4 *)(o + roff + 16 * ks + 8 * hl);
+          const u32x4 lo = *(const u32x4 *)(o_lo + roff + 16 * ks + 8 * hl);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            dso += bf16_lo(of[ks][w]) * (bf16_lo(hi[w]) + bf16_lo(lo[w])) +
+                   bf16_hi(of[ks][w]) * (bf16_hi(hi[w]) + bf16_hi(lo[w]));
+        }
+      }
+      dso += __shfl_xor(dso, 32);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       settle(qf[ks]);
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       sdp(sK + slot(t) * T::TILE, sV + slot(t) * T::TILE, s, dp);
     };
 
-    // pass A: D_i = sum_j P_ij dP_ij
+    // pass A (without o): D_i = sum_j P_ij dP_ij
     float dsa[4] = {0.f, 0.f, 0.f, 0.f};
     auto valu_a = [&](int t, const f32x16 &s, const f32x16 &dp, bool masked) __attribute__((always_inline)) {
       const float *bi = &sBias[slot(t)][hloc][4 * hl];
@@ -249,7 +270,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
         }
       }
     };
-    {
+    float dsum = dso;
+    if (!o) {
       f32x16 s, dp;
       for (int t = 0; t < tu; ++t) {
         sync_tile();
@@ -263,16 +285,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
         tile(t, s, dp, kones, false);
         valu_a(t, s, dp, true);
       }
+      sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
+      dsum = (dsa[0] + dsa[1]) + (dsa[2] + dsa[3]);
+      dsum += __shfl_xor(dsum, 32);
+      // pass B's first tiles (with o, the ones issued above serve it)
+      issue(0, nt);
+      issue(1, nt);
     }
-    sync_vm<0>();  // the tail's zero-fill loads landed, every wave done with the ring
-    float dsum = (dsa[0] + dsa[1]) + (dsa[2] + dsa[3]);
-    dsum += __shfl_xor(dsum, 32);
     if (vq && hl == 0) rowstat[((int64_t)b * Hq + h) * M + qi] = make_float2(la, dsum);
     const u32x4 daug = aug3(-dsum, hl);
 
     // pass B: dS and dQ^T
-    issue(0, nt);
-    issue(1, nt);
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -992,9 +1015,9 @@ hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, 
 
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
-                           const void *dout, const RunRow *runs, int nruns, int Hq, int Hkv, int D, bool bf16,
-                           bool g_per_head, float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma,
-                           float *part, const AttnWs &w, hipStream_t s) {
+                           const void *dout, const void *o, const void *o_lo, const RunRow *runs, int nruns, int Hq,
+                           int Hkv, int D, bool bf16, bool g_per_head, float *dq, float *dk, float *dv, float *dg,
+                           float *dgamma, float *dsigma, float *part, const AttnWs &w, hipStream_t s) {
   const int gph = (int)g_per_head;
   const int64_t esz = bf16 ? 2 : 4;
   auto live = [](const RunRow &r) { return (int64_t)r.n * r.M > 0; };
@@ -1046,7 +1069,8 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
       for (size_t j = 0; j < t1.size(); ++j)
         hipLaunchKernelGGL(k1, dim3(g1[j]), dim3(512), 0, s, (const uint16_t *)q, kh, (const uint16_t *)v, w.bias,
                            pos ? w.cs : nullptr, lse, (const uint16_t *)dout, c, c2, sigma, w.ratio, Hq, Hkv, G, BQ,
-                           dq, w.qhat, w.rowstat, w.tau, w.tstat, t1[j]);
+                           dq, w.qhat, w.rowstat, w.tau, w.tstat, (const uint16_t *)o, (const uint16_t *)o_lo,
+                           t1[j]);
       for (size_t j = 0; j < t2.size(); ++j)
         hipLaunchKernelGGL(k2, dim3(g2[j]), dim3(512), 0, s, qh, (const uint16_t *)dout, w.rowstat,
                            (const float *)w.tau, kh, (const uint16_t *)v, w.bias, pos ? w.cs : nullptr, c, c2, Hq,

@@ -221,12 +221,17 @@ __device__ __forceinline__ u32x4 aug_query(float x, int hl) {
   return hl == 0 ? u32x4{h | (m << 16), l | (0x3F80u << 16), 0x3F803F80u, 0u} : u32x4{0u, 0u, 0u, 0u};
 }
 
-template <int D, bool TEMP>
+// PLO: P enters the P.V product as two bf16 parts (P_hi + P_lo, one product
+// each), so the fp32 output is exact to about 2^-17 instead of carrying P's
+// bf16 rounding; used when the caller asks for o_lo (the backward's row terms
+// D_i = dO . o need that precision).
+template <int D, bool TEMP, bool PLO>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ qfr, int nq32, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, float c2, const float *__restrict__ sigma,
     const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb, int C,
-    float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o, float *__restrict__ lse) {
+    float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o, float *__restrict__ lse,
+    uint16_t *__restrict__ o_lo) {
   using T = BTile<D>;
   using F = FwdCfg<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB;
@@ -398,8 +403,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     return qi >= j0 ? tc2 * (s0[0] + brow[j0] * inv_c2k) : -INFINITY;
   };
   // softmax of 2 of the 16 logits per lane (registers 2c, 2c+1) of a tile
-  auto soft2 = [&](const f32x16 &s, int c, float msub, bool masked, int lim, float &ps, u32x4(&pf)[2])
-      __attribute__((always_inline)) {
+  auto soft2 = [&](const f32x16 &s, int c, float msub, bool masked, int lim, float &ps, u32x4(&pf)[2],
+                   u32x4(&pfl)[2]) __attribute__((always_inline)) {
     float x0 = __builtin_fmaf(s[2 * c], tc2, -msub), x1 = __builtin_fmaf(s[2 * c + 1], tc2, -msub);
     if (masked) {
       if (acc_row(2 * c, hl) > lim) x0 = -INFINITY;
@@ -412,6 +417,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     // written (between the products it overlaps) instead of sunk to its uses
     asm volatile("" : "+v"(ps) : "v"(pk));
     pf[c >> 2][c & 3] = pk;
+    if (PLO) pfl[c >> 2][c & 3] = pack_bf16x2(p0 - bf16_lo(pk), p1 - bf16_hi(pk));
   };
   // One step of the software pipeline: wait for tile t+1;
   // S^T of tile t+1 on the matrix cores while the first half of the softmax
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const int lim = qi - (kt0 + t) * AF_TK;  // keys (within the tile) past the query are masked
     f32x16 sn = f32x16{};
     float ps = 0.f;
-    u32x4 pf[2];
+    u32x4 pf[2], pfl[2];
     {
       u32x4 f[NKS];
 #pragma unroll
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
         sn = mfma32(f[ks], qf[ks], sn);
 #pragma unroll
         for (int c = 0; c < 4; ++c)  // chunk c after the last product of its quarter of the k-steps
-          if ((c + 1) * NKS / 4 - 1 == ks) soft2(sc, c, msub, masked, lim, ps, pf);
+          if ((c + 1) * NKS / 4 - 1 == ks) soft2(sc, c, msub, masked, lim, ps, pf, pfl);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -456,9 +462,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
         if (i + 3 < 2 * NDB) f[i + 3] = fr.tr(V, (i + 3) / NDB, (i + 3) % NDB);
         __builtin_amdgcn_sched_barrier(0);
         acc[i % NDB] = mfma32(f[i], pf[i / NDB], acc[i % NDB]);
+        if (PLO) acc[i % NDB] = mfma32(f[i], pfl[i / NDB], acc[i % NDB]);
 #pragma unroll
         for (int c = 0; c < 4; ++c)  // chunks 4..7 spread over the products of the first 16 keys
-          if (i < NDB && c * NDB / 4 == i) soft2(sc, 4 + c, msub, masked, lim, ps, pf);
+          if (i < NDB && c * NDB / 4 == i) soft2(sc, 4 + c, msub, masked, lim, ps, pf, pfl);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -607,26 +614,37 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // wave w stages its 32 columns x D as rows of D bf16 (16-byte pieces
   // XOR-swizzled by the column), then writes each column's row of o as D/8
   // contiguous 16-byte pieces.
+  // With o_lo, the same tile again as the residual of the bf16 rounding
+  // (o + o_lo is the fp32 output to about 2^-18 relative).
   constexpr int CPR = D / 8;  // 16-byte pieces per row
   __syncthreads();            // every wave is done with the ring
   uint8_t *stg = (uint8_t *)(wave < 4 ? sK : sV) + (wave & 3) * (AF_TK * D * 2);
+  const int qcol0 = q0 + (AF_TK * wave) % BQ;  // query of column 0 of this wave
+  auto emit = [&](uint16_t *dst, bool lo) __attribute__((always_inline)) {
+    auto pk = [&](float a, float c) __attribute__((always_inline)) {
+      const uint32_t h = pack_bf16x2(a, c);
+      return lo ? pack_bf16x2(a - bf16_lo(h), c - bf16_hi(h)) : h;
+    };
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int pc = (4 * db + g4) ^ (l32 & (CPR - 1));  // piece of elements 32 db + 8 g4 ..
-      *(u32x2 *)(stg + l32 * (2 * D) + pc * 16 + 8 * hl) =
-          u32x2{pack_bf16x2(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv),
-                pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int pc = (4 * db + g4) ^ (l32 & (CPR - 1));  // piece of elements 32 db + 8 g4 ..
+        *(u32x2 *)(stg + l32 * (2 * D) + pc * 16 + 8 * hl) =
+            u32x2{pk(acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv),
+                  pk(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back only what it wrote
+#pragma unroll
+    for (int it = 0; it < AF_TK * CPR / 64; ++it) {
+      const int c = lane + 64 * it, col = c / CPR, ch = c % CPR;
+      const u32x4 x = *(const u32x4 *)(stg + col * (2 * D) + ((ch ^ (col & (CPR - 1))) * 16));
+      if (qcol0 + col < M) *(u32x4 *)(dst + ((bM + qcol0 + col) * Hq + hq) * D + 8 * ch) = x;
     }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back only what it wrote
-  const int qcol0 = q0 + (AF_TK * wave) % BQ;           // query of column 0 of this wave
-#pragma unroll
-  for (int it = 0; it < AF_TK * CPR / 64; ++it) {
-    const int c = lane + 64 * it, col = c / CPR, ch = c % CPR;
-    const u32x4 x = *(const u32x4 *)(stg + col * (2 * D) + ((ch ^ (col & (CPR - 1))) * 16));
-    if (qcol0 + col < M) *(u32x4 *)(o + ((bM + qcol0 + col) * Hq + hq) * D + 8 * ch) = x;
-  }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads done before the area is written again
+  };
+  emit(o, false);
+  if (o_lo) emit(o_lo, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -937,8 +955,8 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
 
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
-                           int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, const AttnWs &w,
-                           hipStream_t s) {
+                           int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, void *o_lo,
+                           const AttnWs &w, hipStream_t s) {
   if ((int64_t)B * M == 0) return hipSuccess;
   hipError_t e = launch_attn_prep(k, g, gamma, pos, theta, B, M, Hq, Hkv, D, bf16, bf16, sigma != nullptr, g_per_head,
                                   w, s, bf16 ? q : nullptr);
@@ -950,11 +968,16 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const dim3 grid((unsigned)(f.npieces * B * Hkv));
     const float c2 = (float)(c * 1.4426950408889634);
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
-    auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>)
-                         : (sigma ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>);
+    auto kern = o_lo ? (D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true, true>
+                                          : attn_fwd_bf16_kernel<128, false, true>)
+                                 : (sigma ? attn_fwd_bf16_kernel<64, true, true> : attn_fwd_bf16_kernel<64, false, true>))
+                     : (D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true, false>
+                                          : attn_fwd_bf16_kernel<128, false, false>)
+                                 : (sigma ? attn_fwd_bf16_kernel<64, true, false>
+                                          : attn_fwd_bf16_kernel<64, false, false>));
     hipLaunchKernelGGL(kern, grid, dim3(512), 0, s, (const uint16_t *)w.qhat, (M + 31) / 32, kh, (const uint16_t *)v,
                        w.bias, c2, sigma, w.ratio, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part, w.cnt,
-                       (uint16_t *)o, lse);
+                       (uint16_t *)o, lse, (uint16_t *)o_lo);
   } else {
     const int64_t rows = (int64_t)B * M * Hq;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const float *)q,

@@ -101,18 +101,19 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
                             bool g_per_head, const AttnWs &w, hipStream_t s, const void *q = nullptr);
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
-                           int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, const AttnWs &w,
-                           hipStream_t s);
+                           int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, void *o_lo,
+                           const AttnWs &w, hipStream_t s);
 // Backward over the runs of a packed batch (one run: an ordinary batch).
-// The tensors are the packed ones; w is the workspace of all runs.  With
+// The tensors are the packed ones; w is the workspace of all runs.  With o
+// and o_lo (bf16) the row terms D_i come from dO . (o + o_lo).  With
 // one run dgamma / dsigma receive the sums; with several, part holds 2 Hq
 // floats per run (its dgamma, then its dsigma shares) and one fixed-order
 // pass sums them into dgamma / dsigma.
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                            const int32_t *pos, double theta, float tau, const float *sigma, const float *lse,
-                           const void *dout, const RunRow *runs, int nruns, int Hq, int Hkv, int D, bool bf16,
-                           bool g_per_head, float *dq, float *dk, float *dv, float *dg, float *dgamma, float *dsigma,
-                           float *part, const AttnWs &w, hipStream_t s);
+                           const void *dout, const void *o, const void *o_lo, const RunRow *runs, int nruns, int Hq,
+                           int Hkv, int D, bool bf16, bool g_per_head, float *dq, float *dk, float *dv, float *dg,
+                           float *dgamma, float *dsigma, float *part, const AttnWs &w, hipStream_t s);
 
 hipError_t launch_sum_runs(const float *part, int nruns, int Hq, float *dgamma, float *dsigma, hipStream_t s);
 

@@ -110,7 +110,8 @@ def test_attn_validation():
     f = lib.tg_gated_attn_fwd
     args = lambda **kw: [kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("pos", None), 1e6, kw.get("tau", 1.0),
                          kw.get("sigma", None), 1, 100, kw.get("Hq", 16), kw.get("Hkv", 8), kw.get("D", 128),
-                         kw.get("dt", 1), FAKE, None, kw.get("ws", None), kw.get("wsb", 0), None]
+                         kw.get("dt", 1), FAKE, None, kw.get("o_lo", None), kw.get("ws", None), kw.get("wsb", 0),
+                         None]
     assert f(*args(q=None)) == 1
     assert f(*args(Hq=12, Hkv=8)) == 1          # Hq % Hkv
     assert f(*args(D=96)) == 2                  # bf16 D
@@ -123,24 +124,30 @@ def test_attn_validation():
     assert f(*args(pos=FAKE, ws=FAKE, wsb=need - 1)) == 3
     assert f(*args(q=MIS)) == 1
     assert f(*args(sigma=MIS)) == 1             # misaligned sigma
+    assert f(*args(o_lo=MIS)) == 1              # misaligned o_lo
+    assert f(*args(dt=0, o_lo=FAKE)) == 1       # o_lo with f32
     # the bf16 kernels' 32-bit buffer ranges: M * max(Hq, Hkv) * D * 2 must stay below 2^31
-    big = lambda M: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, M, 16, 8, 128, 1, FAKE, None, FAKE,
+    big = lambda M: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, M, 16, 8, 128, 1, FAKE, None, None, FAKE,
                      1 << 40, None]
     assert f(*big(1 << 20)) == 2
     assert f(*big((1 << 19) + 1)) == 2
     assert b"2^31" in lib.tg_last_error()
-    bbig = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, FAKE, FAKE, 1, 1 << 20, 16, 8, 128, 1, FAKE, FAKE,
-            FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None]
+    bbig = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, FAKE, FAKE, None, None, 1, 1 << 20, 16, 8, 128, 1,
+            FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None]
     assert lib.tg_gated_attn_bwd(*bbig) == 2
     b = lib.tg_gated_attn_bwd
     bargs = lambda **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, kw.get("sigma", None), kw.get("lse", FAKE),
-                          FAKE, 1, 100, 16, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("dsigma", None),
-                          FAKE, kw.get("wsb", 1 << 20), None]
+                          FAKE, kw.get("o", None), kw.get("o_lo", None), 1, 100, 16, 8, 128, kw.get("dt", 1), FAKE,
+                          FAKE, FAKE, FAKE, FAKE, kw.get("dsigma", None), FAKE, kw.get("wsb", 1 << 20), None]
     assert b(*bargs(lse=None)) == 1              # missing lse
     assert b(*bargs(wsb=16)) == 3                # workspace too small
     assert b(*bargs(sigma=FAKE)) == 1            # sigma without dsigma
     assert b(*bargs(dsigma=FAKE)) == 1           # dsigma without sigma
     assert b(*bargs(sigma=FAKE, dsigma=MIS)) == 1
+    assert b(*bargs(o=FAKE)) == 1                # o without o_lo
+    assert b(*bargs(o_lo=FAKE)) == 1             # o_lo without o
+    assert b(*bargs(o=MIS, o_lo=FAKE)) == 1      # misaligned o
+    assert b(*bargs(o=FAKE, o_lo=FAKE, dt=0)) == 1  # o and o_lo with f32
 
 
 def test_norm_gate_validation():
@@ -192,14 +199,15 @@ def test_varlen_validation():
     assert ws(good, 4, 16, 8, 128, 0) > 0
     assert ws(good, 4, 16, 8, 128, 1) > ws(good, 4, 16, 8, 128, 0)
     assert ws(bad0, 4, 16, 8, 128, 0) == 0 and ws(desc, 4, 16, 8, 128, 0) == 0 and ws(None, 4, 16, 8, 128, 0) == 0
-    # the workspace of the largest run: (2 sequences x 100 tokens) here
+    # every run's arrays side by side: at least those of the largest run (2 sequences x 100 tokens)
     assert ws(good, 4, 16, 8, 128, 0) >= lib.tg_gated_attn_workspace_size(2, 100, 16, 8, 128, 0)
     f = lib.tg_gated_attn_fwd_varlen
     f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, i64, i64,
                                           i64, i64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                          ctypes.c_size_t, ctypes.c_void_p]
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     args = lambda cu, **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, cu, 4, kw.get("Hq", 16), 8,
-                             kw.get("D", 128), 1, FAKE, None, kw.get("ws", FAKE), kw.get("wsb", 16), None]
+                             kw.get("D", 128), 1, FAKE, None, kw.get("o_lo", None), kw.get("ws", FAKE),
+                             kw.get("wsb", 16), None]
     assert f(*args(None)) == 1                 # cu_seqlens required
     assert f(*args(bad0)) == 1                 # cu_seqlens[0] != 0
     assert f(*args(desc)) == 1                 # decreasing
@@ -209,14 +217,16 @@ def test_varlen_validation():
     huge = cu_t(0, 1 << 19, 1 << 20, (1 << 20) + 5, (1 << 20) + 5)
     assert f(*args(huge, wsb=1 << 40)) == 2    # the packed tokens exceed the kernels' 32-bit ranges
     b = lib.tg_gated_attn_bwd_varlen
-    b.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 4 + [
+    b.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 6 + [
         i64, i64, i64, i64, ctypes.c_int] + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
     bargs = lambda **kw: [FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, kw.get("sigma", None), kw.get("lse", FAKE),
-                          FAKE, good, 4, 16, 8, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("dsigma", None), FAKE,
-                          kw.get("wsb", 16), None]
+                          FAKE, kw.get("o", None), kw.get("o_lo", None), good, 4, 16, 8, 128, 1, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, kw.get("dsigma", None), FAKE, kw.get("wsb", 16), None]
     assert b(*bargs(lse=None)) == 1
     assert b(*bargs(sigma=FAKE)) == 1          # sigma without dsigma
     assert b(*bargs()) == 3                    # workspace too small
+    assert b(*bargs(o=FAKE)) == 1              # o without o_lo
+    assert f(*args(good, o_lo=MIS)) == 1       # misaligned o_lo
 
 
 def test_heads_validation():
@@ -247,10 +257,10 @@ def test_heads_validation():
     hf = lib.tg_gated_attn_fwd_headgates
     hf.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_float, ctypes.c_float, ctypes.c_void_p, i64, i64, i64, i64, i64,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                           ctypes.c_size_t, ctypes.c_void_p]
-    assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 12, 8, 128, 1, FAKE, None, None, 0,
+                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 12, 8, 128, 1, FAKE, None, None, None, 0,
               None) == 1  # Hq % Hkv
-    assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 16, 8, 128, 1, FAKE, None, None, 0,
+    assert hf(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e6, 1.0, None, 1, 100, 16, 8, 128, 1, FAKE, None, None, None, 0,
               None) == 3  # workspace
 
 

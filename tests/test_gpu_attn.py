@@ -20,7 +20,7 @@ def _wl(B, M, Hq, Hkv, D, dtype="bf16", tau=1.0, seed=21):
 
 
 def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, seed_offset=0, temp=False,
-             gamma_override=None, overrides=None):
+             gamma_override=None, overrides=None, lo=False):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
@@ -38,11 +38,14 @@ def _run_fwd(w, M, rope=True, theta=wl.ROPE_THETA, g_override=None, grad=False, 
     sigma = torch.from_numpy(a["sigma"]).to(dev) if temp else None
     o = torch.full_like(q, float("nan"))
     lse = torch.full((w.B, w.Hq, M), float("nan"), device=dev)
+    o_lo = torch.full_like(q, float("nan")) if lo else None
     ws = tg.attn_workspace(w.B, M, w.Hq, w.Hkv, w.D, True, dev)
-    say("attn_fwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "rope" if rope else "no-rope", "temp" if temp else "")
-    tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, theta, w.tau, o, lse, ws, sigma=sigma)
+    say("attn_fwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "rope" if rope else "no-rope", "temp" if temp else "",
+        "o_lo" if lo else "")
+    tg.tg_gated_attn_fwd(q, k, v, g, gamma, pos, theta, w.tau, o, lse, ws, sigma=sigma, o_lo=o_lo)
     torch.cuda.synchronize()
-    out = dict(a=a, q=q, k=k, v=v, g=g, gamma=gamma, pos=pos, sigma=sigma, o=o, lse=lse, ws=ws, theta=theta)
+    out = dict(a=a, q=q, k=k, v=v, g=g, gamma=gamma, pos=pos, sigma=sigma, o=o, lse=lse, ws=ws, theta=theta,
+               o_lo=o_lo)
     return out
 
 
@@ -180,11 +183,13 @@ def test_fwd_deterministic():
     assert torch.equal(o1.view(torch.int16), r["o"].view(torch.int16))
 
 
-def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA, temp=False, g_override=None, overrides=None):
+def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA, temp=False, g_override=None, overrides=None, use_o=False):
+    """use_o: the forward also writes o_lo and the backward takes D_i from o + o_lo."""
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
-    r = _run_fwd(w, M, rope=rope, theta=theta, grad=True, temp=temp, g_override=g_override, overrides=overrides)
+    r = _run_fwd(w, M, rope=rope, theta=theta, grad=True, temp=temp, g_override=g_override, overrides=overrides,
+                 lo=use_o)
     dev = r["q"].device
     dout = dev_tensor(r["a"]["dout"], w.dtype, dev)
     dq = torch.full(r["q"].shape, float("nan"), device=dev)
@@ -193,9 +198,10 @@ def _run_bwd(w, M, rope=True, theta=wl.ROPE_THETA, temp=False, g_override=None, 
     dg = torch.full(r["g"].shape, float("nan"), device=dev)
     dgam = torch.full(r["gamma"].shape, float("nan"), device=dev)
     dsig = torch.full(r["gamma"].shape, float("nan"), device=dev) if temp else None
-    say("attn_bwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "temp" if temp else "")
+    say("attn_bwd", w.dtype, w.B, M, w.Hq, w.Hkv, w.D, "temp" if temp else "", "D from o" if use_o else "")
     tg.tg_gated_attn_bwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], theta, w.tau, r["lse"], dout, dq, dk,
-                         dv, dg, dgam, r["ws"], sigma=r["sigma"], dsigma=dsig)
+                         dv, dg, dgam, r["ws"], sigma=r["sigma"], dsigma=dsig, o=r["o"] if use_o else None,
+                         o_lo=r["o_lo"] if use_o else None)
     torch.cuda.synchronize()
     r.update(dout=dout, dq=dq, dk=dk, dv=dv, dg=dg, dgamma=dgam, dsigma=dsig)
     return r
@@ -257,6 +263,80 @@ def test_bwd_train_b4_full():
     r = _run_bwd(w, 2048)
     errs = _check_bwd(w, r)
     say("train_b4 bwd max-abs errors", errs)
+
+
+# --- the row terms D_i from the forward's o and its rounding residual o_lo ---
+
+def _bf16_ulp(x):
+    """The spacing of bf16 numbers at |x| (x given as float32 values of bf16 numbers)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), np.float32(2.0 ** -126))))
+    return np.float32(2.0) ** (e - 7)
+
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,D,temp", [(2, 300, 16, 8, 128, False), (1, 1000, 16, 8, 128, True),
+                                               (1, 190, 4, 4, 64, False)])
+def test_fwd_o_lo_residual(B, M, Hq, Hkv, D, temp):
+    """With o_lo the forward's P.V product takes P as two bf16 parts, so its fp32 output carries no
+    rounding of P: o + o_lo matches the oracle within 2e-3 and at least twice as closely as o alone
+    (what is left comes from the rotated q and k, rounded to bf16 from fp32 here and from fp64 in
+    the oracle); o stays within the bound, |o_lo| is at most half a bf16 step of o (it is the
+    rounding residual), and lse is the same as without o_lo.  The 1000-token case splits its long
+    rows into pieces merged at the end."""
+    import torch
+
+    w = _wl(B, M, Hq, Hkv, D, tau=1.1)
+    r0 = _run_fwd(w, M, temp=temp)
+    r = _run_fwd(w, M, temp=temp, lo=True)
+    assert torch.equal(r0["lse"], r["lse"])
+    o, lo = to_np(r["o"]), to_np(r["o_lo"])
+    assert np.all(np.isfinite(lo))
+    assert np.all(np.abs(lo) <= 0.5 * _bf16_ulp(o))
+    o_ref, _ = _oracle_fwd(w, r)
+    e_o = assert_maxabs(o, o_ref, 2e-2, "o")
+    e_lo = assert_maxabs(o + lo, o_ref, 2e-3, "o + o_lo")
+    say("o_lo: max-abs error of o", e_o, "of o + o_lo", e_lo)
+    assert e_lo <= 0.5 * e_o
+
+
+@pytest.mark.parametrize("B,M,Hq,Hkv,D,rope,temp", [
+    (1, 1, 2, 1, 128, True, False), (2, 100, 4, 2, 128, True, False), (1, 257, 8, 2, 128, False, True),
+    (1, 190, 4, 4, 64, True, False), (2, 300, 16, 8, 128, True, True)])
+def test_bwd_d_from_o_shapes(B, M, Hq, Hkv, D, rope, temp):
+    w = _wl(B, M, Hq, Hkv, D, tau=1.1)
+    r = _run_bwd(w, M, rope=rope, temp=temp, use_o=True)
+    _check_bwd(w, r, rope=rope)
+
+
+def test_bwd_d_from_o_zero_gate_rows():
+    w = _wl(1, 150, 4, 2, 128)
+    g = wl.attn_inputs(w, 150)["g"].copy()
+    g[0, 0] = 0.0
+    g[0, 70:80] = 0.0
+    r = _run_bwd(w, 150, g_override=g, use_o=True)
+    _check_bwd(w, r)
+
+
+@pytest.mark.parametrize("temp", [False, True])
+def test_bwd_d_from_o_train_b4_full(temp):
+    w = wl.WORKLOADS["train_b4"]
+    r = _run_bwd(w, 2048, temp=temp, use_o=True)
+    errs = _check_bwd(w, r)
+    say("train_b4 bwd (D from o) max-abs errors", errs)
+
+
+def test_bwd_d_from_o_deterministic():
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    w = _wl(2, 300, 16, 8, 128)
+    r = _run_bwd(w, 300, use_o=True)
+    first = [t.clone() for t in (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"])]
+    tg.tg_gated_attn_bwd(r["q"], r["k"], r["v"], r["g"], r["gamma"], r["pos"], r["theta"], w.tau, r["lse"],
+                         r["dout"], r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"], r["ws"], o=r["o"],
+                         o_lo=r["o_lo"])
+    torch.cuda.synchronize()
+    for a, b in zip(first, (r["dq"], r["dk"], r["dv"], r["dg"], r["dgamma"])):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
 def test_bwd_deterministic():
@@ -378,7 +458,7 @@ def test_temp_bwd_deterministic():
 
 # --- packed variable-length sequences (both training budgets in one call) ---
 
-def _varlen_case(lens, Hq, Hkv, D, dtype="bf16", seed=61, rope=True, temp=False, grad=False):
+def _varlen_case(lens, Hq, Hkv, D, dtype="bf16", seed=61, rope=True, temp=False, grad=False, use_o=False):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
@@ -403,7 +483,8 @@ def _varlen_case(lens, Hq, Hkv, D, dtype="bf16", seed=61, rope=True, temp=False,
     lse = torch.full((Hq * T_,), float("nan"), device=dev)
     ws = tg.attn_varlen_workspace(cu, Hq, Hkv, D, True, dev)
     say("attn_fwd_varlen", dtype, lens, Hq, Hkv, D, "rope" if rope else "", "temp" if temp else "")
-    tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, 1.1, cu, o, lse, ws, sigma=sigma)
+    o_lo = torch.full_like(q, float("nan")) if use_o else None
+    tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, 1.1, cu, o, lse, ws, sigma=sigma, o_lo=o_lo)
     torch.cuda.synchronize()
     f = lambda x: wl.as_float(x, dtype)
     o_ref, l_ref = oracle.attn_fwd_varlen(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], cu,
@@ -422,7 +503,7 @@ def _varlen_case(lens, Hq, Hkv, D, dtype="bf16", seed=61, rope=True, temp=False,
     dsig = torch.full(gamma.shape, float("nan"), device=dev) if temp else None
     say("attn_bwd_varlen", dtype, lens)
     tg.tg_gated_attn_bwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, 1.1, lse, dout, cu, dq, dk, dv, dg, dgam, ws,
-                                sigma=sigma, dsigma=dsig)
+                                sigma=sigma, dsigma=dsig, o=o if use_o else None, o_lo=o_lo)
     torch.cuda.synchronize()
     ref = oracle.attn_bwd_varlen(f(a["q"]), f(a["k"]), f(a["v"]), a["g"], a["gamma"], f(a["dout"]), cu,
                                  pos=a["pos"] if rope else None, theta=wl.ROPE_THETA, tau=1.1,
@@ -453,3 +534,10 @@ def test_varlen_two_budgets_train_shape():
     """Batch 4 at two budgets packed by budget: 4 x 2048 then 4 x 1024 kept tokens (sampled checks are
     the full oracle here: 12288 tokens, 16 / 8 heads, D = 128)."""
     _varlen_case([2048] * 4 + [1024] * 4, 16, 8, 128, temp=True, grad=True, seed=64)
+
+
+@pytest.mark.parametrize("lens,temp", [([300, 300, 150, 150], False), ([0, 1, 257, 0, 257, 33], True),
+                                       ([2048] * 4 + [1024] * 4, True)])
+def test_varlen_d_from_o(lens, temp):
+    """Packed sequences with the row terms from the forward's o + o_lo."""
+    _varlen_case(lens, 16, 8, 128, temp=temp, grad=True, seed=65, use_o=True)

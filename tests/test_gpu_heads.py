@@ -130,7 +130,8 @@ def test_normalize_aggregate_gather_softmax_heads():
                             f"g head {h}")
 
 
-def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=81, zero_heads=False, far=False):
+def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=81, zero_heads=False, far=False,
+                   use_o=False):
     import torch
     import learned_token_pruning_gatescore_amd as tg
 
@@ -160,13 +161,14 @@ def _headgate_case(B, M, Hq, Hkv, D, dtype="bf16", rope=True, temp=False, seed=8
     lse = torch.full((B, Hq, M), float("nan"), device=dev)
     ws = tg.attn_workspace(B, M, Hq, Hkv, D, True, dev)
     say("attn headgates", dtype, B, M, Hq, Hkv, D, "rope" if rope else "", "temp" if temp else "")
-    tg.tg_gated_attn_fwd_headgates(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws, sigma=sigma)
+    o_lo = torch.full_like(q, float("nan")) if use_o else None
+    tg.tg_gated_attn_fwd_headgates(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, o, lse, ws, sigma=sigma, o_lo=o_lo)
     dq, dk, dv = (torch.full(x.shape, float("nan"), device=dev) for x in (q, k, v))
     dg = torch.full(g.shape, float("nan"), device=dev)
     dgam = torch.full(gamma.shape, float("nan"), device=dev)
     dsig = torch.full(gamma.shape, float("nan"), device=dev) if temp else None
     tg.tg_gated_attn_bwd_headgates(q, k, v, g, gamma, pos, wl.ROPE_THETA, w.tau, lse, dout, dq, dk, dv, dg, dgam, ws,
-                                   sigma=sigma, dsigma=dsig)
+                                   sigma=sigma, dsigma=dsig, o=o if use_o else None, o_lo=o_lo)
     torch.cuda.synchronize()
     f = lambda x: wl.as_float(x, dtype)
     kw = dict(pos=a["pos"] if rope else None, theta=wl.ROPE_THETA, tau=w.tau, round_bf16=(dtype == "bf16"),
@@ -202,3 +204,10 @@ def test_headgates_dead_leading_tiles_far_logits(B, M, Hq, Hkv, temp):
 
 def test_headgates_f32():
     _headgate_case(1, 60, 4, 2, 32, dtype="f32", temp=True)
+
+
+@pytest.mark.parametrize("temp", [False, True])
+def test_headgates_d_from_o(temp):
+    """The backward's row terms from the forward's o + o_lo, with per-head gates (one head without
+    its early keys)."""
+    _headgate_case(2, 300, 16, 8, 128, temp=temp, zero_heads=True, use_o=True)
