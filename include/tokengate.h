@@ -289,7 +289,7 @@ size_t tg_gated_attn_workspace_size(int64_t B, int64_t M, int64_t Hq, int64_t Hk
  *   lse [B, Hq, M] f32 out or NULL (needed by the backward)
  *   o_lo [B, M, Hq, D] bf16 out or NULL (bf16 only): the residual of o's
  *     rounding, o_lo = bf16(o32 - o) for the fp32 output o32, so that
- *     o + o_lo is o32 to about 2^-18 relative (for the backward's D_i)
+ *     o + o_lo is o32 to about 2^-18 relative (for the backward)
  * bf16: D in {64, 128}, Hq / Hkv in {1, 2, 4, 8}; q.k and
  * P.v on matrix cores with fp32 accumulation, softmax in fp32, P rounded to
  * bf16 for the P.v product.  f32: D <= 128, plain fp32 arithmetic.
@@ -315,11 +315,13 @@ tg_status tg_gated_attn_fwd(const void *q, const void *k, const void *v, const f
  *     dv_j = sum_i P_ij dout_i,            (dk, dv summed over the group)
  *     dg_j = sum_h gamma_h colsum_h(j) / g_j      (0 where g_j = 0)
  *     dgamma_h = sum_b sum_j colsum_h(j) ln g_j,   colsum_h(j) = sum_i dS_ij
- * with c = 1 / (sqrt(D) tau).  D_i = dout_i . o_i: with o and o_lo (bf16,
- * both given or both NULL; the forward's o and o_lo of the same inputs) it
- * is taken as dout_i . (o_i + o_lo_i); without them it is formed from fp32 P
- * and dP by one more pass over the keys.  The rounded output alone would
- * not do: its rounding moves dg by more than the bf16 tolerance.  With sigma (the temperature of Eq. 7/8, as in the
+ * with c = 1 / (sqrt(D) tau).  D_i is formed exactly from fp32 P and dP.
+ * Without o and o_lo that takes one more pass over the keys.  With them (bf16,
+ * both given or both NULL: the forward's o and o_lo of the same inputs) the
+ * dq pass takes D_o = dout_i . (o_i + o_lo_i) in its dS and sums that dS's row,
+ * which yields the exact D_i for dk, dv, dg, dgamma and dsigma; dq alone keeps
+ * D_o, off by the forward's bf16 rounding of P (an error in dq of about
+ * 2^-9 c |D_i| |sum_j P_ij k^_j|, 2e-3 at the training shape's inputs).  With sigma (the temperature of Eq. 7/8, as in the
  * forward) dS_ij is dL/dS of S = t Z, dL/dZ_ij = t_ih dS_ij takes its place in
  * dq, dk and colsum, and
  *     dsigma_h = sigmoid(sigma_h) sum_b sum_i (ln m_i / ln max(2, p_i)) sum_j dS_ij Z_ij

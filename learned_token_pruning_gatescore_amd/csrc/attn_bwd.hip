@@ -163,8 +163,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       of[ks] = vq ? *(const u32x4 *)(dout + roff + 16 * ks + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
     }
     const float lrow = vq ? lse[((int64_t)b * Hq + h) * M + qi] : -INFINITY;
-    // With the forward's output o and its rounding residual o_lo: D_i = dO_i . O_i
-    // (O_i = sum_j P_ij V_j, so this is sum_j P_ij dP_ij without the pass over the keys)
+    // With the forward's output o and its rounding residual o_lo: D_o = dO_i . (o_i + o_lo_i)
+    // stands for D_i = sum_j P_ij dP_ij (= dO_i . O_i) in pass B's dS, without pass A.  The
+    // forward's O carries P's bf16 rounding, so D_o is off by about 2^-9 relative; pass B also
+    // sums the row of its dS, sum_j P_ij (dP_ij - D_o) = D_i - D_o (sum_j P_ij = 1), so the
+    // exact D_i goes to the key-outer kernel (dk, dv, the column sums, dg) and to the
+    // temperature's term; only dq keeps D_o (an error of c (D_i - D_o) sum_j P_ij k_j).
     float dso = 0.f;
     if (o) {
       if (vq) {
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
         }
       }
     };
-    float dsum = dso;
+    float dsum = dso;  // the D_i of pass B's dS
     if (!o) {
       f32x16 s, dp;
       for (int t = 0; t < tu; ++t) {
@@ -292,7 +296,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       issue(0, nt);
       issue(1, nt);
     }
-    if (vq && hl == 0) rowstat[((int64_t)b * Hq + h) * M + qi] = make_float2(la, dsum);
     const u32x4 daug = aug3(-dsum, hl);
 
     // pass B: dS and dQ^T
@@ -304,6 +307,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     // per-row constant (the exponent's shift), and sum_j dS_ij = 0, so the
     // shifted y = (S + la) c2 + bias serves (-inf clamped: there dS = 0).
     float dty[4] = {0.f, 0.f, 0.f, 0.f};
+    float drs = 0.f, dpy = 0.f;  // with o: sum_j dS_ij and (temperature) sum_j P_ij y_ij
     auto valu_b = [&](int t, const f32x16 &s, const f32x16 &dp, bool masked, u32x4(&dsf)[2]) __attribute__((always_inline)) {
       const float *bi = &sBias[slot(t)][hloc][4 * hl];
       const int lim = qi - t * AB_T;
@@ -317,8 +321,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
           const float y = __builtin_fmaf(s[r], c2, e ? bv.y : bv.x);
           float x = TEMP ? y * tq : y;
           if (masked && acc_row(r, hl) > lim) x = -INFINITY;
-          ds[r] = fast_exp2(x) * dp[r];
+          const float pr = fast_exp2(x);
+          ds[r] = pr * dp[r];
           if (TEMP) dty[r & 3] = __builtin_fmaf(ds[r], fmaxf(y, -1e30f), dty[r & 3]);
+          if (o) {
+            drs += ds[r];
+            if (TEMP) dpy = __builtin_fmaf(pr, fmaxf(y, -1e30f), dpy);
+          }
         }
       }
 #pragma unroll
@@ -345,9 +354,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
       }
     }
     sync_vm<0>();
+    float dex = dsum;  // the exact D_i
+    if (o) {
+      dex += drs + __shfl_xor(drs, 32);
+      dpy += __shfl_xor(dpy, 32);
+    }
+    if (vq && hl == 0) rowstat[((int64_t)b * Hq + h) * M + qi] = make_float2(la, dex);
     if (TEMP) {  // the temperature for the key-outer kernel, and ratio_i dL/dt_ih
       float dts = (dty[0] + dty[1]) + (dty[2] + dty[3]);
       dts += __shfl_xor(dts, 32);
+      // with D_o in dS: sum_j dS_ij y_ij with the exact D_i (the shift of y cancels only then)
+      if (o) dts -= (dex - dsum) * dpy;
       const int64_t Mp = (M + AB_T - 1) / AB_T * AB_T;
       if (hl == 0 && qi < Mp) tau[((int64_t)b * Hq + h) * Mp + qi] = tq;
       if (hl == 0 && vq) tstat[((int64_t)b * Hq + h) * M + qi] = rq * dts * kLn2;

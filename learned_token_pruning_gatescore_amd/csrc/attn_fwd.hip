@@ -221,11 +221,7 @@ __device__ __forceinline__ u32x4 aug_query(float x, int hl) {
   return hl == 0 ? u32x4{h | (m << 16), l | (0x3F80u << 16), 0x3F803F80u, 0u} : u32x4{0u, 0u, 0u, 0u};
 }
 
-// PLO: P enters the P.V product as two bf16 parts (P_hi + P_lo, one product
-// each), so the fp32 output is exact to about 2^-17 instead of carrying P's
-// bf16 rounding; used when the caller asks for o_lo (the backward's row terms
-// D_i = dO . o need that precision).
-template <int D, bool TEMP, bool PLO>
+template <int D, bool TEMP>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ qfr, int nq32, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, float c2, const float *__restrict__ sigma,
@@ -403,8 +399,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     return qi >= j0 ? tc2 * (s0[0] + brow[j0] * inv_c2k) : -INFINITY;
   };
   // softmax of 2 of the 16 logits per lane (registers 2c, 2c+1) of a tile
-  auto soft2 = [&](const f32x16 &s, int c, float msub, bool masked, int lim, float &ps, u32x4(&pf)[2],
-                   u32x4(&pfl)[2]) __attribute__((always_inline)) {
+  auto soft2 = [&](const f32x16 &s, int c, float msub, bool masked, int lim, float &ps, u32x4(&pf)[2])
+      __attribute__((always_inline)) {
     float x0 = __builtin_fmaf(s[2 * c], tc2, -msub), x1 = __builtin_fmaf(s[2 * c + 1], tc2, -msub);
     if (masked) {
       if (acc_row(2 * c, hl) > lim) x0 = -INFINITY;
@@ -417,7 +413,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     // written (between the products it overlaps) instead of sunk to its uses
     asm volatile("" : "+v"(ps) : "v"(pk));
     pf[c >> 2][c & 3] = pk;
-    if (PLO) pfl[c >> 2][c & 3] = pack_bf16x2(p0 - bf16_lo(pk), p1 - bf16_hi(pk));
   };
   // One step of the software pipeline: wait for tile t+1;
   // S^T of tile t+1 on the matrix cores while the first half of the softmax
@@ -436,7 +431,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const int lim = qi - (kt0 + t) * AF_TK;  // keys (within the tile) past the query are masked
     f32x16 sn = f32x16{};
     float ps = 0.f;
-    u32x4 pf[2], pfl[2];
+    u32x4 pf[2];
     {
       u32x4 f[NKS];
 #pragma unroll
@@ -448,7 +443,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
         sn = mfma32(f[ks], qf[ks], sn);
 #pragma unroll
         for (int c = 0; c < 4; ++c)  // chunk c after the last product of its quarter of the k-steps
-          if ((c + 1) * NKS / 4 - 1 == ks) soft2(sc, c, msub, masked, lim, ps, pf, pfl);
+          if ((c + 1) * NKS / 4 - 1 == ks) soft2(sc, c, msub, masked, lim, ps, pf);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -462,10 +457,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
         if (i + 3 < 2 * NDB) f[i + 3] = fr.tr(V, (i + 3) / NDB, (i + 3) % NDB);
         __builtin_amdgcn_sched_barrier(0);
         acc[i % NDB] = mfma32(f[i], pf[i / NDB], acc[i % NDB]);
-        if (PLO) acc[i % NDB] = mfma32(f[i], pfl[i / NDB], acc[i % NDB]);
 #pragma unroll
         for (int c = 0; c < 4; ++c)  // chunks 4..7 spread over the products of the first 16 keys
-          if (i < NDB && c * NDB / 4 == i) soft2(sc, 4 + c, msub, masked, lim, ps, pf, pfl);
+          if (i < NDB && c * NDB / 4 == i) soft2(sc, 4 + c, msub, masked, lim, ps, pf);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -968,13 +962,8 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const dim3 grid((unsigned)(f.npieces * B * Hkv));
     const float c2 = (float)(c * 1.4426950408889634);
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
-    auto kern = o_lo ? (D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true, true>
-                                          : attn_fwd_bf16_kernel<128, false, true>)
-                                 : (sigma ? attn_fwd_bf16_kernel<64, true, true> : attn_fwd_bf16_kernel<64, false, true>))
-                     : (D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true, false>
-                                          : attn_fwd_bf16_kernel<128, false, false>)
-                                 : (sigma ? attn_fwd_bf16_kernel<64, true, false>
-                                          : attn_fwd_bf16_kernel<64, false, false>));
+    auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>)
+                         : (sigma ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>);
     hipLaunchKernelGGL(kern, grid, dim3(512), 0, s, (const uint16_t *)w.qhat, (M + 31) / 32, kh, (const uint16_t *)v,
                        w.bias, c2, sigma, w.ratio, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part, w.cnt,
                        (uint16_t *)o, lse, (uint16_t *)o_lo);
