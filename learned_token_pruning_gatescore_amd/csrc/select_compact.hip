@@ -508,9 +508,22 @@ __global__ __launch_bounds__(SEL_TPB) void select_refine_kernel(const float *__r
     res[1] = res[3] = 1u;
   }
 
-  // global coarse histogram (thread t: coarse bin 255 - t, descending) and forced count
+  // global coarse histogram (thread t: coarse bin 255 - t, descending) and forced count; the
+  // slots' loads go out eight at a time (one at a time, each waited for, they cost a memory
+  // round trip per work-group of the row)
   uint32_t c = 0u;
-  for (int g = 0; g < G; ++g) c += ws.coarse[(slot0 + g) * SEL_NC + (SEL_NC - 1 - tid)];
+  {
+    const uint32_t *cp = ws.coarse + slot0 * SEL_NC + (SEL_NC - 1 - tid);
+    int g = 0;
+    for (; g + 8 <= G; g += 8) {
+      uint32_t x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = cp[(g + j) * SEL_NC];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c += x[j];
+    }
+    for (; g < G; ++g) c += cp[g * SEL_NC];
+  }
   uint32_t nfp = 0u;
   for (int g = tid; g < G; g += SEL_TPB) nfp += ws.nf[slot0 + g];
   const int64_t nF = sel_block_sum(nfp, red);
@@ -561,22 +574,32 @@ __global__ __launch_bounds__(SEL_TPB) void select_refine_kernel(const float *__r
   }
   uint32_t ncw;
   const uint32_t cpos = sel_block_exscan((uint32_t)__popc(cm), red, ncw);
+  // Candidates and the count of surely kept tokens go out as agent-scope
+  // relaxed atomic stores (written where every XCD reads them, not left in
+  // this XCD's L2), and the row's last work-group reads them back with
+  // agent-scope loads; s_waitcnt vmcnt(0) and the barrier put every store of
+  // the work-group before its arrival.  A device-scope fence instead writes
+  // back and invalidates the whole L2 on this chip (on both sides).
   {
     uint64_t *dst = ws.cand + b * N + coff + cpos;
     int r = 0;
 #pragma unroll
     for (int i = 0; i < SEL_IPT; ++i)
-      if ((cm >> i) & 1u) dst[r++] = ((uint64_t)key[i] << 32) | (uint64_t)(n0 + i);
+      if ((cm >> i) & 1u)
+        __hip_atomic_store(dst + r++, ((uint64_t)key[i] << 32) | (uint64_t)(n0 + i), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
   const uint32_t sure_w = sel_block_sum(sure, red);
-  if (tid == 0) ws.sure[slot0 + w] = sure_w;
+  if (tid == 0) __hip_atomic_store(&ws.sure[slot0 + w], sure_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // publish, count arrivals; the last work-group of the row goes on
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&ws.rowp[b * 8], 1u) == (uint32_t)(G - 1);
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&ws.rowp[b * 8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(G - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  auto ld_cand = [&](const uint64_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
 
   for (int g = tid; g < G; g += SEL_TPB) s_above[g] = s_ties[g] = 0u;
   uint32_t T = mode == SEL_ALL ? 0u : 0xFFFFFFFFu, quota = 0u;
@@ -584,9 +607,18 @@ __global__ __launch_bounds__(SEL_TPB) void select_refine_kernel(const float *__r
     // exact threshold inside bin d0: two 10-bit passes over the candidates
     const uint64_t *cg = ws.cand + b * N;
     const bool in_lds = ctot <= (uint32_t)SEL_CCAP;
-    if (in_lds)
-      for (uint32_t i = tid; i < ctot; i += SEL_TPB) scand[i] = cg[i];
-    auto cand = [&](uint32_t i) -> uint64_t { return in_lds ? scand[i] : cg[i]; };
+    if (in_lds) {  // eight loads in flight per thread
+      uint32_t i0 = 0;
+      for (; i0 + 8 * SEL_TPB <= ctot; i0 += 8 * SEL_TPB) {
+        uint64_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = ld_cand(cg + i0 + j * SEL_TPB + tid);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) scand[i0 + j * SEL_TPB + tid] = x[j];
+      }
+      for (uint32_t i = i0 + tid; i < ctot; i += SEL_TPB) scand[i] = ld_cand(cg + i);
+    }
+    auto cand = [&](uint32_t i) -> uint64_t { return in_lds ? scand[i] : ld_cand(cg + i); };
     uint32_t pre = (uint32_t)d0 << 10;  // key >> 10 of the keys still in play
     for (int pass = 0; pass < 2; ++pass) {
       const int sh = pass == 0 ? 10 : 0;
@@ -645,7 +677,9 @@ __global__ __launch_bounds__(SEL_TPB) void select_refine_kernel(const float *__r
   for (int j = 0; j < 4; ++j) {
     const int g = 4 * tid + j;
     qv[j] = tb >= quota ? 0u : (quota - tb < tv[j] ? quota - tb : tv[j]);  // ties this work-group keeps
-    sv[j] = g < G ? ws.sure[slot0 + g] + s_above[g] + qv[j] : 0u;
+    sv[j] = g < G ? __hip_atomic_load(&ws.sure[slot0 + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + s_above[g] +
+                        qv[j]
+                  : 0u;
     tb += tv[j];
     lk += sv[j];
   }
