@@ -368,8 +368,8 @@ tg_status tg_gated_attn_bwd(const void *q, const void *k, const void *v, const f
  *   one gate per (query head, key): g [B, Hq, M] f32 (> = 0), bias
  *   gamma_h ln g_hj; the backward's dg is [B, Hq, M],
  *   dg_hj = gamma_h colsum_h(j) / g_hj (0 where g_hj = 0), and dgamma uses
- *   ln g_hj.  Everything else (sigma, workspace, dtypes, errors) as the
- *   shared-gate calls.
+ *   ln g_hj.  Everything else (sigma, o_lo / o, workspace, dtypes, errors) as
+ *   the shared-gate calls.
  */
 tg_status tg_gate_score_heads(const void *hidden, int ln, const void *ln_w, float ln_eps,
                               const void *w1, const void *w2, int64_t B, int64_t N, int64_t d,
@@ -447,6 +447,8 @@ tg_status tg_gate_score_clone(const void *hidden, int ln, const void *ln_w, floa
  *   q [T, Hq, D], k, v [T, Hkv, D], o [T, Hq, D] (dt); g [T] f32; pos [T] i32
  *     or NULL; sigma [Hq] or NULL (as in tg_gated_attn_fwd);
  *   lse: Hq * T f32, sequence s's [Hq, M_s] block at offset Hq * cu_seqlens[s];
+ *   o_lo (forward, optional) and o, o_lo (backward, optional): [T, Hq, D]
+ *     bf16, as in tg_gated_attn_fwd / _bwd;
  *   backward: dq [T, Hq, D], dk, dv [T, Hkv, D], dg [T] f32 per token; dgamma
  *     (and dsigma) [Hq] summed over all sequences.
  * Maximal runs of adjacent equal-length sequences (empty ones skipped) are
