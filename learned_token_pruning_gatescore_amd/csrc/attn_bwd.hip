@@ -169,19 +169,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     // sums the row of its dS, sum_j P_ij (dP_ij - D_o) = D_i - D_o (sum_j P_ij = 1), so the
     // exact D_i goes to the key-outer kernel (dk, dv, the column sums, dg) and to the
     // temperature's term; only dq keeps D_o (an error of c (D_i - D_o) sum_j P_ij k_j).
+    // (every load issued before the first use: roff names a valid row for every lane, and a
+    // column past M contributes 0)
     float dso = 0.f;
     if (o) {
-      if (vq) {
+      u32x4 oh[NKS], ol[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 hi = *(const u32x4 *)(o + roff + 16 * ks + 8 * hl);
-          const u32x4 lo = *(const u32x4 *)(o_lo + roff + 16 * ks + 8 * hl);
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            dso += bf16_lo(of[ks][w]) * (bf16_lo(hi[w]) + bf16_lo(lo[w])) +
-                   bf16_hi(of[ks][w]) * (bf16_hi(hi[w]) + bf16_hi(lo[w]));
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        oh[ks] = *(const u32x4 *)(o + roff + 16 * ks + 8 * hl);
+        ol[ks] = *(const u32x4 *)(o_lo + roff + 16 * ks + 8 * hl);
       }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          dso += bf16_lo(of[ks][w]) * (bf16_lo(oh[ks][w]) + bf16_lo(ol[ks][w])) +
+                 bf16_hi(of[ks][w]) * (bf16_hi(oh[ks][w]) + bf16_hi(ol[ks][w]));
+      if (!vq) dso = 0.f;
       dso += __shfl_xor(dso, 32);
     }
 #pragma unroll
@@ -193,13 +197,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_kernel(
     settle(tq);
     settle(rq);
     if (cs) {
+      // the row's angles in one batch of loads (in four, one per step pair, they cost a memory
+      // round trip each)
       const f32x4 *crow = (const f32x4 *)(cs + (bM + (vq ? qi : 0)) * HALF);
+      f32x4 ang[NKS / 2][4];
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ang[ks][w] = crow[(16 * ks + 8 * hl) / 2 + w];
 #pragma unroll
       for (int ks = 0; ks < NKS / 2; ++ks) {
         u32x4 &x = qf[ks], &y = qf[ks + NKS / 2];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const f32x4 t = crow[(16 * ks + 8 * hl) / 2 + w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
+          const f32x4 t = ang[ks][w];  // pairs 2w, 2w+1: (cos, sin, cos, sin)
           const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
           const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
           x[w] = pack_bf16x2(x0 * t[0] - y0 * t[1], x1 * t[2] - y1 * t[3]);
