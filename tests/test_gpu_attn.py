@@ -553,6 +553,15 @@ def test_varlen_two_budgets_train_shape():
     _varlen_case([2048] * 4 + [1024] * 4, 16, 8, 128, temp=True, grad=True, seed=64)
 
 
+@pytest.mark.parametrize("use_o", [False, True])
+def test_varlen_many_distinct_lengths(use_o):
+    """20 sequences of distinct lengths (600 .. 1300 tokens): 20 runs, so the backward's one-launch
+    schedule splits into two groups of runs, each with more than 64 work-group ranges, i.e. several
+    launches per kernel."""
+    lens = [int(x) for x in np.random.default_rng(66).choice(np.arange(600, 1301), 20, replace=False)]
+    _varlen_case(lens, 8, 4, 128, temp=True, grad=True, seed=66, use_o=use_o)
+
+
 @pytest.mark.parametrize("lens,temp", [([300, 300, 150, 150], False), ([0, 1, 257, 0, 257, 33], True),
                                        ([2048] * 4 + [1024] * 4, True)])
 def test_varlen_d_from_o(lens, temp):
