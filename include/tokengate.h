@@ -452,11 +452,13 @@ tg_status tg_gate_score_clone(const void *hidden, int ln, const void *ln_w, floa
  *   backward: dq [T, Hq, D], dk, dv [T, Hkv, D], dg [T] f32 per token; dgamma
  *     (and dsigma) [Hq] summed over all sequences.
  * Maximal runs of adjacent equal-length sequences (empty ones skipped) are
- * the unit of work.  The backward's matrix-core kernels take every run in
- * one launch each: each work-group holds one block of one sequence of one
- * run, with the blocks of all runs ordered longest first, so sequences of
- * different lengths share the compute units.  The forward runs one batched
- * launch per run.  The workspace (tg_gated_attn_varlen_workspace_size,
+ * the unit of work.  The matrix-core kernels take up to 16 runs per launch:
+ * each work-group holds one block (the forward: one piece of a block) of one
+ * sequence of one run, with the blocks of all runs ordered longest first, so
+ * sequences of different lengths share the compute units.  The bf16 forward
+ * picks its key-split length once for the 16 runs of a launch, and its prep
+ * pass covers them in one launch too (f32: one forward launch per run).
+ * The workspace (tg_gated_attn_varlen_workspace_size,
  * 256-byte aligned) holds every run's arrays side by side.  Validation,
  * dtypes and errors as the batched calls; dgamma / dsigma are summed in run
  * order (deterministic).

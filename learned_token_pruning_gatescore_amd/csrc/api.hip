@@ -596,6 +596,11 @@ tg_status tg_gated_attn_fwd_varlen(const void *q, const void *k, const void *v, 
   REQUIRE(reinterpret_cast<uintptr_t>(ws) % kAlign == 0, TG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const size_t esz = dt == TG_BF16 ? 2 : 4;
   const tg::AttnWs wall = tg::carve_attn_ws_runs(ws, runs.data(), (int)runs.size(), Hq, Hkv, D);
+  if (dt == TG_BF16 && runs.size() > 1)  // every run's blocks in one launch per group of runs
+    return hip_status(tg::launch_attn_fwd_runs(q, k, v, g, gamma, pos, (double)rope_theta, tau, sigma, runs.data(),
+                                               (int)runs.size(), (int)Hq, (int)Hkv, (int)D, o, lse, o_lo, wall,
+                                               (hipStream_t)stream),
+                      "tg_gated_attn_fwd_varlen launch");
   for (const tg::RunRow &r : runs) {
     const tg::AttnWs w = tg::run_view(wall, r, Hq, Hkv, D);
     const int64_t off = r.off;

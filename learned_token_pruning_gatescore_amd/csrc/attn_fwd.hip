@@ -78,6 +78,36 @@ __device__ __forceinline__ void rot8(u32x4 &x, u32x4 &y, const float2 *cp) {
   }
 }
 
+// The runs of a packed group for the prep pass: run i starts at row off[i]
+// (off[0] = 0, rows counted from the group's first token) and at padded row
+// poff[i]; its sequences have M[i] tokens.
+struct PrepRuns {
+  int nr;
+  int off[kMaxRuns], poff[kMaxRuns], M[kMaxRuns];
+};
+// Row r of a group: its run's length M, the row's sequence bb within the run
+// and index j within the sequence, and the run's first row and padded row.
+struct PrepRow {
+  int M, bb, j, off, poff;
+};
+__device__ __forceinline__ PrepRow prep_row(const PrepRuns &pr, int64_t r) {
+  PrepRow x{pr.M[0], 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 1; i < kMaxRuns; ++i)
+    if (i < pr.nr && r >= pr.off[i]) {
+      x.M = pr.M[i];
+      x.off = pr.off[i];
+      x.poff = pr.poff[i];
+    }
+  const int loc = (int)(r - x.off);
+  x.bb = loc / x.M;
+  x.j = loc - x.bb * x.M;
+  return x;
+}
+
+// MR: the rows are a packed group of runs (pr); bias and the query
+// fragments are placed per run, M and nq32 are unused.
+template <bool MR>
 __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restrict__ k, const float *__restrict__ g,
                                                         const float *__restrict__ gamma,
                                                         const int32_t *__restrict__ pos, InvFreq inv, int64_t rows,
@@ -85,8 +115,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
                                                         uint16_t *__restrict__ khat, float *__restrict__ bias,
                                                         float *__restrict__ ratio, int *__restrict__ cnt, int ncnt,
                                                         int gph, const uint16_t *__restrict__ q,
-                                                        uint16_t *__restrict__ qfr, int nq32) {
+                                                        uint16_t *__restrict__ qfr, int nq32, const PrepRuns pr) {
   __shared__ float2 scs[256];
+  __shared__ PrepRow srow[8];  // MR: the placement of the work-group's rows, found once
   const int half = D / 2, R = 256 / half;  // R rows per work-group, one thread per (row, rotary pair)
   const int t = threadIdx.x;
   const int64_t idx = (int64_t)blockIdx.x * 256 + t;
@@ -94,6 +125,10 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
   const int lr = t / half, i = t - lr * half;
   const int64_t r0 = (int64_t)blockIdx.x * R, r = r0 + lr;
   const bool vr = lr < R && r < rows;
+  if constexpr (MR) {
+    if (t < R && r0 + t < rows) srow[t] = prep_row(pr, r0 + t);
+    __syncthreads();
+  }
   if (pos && vr) {
     double sn, cn;
     sincos((double)pos[r] * inv.v[i], &sn, &cn);
@@ -129,13 +164,27 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
       const int64_t o = (row * Hq + h) * D + e;
       u32x4 x = *(const u32x4 *)(q + o), y = *(const u32x4 *)(q + o + half);
       if (pos) rot8(x, y, scs + lr2 * half + e);
-      const int bb = (int)(row / M), j = (int)(row - (int64_t)bb * M);
-      uint16_t *blk = qfr + ((((int64_t)bb * Hq + h) * nq32 + j / 32) * nks) * 512 + ((j & 31) + 32 * hl) * 8;
+      uint16_t *blk;
+      if constexpr (MR) {
+        const PrepRow x = srow[lr2];
+        blk = qfr + (int64_t)x.poff * Hq * D +
+              ((((int64_t)x.bb * Hq + h) * ((x.M + 31) / 32) + x.j / 32) * nks) * 512 + ((x.j & 31) + 32 * hl) * 8;
+      } else {
+        const int bb = (int)(row / M), j = (int)(row - (int64_t)bb * M);
+        blk = qfr + ((((int64_t)bb * Hq + h) * nq32 + j / 32) * nks) * 512 + ((j & 31) + 32 * hl) * 8;
+      }
       *(u32x4 *)(blk + kp * 512) = x;
       *(u32x4 *)(blk + (kp + npair) * 512) = y;
     }
   }
-  if (bias && vr) {  // gph: one gate per (head, key), g [B, Hq, M]; else one per key, g [B, M]
+  if constexpr (MR) {  // one gate per key, g [rows]; each run's bias [n, Hq, M] from its first row's Hq-fold
+    if (bias && vr) {
+      const PrepRow x = srow[lr];
+      float *bq = bias + (int64_t)x.off * Hq + ((int64_t)x.bb * Hq) * x.M + x.j;
+      const float gv = g[r];
+      for (int h = i; h < Hq; h += half) bq[(int64_t)h * x.M] = gv > 0.f ? gamma[h] * log2f(gv) : -INFINITY;
+    }
+  } else if (bias && vr) {  // gph: one gate per (head, key), g [B, Hq, M]; else one per key, g [B, M]
     const int64_t bb = r / M, j = r - bb * M;
     for (int h = i; h < Hq; h += half) {
       const float gv = g[gph ? (bb * Hq + h) * M + j : r];
@@ -143,7 +192,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const uint16_t *__restri
     }
   }
   if (ratio && vr && i == 0) {  // the temperature's row factor ln m_i / ln max(2, p_i) (fp64 logs)
-    const int64_t bb = r / M, j = r - bb * M;
+    int64_t j;
+    if constexpr (MR) j = srow[lr].j;
+    else j = r - (r / M) * M;
     const double m = (double)j + 1.0, pp = pos ? (double)pos[r] + 1.0 : m;
     ratio[r] = (float)(log(m) / log(pp > 2.0 ? pp : 2.0));
   }
@@ -221,13 +272,24 @@ __device__ __forceinline__ u32x4 aug_query(float x, int hl) {
   return hl == 0 ? u32x4{h | (m << 16), l | (0x3F80u << 16), 0x3F803F80u, 0u} : u32x4{0u, 0u, 0u, 0u};
 }
 
-template <int D, bool TEMP>
+// The work-group table argument: a RunTable over packed runs, nothing for
+// one batch.
+struct NoTable {
+  int unused;
+};
+template <bool MR>
+using FwdTab = std::conditional_t<MR, RunTable, NoTable>;
+
+// MR: the work-groups cover the runs of a packed group through the table rt;
+// the pointers are those of the whole packed batch and workspace, and B, M,
+// nq32, nqb and C are taken from the work-group's run.
+template <int D, bool TEMP, bool MR>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ qfr, int nq32, const uint16_t *__restrict__ khat, const uint16_t *__restrict__ v,
     const float *__restrict__ bias, float c2, const float *__restrict__ sigma,
     const float *__restrict__ ratio, int B, int M, int Hq, int Hkv, int G, int BQ, int nqb, int C,
     float *__restrict__ part, int *__restrict__ cnt, uint16_t *__restrict__ o, float *__restrict__ lse,
-    uint16_t *__restrict__ o_lo) {
+    uint16_t *__restrict__ o_lo, const FwdTab<MR> rt) {
   using T = BTile<D>;
   using F = FwdCfg<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB;
@@ -245,19 +307,55 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int l32 = lane & 31, hl = lane >> 5;
+  constexpr int RW = AB_NW * F::NR * 64;  // floats per work-group record
+  unsigned wg = blockIdx.x;  // the work-group within its range of the table (all of them for one batch)
+  int top = nqb - 1;         // the piece listing: blocks top, top - 1, ...
+  bool across = false;       // one block of consecutive runs, one piece each
+  int ri = 0;                // the run (MR)
+  if constexpr (MR) {
+    // the range: the last e with start[e] <= wg (binary search, uniform)
+    int e = 0;
+#pragma unroll
+    for (int step = kMaxEnt / 2; step >= 1; step >>= 1)
+      if ((int)wg >= rt.start[e + step]) e += step;
+    const int code = rt.code[e];
+    ri = code & 0xFF;
+    wg -= rt.start[e];
+    top = (code >> 8) & 0x3FFFFF;
+    across = (code >> 30) & 1;
+    if (across)
+      for (int i = 0; i < kMaxRuns - 1; ++i) {
+        const unsigned nb = rt.run[ri].n * Hkv;
+        if (wg < nb) break;
+        wg -= nb;
+        ++ri;
+      }
+    const RunRow &r = rt.run[ri];
+    B = r.n;
+    M = r.M;
+    C = r.C;
+    nqb = (M + BQ - 1) / BQ;
+    nq32 = (M + 31) / 32;
+    const int64_t off = r.off;
+    qfr += (int64_t)r.poff * Hq * D;
+    khat += off * Hkv * D;
+    v += off * Hkv * D;
+    bias += off * Hq;
+    if (TEMP) ratio += off;
+  }
   const int nbh = B * Hkv;
   // consecutive work-groups take consecutive (batch, kv head): with the
   // round-robin placement over the 8 XCDs one head's keys stay in one L2
-  const int bh = blockIdx.x % nbh;
+  const int bh = wg % nbh;
   const int b = bh / Hkv, kvh = bh % Hkv;
 
   // Piece -> (query block, piece index).  Pieces are listed by descending query
   // block (longest rows first); each wave scans 64 blocks at a time.
-  int qb = 0, p = 0, np = 1, pfirst = 0;
-  {
-    int rem = blockIdx.x / nbh, base = 0;
-    for (int c0 = 0; c0 < nqb; c0 += 64) {
-      const int qq = nqb - 1 - (c0 + lane);
+  int qb = across ? top : 0, p = 0, np = 1, pfirst = 0;
+  if (!across) {
+    int rem = wg / nbh, base = 0;
+    for (int c0 = 0; c0 <= top; c0 += 64) {
+      const int qq = top - (c0 + lane);
       const int mine = qq >= 0 ? fwd_npieces(fwd_ntiles(qq, BQ, M), C) : 0;
       int incl = mine;
       for (int o2 = 1; o2 < 64; o2 <<= 1) {
@@ -268,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       if (rem < tot) {
         const int src = __ffsll((unsigned long long)__ballot(incl > rem)) - 1;
         const int excl = __shfl(incl - mine, src);
-        qb = nqb - 1 - (c0 + src);
+        qb = top - (c0 + src);
         np = __shfl(mine, src);
         p = rem - excl;
         pfirst = base + excl;
@@ -541,7 +639,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   auto ld_dev = [](const float *a) __attribute__((always_inline)) {
     return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  constexpr int RW = AB_NW * F::NR * 64;  // floats per work-group record
+  if constexpr (MR) {
+    // the outputs of the work-group's run, placed only now (the run read from
+    // the table again instead of holding its pointers through the loop)
+    int rj = ri;
+    asm volatile("" : "+s"(rj));
+    const RunRow &r = rt.run[rj];
+    const int64_t off = r.off;
+    part += (int64_t)r.rec0 * RW;
+    cnt += r.cnt0;
+    o += off * Hq * D;
+    if (lse) lse += off * Hq;
+    if (o_lo) o_lo += off * Hq * D;
+  }
   int npm = 1;
   if (np > 1) {
     float *rec = part + ((int64_t)(pfirst + p) * nbh + bh) * RW + wave * F::NR * 64 + lane;
@@ -721,39 +831,60 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
 // unit (blocks longer than that are split).  Otherwise C is the smallest piece
 // length (at least 8 tiles) that keeps every piece in a single wave of 256
 // work-groups.  Pieces of split blocks get a partial record each; split
-// blocks form a prefix of the piece list.
-FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
-  FwdSched f{};
+// blocks form a prefix of the piece list.  Runs launched together share one
+// C, chosen the same way over all their blocks.
+static int fwd_group_c(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv) {
   const int64_t G = Hkv > 0 ? Hq / Hkv : 0;
-  if (M <= 0 || G < 1 || G > 8 || (G & (G - 1)) != 0) return f;
-  f.BQ = (int)(256 / G);
-  f.nqb = (int)((M + f.BQ - 1) / f.BQ);
-  const int64_t nbh = B * Hkv;
-  int64_t tiles = 0;
+  if (G < 1 || G > 8 || (G & (G - 1)) != 0) return 0;
+  const int BQ = (int)(256 / G);
+  int64_t blocks = 0, tiles = 0;
   int nmax = 0;
-  for (int qb = 0; qb < f.nqb; ++qb) {
-    const int n = fwd_ntiles(qb, f.BQ, (int)M);
-    tiles += n;
-    nmax = n > nmax ? n : nmax;
+  for (int i = 0; i < nruns; ++i) {
+    const int64_t nbh = (int64_t)runs[i].n * Hkv;
+    const int M = runs[i].M, nqb = (M + BQ - 1) / BQ;
+    blocks += nbh * nqb;
+    for (int qb = 0; qb < nqb; ++qb) {
+      const int n = fwd_ntiles(qb, BQ, M);
+      tiles += nbh * n;
+      nmax = n > nmax ? n : nmax;
+    }
+  }
+  if (blocks >= 256) {
+    const int64_t avg = (tiles + 255) / 256;
+    return (int)(avg > 8 ? avg : 8);
   }
   auto pieces = [&](int C) {
     int64_t np = 0;
-    for (int qb = 0; qb < f.nqb; ++qb) np += fwd_npieces(fwd_ntiles(qb, f.BQ, (int)M), C);
+    for (int i = 0; i < nruns; ++i) {
+      const int M = runs[i].M, nqb = (M + BQ - 1) / BQ;
+      for (int qb = 0; qb < nqb; ++qb) np += (int64_t)runs[i].n * Hkv * fwd_npieces(fwd_ntiles(qb, BQ, M), C);
+    }
     return np;
   };
-  if (nbh * f.nqb >= 256) {
-    const int64_t avg = (nbh * tiles + 255) / 256;
-    f.C = (int)(avg > 8 ? avg : 8);
-  } else {
-    f.C = 8;
-    while (f.C < nmax && nbh * pieces(f.C) > 256) ++f.C;
-  }
+  int C = 8;
+  while (C < nmax && pieces(C) > 256) ++C;
+  return C;
+}
+
+FwdSched fwd_sched_c(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int C) {
+  FwdSched f{};
+  const int64_t G = Hkv > 0 ? Hq / Hkv : 0;
+  if (M <= 0 || G < 1 || G > 8 || (G & (G - 1)) != 0 || C < 1) return f;
+  (void)B;
+  f.BQ = (int)(256 / G);
+  f.nqb = (int)((M + f.BQ - 1) / f.BQ);
+  f.C = C;
   for (int qb = 0; qb < f.nqb; ++qb) {
     const int np = fwd_npieces(fwd_ntiles(qb, f.BQ, (int)M), f.C);
     f.npieces += np;
     if (np > 1) f.nmulti += np;
   }
   return f;
+}
+
+FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
+  const RunRow r{0, 0, (int)B, (int)M, 0, 0, 0};
+  return fwd_sched_c(B, M, Hq, Hkv, M > 0 && B > 0 ? fwd_group_c(&r, 1, Hq, Hkv) : 0);
 }
 
 // Workspace of the attention calls (256-byte aligned regions):
@@ -763,12 +894,6 @@ FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
 //   (backward) qhat [B*M*Hq*D] bf16 | rowstat [B*Hq*M] float2 | colsum [B*Hq*M] f32 |
 //   tau [B*Hq*Mp] f32 (Mp = M rounded up to 32) | tstat [B*Hq*M] f32
 static size_t rup(size_t x) { return (x + 255) / 256 * 256; }
-
-static size_t part_floats(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
-  const FwdSched f = fwd_sched(B, M, Hq, Hkv);
-  const int64_t nr = (D / 32) * 16 + 2;  // floats per lane of a record, 8 waves per work-group
-  return (size_t)(f.nmulti * B * Hkv * 8 * nr * 64);
-}
 
 static size_t cnt_ints(int64_t B, int64_t M, int64_t Hq, int64_t Hkv) {
   return (size_t)(B * Hkv * fwd_sched(B, M, Hq, Hkv).nqb);
@@ -785,13 +910,18 @@ static int64_t rec_floats(int64_t D) { return 8 * ((D / 32) * 16 + 2) * 64; }
 
 void plan_runs(RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D) {
   (void)D;
+  for (int g0 = 0; g0 < nruns; g0 += kMaxRuns) {
+    const int ng = nruns - g0 < kMaxRuns ? nruns - g0 : kMaxRuns;
+    const int C = fwd_group_c(runs + g0, ng, Hq, Hkv);
+    for (int i = g0; i < g0 + ng; ++i) runs[i].C = C;
+  }
   int64_t poff = 0, rec = 0, cnt = 0;
   for (int i = 0; i < nruns; ++i) {
     RunRow &r = runs[i];
     r.poff = (int)poff;
     r.rec0 = (int)rec;
     r.cnt0 = (int)cnt;
-    const FwdSched f = fwd_sched(r.n, r.M, Hq, Hkv);
+    const FwdSched f = fwd_sched_c(r.n, r.M, Hq, Hkv, r.C);
     poff += (int64_t)r.n * ((r.M + 31) / 32 * 32);
     rec += (int64_t)f.nmulti * r.n * Hkv;
     cnt += (int64_t)r.n * Hkv * f.nqb;
@@ -802,11 +932,13 @@ namespace {
 struct RunTotals {
   int64_t T = 0, PT = 0, recs = 0, cnts = 0;
 };
-RunTotals run_totals(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv) {
+// totals over the runs as plan_runs places them
+RunTotals run_totals(const RunRow *runs_in, int nruns, int64_t Hq, int64_t Hkv) {
+  std::vector<RunRow> runs(runs_in, runs_in + nruns);
+  plan_runs(runs.data(), nruns, Hq, Hkv, 0);
   RunTotals t;
-  for (int i = 0; i < nruns; ++i) {
-    const RunRow &r = runs[i];
-    const FwdSched f = fwd_sched(r.n, r.M, Hq, Hkv);
+  for (const RunRow &r : runs) {
+    const FwdSched f = fwd_sched_c(r.n, r.M, Hq, Hkv, r.C);
     t.T += (int64_t)r.n * r.M;
     t.PT += (int64_t)r.n * ((r.M + 31) / 32 * 32);
     t.recs += (int64_t)f.nmulti * r.n * Hkv;
@@ -876,12 +1008,12 @@ AttnWs run_view(const AttnWs &w, const RunRow &r, int64_t Hq, int64_t Hkv, int64
 }
 
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd) {
-  const RunRow r{0, 0, (int)B, (int)M, 0, 0};
+  const RunRow r{0, 0, (int)B, (int)M, 0, 0, 0};
   return attn_workspace_bytes_runs(&r, 1, Hq, Hkv, D, bwd);
 }
 
 AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
-  const RunRow r{0, 0, (int)B, (int)M, 0, 0};
+  const RunRow r{0, 0, (int)B, (int)M, 0, 0, 0};
   return carve_attn_ws_runs(ws, &r, 1, Hq, Hkv, D);
 }
 
@@ -901,7 +1033,7 @@ void make_tables(std::vector<Level> &lv, const RunRow *runs, int nruns, int Hkv,
       t.start[i] = INT_MAX;
       t.code[i] = 0;
     }
-    for (int i = 0; i < kMaxRuns; ++i) t.run[i] = i < nruns ? runs[i] : RunRow{0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < kMaxRuns; ++i) t.run[i] = i < nruns ? runs[i] : RunRow{0, 0, 0, 0, 0, 0, 0};
     tabs.push_back(t);
     grids.push_back(wg);
     ne = 0;
@@ -931,6 +1063,76 @@ void make_tables(std::vector<Level> &lv, const RunRow *runs, int nruns, int Hkv,
   if (ne) flush();
 }
 
+bool make_fwd_tables(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, std::vector<RunTable> &tabs,
+                     std::vector<unsigned> &grids) {
+  struct FL {
+    int run, blk, cost;
+    bool split, top;
+    unsigned wgs;
+  };
+  std::vector<FL> lv;
+  for (int i = 0; i < nruns; ++i) {
+    const RunRow &r = runs[i];
+    const FwdSched f = fwd_sched_c(r.n, r.M, Hq, Hkv, r.C);
+    if (f.nqb == 0 || r.n <= 0) return false;
+    for (int qb = f.nqb - 1; qb >= 0; --qb) {
+      const int nt = fwd_ntiles(qb, f.BQ, r.M), np = fwd_npieces(nt, f.C);
+      lv.push_back(FL{i, qb, np > 1 ? f.C : nt, np > 1, qb == f.nqb - 1, (unsigned)(np * r.n * Hkv)});
+    }
+  }
+  // split blocks first, each run's from the top; then the unsplit blocks
+  // longest first, equal lengths by block (down), then run
+  std::stable_sort(lv.begin(), lv.end(), [](const FL &a, const FL &b) {
+    if (a.split != b.split) return a.split;
+    if (a.split) return a.run != b.run ? a.run < b.run : a.blk > b.blk;
+    if (a.cost != b.cost) return a.cost > b.cost;
+    return a.blk != b.blk ? a.blk > b.blk : a.run < b.run;
+  });
+  tabs.clear();
+  grids.clear();
+  RunTable t;
+  int ne = 0, run0 = 0, blk0 = 0, last_run = -1, last_blk = 0, len = 0;
+  bool across = false, unsplit = false;
+  uint64_t wg = 0;
+  auto flush = [&]() {
+    for (int i = ne; i < kMaxEnt; ++i) {
+      t.start[i] = INT_MAX;
+      t.code[i] = 0;
+    }
+    for (int i = 0; i < kMaxRuns; ++i) t.run[i] = i < nruns ? runs[i] : RunRow{0, 0, 0, 0, 0, 0, 0};
+    tabs.push_back(t);
+    grids.push_back((unsigned)wg);
+    ne = 0;
+    wg = 0;
+    last_run = -1;
+  };
+  for (const FL &L : lv) {
+    const bool down = L.run == last_run && L.blk == last_blk - 1;
+    const bool side = unsplit && !L.split && L.blk == last_blk && L.run == last_run + 1;
+    bool merge = ne > 0 && last_run >= 0 && (len == 1 ? down || side : across ? side : down);
+    if (merge && len == 1) across = side;
+    if (!merge) {
+      if (L.split && !L.top) return false;  // a run's split blocks are numbered from its top block
+      if (ne == kMaxEnt) flush();
+      t.start[ne++] = (int)wg;
+      run0 = L.run;
+      blk0 = L.blk;
+      len = 0;
+      across = false;
+      unsplit = true;
+    }
+    unsplit = unsplit && !L.split;
+    last_run = L.run;
+    last_blk = L.blk;
+    ++len;
+    t.code[ne - 1] = run0 | blk0 << 8 | (across ? 1 : 0) << 30;
+    wg += L.wgs;
+    if (wg > (uint64_t)INT_MAX) return false;
+  }
+  if (ne) flush();
+  return true;
+}
+
 hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
                             int B, int M, int Hq, int Hkv, int D, bool rot_k, bool with_bias, bool with_ratio,
                             bool g_per_head, const AttnWs &w, hipStream_t s, const void *q) {
@@ -939,11 +1141,11 @@ hipError_t launch_attn_prep(const void *k, const float *g, const float *gamma, c
   for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
   const int64_t rows = (int64_t)B * M;
   const int64_t R = 256 / (D / 2), nwg_rows = (rows + R - 1) / R, nwg_cnt = ((int64_t)w.ncnt + 255) / 256;
-  hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0, s,
-                     (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
+  hipLaunchKernelGGL(attn_prep_kernel<false>, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0,
+                     s, (rot_k && pos) ? (const uint16_t *)k : nullptr, g, gamma, pos, inv, rows, M, Hq, Hkv, D, w.cs,
                      (rot_k && pos) ? w.khat : nullptr, with_bias ? w.bias : nullptr, with_ratio ? w.ratio : nullptr,
                      w.cnt, with_bias ? w.ncnt : 0, (int)g_per_head, (const uint16_t *)q, q ? w.qhat : nullptr,
-                     (M + 31) / 32);
+                     (M + 31) / 32, PrepRuns{});
   return hipGetLastError();
 }
 
@@ -962,11 +1164,11 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
     const dim3 grid((unsigned)(f.npieces * B * Hkv));
     const float c2 = (float)(c * 1.4426950408889634);
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
-    auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>)
-                         : (sigma ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>);
+    auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true, false> : attn_fwd_bf16_kernel<128, false, false>)
+                         : (sigma ? attn_fwd_bf16_kernel<64, true, false> : attn_fwd_bf16_kernel<64, false, false>);
     hipLaunchKernelGGL(kern, grid, dim3(512), 0, s, (const uint16_t *)w.qhat, (M + 31) / 32, kh, (const uint16_t *)v,
                        w.bias, c2, sigma, w.ratio, B, M, Hq, Hkv, Hq / Hkv, f.BQ, f.nqb, f.C, w.part, w.cnt,
-                       (uint16_t *)o, lse, (uint16_t *)o_lo);
+                       (uint16_t *)o, lse, (uint16_t *)o_lo, NoTable{});
   } else {
     const int64_t rows = (int64_t)B * M * Hq;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const float *)q,
@@ -974,6 +1176,58 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
                        D, (int)g_per_head, (float *)o, lse);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_runs(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                                const int32_t *pos, double theta, float tau, const float *sigma, const RunRow *runs,
+                                int nruns, int Hq, int Hkv, int D, void *o, float *lse, void *o_lo, const AttnWs &w,
+                                hipStream_t s) {
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  InvFreq inv;
+  for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
+  const double c = 1.0 / (sqrt((double)D) * (double)tau);
+  const float c2 = (float)(c * 1.4426950408889634);
+  const int G = Hq / Hkv, BQ = 256 / G;
+  auto kern = D == 128 ? (sigma ? attn_fwd_bf16_kernel<128, true, true> : attn_fwd_bf16_kernel<128, false, true>)
+                       : (sigma ? attn_fwd_bf16_kernel<64, true, true> : attn_fwd_bf16_kernel<64, false, true>);
+  std::vector<RunTable> tabs;
+  std::vector<unsigned> grids;
+  for (int g0 = 0; g0 < nruns; g0 += kMaxRuns) {
+    const int ng = nruns - g0 < kMaxRuns ? nruns - g0 : kMaxRuns;
+    const RunRow *gr = runs + g0;
+    // prep of the group's rows: rotations, bias, temperature ratios, query
+    // fragments; the group's arrival counters cleared
+    PrepRuns pr{};
+    pr.nr = ng;
+    int64_t rows = 0, ncnt = 0;
+    for (int i = 0; i < ng; ++i) {
+      pr.off[i] = gr[i].off - gr[0].off;
+      pr.poff[i] = gr[i].poff - gr[0].poff;
+      pr.M[i] = gr[i].M;
+      rows += (int64_t)gr[i].n * gr[i].M;
+      ncnt += (int64_t)gr[i].n * Hkv * ((gr[i].M + BQ - 1) / BQ);
+    }
+    if (rows == 0) continue;
+    const int64_t off0 = gr[0].off, R = 256 / (D / 2), nwg_rows = (rows + R - 1) / R, nwg_cnt = (ncnt + 255) / 256;
+    hipLaunchKernelGGL(attn_prep_kernel<true>, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256),
+                       0, s, pos ? (const uint16_t *)k + off0 * Hkv * D : nullptr, g + off0, gamma,
+                       pos ? pos + off0 : nullptr, inv, rows, 0, Hq, Hkv, D, w.cs + off0 * (D / 2),
+                       pos ? w.khat + off0 * Hkv * D : nullptr, w.bias + off0 * Hq, sigma ? w.ratio + off0 : nullptr,
+                       w.cnt + gr[0].cnt0, (int)ncnt, 0, (const uint16_t *)q + off0 * Hq * D,
+                       w.qhat + (int64_t)gr[0].poff * Hq * D, 0, pr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!make_fwd_tables(gr, ng, Hq, Hkv, tabs, grids)) return hipErrorInvalidValue;
+    const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;
+    for (size_t t = 0; t < tabs.size(); ++t) {
+      hipLaunchKernelGGL(kern, dim3(grids[t]), dim3(512), 0, s, (const uint16_t *)w.qhat, 0, kh, (const uint16_t *)v,
+                         w.bias, c2, sigma, w.ratio, 0, 0, Hq, Hkv, G, BQ, 0, 0, w.part, w.cnt, (uint16_t *)o, lse,
+                         (uint16_t *)o_lo, tabs[t]);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace tg

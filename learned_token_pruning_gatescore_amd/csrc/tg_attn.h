@@ -29,9 +29,10 @@ struct AttnWs {
 // another from token off of the packed tensors; poff counts the padded tokens
 // before it (each sequence's length rounded up to 32), which place the
 // padded workspace arrays.  rec0 and cnt0 are the run's first partial record
-// and first arrival counter of the forward's split query blocks.
+// and first arrival counter of the forward's split query blocks, C the key
+// tiles per piece of its forward (one value for all runs of a launch).
 struct RunRow {
-  int off, poff, n, M, rec0, cnt0;
+  int off, poff, n, M, rec0, cnt0, C;
 };
 constexpr int kMaxRuns = 16;  // runs per launch
 constexpr int kMaxEnt = 64;   // work-group ranges per launch
@@ -81,18 +82,34 @@ void make_tables(std::vector<Level> &lv, const RunRow *runs, int nruns, int Hkv,
 // arrays of every run side by side (the layout of one run's workspace with
 // B M tokens replaced by the runs' total, and the padded arrays by the
 // padded total).  run_view gives one run's part of it as a workspace of its
-// own.
+// own.  plan_runs sets each run's placement and its forward's C, one per
+// group of kMaxRuns consecutive runs (the runs one forward launch takes).
 void plan_runs(RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D);
 size_t attn_workspace_bytes_runs(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D, bool bwd);
 AttnWs carve_attn_ws_runs(void *ws, const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, int64_t D);
 AttnWs run_view(const AttnWs &w, const RunRow &r, int64_t Hq, int64_t Hkv, int64_t D);
 
 // Split schedule of the bf16 forward (query block size, blocks, tiles per
-// piece, pieces, pieces of split blocks).
+// piece, pieces, pieces of split blocks).  fwd_sched_c: the schedule with C
+// tiles per piece; fwd_sched: with the C chosen for the batch alone.
 struct FwdSched {
   int BQ, nqb, C, npieces, nmulti;
 };
 FwdSched fwd_sched(int64_t B, int64_t M, int64_t Hq, int64_t Hkv);
+FwdSched fwd_sched_c(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int C);
+
+// Work-group tables of the bf16 forward over runs[0 .. nruns) (one group of
+// at most kMaxRuns runs, planned by plan_runs, so every run has the same C).
+// A level is one query block of one run with all its pieces (n Hkv
+// work-groups per piece, the pieces outer).  Levels of split blocks come
+// first, each run's from its top block down (their records are numbered from
+// the top); then the unsplit blocks longest first.  A range holds the blocks
+// blk0, blk0 - 1, ... of one run (code bit 30 clear), or block blk0 of the
+// runs run, run + 1, ... (bit 30 set; unsplit blocks only).
+// code[e] = run | blk0 << 8 | across_runs << 30.  Returns false when a table
+// cannot hold the schedule (never for the shapes the planner admits).
+bool make_fwd_tables(const RunRow *runs, int nruns, int64_t Hq, int64_t Hkv, std::vector<RunTable> &tabs,
+                     std::vector<unsigned> &grids);
 
 size_t attn_workspace_bytes(int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D, bool bwd);
 AttnWs carve_attn_ws(void *ws, int64_t B, int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
@@ -103,6 +120,13 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
                            int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, void *o_lo,
                            const AttnWs &w, hipStream_t s);
+// bf16 forward over the runs of a packed batch (planned by plan_runs; w is
+// the workspace of all runs): per group of kMaxRuns runs one prep launch and
+// one forward launch per work-group table.  The tensors are the packed ones.
+hipError_t launch_attn_fwd_runs(const void *q, const void *k, const void *v, const float *g, const float *gamma,
+                                const int32_t *pos, double theta, float tau, const float *sigma, const RunRow *runs,
+                                int nruns, int Hq, int Hkv, int D, void *o, float *lse, void *o_lo, const AttnWs &w,
+                                hipStream_t s);
 // Backward over the runs of a packed batch (one run: an ordinary batch).
 // The tensors are the packed ones; w is the workspace of all runs.  With o
 // and o_lo (bf16) the row terms D_i come from dO . (o + o_lo).  With
