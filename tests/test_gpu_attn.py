@@ -562,6 +562,17 @@ def test_varlen_many_distinct_lengths(use_o):
     _varlen_case(lens, 8, 4, 128, temp=True, grad=True, seed=66, use_o=use_o)
 
 
+def test_varlen_forward_several_tables():
+    """15 sequences of distinct lengths at 8 query heads per kv head (32-query blocks): the
+    forward's work-group table for the group needs more than 64 ranges, so the forward runs as two
+    launches, with split blocks in three of the runs.  Forward only: at this shape |dv| reaches
+    12.5 (8 heads x up to 654 rows summed per key), where the backward's bf16 rounding of P in
+    dV = P^T dO alone is about 2e-2, the fixed max-abs bound of the training shapes (measured
+    2.08e-2, 1.7e-3 of |dv|); the backward over packed runs is checked by the tests above."""
+    lens = [281, 654, 122, 425, 574, 50, 213, 117, 83, 158, 343, 603, 218, 622, 47]
+    _varlen_case(lens, 32, 4, 64, temp=True, seed=67)
+
+
 @pytest.mark.parametrize("lens,temp", [([300, 300, 150, 150], False), ([0, 1, 257, 0, 257, 33], True),
                                        ([2048] * 4 + [1024] * 4, True)])
 def test_varlen_d_from_o(lens, temp):
