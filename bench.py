@@ -648,12 +648,17 @@ def run_sweep(args):
             torch.cuda.synchronize()
             per = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
                    for j, (nm, _) in enumerate(launches)}
+            # step: back-to-back passes between two events on the launch stream (a wall clock over a
+            # few passes from a synchronised start also counts the first enqueue and the final sync)
+            nw = max(args.steps, 10)
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(n):
+            t0.record()
+            for _ in range(nw):
                 step()
+            t1.record()
             torch.cuda.synchronize()
-            wall = (time.perf_counter() - t0) / n
+            wall = t0.elapsed_time(t1) * 1e-3 / nw
             attn_flops = 4.0 * w.B * w.Hq * w.D * M * (M + 1) / 2
             print(json.dumps(dict(sweep=name, N=w.N, K=K, M=M, step_us=wall * 1e6, tokens_per_s=w.B * w.N / wall,
                                   kernels_us_with_events=per,
