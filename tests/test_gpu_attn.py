@@ -573,6 +573,40 @@ def test_varlen_forward_several_tables():
     _varlen_case(lens, 32, 4, 64, temp=True, seed=67)
 
 
+def test_varlen_fwd_deterministic():
+    """The packed forward twice on the same inputs (20 distinct lengths: two groups of runs, split
+    blocks merged in the second group, the temperature, o_lo): o, o_lo and lse bitwise equal."""
+    import torch
+    import learned_token_pruning_gatescore_amd as tg
+
+    lens = [int(x) for x in np.random.default_rng(66).choice(np.arange(600, 1301), 20, replace=False)]
+    Hq, Hkv, D = 8, 4, 128
+    rng = np.random.default_rng(68)
+    T_ = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    dev = device()
+    q, k, v = (dev_tensor(wl.bf16_bits(rng.standard_normal((T_, h, D), dtype=np.float32)), "bf16", dev)
+               for h in (Hq, Hkv, Hkv))
+    g = torch.from_numpy((1.0 / (1.0 + np.exp(-rng.standard_normal(T_)))).astype(np.float32)).to(dev)
+    gamma = torch.from_numpy(rng.uniform(0.5, 1.5, Hq).astype(np.float32)).to(dev)
+    pos = torch.from_numpy(np.concatenate([np.sort(rng.choice(4 * n, n, replace=False)) for n in lens])
+                           .astype(np.int32)).to(dev)
+    sigma = torch.from_numpy((0.54 + 0.5 * rng.standard_normal(Hq)).astype(np.float32)).to(dev)
+    ws = tg.attn_varlen_workspace(cu, Hq, Hkv, D, False, dev)
+    outs = []
+    for _ in range(2):
+        o, o_lo = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+        lse = torch.full((Hq * T_,), float("nan"), device=dev)
+        tg.tg_gated_attn_fwd_varlen(q, k, v, g, gamma, pos, wl.ROPE_THETA, 1.1, cu, o, lse, ws, sigma=sigma,
+                                    o_lo=o_lo)
+        torch.cuda.synchronize()
+        outs.append((o, o_lo, lse))
+    for a, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32),
+                           b_.view(torch.int16 if b_.dtype == torch.bfloat16 else torch.int32))
+    assert not torch.isnan(outs[0][2]).any()
+
+
 @pytest.mark.parametrize("lens,temp", [([300, 300, 150, 150], False), ([0, 1, 257, 0, 257, 33], True),
                                        ([2048] * 4 + [1024] * 4, True)])
 def test_varlen_d_from_o(lens, temp):
