@@ -221,6 +221,8 @@ def run_gpu(args):
         log(f"copy calibration: {nb} bytes read + {nb} bytes written")
     if args.train_steps:
         res["training_path"] = run_train(args, tg, wl, dev)
+    res["plain_attention_reference"] = run_plain_reference(
+        dev, M, kern["attn_fwd"]["us"], res["training_path"]["fwd_us"] if "training_path" in res else None)
     # gpu-side data needed by the CPU baseline (the same inputs)
     res["host_inputs"] = dict(gi=gi, sel=sel, at=at)
     return res
@@ -530,6 +532,42 @@ def run_train_varlen(args, tg, wl, dev, w, use_o):
                 tokens_per_s=T_ / (fwd + bwd))
 
 
+def run_plain_reference(dev, M, gated_c3_us, gated_train_us):
+    """Context for DeepDive section 3.2's statement that the gate-biased attention call costs about what a
+    plain fused call costs: PyTorch's fused attention (flash backend only, so no fallback path runs) doing
+    plain causal softmax attention -- no gate bias, no RoPE, no temperature, K and V repeated to all 16
+    query heads -- at the 32K-context shape (B=1, M kept rows) and at the training shape (B=4, M=2048),
+    next to tg_gated_attn_fwd's per-call time (prep + forward) at the same shapes. Not part of `value`."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    out = dict(impl="torch.nn.functional.scaled_dot_product_attention, flash backend only (plain causal: "
+                    "no gate bias, no RoPE, no temperature; K/V repeated to the 16 query heads), bf16")
+    for name, B, Mx, ours in (("long_context", 1, M, gated_c3_us), ("training", 4, 2048, gated_train_us)):
+        try:
+            q = torch.randn(B, 16, Mx, 128, device=dev, dtype=torch.bfloat16)
+            k = torch.randn(B, 8, Mx, 128, device=dev, dtype=torch.bfloat16).repeat_interleave(2, dim=1).contiguous()
+            v = torch.randn(B, 8, Mx, 128, device=dev, dtype=torch.bfloat16).repeat_interleave(2, dim=1).contiguous()
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                f = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+                for _ in range(5):
+                    f()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = 30
+                e0.record()
+                for _ in range(n):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+            plain = e0.elapsed_time(e1) / n * 1e3
+            out[name] = dict(B=B, M=Mx, plain_us=plain, gated_us=ours,
+                             gated_over_plain=None if ours is None else ours / plain)
+        except Exception as e:  # backend not available on this build: report, do not fall back
+            out[name] = dict(B=B, M=Mx, error=repr(e)[:200])
+    return out
+
+
 def load_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (profiles/traffic.json), or None when there is none or the kernel's source has
@@ -726,6 +764,7 @@ def main():
     }
     if "training_path" in res:
         line["training_path"] = res["training_path"]
+    line["plain_attention_reference"] = res["plain_attention_reference"]
     if cpu is not None:
         line["cpu_baseline_stage_s"] = cpu["seconds"]
     print(json.dumps(line), flush=True)
