@@ -456,8 +456,9 @@ tg_status tg_gate_score_clone(const void *hidden, int ln, const void *ln_w, floa
  * each work-group holds one block (the forward: one piece of a block) of one
  * sequence of one run, with the blocks of all runs ordered longest first, so
  * sequences of different lengths share the compute units.  The bf16 forward
- * picks its key-split length once for the 16 runs of a launch, and its prep
- * pass covers them in one launch too (f32: one forward launch per run).
+ * picks its key-split length once for the 16 runs of a launch; the prep
+ * passes, and the backward's dg pass, also take 16 runs per launch, and one
+ * reduction gives dgamma (dsigma) (f32: one launch of each kernel per run).
  * The workspace (tg_gated_attn_varlen_workspace_size,
  * 256-byte aligned) holds every run's arrays side by side.  Validation,
  * dtypes and errors as the batched calls; dgamma / dsigma are summed in run

@@ -932,66 +932,105 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_f32_kernel(
 // chunks of 64 per barrier.
 // With per-head gates (gph) g and dg are [B, Hq, M]: dg_hj = gamma_h colsum_h(j) / g_hj and the
 // dgamma share uses ln g_hj.
+// One sequence's 256-token block: token j of row pointers colsum_b, tstat_b
+// ([Hq, M] each), g_b, dg_b; the block's shares go to share[h] (dgamma) and
+// share_t[h] (dsigma, with the temperature).
+__device__ __forceinline__ void dg_tile(const float *__restrict__ colsum_b, const float *__restrict__ tstat_b,
+                                        const float *__restrict__ g_b, const float *__restrict__ gamma, int M, int Hq,
+                                        int gph, int j, float *__restrict__ dg_b, float *__restrict__ share,
+                                        float *__restrict__ share_t, float (*red)[64][4]) {
+  const bool vj = j < M;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float *cr = colsum_b + j;
+  const float *tr = tstat_b ? tstat_b + j : nullptr;
+  const float gv = vj && !gph ? g_b[j] : 0.f;
+  const float lg = gv > 0.f ? logf(gv) : 0.f;
+  float acc = 0.f;
+  for (int h0 = 0; h0 < Hq; h0 += 64) {
+    const int nh = Hq - h0 < 64 ? Hq - h0 : 64;
+    for (int hh = 0; hh < nh; hh += 8) {
+      float v[8], ts[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // eight independent loads in flight
+        const bool ok = vj && hh + e < nh;
+        v[e] = ok ? cr[(int64_t)(h0 + hh + e) * M] : 0.f;
+        ts[e] = ok && tr ? tr[(int64_t)(h0 + hh + e) * M] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (hh + e >= nh) break;
+        acc += gamma[h0 + hh + e] * v[e];
+        float t = gv > 0.f ? v[e] * lg : 0.f;
+        if (gph) {  // this head's own gate
+          const int64_t o = (int64_t)(h0 + hh + e) * M + j;
+          const float gh = vj ? g_b[o] : 0.f;
+          t = gh > 0.f ? v[e] * logf(gh) : 0.f;
+          if (vj) dg_b[o] = gh > 0.f ? gamma[h0 + hh + e] * v[e] / gh : 0.f;
+        }
+        float u = ts[e];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          t += __shfl_xor(t, o);
+          u += __shfl_xor(u, o);
+        }
+        if (lane == 0) {
+          red[0][hh + e][wave] = t;
+          red[1][hh + e][wave] = u;
+        }
+      }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nh) {
+      const int h = h0 + threadIdx.x;
+      const float(*r0)[4] = red[0], (*r1)[4] = red[1];
+      share[h] = (r0[threadIdx.x][0] + r0[threadIdx.x][1]) + (r0[threadIdx.x][2] + r0[threadIdx.x][3]);
+      if (tstat_b) share_t[h] = (r1[threadIdx.x][0] + r1[threadIdx.x][1]) + (r1[threadIdx.x][2] + r1[threadIdx.x][3]);
+    }
+    __syncthreads();
+  }
+  if (vj && !gph) dg_b[j] = gv > 0.f ? acc / gv : 0.f;
+}
+
 __global__ __launch_bounds__(256) void dg_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
                                                  const float *__restrict__ gamma, const float *__restrict__ tstat,
                                                  int B, int M, int Hq, int gph, float *__restrict__ dg,
                                                  float *__restrict__ part) {
   __shared__ float red[2][64][4];
   const int j = blockIdx.x * 256 + threadIdx.x;  // grid (ceil(M / 256), min(B, 65535))
-  const bool vj = j < M;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nshare = (int64_t)B * gridDim.x * Hq;
   for (int b = blockIdx.y; b < B; b += gridDim.y) {
-    const float *cr = colsum + (int64_t)b * Hq * M + j;
-    const float *tr = tstat ? tstat + (int64_t)b * Hq * M + j : nullptr;
-    const float gv = vj && !gph ? g[(int64_t)b * M + j] : 0.f;
-    const float lg = gv > 0.f ? logf(gv) : 0.f;
-    float acc = 0.f;
-    for (int h0 = 0; h0 < Hq; h0 += 64) {
-      const int nh = Hq - h0 < 64 ? Hq - h0 : 64;
-      for (int hh = 0; hh < nh; hh += 8) {
-        float v[8], ts[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {  // eight independent loads in flight
-          const bool ok = vj && hh + e < nh;
-          v[e] = ok ? cr[(int64_t)(h0 + hh + e) * M] : 0.f;
-          ts[e] = ok && tr ? tr[(int64_t)(h0 + hh + e) * M] : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (hh + e >= nh) break;
-          acc += gamma[h0 + hh + e] * v[e];
-          float t = gv > 0.f ? v[e] * lg : 0.f;
-          if (gph) {  // this head's own gate
-            const int64_t o = ((int64_t)b * Hq + h0 + hh + e) * M + j;
-            const float gh = vj ? g[o] : 0.f;
-            t = gh > 0.f ? v[e] * logf(gh) : 0.f;
-            if (vj) dg[o] = gh > 0.f ? gamma[h0 + hh + e] * v[e] / gh : 0.f;
-          }
-          float u = ts[e];
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            t += __shfl_xor(t, o);
-            u += __shfl_xor(u, o);
-          }
-          if (lane == 0) {
-            red[0][hh + e][wave] = t;
-            red[1][hh + e][wave] = u;
-          }
-        }
-      }
-      __syncthreads();
-      if ((int)threadIdx.x < nh) {
-        const int h = h0 + threadIdx.x;
-        const int64_t o = ((int64_t)b * gridDim.x + blockIdx.x) * Hq + h;
-        const float(*r0)[4] = red[0], (*r1)[4] = red[1];
-        part[o] = (r0[threadIdx.x][0] + r0[threadIdx.x][1]) + (r0[threadIdx.x][2] + r0[threadIdx.x][3]);
-        if (tstat) part[nshare + o] = (r1[threadIdx.x][0] + r1[threadIdx.x][1]) + (r1[threadIdx.x][2] + r1[threadIdx.x][3]);
-      }
-      __syncthreads();
-    }
-    if (vj && !gph) dg[(int64_t)b * M + j] = gv > 0.f ? acc / gv : 0.f;
+    const int64_t o = ((int64_t)b * gridDim.x + blockIdx.x) * Hq;
+    const int64_t gb = gph ? (int64_t)b * Hq * M : (int64_t)b * M;
+    dg_tile(colsum + (int64_t)b * Hq * M, tstat ? tstat + (int64_t)b * Hq * M : nullptr, g + gb, gamma, M, Hq, gph,
+            j, dg + gb, part + o, tstat ? part + nshare + o : nullptr, red);
   }
+}
+
+// The same over a packed group of runs (one gate per key): work-group w takes
+// block x of sequence b of run i, where w = wg0[i] + b ceil(M_i / 256) + x;
+// its shares go to slot sh0 + w of a share array that lists every run's
+// blocks in order (nshare slots in all, dsigma shares after them).
+struct DgRuns {
+  int nr, sh0;
+  int wg0[kMaxRuns + 1];
+  int off[kMaxRuns], M[kMaxRuns];
+};
+
+__global__ __launch_bounds__(256) void dg_runs_kernel(const float *__restrict__ colsum, const float *__restrict__ g,
+                                                      const float *__restrict__ gamma,
+                                                      const float *__restrict__ tstat, int Hq, int64_t nshare,
+                                                      float *__restrict__ dg, float *__restrict__ part,
+                                                      const DgRuns dr) {
+  __shared__ float red[2][64][4];
+  const int w = blockIdx.x;
+  int ri = 0;
+  for (int i = 1; i < dr.nr; ++i) ri = w >= dr.wg0[i] ? i : ri;  // uniform
+  const int M = dr.M[ri], nbx = (M + 255) / 256, loc = w - dr.wg0[ri], b = loc / nbx, x = loc - b * nbx;
+  const int64_t off = dr.off[ri];
+  const int64_t rb = off * Hq + (int64_t)b * Hq * M;  // [Hq, M] block of sequence b in a run's [n, Hq, M] array
+  const int64_t o = ((int64_t)dr.sh0 + w) * Hq;
+  dg_tile(colsum + rb, tstat ? tstat + rb : nullptr, g + off + (int64_t)b * M, gamma, M, Hq, 0, x * 256 + threadIdx.x,
+          dg + off + (int64_t)b * M, part + o, tstat ? part + nshare * Hq + o : nullptr, red);
 }
 
 // Block h < Hq: dgamma_h = sum over the n = B * ceil(M / 256) shares of head h;
@@ -1049,8 +1088,19 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
   const int gph = (int)g_per_head;
   const int64_t esz = bf16 ? 2 : 4;
   auto live = [](const RunRow &r) { return (int64_t)r.n * r.M > 0; };
+  // Packed bf16 runs with one gate per key: the prep and dg passes take a
+  // group of runs per launch, and one reduction gives dgamma (dsigma).
+  const bool grouped = bf16 && nruns > 1 && !g_per_head;
+  if (grouped) {
+    for (int g0 = 0; g0 < nruns; g0 += kMaxRuns) {
+      const int ng = nruns - g0 < kMaxRuns ? nruns - g0 : kMaxRuns;
+      const hipError_t e =
+          launch_attn_prep_runs(k, g, gamma, pos, theta, runs + g0, ng, Hq, Hkv, D, sigma != nullptr, w, s, nullptr);
+      if (e != hipSuccess) return e;
+    }
+  }
   // rotated keys, biases, temperature ratios of every run
-  for (int i = 0; i < nruns; ++i) {
+  for (int i = 0; i < nruns && !grouped; ++i) {
     const RunRow &r = runs[i];
     if (!live(r) || !(pos || bf16 || sigma)) continue;
     const int64_t t0 = r.off;
@@ -1123,6 +1173,37 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const fl
                          gamma, cs, lr, dr, delta, c, sigma, wv.ratio, r.n, r.M, Hq, Hkv, D, gph, dk + t0 * Hkv * D,
                          dv + t0 * Hkv * D, wv.colsum);
     }
+  }
+  if (grouped) {
+    // every run's 256-token blocks in order, one share slot each; the row
+    // statistics of all runs are dead by now and hold the shares (2 nshare Hq
+    // floats of their 2 Hq T)
+    int64_t nshare = 0;
+    for (int i = 0; i < nruns; ++i) nshare += (int64_t)runs[i].n * ((runs[i].M + 255) / 256);
+    float *shares = (float *)w.rowstat;
+    int64_t sh = 0;
+    for (int g0 = 0; g0 < nruns; g0 += kMaxRuns) {
+      const int ng = nruns - g0 < kMaxRuns ? nruns - g0 : kMaxRuns;
+      DgRuns dr{};
+      dr.nr = ng;
+      dr.sh0 = (int)sh;
+      int64_t wg = 0;
+      for (int i = 0; i < ng; ++i) {
+        const RunRow &r = runs[g0 + i];
+        dr.wg0[i] = (int)wg;
+        dr.off[i] = r.off;
+        dr.M[i] = r.M;
+        wg += (int64_t)r.n * ((r.M + 255) / 256);
+      }
+      dr.wg0[ng] = (int)wg;
+      if (wg > 0)
+        hipLaunchKernelGGL(dg_runs_kernel, dim3((unsigned)wg), dim3(256), 0, s, w.colsum, g, gamma,
+                           sigma ? (const float *)w.tstat : nullptr, Hq, nshare, dg, shares, dr);
+      sh += wg;
+    }
+    hipLaunchKernelGGL(dgamma_kernel, dim3((unsigned)(sigma ? 2 * Hq : Hq)), dim3(256), 0, s, (const float *)shares,
+                       (int)nshare, Hq, sigma, dgamma, dsigma);
+    return hipGetLastError();
   }
   // dg per token, and per run the dgamma (dsigma) sums; a run's row
   // statistics are dead by now: their space (2 n Hq M floats) takes its

@@ -1178,13 +1178,39 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
   return hipGetLastError();
 }
 
+hipError_t launch_attn_prep_runs(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
+                                 const RunRow *runs, int nruns, int Hq, int Hkv, int D, bool with_ratio,
+                                 const AttnWs &w, hipStream_t s, const void *q) {
+  if (nruns < 1 || nruns > kMaxRuns) return hipErrorInvalidValue;
+  InvFreq inv;
+  for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
+  const int BQ = 256 / (Hq / Hkv);
+  PrepRuns pr{};
+  pr.nr = nruns;
+  int64_t rows = 0, ncnt = 0;
+  for (int i = 0; i < nruns; ++i) {
+    pr.off[i] = runs[i].off - runs[0].off;
+    pr.poff[i] = runs[i].poff - runs[0].poff;
+    pr.M[i] = runs[i].M;
+    rows += (int64_t)runs[i].n * runs[i].M;
+    ncnt += (int64_t)runs[i].n * Hkv * ((runs[i].M + BQ - 1) / BQ);
+  }
+  if (rows == 0) return hipSuccess;
+  const int64_t off0 = runs[0].off, R = 256 / (D / 2), nwg_rows = (rows + R - 1) / R, nwg_cnt = (ncnt + 255) / 256;
+  hipLaunchKernelGGL(attn_prep_kernel<true>, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256), 0,
+                     s, pos ? (const uint16_t *)k + off0 * Hkv * D : nullptr, g + off0, gamma,
+                     pos ? pos + off0 : nullptr, inv, rows, 0, Hq, Hkv, D, w.cs + off0 * (D / 2),
+                     pos ? w.khat + off0 * Hkv * D : nullptr, w.bias + off0 * Hq, with_ratio ? w.ratio + off0 : nullptr,
+                     w.cnt + runs[0].cnt0, (int)ncnt, 0, q ? (const uint16_t *)q + off0 * Hq * D : nullptr,
+                     q ? w.qhat + (int64_t)runs[0].poff * Hq * D : nullptr, 0, pr);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd_runs(const void *q, const void *k, const void *v, const float *g, const float *gamma,
                                 const int32_t *pos, double theta, float tau, const float *sigma, const RunRow *runs,
                                 int nruns, int Hq, int Hkv, int D, void *o, float *lse, void *o_lo, const AttnWs &w,
                                 hipStream_t s) {
   if (D != 64 && D != 128) return hipErrorInvalidValue;
-  InvFreq inv;
-  for (int i = 0; i < 64; ++i) inv.v[i] = i < D / 2 ? pow(theta, -2.0 * (double)i / (double)D) : 0.0;
   const double c = 1.0 / (sqrt((double)D) * (double)tau);
   const float c2 = (float)(c * 1.4426950408889634);
   const int G = Hq / Hkv, BQ = 256 / G;
@@ -1195,27 +1221,7 @@ hipError_t launch_attn_fwd_runs(const void *q, const void *k, const void *v, con
   for (int g0 = 0; g0 < nruns; g0 += kMaxRuns) {
     const int ng = nruns - g0 < kMaxRuns ? nruns - g0 : kMaxRuns;
     const RunRow *gr = runs + g0;
-    // prep of the group's rows: rotations, bias, temperature ratios, query
-    // fragments; the group's arrival counters cleared
-    PrepRuns pr{};
-    pr.nr = ng;
-    int64_t rows = 0, ncnt = 0;
-    for (int i = 0; i < ng; ++i) {
-      pr.off[i] = gr[i].off - gr[0].off;
-      pr.poff[i] = gr[i].poff - gr[0].poff;
-      pr.M[i] = gr[i].M;
-      rows += (int64_t)gr[i].n * gr[i].M;
-      ncnt += (int64_t)gr[i].n * Hkv * ((gr[i].M + BQ - 1) / BQ);
-    }
-    if (rows == 0) continue;
-    const int64_t off0 = gr[0].off, R = 256 / (D / 2), nwg_rows = (rows + R - 1) / R, nwg_cnt = (ncnt + 255) / 256;
-    hipLaunchKernelGGL(attn_prep_kernel<true>, dim3((unsigned)(nwg_rows > nwg_cnt ? nwg_rows : nwg_cnt)), dim3(256),
-                       0, s, pos ? (const uint16_t *)k + off0 * Hkv * D : nullptr, g + off0, gamma,
-                       pos ? pos + off0 : nullptr, inv, rows, 0, Hq, Hkv, D, w.cs + off0 * (D / 2),
-                       pos ? w.khat + off0 * Hkv * D : nullptr, w.bias + off0 * Hq, sigma ? w.ratio + off0 : nullptr,
-                       w.cnt + gr[0].cnt0, (int)ncnt, 0, (const uint16_t *)q + off0 * Hq * D,
-                       w.qhat + (int64_t)gr[0].poff * Hq * D, 0, pr);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_attn_prep_runs(k, g, gamma, pos, theta, gr, ng, Hq, Hkv, D, sigma != nullptr, w, s, q);
     if (e != hipSuccess) return e;
     if (!make_fwd_tables(gr, ng, Hq, Hkv, tabs, grids)) return hipErrorInvalidValue;
     const uint16_t *kh = pos ? w.khat : (const uint16_t *)k;

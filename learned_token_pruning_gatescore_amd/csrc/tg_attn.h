@@ -120,6 +120,13 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const fl
                            const int32_t *pos, double theta, float tau, const float *sigma, int B, int M, int Hq,
                            int Hkv, int D, bool bf16, bool g_per_head, void *o, float *lse, void *o_lo,
                            const AttnWs &w, hipStream_t s);
+// The prep pass over one group of at most kMaxRuns consecutive runs of a
+// packed batch, in one launch: the angles, rotated keys (bf16, with positions),
+// biases (one gate per key), temperature ratios (with_ratio), and with q the
+// forward's query fragments; the group's arrival counters cleared.
+hipError_t launch_attn_prep_runs(const void *k, const float *g, const float *gamma, const int32_t *pos, double theta,
+                                 const RunRow *runs, int nruns, int Hq, int Hkv, int D, bool with_ratio,
+                                 const AttnWs &w, hipStream_t s, const void *q);
 // bf16 forward over the runs of a packed batch (planned by plan_runs; w is
 // the workspace of all runs): per group of kMaxRuns runs one prep launch and
 // one forward launch per work-group table.  The tensors are the packed ones.
