@@ -53,9 +53,12 @@ struct Unit {
 };
 // The run, block and (batch row * Hkv + kv head) of work-group w.
 __host__ __device__ __forceinline__ Unit unit_of(const RunTable &rt, int w, int Hkv) {
+  // the range: the last e with start[e] <= w (start rises from start[0] = 0,
+  // INT_MAX past the last range); a binary search, uniform on the device
   int e = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxEnt; ++i) e += w >= rt.start[i] ? 1 : 0;
+  for (int step = kMaxEnt / 2; step >= 1; step >>= 1)
+    if (w >= rt.start[e + step]) e += step;
   const int code = rt.code[e];
   Unit u;
   u.run = code & 0xFF;
