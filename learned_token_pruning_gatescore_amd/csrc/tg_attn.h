@@ -35,7 +35,7 @@ struct RunRow {
   int off, poff, n, M, rec0, cnt0, C;
 };
 constexpr int kMaxRuns = 16;  // runs per launch
-constexpr int kMaxEnt = 64;   // work-group ranges per launch
+constexpr int kMaxEnt = 256;  // work-group ranges per launch
 
 // Work-group table of one launch over runs.  The launch's work-groups are
 // cut into ranges; range e starts at work-group start[e] (start[0] = 0,
