@@ -582,6 +582,15 @@ def test_varlen_forward_g8_split_runs():
     _varlen_case(lens, 32, 4, 64, temp=True, seed=67)
 
 
+def test_varlen_runs_over_groups_g1_no_rope():
+    """40 sequences (4205 tokens) forming 32 runs, 8 of them of two equal-length sequences: two
+    groups of 16 runs, with runs of n > 1 in both; one query head per kv head (256-query blocks),
+    no positions, the temperature; forward and backward against the oracle."""
+    lens = [149, 149, 84, 164, 89, 84, 84, 213, 188, 168, 137, 137, 102, 61, 143, 20, 20, 176, 75, 66, 98, 98,
+            107, 88, 144, 54, 54, 29, 140, 67, 120, 120, 138, 163, 204, 53, 53, 24, 106, 36]
+    _varlen_case(lens, 4, 4, 64, rope=False, temp=True, grad=True, seed=70)
+
+
 def test_varlen_fwd_deterministic():
     """The packed forward twice on the same inputs (20 distinct lengths: two groups of runs, split
     blocks merged in the second group, the temperature, o_lo): o, o_lo and lse bitwise equal."""
