@@ -453,6 +453,7 @@ def run_train(args, tg, wl, dev):
     out = dict(workload=w.name, B=w.B, M=M)
     out["two_budgets_packed"] = run_train_varlen(args, tg, wl, dev, w, False)
     out["two_budgets_packed_d_from_o"] = run_train_varlen(args, tg, wl, dev, w, True)
+    out["per_sample_budgets_packed"] = run_train_varlen(args, tg, wl, dev, w, False, per_sample=True)
     # without o: the backward forms D_i by its own pass over the keys; with o: the forward also
     # writes o_lo and the backward takes D_i = dO . (o + o_lo)
     for use_o in (False, True):
@@ -476,13 +477,20 @@ def run_train(args, tg, wl, dev):
     return out
 
 
-def run_train_varlen(args, tg, wl, dev, w, use_o):
+def run_train_varlen(args, tg, wl, dev, w, use_o, per_sample=False):
     """Both training budgets in one packed call (DeepDive section 3.3): each of the B rows at its
     full budget (M = 2048 kept) and at half of it (1024), packed by budget, forward + backward with
-    the Eq. 7/8 temperature (not part of `value`); use_o: the backward's row terms from o + o_lo."""
+    the Eq. 7/8 temperature (not part of `value`); use_o: the backward's row terms from o + o_lo.
+    per_sample: the budget drawn per sample, as the pages train (log-uniform): 2B rows, each row's
+    kept count drawn log-uniform in [512, 2048] and the same row again at half of it, so every
+    sequence of the packing has its own length."""
     import torch
 
     lens = [w.M_fixed] * w.B + [w.M_fixed // 2] * w.B
+    if per_sample:
+        kr = np.exp(np.random.default_rng(w.seed + 3100).uniform(np.log(512), np.log(2048), 2 * w.B))
+        full = [int(x) for x in np.round(kr)]
+        lens = full + [m // 2 for m in full]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     T_ = int(cu[-1])
     rs = np.random.default_rng(w.seed + 3000)
@@ -527,7 +535,8 @@ def run_train_varlen(args, tg, wl, dev, w, use_o):
     fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
     bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
     ff = sum(4.0 * w.Hq * w.D * n * (n + 1) / 2 for n in lens)
-    return dict(lens=f"{w.B} x {w.M_fixed} + {w.B} x {w.M_fixed // 2}", tokens=T_, fwd_us=fwd * 1e6,
+    return dict(lens=(f"{len(lens)} lengths (2 x {2 * w.B} rows, budgets drawn log-uniform per row)" if per_sample
+                      else f"{w.B} x {w.M_fixed} + {w.B} x {w.M_fixed // 2}"), tokens=T_, fwd_us=fwd * 1e6,
                 bwd_us=bwd * 1e6, fwd_mfma_frac=ff / fwd / PEAK_BF16, bwd_mfma_frac=2.5 * ff / bwd / PEAK_BF16,
                 tokens_per_s=T_ / (fwd + bwd))
 
