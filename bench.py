@@ -572,7 +572,7 @@ def run_plain_reference(dev, M, gated_c3_us, gated_train_us):
             plain = e0.elapsed_time(e1) / n * 1e3
             out[name] = dict(B=B, M=Mx, plain_us=plain, gated_us=ours,
                              gated_over_plain=None if ours is None else ours / plain)
-        except Exception as e:  # backend not available on this build: report, do not fall back
+        except Exception as e:  # backend not available in this PyTorch: report, do not fall back
             out[name] = dict(B=B, M=Mx, error=repr(e)[:200])
     return out
 
