@@ -229,6 +229,41 @@ def test_select_sweep_128k(K):
     np.testing.assert_array_equal(got, ref)
 
 
+def test_select_longest_rows():
+    # the longest rows selection accepts (2^22 tokens, 1024 work-groups per row in the multi-work-group form), two
+    # rows on the bf16 grid with high-score spans (ties everywhere), a budget that cuts inside a tie class and a
+    # second row whose budget keeps every prunable token but one
+    N = 1 << 22
+    rng = np.random.default_rng(22)
+    s = wl.bf16_to_f32(wl.bf16_bits(rng.standard_normal((2, N)).astype(np.float32)))
+    for b in range(2):
+        for st in rng.choice(N - 64, 400, replace=False):
+            s[b, st:st + int(rng.integers(8, 64))] += 3.0
+    f = np.zeros((2, N), np.uint8)
+    f[:, :256] = 1
+    f[:, rng.choice(N, 1000, replace=False)] = 1
+    nF = int(f[0].sum())
+    f[1] = f[0]
+    for K in (65536, N - nF - 1):
+        got, cnt, ref, rc = _select(s, f, K, nF)
+        np.testing.assert_array_equal(got, ref)
+        np.testing.assert_array_equal(cnt, rc)
+        assert cnt[0] == nF + K
+
+
+def test_select_most_rows():
+    # the largest batch selection accepts (65535 rows, one work-group each), short rows with ties and forced tokens
+    B, N, K = 65535, 40, 5
+    rng = np.random.default_rng(65535)
+    s = rng.integers(-3, 4, (B, N)).astype(np.float32)
+    f = np.zeros((B, N), np.uint8)
+    f[:, 0] = 1
+    f[:, 17] = 1
+    got, cnt, ref, rc = _select(s, f, K, 2)
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(cnt, rc)
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 2048), ("f32", 256), ("bf16", 8)])
 def test_compact_bit_exact(dtype, d):
     import torch
